@@ -1,0 +1,188 @@
+"""CPU oracle for the single-GPU MoE route -> dispatch -> expert FFN -> combine path.
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by __graft_entry__.smoke() and by
+bench.py's cpu_baseline leg, never by the product package.  It wraps the plain
+C reference in moe_oracle.c (fp64 arithmetic except where a step fixes another
+precision; see that file's header for the sources of each step) and shares no
+code with the GPU library.
+
+Every oracle function here is pinned by the CPU tests in tests/test_oracle_pins.py
+against brute force on tiny inputs, closed forms and invariants.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_HERE = Path(__file__).resolve().parent
+_SRC = _HERE / "moe_oracle.c"
+_LIB = _HERE / "libmoe_oracle.so"
+
+DT_F32 = 0
+DT_BF16 = 1
+
+
+def build(force: bool = True) -> Path:
+    """Compile moe_oracle.c with gcc (plain C11, -O2, no floating-point contraction)."""
+    if force or not _LIB.exists():
+        tmp = _LIB.with_suffix(".so.tmp")
+        subprocess.check_call(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
+                               "-shared", "-o", str(tmp), str(_SRC), "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not _LIB.exists():
+            build()
+        L = C.CDLL(str(_LIB))
+        p, i64, i32 = C.c_void_p, C.c_int64, C.c_int
+        L.oracle_route.argtypes = [i64, i32, i32, p, p, p, p, p]
+        L.oracle_route.restype = i32
+        L.oracle_layout_rows.argtypes = [i64, i32, i32, i32, i64]
+        L.oracle_layout_rows.restype = i64
+        L.oracle_layout.argtypes = [i64, i32, i32, i32, i64, p, p, p, p, p, p, p, p, p]
+        L.oracle_layout.restype = i32
+        L.oracle_scatter.argtypes = [i64, i32, i64, p, p, p, i64, p, i32, p, p]
+        L.oracle_scatter.restype = None
+        L.oracle_expert_ffn_rows.argtypes = [i64, p, i32, i64, i64, p, p, p, p, p, p, p]
+        L.oracle_expert_ffn_rows.restype = None
+        L.oracle_combine.argtypes = [i64, i32, i64, i32, p, p, p, p]
+        L.oracle_combine.restype = None
+        L.oracle_combine_bwd.argtypes = [i64, i32, i64, i32, p, p, p, p, i64, p, i32, p, p]
+        L.oracle_combine_bwd.restype = None
+        L.oracle_bf16_round.argtypes = [C.c_double]
+        L.oracle_bf16_round.restype = C.c_uint16
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(C.c_void_p)
+
+
+def _dt(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return DT_F32
+    if a.dtype == np.uint16:
+        return DT_BF16
+    raise TypeError(f"activations must be float32 or bf16 bits (uint16), got {a.dtype}")
+
+
+def route(logits: np.ndarray, k: int):
+    """-> topk_idx int32 [N,k], topk_w fp32 [N,k], routing_map uint8 [N,E], tokens_per_expert int32 [E]."""
+    logits = np.ascontiguousarray(logits, dtype=np.float32)
+    n, e = logits.shape
+    idx = np.empty((n, k), np.int32)
+    w = np.empty((n, k), np.float32)
+    rmap = np.empty((n, e), np.uint8)
+    tpe = np.empty(e, np.int32)
+    rc = lib().oracle_route(n, e, k, _p(logits), _p(idx), _p(w), _p(rmap), _p(tpe))
+    if rc != 0:
+        raise ValueError(f"oracle_route: bad arguments (rc={rc})")
+    return idx, w, rmap, tpe
+
+
+def layout(topk_idx: np.ndarray, n_experts: int, capacity: int = 0, max_rows: int = 0) -> dict:
+    """Dispatch layout; returns a dict of numpy arrays (see moe_oracle.c oracle_layout)."""
+    topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    n, k = topk_idx.shape
+    rows = lib().oracle_layout_rows(n, k, n_experts, capacity, max_rows)
+    out = dict(
+        tokens_per_expert=np.empty(n_experts, np.int32),
+        expert_offsets=np.empty(n_experts + 1, np.int32),
+        ordinal=np.empty(n * k, np.int32),
+        assign_row=np.empty(n * k, np.int32),
+        row_src=np.empty(rows, np.int32),
+        drop_mask=np.empty(n * k, np.uint8),
+        pad_mask=np.empty(rows, np.uint8),
+        counters=np.empty(4, np.int32),
+    )
+    rc = lib().oracle_layout(n, k, n_experts, capacity, max_rows, _p(topk_idx),
+                             *[_p(out[f]) for f in ("tokens_per_expert", "expert_offsets", "ordinal",
+                                                    "assign_row", "row_src", "drop_mask", "pad_mask", "counters")])
+    if rc != 0:
+        raise ValueError(f"oracle_layout: bad arguments (rc={rc})")
+    out["rows"] = int(rows)
+    return out
+
+
+def scatter(x: np.ndarray, k: int, lay: dict, topk_w: np.ndarray, capacity: int = 0, x_perm=None):
+    """Permuted rows and weights: -> (x_perm [rows, H], w_perm [rows]).  Rows of an
+    unused dropless tail keep what `x_perm` held (zeros if not given)."""
+    x = np.ascontiguousarray(x)
+    n, h = x.shape
+    rows = lay["rows"]
+    if x_perm is None:
+        x_perm = np.zeros((rows, h), x.dtype)
+    w_perm = np.empty(rows, np.float32)
+    topk_w = np.ascontiguousarray(topk_w, dtype=np.float32)
+    lib().oracle_scatter(n, k, h * x.itemsize, _p(x), _p(lay["assign_row"]), _p(topk_w), rows,
+                         _p(lay["row_src"]), capacity, _p(x_perm), _p(w_perm))
+    return x_perm, w_perm
+
+
+def expert_ffn_rows(rows, x_perm, lay, w_gate_up, w_down):
+    """SwiGLU FFN output rows (bf16 bits) for the listed permuted rows -> (y_rows [len, H], expert_of)."""
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    e, two_i, h = w_gate_up.shape
+    inter = two_i // 2
+    assert x_perm.dtype == np.uint16 and w_gate_up.dtype == np.uint16 and w_down.dtype == np.uint16
+    assert w_down.shape == (e, h, inter)
+    y = np.zeros((rows.size, h), np.uint16)
+    ex = np.empty(rows.size, np.int32)
+    lib().oracle_expert_ffn_rows(rows.size, _p(rows), e, h, inter, _p(np.ascontiguousarray(x_perm)),
+                                 _p(lay["expert_offsets"]), _p(lay["tokens_per_expert"]),
+                                 _p(np.ascontiguousarray(w_gate_up)), _p(np.ascontiguousarray(w_down)),
+                                 _p(y), _p(ex))
+    return y, ex
+
+
+def expert_ffn(x_perm, lay, w_gate_up, w_down):
+    """FFN over every kept row; rows outside the segments are returned as zeros."""
+    rows = np.nonzero(lay["pad_mask"] == 0)[0]
+    y_rows, _ = expert_ffn_rows(rows, x_perm, lay, w_gate_up, w_down)
+    y = np.zeros((lay["rows"], x_perm.shape[1]), np.uint16)
+    y[rows] = y_rows
+    return y
+
+
+def combine(y: np.ndarray, topk_w: np.ndarray, lay: dict, n: int, k: int):
+    y = np.ascontiguousarray(y)
+    h = y.shape[1]
+    out = np.empty((n, h), y.dtype)
+    lib().oracle_combine(n, k, h, _dt(y), _p(y), _p(np.ascontiguousarray(topk_w, dtype=np.float32)),
+                         _p(lay["assign_row"]), _p(out))
+    return out
+
+
+def combine_bwd(grad_out: np.ndarray, y: np.ndarray, topk_w: np.ndarray, lay: dict, k: int,
+                capacity: int = 0, grad_y=None):
+    """-> (grad_y [rows, H], grad_w fp32 [N, k]).  Unused dropless tail rows keep what
+    `grad_y` held (zeros if not given)."""
+    grad_out = np.ascontiguousarray(grad_out)
+    y = np.ascontiguousarray(y)
+    n, h = grad_out.shape
+    assert y.dtype == grad_out.dtype
+    rows = lay["rows"]
+    if grad_y is None:
+        grad_y = np.zeros((rows, h), y.dtype)
+    grad_w = np.empty((n, k), np.float32)
+    lib().oracle_combine_bwd(n, k, h, _dt(y), _p(grad_out), _p(y),
+                             _p(np.ascontiguousarray(topk_w, dtype=np.float32)), _p(lay["assign_row"]),
+                             rows, _p(lay["row_src"]), capacity, _p(grad_y), _p(grad_w))
+    return grad_y, grad_w
+
+
+def bf16_round(x: float) -> int:
+    return int(lib().oracle_bf16_round(float(x)))

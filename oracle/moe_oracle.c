@@ -1,0 +1,351 @@
+/*
+ * moe_oracle.c -- plain, slow, obviously-correct CPU reference of the single-GPU
+ * Mixture-of-Experts path: route -> dispatch (layout + row scatter) -> SwiGLU
+ * expert FFN -> probability-weighted combine, and the combine's backward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg may load this file's library.  The GPU library
+ * shares no code, header, table or helper with it.
+ *
+ * Arithmetic: fp64 unless a step fixes another precision:
+ *   - router weights: softmax and renormalisation in double, one rounding to fp32;
+ *   - combine: fp32 fused multiply-add accumulation in top-k slot order (the
+ *     required "fp32 combine accumulation"), one rounding to the output type;
+ *   - expert FFN: double accumulation, bf16 rounding of the SwiGLU intermediate
+ *     and of the output (both are bf16 tensors in the method);
+ *   - combine backward: double, one rounding per stored value.
+ * Compiled with -O2 -ffp-contract=off so no fused operation appears that the
+ * source does not write.
+ *
+ * Sources (the web pages this path is built from):
+ *   [MEG]  "Megatron MoE 实现" (Megatron MoE implementation), MoELayer.forward and
+ *          its four stages: router -> (probs, routing_map), dispatch_preprocess,
+ *          dispatch_postprocess -> (dispatched_input, tokens_per_expert,
+ *          permuted_probs), experts, combine_postprocess.
+ *   [MORI] ROCm/Megatron-LM pull request "Add MORI as a Token Dispatcher", commit
+ *          log: -1 sentinels for non-local experts, multihot routing map,
+ *          sync-free per-expert counts, fixed-size buffers with masked tails.
+ *   [DS]   DeepSpeed deepspeed/moe/ep_tp_dispatch.py: RoutedAssignmentPayload
+ *          (capacity_slots, drop_mask, pad_mask), assignment_ordinals_by_expert
+ *          (stable ordinals within expert segments), restore_combined (weighted
+ *          rows added one top-k slot at a time into a zeroed output).
+ *   [HT]   mscclpp commit "high-throughput MoE dispatch/combine", Validation
+ *          (e256 / top-8 / hidden 7168 / 4096 tokens, exact dispatch/combine).
+ * The router arithmetic (softmax, top-k with lowest-index tie-break,
+ * renormalisation), the capacity factor and the SwiGLU expert are fixed by the
+ * workload definitions, not by the pages; each reading is stated where used.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define DT_F32 0
+#define DT_BF16 1
+
+/* ------------------------------------------------------------------ formats */
+
+static float f32_from_bits(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+static uint32_t bits_from_f32(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+
+/* bf16 -> double: a bf16 is the top half of an fp32, so the widening is exact. */
+static double bf16_value(uint16_t h) { return (double)f32_from_bits((uint32_t)h << 16); }
+
+/* double -> bf16, round to nearest, ties to even, in one rounding.  bf16 keeps
+ * 8 significant bits; below 2^-126 the spacing is fixed at 2^-133. */
+static uint16_t bf16_round(double x) {
+  if (isnan(x)) return 0x7FC0;
+  uint16_t sign = signbit(x) ? 0x8000 : 0;
+  double a = fabs(x);
+  if (a == 0.0) return sign;
+  if (isinf(a)) return sign | 0x7F80;
+  int e;
+  frexp(a, &e);                       /* 2^(e-1) <= a < 2^e */
+  int q = e - 8;                      /* exponent of the last kept bit */
+  if (q < -133) q = -133;
+  double r = ldexp(nearbyint(ldexp(a, -q)), q);   /* nearbyint: ties to even */
+  if (r >= 0x1p128) return sign | 0x7F80;
+  return sign | (uint16_t)(bits_from_f32((float)r) >> 16);   /* (float)r is exact */
+}
+
+/* Read element i of an activation tensor of type dt as a double (exact). */
+static double act_load(const void *p, int dt, int64_t i) {
+  if (dt == DT_F32) return (double)((const float *)p)[i];
+  return bf16_value(((const uint16_t *)p)[i]);
+}
+
+/* Store a double into an activation tensor of type dt with one rounding. */
+static void act_store(void *p, int dt, int64_t i, double v) {
+  if (dt == DT_F32) ((float *)p)[i] = (float)v;
+  else ((uint16_t *)p)[i] = bf16_round(v);
+}
+
+/* ------------------------------------------------------------------- route */
+
+/* Selection order on experts of one token: expert a comes before expert b when
+ * its logit is larger, or the logits are equal and a < b (lowest-index
+ * tie-break).  -0.0 and +0.0 compare equal (C's == does that); a NaN logit
+ * comes after every number. */
+static int selected_before(float va, int a, float vb, int b) {
+  int na = isnan(va), nb = isnan(vb);
+  if (na || nb) {
+    if (na && nb) return a < b;
+    return nb;
+  }
+  if (va > vb) return 1;
+  if (va < vb) return 0;
+  return a < b;
+}
+
+/* Router [MEG MoELayer.forward, stage 1: probs, routing_map = router(hidden)].
+ * Per token: the k experts first in selection order, stored largest first;
+ * probabilities p = softmax over all E logits (double); the k chosen are
+ * renormalised, w_j = p_j / sum_j' p_j', and rounded once to fp32; the routing
+ * map is the multihot [N, E] row ([MORI] multihot conversion); tokens_per_expert
+ * is the column sum of the map. */
+int oracle_route(int64_t n, int e, int k, const float *logits, int32_t *topk_idx, float *topk_w,
+                 uint8_t *routing_map, int32_t *tokens_per_expert) {
+  if (n < 0 || e < 1 || k < 1 || k > e) return -1;
+  char *taken = (char *)malloc((size_t)e);
+  double *p = (double *)malloc(sizeof(double) * (size_t)e);
+  if (!taken || !p) { free(taken); free(p); return -2; }
+  if (tokens_per_expert) memset(tokens_per_expert, 0, sizeof(int32_t) * (size_t)e);
+  for (int64_t t = 0; t < n; ++t) {
+    const float *l = logits + t * e;
+    memset(taken, 0, (size_t)e);
+    for (int j = 0; j < k; ++j) {
+      int best = -1;
+      for (int x = 0; x < e; ++x) {
+        if (taken[x]) continue;
+        if (best < 0 || selected_before(l[x], x, l[best], best)) best = x;
+      }
+      taken[best] = 1;
+      topk_idx[t * k + j] = best;
+    }
+    double m = -INFINITY;
+    for (int x = 0; x < e; ++x) if ((double)l[x] > m) m = (double)l[x];
+    double z = 0.0;
+    for (int x = 0; x < e; ++x) { p[x] = exp((double)l[x] - m); z += p[x]; }
+    for (int x = 0; x < e; ++x) p[x] /= z;
+    double s = 0.0;
+    for (int j = 0; j < k; ++j) s += p[topk_idx[t * k + j]];
+    for (int j = 0; j < k; ++j) topk_w[t * k + j] = (float)(p[topk_idx[t * k + j]] / s);
+    if (routing_map) for (int x = 0; x < e; ++x) routing_map[t * e + x] = (uint8_t)taken[x];
+    if (tokens_per_expert) for (int x = 0; x < e; ++x) tokens_per_expert[x] += taken[x];
+  }
+  free(taken);
+  free(p);
+  return 0;
+}
+
+/* ------------------------------------------------------------------ layout */
+
+/* Rows of the permuted buffer: E*C with a capacity, else max_rows if given,
+ * else one row per assignment. */
+int64_t oracle_layout_rows(int64_t n, int k, int e, int capacity, int64_t max_rows) {
+  if (capacity > 0) return (int64_t)e * capacity;
+  return max_rows > 0 ? max_rows : n * k;
+}
+
+/* Dispatch layout [MEG dispatch_preprocess / dispatch_postprocess; DS
+ * RoutedAssignmentPayload and assignment_ordinals_by_expert; MORI sentinels].
+ * Assignment a = t*k + j goes to expert topk_idx[a]; -1 is a non-local slot and is
+ * skipped; ids < -1 or >= E are invalid, skipped and counted.
+ *  - ordinal[a]: number of earlier assignments (smaller a) to the same expert
+ *    (a stable counting sort by expert; equals the segment-start/cummax ordinal
+ *    of the stably expert-sorted list).
+ *  - capacity C > 0: segment of expert e starts at e*C, the first C assignments
+ *    (by ordinal) are kept, the rest dropped; slots kept_e..C-1 are pad rows.
+ *    C <= 0: segments are the exclusive scan of the counts, clipped to the row
+ *    budget; assignments past the budget are dropped.
+ *  - assign_row[a] = offset[e] + ordinal[a] when kept, else -1.
+ *  - row_src[r] = the assignment placed in row r, else -1; pad_mask[r] = 1 for
+ *    every row that holds no assignment (capacity pad or unused tail).
+ *  - counters = {kept, dropped, capacity pad rows, invalid ids}. */
+int oracle_layout(int64_t n, int k, int e, int capacity, int64_t max_rows, const int32_t *topk_idx,
+                  int32_t *tokens_per_expert, int32_t *expert_offsets, int32_t *ordinal,
+                  int32_t *assign_row, int32_t *row_src, uint8_t *drop_mask, uint8_t *pad_mask,
+                  int32_t *counters) {
+  if (n < 0 || k < 1 || e < 1) return -1;
+  int64_t a_total = n * k;
+  int64_t rows = oracle_layout_rows(n, k, e, capacity, max_rows);
+  int64_t *count = (int64_t *)calloc((size_t)e, sizeof(int64_t));
+  int64_t *seen = (int64_t *)calloc((size_t)e, sizeof(int64_t));
+  int64_t *kept = (int64_t *)calloc((size_t)e, sizeof(int64_t));
+  if (!count || !seen || !kept) { free(count); free(seen); free(kept); return -2; }
+  int64_t invalid = 0;
+  for (int64_t a = 0; a < a_total; ++a) {
+    int32_t x = topk_idx[a];
+    if (x == -1) continue;
+    if (x < -1 || x >= e) { ++invalid; continue; }
+    ++count[x];
+  }
+  if (capacity > 0) {
+    for (int x = 0; x < e; ++x) {
+      expert_offsets[x] = (int32_t)((int64_t)x * capacity);
+      kept[x] = count[x] < capacity ? count[x] : capacity;
+    }
+    expert_offsets[e] = (int32_t)rows;
+  } else {
+    int64_t off = 0;
+    for (int x = 0; x < e; ++x) {
+      expert_offsets[x] = (int32_t)(off < rows ? off : rows);
+      off += count[x];
+    }
+    expert_offsets[e] = (int32_t)(off < rows ? off : rows);
+    for (int x = 0; x < e; ++x) kept[x] = expert_offsets[x + 1] - expert_offsets[x];
+  }
+  for (int64_t r = 0; r < rows; ++r) { row_src[r] = -1; pad_mask[r] = 1; }
+  int64_t dropped = 0, kept_total = 0;
+  for (int64_t a = 0; a < a_total; ++a) {
+    int32_t x = topk_idx[a];
+    drop_mask[a] = 0;
+    if (x < 0 || x >= e) { ordinal[a] = -1; assign_row[a] = -1; continue; }
+    int64_t o = seen[x]++;
+    ordinal[a] = (int32_t)o;
+    if (o < kept[x]) {
+      int64_t r = expert_offsets[x] + o;
+      assign_row[a] = (int32_t)r;
+      row_src[r] = (int32_t)a;
+      pad_mask[r] = 0;
+      ++kept_total;
+    } else {
+      assign_row[a] = -1;
+      drop_mask[a] = 1;
+      ++dropped;
+    }
+  }
+  for (int x = 0; x < e; ++x) tokens_per_expert[x] = (int32_t)kept[x];
+  counters[0] = (int32_t)kept_total;
+  counters[1] = (int32_t)dropped;
+  counters[2] = capacity > 0 ? (int32_t)(rows - kept_total) : 0;
+  counters[3] = (int32_t)invalid;
+  free(count);
+  free(seen);
+  free(kept);
+  return 0;
+}
+
+/* ----------------------------------------------------------------- scatter */
+
+/* Row scatter [MEG dispatch_preprocess permutes hidden states and probs; HT
+ * Validation: the dispatched copy is exact].  Each kept assignment's token row
+ * is copied bit for bit into its row; its weight goes to w_perm.  With a
+ * capacity, pad rows are all-zero bits with weight 0 ([MORI] masked tails are
+ * filled with 0).  Rows of an unused dropless tail get weight 0 and keep their
+ * data. */
+void oracle_scatter(int64_t n, int k, int64_t row_bytes, const uint8_t *x, const int32_t *assign_row,
+                    const float *topk_w, int64_t rows, const int32_t *row_src, int capacity,
+                    uint8_t *x_perm, float *w_perm) {
+  for (int64_t a = 0; a < n * k; ++a) {
+    int32_t r = assign_row[a];
+    if (r < 0) continue;
+    memcpy(x_perm + (int64_t)r * row_bytes, x + (a / k) * row_bytes, (size_t)row_bytes);
+    if (w_perm) w_perm[r] = topk_w[a];
+  }
+  for (int64_t r = 0; r < rows; ++r) {
+    if (row_src[r] >= 0) continue;
+    if (capacity > 0) memset(x_perm + r * row_bytes, 0, (size_t)row_bytes);
+    if (w_perm) w_perm[r] = 0.0f;
+  }
+}
+
+/* ------------------------------------------------------------- expert FFN */
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* SwiGLU expert [MEG experts(dispatched_input, tokens_per_expert, ...)], no bias.
+ * For a row r in expert e's segment [offset_e, offset_e + kept_e):
+ *   g_i = sum_h x[r,h] W_gu[e, i, h],  u_i = sum_h x[r,h] W_gu[e, I+i, h]
+ *   a_i = bf16(silu(g_i) * u_i),       y[r,c] = bf16(sum_i a_i W_d[e, c, i])
+ * with every sum in double (bf16 x bf16 products are exact in double).
+ * Computes only the listed rows (y_rows[j] receives row rows[j]); a row outside
+ * every segment is left untouched and reported by a -1 in expert_of. */
+void oracle_expert_ffn_rows(int64_t nrows, const int64_t *rows, int e, int64_t h, int64_t inter,
+                            const uint16_t *x_perm, const int32_t *expert_offsets,
+                            const int32_t *tokens_per_expert, const uint16_t *w_gate_up,
+                            const uint16_t *w_down, uint16_t *y_rows, int32_t *expert_of) {
+  double *act = (double *)malloc(sizeof(double) * (size_t)inter);
+  for (int64_t j = 0; j < nrows; ++j) {
+    int64_t r = rows[j];
+    int ex = -1;
+    for (int x = 0; x < e; ++x)
+      if (r >= expert_offsets[x] && r < (int64_t)expert_offsets[x] + tokens_per_expert[x]) { ex = x; break; }
+    if (expert_of) expert_of[j] = ex;
+    if (ex < 0) continue;
+    const uint16_t *xr = x_perm + r * h;
+    const uint16_t *wg = w_gate_up + (int64_t)ex * 2 * inter * h;
+    const uint16_t *wd = w_down + (int64_t)ex * h * inter;
+    for (int64_t i = 0; i < inter; ++i) {
+      double g = 0.0, u = 0.0;
+      for (int64_t c = 0; c < h; ++c) {
+        double xv = bf16_value(xr[c]);
+        g += xv * bf16_value(wg[i * h + c]);
+        u += xv * bf16_value(wg[(inter + i) * h + c]);
+      }
+      act[i] = bf16_value(bf16_round(silu(g) * u));
+    }
+    for (int64_t c = 0; c < h; ++c) {
+      double s = 0.0;
+      for (int64_t i = 0; i < inter; ++i) s += act[i] * bf16_value(wd[c * inter + i]);
+      y_rows[j * h + c] = bf16_round(s);
+    }
+  }
+  free(act);
+}
+
+/* ----------------------------------------------------------------- combine */
+
+/* Probability-weighted combine [DS restore_combined: weighted rows are added by
+ * token index into a zeroed output one top-k slot at a time; MEG
+ * combine_postprocess].  out[t,h] = sum over kept slots j = 0..k-1, in that
+ * order, of topk_w[t,j] * y[assign_row[t,j], h], accumulated in fp32 with a
+ * fused multiply-add per term (C99 fmaf is correctly rounded), then rounded once
+ * to the output type.  A token with no kept slot gets a zero row. */
+void oracle_combine(int64_t n, int k, int64_t h, int dt, const void *y, const float *topk_w,
+                    const int32_t *assign_row, void *out) {
+  for (int64_t t = 0; t < n; ++t) {
+    for (int64_t c = 0; c < h; ++c) {
+      float acc = 0.0f;
+      for (int j = 0; j < k; ++j) {
+        int32_t r = assign_row[t * k + j];
+        if (r < 0) continue;
+        acc = fmaf(topk_w[t * k + j], (float)act_load(y, dt, (int64_t)r * h + c), acc);
+      }
+      act_store(out, dt, t * h + c, (double)acc);
+    }
+  }
+}
+
+/* Combine backward (the vector-Jacobian product of the combine above; the MORI
+ * commit log's combine backward takes the receiver-side weights and indices).
+ * For each kept assignment a = (t, j) in row r:
+ *   grad_y[r, :] = w[t,j] * g[t, :]        (one rounding to the activation type)
+ *   grad_w[t, j] = sum_h g[t,h] * y[r,h]   (double, one rounding to fp32)
+ * grad_w is 0 for dropped, sentinel and invalid slots; capacity pad rows of
+ * grad_y are 0; rows of an unused dropless tail are not written. */
+void oracle_combine_bwd(int64_t n, int k, int64_t h, int dt, const void *grad_out, const void *y,
+                        const float *topk_w, const int32_t *assign_row, int64_t rows,
+                        const int32_t *row_src, int capacity, void *grad_y, float *grad_w) {
+  for (int64_t t = 0; t < n; ++t) {
+    for (int j = 0; j < k; ++j) {
+      int64_t a = t * k + j;
+      int32_t r = assign_row[a];
+      if (r < 0) { grad_w[a] = 0.0f; continue; }
+      double dot = 0.0;
+      for (int64_t c = 0; c < h; ++c) {
+        double g = act_load(grad_out, dt, t * h + c);
+        dot += g * act_load(y, dt, (int64_t)r * h + c);
+        act_store(grad_y, dt, (int64_t)r * h + c, (double)topk_w[a] * g);
+      }
+      grad_w[a] = (float)dot;
+    }
+  }
+  if (capacity > 0)
+    for (int64_t r = 0; r < rows; ++r)
+      if (row_src[r] < 0)
+        for (int64_t c = 0; c < h; ++c) act_store(grad_y, dt, r * h + c, 0.0);
+}
+
+/* Exposed for the tests that pin the number formats. */
+uint16_t oracle_bf16_round(double x) { return bf16_round(x); }

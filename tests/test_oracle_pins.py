@@ -1,0 +1,552 @@
+"""Pins for the CPU oracle: each oracle function checked against something other than
+itself -- brute force with a different algorithm on tiny inputs, closed forms,
+library routines and invariants of the method.  CPU only.
+
+Sources of the checked facts:
+  * Router top-k with lowest-index tie-break, softmax then renormalisation over the
+    chosen k, capacity factor, SwiGLU expert: the workload definitions (not the pages).
+  * Stable per-expert ordinals: DeepSpeed ep_tp_dispatch.py,
+    assignment_ordinals_by_expert (segment starts where the expert id changes, a
+    running maximum of the start positions, ordinal = position - segment start).
+  * Drop/pad masks and "active = not dropped and not padded": DeepSpeed
+    ep_tp_dispatch.py, RoutedAssignmentPayload / partition_assignments.
+  * Slot-ordered weighted combine into a zeroed output: DeepSpeed
+    ep_tp_dispatch.py, restore_combined.
+  * Exact dispatched copies (max |got - expected| = 0): mscclpp HT commit, Validation.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import pytest
+
+import moe_inputs as mi
+import oracle
+
+RNG = np.random.default_rng(12345)
+
+
+# ----------------------------------------------------------------- brute force
+
+def bf_topk(row: np.ndarray, k: int):
+    """Python sort over (NaN last, -value with -0 == +0, index)."""
+    def key(e):
+        v = float(row[e])
+        if math.isnan(v):
+            return (1, 0.0, e)
+        return (0, -(v + 0.0), e)
+    return sorted(range(row.size), key=key)[:k]
+
+
+def bf_weights(row: np.ndarray, sel):
+    """Softmax restricted to the chosen experts (equal to softmax-then-renormalise),
+    with math.fsum, in double."""
+    v = [float(row[e]) for e in sel]
+    m = max(v)
+    ex = [math.exp(x - m) for x in v]
+    s = math.fsum(ex)
+    return [x / s for x in ex]
+
+
+def bf_layout(idx: np.ndarray, e: int, capacity: int, max_rows: int):
+    """Permutation by a comparison sort on (expert, assignment); ordinals by the
+    segment-start / running-max construction over the expert-sorted list."""
+    flat = idx.reshape(-1)
+    a_total = flat.size
+    valid = [a for a in range(a_total) if 0 <= flat[a] < e]
+    order = sorted(valid, key=lambda a: (int(flat[a]), a))
+    ids = np.array([flat[a] for a in order], dtype=np.int64)
+    pos = np.arange(ids.size)
+    if ids.size:
+        seg_start = np.zeros(ids.size, bool)
+        seg_start[0] = True
+        seg_start[1:] = ids[1:] != ids[:-1]
+        starts = np.maximum.accumulate(np.where(seg_start, pos, 0))
+        ords_sorted = pos - starts
+    else:
+        ords_sorted = pos
+    ordinal = np.full(a_total, -1, np.int64)
+    for p, a in enumerate(order):
+        ordinal[a] = ords_sorted[p]
+    counts = np.bincount(ids, minlength=e) if ids.size else np.zeros(e, np.int64)
+    if capacity > 0:
+        rows = e * capacity
+        offsets = np.arange(e + 1) * capacity
+        kept = np.minimum(counts, capacity)
+    else:
+        rows = max_rows if max_rows > 0 else a_total
+        offsets = np.minimum(np.concatenate([[0], np.cumsum(counts)]), rows)
+        kept = np.diff(offsets)
+    assign_row = np.full(a_total, -1, np.int64)
+    drop = np.zeros(a_total, np.uint8)
+    for a in valid:
+        ex = flat[a]
+        if ordinal[a] < kept[ex]:
+            assign_row[a] = offsets[ex] + ordinal[a]
+        else:
+            drop[a] = 1
+    row_src = np.full(rows, -1, np.int64)
+    for a in valid:
+        if assign_row[a] >= 0:
+            row_src[assign_row[a]] = a
+    invalid = int(sum(1 for v in flat if v < -1 or v >= e))
+    return dict(ordinal=ordinal, assign_row=assign_row, drop_mask=drop, row_src=row_src,
+                pad_mask=(row_src < 0).astype(np.uint8), tokens_per_expert=kept,
+                expert_offsets=offsets, counters=np.array([kept.sum(), drop.sum(),
+                                                           (rows - kept.sum()) if capacity > 0 else 0,
+                                                           invalid]))
+
+
+def dense_combine_matrix(n, k, rows, topk_w, assign_row):
+    m = np.zeros((n, rows), np.float64)
+    for t in range(n):
+        for j in range(k):
+            r = assign_row[t * k + j]
+            if r >= 0:
+                m[t, r] += float(topk_w[t, j])
+    return m
+
+
+def f32_ulp(x):
+    return np.spacing(np.abs(np.float32(x)).astype(np.float32))
+
+
+def bf16_vals(b):
+    return mi.bf16_bits_to_f32(b).astype(np.float64)
+
+
+def bf16_from_double_ref(x: np.ndarray) -> np.ndarray:
+    """Independent double -> bf16 (ties to even) for normal-range values: pick the
+    nearer of the two bf16 neighbours obtained by truncation, breaking ties on the
+    even mantissa."""
+    x = np.asarray(x, np.float64)
+    f = x.astype(np.float32)      # only used to get a bracket; corrected below
+    u = f.view(np.uint32)
+    lo = (u >> 16).astype(np.uint32)
+    cands = np.stack([lo - 1, lo, lo + 1]).astype(np.uint32) & 0xFFFF
+    vals = (cands.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    d = np.abs(vals - x[None])
+    best = np.argmin(d, axis=0)
+    dmin = d.min(axis=0)
+    tie = (d == dmin[None]).sum(axis=0) > 1
+    out = cands[best, np.arange(x.size)] if x.ndim == 1 else None
+    if x.ndim != 1:
+        raise ValueError
+    for i in np.nonzero(tie)[0]:
+        opts = cands[d[:, i] == dmin[i], i]
+        out[i] = [o for o in opts if o % 2 == 0][0]
+    return out.astype(np.uint16)
+
+
+# ------------------------------------------------------------------- formats
+
+def test_bf16_round_closed_forms():
+    assert oracle.bf16_round(1.0) == 0x3F80
+    assert oracle.bf16_round(-2.0) == 0xC000
+    assert oracle.bf16_round(1.0 + 2.0 ** -8) == 0x3F80           # tie -> even (down)
+    assert oracle.bf16_round(1.0 + 3 * 2.0 ** -8) == 0x3F82       # tie -> even (up)
+    assert oracle.bf16_round(1.0 + 2.0 ** -8 + 2.0 ** -40) == 0x3F81  # just above the tie
+    assert oracle.bf16_round(0.0) == 0x0000
+    assert oracle.bf16_round(-0.0) == 0x8000
+    assert oracle.bf16_round(float("inf")) == 0x7F80
+    assert oracle.bf16_round(2.0 ** -133) == 0x0001               # smallest subnormal
+    assert oracle.bf16_round(3.0e38) == 0x7F62                    # largest finite range
+    assert oracle.bf16_round(3.5e38) == 0x7F80                    # overflow -> inf
+
+
+def test_bf16_round_matches_independent_rounding():
+    x = RNG.standard_normal(4000) * np.exp(RNG.uniform(-20, 20, 4000))
+    got = np.array([oracle.bf16_round(v) for v in x], np.uint16)
+    np.testing.assert_array_equal(got, bf16_from_double_ref(x))
+    # fp32-representable inputs: the integer trick of the input generator agrees
+    f = RNG.standard_normal(4000).astype(np.float32)
+    got = np.array([oracle.bf16_round(float(v)) for v in f], np.uint16)
+    np.testing.assert_array_equal(got, mi.f32_to_bf16_bits(f))
+
+
+# --------------------------------------------------------------------- route
+
+def _check_route_against_brute_force(logits, k):
+    idx, w, rmap, tpe = oracle.route(logits, k)
+    n, e = logits.shape
+    for t in range(n):
+        sel = bf_topk(logits[t], k)
+        assert list(idx[t]) == sel, (t, logits[t], idx[t], sel)
+        if not np.isnan(logits[t]).any():
+            ref = bf_weights(logits[t], sel)
+            assert np.all(np.abs(w[t].astype(np.float64) - ref) <= f32_ulp(np.float32(ref)) * 1.0001), (w[t], ref)
+        mrow = np.zeros(e, np.uint8)
+        mrow[sel] = 1
+        np.testing.assert_array_equal(rmap[t], mrow)
+    np.testing.assert_array_equal(tpe, rmap.sum(axis=0))
+    return idx, w, rmap, tpe
+
+
+@pytest.mark.parametrize("trial", range(40))
+def test_route_brute_force_random(trial):
+    g = np.random.default_rng(trial)
+    e = int(g.integers(1, 17))
+    k = int(g.integers(1, e + 1))
+    n = int(g.integers(0, 40))
+    logits = g.standard_normal((n, e)).astype(np.float32)
+    _check_route_against_brute_force(logits, k)
+
+
+@pytest.mark.parametrize("trial", range(40))
+def test_route_brute_force_ties_signed_zero_nan(trial):
+    g = np.random.default_rng(1000 + trial)
+    e = int(g.integers(2, 17))
+    k = int(g.integers(1, e + 1))
+    n = 30
+    vals = np.array([-1.0, -0.0, 0.0, 1.0, np.nan], np.float32)
+    p = [0.25, 0.2, 0.2, 0.25, 0.1] if trial % 2 else [0.3, 0.2, 0.2, 0.3, 0.0]
+    logits = g.choice(vals, size=(n, e), p=p).astype(np.float32)
+    _check_route_against_brute_force(logits, k)
+
+
+def test_route_tiny_workload_brute_force():
+    w = mi.workload(1)
+    _check_route_against_brute_force(mi.router_logits(w), w.top_k)
+
+
+def test_route_closed_forms():
+    # all-equal logits: lowest indices, weights exactly 1/k for k a power of two
+    for k in (1, 2, 4, 8):
+        idx, w, _, _ = oracle.route(np.full((3, 16), 0.7, np.float32), k)
+        assert (idx == np.arange(k)).all()
+        assert (w == np.float32(1.0 / k)).all()
+    # k = 1: weight exactly 1
+    logits = RNG.standard_normal((50, 9)).astype(np.float32)
+    idx, w, _, _ = oracle.route(logits, 1)
+    assert (w == 1.0).all() and (idx[:, 0] == logits.argmax(1)).all()
+    # k = E: weights are the softmax (closed form), in order of decreasing logit
+    idx, w, _, _ = oracle.route(logits, 9)
+    for t in range(50):
+        ex = np.exp(logits[t].astype(np.float64) - logits[t].max())
+        sm = ex / ex.sum()
+        np.testing.assert_allclose(w[t], sm[idx[t]], rtol=2 ** -23)
+        assert (np.diff(logits[t][idx[t]]) <= 0).all()
+    # one dominant logit: it takes slot 0 with weight ~1
+    l2 = np.zeros((4, 12), np.float32)
+    l2[:, 5] = 60.0
+    idx, w, _, _ = oracle.route(l2, 3)
+    assert (idx[:, 0] == 5).all() and (idx[:, 1:] == [0, 1]).all()
+    assert np.allclose(w[:, 0], 1.0) and (w[:, 1:] < 1e-25).all()
+
+
+def test_route_invariants_uniform_workload():
+    w = mi.workload(2)
+    logits = mi.router_logits(w)
+    idx, wt, rmap, tpe = oracle.route(logits, w.top_k)
+    assert tpe.sum() == w.n_tokens * w.top_k
+    np.testing.assert_array_equal(tpe, rmap.sum(0))
+    assert all(len(set(r)) == w.top_k for r in idx[:512])
+    s = wt.astype(np.float64).sum(1)
+    assert np.abs(s - 1).max() <= 4 * 2 ** -24 * w.top_k
+    # shift invariance: adding a constant keeps the choice, weights within 1e-6
+    idx2, wt2, _, _ = oracle.route((logits[:256] + np.float32(3.0)).astype(np.float32), w.top_k)
+    same = (idx2 == idx[:256]).all(1)
+    assert same.mean() > 0.99  # adding 3.0 can merge two nearby logits into a tie after rounding
+    assert np.abs(wt2[same] - wt[:256][same]).max() < 1e-6
+    # slot order: logits non-increasing along the slots
+    chosen = np.take_along_axis(logits, idx, 1)
+    assert (np.diff(chosen, axis=1) <= 0).all()
+
+
+# -------------------------------------------------------------------- layout
+
+def _check_layout(idx, e, capacity=0, max_rows=0):
+    got = oracle.layout(idx, e, capacity, max_rows)
+    ref = bf_layout(idx, e, capacity, max_rows)
+    for f in ("ordinal", "assign_row", "drop_mask", "row_src", "pad_mask", "tokens_per_expert",
+              "expert_offsets", "counters"):
+        np.testing.assert_array_equal(got[f], ref[f], err_msg=f)
+    return got
+
+
+@pytest.mark.parametrize("trial", range(60))
+def test_layout_brute_force_random(trial):
+    g = np.random.default_rng(2000 + trial)
+    e = int(g.integers(1, 17))
+    k = int(g.integers(1, 5))
+    n = int(g.integers(0, 65))
+    mode = trial % 4
+    idx = g.integers(-1, e, size=(n, k)).astype(np.int32)
+    if mode == 3 and idx.size:   # invalid ids as well
+        bad = g.random(idx.shape) < 0.1
+        idx[bad] = g.choice([-7, e, e + 3], size=bad.sum())
+    capacity = int(g.integers(1, 6)) if mode == 1 else 0
+    max_rows = int(g.integers(0, n * k + 1)) if mode == 2 else 0
+    _check_layout(idx, e, capacity, max_rows)
+
+
+def test_layout_all_to_one_expert_and_capacity_one():
+    idx = np.zeros((20, 1), np.int32)
+    got = _check_layout(idx, 4, capacity=1)
+    assert got["counters"].tolist() == [1, 19, 3, 0]
+    got = _check_layout(np.full((5, 3), 2, np.int32), 3)
+    assert got["tokens_per_expert"].tolist() == [0, 0, 15]
+    _check_layout(np.zeros((0, 4), np.int32), 5)
+    _check_layout(np.full((6, 2), -1, np.int32), 5)
+
+
+def _layout_invariants(idx, e, got, capacity):
+    flat = idx.reshape(-1)
+    valid = (flat >= 0) & (flat < e)
+    sentinels = int((flat == -1).sum())
+    drops = int(got["drop_mask"].sum())
+    assert got["counters"][0] == idx.size - drops - sentinels - got["counters"][3]
+    assert got["tokens_per_expert"].sum() == got["counters"][0]
+    for x in range(e):
+        o0, kx = got["expert_offsets"][x], got["tokens_per_expert"][x]
+        seg = got["row_src"][o0:o0 + kx]
+        assert (seg >= 0).all() and (np.diff(seg) > 0).all()          # stable: source order kept
+        assert (got["ordinal"][seg] == np.arange(kx)).all()            # ordinals 0..kept-1
+        if capacity:
+            assert (got["row_src"][o0 + kx:o0 + capacity] == -1).all()  # pads
+    kept = got["assign_row"] >= 0
+    assert (got["row_src"][got["assign_row"][kept]] == np.nonzero(kept)[0]).all()  # inverse maps
+    if capacity:
+        assert ((got["ordinal"] >= capacity) == (got["drop_mask"] == 1)).all()
+        assert got["counters"][2] == (e * capacity - got["counters"][0])
+    assert (got["ordinal"][~valid] == -1).all()
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 5])
+def test_layout_invariants_workloads(wid):
+    w = mi.workload(wid)
+    if w.has_router:
+        idx, _, _, _ = oracle.route(mi.router_logits(w), w.top_k)
+    else:
+        idx, _ = mi.received_routing(w)
+    got = oracle.layout(idx, w.n_experts, w.capacity, w.rows)
+    _layout_invariants(idx, w.n_experts, got, w.capacity)
+    if wid == 5:
+        assert got["counters"].tolist() == [32768, 0, 0, 0]
+        assert got["tokens_per_expert"].tolist() == mi.zipf_targets(32, 32768, 1.2, 16384).tolist()
+    if wid == 3:
+        assert got["counters"][1] > 10000 and got["counters"][2] > 10000  # skew drops and pads
+
+
+def test_layout_matches_brute_force_on_uniform_workload_sample():
+    w = mi.workload(2)
+    idx, _, _, _ = oracle.route(mi.router_logits(w)[:300], w.top_k)
+    _check_layout(idx, w.n_experts)
+    _check_layout(idx, w.n_experts, capacity=7)
+
+
+# ------------------------------------------------------------------- scatter
+
+@pytest.mark.parametrize("dt,capacity", [(mi.DT_F32, 0), (mi.DT_BF16, 0), (mi.DT_BF16, 3), (mi.DT_F32, 2)])
+def test_scatter_bitwise(dt, capacity):
+    g = np.random.default_rng(7)
+    n, k, e, h = 37, 3, 6, 24
+    idx = np.stack([g.permutation(e)[:k] for _ in range(n)]).astype(np.int32)
+    idx[g.random(idx.shape) < 0.15] = -1
+    wts = g.random((n, k)).astype(np.float32)
+    x = mi.normal_activations((n, h), dt, 99, 1)
+    lay = oracle.layout(idx, e, capacity)
+    xp, wp = oracle.scatter(x, k, lay, wts, capacity)
+    kept = np.nonzero(lay["assign_row"] >= 0)[0]
+    assert (xp[lay["assign_row"][kept]].view(np.uint8) == x[kept // k].view(np.uint8)).all()
+    assert (wp[lay["assign_row"][kept]] == wts.reshape(-1)[kept]).all()
+    pads = lay["row_src"] < 0
+    assert (wp[pads] == 0).all()
+    if capacity:
+        assert (xp[pads].view(np.uint8) == 0).all()
+
+
+# ------------------------------------------------------------------- combine
+
+@pytest.mark.parametrize("dt", [mi.DT_F32, mi.DT_BF16])
+@pytest.mark.parametrize("capacity", [0, 2])
+def test_combine_dense_matrix(dt, capacity):
+    g = np.random.default_rng(11 + capacity)
+    n, k, e, h = 29, 4, 7, 40
+    idx = np.stack([g.permutation(e)[:k] for _ in range(n)]).astype(np.int32)
+    idx[g.random(idx.shape) < 0.1] = -1
+    wts = g.random((n, k)).astype(np.float32)
+    lay = oracle.layout(idx, e, capacity)
+    y = mi.normal_activations((lay["rows"], h), dt, 5, 5)
+    out = oracle.combine(y, wts, lay, n, k)
+    yv = y.astype(np.float64) if dt == mi.DT_F32 else bf16_vals(y)
+    ref = dense_combine_matrix(n, k, lay["rows"], wts, lay["assign_row"]) @ yv
+    if dt == mi.DT_F32:
+        bound = k * 2.0 ** -24 * (np.abs(dense_combine_matrix(n, k, lay["rows"], wts, lay["assign_row"])) @ np.abs(yv)) + 1e-30
+        assert (np.abs(out.astype(np.float64) - ref) <= bound).all()
+    else:
+        got = bf16_vals(out)
+        # one bf16 rounding of an fp32 sum within k fp32 ulps of the exact value
+        assert (np.abs(got - ref) <= np.abs(ref) * (2.0 ** -8 + k * 2.0 ** -23) + 1e-30).all()
+    # a token with no kept slot gets a zero row
+    none = np.all(lay["assign_row"].reshape(n, k) < 0, axis=1)
+    if none.any():
+        assert (out[none].view(np.uint8) == 0).all()
+
+
+def test_combine_identity_expert_returns_input():
+    # combine(dispatch(x)) == x for an identity expert and renormalised weights:
+    # bitwise for bf16 (the fp32 sum lies within a few fp32 ulps of x, far inside
+    # half a bf16 ulp), within k fp32 ulps for fp32.
+    for wid in (1, 2):
+        w = mi.workload(wid, n_tokens=256 if wid == 2 else 64, hidden=256 if wid == 2 else 128)
+        logits = mi.router_logits(w)
+        idx, wts, _, _ = oracle.route(logits, w.top_k)
+        x = mi.activations(w)
+        lay = oracle.layout(idx, w.n_experts)
+        xp, _ = oracle.scatter(x, w.top_k, lay, wts)
+        out = oracle.combine(xp, wts, lay, w.n_tokens, w.top_k)
+        if w.dtype == mi.DT_BF16:
+            assert (out == x).all()
+        else:
+            assert np.abs(out - x).max() <= (w.top_k + 1) * 2.0 ** -23 * np.abs(x).max()
+
+
+def test_combine_exact_half_half():
+    x = mi.normal_activations((10, 16), mi.DT_BF16, 3, 3)
+    idx = np.array([[0, 1]] * 10, np.int32)
+    lay = oracle.layout(idx, 2)
+    xp, _ = oracle.scatter(x, 2, lay, np.full((10, 2), 0.5, np.float32))
+    out = oracle.combine(xp, np.full((10, 2), 0.5, np.float32), lay, 10, 2)
+    assert (out == x).all()
+
+
+def test_combine_capacity_reduces_to_kept_weights():
+    w = mi.workload(3, n_tokens=512, hidden=64)
+    idx, wts, _, _ = oracle.route(mi.router_logits(w), w.top_k)
+    lay = oracle.layout(idx, w.n_experts, w.capacity)
+    x = mi.normal_activations((w.n_tokens, w.hidden), mi.DT_F32, 3, 1)
+    xp, _ = oracle.scatter(x, w.top_k, lay, wts, w.capacity)
+    out = oracle.combine(xp, wts, lay, w.n_tokens, w.top_k)
+    kept_w = np.where(lay["assign_row"].reshape(w.n_tokens, w.top_k) >= 0, wts, 0).astype(np.float64).sum(1)
+    np.testing.assert_allclose(out, x * kept_w[:, None], rtol=1e-5, atol=1e-6)
+
+
+# ------------------------------------------------------------ combine backward
+
+@pytest.mark.parametrize("dt", [mi.DT_F32, mi.DT_BF16])
+def test_combine_bwd_adjoint_euler_and_finite_differences(dt):
+    g = np.random.default_rng(21)
+    n, k, e, h, cap = 23, 3, 5, 32, 4
+    idx = np.stack([g.permutation(e)[:k] for _ in range(n)]).astype(np.int32)
+    wts = g.random((n, k)).astype(np.float32)
+    lay = oracle.layout(idx, e, cap)
+    y = mi.normal_activations((lay["rows"], h), dt, 8, 8)
+    go = mi.normal_activations((n, h), dt, 9, 9)
+    gy, gw = oracle.combine_bwd(go, y, wts, lay, k, cap)
+    val = (lambda a: a.astype(np.float64)) if dt == mi.DT_F32 else bf16_vals
+    yv, gv, gyv = val(y), val(go), val(gy)
+    M = dense_combine_matrix(n, k, lay["rows"], wts, lay["assign_row"])
+    out64 = M @ yv
+    # adjoint: <combine(y), g> = <y, grad_y>   (combine is linear in y)
+    lhs = (out64 * gv).sum()
+    rhs = (yv * gyv).sum()
+    rel = 2.0 ** -23 if dt == mi.DT_F32 else 2.0 ** -8
+    assert abs(lhs - rhs) <= rel * (np.abs(yv) * np.abs(gyv)).sum() + 1e-12
+    # Euler: sum_tj w * grad_w = <out, g>   (combine is linear in w)
+    euler = (wts.astype(np.float64) * gw.astype(np.float64)).sum()
+    assert abs(euler - lhs) <= 1e-6 * (np.abs(out64) * np.abs(gv)).sum()
+    # central finite differences of L(w) = <combine(y, w), g> in fp64
+    for t in range(n):
+        for j in range(k):
+            eps = 1e-3
+            wp, wm = wts.astype(np.float64).copy(), wts.astype(np.float64).copy()
+            wp[t, j] += eps
+            wm[t, j] -= eps
+            fd = (((dense_combine_matrix(n, k, lay["rows"], wp, lay["assign_row"]) @ yv) * gv).sum()
+                  - ((dense_combine_matrix(n, k, lay["rows"], wm, lay["assign_row"]) @ yv) * gv).sum()) / (2 * eps)
+            assert abs(fd - gw[t, j]) <= 1e-6 * (1 + abs(fd)), (t, j, fd, gw[t, j])
+    # pads of grad_y are zero; dropped slots have zero grad_w
+    assert (gy[lay["row_src"] < 0].view(np.uint8) == 0).all()
+    assert (gw.reshape(-1)[lay["assign_row"] < 0] == 0).all()
+
+
+def test_combine_bwd_identity_expert():
+    w = mi.workload(2, n_tokens=64, hidden=96)
+    idx, wts, _, _ = oracle.route(mi.router_logits(w), w.top_k)
+    lay = oracle.layout(idx, w.n_experts)
+    x = mi.activations(w)
+    xp, _ = oracle.scatter(x, w.top_k, lay, wts)
+    go = mi.grad_output(w)
+    gy, gw = oracle.combine_bwd(go, xp, wts, lay, w.top_k)
+    ref = (bf16_vals(go) * bf16_vals(x)).sum(1)
+    np.testing.assert_allclose(gw, np.repeat(ref[:, None], w.top_k, 1), rtol=1e-6, atol=1e-6)
+
+
+# ---------------------------------------------------------------- expert FFN
+
+def ffn_numpy(xv, wg, wu, wd):
+    """fp64 numpy matmuls with bf16 rounding of the intermediate and output."""
+    gg = xv @ wg.T
+    uu = xv @ wu.T
+    act = bf16_vals(bf16_from_double_ref((gg / (1 + np.exp(-gg)) * uu).reshape(-1))).reshape(gg.shape)
+    return bf16_from_double_ref((act @ wd.T).reshape(-1)).reshape(xv.shape[0], wd.shape[0])
+
+
+def _small_ffn_case(e=3, n=40, k=2, h=48, inter=32, seed=0, same_weights=False):
+    w = mi.workload(4, n_tokens=n, hidden=h, n_experts=e, top_k=k, inter=inter)
+    idx, wts, _, _ = oracle.route(mi.router_logits(w, seed), k)
+    lay = oracle.layout(idx, e)
+    x = mi.normal_activations((n, h), mi.DT_BF16, 4, 1, seed)
+    xp, _ = oracle.scatter(x, k, lay, wts)
+    wgu, wd = mi.expert_weights(w, seed)
+    wgu = wgu.copy()
+    wd = wd.copy()
+    if same_weights:
+        wgu[:] = wgu[0]
+        wd[:] = wd[0]
+    return w, idx, wts, lay, x, xp, wgu, wd
+
+
+def test_ffn_matches_numpy_matmul_per_expert():
+    w, idx, wts, lay, x, xp, wgu, wd = _small_ffn_case()
+    y = oracle.expert_ffn(xp, lay, wgu, wd)
+    inter = w.inter
+    for e in range(w.n_experts):
+        o0, kx = lay["expert_offsets"][e], lay["tokens_per_expert"][e]
+        if kx == 0:
+            continue
+        ref = ffn_numpy(bf16_vals(xp[o0:o0 + kx]), bf16_vals(wgu[e, :inter]), bf16_vals(wgu[e, inter:]),
+                        bf16_vals(wd[e]))
+        got = y[o0:o0 + kx]
+        assert (got == ref).mean() > 0.97
+        assert np.abs(bf16_vals(got) - bf16_vals(ref)).max() <= 2e-2 * np.abs(bf16_vals(ref)).max()
+
+
+def test_ffn_single_expert_is_plain_gemm_pair():
+    w, idx, wts, lay, x, xp, wgu, wd = _small_ffn_case(e=1, k=1, n=30)
+    y = oracle.expert_ffn(xp, lay, wgu, wd)
+    ref = ffn_numpy(bf16_vals(x), bf16_vals(wgu[0, :w.inter]), bf16_vals(wgu[0, w.inter:]), bf16_vals(wd[0]))
+    assert (y == ref).mean() > 0.97
+
+
+def test_ffn_zero_gate_or_up_gives_zero():
+    w, idx, wts, lay, x, xp, wgu, wd = _small_ffn_case()
+    z = wgu.copy()
+    z[:, :w.inter] = 0
+    assert (oracle.expert_ffn(xp, lay, z, wd) == 0).all()
+    z = wgu.copy()
+    z[:, w.inter:] = 0
+    y = oracle.expert_ffn(xp, lay, z, wd)
+    assert (bf16_vals(y) == 0).all()
+
+
+def test_ffn_identical_experts_commute_with_permutation():
+    w, idx, wts, lay, x, xp, wgu, wd = _small_ffn_case(same_weights=True)
+    y = oracle.expert_ffn(xp, lay, wgu, wd)
+    dense = oracle.expert_ffn(x, dict(expert_offsets=np.array([0] + [w.n_tokens] * w.n_experts, np.int32),
+                                      tokens_per_expert=np.array([w.n_tokens] + [0] * (w.n_experts - 1), np.int32),
+                                      pad_mask=np.zeros(w.n_tokens, np.uint8), rows=w.n_tokens), wgu, wd)
+    kept = lay["assign_row"] >= 0
+    np.testing.assert_array_equal(y[lay["assign_row"][kept]], dense[np.nonzero(kept)[0] // w.top_k])
+
+
+def test_ffn_rows_outside_segments_untouched():
+    w, idx, wts, lay, x, xp, wgu, wd = _small_ffn_case()
+    rows = np.array([lay["rows"] - 1, 0], np.int64)
+    lay2 = dict(lay)
+    lay2["tokens_per_expert"] = lay["tokens_per_expert"].copy()
+    lay2["tokens_per_expert"][-1] = max(0, lay2["tokens_per_expert"][-1] - 1)
+    _, ex = oracle.expert_ffn_rows(rows, xp, lay2, wgu, wd)
+    assert ex[0] == -1 and ex[1] >= 0
