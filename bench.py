@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the single-GPU MoE path on MI355X.
+
+Headline: dispatch + combine at 4096 tokens, hidden 7168, 256 experts, top-8,
+bf16 activations, fp32 N(0,1) router logits, identity expert (the
+dispatch/combine shape of the mscclpp high-throughput MoE validation).  One
+step = moe_route -> moe_dispatch -> moe_combine on inputs already resident in
+HBM; value = algorithmic dispatch+combine bytes per step / step time (route
+time included).  Also reported: per-call times, combine backward on the same
+shape, and the grouped SwiGLU expert GEMM (TFLOP/s) at the Qwen3-235B-A22B-like
+layer (N=8192 H=4096 E=128 k=8 I=1536) and the DeepSeek-V3-like expert share
+(32 experts, H=7168, I=2048, 32768 Zipf(1.2) rows).
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+from pathlib import Path
+
+ROOT = Path(__file__).resolve().parent
+sys.path.insert(0, str(ROOT))
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk/CU)
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def events_ms(pairs):
+    return [s.elapsed_time(e) for s, e in pairs]
+
+
+def median(v):
+    v = sorted(v)
+    return v[len(v) // 2] if v else float("nan")
+
+
+def bench_dispatch_combine(moe, mi, torch, steps, warmup):
+    import numpy as np
+    w = mi.workload(2)
+    logits = torch.from_numpy(mi.router_logits(w)).cuda()
+    x_np = mi.activations(w)
+    x = torch.from_numpy(x_np.view(np.int16)).cuda().view(torch.bfloat16)
+    n, k, e, h = w.n_tokens, w.top_k, w.n_experts, w.hidden
+    dev = x.device
+    r = moe.moe_route(logits, k)
+    xp, wp, lay = moe.moe_dispatch(x, r.topk_idx, r.topk_w, e)
+    shape = moe.make_shape(n, h, e, k, act_dtype=moe.MOE_DT_BF16)
+    ws = torch.empty(moe.workspace_size(moe.MOE_OP_DISPATCH, shape) + 256, dtype=torch.uint8, device=dev)
+    out = torch.empty_like(x)
+    go = torch.randn(x.shape, generator=torch.Generator(device=dev).manual_seed(4), device=dev).to(torch.bfloat16)
+    gy = torch.empty_like(xp)
+    gw = torch.empty((n, k), dtype=torch.float32, device=dev)
+
+    def step(rec=None):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if rec is not None else None
+        if ev: ev[0].record()
+        moe.moe_route(logits, k, out=r)
+        if ev: ev[1].record()
+        moe.moe_dispatch(x, r.topk_idx, r.topk_w, e, layout=lay, x_perm=xp, w_perm_out=wp, workspace=ws)
+        if ev: ev[2].record()
+        moe.moe_combine(xp, r.topk_w, lay, out=out)
+        if ev: ev[3].record(); rec.append(ev)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    recs = []
+    t0.record()
+    for _ in range(steps):
+        step(recs)
+    t1.record()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    route_ms = median([r_[0].elapsed_time(r_[1]) for r_ in recs])
+    disp_ms = median([r_[1].elapsed_time(r_[2]) for r_ in recs])
+    comb_ms = median([r_[2].elapsed_time(r_[3]) for r_ in recs])
+    counters = lay.counters.cpu().tolist()
+    kept = counters[0]
+    row_b = h * 2
+    dispatch_bytes = n * row_b + kept * row_b
+    combine_bytes = kept * row_b + n * row_b
+    # combine backward on the same layout (y = x_perm: identity expert)
+    for _ in range(warmup):
+        moe.moe_combine_bwd(go, xp, r.topk_w, lay, grad_y=gy, grad_w=gw)
+    torch.cuda.synchronize()
+    b0 = torch.cuda.Event(enable_timing=True)
+    b1 = torch.cuda.Event(enable_timing=True)
+    b0.record()
+    for _ in range(steps):
+        moe.moe_combine_bwd(go, xp, r.topk_w, lay, grad_y=gy, grad_w=gw)
+    b1.record()
+    torch.cuda.synchronize()
+    bwd_ms = b0.elapsed_time(b1) / steps
+    bwd_bytes = n * row_b + kept * row_b * 2
+    return dict(total_ms=total_ms, route_ms=route_ms, dispatch_ms=disp_ms, combine_ms=comb_ms, kept=kept,
+                dispatch_bytes=dispatch_bytes, combine_bytes=combine_bytes, bwd_ms=bwd_ms, bwd_bytes=bwd_bytes,
+                n=n, k=k, e=e, h=h)
+
+
+def bench_expert_gemm(moe, mi, torch, wid, iters, warmup):
+    import numpy as np
+    w = mi.workload(wid)
+    dev = torch.device("cuda")
+    g = torch.Generator(device=dev).manual_seed(1000 + wid)
+    e, h, inter = w.n_experts, w.hidden, w.inter
+    wgu = (torch.randn((e, 2 * inter, h), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    wd = (torch.randn((e, h, inter), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    x = torch.randn((w.n_tokens, h), generator=g, device=dev).to(torch.bfloat16)
+    if w.has_router:
+        logits = torch.from_numpy(mi.router_logits(w)).cuda()
+        r = moe.moe_route(logits, w.top_k)
+        idx, wts = r.topk_idx, r.topk_w
+    else:
+        idx_np, w_np = mi.received_routing(w)
+        idx, wts = torch.from_numpy(idx_np).cuda(), torch.from_numpy(w_np).cuda()
+    xp, wp, lay = moe.moe_dispatch(x, idx, wts, e, max_rows=w.rows)
+    y = torch.empty_like(xp)
+    shape = lay.shape(h, moe.MOE_DT_BF16, inter)
+    ws = torch.empty(moe.workspace_size(moe.MOE_OP_EXPERT_FFN, shape) + 256, dtype=torch.uint8, device=dev)
+    for _ in range(warmup):
+        moe.moe_expert_ffn(xp, lay, wgu, wd, y=y, workspace=ws)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(iters):
+        moe.moe_expert_ffn(xp, lay, wgu, wd, y=y, workspace=ws)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / iters
+    rows = int(lay.counters[0].item())
+    flops = 2.0 * rows * h * 3 * inter
+    del wgu, wd, x, xp, y, ws
+    torch.cuda.empty_cache()
+    return dict(workload=w.name, rows=rows, ms=ms, tflops=flops / ms / 1e9, flops=flops)
+
+
+def cpu_baseline(mi):
+    import numpy as np
+    import oracle
+    w = mi.workload(2)
+    logits = mi.router_logits(w)
+    x = mi.activations(w)
+    t0 = time.perf_counter()
+    idx, wts, _, _ = oracle.route(logits, w.top_k)
+    t1 = time.perf_counter()
+    lay = oracle.layout(idx, w.n_experts)
+    xp, _ = oracle.scatter(x, w.top_k, lay, wts)
+    t2 = time.perf_counter()
+    oracle.combine(xp, wts, lay, w.n_tokens, w.top_k)
+    t3 = time.perf_counter()
+    kept = int(lay["counters"][0])
+    row_b = w.hidden * 2
+    byts = (w.n_tokens + kept) * row_b * 2
+    return dict(value=byts / (t3 - t0) / 1e9, unit="GB/s", cores=1, kind="oracle",
+                sample=f"one full step (route+layout+scatter+combine) of the uniform workload, single thread: "
+                       f"route {1e3*(t1-t0):.0f} ms, dispatch {1e3*(t2-t1):.0f} ms, combine {1e3*(t3-t2):.0f} ms")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--gemm-iters", type=int, default=10)
+    ap.add_argument("--skip-gemm", action="store_true")
+    ap.add_argument("--skip-cpu", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (the expert-parallel all-to-all is out "
+              "of scope); run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import moe_inputs as mi
+    import combine_router_softmax_amd as moe
+
+    torch.cuda.set_device(0)
+    log("dispatch+combine: uniform workload N=4096 H=7168 E=256 k=8")
+    dc = bench_dispatch_combine(moe, mi, torch, args.steps, args.warmup)
+    gemm = []
+    if not args.skip_gemm:
+        for wid in (4, 5):
+            log(f"expert GEMM: workload {mi.workload(wid).name}")
+            gemm.append(bench_expert_gemm(moe, mi, torch, wid, args.gemm_iters, 2))
+    cpu = None
+    if not args.skip_cpu:
+        log("cpu baseline (oracle)")
+        cpu = cpu_baseline(mi)
+
+    step_ms = dc["total_ms"] / args.steps
+    byts = dc["dispatch_bytes"] + dc["combine_bytes"]
+    comb_gbs = dc["combine_bytes"] / (dc["combine_ms"] * 1e-3) / 1e9
+    line = {
+        "metric": "dispatch+combine µs & GB/s (4096 tok, h7168, E256, top8); expert GEMM TFLOPS",
+        "value": round(byts / (step_ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(step_ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "uniform: N=4096 tokens, hidden=7168, E=256 experts, top-8, bf16 activations, "
+                               "fp32 N(0,1) logits, identity expert, dropless",
+                   "step": "moe_route -> moe_dispatch -> moe_combine", "global_batch": 4096,
+                   "parallelism": "single GPU"},
+        "route_us": round(dc["route_ms"] * 1e3, 2),
+        "dispatch_us": round(dc["dispatch_ms"] * 1e3, 2),
+        "combine_us": round(dc["combine_ms"] * 1e3, 2),
+        "dispatch_combine_us": round((dc["dispatch_ms"] + dc["combine_ms"]) * 1e3, 2),
+        "dispatch_combine_gbs": round(byts / ((dc["dispatch_ms"] + dc["combine_ms"]) * 1e-3) / 1e9, 2),
+        "combine_bwd_us": round(dc["bwd_ms"] * 1e3, 2),
+        "combine_bwd_gbs": round(dc["bwd_bytes"] / (dc["bwd_ms"] * 1e-3) / 1e9, 2),
+        "roofline": {"kernel": "combine_kernel<bf16,8>", "bound": "hbm", "achieved": round(comb_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(comb_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": None},
+        "expert_gemm": [{"workload": g["workload"], "rows": g["rows"], "us": round(g["ms"] * 1e3, 1),
+                         "tflops": round(g["tflops"], 1), "frac_bf16_peak": round(g["tflops"] / BF16_PEAK_TFLOPS, 4)}
+                        for g in gemm],
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

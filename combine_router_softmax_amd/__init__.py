@@ -1,0 +1,285 @@
+"""MI355X (gfx950) single-GPU Mixture-of-Experts path: route -> dispatch ->
+grouped SwiGLU expert FFN -> combine (+ combine backward).
+
+A thin ctypes binding over the C ABI of libmoe_mi355x.so (include/moe.h).  It
+only marshals arguments: tensors are passed as device pointers with
+torch.cuda.current_stream() as the HIP stream, outputs and workspaces are
+allocated with torch.  Every step of the path runs in the library's HIP
+kernels; there is no other implementation behind these functions, and
+importing this package fails if the library has not been built.
+"""
+from __future__ import annotations
+
+import ctypes as C
+from dataclasses import dataclass
+from pathlib import Path
+
+import torch
+
+_LIB_PATH = Path(__file__).resolve().parent / "libmoe_mi355x.so"
+
+MOE_DT_F32 = 0
+MOE_DT_BF16 = 1
+MOE_OP_ROUTE, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE, MOE_OP_COMBINE_BWD = range(5)
+
+# Every symbol include/moe.h declares.
+EXPORTS = ("moe_layout_rows", "moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
+           "moe_combine_bwd", "moe_status_string", "moe_version")
+
+
+class MoeShape(C.Structure):
+    _fields_ = [("n_tokens", C.c_int64), ("hidden", C.c_int64), ("n_experts", C.c_int32), ("top_k", C.c_int32),
+                ("capacity", C.c_int32), ("inter", C.c_int32), ("max_rows", C.c_int64), ("act_dtype", C.c_int32),
+                ("reserved", C.c_int32)]
+
+
+class MoeLayoutC(C.Structure):
+    _fields_ = [(name, C.c_void_p) for name in ("tokens_per_expert", "expert_offsets", "ordinal", "assign_row",
+                                                "row_src", "drop_mask", "pad_mask", "counters")]
+
+
+class MoeError(RuntimeError):
+    pass
+
+
+def _load():
+    if not _LIB_PATH.exists():
+        raise ImportError(f"{_LIB_PATH} is missing: build it first (python __graft_entry__.py build, or "
+                          f"python -m combine_router_softmax_amd._build)")
+    lib = C.CDLL(str(_LIB_PATH))
+    p, i32 = C.c_void_p, C.c_int
+    sp = C.POINTER(MoeShape)
+    lp = C.POINTER(MoeLayoutC)
+    lib.moe_layout_rows.argtypes = [sp]
+    lib.moe_layout_rows.restype = C.c_int64
+    lib.moe_workspace_size.argtypes = [i32, sp, C.POINTER(C.c_size_t)]
+    lib.moe_route.argtypes = [sp, p, p, p, p, p, p]
+    lib.moe_dispatch.argtypes = [sp, p, p, p, lp, p, p, p, C.c_size_t, p]
+    lib.moe_expert_ffn.argtypes = [sp, p, lp, p, p, p, p, C.c_size_t, p]
+    lib.moe_combine.argtypes = [sp, p, p, lp, p, p]
+    lib.moe_combine_bwd.argtypes = [sp, p, p, p, lp, p, p, p]
+    for f in ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_combine_bwd"):
+        getattr(lib, f).restype = i32
+    lib.moe_status_string.argtypes = [i32]
+    lib.moe_status_string.restype = C.c_char_p
+    lib.moe_version.argtypes = []
+    lib.moe_version.restype = C.c_char_p
+    return lib
+
+
+lib = _load()
+library_path = str(_LIB_PATH)
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise MoeError(f"{what}: {lib.moe_status_string(status).decode()} (status {status})")
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream(device) -> C.c_void_p:
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _act_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return MOE_DT_F32
+    if t.dtype == torch.bfloat16:
+        return MOE_DT_BF16
+    raise TypeError(f"activations must be float32 or bfloat16, got {t.dtype}")
+
+
+def _torch_dtype(dt: int):
+    return torch.float32 if dt == MOE_DT_F32 else torch.bfloat16
+
+
+def _contig(t: torch.Tensor, name: str):
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def make_shape(n_tokens, hidden, n_experts, top_k, capacity=0, inter=0, max_rows=0, act_dtype=MOE_DT_BF16):
+    return MoeShape(int(n_tokens), int(hidden), int(n_experts), int(top_k), int(capacity), int(inter), int(max_rows),
+                    int(act_dtype), 0)
+
+
+def workspace_size(op: int, shape: MoeShape) -> int:
+    out = C.c_size_t(0)
+    _check(lib.moe_workspace_size(op, C.byref(shape), C.byref(out)), "moe_workspace_size")
+    return int(out.value)
+
+
+def _workspace(op, shape, device):
+    n = workspace_size(op, shape)
+    if n == 0:
+        return None, 0
+    return torch.empty(n + 256, dtype=torch.uint8, device=device), n
+
+
+def _ws_ptr(ws):
+    if ws is None:
+        return None
+    base = ws.data_ptr()
+    return C.c_void_p((base + 255) & ~255)
+
+
+@dataclass
+class RouteOut:
+    topk_idx: torch.Tensor
+    topk_w: torch.Tensor
+    routing_map: torch.Tensor | None
+    tokens_per_expert: torch.Tensor | None
+
+
+@dataclass
+class Layout:
+    """The dispatch layout (the "handle" moe_dispatch writes and the later calls read)."""
+    n_tokens: int
+    top_k: int
+    n_experts: int
+    capacity: int
+    rows: int
+    tokens_per_expert: torch.Tensor
+    expert_offsets: torch.Tensor
+    ordinal: torch.Tensor
+    assign_row: torch.Tensor
+    row_src: torch.Tensor
+    drop_mask: torch.Tensor
+    pad_mask: torch.Tensor
+    counters: torch.Tensor
+
+    @staticmethod
+    def empty(n_tokens, top_k, n_experts, capacity, rows, device) -> "Layout":
+        i32 = dict(dtype=torch.int32, device=device)
+        u8 = dict(dtype=torch.uint8, device=device)
+        a = n_tokens * top_k
+        return Layout(n_tokens, top_k, n_experts, capacity, rows, torch.empty(n_experts, **i32),
+                      torch.empty(n_experts + 1, **i32), torch.empty(a, **i32), torch.empty(a, **i32),
+                      torch.empty(rows, **i32), torch.empty(a, **u8), torch.empty(rows, **u8), torch.empty(4, **i32))
+
+    def c(self) -> MoeLayoutC:
+        return MoeLayoutC(*[t.data_ptr() for t in (self.tokens_per_expert, self.expert_offsets, self.ordinal,
+                                                   self.assign_row, self.row_src, self.drop_mask, self.pad_mask,
+                                                   self.counters)])
+
+    def shape(self, hidden, act_dtype, inter=0) -> MoeShape:
+        return make_shape(self.n_tokens, hidden, self.n_experts, self.top_k, self.capacity, inter,
+                          0 if self.capacity > 0 else self.rows, act_dtype)
+
+
+def moe_route(logits: torch.Tensor, top_k: int, *, routing_map: bool = True, counts: bool = True,
+              out: RouteOut | None = None) -> RouteOut:
+    """Router softmax / top-k (include/moe.h moe_route).  logits fp32 [N, E] on the GPU."""
+    _contig(logits, "logits")
+    if logits.dtype != torch.float32 or logits.dim() != 2:
+        raise TypeError("logits must be a float32 [N, E] tensor")
+    n, e = logits.shape
+    dev = logits.device
+    if out is None:
+        out = RouteOut(torch.empty((n, top_k), dtype=torch.int32, device=dev),
+                       torch.empty((n, top_k), dtype=torch.float32, device=dev),
+                       torch.empty((n, e), dtype=torch.uint8, device=dev) if routing_map else None,
+                       torch.empty(e, dtype=torch.int32, device=dev) if counts else None)
+    shape = make_shape(n, 1, e, top_k, act_dtype=MOE_DT_F32)
+    _check(lib.moe_route(C.byref(shape), _ptr(logits), _ptr(out.topk_idx), _ptr(out.topk_w), _ptr(out.routing_map),
+                         _ptr(out.tokens_per_expert), _stream(dev)), "moe_route")
+    return out
+
+
+def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor | None, n_experts: int, *,
+                 capacity: int = 0, max_rows: int = 0, w_perm: bool = True, layout: Layout | None = None,
+                 x_perm: torch.Tensor | None = None, w_perm_out: torch.Tensor | None = None, workspace=None):
+    """Layout + row scatter (include/moe.h moe_dispatch) -> (x_perm, w_perm, layout)."""
+    _contig(x, "x")
+    _contig(topk_idx, "topk_idx")
+    n, h = x.shape
+    k = topk_idx.shape[1]
+    dev = x.device
+    dt = _act_dtype(x)
+    shape = make_shape(n, h, n_experts, k, capacity, 0, max_rows, dt)
+    rows = int(lib.moe_layout_rows(C.byref(shape)))
+    if rows < 0:
+        _check(-1, "moe_dispatch")
+    if layout is None:
+        layout = Layout.empty(n, k, n_experts, capacity, rows, dev)
+    if x_perm is None:
+        x_perm = torch.empty((rows, h), dtype=x.dtype, device=dev)
+    if w_perm and w_perm_out is None:
+        w_perm_out = torch.empty(rows, dtype=torch.float32, device=dev)
+    if workspace is None:
+        ws, nbytes = _workspace(MOE_OP_DISPATCH, shape, dev)
+    else:
+        ws, nbytes = workspace, workspace.numel() - 256
+    lc = layout.c()
+    _check(lib.moe_dispatch(C.byref(shape), _ptr(x), _ptr(topk_idx), _ptr(topk_w), C.byref(lc), _ptr(x_perm),
+                            _ptr(w_perm_out if w_perm else None), _ws_ptr(ws), nbytes, _stream(dev)), "moe_dispatch")
+    return x_perm, (w_perm_out if w_perm else None), layout
+
+
+def moe_expert_ffn(x_perm: torch.Tensor, layout: Layout, w_gate_up: torch.Tensor, w_down: torch.Tensor, *,
+                   y: torch.Tensor | None = None, workspace=None) -> torch.Tensor:
+    """Grouped SwiGLU FFN (include/moe.h moe_expert_ffn): bf16 x_perm [R, H], w_gate_up [E, 2I, H], w_down [E, H, I]."""
+    for t, name in ((x_perm, "x_perm"), (w_gate_up, "w_gate_up"), (w_down, "w_down")):
+        _contig(t, name)
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16")
+    rows, h = x_perm.shape
+    e, two_i, h2 = w_gate_up.shape
+    inter = two_i // 2
+    if h2 != h or tuple(w_down.shape) != (e, h, inter) or e != layout.n_experts or rows != layout.rows:
+        raise ValueError("inconsistent expert FFN shapes")
+    dev = x_perm.device
+    shape = layout.shape(h, MOE_DT_BF16, inter)
+    if y is None:
+        y = torch.empty_like(x_perm)
+    if workspace is None:
+        ws, nbytes = _workspace(MOE_OP_EXPERT_FFN, shape, dev)
+    else:
+        ws, nbytes = workspace, workspace.numel() - 256
+    lc = layout.c()
+    _check(lib.moe_expert_ffn(C.byref(shape), _ptr(x_perm), C.byref(lc), _ptr(w_gate_up), _ptr(w_down), _ptr(y),
+                              _ws_ptr(ws), nbytes, _stream(dev)), "moe_expert_ffn")
+    return y
+
+
+def moe_combine(y: torch.Tensor, topk_w: torch.Tensor, layout: Layout, *, out: torch.Tensor | None = None):
+    """Probability-weighted combine (include/moe.h moe_combine) -> out [N, H]."""
+    _contig(y, "y")
+    _contig(topk_w, "topk_w")
+    h = y.shape[1]
+    dt = _act_dtype(y)
+    if out is None:
+        out = torch.empty((layout.n_tokens, h), dtype=y.dtype, device=y.device)
+    shape = layout.shape(h, dt)
+    lc = layout.c()
+    _check(lib.moe_combine(C.byref(shape), _ptr(y), _ptr(topk_w), C.byref(lc), _ptr(out), _stream(y.device)),
+           "moe_combine")
+    return out
+
+
+def moe_combine_bwd(grad_out: torch.Tensor, y: torch.Tensor, topk_w: torch.Tensor, layout: Layout, *,
+                    grad_y: torch.Tensor | None = None, grad_w: torch.Tensor | None = None):
+    """Backward of moe_combine (include/moe.h moe_combine_bwd) -> (grad_y [R, H], grad_w fp32 [N, k])."""
+    _contig(grad_out, "grad_out")
+    _contig(y, "y")
+    h = y.shape[1]
+    dt = _act_dtype(y)
+    if grad_out.dtype != y.dtype:
+        raise TypeError("grad_out and y must have the same dtype")
+    if grad_y is None:
+        grad_y = torch.empty_like(y)
+    if grad_w is None:
+        grad_w = torch.empty((layout.n_tokens, layout.top_k), dtype=torch.float32, device=y.device)
+    shape = layout.shape(h, dt)
+    lc = layout.c()
+    _check(lib.moe_combine_bwd(C.byref(shape), _ptr(grad_out), _ptr(y), _ptr(topk_w), C.byref(lc), _ptr(grad_y),
+                               _ptr(grad_w), _stream(y.device)), "moe_combine_bwd")
+    return grad_y, grad_w
+
+
+__all__ = ["moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_combine_bwd", "Layout", "RouteOut",
+           "MoeError", "make_shape", "workspace_size", "lib", "library_path", "EXPORTS"]

@@ -1,0 +1,208 @@
+// C ABI of the MoE path (declared in include/moe.h): host-side validation,
+// workspace carving and kernel launches on the caller's stream.  No device
+// memory is read on the host and nothing is allocated.
+#include "../../include/moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include "moe_kernels.hpp"
+
+namespace {
+
+constexpr int kMaxExperts = 1024;
+constexpr int64_t kMaxIndex = 0x7FFFFFFFll;  // row and assignment indices are int32
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int64_t elem_bytes(int32_t dt) { return dt == MOE_DT_F32 ? 4 : 2; }
+
+// Checks every field common to all calls.
+moe_status check_shape(const moe_shape *s) {
+  if (!s) return MOE_ERR_INVALID_ARG;
+  if (s->n_tokens < 0 || s->hidden < 1 || s->n_experts < 1 || s->top_k < 1 || s->max_rows < 0) return MOE_ERR_INVALID_ARG;
+  if (s->act_dtype != MOE_DT_F32 && s->act_dtype != MOE_DT_BF16) return MOE_ERR_INVALID_ARG;
+  if (s->reserved != 0) return MOE_ERR_INVALID_ARG;
+  if (s->n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (s->n_tokens > kMaxIndex / s->top_k) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int64_t rows_of(const moe_shape *s) {
+  if (s->capacity > 0) return (int64_t)s->n_experts * s->capacity;
+  return s->max_rows > 0 ? s->max_rows : s->n_tokens * s->top_k;
+}
+
+// Row geometry and the rows of the permuted buffer.
+moe_status check_rows(const moe_shape *s, int64_t *row_bytes, int64_t *rows) {
+  const int64_t rb = s->hidden * elem_bytes(s->act_dtype);
+  if (rb % 16 != 0) return MOE_ERR_MISALIGNED;
+  if (s->capacity > 0) {
+    const int64_t ec = (int64_t)s->n_experts * s->capacity;
+    if (s->max_rows != 0 && s->max_rows != ec) return MOE_ERR_INVALID_ARG;
+    if (ec > kMaxIndex) return MOE_ERR_UNSUPPORTED;
+  }
+  const int64_t r = rows_of(s);
+  if (r > kMaxIndex) return MOE_ERR_UNSUPPORTED;
+  *row_bytes = rb;
+  *rows = r;
+  return MOE_OK;
+}
+
+moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+hipStream_t as_stream(void *s) { return reinterpret_cast<hipStream_t>(s); }
+
+// A pointer the call dereferences must be non-null and aligned when its tensor
+// is non-empty.
+bool need(const void *p, int64_t elems, bool (*aligned)(const void *)) {
+  return elems == 0 || p == nullptr || aligned(p);
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_layout_rows(const moe_shape *s) {
+  if (check_shape(s) != MOE_OK) return -1;
+  return rows_of(s);
+}
+
+moe_status moe_workspace_size(moe_op op, const moe_shape *s, size_t *bytes) {
+  if (!bytes) return MOE_ERR_INVALID_ARG;
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  switch (op) {
+    case MOE_OP_ROUTE:
+    case MOE_OP_COMBINE:
+    case MOE_OP_COMBINE_BWD:
+      *bytes = 0;
+      return MOE_OK;
+    case MOE_OP_DISPATCH:
+      *bytes = moe::layout_workspace_bytes(s->n_tokens * s->top_k, s->n_experts);
+      return MOE_OK;
+    case MOE_OP_EXPERT_FFN:
+      if (s->inter < 1) return MOE_ERR_INVALID_ARG;
+      *bytes = moe::ffn_workspace_bytes(rows_of(s), s->inter);
+      return MOE_OK;
+  }
+  return MOE_ERR_INVALID_ARG;
+}
+
+moe_status moe_route(const moe_shape *s, const float *logits, int32_t *topk_idx, float *topk_w,
+                     uint8_t *routing_map, int32_t *tokens_per_expert, void *stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->top_k > s->n_experts) return MOE_ERR_INVALID_ARG;
+  const int64_t n = s->n_tokens;
+  if (n > 0 && (!logits || !topk_idx || !topk_w)) return MOE_ERR_INVALID_ARG;
+  if (n > 0 && (!aligned4(logits) || !aligned4(topk_idx) || !aligned4(topk_w))) return MOE_ERR_MISALIGNED;
+  if (tokens_per_expert && !aligned4(tokens_per_expert)) return MOE_ERR_MISALIGNED;
+  return hip_status(moe::launch_route(logits, n, s->n_experts, s->top_k, topk_idx, topk_w, routing_map,
+                                      tokens_per_expert, as_stream(stream)));
+}
+
+moe_status moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_idx, const float *topk_w,
+                        const moe_layout *layout, void *x_perm, float *w_perm, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  int64_t row_bytes, rows;
+  if ((st = check_rows(s, &row_bytes, &rows)) != MOE_OK) return st;
+  if (!layout) return MOE_ERR_INVALID_ARG;
+  const int64_t n = s->n_tokens, a = n * s->top_k;
+  if (!layout->tokens_per_expert || !layout->expert_offsets || !layout->counters) return MOE_ERR_INVALID_ARG;
+  if ((a > 0 && (!topk_idx || !layout->ordinal || !layout->assign_row || !layout->drop_mask)) ||
+      (rows > 0 && (!layout->row_src || !layout->pad_mask || !x_perm)) || (n > 0 && !x) ||
+      (w_perm && a > 0 && !topk_w))
+    return MOE_ERR_INVALID_ARG;
+  if (!need(x, n, aligned16) || !need(x_perm, rows, aligned16)) return MOE_ERR_MISALIGNED;
+  const size_t need_ws = moe::layout_workspace_bytes(a, s->n_experts);
+  if (workspace_bytes < need_ws || (need_ws > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))))
+    return MOE_ERR_WORKSPACE;
+  hipStream_t hs = as_stream(stream);
+  hipError_t e = moe::launch_layout(topk_idx, topk_w, n, s->top_k, s->n_experts, s->capacity, rows,
+                                    layout->tokens_per_expert, layout->expert_offsets, layout->ordinal,
+                                    layout->assign_row, layout->row_src, layout->drop_mask, layout->pad_mask,
+                                    layout->counters, w_perm, workspace, hs);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  const int64_t pad_rows = s->capacity > 0 ? rows : 0;
+  return hip_status(moe::launch_scatter(x, n, s->top_k, row_bytes, layout->assign_row, x_perm, pad_rows,
+                                        layout->row_src, hs));
+}
+
+moe_status moe_expert_ffn(const moe_shape *s, const void *x_perm, const moe_layout *layout, const void *w_gate_up,
+                          const void *w_down, void *y, void *workspace, size_t workspace_bytes, void *stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  int64_t row_bytes, rows;
+  if ((st = check_rows(s, &row_bytes, &rows)) != MOE_OK) return st;
+  if (s->act_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
+  if (s->inter < 1) return MOE_ERR_INVALID_ARG;
+  if (s->inter % 64 != 0 || s->hidden % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!layout || !layout->tokens_per_expert || !layout->expert_offsets || !w_gate_up || !w_down)
+    return MOE_ERR_INVALID_ARG;
+  if (rows > 0 && (!x_perm || !y)) return MOE_ERR_INVALID_ARG;
+  if (!need(x_perm, rows, aligned16) || !need(y, rows, aligned16) || !aligned16(w_gate_up) || !aligned16(w_down))
+    return MOE_ERR_MISALIGNED;
+  const size_t need_ws = moe::ffn_workspace_bytes(rows, s->inter);
+  if (workspace_bytes < need_ws || (need_ws > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))))
+    return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_expert_ffn(static_cast<const uint16_t *>(x_perm), rows, s->hidden, s->inter,
+                                           s->n_experts, s->capacity, layout->tokens_per_expert,
+                                           layout->expert_offsets, static_cast<const uint16_t *>(w_gate_up),
+                                           static_cast<const uint16_t *>(w_down), static_cast<uint16_t *>(y),
+                                           workspace, as_stream(stream)));
+}
+
+moe_status moe_combine(const moe_shape *s, const void *y, const float *topk_w, const moe_layout *layout, void *out,
+                       void *stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  int64_t row_bytes, rows;
+  if ((st = check_rows(s, &row_bytes, &rows)) != MOE_OK) return st;
+  const int64_t n = s->n_tokens;
+  if (!layout) return MOE_ERR_INVALID_ARG;
+  if (n > 0 && (!topk_w || !layout->assign_row || !out || (rows > 0 && !y))) return MOE_ERR_INVALID_ARG;
+  if (!need(y, rows, aligned16) || !need(out, n, aligned16)) return MOE_ERR_MISALIGNED;
+  if (n > 0 && y == out) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_combine(s->act_dtype == MOE_DT_BF16, y, topk_w, layout->assign_row, n, s->top_k,
+                                        row_bytes, out, as_stream(stream)));
+}
+
+moe_status moe_combine_bwd(const moe_shape *s, const void *grad_out, const void *y, const float *topk_w,
+                           const moe_layout *layout, void *grad_y, float *grad_w, void *stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  int64_t row_bytes, rows;
+  if ((st = check_rows(s, &row_bytes, &rows)) != MOE_OK) return st;
+  const int64_t n = s->n_tokens;
+  if (!layout) return MOE_ERR_INVALID_ARG;
+  if (n > 0 && (!grad_out || !topk_w || !layout->assign_row || !grad_w || (rows > 0 && (!y || !grad_y))))
+    return MOE_ERR_INVALID_ARG;
+  if (s->capacity > 0 && rows > 0 && (!layout->row_src || !grad_y)) return MOE_ERR_INVALID_ARG;
+  if (!need(grad_out, n, aligned16) || !need(y, rows, aligned16) || !need(grad_y, rows, aligned16) ||
+      !need(grad_w, n, aligned4))
+    return MOE_ERR_MISALIGNED;
+  if (rows > 0 && grad_y && (grad_y == y || grad_y == grad_out)) return MOE_ERR_INVALID_ARG;
+  const int64_t pad_rows = s->capacity > 0 ? rows : 0;
+  return hip_status(moe::launch_combine_bwd(s->act_dtype == MOE_DT_BF16, grad_out, y, topk_w, layout->assign_row, n,
+                                            s->top_k, row_bytes, grad_y, grad_w, pad_rows, layout->row_src,
+                                            as_stream(stream)));
+}
+
+const char *moe_status_string(moe_status st) {
+  switch (st) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_MISALIGNED: return "misaligned pointer or row size";
+    case MOE_ERR_WORKSPACE: return "workspace missing, too small or not 256-byte aligned";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_ERR_HIP: return "HIP launch failed";
+  }
+  return "unknown status";
+}
+
+const char *moe_version(void) { return "0.1.0"; }
+
+}  // extern "C"

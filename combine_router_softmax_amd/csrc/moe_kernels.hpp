@@ -1,0 +1,40 @@
+// Host launchers of the gfx950 kernels (internal; the public surface is moe.h).
+// Each launcher enqueues on `stream` and returns the launch status; argument
+// checking happens before, in moe_abi.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- route (moe_route.hip)
+hipError_t launch_route(const float *logits, int64_t n, int e, int k, int32_t *topk_idx, float *topk_w,
+                        uint8_t *routing_map, int32_t *tokens_per_expert, hipStream_t stream);
+
+// ---- layout (moe_layout.hip)
+constexpr int kLayoutTile = 512;  // assignments per layout tile
+inline int64_t layout_tiles(int64_t assignments) { return (assignments + kLayoutTile - 1) / kLayoutTile; }
+size_t layout_workspace_bytes(int64_t assignments, int e);
+hipError_t launch_layout(const int32_t *topk_idx, const float *topk_w, int64_t n, int k, int e, int capacity,
+                         int64_t rows, int32_t *tokens_per_expert, int32_t *expert_offsets, int32_t *ordinal,
+                         int32_t *assign_row, int32_t *row_src, uint8_t *drop_mask, uint8_t *pad_mask,
+                         int32_t *counters, float *w_perm, void *workspace, hipStream_t stream);
+
+// ---- row movement (moe_rows.hip); `row_bytes` is a multiple of 16
+hipError_t launch_scatter(const void *x, int64_t n, int k, int64_t row_bytes, const int32_t *assign_row,
+                          void *x_perm, int64_t pad_rows, const int32_t *row_src, hipStream_t stream);
+hipError_t launch_combine(bool bf16, const void *y, const float *topk_w, const int32_t *assign_row, int64_t n,
+                          int k, int64_t row_bytes, void *out, hipStream_t stream);
+hipError_t launch_combine_bwd(bool bf16, const void *grad_out, const void *y, const float *topk_w,
+                              const int32_t *assign_row, int64_t n, int k, int64_t row_bytes, void *grad_y,
+                              float *grad_w, int64_t pad_rows, const int32_t *row_src, hipStream_t stream);
+
+// ---- grouped SwiGLU FFN (moe_ffn.hip); bf16 operands as uint16_t bit patterns
+size_t ffn_workspace_bytes(int64_t rows, int inter);
+hipError_t launch_expert_ffn(const uint16_t *x_perm, int64_t rows, int64_t hidden, int inter, int e,
+                             int capacity, const int32_t *tokens_per_expert, const int32_t *expert_offsets,
+                             const uint16_t *w_gate_up, const uint16_t *w_down, uint16_t *y, void *workspace,
+                             hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,247 @@
+// Row-movement kernels of the MoE path, all HBM-bound:
+//   scatter      token rows -> expert-contiguous rows (dispatch data move)
+//   combine      probability-weighted gather of the k expert rows of a token
+//   combine_bwd  its backward: grad of expert rows and grad of the weights
+//
+// Sources: "Megatron MoE 实现" (dispatch_preprocess permutes the hidden states;
+// combine_postprocess unpermutes); DeepSpeed ep_tp_dispatch.py restore_combined
+// (weighted rows added into a zeroed output one top-k slot at a time, in
+// ascending slot order); the mscclpp high-throughput dispatch/combine commit
+// (a direct-gather combine per token; exact dispatched copies).
+//
+// Design: one workgroup per source token, 16-byte vectors per lane.  The
+// scatter reads each token row once and writes it to its k rows (source-major:
+// HBM reads = N rows, writes = kept rows).  The combine gathers the token's k
+// rows (destination-major: reads = kept rows, writes = N rows) and keeps one
+// fp32 accumulator per element, updated with one fused multiply-add per slot in
+// slot order j = 0..k-1, then rounds once.  Capacity pad rows are zero-filled
+// by extra workgroups placed after the token workgroups.  Slots are handled in
+// chunks of KC (compile-time) so the k row indices and weights of a chunk stay
+// in scalar registers and the chunk's k loads are in flight together.
+#include "moe_device.hpp"
+#include "moe_kernels.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kRowThreads = 256;
+constexpr int kMaxPadBlocks = 2048;
+
+__device__ __forceinline__ char *row_ptr(void *base, int64_t row, int64_t row_bytes) {
+  return static_cast<char *>(base) + row * row_bytes;
+}
+__device__ __forceinline__ const char *row_ptr(const void *base, int64_t row, int64_t row_bytes) {
+  return static_cast<const char *>(base) + row * row_bytes;
+}
+
+// Zero-fill rows r < pad_rows with row_src[r] < 0 (capacity pad slots).
+__device__ __forceinline__ void zero_pad_rows(void *dst, int64_t pad_rows, const int32_t *row_src,
+                                              int64_t row_bytes, int64_t pad_block, int64_t pad_blocks) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  const int64_t vpr = row_bytes / 16;
+  for (int64_t r = pad_block; r < pad_rows; r += pad_blocks) {
+    if (row_src[r] >= 0) continue;
+    char *d = row_ptr(dst, r, row_bytes);
+    for (int64_t v = threadIdx.x; v < vpr; v += kRowThreads) st16_stream(d + v * 16, z);
+  }
+}
+
+template <int KC>
+__global__ __launch_bounds__(kRowThreads) void scatter_kernel(const void *__restrict__ x, int64_t n, int k,
+                                                              int64_t row_bytes, const int32_t *__restrict__ assign_row,
+                                                              void *__restrict__ x_perm, int64_t pad_rows,
+                                                              const int32_t *__restrict__ row_src, int64_t pad_blocks) {
+  const int64_t b = blockIdx.x;
+  if (b >= n) {
+    zero_pad_rows(x_perm, pad_rows, row_src, row_bytes, b - n, pad_blocks);
+    return;
+  }
+  const int64_t vpr = row_bytes / 16;
+  const char *src = row_ptr(x, b, row_bytes);
+  for (int j0 = 0; j0 < k; j0 += KC) {
+    int32_t rows[KC];
+#pragma unroll
+    for (int j = 0; j < KC; ++j) rows[j] = j0 + j < k ? assign_row[b * k + j0 + j] : -1;
+    for (int64_t v = threadIdx.x; v < vpr; v += kRowThreads) {
+      const u32x4 val = ld16(src + v * 16);
+#pragma unroll
+      for (int j = 0; j < KC; ++j)
+        if (rows[j] >= 0) st16_stream(row_ptr(x_perm, rows[j], row_bytes) + v * 16, val);
+    }
+  }
+}
+
+template <bool BF16, int KC>
+__global__ __launch_bounds__(kRowThreads) void combine_kernel(const void *__restrict__ y, const float *__restrict__ topk_w,
+                                                              const int32_t *__restrict__ assign_row, int64_t n, int k,
+                                                              int64_t row_bytes, void *__restrict__ out) {
+  using V = Vec16<BF16>;
+  constexpr int EL = V::kElems;
+  const int64_t t = blockIdx.x;
+  const int64_t vpr = row_bytes / 16;
+  char *dst = row_ptr(out, t, row_bytes);
+  for (int64_t v = threadIdx.x; v < vpr; v += kRowThreads) {
+    float acc[EL];
+#pragma unroll
+    for (int i = 0; i < EL; ++i) acc[i] = 0.0f;
+    for (int j0 = 0; j0 < k; j0 += KC) {
+      int32_t rows[KC];
+      float wts[KC];
+      u32x4 vals[KC];
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        rows[j] = j0 + j < k ? assign_row[t * k + j0 + j] : -1;
+        wts[j] = j0 + j < k ? topk_w[t * k + j0 + j] : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < KC; ++j)
+        if (rows[j] >= 0) vals[j] = ld16(row_ptr(y, rows[j], row_bytes) + v * 16);
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        if (rows[j] < 0) continue;
+        float f[EL];
+        V::unpack(vals[j], f);
+#pragma unroll
+        for (int i = 0; i < EL; ++i) acc[i] = __builtin_fmaf(wts[j], f[i], acc[i]);
+      }
+    }
+    st16(dst + v * 16, V::pack(acc));
+  }
+}
+
+template <bool BF16, int KC>
+__global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
+    const void *__restrict__ grad_out, const void *__restrict__ y, const float *__restrict__ topk_w,
+    const int32_t *__restrict__ assign_row, int64_t n, int k, int64_t row_bytes, void *__restrict__ grad_y,
+    float *__restrict__ grad_w, int64_t pad_rows, const int32_t *__restrict__ row_src, int64_t pad_blocks) {
+  using V = Vec16<BF16>;
+  constexpr int EL = V::kElems;
+  constexpr int kWaves = kRowThreads / kWave;
+  __shared__ float part[kWaves][KC];
+  const int64_t t = blockIdx.x;
+  if (t >= n) {
+    zero_pad_rows(grad_y, pad_rows, row_src, row_bytes, t - n, pad_blocks);
+    return;
+  }
+  const int64_t vpr = row_bytes / 16;
+  const char *g = row_ptr(grad_out, t, row_bytes);
+  const int w = threadIdx.x / kWave;
+  for (int j0 = 0; j0 < k; j0 += KC) {
+    int32_t rows[KC];
+    float wts[KC], dot[KC];
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      rows[j] = j0 + j < k ? assign_row[t * k + j0 + j] : -1;
+      wts[j] = j0 + j < k ? topk_w[t * k + j0 + j] : 0.0f;
+      dot[j] = 0.0f;
+    }
+    for (int64_t v = threadIdx.x; v < vpr; v += kRowThreads) {
+      float gf[EL];
+      V::unpack(ld16(g + v * 16), gf);
+      u32x4 yv[KC];
+#pragma unroll
+      for (int j = 0; j < KC; ++j)
+        if (rows[j] >= 0) yv[j] = ld16(row_ptr(y, rows[j], row_bytes) + v * 16);
+#pragma unroll
+      for (int j = 0; j < KC; ++j) {
+        if (rows[j] < 0) continue;
+        float yf[EL], o[EL];
+        V::unpack(yv[j], yf);
+#pragma unroll
+        for (int i = 0; i < EL; ++i) {
+          dot[j] = __builtin_fmaf(gf[i], yf[i], dot[j]);
+          o[i] = wts[j] * gf[i];
+        }
+        st16_stream(row_ptr(grad_y, rows[j], row_bytes) + v * 16, V::pack(o));
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      const float s = wave_sum_f32(dot[j]);
+      if (lane_id() == 0) part[w][j] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x < KC && j0 + (int)threadIdx.x < k) {
+      const int j = threadIdx.x;
+      float s = 0.0f;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) s += part[ww][j];
+      grad_w[t * k + j0 + j] = assign_row[t * k + j0 + j] >= 0 ? s : 0.0f;
+    }
+    __syncthreads();
+  }
+}
+
+inline int slot_chunk(int k) { return k >= 8 ? 8 : (k >= 4 ? 4 : (k >= 2 ? 2 : 1)); }
+
+inline int64_t pad_block_count(int64_t pad_rows) {
+  return pad_rows <= 0 ? 0 : (pad_rows < kMaxPadBlocks ? pad_rows : kMaxPadBlocks);
+}
+
+}  // namespace
+
+hipError_t launch_scatter(const void *x, int64_t n, int k, int64_t row_bytes, const int32_t *assign_row,
+                          void *x_perm, int64_t pad_rows, const int32_t *row_src, hipStream_t stream) {
+  const int64_t pb = pad_block_count(pad_rows);
+  const int64_t blocks = n + pb;
+  if (blocks == 0) return hipSuccess;
+  const dim3 grid((unsigned)blocks), block(kRowThreads);
+  switch (slot_chunk(k)) {
+    case 1: hipLaunchKernelGGL(scatter_kernel<1>, grid, block, 0, stream, x, n, k, row_bytes, assign_row, x_perm, pad_rows, row_src, pb); break;
+    case 2: hipLaunchKernelGGL(scatter_kernel<2>, grid, block, 0, stream, x, n, k, row_bytes, assign_row, x_perm, pad_rows, row_src, pb); break;
+    case 4: hipLaunchKernelGGL(scatter_kernel<4>, grid, block, 0, stream, x, n, k, row_bytes, assign_row, x_perm, pad_rows, row_src, pb); break;
+    default: hipLaunchKernelGGL(scatter_kernel<8>, grid, block, 0, stream, x, n, k, row_bytes, assign_row, x_perm, pad_rows, row_src, pb); break;
+  }
+  return hipGetLastError();
+}
+
+template <bool BF16>
+static hipError_t launch_combine_t(const void *y, const float *topk_w, const int32_t *assign_row, int64_t n, int k,
+                                   int64_t row_bytes, void *out, hipStream_t stream) {
+  const dim3 grid((unsigned)n), block(kRowThreads);
+  switch (slot_chunk(k)) {
+    case 1: hipLaunchKernelGGL((combine_kernel<BF16, 1>), grid, block, 0, stream, y, topk_w, assign_row, n, k, row_bytes, out); break;
+    case 2: hipLaunchKernelGGL((combine_kernel<BF16, 2>), grid, block, 0, stream, y, topk_w, assign_row, n, k, row_bytes, out); break;
+    case 4: hipLaunchKernelGGL((combine_kernel<BF16, 4>), grid, block, 0, stream, y, topk_w, assign_row, n, k, row_bytes, out); break;
+    default: hipLaunchKernelGGL((combine_kernel<BF16, 8>), grid, block, 0, stream, y, topk_w, assign_row, n, k, row_bytes, out); break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_combine(bool bf16, const void *y, const float *topk_w, const int32_t *assign_row, int64_t n, int k,
+                          int64_t row_bytes, void *out, hipStream_t stream) {
+  if (n == 0) return hipSuccess;
+  return bf16 ? launch_combine_t<true>(y, topk_w, assign_row, n, k, row_bytes, out, stream)
+              : launch_combine_t<false>(y, topk_w, assign_row, n, k, row_bytes, out, stream);
+}
+
+template <bool BF16>
+static hipError_t launch_combine_bwd_t(const void *grad_out, const void *y, const float *topk_w,
+                                       const int32_t *assign_row, int64_t n, int k, int64_t row_bytes, void *grad_y,
+                                       float *grad_w, int64_t pad_rows, const int32_t *row_src, hipStream_t stream) {
+  const int64_t pb = pad_block_count(pad_rows);
+  const dim3 grid((unsigned)(n + pb)), block(kRowThreads);
+#define MOE_CBWD(KC)                                                                                         \
+  hipLaunchKernelGGL((combine_bwd_kernel<BF16, KC>), grid, block, 0, stream, grad_out, y, topk_w, assign_row, n, \
+                     k, row_bytes, grad_y, grad_w, pad_rows, row_src, pb)
+  switch (slot_chunk(k)) {
+    case 1: MOE_CBWD(1); break;
+    case 2: MOE_CBWD(2); break;
+    case 4: MOE_CBWD(4); break;
+    default: MOE_CBWD(8); break;
+  }
+#undef MOE_CBWD
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bwd(bool bf16, const void *grad_out, const void *y, const float *topk_w,
+                              const int32_t *assign_row, int64_t n, int k, int64_t row_bytes, void *grad_y,
+                              float *grad_w, int64_t pad_rows, const int32_t *row_src, hipStream_t stream) {
+  if (n + pad_block_count(pad_rows) == 0) return hipSuccess;
+  return bf16 ? launch_combine_bwd_t<true>(grad_out, y, topk_w, assign_row, n, k, row_bytes, grad_y, grad_w, pad_rows,
+                                           row_src, stream)
+              : launch_combine_bwd_t<false>(grad_out, y, topk_w, assign_row, n, k, row_bytes, grad_y, grad_w,
+                                            pad_rows, row_src, stream);
+}
+
+}  // namespace moe

@@ -1,0 +1,194 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) single-GPU Mixture-of-Experts path:
+ *
+ *   moe_route       router softmax / top-k / renormalise / multihot map / counts
+ *   moe_dispatch    per-expert histogram + prefix sum, stable per-expert ordinals,
+ *                   capacity drop/pad masks, row scatter into expert-contiguous rows
+ *   moe_expert_ffn  grouped SwiGLU expert GEMM (bf16 MFMA, fp32 accumulation)
+ *   moe_combine     probability-weighted unpermute / combine (fp32 accumulation)
+ *   moe_combine_bwd backward of moe_combine (grad of expert rows, grad of weights)
+ *
+ * The steps follow the four stages of Megatron-Core's MoELayer.forward as laid
+ * out on the page "Megatron MoE 实现" (router -> (probs, routing_map);
+ * dispatch_preprocess / token_dispatch / dispatch_postprocess ->
+ * (dispatched_input, tokens_per_expert, permuted_probs); experts;
+ * combine_postprocess), restricted to one GPU: the expert-parallel all-to-all
+ * between those stages is not part of this library.
+ *
+ * Conventions for every entry point:
+ *  - Pointers to tensors are DEVICE pointers owned by the caller; the library
+ *    never allocates or frees memory and keeps no state between calls.  Scratch
+ *    space is a caller-provided device workspace of moe_workspace_size() bytes.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the default
+ *    stream) and never reads device memory on the host, so it never blocks.
+ *    Calls with distinct outputs and workspaces may be in flight on different
+ *    streams at once.
+ *  - Host-side validation runs before anything is enqueued; on error nothing is
+ *    enqueued and a negative moe_status is returned.  A failed kernel launch
+ *    returns MOE_ERR_HIP.  Device-side data errors (expert ids out of range) are
+ *    never used as addresses: they are skipped and counted.
+ *  - Tensors are dense row-major.  Activation rows must be 16-byte aligned and
+ *    hold a multiple of 16 bytes (hidden * sizeof(dtype) % 16 == 0).
+ *  - Logits and weights are fp32; activations are fp32 or bf16 (bf16 stored as
+ *    raw 16-bit patterns); moe_expert_ffn is bf16 only.  Every bf16 result is
+ *    rounded to nearest, ties to even, from fp32.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, negative or inconsistent size */
+  MOE_ERR_MISALIGNED = -2,  /* pointer or row size breaks the 16-byte rule */
+  MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than moe_workspace_size */
+  MOE_ERR_UNSUPPORTED = -4, /* valid but outside what the kernels implement */
+  MOE_ERR_HIP = -5          /* a HIP launch failed */
+} moe_status;
+
+typedef enum moe_dtype { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype;
+
+typedef enum moe_op {
+  MOE_OP_ROUTE = 0,
+  MOE_OP_DISPATCH = 1,
+  MOE_OP_EXPERT_FFN = 2,
+  MOE_OP_COMBINE = 3,
+  MOE_OP_COMBINE_BWD = 4
+} moe_op;
+
+/* Shapes and options; read on the host only, never kept. */
+typedef struct moe_shape {
+  int64_t n_tokens;  /* N >= 0: tokens (rows of logits, x, out, grad_out) */
+  int64_t hidden;    /* H >= 1: activation row length */
+  int32_t n_experts; /* E in [1, 1024]: experts on this GPU */
+  int32_t top_k;     /* k >= 1: slots per token (route: k <= E) */
+  int32_t capacity;  /* C: rows per expert; <= 0 means dropless */
+  int32_t inter;     /* I: SwiGLU intermediate size (moe_expert_ffn only) */
+  int64_t max_rows;  /* R: rows of the permuted buffer; 0 = default (E*C with a
+                        capacity, else N*k).  With a capacity R must be E*C or 0. */
+  int32_t act_dtype; /* moe_dtype of the activations */
+  int32_t reserved;  /* must be 0 */
+} moe_shape;
+
+/* The dispatch layout ("handle"): written by moe_dispatch, read by the other
+ * calls.  All arrays are device int32/uint8 arrays of the stated lengths
+ * (A = N*k assignments, a = t*k + j; R = rows of the permuted buffer). */
+typedef struct moe_layout {
+  int32_t *tokens_per_expert; /* [E]   rows kept per expert */
+  int32_t *expert_offsets;    /* [E+1] first row of each expert segment; E*C
+                                 spacing with a capacity, else the exclusive scan
+                                 of the counts clipped to R; [E] = rows used */
+  int32_t *ordinal;           /* [A]   stable per-expert ordinal (number of earlier
+                                 assignments to the same expert), -1 for -1 /
+                                 invalid ids; dropped assignments keep theirs */
+  int32_t *assign_row;        /* [A]   row of assignment a, -1 if not placed */
+  int32_t *row_src;           /* [R]   assignment placed in the row, -1 if none */
+  uint8_t *drop_mask;         /* [A]   1 = valid id but over capacity / R */
+  uint8_t *pad_mask;          /* [R]   1 = row holds no assignment (capacity pad
+                                 or unused dropless tail) */
+  int32_t *counters;          /* [4]   kept, dropped, capacity pad rows, invalid ids */
+} moe_layout;
+
+/* Rows R of the permuted buffer for this shape (E*C, max_rows or N*k). */
+int64_t moe_layout_rows(const moe_shape *s);
+
+/* Bytes of device workspace `op` needs for shape `s` (0 is a valid answer).
+ * Workspace must be 256-byte aligned; its contents need no initialisation. */
+moe_status moe_workspace_size(moe_op op, const moe_shape *s, size_t *bytes);
+
+/* Router: the routing stage of MoELayer.forward ("Megatron MoE 实现",
+ * router_and_preprocess: probs, routing_map = router(hidden_states)) with the
+ * multihot [N, E] map of the MORI dispatcher's _indices_to_multihot and its
+ * sync-free per-expert counting (ROCm/Megatron-LM "Add MORI as a Token
+ * Dispatcher", commit log).  Per token t:
+ *   topk_idx[t, 0..k-1] = the k experts with the largest logits, ties broken
+ *     towards the lower index (-0.0 == +0.0, NaN ranks below every number),
+ *     stored in that order;
+ *   topk_w[t, j] = softmax(logits[t])[idx_j] / sum_j' softmax(logits[t])[idx_j']
+ *     (fp32; equal to the softmax over the k chosen logits);
+ *   routing_map[t, e] = 1 if e was chosen else 0 (nullable, uint8 [N, E]);
+ *   tokens_per_expert[e] = number of tokens choosing e (nullable, int32 [E]).
+ * Inputs: logits fp32 [N, E].  Outputs: topk_idx int32 [N, k], topk_w fp32 [N, k].
+ * Infinite logits are unsupported (their weights are NaN).  k <= E <= 1024.
+ * No workspace. */
+moe_status moe_route(const moe_shape *s, const float *logits, int32_t *topk_idx, float *topk_w,
+                     uint8_t *routing_map, int32_t *tokens_per_expert, void *stream);
+
+/* Dispatch: local permutation of token rows into expert-contiguous rows
+ * ("Megatron MoE 实现", dispatch_preprocess / dispatch_postprocess ->
+ * dispatched_input, tokens_per_expert, permuted_probs), with DeepSpeed's
+ * per-assignment payload (ep_tp_dispatch.py RoutedAssignmentPayload:
+ * capacity slots, drop and pad masks; assignment_ordinals_by_expert: stable
+ * ordinals within each expert segment) and the MORI dispatcher's -1 sentinel
+ * for non-local slots.
+ * Inputs: x [N, H] activations; topk_idx int32 [N, k] expert ids (-1 = skip;
+ *   < -1 or >= E: invalid, skipped, counted in counters[3]); topk_w fp32 [N, k].
+ * Outputs: every array of *layout (see moe_layout); x_perm [R, H]: row
+ *   assign_row[a] = x[a / k] bit for bit, capacity pad rows all-zero, unused
+ *   dropless tail rows not written; w_perm fp32 [R] (nullable): topk_w[a] in
+ *   row assign_row[a], 0 in every other row.
+ * Stability: within an expert, rows follow assignment order a = t*k + j.
+ * With a capacity C the first C assignments of each expert (by ordinal) are
+ * kept; without one, assignments past row R are dropped.
+ * Workspace: moe_workspace_size(MOE_OP_DISPATCH). */
+moe_status moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_idx, const float *topk_w,
+                        const moe_layout *layout, void *x_perm, float *w_perm, void *workspace,
+                        size_t workspace_bytes, void *stream);
+
+/* Grouped SwiGLU expert FFN over the expert segments of a dispatch layout
+ * ("Megatron MoE 实现", experts(dispatched_input, tokens_per_expert, ...), one
+ * GEMM group per expert as in the grouped-GEMM paths of the MORI and UltraEP
+ * pull requests, fed by device-resident counts with no host synchronisation).
+ * For every row r of expert e's segment [offset_e, offset_e + kept_e):
+ *   a[r, i] = bf16( silu(x_perm[r] . w_gate_up[e, i]) * (x_perm[r] . w_gate_up[e, I + i]) )
+ *   y[r, c] = bf16( a[r] . w_down[e, c] )
+ * bf16 operands, fp32 accumulation, no bias.  Rows outside the segments of y are
+ * not written.  Shapes: x_perm bf16 [R, H]; w_gate_up bf16 [E, 2I, H] (gate rows
+ * first); w_down bf16 [E, H, I]; y bf16 [R, H].  H and I must be multiples of 64.
+ * Workspace: moe_workspace_size(MOE_OP_EXPERT_FFN) (holds a [R, I] bf16). */
+moe_status moe_expert_ffn(const moe_shape *s, const void *x_perm, const moe_layout *layout,
+                          const void *w_gate_up, const void *w_down, void *y, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/* Combine: probability-weighted unpermute (DeepSpeed ep_tp_dispatch.py
+ * restore_combined: weighted expert rows added into a zeroed [N, H] output by
+ * token index, one top-k slot at a time in ascending slot order; "Megatron MoE
+ * 实现", combine_postprocess).
+ *   out[t, :] = sum over j = 0..k-1 with assign_row[t*k+j] >= 0, in that order,
+ *               of topk_w[t, j] * y[assign_row[t*k+j], :]
+ * accumulated in fp32 with one fused multiply-add per term and rounded once to
+ * the activation type; a token with no kept slot gets a zero row.  Weights are
+ * indexed like the assignments (receiver-side, as the MORI combine requires).
+ * y [R, H] and out [N, H] have the activation type; out must not alias y.
+ * For an identity expert pass x_perm as y.  No workspace. */
+moe_status moe_combine(const moe_shape *s, const void *y, const float *topk_w, const moe_layout *layout,
+                       void *out, void *stream);
+
+/* Combine backward: the vector-Jacobian product of moe_combine (the MORI pull
+ * request's combine backward, with receiver-side weights and indices).
+ * For every kept assignment a = (t, j) in row r = assign_row[a]:
+ *   grad_y[r, :] = topk_w[t, j] * grad_out[t, :]     (rounded to the activation type)
+ *   grad_w[t, j] = sum_h grad_out[t, h] * y[r, h]    (fp32 accumulation)
+ * grad_w = 0 for dropped, -1 and invalid slots; capacity pad rows of grad_y are
+ * zero; unused dropless tail rows are not written.  grad_y must not alias y or
+ * grad_out.  No workspace. */
+moe_status moe_combine_bwd(const moe_shape *s, const void *grad_out, const void *y, const float *topk_w,
+                           const moe_layout *layout, void *grad_y, float *grad_w, void *stream);
+
+/* Static description of a status code. */
+const char *moe_status_string(moe_status st);
+
+/* Library version, "major.minor.patch". */
+const char *moe_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,76 @@
+"""Helpers for the GPU parity tests: host <-> device transfer of the seeded
+inputs and the error measures the tolerances are stated in."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import moe_inputs as mi
+
+# Tolerances (max relative error = max|got - ref| / max|ref| over a tensor).
+TOL_BF16 = 2e-2
+TOL_F32 = 1e-5
+
+
+def dev(a: np.ndarray, device="cuda") -> torch.Tensor:
+    """numpy -> device tensor; uint16 arrays are bf16 bit patterns."""
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    """device tensor -> numpy; bf16 comes back as uint16 bit patterns."""
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy().view(np.uint16)
+    return t.cpu().numpy()
+
+
+def values(a: np.ndarray) -> np.ndarray:
+    """Numeric values in float64 (bf16 bit patterns are widened exactly)."""
+    if a.dtype == np.uint16:
+        return mi.bf16_bits_to_f32(a).astype(np.float64)
+    return a.astype(np.float64)
+
+
+def max_rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    g, r = values(got), values(ref)
+    denom = np.abs(r).max() if r.size else 0.0
+    if denom == 0.0:
+        return float(np.abs(g - r).max()) if g.size else 0.0
+    return float(np.abs(g - r).max() / denom)
+
+
+def tol_for(dtype_or_array) -> float:
+    dt = dtype_or_array.dtype if hasattr(dtype_or_array, "dtype") else dtype_or_array
+    return TOL_BF16 if dt in (np.uint16, torch.bfloat16) else TOL_F32
+
+
+def layout_host(layout) -> dict:
+    return {f: host(getattr(layout, f)) for f in ("tokens_per_expert", "expert_offsets", "ordinal", "assign_row",
+                                                  "row_src", "drop_mask", "pad_mask", "counters")}
+
+
+LAYOUT_FIELDS = ("tokens_per_expert", "expert_offsets", "ordinal", "assign_row", "row_src", "drop_mask", "pad_mask",
+                 "counters")
+
+
+def assert_layout_equal(got: dict, ref: dict):
+    for f in LAYOUT_FIELDS:
+        g, r = got[f], ref[f]
+        assert g.shape == r.shape, (f, g.shape, r.shape)
+        if not np.array_equal(g, r):
+            bad = np.nonzero(g != r)[0]
+            raise AssertionError(f"layout field {f} differs at {bad.size} positions, first {bad[:8]}: "
+                                 f"got {g[bad[:8]]} ref {r[bad[:8]]}")
+
+
+def workload_inputs(w: mi.Workload, seed: int = 0):
+    """(topk_idx or None, topk_w or None, logits or None, x) as numpy arrays."""
+    x = mi.activations(w, seed)
+    if w.has_router:
+        return None, None, mi.router_logits(w, seed), x
+    idx, wts = mi.received_routing(w, seed)
+    return idx, wts, None, x

@@ -1,0 +1,105 @@
+"""Host-side checks of the C ABI library (no GPU needed, no kernel launched):
+the library loads, exports every function include/moe.h declares, sizes its
+workspaces, and rejects bad arguments before touching the device."""
+from __future__ import annotations
+
+import ctypes as C
+import re
+from pathlib import Path
+
+import pytest
+
+ROOT = Path(__file__).resolve().parents[1]
+
+
+def header_functions():
+    text = (ROOT / "include" / "moe.h").read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w \*]*?\b(moe_\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import combine_router_softmax_amd as m
+    return m
+
+
+def test_library_exports_every_declared_function(moe):
+    declared = header_functions()
+    assert len(declared) == 9, declared
+    assert sorted(moe.EXPORTS) == declared
+    for name in declared:
+        assert hasattr(moe.lib, name), name
+    assert moe.lib.moe_version().decode().count(".") == 2
+
+
+def test_library_is_built_for_gfx950(moe):
+    data = Path(moe.library_path).read_bytes()
+    assert b"gfx950" in data
+
+
+def test_status_strings(moe):
+    for st in range(0, -6, -1):
+        s = moe.lib.moe_status_string(st).decode()
+        assert s and s != "unknown status"
+    assert moe.lib.moe_status_string(-99).decode() == "unknown status"
+
+
+def test_layout_rows_and_workspace_sizes(moe):
+    s = moe.make_shape(4096, 7168, 256, 8)
+    assert moe.lib.moe_layout_rows(C.byref(s)) == 32768
+    s = moe.make_shape(4096, 7168, 256, 8, capacity=160)
+    assert moe.lib.moe_layout_rows(C.byref(s)) == 40960
+    s = moe.make_shape(16384, 7168, 32, 8, max_rows=32768)
+    assert moe.lib.moe_layout_rows(C.byref(s)) == 32768
+    assert moe.workspace_size(moe.MOE_OP_ROUTE, s) == 0
+    assert moe.workspace_size(moe.MOE_OP_COMBINE, s) == 0
+    tiles = (16384 * 8 + 511) // 512
+    assert moe.workspace_size(moe.MOE_OP_DISPATCH, s) >= tiles * 32 * 4
+    s = moe.make_shape(8192, 4096, 128, 8, inter=1536)
+    assert moe.workspace_size(moe.MOE_OP_EXPERT_FFN, s) >= 65536 * 1536 * 2
+    assert moe.workspace_size(moe.MOE_OP_DISPATCH, moe.make_shape(0, 64, 4, 2)) == 0
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("n_tokens", -1, -1), ("hidden", 0, -1), ("n_experts", 0, -1), ("n_experts", 1025, -4), ("top_k", 0, -1),
+    ("act_dtype", 7, -1), ("reserved", 1, -1), ("max_rows", -5, -1),
+])
+def test_bad_shapes_are_rejected(moe, field, value, status):
+    s = moe.make_shape(16, 64, 8, 2)
+    setattr(s, field, value)
+    out = C.c_size_t(0)
+    assert moe.lib.moe_workspace_size(moe.MOE_OP_DISPATCH, C.byref(s), C.byref(out)) == status
+    assert moe.lib.moe_layout_rows(C.byref(s)) == -1
+
+
+def test_validation_errors_enqueue_nothing(moe):
+    """Every call below fails host-side validation, so no HIP call is made."""
+    lib = moe.lib
+    p = C.c_void_p(4096)          # a fake, 16-byte-aligned "device" address: never dereferenced
+    odd = C.c_void_p(4096 + 2)
+    s = moe.make_shape(16, 64, 8, 9, act_dtype=moe.MOE_DT_F32)
+    assert lib.moe_route(C.byref(s), p, p, p, None, None, None) == -1          # k > E
+    s = moe.make_shape(16, 64, 8, 2, act_dtype=moe.MOE_DT_F32)
+    assert lib.moe_route(C.byref(s), None, p, p, None, None, None) == -1       # null logits
+    assert lib.moe_route(C.byref(s), odd, p, p, None, None, None) == -2        # misaligned
+    assert lib.moe_route(None, p, p, p, None, None, None) == -1
+    lay = moe.MoeLayoutC(*([4096] * 8))
+    s = moe.make_shape(16, 60, 8, 2, act_dtype=moe.MOE_DT_BF16)                # 120-byte rows
+    assert lib.moe_dispatch(C.byref(s), p, p, p, C.byref(lay), p, p, p, 1 << 20, None) == -2
+    s = moe.make_shape(16, 64, 8, 2, act_dtype=moe.MOE_DT_BF16)
+    assert lib.moe_dispatch(C.byref(s), odd, p, p, C.byref(lay), p, p, p, 1 << 20, None) == -2
+    assert lib.moe_dispatch(C.byref(s), p, p, p, C.byref(lay), p, p, p, 0, None) == -3       # no workspace
+    assert lib.moe_dispatch(C.byref(s), p, p, p, C.byref(lay), p, p, odd, 1 << 20, None) == -3  # unaligned ws
+    assert lib.moe_dispatch(C.byref(s), p, p, p, None, p, p, p, 1 << 20, None) == -1
+    s = moe.make_shape(16, 64, 8, 2, capacity=4, max_rows=7)                   # max_rows != E*C
+    assert lib.moe_dispatch(C.byref(s), p, p, p, C.byref(lay), p, p, p, 1 << 20, None) == -1
+    s = moe.make_shape(16, 64, 8, 2, inter=64, act_dtype=moe.MOE_DT_F32)
+    assert lib.moe_expert_ffn(C.byref(s), p, C.byref(lay), p, p, p, p, 1 << 30, None) == -4  # fp32 FFN
+    s = moe.make_shape(16, 64, 8, 2, inter=96)
+    assert lib.moe_expert_ffn(C.byref(s), p, C.byref(lay), p, p, p, p, 1 << 30, None) == -4  # I % 64
+    s = moe.make_shape(16, 64, 8, 2, inter=64)
+    assert lib.moe_expert_ffn(C.byref(s), p, C.byref(lay), p, p, p, p, 16, None) == -3
+    assert lib.moe_combine(C.byref(s), p, p, C.byref(lay), p, None) == -1     # out aliases y
+    assert lib.moe_combine(C.byref(s), odd, p, C.byref(lay), p, None) == -2
+    assert lib.moe_combine_bwd(C.byref(s), p, p, p, C.byref(lay), p, p, None) == -1  # grad_y aliases

@@ -1,0 +1,208 @@
+"""GPU parity of moe_combine, moe_combine_bwd and moe_expert_ffn against the CPU
+oracle, through the C ABI.  Floating-point outputs: max relative error
+(max|got - ref| / max|ref|) <= 2e-2 for bf16 tensors and <= 1e-5 for fp32
+tensors; layouts come from the GPU dispatch, which the dispatch tests prove
+bit-exact against the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+from parity_util import TOL_BF16, TOL_F32, dev, host, layout_host, max_rel_err, tol_for, workload_inputs, values
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import combine_router_softmax_amd as m
+    return m
+
+
+def dispatch_case(moe, w: mi.Workload, seed=0):
+    idx, wts, logits, x = workload_inputs(w, seed)
+    if idx is None:
+        idx, wts, _, _ = oracle.route(logits, w.top_k)
+    xp, wp, lay = moe.moe_dispatch(dev(x), dev(idx), dev(wts), w.n_experts, capacity=w.capacity, max_rows=w.rows)
+    return idx, wts, x, xp, lay
+
+
+# ------------------------------------------------------------------ combine
+
+@pytest.mark.parametrize("wid", [1, 2, 3])
+def test_combine_identity_expert_full_size(moe, wid):
+    w = mi.workload(wid)
+    idx, wts, x, xp, lay = dispatch_case(moe, w)
+    out = moe.moe_combine(xp, dev(wts), lay)
+    got = host(out)
+    ref_lay = layout_host(lay)
+    ref_lay["rows"] = lay.rows
+    ref = oracle.combine(host(xp), wts, ref_lay, w.n_tokens, w.top_k)
+    assert max_rel_err(got, ref) <= tol_for(ref)
+    if wid == 2:
+        # identity expert, renormalised weights, nothing dropped: combine(dispatch(x)) == x bit for bit
+        assert (got == x).all()
+    if wid == 1:
+        assert np.abs(values(got) - values(x)).max() <= 4 * 2.0 ** -23 * np.abs(x).max()
+
+
+@pytest.mark.parametrize("dt", [mi.DT_F32, mi.DT_BF16])
+@pytest.mark.parametrize("capacity", [0, 5])
+def test_combine_random_rows_with_drops_and_sentinels(moe, dt, capacity):
+    g = np.random.default_rng(40 + dt * 2 + (capacity > 0))
+    n, e, k, h = 777, 64, 6, 320 if dt == mi.DT_F32 else 640
+    idx = np.stack([g.permutation(e)[:k] for _ in range(n)]).astype(np.int32)
+    idx[g.random(idx.shape) < 0.3] = -1
+    wts = g.random((n, k)).astype(np.float32)
+    x = mi.normal_activations((n, h), dt, 41, 1)
+    xp, wp, lay = moe.moe_dispatch(dev(x), dev(idx), dev(wts), e, capacity=capacity)
+    y = mi.normal_activations((lay.rows, h), dt, 41, 2)
+    out = moe.moe_combine(dev(y), dev(wts), lay)
+    ref_lay = oracle.layout(idx, e, capacity)
+    ref = oracle.combine(y, wts, ref_lay, n, k)
+    got = host(out)
+    assert max_rel_err(got, ref) <= tol_for(ref)
+    none = (ref_lay["assign_row"].reshape(n, k) < 0).all(1)
+    assert (got[none].view(np.uint8) == 0).all()
+
+
+# --------------------------------------------------------- combine backward
+
+def check_combine_bwd(moe, idx, wts, e, capacity, go, y, max_rows=0):
+    n, k = idx.shape
+    ref_lay = oracle.layout(idx, e, capacity, max_rows)
+    x_dummy = np.zeros((n, y.shape[1]), y.dtype)
+    _, _, lay = moe.moe_dispatch(dev(x_dummy), dev(idx), dev(wts), e, capacity=capacity, max_rows=max_rows)
+    gy, gw = moe.moe_combine_bwd(dev(go), dev(y), dev(wts), lay)
+    gy_h, gw_h = host(gy), host(gw)
+    ref_gy, ref_gw = oracle.combine_bwd(go, y, wts, ref_lay, k, capacity, grad_y=gy_h.copy())
+    written = ref_lay["row_src"] >= 0
+    if capacity:
+        written[:] = True
+    assert max_rel_err(gy_h[written], ref_gy[written]) <= tol_for(y)
+    assert max_rel_err(gw_h, ref_gw) <= TOL_F32
+    assert (gw_h.reshape(-1)[ref_lay["assign_row"] < 0] == 0).all()
+
+
+@pytest.mark.parametrize("dt", [mi.DT_F32, mi.DT_BF16])
+@pytest.mark.parametrize("capacity", [0, 7])
+def test_combine_bwd_small(moe, dt, capacity):
+    g = np.random.default_rng(60 + dt + capacity)
+    n, e, k, h = 501, 32, 4, 384
+    idx = np.stack([g.permutation(e)[:k] for _ in range(n)]).astype(np.int32)
+    idx[g.random(idx.shape) < 0.2] = -1
+    wts = g.random((n, k)).astype(np.float32)
+    rows = e * capacity if capacity else n * k
+    go = mi.normal_activations((n, h), dt, 61, 1)
+    y = mi.normal_activations((rows, h), dt, 61, 2)
+    check_combine_bwd(moe, idx, wts, e, capacity, go, y)
+
+
+def test_combine_bwd_expert_share_full_size(moe):
+    w = mi.workload(5)
+    idx, wts = mi.received_routing(w)
+    go = mi.grad_output(w)
+    y = mi.normal_activations((w.rows, w.hidden), mi.DT_BF16, 5, 9)
+    check_combine_bwd(moe, idx, wts, w.n_experts, 0, go, y, max_rows=w.rows)
+
+
+# --------------------------------------------------------------- expert FFN
+
+def ffn_case(moe, n, e, k, h, inter, capacity=0, seed=0, zero_expert=None):
+    w = mi.workload(4, n_tokens=n, hidden=h, n_experts=e, top_k=k, inter=inter,
+                    capacity_factor=0.0 if not capacity else capacity)
+    logits = mi.router_logits(w, seed)
+    if zero_expert is not None:
+        logits[:, zero_expert] = -50.0
+    idx, wts, _, _ = oracle.route(logits, k)
+    x = mi.activations(w, seed)
+    wgu, wd = mi.expert_weights(w, seed)
+    xp, wp, lay = moe.moe_dispatch(dev(x), dev(idx), dev(wts), e, capacity=w.capacity)
+    y = moe.moe_expert_ffn(xp, lay, dev(wgu), dev(wd))
+    torch.cuda.synchronize()
+    return w, idx, wts, x, wgu, wd, xp, lay, y
+
+
+@pytest.mark.parametrize("n,e,k,h,inter,cap", [
+    (300, 4, 2, 256, 192, 0),     # several m-tiles per expert, ragged tails
+    (257, 8, 2, 192, 128, 0),     # hidden not a multiple of 128 (masked columns)
+    (1000, 16, 4, 512, 256, 0),
+    (600, 8, 2, 256, 64, 1.0),    # capacity layout with drops and pads
+    (5, 4, 1, 64, 64, 0),         # tiny, most experts empty
+])
+def test_expert_ffn_small_full_compare(moe, n, e, k, h, inter, cap):
+    w, idx, wts, x, wgu, wd, xp, lay, y = ffn_case(moe, n, e, k, h, inter, cap, zero_expert=1 if e > 2 else None)
+    lay_h = layout_host(lay)
+    lay_h["rows"] = lay.rows
+    ref = oracle.expert_ffn(host(xp), lay_h, wgu, wd)
+    got = host(y)
+    kept = lay_h["pad_mask"] == 0
+    assert kept.sum() == lay_h["counters"][0]
+    assert max_rel_err(got[kept], ref[kept]) <= TOL_BF16
+    # most outputs should round to the same bf16 value
+    assert (got[kept] == ref[kept]).mean() > 0.9
+
+
+def sample_rows(lay_h: dict, g: np.random.Generator, per_expert: int = 2, experts: int = 16):
+    e = lay_h["tokens_per_expert"].size
+    chosen = g.choice(e, size=min(experts, e), replace=False)
+    rows = []
+    for x in chosen:
+        o, c = int(lay_h["expert_offsets"][x]), int(lay_h["tokens_per_expert"][x])
+        if c == 0:
+            continue
+        rows += [o, o + c - 1] + list(o + g.integers(0, c, size=per_expert))
+    return np.unique(np.array(rows, np.int64))
+
+
+@pytest.mark.parametrize("wid", [4, 5])
+def test_expert_ffn_full_size_sampled_rows(moe, wid):
+    w = mi.workload(wid)
+    idx, wts, logits, x = workload_inputs(w)
+    if idx is None:
+        idx, wts, _, _ = oracle.route(logits, w.top_k)
+    wgu, wd = mi.expert_weights(w)
+    xp, wp, lay = moe.moe_dispatch(dev(x), dev(idx), dev(wts), w.n_experts, max_rows=w.rows)
+    y = moe.moe_expert_ffn(xp, lay, dev(wgu), dev(wd))
+    torch.cuda.synchronize()
+    lay_h = layout_host(lay)
+    rows = sample_rows(lay_h, np.random.default_rng(wid), per_expert=1, experts=12)
+    xp_h = host(xp)
+    ref, ex = oracle.expert_ffn_rows(rows, xp_h, lay_h, wgu, wd)
+    assert (ex >= 0).all()
+    got = host(y)[rows]
+    assert max_rel_err(got, ref) <= TOL_BF16
+    assert (got == ref).mean() > 0.9
+
+
+def test_full_layer_qwen3_shape_sampled_tokens(moe):
+    """route -> dispatch -> grouped SwiGLU FFN -> combine at N=8192 H=4096 E=128 k=8 I=1536;
+    sampled output tokens against the oracle's route, layout, FFN rows and combine."""
+    w = mi.workload(4)
+    logits = mi.router_logits(w)
+    x = mi.activations(w)
+    wgu, wd = mi.expert_weights(w)
+    r = moe.moe_route(dev(logits), w.top_k)
+    xp, wp, lay = moe.moe_dispatch(dev(x), r.topk_idx, r.topk_w, w.n_experts)
+    y = moe.moe_expert_ffn(xp, lay, dev(wgu), dev(wd))
+    out = moe.moe_combine(y, r.topk_w, lay)
+    torch.cuda.synchronize()
+    idx, wts, _, _ = oracle.route(logits, w.top_k)
+    ref_lay = oracle.layout(idx, w.n_experts)
+    toks = np.random.default_rng(9).choice(w.n_tokens, size=6, replace=False)
+    xp_ref, _ = oracle.scatter(x, w.top_k, ref_lay, wts)
+    out_h = host(out)
+    for t in toks:
+        rows = ref_lay["assign_row"][t * w.top_k:(t + 1) * w.top_k].astype(np.int64)
+        y_rows, _ = oracle.expert_ffn_rows(rows, xp_ref, ref_lay, wgu, wd)
+        y_full = np.zeros((ref_lay["rows"], w.hidden), np.uint16)
+        y_full[rows] = y_rows
+        sub_lay = dict(ref_lay)
+        sub_lay["assign_row"] = ref_lay["assign_row"][t * w.top_k:(t + 1) * w.top_k]
+        ref = oracle.combine(y_full, wts[t:t + 1], sub_lay, 1, w.top_k)
+        assert max_rel_err(out_h[t:t + 1], ref) <= TOL_BF16

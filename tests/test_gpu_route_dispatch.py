@@ -1,0 +1,169 @@
+"""GPU parity of moe_route and moe_dispatch against the CPU oracle, through the
+C ABI.  Bit-exact: top-k indices, routing map, counts, every layout array,
+dispatched rows and permuted weights.  Router weights: max relative error
+<= 1e-5 (fp32)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+from parity_util import TOL_F32, assert_layout_equal, dev, host, layout_host, max_rel_err, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import combine_router_softmax_amd as m
+    return m
+
+
+def check_route(moe, logits: np.ndarray, k: int):
+    r = moe.moe_route(dev(logits), k)
+    torch.cuda.synchronize()
+    idx, w, rmap, tpe = oracle.route(logits, k)
+    np.testing.assert_array_equal(host(r.topk_idx), idx)
+    np.testing.assert_array_equal(host(r.routing_map), rmap)
+    np.testing.assert_array_equal(host(r.tokens_per_expert), tpe)
+    if not np.isnan(logits).any() and idx.size:
+        assert max_rel_err(host(r.topk_w), w) <= TOL_F32
+    return r
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 4])
+def test_route_workloads_full_size(moe, wid):
+    w = mi.workload(wid)
+    check_route(moe, mi.router_logits(w), w.top_k)
+
+
+@pytest.mark.parametrize("e,k", [(8, 1), (8, 8), (64, 2), (100, 7), (256, 8), (300, 5), (1024, 16), (1000, 1000)])
+def test_route_shapes_ties_signed_zero_nan(moe, e, k):
+    g = np.random.default_rng(e * 31 + k)
+    n = 1003 if e * k < 100000 else 37
+    logits = g.standard_normal((n, e)).astype(np.float32)
+    check_route(moe, logits, k)
+    vals = np.array([-1.0, -0.0, 0.0, 1.0, np.nan], np.float32)
+    ties = g.choice(vals, size=(n, e), p=[0.25, 0.2, 0.2, 0.25, 0.1]).astype(np.float32)
+    check_route(moe, ties, k)
+
+
+def test_route_empty(moe):
+    r = moe.moe_route(torch.empty((0, 16), dtype=torch.float32, device="cuda"), 4)
+    torch.cuda.synchronize()
+    assert (host(r.tokens_per_expert) == 0).all()
+
+
+def run_dispatch(moe, x: np.ndarray, idx: np.ndarray, wts: np.ndarray, e: int, capacity=0, max_rows=0):
+    x_d = dev(x)
+    xp, wp, lay = moe.moe_dispatch(x_d, dev(idx), dev(wts), e, capacity=capacity, max_rows=max_rows)
+    torch.cuda.synchronize()
+    return xp, wp, lay
+
+
+def check_dispatch(moe, x, idx, wts, e, capacity=0, max_rows=0):
+    xp, wp, lay = run_dispatch(moe, x, idx, wts, e, capacity, max_rows)
+    ref = oracle.layout(idx, e, capacity, max_rows)
+    got = layout_host(lay)
+    assert_layout_equal(got, ref)
+    xp_h = host(xp)
+    k = idx.shape[1]
+    kept = np.nonzero(ref["assign_row"] >= 0)[0]
+    rows = ref["assign_row"][kept]
+    # dispatched rows: bit-exact copies; capacity pads: all-zero bits
+    assert (xp_h[rows].view(np.uint8) == x[kept // k].view(np.uint8)).all()
+    if capacity > 0:
+        pads = np.nonzero(ref["row_src"] < 0)[0]
+        assert (xp_h[pads].view(np.uint8) == 0).all()
+    ref_xp, ref_wp = oracle.scatter(x, k, ref, wts, capacity, x_perm=xp_h.copy())
+    np.testing.assert_array_equal(host(wp), ref_wp)
+    assert (xp_h.view(np.uint8) == ref_xp.view(np.uint8)).all()
+    return xp, wp, lay, ref
+
+
+@pytest.mark.parametrize("wid", [1, 2, 3, 5])
+def test_dispatch_workloads_full_size(moe, wid):
+    w = mi.workload(wid)
+    idx, wts, logits, x = workload_inputs(w)
+    if idx is None:
+        idx, wts, _, _ = oracle.route(logits, w.top_k)
+    check_dispatch(moe, x, idx, wts, w.n_experts, w.capacity, w.rows)
+
+
+EDGE_CASES = ["ragged", "capacity", "clip_rows", "invalid_ids", "one_expert", "all_to_one", "capacity_one", "k1",
+              "e1024", "sentinels"]
+
+
+@pytest.mark.parametrize("case", EDGE_CASES)
+def test_dispatch_edge_cases(moe, case):
+    g = np.random.default_rng(100 + EDGE_CASES.index(case))
+    n, e, k, h, cap, max_rows = 1001, 256, 8, 512, 0, 0
+    if case == "one_expert":
+        e, k = 1, 1
+    if case == "k1":
+        k = 1
+    if case == "e1024":
+        e = 1024
+    idx = np.stack([g.permutation(e)[:k] for _ in range(n)]).astype(np.int32)
+    if case == "capacity":
+        cap = 30
+    if case == "clip_rows":
+        max_rows = n * k - 777
+    if case == "invalid_ids":
+        bad = g.random(idx.shape) < 0.05
+        idx[bad] = g.choice([-5, e, e + 100, -2], size=bad.sum())
+    if case == "all_to_one":
+        idx[:, 0] = 3
+        idx[:, 1:] = -1
+    if case == "capacity_one":
+        cap = 1
+    if case == "sentinels":
+        idx[g.random(idx.shape) < 0.75] = -1
+    wts = g.random((n, k)).astype(np.float32)
+    x = mi.normal_activations((n, h), mi.DT_BF16, 77, 1)
+    check_dispatch(moe, x, idx, wts, e, cap, max_rows)
+
+
+def test_dispatch_fp32_tiny_and_empty(moe):
+    g = np.random.default_rng(5)
+    idx = np.stack([g.permutation(8)[:2] for _ in range(64)]).astype(np.int32)
+    x = mi.normal_activations((64, 128), mi.DT_F32, 1, 1)
+    check_dispatch(moe, x, idx, g.random((64, 2)).astype(np.float32), 8)
+    check_dispatch(moe, x[:0], idx[:0], np.zeros((0, 2), np.float32), 8)
+    check_dispatch(moe, x[:0], idx[:0], np.zeros((0, 2), np.float32), 8, capacity=3)
+
+
+def test_dispatch_deterministic_and_no_out_of_bounds_writes(moe):
+    w = mi.workload(3, n_tokens=2048, hidden=256)
+    logits = mi.router_logits(w)
+    idx, wts, _, _ = oracle.route(logits, w.top_k)
+    x = mi.activations(w)
+    rows = w.max_rows
+    guard = 4096
+    buf = torch.full((rows * w.hidden + 2 * guard,), 7, dtype=torch.int16, device="cuda")
+    xp = buf[guard:guard + rows * w.hidden].view(torch.bfloat16).view(rows, w.hidden)
+    a = moe.moe_dispatch(dev(x), dev(idx), dev(wts), w.n_experts, capacity=w.capacity, x_perm=xp)
+    first = host(xp).copy()
+    lay1 = layout_host(a[2])
+    b = moe.moe_dispatch(dev(x), dev(idx), dev(wts), w.n_experts, capacity=w.capacity, x_perm=xp)
+    torch.cuda.synchronize()
+    assert (host(xp) == first).all()
+    assert_layout_equal(layout_host(b[2]), lay1)
+    hb = host(buf)
+    assert (hb[:guard] == 7).all() and (hb[-guard:] == 7).all()
+
+
+def test_route_then_dispatch_on_device(moe):
+    """Route output feeds dispatch without leaving the GPU (uniform workload shape)."""
+    w = mi.workload(2)
+    logits = mi.router_logits(w)
+    x = mi.activations(w)
+    r = moe.moe_route(dev(logits), w.top_k)
+    xp, wp, lay = moe.moe_dispatch(dev(x), r.topk_idx, r.topk_w, w.n_experts)
+    torch.cuda.synchronize()
+    idx, wts, _, _ = oracle.route(logits, w.top_k)
+    assert_layout_equal(layout_host(lay), oracle.layout(idx, w.n_experts))
