@@ -1,7 +1,7 @@
 // C ABI of the MoE path (declared in include/moe.h): host-side validation,
 // workspace carving and kernel launches on the caller's stream.  No device
 // memory is read on the host and nothing is allocated.
-#include "../../include/moe.h"
+#include "moe.h"
 
 #include <hip/hip_runtime.h>
 
@@ -140,6 +140,7 @@ moe_status moe_expert_ffn(const moe_shape *s, const void *x_perm, const moe_layo
   if (s->act_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
   if (s->inter < 1) return MOE_ERR_INVALID_ARG;
   if (s->inter % 64 != 0 || s->hidden % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (4 * (int64_t)s->inter * s->hidden >= (int64_t)1 << 32) return MOE_ERR_UNSUPPORTED;  // 32-bit weight offsets
   if (!layout || !layout->tokens_per_expert || !layout->expert_offsets || !w_gate_up || !w_down)
     return MOE_ERR_INVALID_ARG;
   if (rows > 0 && (!x_perm || !y)) return MOE_ERR_INVALID_ARG;

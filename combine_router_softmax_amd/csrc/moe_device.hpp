@@ -66,6 +66,10 @@ struct Vec16<false> {
 // 16-byte global load / store (global_load_dwordx4 / global_store_dwordx4).
 __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ void st16(void *p, const u32x4 &v) { *reinterpret_cast<u32x4 *>(p) = v; }
+// Streaming load: the source is read once by this kernel.
+__device__ __forceinline__ u32x4 ld16_stream(const void *p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
 // Streaming store: the destination is not re-read by this kernel.
 __device__ __forceinline__ void st16_stream(void *p, const u32x4 &v) {
   __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));

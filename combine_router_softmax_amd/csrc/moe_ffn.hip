@@ -21,10 +21,15 @@
 // receives one contiguous range of that order: weight and activation tiles are
 // then re-read from the XCD's own L2.  Surplus workgroups exit at once.
 //
-// Tile: 128 rows x 128 columns (GEMM1: 64 gate + 64 up columns), K step 64,
-// 4 waves in a 2 x 2 arrangement of 64 x 64 sub-tiles (2 x 2 MFMA 32x32 blocks),
-// LDS double buffer fed through registers (one barrier per K step), 16-byte
-// padded LDS rows.
+// Tile: 256 rows x 256 columns (GEMM1: 128 gate + 128 up columns), 4 waves in
+// a 2 x 2 arrangement of 128 x 128 sub-tiles (4 x 4 MFMA 32x32 blocks, 256 fp32
+// accumulators per lane, held in AGPRs).  Operands go global -> LDS directly
+// (global_load_lds_dwordx4, no register staging) through a ring of LDS stages
+// (K step 32, 4 stages of 32 KiB, three K steps in flight).  A wave's load
+// instruction fills 1 KiB of a stage; each lane picks which 16-byte chunk of
+// its row to fetch so that chunk c of row r lands at position c ^ swz(r), which
+// keeps the MFMA fragment reads free of LDS bank conflicts.  Rows past the end
+// of an expert's segment re-read its last row and are not stored.
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
 
@@ -34,14 +39,40 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kBM = 128;
-constexpr int kBN = 128;
-constexpr int kBK = 64;
-constexpr int kLds = kBK + 8;  // bf16 per LDS row
+constexpr int kBM = 256;
+constexpr int kBN = 256;
+constexpr int kBK = 32;                          // K per pipeline stage
+constexpr int kStages = 4;                       // LDS stages (kStages - 1 K steps in flight)
+constexpr int kRowBytes = kBK * 2;               // bytes of K per tile row
+constexpr int kChunks = kRowBytes / 16;          // 16-byte chunks per tile row
+constexpr int kLoadRows = 1024 / kRowBytes;      // tile rows one wave load instruction fills
+constexpr int kLoadsPerOperand = kBM / kLoadRows / 4;  // load instructions per wave per operand per stage
+constexpr int kOperandBytes = kBM * kRowBytes;
+constexpr int kStageBytes = 2 * kOperandBytes;
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 constexpr int kMaxExperts = 1024;
-constexpr int kTileElems = kBM * kLds;  // per operand per buffer
+static_assert(kBK == 32 || kBK == 64, "tile K step");
+static_assert(kStages * kStageBytes <= 128 * 1024, "LDS budget");
+
+// LDS position of 16-byte chunk c of tile row r is c ^ swz(r): the 16-byte
+// fragment reads of 16 consecutive rows then fall in distinct bank groups
+// whether the LDS serves 8 lanes over 32 banks or 16 lanes over 64 banks.
+__device__ __forceinline__ int swz(int r) {
+  return kBK == 64 ? ((r & 7) ^ ((r >> 3) & 1)) : (((r >> 1) ^ (r >> 3)) & 3);
+}
+
+// Workgroup barrier for LDS: waits for this wave's LDS operations, then
+// s_barrier; the memory clobber keeps the compiler from moving memory accesses
+// across it.  Unlike __syncthreads() it does not wait for vector-memory loads.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// s_waitcnt on vector-memory operations only (expcnt and lgkmcnt left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -83,7 +114,6 @@ __device__ bool find_tile(const int32_t *__restrict__ tokens_per_expert, const i
     run += local[i];
   }
   const int64_t total = part[kThreads - 1];
-  if (tid == 0) scratch[kMaxExperts] = total;
   __syncthreads();
 
   const int64_t bid = blockIdx.x;
@@ -113,121 +143,166 @@ __device__ bool find_tile(const int32_t *__restrict__ tokens_per_expert, const i
 
 __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
 
-// kSwiGLU: B rows 0..63 are gate rows n0.., 64..127 are up rows I+n0..; output
-// the [rows, I] SwiGLU intermediate.  Otherwise a plain 128-column tile of y.
+__device__ __forceinline__ uint16_t bf16_bits(float v) { return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu); }
+
+// One K step of MFMAs on an LDS stage.  A fragment of rows
+// (wm*128 + mi*32 + l%32), k-chunk 2*ks + l/32; B likewise on its rows.
 template <bool kSwiGLU>
-__global__ __launch_bounds__(kThreads, 2) void grouped_gemm_kernel(
+__device__ __forceinline__ void mma_stage(const char *__restrict__ stage, int wm, int wn, int l, f32x16 (&acc)[4][4]) {
+  const char *as = stage;
+  const char *bs = stage + kOperandBytes;
+  const int r32 = l & 31;
+  const int sw = swz(r32);  // every row this lane reads is r32 plus a multiple of 32
+#pragma unroll
+  for (int ks = 0; ks < kBK / 16; ++ks) {
+    const int pos = ((2 * ks + (l >> 5)) ^ sw) * 16;
+    bf16x8 b[4], a[4];
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) {
+      // SwiGLU: blocks 0,1 are gate columns wn*64 + ni*32, blocks 2,3 the matching up columns
+      const int brow = kSwiGLU ? ((ni >> 1) * (kBN / 2) + wn * 64 + (ni & 1) * 32 + r32) : (wn * 128 + ni * 32 + r32);
+      b[ni] = *reinterpret_cast<const bf16x8 *>(bs + brow * kRowBytes + pos);
+    }
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+      a[mi] = *reinterpret_cast<const bf16x8 *>(as + (wm * 128 + mi * 32 + r32) * kRowBytes + pos);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+  }
+}
+
+// kSwiGLU: B tile rows 0..127 are gate rows n0.., rows 128..255 the up rows
+// I+n0..; output the [rows, I] SwiGLU intermediate.  Otherwise a plain
+// 256-column tile of y.
+template <bool kSwiGLU>
+__global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int64_t b_expert_stride, int K, int N,
     int n_tiles, const int32_t *__restrict__ tokens_per_expert, const int32_t *__restrict__ expert_offsets, int e,
-    uint16_t *__restrict__ C, int64_t ldc, int inter) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * 2 * kTileElems];
+    uint16_t *__restrict__ C, int64_t ldc) {
+  // one object per stage, so the compiler can tell a stage being read from the
+  // stages the direct loads are still filling
+  __shared__ __attribute__((aligned(1024))) char lds0[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds1[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds2[kStageBytes];
+  __shared__ __attribute__((aligned(1024))) char lds3[kStageBytes];
   TileCoord tc;
-  if (!find_tile(tokens_per_expert, expert_offsets, e, n_tiles, reinterpret_cast<int64_t *>(lds), tc)) return;
+  if (!find_tile(tokens_per_expert, expert_offsets, e, n_tiles, reinterpret_cast<int64_t *>(lds0), tc)) return;
 
-  const int tid = threadIdx.x;
   const int l = lane_id();
-  const int w = tid / kWave;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wm = w >> 1, wn = w & 1;
-  const int n0 = tc.n_tile * (kSwiGLU ? kBN / 2 : kBN);
-  const uint16_t *Be = B + (int64_t)tc.e * b_expert_stride;
+  // tile coordinates are the same in every lane: keep them in scalar registers
+  const int te = __builtin_amdgcn_readfirstlane(tc.e);
+  const int n0 = __builtin_amdgcn_readfirstlane(tc.n_tile) * (kSwiGLU ? kBN / 2 : kBN);
+  const int64_t row0 = ((int64_t)__builtin_amdgcn_readfirstlane((int)(tc.row0 >> 32)) << 32) |
+                       (uint32_t)__builtin_amdgcn_readfirstlane((int)tc.row0);
+  const int rows_valid = __builtin_amdgcn_readfirstlane((int)(tc.row_end - tc.row0 < kBM ? tc.row_end - tc.row0 : kBM));
 
-  // global -> register staging: 4 x 16 B per operand per thread
-  const uint16_t *a_src[4];
-  const uint16_t *b_src[4];
-  int lds_off[4];
+  // 32-row MFMA blocks of this wave's 128-row half that hold rows of the segment
+  int valid = rows_valid - wm * 128;
+  valid = valid < 0 ? 0 : (valid > 128 ? 128 : valid);
+  const int mi_count = (valid + 31) / 32;
+
+  // direct-load sources: this wave fills tile rows w*64 .. w*64+63 of A and of
+  // B, kLoadRows rows per instruction; lane l writes LDS bytes l*16..l*16+15 of
+  // the instruction's block, i.e. row l / kChunks, position l % kChunks, so it
+  // fetches global chunk position ^ swz(row).  Addresses are a per-tile scalar
+  // base plus a 32-bit per-lane byte offset.
+  const char *a_base = reinterpret_cast<const char *>(A + row0 * K);
+  const char *b_base = reinterpret_cast<const char *>(B + (int64_t)te * b_expert_stride);
+  uint32_t a_off[kLoadsPerOperand], b_off[kLoadsPerOperand];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int v = tid + kThreads * p;
-    const int r = v >> 3, kc = v & 7;
-    int64_t ar = tc.row0 + r;
-    if (ar > tc.row_end - 1) ar = tc.row_end - 1;
-    a_src[p] = A + ar * K + kc * 8;
-    int64_t br;
-    if (kSwiGLU) br = r < kBN / 2 ? n0 + r : inter + n0 + (r - kBN / 2);
-    else br = n0 + r < N ? n0 + r : N - 1;
-    b_src[p] = Be + br * K + kc * 8;
-    lds_off[p] = r * kLds + kc * 8;
+  for (int i = 0; i < kLoadsPerOperand; ++i) {
+    const int r = w * 64 + i * kLoadRows + l / kChunks;
+    const int c = (l % kChunks) ^ swz(r);
+    const int ar = r < rows_valid ? r : rows_valid - 1;  // ragged tail: re-read the last row
+    a_off[i] = ((uint32_t)ar * (uint32_t)K + (uint32_t)(c * 8)) * 2u;
+    int br;
+    if (kSwiGLU) {
+      int col = n0 + (r & (kBN / 2 - 1));
+      if (col > N - 1) col = N - 1;  // N = I: up rows start at I
+      br = (r >= kBN / 2 ? N : 0) + col;
+    } else {
+      br = n0 + r < N ? n0 + r : N - 1;
+    }
+    b_off[i] = ((uint32_t)br * (uint32_t)K + (uint32_t)(c * 8)) * 2u;  // < 4*I*H bytes
   }
-  u32x4 ra[4], rb[4];
-  auto load_regs = [&](int k0) {
+  auto issue = [&](char *stage, int k0) {
+    const char *ab = a_base + 2 * k0;
+    const char *bb = b_base + 2 * k0;
+    char *dst = stage + w * 64 * kRowBytes;
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      ra[p] = ld16(a_src[p] + k0);
-      rb[p] = ld16(b_src[p] + k0);
-    }
-  };
-  auto store_lds = [&](int buf) {
-    uint16_t *as = lds + buf * 2 * kTileElems;
-    uint16_t *bs = as + kTileElems;
+    for (int i = 0; i < kLoadsPerOperand; ++i)
+      __builtin_amdgcn_global_load_lds(ab + a_off[i], dst + i * 1024, 16, 0, 0);
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      *reinterpret_cast<u32x4 *>(as + lds_off[p]) = ra[p];
-      *reinterpret_cast<u32x4 *>(bs + lds_off[p]) = rb[p];
-    }
+    for (int i = 0; i < kLoadsPerOperand; ++i)
+      __builtin_amdgcn_global_load_lds(bb + b_off[i], dst + kOperandBytes + i * 1024, 16, 0, 0);
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
+  // K loop: kStages - 1 steps in flight.  Before computing step kt a wave waits
+  // until at most the loads of the kStages - 2 younger steps are outstanding,
+  // then the barrier makes every wave's share visible and frees the buffer of
+  // step kt - 1, which receives step kt + kStages - 1.  The barrier orders LDS
+  // accesses only (a full workgroup fence would also wait for the loads in
+  // flight).  The loop is unrolled by kStages so each step names its buffers.
+  static_assert(kStages == 4, "the unrolled loop below names four stage buffers");
   const int KT = K / kBK;
-  load_regs(0);
-  store_lds(0);
-  __syncthreads();
-  const int frag_row = l & 31;
-  const int frag_k = (l >> 5) * 8;
-  for (int kt = 0; kt < KT; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < KT) load_regs((kt + 1) * kBK);
-    const uint16_t *as = lds + cur * 2 * kTileElems;
-    const uint16_t *bs = as + kTileElems;
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int kk = ks * 16 + frag_k;
-      bf16x8 a[2], b[2];
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-        a[mi] = *reinterpret_cast<const bf16x8 *>(as + (wm * 64 + mi * 32 + frag_row) * kLds + kk);
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni) {
-        // SwiGLU: ni = 0 gate columns wn*32.., ni = 1 the matching up columns
-        const int brow = kSwiGLU ? (ni * (kBN / 2) + wn * 32 + frag_row) : (wn * 64 + ni * 32 + frag_row);
-        b[ni] = *reinterpret_cast<const bf16x8 *>(bs + brow * kLds + kk);
-      }
-#pragma unroll
-      for (int mi = 0; mi < 2; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
-    }
-    if (kt + 1 < KT) store_lds(cur ^ 1);
-    __syncthreads();
+  if (0 < KT) issue(lds0, 0);
+  if (1 < KT) issue(lds1, kBK);
+  if (2 < KT) issue(lds2, 2 * kBK);
+#define MOE_K_STEP(CUR, NEXT, J)                                                        \
+  {                                                                                     \
+    const int kt = kt0 + (J);                                                           \
+    if (kt + kStages - 2 < KT) wait_vmcnt<(kStages - 2) * 2 * kLoadsPerOperand>();     \
+    else wait_vmcnt<0>();                                                               \
+    lds_barrier();                                                                      \
+    if (kt + kStages - 1 < KT) issue(NEXT, (kt + kStages - 1) * kBK);                   \
+    mma_stage<kSwiGLU>(CUR, wm, wn, l, acc);                                            \
   }
+  int kt0 = 0;
+  for (; kt0 + kStages <= KT; kt0 += kStages) {
+    MOE_K_STEP(lds0, lds3, 0)
+    MOE_K_STEP(lds1, lds0, 1)
+    MOE_K_STEP(lds2, lds1, 2)
+    MOE_K_STEP(lds3, lds2, 3)
+  }
+  if (kt0 < KT) MOE_K_STEP(lds0, lds3, 0)
+  if (kt0 + 1 < KT) MOE_K_STEP(lds1, lds0, 1)
+  if (kt0 + 2 < KT) MOE_K_STEP(lds2, lds1, 2)
+#undef MOE_K_STEP
 
   // epilogue: lane holds column (l & 31) of each 32x32 block, rows
   // 8*(q/4) + 4*(l/32) + q%4 for accumulator element q
   const int col_in = l & 31;
+  uint16_t *c_base = C + row0 * ldc;
 #pragma unroll
-  for (int mi = 0; mi < 2; ++mi) {
+  for (int mi = 0; mi < 4; ++mi) {
+    if (mi >= mi_count) continue;
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
-      const int rl = wm * 64 + mi * 32 + 8 * (q >> 2) + 4 * (l >> 5) + (q & 3);
-      const int64_t row = tc.row0 + rl;
-      if (row >= tc.row_end) continue;
+      const int row = wm * 128 + mi * 32 + 8 * (q >> 2) + 4 * (l >> 5) + (q & 3);
+      if (row >= rows_valid) continue;
       if (kSwiGLU) {
-        const int col = n0 + wn * 32 + col_in;
-        const float g = acc[mi][0][q], u = acc[mi][1][q];
-        const float a = silu_f(g) * u;
-        C[row * ldc + col] = (uint16_t)(pack_bf16x2(a, 0.0f) & 0xFFFFu);
-      } else {
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni) {
           const int col = n0 + wn * 64 + ni * 32 + col_in;
-          if (col < N) C[row * ldc + col] = (uint16_t)(pack_bf16x2(acc[mi][ni][q], 0.0f) & 0xFFFFu);
+          if (col < N) c_base[(int64_t)row * ldc + col] = bf16_bits(silu_f(acc[mi][ni][q]) * acc[mi][ni + 2][q]);
+        }
+      } else {
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          const int col = n0 + wn * 128 + ni * 32 + col_in;
+          if (col < N) c_base[(int64_t)row * ldc + col] = bf16_bits(acc[mi][ni][q]);
         }
       }
     }
@@ -254,18 +329,18 @@ hipError_t launch_expert_ffn(const uint16_t *x_perm, int64_t rows, int64_t hidde
                              hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   uint16_t *act = static_cast<uint16_t *>(workspace);
-  const int n1 = inter / (kBN / 2);
+  const int n1 = (inter + kBN / 2 - 1) / (kBN / 2);
   const int64_t g1 = tile_bound(rows, e, capacity, n1);
   hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3((unsigned)g1), dim3(kThreads), 0, stream, x_perm, w_gate_up,
                      (int64_t)2 * inter * hidden, (int)hidden, inter, n1, tokens_per_expert, expert_offsets, e, act,
-                     (int64_t)inter, inter);
+                     (int64_t)inter);
   hipError_t st = hipGetLastError();
   if (st != hipSuccess) return st;
   const int n2 = (int)((hidden + kBN - 1) / kBN);
   const int64_t g2 = tile_bound(rows, e, capacity, n2);
   hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3((unsigned)g2), dim3(kThreads), 0, stream, act, w_down,
                      (int64_t)hidden * inter, inter, (int)hidden, n2, tokens_per_expert, expert_offsets, e, y,
-                     hidden, inter);
+                     hidden);
   return hipGetLastError();
 }
 

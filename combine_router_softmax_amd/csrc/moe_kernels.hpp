@@ -13,7 +13,7 @@ hipError_t launch_route(const float *logits, int64_t n, int e, int k, int32_t *t
                         uint8_t *routing_map, int32_t *tokens_per_expert, hipStream_t stream);
 
 // ---- layout (moe_layout.hip)
-constexpr int kLayoutTile = 512;  // assignments per layout tile
+constexpr int kLayoutTile = 2048;  // assignments per layout tile
 inline int64_t layout_tiles(int64_t assignments) { return (assignments + kLayoutTile - 1) / kLayoutTile; }
 size_t layout_workspace_bytes(int64_t assignments, int e);
 hipError_t launch_layout(const int32_t *topk_idx, const float *topk_w, int64_t n, int k, int e, int capacity,

@@ -11,18 +11,25 @@
 //                   clipped to the row budget R
 //   assign_row[a] = offset[id[a]] + ordinal[a] if kept, else -1
 //
-// How (three launches, no host synchronisation, no atomics on the ordering
+// How (two launches, no host synchronisation, no atomics on the ordering
 // path, so the result does not depend on scheduling):
-//   1. layout_count: one workgroup per tile of 512 assignments builds an LDS
-//      histogram of the tile's ids -> tile_counts[tile][e].
-//   2. layout_scan: one workgroup turns tile_counts into per-expert exclusive
-//      prefixes over tiles (in place), totals, offsets and counters.
-//   3. layout_place: per tile, each wave walks its 64-assignment chunks in order;
+//   1. layout_count: one workgroup per tile of 2048 assignments builds an LDS
+//      histogram of the tile's ids -> tile_counts[tile][e] (a small matrix).
+//   2. layout_place: every workgroup reads the whole tile_counts matrix once (a
+//      single round of independent loads) and scans it in LDS: per expert, the
+//      sum over earlier tiles (this tile's base) and over all tiles (the
+//      expert's count); a block scan over experts gives the segment offsets.
+//      Then each wave walks its 64-assignment chunks of the tile in order;
 //      lanes holding the same expert find each other with one ballot per bit of
 //      the expert id (a wave64 "match"), rank = popcount(peers below the lane);
 //      the per-wave running count per expert lives in LDS and starts at the
-//      tile's prefix plus the counts of the earlier waves of the tile.  The same
-//      launch marks every row that receives no assignment (pad or tail).
+//      tile's base plus the counts of the earlier waves of the tile.  The same
+//      launch marks every row that receives no assignment (pad or tail), and
+//      workgroup 0 writes the counts, offsets and counters.
+// Re-scanning the count matrix in every workgroup replaces a separate scan
+// launch: the matrix is tiles x E ints (16 x 256 for 4096 tokens, top-8, 256
+// experts), and a dependent kernel-to-kernel round trip costs more than
+// re-reading it.
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
 
@@ -33,11 +40,54 @@ constexpr int kLayoutThreads = 256;
 constexpr int kLayoutWaves = kLayoutThreads / kWave;
 constexpr int kChunksPerWave = kLayoutTile / kLayoutThreads;  // 64-assignment chunks per wave
 static_assert(kLayoutTile % kLayoutThreads == 0, "tile must be a multiple of the block");
-constexpr int kScanThreads = 1024;
+constexpr int kMaxExperts = 1024;
 
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 __device__ __forceinline__ bool valid_id(int32_t x, int e) { return x >= 0 && x < e; }
+
+__device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
+  const int l = lane_id();
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int32_t o = __shfl_up(v, off, kWave);
+    if (l >= off) v += o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int32_t wave_sum_i32(int32_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Exclusive scan of in[0..n) (n <= 1024) into out[]; every thread of the block calls it.
+__device__ void block_exclusive_scan(const int32_t *in, int32_t *out, int n) {
+  __shared__ int32_t wave_tot[kLayoutWaves];
+  constexpr int kPer = kMaxExperts / kLayoutThreads;
+  const int t = threadIdx.x;
+  int32_t v[kPer];
+  int32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int x = t * kPer + i;
+    v[i] = x < n ? in[x] : 0;
+    s += v[i];
+  }
+  const int32_t incl = wave_incl_scan(s);
+  if (lane_id() == kWave - 1) wave_tot[t / kWave] = incl;
+  __syncthreads();
+  int32_t run = incl - s;
+  for (int w = 0; w < t / kWave; ++w) run += wave_tot[w];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int x = t * kPer + i;
+    if (x < n) out[x] = run;
+    run += v[i];
+  }
+  __syncthreads();
+}
 
 __global__ __launch_bounds__(kLayoutThreads) void layout_count(const int32_t *__restrict__ topk_idx, int64_t a_total,
                                                                int e, int32_t *__restrict__ tile_counts,
@@ -46,143 +96,171 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count(const int32_t *__
   for (int x = threadIdx.x; x <= e; x += kLayoutThreads) cnt[x] = 0;
   __syncthreads();
   const int64_t a0 = (int64_t)blockIdx.x * kLayoutTile;
-  for (int i = threadIdx.x; i < kLayoutTile; i += kLayoutThreads) {
-    const int64_t a = a0 + i;
-    if (a < a_total) {
-      const int32_t x = topk_idx[a];
-      if (valid_id(x, e)) atomicAdd(&cnt[x], 1);
-      else if (x != -1) atomicAdd(&cnt[e], 1);
-    }
+  int32_t ids[kChunksPerWave];
+#pragma unroll
+  for (int i = 0; i < kChunksPerWave; ++i) {
+    const int64_t a = a0 + threadIdx.x + i * kLayoutThreads;
+    ids[i] = a < a_total ? topk_idx[a] : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < kChunksPerWave; ++i) {
+    if (valid_id(ids[i], e)) atomicAdd(&cnt[ids[i]], 1);
+    else if (ids[i] != -1) atomicAdd(&cnt[e], 1);
   }
   __syncthreads();
   for (int x = threadIdx.x; x < e; x += kLayoutThreads) tile_counts[(int64_t)blockIdx.x * e + x] = cnt[x];
   if (threadIdx.x == 0) tile_invalid[blockIdx.x] = cnt[e];
 }
 
-// Thread (x, g) owns expert x and a contiguous group g of tiles; the group sums
-// are scanned in LDS, so every global load of the tile counts is independent.
-__global__ __launch_bounds__(kScanThreads) void layout_scan(int32_t *__restrict__ tile_counts,
-                                                            const int32_t *__restrict__ tile_invalid, int64_t tiles,
-                                                            int e, int groups, int capacity, int64_t rows,
-                                                            int32_t *__restrict__ tokens_per_expert,
-                                                            int32_t *__restrict__ expert_offsets,
-                                                            int32_t *__restrict__ counters) {
-  __shared__ int64_t scan[kScanThreads];    // per expert: inclusive scan of totals
-  __shared__ int32_t grp[kScanThreads];     // [groups][e] group sums, then group prefixes
-  __shared__ unsigned long long sums[3];    // kept, dropped, invalid
-  const int tid = threadIdx.x;
-  const int x = tid % e;
-  const int g = tid / e;
-  const bool active = g < groups;
-  const int64_t per_group = (tiles + groups - 1) / groups;
-  const int64_t t0 = (int64_t)g * per_group;
-  const int64_t t1 = t0 + per_group < tiles ? t0 + per_group : tiles;
-  if (tid < 3) sums[tid] = 0;
-  int32_t s = 0;
-  if (active)
-    for (int64_t t = t0; t < t1; ++t) s += tile_counts[t * e + x];
-  if (active) grp[g * e + x] = s;
-  __syncthreads();
-  int32_t prefix = 0;
-  int64_t total = 0;
-  if (active) {
-    for (int gg = 0; gg < groups; ++gg) {
-      const int32_t v = grp[gg * e + x];
-      if (gg < g) prefix += v;
-      total += v;
-    }
-  }
-  __syncthreads();
-  if (active) {  // per-expert exclusive prefix over tiles, in place
-    int32_t run = prefix;
-    for (int64_t t = t0; t < t1; t += 8) {
-      int32_t c[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) c[u] = t + u < t1 ? tile_counts[(t + u) * e + x] : 0;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (t + u < t1) {
-          tile_counts[(t + u) * e + x] = run;
-          run += c[u];
-        }
-    }
-  }
-  scan[tid] = (g == 0 && tid < e) ? total : 0;
-  __syncthreads();
-  for (int off = 1; off < kScanThreads; off <<= 1) {  // inclusive scan over experts
-    const int64_t v = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += v;
-    __syncthreads();
-  }
-  if (g == 0 && tid < e) {
-    int64_t start, kept;
-    if (capacity > 0) {
-      start = (int64_t)x * capacity;
-      kept = total < capacity ? total : capacity;
-    } else {
-      const int64_t excl = scan[x] - total;
-      const int64_t incl = scan[x];
-      start = excl < rows ? excl : rows;
-      kept = (incl < rows ? incl : rows) - start;
-    }
-    expert_offsets[x] = (int32_t)start;
-    if (x == e - 1) expert_offsets[e] = (int32_t)(capacity > 0 ? rows : (scan[x] < rows ? scan[x] : rows));
-    tokens_per_expert[x] = (int32_t)kept;
-    atomicAdd(&sums[0], (unsigned long long)kept);
-    atomicAdd(&sums[1], (unsigned long long)(total - kept));
-  }
-  for (int64_t t = tid; t < tiles; t += kScanThreads) atomicAdd(&sums[2], (unsigned long long)tile_invalid[t]);
-  __syncthreads();
-  if (tid == 0) {
-    counters[0] = (int32_t)sums[0];
-    counters[1] = (int32_t)sums[1];
-    counters[2] = capacity > 0 ? (int32_t)(rows - (int64_t)sums[0]) : 0;
-    counters[3] = (int32_t)sums[2];
-  }
-}
-
 __global__ __launch_bounds__(kLayoutThreads) void layout_place(
     const int32_t *__restrict__ topk_idx, const float *__restrict__ topk_w, int64_t a_total, int64_t tiles, int e,
-    int id_bits, int capacity, int64_t rows, const int32_t *__restrict__ tile_base,
-    const int32_t *__restrict__ expert_offsets, const int32_t *__restrict__ tokens_per_expert,
-    int32_t *__restrict__ ordinal, int32_t *__restrict__ assign_row, int32_t *__restrict__ row_src,
-    uint8_t *__restrict__ drop_mask, uint8_t *__restrict__ pad_mask, float *__restrict__ w_perm) {
+    int id_bits, int capacity, int64_t rows, const int32_t *__restrict__ tile_counts,
+    const int32_t *__restrict__ tile_invalid, int32_t *__restrict__ tokens_per_expert,
+    int32_t *__restrict__ expert_offsets, int32_t *__restrict__ counters, int32_t *__restrict__ ordinal,
+    int32_t *__restrict__ assign_row, int32_t *__restrict__ row_src, uint8_t *__restrict__ drop_mask,
+    uint8_t *__restrict__ pad_mask, float *__restrict__ w_perm) {
   extern __shared__ int32_t sm[];
-  int32_t *run = sm;                        // [waves][e] running per-expert count of each wave
-  int32_t *off = sm + kLayoutWaves * e;     // [e + 1]
-  int32_t *kept = off + e + 1;              // [e]
-  const int w = threadIdx.x / kWave;
+  int32_t *run = sm;                      // [waves][e] running per-expert count of each wave
+  int32_t *off = run + kLayoutWaves * e;  // [e + 1] segment starts
+  int32_t *kept = off + e + 1;            // [e]
+  int32_t *base = kept + e;               // [e] this tile's base (counts of earlier tiles)
+  int32_t *total = base + e;              // [e] expert counts over all tiles
+  __shared__ int32_t part[2][kLayoutThreads];
+  __shared__ int32_t red[3][kLayoutWaves];
+  const int tid = threadIdx.x;
+  const int w = tid / kWave;
   const int l = lane_id();
   const int64_t tile = blockIdx.x;
 
-  for (int x = threadIdx.x; x < e; x += kLayoutThreads) {
-    off[x] = expert_offsets[x];
-    kept[x] = tokens_per_expert[x];
+  // ---- per-expert sums over tiles: before this tile, and over all tiles
+  if (e <= kLayoutThreads) {
+    // thread (g, x): expert x, tiles g, g+G, g+2G, ...  (G groups of e threads)
+    const int groups = kLayoutThreads / e;
+    const int g = tid / e, x = tid % e;
+    if (g < groups) {
+      int32_t before = 0, all = 0;
+      for (int64_t t0 = g; t0 < tiles; t0 += 16 * (int64_t)groups) {
+        int32_t c[16];
 #pragma unroll
-    for (int ww = 0; ww < kLayoutWaves; ++ww) run[ww * e + x] = 0;
+        for (int u = 0; u < 16; ++u) {
+          const int64_t t = t0 + (int64_t)u * groups;
+          c[u] = t < tiles ? tile_counts[t * e + x] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          all += c[u];
+          if (t0 + (int64_t)u * groups < tile) before += c[u];
+        }
+      }
+      part[0][tid] = before;
+      part[1][tid] = all;
+    }
+    __syncthreads();
+    if (tid < e) {
+      int32_t b = 0, a = 0;
+      for (int gg = 0; gg < groups; ++gg) {
+        b += part[0][gg * e + tid];
+        a += part[1][gg * e + tid];
+      }
+      base[tid] = b;
+      total[tid] = a;
+    }
+  } else {
+    for (int x = tid; x < e; x += kLayoutThreads) {
+      int32_t before = 0, all = 0;
+      for (int64_t t0 = 0; t0 < tiles; t0 += 16) {
+        int32_t c[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) c[u] = t0 + u < tiles ? tile_counts[(t0 + u) * e + x] : 0;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          all += c[u];
+          if (t0 + u < tile) before += c[u];
+        }
+      }
+      base[x] = before;
+      total[x] = all;
+    }
   }
-  if (threadIdx.x == 0) off[e] = expert_offsets[e];
   __syncthreads();
 
+  // ---- segment offsets and kept counts
+  if (capacity > 0) {
+    for (int x = tid; x < e; x += kLayoutThreads) {
+      off[x] = x * capacity;
+      kept[x] = total[x] < capacity ? total[x] : capacity;
+    }
+    if (tid == 0) off[e] = (int32_t)rows;
+    __syncthreads();
+  } else {
+    block_exclusive_scan(total, off, e);
+    for (int x = tid; x < e; x += kLayoutThreads) {
+      const int64_t s0 = off[x] < rows ? off[x] : rows;
+      const int64_t s1 = (int64_t)off[x] + total[x];
+      kept[x] = (int32_t)((s1 < rows ? s1 : rows) - s0);
+    }
+    __syncthreads();
+    for (int x = tid; x < e; x += kLayoutThreads) off[x] = off[x] < rows ? off[x] : (int32_t)rows;
+    __syncthreads();
+    if (tid == 0) off[e] = off[e - 1] + kept[e - 1];
+    __syncthreads();
+  }
+
+  if (blockIdx.x == 0) {  // the expert counts, offsets and counters
+    int32_t k_sum = 0, t_sum = 0, inv = 0;
+    for (int x = tid; x < e; x += kLayoutThreads) {
+      tokens_per_expert[x] = kept[x];
+      expert_offsets[x] = off[x];
+      k_sum += kept[x];
+      t_sum += total[x];
+    }
+    if (tid == 0) expert_offsets[e] = off[e];
+    for (int64_t t = tid; t < tiles; t += kLayoutThreads) inv += tile_invalid[t];
+    k_sum = wave_sum_i32(k_sum);
+    t_sum = wave_sum_i32(t_sum);
+    inv = wave_sum_i32(inv);
+    if (l == 0) {
+      red[0][w] = k_sum;
+      red[1][w] = t_sum;
+      red[2][w] = inv;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int32_t ks = 0, ts = 0, is = 0;
+      for (int ww = 0; ww < kLayoutWaves; ++ww) {
+        ks += red[0][ww];
+        ts += red[1][ww];
+        is += red[2][ww];
+      }
+      counters[0] = ks;
+      counters[1] = ts - ks;
+      counters[2] = capacity > 0 ? (int32_t)(rows - ks) : 0;
+      counters[3] = is;
+    }
+  }
+
   if (tile < tiles) {  // block-uniform
+    for (int x = tid; x < kLayoutWaves * e; x += kLayoutThreads) run[x] = 0;
+    __syncthreads();
     const int64_t a_wave = tile * kLayoutTile + (int64_t)w * kChunksPerWave * kWave;
     int32_t ids[kChunksPerWave];
 #pragma unroll
     for (int c = 0; c < kChunksPerWave; ++c) {
       const int64_t a = a_wave + c * kWave + l;
       ids[c] = a < a_total ? topk_idx[a] : -1;
-      if (valid_id(ids[c], e)) atomicAdd(&run[w * e + ids[c]], 1);
     }
+#pragma unroll
+    for (int c = 0; c < kChunksPerWave; ++c)
+      if (valid_id(ids[c], e)) atomicAdd(&run[w * e + ids[c]], 1);
     __syncthreads();
     // exclusive prefix over the waves of this tile, on top of the tile's base
-    for (int x = threadIdx.x; x < e; x += kLayoutThreads) {
-      int32_t base = tile_base[tile * e + x];
+    for (int x = tid; x < e; x += kLayoutThreads) {
+      int32_t b = base[x];
 #pragma unroll
       for (int ww = 0; ww < kLayoutWaves; ++ww) {
         const int32_t c = run[ww * e + x];
-        run[ww * e + x] = base;
-        base += c;
+        run[ww * e + x] = b;
+        b += c;
       }
     }
     __syncthreads();
@@ -200,9 +278,9 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place(
       }
       if (valid) {
         const int rank = __popcll(peers & below);
-        const int32_t base = run[w * e + x];
-        if (rank == 0) run[w * e + x] = base + __popcll(peers);
-        const int32_t o = base + rank;
+        const int32_t b = run[w * e + x];
+        if (rank == 0) run[w * e + x] = b + __popcll(peers);
+        const int32_t o = b + rank;
         ordinal[a] = o;
         if (o < kept[x]) {
           const int32_t r = off[x] + o;
@@ -225,8 +303,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place(
   }
 
   // rows that receive no assignment: capacity pads and the unused dropless tail
-  for (int64_t r = (int64_t)blockIdx.x * kLayoutThreads + threadIdx.x; r < rows;
-       r += (int64_t)gridDim.x * kLayoutThreads) {
+  for (int64_t r = (int64_t)blockIdx.x * kLayoutThreads + tid; r < rows; r += (int64_t)gridDim.x * kLayoutThreads) {
     int x;
     if (capacity > 0) {
       x = (int)(r / capacity);
@@ -268,22 +345,15 @@ hipError_t launch_layout(const int32_t *topk_idx, const float *topk_w, int64_t n
     hipError_t st = hipGetLastError();
     if (st != hipSuccess) return st;
   }
-  int groups = kScanThreads / e;
-  if (groups > 64) groups = 64;
-  if (groups > tiles) groups = tiles > 0 ? (int)tiles : 1;
-  hipLaunchKernelGGL(layout_scan, dim3(1), dim3(kScanThreads), 0, stream, tile_counts, tile_invalid, tiles, e,
-                     groups, capacity, rows, tokens_per_expert, expert_offsets, counters);
-  hipError_t st = hipGetLastError();
-  if (st != hipSuccess) return st;
   int64_t row_blocks = (rows + kLayoutThreads - 1) / kLayoutThreads;
-  if (row_blocks > 1024) row_blocks = 1024;
-  const int64_t blocks = tiles > row_blocks ? tiles : row_blocks;
-  if (blocks == 0) return hipSuccess;
+  if (row_blocks > 256) row_blocks = 256;
+  int64_t blocks = tiles > row_blocks ? tiles : row_blocks;
+  if (blocks == 0) blocks = 1;  // workgroup 0 still writes counts, offsets and counters
   const int id_bits = e <= 1 ? 0 : 32 - __builtin_clz((unsigned)(e - 1));
-  const size_t lds = sizeof(int32_t) * ((size_t)kLayoutWaves * e + 2 * (size_t)e + 1);
+  const size_t lds = sizeof(int32_t) * ((size_t)kLayoutWaves * e + 4 * (size_t)e + 1);
   hipLaunchKernelGGL(layout_place, dim3((unsigned)blocks), dim3(kLayoutThreads), lds, stream, topk_idx, topk_w,
-                     a_total, tiles, e, id_bits, capacity, rows, tile_counts, expert_offsets, tokens_per_expert,
-                     ordinal, assign_row, row_src, drop_mask, pad_mask, w_perm);
+                     a_total, tiles, e, id_bits, capacity, rows, tile_counts, tile_invalid, tokens_per_expert,
+                     expert_offsets, counters, ordinal, assign_row, row_src, drop_mask, pad_mask, w_perm);
   return hipGetLastError();
 }
 

@@ -10,8 +10,10 @@
 // wave max-reduction select the top-k in order; the chosen key is zeroed.
 // Weights use the identity softmax(l)[i] / sum_chosen softmax(l) =
 // exp(l_i - l_max) / sum_chosen exp(l_j - l_max), with l_max the slot-0 logit.
-// Counts go through an LDS histogram per block, then global atomics (integer
-// adds commute, so the counts are exact and order-independent).
+// Counts: when the routing map is written (E % 16 == 0), a second kernel takes
+// its column sums in a few dozen workgroups, one global atomic per expert and
+// workgroup; otherwise each router workgroup adds its LDS histogram with global
+// atomics.  Integer adds commute, so the counts are exact either way.
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
 
@@ -40,13 +42,51 @@ __global__ void fill_i32(int32_t *p, int64_t n, int32_t v) {
   if (i < n) p[i] = v;
 }
 
+// Column sums of the [N, E] uint8 routing map (E % 16 == 0, 16-byte rows): a
+// thread owns one 16-byte column slice and a strided set of rows of the block's
+// row range; a few dozen workgroups each add their partial counts with one
+// atomic per expert, which keeps same-address atomic traffic small.
+__global__ __launch_bounds__(kRouteThreads) void count_map_kernel(const uint8_t *__restrict__ routing_map, int64_t n,
+                                                                  int e, int64_t rows_per_block,
+                                                                  int32_t *__restrict__ tokens_per_expert) {
+  extern __shared__ int32_t red[];  // [e]
+  const int vpr = e / 16;
+  const int row_lanes = kRouteThreads / vpr;
+  const int v = threadIdx.x % vpr;
+  const int rl = threadIdx.x / vpr;
+  for (int x = threadIdx.x; x < e; x += kRouteThreads) red[x] = 0;
+  __syncthreads();
+  const int64_t r0 = (int64_t)blockIdx.x * rows_per_block;
+  const int64_t r1 = r0 + rows_per_block < n ? r0 + rows_per_block : n;
+  if (rl < row_lanes) {
+    uint32_t c[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) c[i] = 0;
+    for (int64_t r = r0 + rl; r < r1; r += row_lanes) {
+      const u32x4 m = ld16(routing_map + r * e + v * 16);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) c[i] += (m[i / 4] >> (8 * (i % 4))) & 0xFFu;
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      if (c[i]) atomicAdd(&red[v * 16 + i], (int32_t)c[i]);
+  }
+  __syncthreads();
+  for (int x = threadIdx.x; x < e; x += kRouteThreads)
+    if (red[x]) atomicAdd(&tokens_per_expert[x], red[x]);
+}
+
 template <int VPL>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float *__restrict__ logits, int64_t n, int e,
                                                               int k, int32_t *__restrict__ topk_idx,
                                                               float *__restrict__ topk_w,
                                                               uint8_t *__restrict__ routing_map,
-                                                              int32_t *__restrict__ tokens_per_expert) {
+                                                              int32_t *__restrict__ tokens_per_expert,
+                                                              int32_t *__restrict__ zero_counts) {
   extern __shared__ uint32_t smem[];
+  // counts taken later from the routing map start from zero (a later launch adds them)
+  if (zero_counts && blockIdx.x == 0)
+    for (int x = threadIdx.x; x < e; x += kRouteThreads) zero_counts[x] = 0;
   const int w = threadIdx.x / kWave;
   const int l = lane_id();
   uint32_t *sel_key = smem + w * k;                                        // [4][k]
@@ -116,11 +156,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float *__res
 
 template <int VPL>
 hipError_t launch_route_vpl(const float *logits, int64_t n, int e, int k, int32_t *topk_idx, float *topk_w,
-                            uint8_t *routing_map, int32_t *tokens_per_expert, hipStream_t stream) {
+                            uint8_t *routing_map, int32_t *tokens_per_expert, int32_t *zero_counts,
+                            hipStream_t stream) {
   const int64_t blocks = (n + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock;
   const size_t lds = sizeof(uint32_t) * (2 * kRouteTokensPerBlock * (size_t)k + (size_t)e);
   hipLaunchKernelGGL(route_kernel<VPL>, dim3((unsigned)blocks), dim3(kRouteThreads), lds, stream, logits, n, e, k,
-                     topk_idx, topk_w, routing_map, tokens_per_expert);
+                     topk_idx, topk_w, routing_map, tokens_per_expert, zero_counts);
   return hipGetLastError();
 }
 
@@ -128,18 +169,33 @@ hipError_t launch_route_vpl(const float *logits, int64_t n, int e, int k, int32_
 
 hipError_t launch_route(const float *logits, int64_t n, int e, int k, int32_t *topk_idx, float *topk_w,
                         uint8_t *routing_map, int32_t *tokens_per_expert, hipStream_t stream) {
-  if (tokens_per_expert) {
+  const bool map_counts = n > 0 && tokens_per_expert && routing_map && e % 16 == 0 &&
+                          (reinterpret_cast<uintptr_t>(routing_map) & 15u) == 0;
+  if (tokens_per_expert && !map_counts) {  // the router kernel adds into zeroed counts
     hipLaunchKernelGGL(fill_i32, dim3((unsigned)((e + 255) / 256)), dim3(256), 0, stream, tokens_per_expert,
                        (int64_t)e, 0);
     hipError_t st = hipGetLastError();
     if (st != hipSuccess) return st;
   }
   if (n == 0) return hipSuccess;
-  if (e <= 64) return launch_route_vpl<1>(logits, n, e, k, topk_idx, topk_w, routing_map, tokens_per_expert, stream);
-  if (e <= 128) return launch_route_vpl<2>(logits, n, e, k, topk_idx, topk_w, routing_map, tokens_per_expert, stream);
-  if (e <= 256) return launch_route_vpl<4>(logits, n, e, k, topk_idx, topk_w, routing_map, tokens_per_expert, stream);
-  if (e <= 512) return launch_route_vpl<8>(logits, n, e, k, topk_idx, topk_w, routing_map, tokens_per_expert, stream);
-  return launch_route_vpl<16>(logits, n, e, k, topk_idx, topk_w, routing_map, tokens_per_expert, stream);
+  int32_t *kernel_counts = map_counts ? nullptr : tokens_per_expert;
+  int32_t *zero_counts = map_counts ? tokens_per_expert : nullptr;
+  hipError_t st;
+#define MOE_ROUTE(V) \
+  launch_route_vpl<V>(logits, n, e, k, topk_idx, topk_w, routing_map, kernel_counts, zero_counts, stream)
+  if (e <= 64) st = MOE_ROUTE(1);
+  else if (e <= 128) st = MOE_ROUTE(2);
+  else if (e <= 256) st = MOE_ROUTE(4);
+  else if (e <= 512) st = MOE_ROUTE(8);
+  else st = MOE_ROUTE(16);
+#undef MOE_ROUTE
+  if (st != hipSuccess || !map_counts) return st;
+  int64_t blocks = (n + 63) / 64;
+  if (blocks > 32) blocks = 32;
+  const int64_t rows_per_block = (n + blocks - 1) / blocks;
+  hipLaunchKernelGGL(count_map_kernel, dim3((unsigned)blocks), dim3(kRouteThreads), sizeof(int32_t) * e, stream,
+                     routing_map, n, e, rows_per_block, tokens_per_expert);
+  return hipGetLastError();
 }
 
 }  // namespace moe

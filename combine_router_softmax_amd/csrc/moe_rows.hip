@@ -17,7 +17,10 @@
 // slot order j = 0..k-1, then rounds once.  Capacity pad rows are zero-filled
 // by extra workgroups placed after the token workgroups.  Slots are handled in
 // chunks of KC (compile-time) so the k row indices and weights of a chunk stay
-// in scalar registers and the chunk's k loads are in flight together.
+// in scalar registers and the chunk's k loads are in flight together.  Rows
+// written, and the expert rows the combines read, are touched once per call and
+// use non-temporal (streaming) accesses; the scatter's source rows use plain
+// loads, which measured faster for that 1-read / k-write pattern.
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
 
@@ -95,7 +98,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(const void *__rest
       }
 #pragma unroll
       for (int j = 0; j < KC; ++j)
-        if (rows[j] >= 0) vals[j] = ld16(row_ptr(y, rows[j], row_bytes) + v * 16);
+        if (rows[j] >= 0) vals[j] = ld16_stream(row_ptr(y, rows[j], row_bytes) + v * 16);
 #pragma unroll
       for (int j = 0; j < KC; ++j) {
         if (rows[j] < 0) continue;
@@ -105,7 +108,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(const void *__rest
         for (int i = 0; i < EL; ++i) acc[i] = __builtin_fmaf(wts[j], f[i], acc[i]);
       }
     }
-    st16(dst + v * 16, V::pack(acc));
+    st16_stream(dst + v * 16, V::pack(acc));
   }
 }
 
@@ -137,11 +140,11 @@ __global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
     }
     for (int64_t v = threadIdx.x; v < vpr; v += kRowThreads) {
       float gf[EL];
-      V::unpack(ld16(g + v * 16), gf);
+      V::unpack(ld16_stream(g + v * 16), gf);
       u32x4 yv[KC];
 #pragma unroll
       for (int j = 0; j < KC; ++j)
-        if (rows[j] >= 0) yv[j] = ld16(row_ptr(y, rows[j], row_bytes) + v * 16);
+        if (rows[j] >= 0) yv[j] = ld16_stream(row_ptr(y, rows[j], row_bytes) + v * 16);
 #pragma unroll
       for (int j = 0; j < KC; ++j) {
         if (rows[j] < 0) continue;

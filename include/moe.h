@@ -150,7 +150,8 @@ moe_status moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_i
  *   y[r, c] = bf16( a[r] . w_down[e, c] )
  * bf16 operands, fp32 accumulation, no bias.  Rows outside the segments of y are
  * not written.  Shapes: x_perm bf16 [R, H]; w_gate_up bf16 [E, 2I, H] (gate rows
- * first); w_down bf16 [E, H, I]; y bf16 [R, H].  H and I must be multiples of 64.
+ * first); w_down bf16 [E, H, I]; y bf16 [R, H].  H and I must be multiples of 64
+ * and 4*I*H < 2^32 (one expert's weights are addressed with 32-bit offsets).
  * Workspace: moe_workspace_size(MOE_OP_EXPERT_FFN) (holds a [R, I] bf16). */
 moe_status moe_expert_ffn(const moe_shape *s, const void *x_perm, const moe_layout *layout,
                           const void *w_gate_up, const void *w_down, void *y, void *workspace,
