@@ -67,6 +67,23 @@ __device__ __forceinline__ int swz(int r) {
 // across it.  Unlike __syncthreads() it does not wait for vector-memory loads.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// 16 bytes per lane global -> LDS (global_load_lds_dwordx4): lane l's bytes land
+// at LDS address lds_addr + 16*l (lds_addr is wave-uniform, passed in M0).  The
+// instruction has no register result.  It is issued from inline asm so that the
+// compiler's memory-counter bookkeeping does not see it: the compiler cannot
+// tell which LDS stage such a load writes and would otherwise drain every load
+// in flight before reading any stage; the K loop below waits for these loads
+// itself with explicit vmcnt waits, and no other vector load is issued while
+// they are in flight.
+__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(gptr)
+               : "memory", "m0");
+}
+
+// LDS byte address of a pointer into a __shared__ array (the low 32 bits of its
+// flat address).
+__device__ __forceinline__ uint32_t lds_address(const void *p) { return (uint32_t)reinterpret_cast<uintptr_t>(p); }
+
 // s_waitcnt on vector-memory operations only (expcnt and lgkmcnt left at their maxima).
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -145,32 +162,48 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)
 
 __device__ __forceinline__ uint16_t bf16_bits(float v) { return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu); }
 
-// One K step of MFMAs on an LDS stage.  A fragment of rows
-// (wm*128 + mi*32 + l%32), k-chunk 2*ks + l/32; B likewise on its rows.
+// Fragments of one 16-wide K slice: A rows (wm*128 + mi*32 + l%32), B rows
+// likewise, k-chunk 2*ks + l/32.
 template <bool kSwiGLU>
-__device__ __forceinline__ void mma_stage(const char *__restrict__ stage, int wm, int wn, int l, f32x16 (&acc)[4][4]) {
+__device__ __forceinline__ void load_frags(const char *__restrict__ stage, int ks, int wm, int wn, int l,
+                                           bf16x8 (&a)[4], bf16x8 (&b)[4]) {
   const char *as = stage;
   const char *bs = stage + kOperandBytes;
   const int r32 = l & 31;
-  const int sw = swz(r32);  // every row this lane reads is r32 plus a multiple of 32
+  const int pos = ((2 * ks + (l >> 5)) ^ swz(r32)) * 16;  // every row read is r32 plus a multiple of 32
 #pragma unroll
-  for (int ks = 0; ks < kBK / 16; ++ks) {
-    const int pos = ((2 * ks + (l >> 5)) ^ sw) * 16;
-    bf16x8 b[4], a[4];
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      // SwiGLU: blocks 0,1 are gate columns wn*64 + ni*32, blocks 2,3 the matching up columns
-      const int brow = kSwiGLU ? ((ni >> 1) * (kBN / 2) + wn * 64 + (ni & 1) * 32 + r32) : (wn * 128 + ni * 32 + r32);
-      b[ni] = *reinterpret_cast<const bf16x8 *>(bs + brow * kRowBytes + pos);
-    }
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-      a[mi] = *reinterpret_cast<const bf16x8 *>(as + (wm * 128 + mi * 32 + r32) * kRowBytes + pos);
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mi], b[ni], acc[mi][ni], 0, 0, 0);
+  for (int ni = 0; ni < 4; ++ni) {
+    // SwiGLU: blocks 0,1 are gate columns wn*64 + ni*32, blocks 2,3 the matching up columns
+    const int brow = kSwiGLU ? ((ni >> 1) * (kBN / 2) + wn * 64 + (ni & 1) * 32 + r32) : (wn * 128 + ni * 32 + r32);
+    b[ni] = *reinterpret_cast<const bf16x8 *>(bs + brow * kRowBytes + pos);
   }
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+    a[mi] = *reinterpret_cast<const bf16x8 *>(as + (wm * 128 + mi * 32 + r32) * kRowBytes + pos);
+}
+
+// The 16 MFMAs of one 16-wide K slice.  The weight fragment is the MFMA's
+// first operand, so block (mi, ni) of the result holds, in lane l, activation
+// row mi*32 + l%32 and output features ni*32 + 8*(q/4) + 4*(l/32) + q%4 for
+// accumulator element q: four consecutive features per group of four elements.
+__device__ __forceinline__ void mfma_slice(const bf16x8 (&a)[4], const bf16x8 (&b)[4], f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[ni], a[mi], acc[mi][ni], 0, 0, 0);
+}
+
+// Instruction order for a region holding the 8 fragment reads of the next
+// slice and the 16 MFMAs of the current one: reads and MFMAs one-to-one, then
+// the remaining 8 MFMAs.  The reads' latency hides behind the MFMAs.
+__device__ __forceinline__ void pin_reads_under_mfmas() {
+  constexpr int kDsRead = 0x100, kMfma = 0x008;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+  }
+  __builtin_amdgcn_sched_group_barrier(kMfma, 8, 0);
 }
 
 // kSwiGLU: B tile rows 0..127 are gate rows n0.., rows 128..255 the up rows
@@ -232,13 +265,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   auto issue = [&](char *stage, int k0) {
     const char *ab = a_base + 2 * k0;
     const char *bb = b_base + 2 * k0;
-    char *dst = stage + w * 64 * kRowBytes;
+    const uint32_t dst = lds_address(stage) + w * 64 * kRowBytes;
 #pragma unroll
-    for (int i = 0; i < kLoadsPerOperand; ++i)
-      __builtin_amdgcn_global_load_lds(ab + a_off[i], dst + i * 1024, 16, 0, 0);
+    for (int i = 0; i < kLoadsPerOperand; ++i) dma16(ab + a_off[i], dst + i * 1024);
 #pragma unroll
-    for (int i = 0; i < kLoadsPerOperand; ++i)
-      __builtin_amdgcn_global_load_lds(bb + b_off[i], dst + kOperandBytes + i * 1024, 16, 0, 0);
+    for (int i = 0; i < kLoadsPerOperand; ++i) dma16(bb + b_off[i], dst + kOperandBytes + i * 1024);
   };
 
   f32x16 acc[4][4];
@@ -249,63 +280,113 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  // K loop: kStages - 1 steps in flight.  Before computing step kt a wave waits
-  // until at most the loads of the kStages - 2 younger steps are outstanding,
-  // then the barrier makes every wave's share visible and frees the buffer of
-  // step kt - 1, which receives step kt + kStages - 1.  The barrier orders LDS
-  // accesses only (a full workgroup fence would also wait for the loads in
-  // flight).  The loop is unrolled by kStages so each step names its buffers.
+  // K loop over a ring of kStages LDS buffers, kStages K steps in flight.
+  // Step kt multiplies stage kt slice by slice, reading the fragments of slice
+  // ks+1 while the MFMAs of slice ks run.  Before its last slice it waits for
+  // its own loads of stage kt+1 (at most the kStages-2 younger stages left in
+  // flight), passes a barrier -- after which every wave's loads of stage kt+1
+  // are visible and nobody reads stage kt any more -- refills the buffer of
+  // stage kt with stage kt+kStages, and reads slice 0 of stage kt+1 under the
+  // MFMAs of its last slice.  So no LDS read latency is exposed.  The barrier
+  // orders LDS accesses only (a full workgroup fence would also wait for the
+  // loads in flight).  The loop is unrolled by kStages so every step names its
+  // buffers at compile time.
   static_assert(kStages == 4, "the unrolled loop below names four stage buffers");
+  constexpr int kSlices = kBK / 16;
+  static_assert(kSlices % 2 == 0, "slice fragments alternate between two register sets");
+  constexpr int kLoadsPerStage = 2 * kLoadsPerOperand;
   const int KT = K / kBK;
+  bf16x8 fa[2][4], fb[2][4];
   if (0 < KT) issue(lds0, 0);
   if (1 < KT) issue(lds1, kBK);
   if (2 < KT) issue(lds2, 2 * kBK);
-#define MOE_K_STEP(CUR, NEXT, J)                                                        \
-  {                                                                                     \
-    const int kt = kt0 + (J);                                                           \
-    if (kt + kStages - 2 < KT) wait_vmcnt<(kStages - 2) * 2 * kLoadsPerOperand>();     \
-    else wait_vmcnt<0>();                                                               \
-    lds_barrier();                                                                      \
-    if (kt + kStages - 1 < KT) issue(NEXT, (kt + kStages - 1) * kBK);                   \
-    mma_stage<kSwiGLU>(CUR, wm, wn, l, acc);                                            \
+  if (3 < KT) issue(lds3, 3 * kBK);
+  if (KT >= kStages) wait_vmcnt<(kStages - 1) * kLoadsPerStage>();
+  else wait_vmcnt<0>();
+  lds_barrier();
+  load_frags<kSwiGLU>(lds0, 0, wm, wn, l, fa[0], fb[0]);
+#define MOE_K_STEP(CUR, NXT, J)                                                              \
+  {                                                                                          \
+    const int kt = kt0 + (J);                                                                \
+    _Pragma("unroll") for (int ks = 0; ks + 1 < kSlices; ++ks) {                             \
+      load_frags<kSwiGLU>(CUR, ks + 1, wm, wn, l, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);       \
+      mfma_slice(fa[ks & 1], fb[ks & 1], acc);                                               \
+      pin_reads_under_mfmas();                                                               \
+      __builtin_amdgcn_sched_barrier(0);                                                     \
+    }                                                                                        \
+    if (kt + kStages - 1 < KT) wait_vmcnt<(kStages - 2) * kLoadsPerStage>();                 \
+    else wait_vmcnt<0>();                                                                    \
+    lds_barrier();                                                                           \
+    if (kt + kStages < KT) issue(CUR, (kt + kStages) * kBK);                                 \
+    __builtin_amdgcn_sched_barrier(0);                                                       \
+    load_frags<kSwiGLU>(NXT, 0, wm, wn, l, fa[0], fb[0]);                                    \
+    mfma_slice(fa[(kSlices - 1) & 1], fb[(kSlices - 1) & 1], acc);                           \
+    pin_reads_under_mfmas();                                                                 \
+    __builtin_amdgcn_sched_barrier(0);                                                       \
   }
   int kt0 = 0;
   for (; kt0 + kStages <= KT; kt0 += kStages) {
-    MOE_K_STEP(lds0, lds3, 0)
-    MOE_K_STEP(lds1, lds0, 1)
-    MOE_K_STEP(lds2, lds1, 2)
-    MOE_K_STEP(lds3, lds2, 3)
+    MOE_K_STEP(lds0, lds1, 0)
+    MOE_K_STEP(lds1, lds2, 1)
+    MOE_K_STEP(lds2, lds3, 2)
+    MOE_K_STEP(lds3, lds0, 3)
   }
-  if (kt0 < KT) MOE_K_STEP(lds0, lds3, 0)
-  if (kt0 + 1 < KT) MOE_K_STEP(lds1, lds0, 1)
-  if (kt0 + 2 < KT) MOE_K_STEP(lds2, lds1, 2)
+  if (kt0 < KT) MOE_K_STEP(lds0, lds1, 0)
+  if (kt0 + 1 < KT) MOE_K_STEP(lds1, lds2, 1)
+  if (kt0 + 2 < KT) MOE_K_STEP(lds2, lds3, 2)
 #undef MOE_K_STEP
+  wait_vmcnt<0>();  // no direct load may still be writing LDS when the wave ends
 
-  // epilogue: lane holds column (l & 31) of each 32x32 block, rows
-  // 8*(q/4) + 4*(l/32) + q%4 for accumulator element q
-  const int col_in = l & 31;
-  uint16_t *c_base = C + row0 * ldc;
+  // epilogue: every real LDS read is done (the last barrier has passed), so
+  // each wave stages its bf16 sub-tile in its own LDS buffer -- 128 rows x
+  // (64 SwiGLU features or 128 output columns), 16-byte chunks XOR-swizzled by
+  // row -- and writes it out as whole rows of 16-byte stores.
+  constexpr int kCols = kSwiGLU ? 64 : 128;     // output columns of this wave
+  constexpr int kPitch = kCols * 2;             // LDS bytes per staged row
+  constexpr int kChunksPerRow = kPitch / 16;
+  static_assert(128 * kPitch <= kStageBytes, "staging fits one stage buffer");
+  auto out_pos = [](int r, int c) {             // LDS chunk position of chunk c of staged row r
+    return kChunksPerRow == 16 ? (c ^ (r & 15)) : (c ^ ((r & 7) ^ ((r >> 3) & 1)));
+  };
+  char *stage = w == 0 ? lds0 : (w == 1 ? lds1 : (w == 2 ? lds2 : lds3));
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
-    if (mi >= mi_count) continue;
+    const int r = mi * 32 + (l & 31);
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int row = wm * 128 + mi * 32 + 8 * (q >> 2) + 4 * (l >> 5) + (q & 3);
-      if (row >= rows_valid) continue;
+    for (int g = 0; g < 4; ++g) {
       if (kSwiGLU) {
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni) {
-          const int col = n0 + wn * 64 + ni * 32 + col_in;
-          if (col < N) c_base[(int64_t)row * ldc + col] = bf16_bits(silu_f(acc[mi][ni][q]) * acc[mi][ni + 2][q]);
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = silu_f(acc[mi][ni][4 * g + i]) * acc[mi][ni + 2][4 * g + i];
+          const int f = ni * 32 + 8 * g + 4 * (l >> 5);
+          *reinterpret_cast<uint2 *>(stage + r * kPitch + out_pos(r, f >> 3) * 16 + (f & 7) * 2) =
+              make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
       } else {
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
-          const int col = n0 + wn * 128 + ni * 32 + col_in;
-          if (col < N) c_base[(int64_t)row * ldc + col] = bf16_bits(acc[mi][ni][q]);
+          const f32x16 &c = acc[mi][ni];
+          const int f = ni * 32 + 8 * g + 4 * (l >> 5);
+          *reinterpret_cast<uint2 *>(stage + r * kPitch + out_pos(r, f >> 3) * 16 + (f & 7) * 2) =
+              make_uint2(pack_bf16x2(c[4 * g], c[4 * g + 1]), pack_bf16x2(c[4 * g + 2], c[4 * g + 3]));
         }
       }
     }
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+  __builtin_amdgcn_wave_barrier();
+  constexpr int kRowsPerPass = kWave / kChunksPerRow;
+  const int col0 = n0 + wn * kCols;
+  uint16_t *c_base = C + row0 * ldc;
+  const int ch = l % kChunksPerRow;
+#pragma unroll 4
+  for (int r = l / kChunksPerRow; r < 128; r += kRowsPerPass) {
+    const int row = wm * 128 + r;
+    const int col = col0 + ch * 8;
+    const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * kPitch + out_pos(r, ch) * 16);
+    if (row < rows_valid && col < N) st16(c_base + (int64_t)row * ldc + col, v);
   }
 }
 
