@@ -102,7 +102,17 @@ def bench_dispatch_combine(moe, mi, torch, steps, warmup):
     torch.cuda.synchronize()
     bwd_ms = b0.elapsed_time(b1) / steps
     bwd_bytes = n * row_b + kept * row_b * 2
-    return dict(total_ms=total_ms, route_ms=route_ms, dispatch_ms=disp_ms, combine_ms=comb_ms, kept=kept,
+    # the roofline kernel alone: back-to-back combine launches on the stream
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(steps):
+        moe.moe_combine(xp, r.topk_w, lay, out=out)
+    c1.record()
+    torch.cuda.synchronize()
+    comb_kernel_ms = c0.elapsed_time(c1) / steps
+    return dict(total_ms=total_ms, route_ms=route_ms, dispatch_ms=disp_ms, combine_ms=comb_ms,
+                comb_kernel_ms=comb_kernel_ms, kept=kept,
                 dispatch_bytes=dispatch_bytes, combine_bytes=combine_bytes, bwd_ms=bwd_ms, bwd_bytes=bwd_bytes,
                 n=n, k=k, e=e, h=h)
 
@@ -145,6 +155,38 @@ def bench_expert_gemm(moe, mi, torch, wid, iters, warmup):
     return dict(workload=w.name, rows=rows, ms=ms, tflops=flops / ms / 1e9, flops=flops)
 
 
+def recorded_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None
+    when the kernel source changed since the counters were taken."""
+    import hashlib
+    import re
+    path = ROOT / "profiles" / "row_kernels_uniform_hbm_traffic.md"
+    if not path.exists():
+        return None
+    m = re.search(r"```json\n(.*?)\n```", path.read_text(), re.S)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    src = (ROOT / rec["source"]).read_bytes()
+    if hashlib.sha256(src).hexdigest() != rec["source_sha256"]:
+        return None
+    return rec["traffic_bytes"].get(kernel)
+
+
+def counter_pass():
+    """Short run for rocprofv3 counter passes: three uniform-workload steps, then one
+    1 GiB device-to-device copy as the calibration kernel of known size."""
+    import torch
+    import moe_inputs as mi
+    import combine_router_softmax_amd as moe
+    torch.cuda.set_device(0)
+    bench_dispatch_combine(moe, mi, torch, 3, 1)
+    a = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+
+
 def cpu_baseline(mi):
     import numpy as np
     import oracle
@@ -175,7 +217,12 @@ def main():
     ap.add_argument("--gemm-iters", type=int, default=10)
     ap.add_argument("--skip-gemm", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="short run for rocprofv3 --pmc passes (prints no JSON line)")
     args = ap.parse_args()
+    if args.counter_pass:
+        counter_pass()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (the expert-parallel all-to-all is out "
               "of scope); run it with --gpus 1", file=sys.stderr)
@@ -200,7 +247,8 @@ def main():
 
     step_ms = dc["total_ms"] / args.steps
     byts = dc["dispatch_bytes"] + dc["combine_bytes"]
-    comb_gbs = dc["combine_bytes"] / (dc["combine_ms"] * 1e-3) / 1e9
+    comb_gbs = dc["combine_bytes"] / (dc["comb_kernel_ms"] * 1e-3) / 1e9
+    traffic = recorded_traffic("combine_kernel<true, 8>")
     line = {
         "metric": "dispatch+combine µs & GB/s (4096 tok, h7168, E256, top8); expert GEMM TFLOPS",
         "value": round(byts / (step_ms * 1e-3) / 1e9, 2),
@@ -225,9 +273,10 @@ def main():
         "dispatch_combine_gbs": round(byts / ((dc["dispatch_ms"] + dc["combine_ms"]) * 1e-3) / 1e9, 2),
         "combine_bwd_us": round(dc["bwd_ms"] * 1e3, 2),
         "combine_bwd_gbs": round(dc["bwd_bytes"] / (dc["bwd_ms"] * 1e-3) / 1e9, 2),
-        "roofline": {"kernel": "combine_kernel<bf16,8>", "bound": "hbm", "achieved": round(comb_gbs, 1),
+        "roofline": {"kernel": "combine_kernel<true, 8>", "bound": "hbm", "achieved": round(comb_gbs, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(comb_gbs / HBM_PEAK_GBS, 4),
-                     "traffic": None},
+                     "traffic": traffic, "launch_us": round(dc["comb_kernel_ms"] * 1e3, 2),
+                     "algorithmic_bytes": dc["combine_bytes"]},
         "expert_gemm": [{"workload": g["workload"], "rows": g["rows"], "us": round(g["ms"] * 1e3, 1),
                          "tflops": round(g["tflops"], 1), "frac_bf16_peak": round(g["tflops"] / BF16_PEAK_TFLOPS, 4)}
                         for g in gemm],

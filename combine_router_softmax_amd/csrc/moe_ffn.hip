@@ -179,16 +179,18 @@ __device__ __forceinline__ void load_frags(const char *__restrict__ stage, int k
   }
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
-    a[mi] = *reinterpret_cast<const bf16x8 *>(as + (wm * 128 + mi * 32 + r32) * kRowBytes + pos);
+    a[mi] = *reinterpret_cast<const bf16x8 *>(as + ((2 * mi + wm) * 32 + r32) * kRowBytes + pos);
 }
 
-// The 16 MFMAs of one 16-wide K slice.  The weight fragment is the MFMA's
-// first operand, so block (mi, ni) of the result holds, in lane l, activation
-// row mi*32 + l%32 and output features ni*32 + 8*(q/4) + 4*(l/32) + q%4 for
-// accumulator element q: four consecutive features per group of four elements.
-__device__ __forceinline__ void mfma_slice(const bf16x8 (&a)[4], const bf16x8 (&b)[4], f32x16 (&acc)[4][4]) {
+// The MFMAs of one 16-wide K slice for the wave's first MI row blocks.  The
+// weight fragment is the MFMA's first operand, so block (mi, ni) of the result
+// holds, in lane l, activation row l%32 of the wave's row block mi and output
+// features ni*32 + 8*(q/4) + 4*(l/32) + q%4 for accumulator element q: four
+// consecutive features per group of four elements.
+template <int MI>
+__device__ __forceinline__ void mfma_rows(const bf16x8 (&a)[4], const bf16x8 (&b)[4], f32x16 (&acc)[4][4]) {
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[ni], a[mi], acc[mi][ni], 0, 0, 0);
 }
@@ -233,10 +235,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
                        (uint32_t)__builtin_amdgcn_readfirstlane((int)tc.row0);
   const int rows_valid = __builtin_amdgcn_readfirstlane((int)(tc.row_end - tc.row0 < kBM ? tc.row_end - tc.row0 : kBM));
 
-  // 32-row MFMA blocks of this wave's 128-row half that hold rows of the segment
-  int valid = rows_valid - wm * 128;
-  valid = valid < 0 ? 0 : (valid > 128 ? 128 : valid);
-  const int mi_count = (valid + 31) / 32;
+  // the tile's 32-row blocks 0..7 alternate between the two row groups of waves
+  // (block 2*mi + wm is this wave's block mi); count this wave's blocks that
+  // hold rows of the segment
+  const int blocks_valid = (rows_valid + 31) / 32;
+  const int mi_count = blocks_valid > wm ? (blocks_valid - wm + 1) / 2 : 0;
 
   // direct-load sources: this wave fills tile rows w*64 .. w*64+63 of A and of
   // B, kLoadRows rows per instruction; lane l writes LDS bytes l*16..l*16+15 of
@@ -305,13 +308,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   else wait_vmcnt<0>();
   lds_barrier();
   load_frags<kSwiGLU>(lds0, 0, wm, wn, l, fa[0], fb[0]);
-#define MOE_K_STEP(CUR, NXT, J)                                                              \
+#define MOE_K_STEP(CUR, NXT, J, MI)                                                              \
   {                                                                                          \
     const int kt = kt0 + (J);                                                                \
     _Pragma("unroll") for (int ks = 0; ks + 1 < kSlices; ++ks) {                             \
       load_frags<kSwiGLU>(CUR, ks + 1, wm, wn, l, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);       \
-      mfma_slice(fa[ks & 1], fb[ks & 1], acc);                                               \
-      pin_reads_under_mfmas();                                                               \
+      mfma_rows<MI>(fa[ks & 1], fb[ks & 1], acc);                                            \
+      if (MI == 4) pin_reads_under_mfmas();                                                  \
       __builtin_amdgcn_sched_barrier(0);                                                     \
     }                                                                                        \
     if (kt + kStages - 1 < KT) wait_vmcnt<(kStages - 2) * kLoadsPerStage>();                 \
@@ -320,20 +323,43 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     if (kt + kStages < KT) issue(CUR, (kt + kStages) * kBK);                                 \
     __builtin_amdgcn_sched_barrier(0);                                                       \
     load_frags<kSwiGLU>(NXT, 0, wm, wn, l, fa[0], fb[0]);                                    \
-    mfma_slice(fa[(kSlices - 1) & 1], fb[(kSlices - 1) & 1], acc);                           \
-    pin_reads_under_mfmas();                                                                 \
+    mfma_rows<MI>(fa[(kSlices - 1) & 1], fb[(kSlices - 1) & 1], acc);                        \
+    if (MI == 4) pin_reads_under_mfmas();                                                    \
     __builtin_amdgcn_sched_barrier(0);                                                       \
   }
+  // waves whose valid row blocks are at most two (ragged last tile of an
+  // expert) run the loop with half the MFMAs
+  if (mi_count > 2) {
+#define MI_ 4
+  {
   int kt0 = 0;
   for (; kt0 + kStages <= KT; kt0 += kStages) {
-    MOE_K_STEP(lds0, lds1, 0)
-    MOE_K_STEP(lds1, lds2, 1)
-    MOE_K_STEP(lds2, lds3, 2)
-    MOE_K_STEP(lds3, lds0, 3)
+    MOE_K_STEP(lds0, lds1, 0, MI_)
+    MOE_K_STEP(lds1, lds2, 1, MI_)
+    MOE_K_STEP(lds2, lds3, 2, MI_)
+    MOE_K_STEP(lds3, lds0, 3, MI_)
   }
-  if (kt0 < KT) MOE_K_STEP(lds0, lds1, 0)
-  if (kt0 + 1 < KT) MOE_K_STEP(lds1, lds2, 1)
-  if (kt0 + 2 < KT) MOE_K_STEP(lds2, lds3, 2)
+  if (kt0 < KT) MOE_K_STEP(lds0, lds1, 0, MI_)
+  if (kt0 + 1 < KT) MOE_K_STEP(lds1, lds2, 1, MI_)
+  if (kt0 + 2 < KT) MOE_K_STEP(lds2, lds3, 2, MI_)
+  }
+#undef MI_
+  } else {
+#define MI_ 2
+  {
+  int kt0 = 0;
+  for (; kt0 + kStages <= KT; kt0 += kStages) {
+    MOE_K_STEP(lds0, lds1, 0, MI_)
+    MOE_K_STEP(lds1, lds2, 1, MI_)
+    MOE_K_STEP(lds2, lds3, 2, MI_)
+    MOE_K_STEP(lds3, lds0, 3, MI_)
+  }
+  if (kt0 < KT) MOE_K_STEP(lds0, lds1, 0, MI_)
+  if (kt0 + 1 < KT) MOE_K_STEP(lds1, lds2, 1, MI_)
+  if (kt0 + 2 < KT) MOE_K_STEP(lds2, lds3, 2, MI_)
+  }
+#undef MI_
+  }
 #undef MOE_K_STEP
   wait_vmcnt<0>();  // no direct load may still be writing LDS when the wave ends
 
@@ -383,7 +409,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   const int ch = l % kChunksPerRow;
 #pragma unroll 4
   for (int r = l / kChunksPerRow; r < 128; r += kRowsPerPass) {
-    const int row = wm * 128 + r;
+    const int row = (2 * (r >> 5) + wm) * 32 + (r & 31);  // staged row r is row r%32 of block r/32
     const int col = col0 + ch * 8;
     const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * kPitch + out_pos(r, ch) * 16);
     if (row < rows_valid && col < N) st16(c_base + (int64_t)row * ldc + col, v);
