@@ -36,7 +36,7 @@
 namespace moe {
 namespace {
 
-constexpr int kLayoutThreads = 256;
+constexpr int kLayoutThreads = 512;
 constexpr int kLayoutWaves = kLayoutThreads / kWave;
 constexpr int kChunksPerWave = kLayoutTile / kLayoutThreads;  // 64-assignment chunks per wave
 static_assert(kLayoutTile % kLayoutThreads == 0, "tile must be a multiple of the block");
@@ -131,6 +131,15 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place(
   const int w = tid / kWave;
   const int l = lane_id();
   const int64_t tile = blockIdx.x;
+
+  // this tile's expert ids, loaded first so they arrive while the count matrix is read
+  const int64_t a_wave = tile * kLayoutTile + (int64_t)w * kChunksPerWave * kWave;
+  int32_t ids[kChunksPerWave];
+#pragma unroll
+  for (int c = 0; c < kChunksPerWave; ++c) {
+    const int64_t a = a_wave + c * kWave + l;
+    ids[c] = (tile < tiles && a < a_total) ? topk_idx[a] : -1;
+  }
 
   // ---- per-expert sums over tiles: before this tile, and over all tiles
   if (e <= kLayoutThreads) {
@@ -242,13 +251,6 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place(
   if (tile < tiles) {  // block-uniform
     for (int x = tid; x < kLayoutWaves * e; x += kLayoutThreads) run[x] = 0;
     __syncthreads();
-    const int64_t a_wave = tile * kLayoutTile + (int64_t)w * kChunksPerWave * kWave;
-    int32_t ids[kChunksPerWave];
-#pragma unroll
-    for (int c = 0; c < kChunksPerWave; ++c) {
-      const int64_t a = a_wave + c * kWave + l;
-      ids[c] = a < a_total ? topk_idx[a] : -1;
-    }
 #pragma unroll
     for (int c = 0; c < kChunksPerWave; ++c)
       if (valid_id(ids[c], e)) atomicAdd(&run[w * e + ids[c]], 1);
