@@ -24,10 +24,12 @@
 // Tile: 256 rows x 256 columns (GEMM1: 128 gate + 128 up columns), 4 waves in
 // a 2 x 2 arrangement of 128 x 128 sub-tiles (4 x 4 MFMA 32x32 blocks, 256 fp32
 // accumulators per lane, held in AGPRs).  Operands go global -> LDS directly
-// (global_load_lds_dwordx4, no register staging) through a ring of LDS stages
-// (K step 32, 4 stages of 32 KiB, three K steps in flight).  A wave's load
-// instruction fills 1 KiB of a stage; each lane picks which 16-byte chunk of
-// its row to fetch so that chunk c of row r lands at position c ^ swz(r), which
+// (global_load_lds_dwordx4, no register staging).  A K step is 64 wide, so every
+// tile row of a step is one whole 128-byte line of the operand.  LDS holds a
+// ring of five 32 KiB operand tiles (160 KiB): while one step's A and B tiles
+// are read, the three other slots fill, 1.5 steps ahead.  A wave's load
+// instruction fills 1 KiB (8 rows); each lane picks which 16-byte chunk of its
+// row to fetch so that chunk c of row r lands at position c ^ swz(r), which
 // keeps the MFMA fragment reads free of LDS bank conflicts.  Rows past the end
 // of an expert's segment re-read its last row and are not stored.
 #include "moe_device.hpp"
@@ -41,43 +43,45 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBM = 256;
 constexpr int kBN = 256;
-constexpr int kBK = 32;                          // K per pipeline stage
-constexpr int kStages = 4;                       // LDS stages (kStages - 1 K steps in flight)
-constexpr int kRowBytes = kBK * 2;               // bytes of K per tile row
+constexpr int kBK = 64;                          // K per step
+constexpr int kRowBytes = kBK * 2;               // bytes of K per tile row: one 128-byte line
 constexpr int kChunks = kRowBytes / 16;          // 16-byte chunks per tile row
 constexpr int kLoadRows = 1024 / kRowBytes;      // tile rows one wave load instruction fills
-constexpr int kLoadsPerOperand = kBM / kLoadRows / 4;  // load instructions per wave per operand per stage
-constexpr int kOperandBytes = kBM * kRowBytes;
-constexpr int kStageBytes = 2 * kOperandBytes;
+constexpr int kLoads = kBM / kLoadRows / 4;      // load instructions per wave per operand tile
+constexpr int kOperandBytes = kBM * kRowBytes;   // one operand tile of one K step: 32 KiB
+constexpr int kSlots = 5;                        // ring of operand tiles
 constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 constexpr int kMaxExperts = 1024;
-static_assert(kBK == 32 || kBK == 64, "tile K step");
-static_assert(kStages * kStageBytes <= 128 * 1024, "LDS budget");
+static_assert(kSlots * kOperandBytes <= 160 * 1024, "LDS budget");
+static_assert(kLoads == 8, "load schedule below: 8 load instructions per wave per operand tile");
 
-// LDS position of 16-byte chunk c of tile row r is c ^ swz(r): the 16-byte
-// fragment reads of 16 consecutive rows then fall in distinct bank groups
-// whether the LDS serves 8 lanes over 32 banks or 16 lanes over 64 banks.
-__device__ __forceinline__ int swz(int r) {
-  return kBK == 64 ? ((r & 7) ^ ((r >> 3) & 1)) : (((r >> 1) ^ (r >> 3)) & 3);
-}
+// LDS position of 16-byte chunk c of tile row r is c ^ swz(r).  A fragment
+// read (ds_read_b128) has lane l read row l%32 of a 32-row block, chunk
+// 2*slice + l/32.  Measured on gfx950, the permutation (r ^ r/4) % 8 of the
+// eight chunks of a 128-byte row lets these reads run at the throughput of a
+// linear 16-bytes-per-lane read; permuting by r % 8 alone, or by r/4 alone,
+// reaches about 0.6 of it.
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 2)) & 7; }
 
 // Workgroup barrier for LDS: waits for this wave's LDS operations, then
 // s_barrier; the memory clobber keeps the compiler from moving memory accesses
 // across it.  Unlike __syncthreads() it does not wait for vector-memory loads.
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// 16 bytes per lane global -> LDS (global_load_lds_dwordx4): lane l's bytes land
-// at LDS address lds_addr + 16*l (lds_addr is wave-uniform, passed in M0).  The
-// instruction has no register result.  It is issued from inline asm so that the
-// compiler's memory-counter bookkeeping does not see it: the compiler cannot
-// tell which LDS stage such a load writes and would otherwise drain every load
-// in flight before reading any stage; the K loop below waits for these loads
-// itself with explicit vmcnt waits, and no other vector load is issued while
-// they are in flight.
-__device__ __forceinline__ void dma16(const void *gptr, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off" ::"s"(lds_addr), "v"(gptr)
-               : "memory", "m0");
+// 16 bytes per lane global -> LDS (global_load_lds_dwordx4): lane l reads
+// base + off (base wave-uniform, in SGPRs; off a 32-bit per-lane byte offset)
+// and its bytes land at LDS address lds_addr + 16*l (lds_addr is wave-uniform,
+// passed in M0).  The instruction has no register result.  It is issued from
+// inline asm so that the compiler's memory-counter bookkeeping does not see it:
+// the compiler cannot tell which LDS stage such a load writes and would
+// otherwise drain every load in flight before reading any stage; the K loop
+// below waits for these loads itself with explicit vmcnt waits, and no other
+// vector load is issued while they are in flight.  M0 is an input operand, so
+// the compiler writes it and knows its value; the s_nop keeps one wait state
+// between that write and the load that reads M0.
+__device__ __forceinline__ void dma16(const void *base, uint32_t off, uint32_t lds_addr) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %1, %2" ::"{m0}"(lds_addr), "v"(off), "s"(base) : "memory");
 }
 
 // LDS byte address of a pointer into a __shared__ array (the low 32 bits of its
@@ -101,11 +105,12 @@ struct TileCoord {
 };
 
 // Maps blockIdx.x to an output tile; returns false for surplus workgroups.
-// `scratch` must hold kMaxExperts + 1 int64 and is free again on return.
+// `scratch` (LDS) must hold kMaxExperts + kThreads int64 and is free again on
+// return.
 __device__ bool find_tile(const int32_t *__restrict__ tokens_per_expert, const int32_t *__restrict__ expert_offsets,
                           int e, int n_tiles, int64_t *scratch, TileCoord &tc) {
   constexpr int kPer = kMaxExperts / kThreads;  // experts per thread
-  __shared__ int64_t part[kThreads];
+  int64_t *part = scratch + kMaxExperts;
   const int tid = threadIdx.x;
   int64_t local[kPer];
   int64_t s = 0;
@@ -162,13 +167,11 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)
 
 __device__ __forceinline__ uint16_t bf16_bits(float v) { return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu); }
 
-// Fragments of one 16-wide K slice: A rows (wm*128 + mi*32 + l%32), B rows
-// likewise, k-chunk 2*ks + l/32.
+// Fragments of one 16-wide K slice ks from the A tile `as` and the B tile `bs`:
+// A rows (2*mi + wm)*32 + l%32, B rows as below, k-chunk 2*ks + l/32.
 template <bool kSwiGLU>
-__device__ __forceinline__ void load_frags(const char *__restrict__ stage, int ks, int wm, int wn, int l,
-                                           bf16x8 (&a)[4], bf16x8 (&b)[4]) {
-  const char *as = stage;
-  const char *bs = stage + kOperandBytes;
+__device__ __forceinline__ void load_frags(const char *__restrict__ as, const char *__restrict__ bs, int ks, int wm,
+                                           int wn, int l, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
   const int r32 = l & 31;
   const int pos = ((2 * ks + (l >> 5)) ^ swz(r32)) * 16;  // every row read is r32 plus a multiple of 32
 #pragma unroll
@@ -182,30 +185,54 @@ __device__ __forceinline__ void load_frags(const char *__restrict__ stage, int k
     a[mi] = *reinterpret_cast<const bf16x8 *>(as + ((2 * mi + wm) * 32 + r32) * kRowBytes + pos);
 }
 
-// The MFMAs of one 16-wide K slice for the wave's first MI row blocks.  The
-// weight fragment is the MFMA's first operand, so block (mi, ni) of the result
-// holds, in lane l, activation row l%32 of the wave's row block mi and output
-// features ni*32 + 8*(q/4) + 4*(l/32) + q%4 for accumulator element q: four
-// consecutive features per group of four elements.
-template <int MI>
-__device__ __forceinline__ void mfma_rows(const bf16x8 (&a)[4], const bf16x8 (&b)[4], f32x16 (&acc)[4][4]) {
+// MFMAs FIRST .. FIRST+COUNT-1 of one 16-wide K slice, numbered row block
+// major (i = 4*mi + ni).  The weight fragment is the MFMA's first operand, so
+// block (mi, ni) of the result holds, in lane l, activation row l%32 of the
+// wave's row block mi and output features ni*32 + 8*(q/4) + 4*(l/32) + q%4 for
+// accumulator element q: four consecutive features per group of four elements.
+template <int FIRST, int COUNT>
+__device__ __forceinline__ void mfma_range(const bf16x8 (&a)[4], const bf16x8 (&b)[4], f32x16 (&acc)[4][4]) {
 #pragma unroll
-  for (int mi = 0; mi < MI; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[ni], a[mi], acc[mi][ni], 0, 0, 0);
+  for (int i = FIRST; i < FIRST + COUNT; ++i)
+    acc[i / 4][i % 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(b[i % 4], a[i / 4], acc[i / 4][i % 4], 0, 0, 0);
 }
 
-// Instruction order for a region holding the 8 fragment reads of the next
-// slice and the 16 MFMAs of the current one: reads and MFMAs one-to-one, then
-// the remaining 8 MFMAs.  The reads' latency hides behind the MFMAs.
-__device__ __forceinline__ void pin_reads_under_mfmas() {
+// The 4*MI MFMAs of one K slice for the wave's first MI row blocks.  The
+// fragment reads of the following slice (issued just before, in the same
+// scheduling region) are paired with the first half of the MFMAs; the slice's
+// four direct-load instructions (dma(0..3)) sit between the MFMAs of the
+// second half.  A run of load instructions would stall the wave -- and with it
+// the matrix pipe -- while the address unit works through them; spread out,
+// each load issues while the previous MFMAs run.
+template <int MI, typename Dma>
+__device__ __forceinline__ void slice(const bf16x8 (&a)[4], const bf16x8 (&b)[4], f32x16 (&acc)[4][4],
+                                      Dma &&dma) {
+  constexpr int kPart = MI / 2;                  // MFMAs between two load slots (MI = 1: none)
+  constexpr int kHead = 4 * MI - 4 * kPart;      // MFMAs paired with the fragment reads
   constexpr int kDsRead = 0x100, kMfma = 0x008;
+  mfma_range<0, kHead>(a, b, acc);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kHead; ++i) {
     __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, 8 / kHead, 0);
   }
-  __builtin_amdgcn_sched_group_barrier(kMfma, 8, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_range<kHead, kPart>(a, b, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  dma(0);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_range<kHead + kPart, kPart>(a, b, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  dma(1);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_range<kHead + 2 * kPart, kPart>(a, b, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  dma(2);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma_range<kHead + 3 * kPart, kPart>(a, b, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  dma(3);
+  __builtin_amdgcn_sched_barrier(0);
 }
 
 // kSwiGLU: B tile rows 0..127 are gate rows n0.., rows 128..255 the up rows
@@ -216,14 +243,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int64_t b_expert_stride, int K, int N,
     int n_tiles, const int32_t *__restrict__ tokens_per_expert, const int32_t *__restrict__ expert_offsets, int e,
     uint16_t *__restrict__ C, int64_t ldc) {
-  // one object per stage, so the compiler can tell a stage being read from the
-  // stages the direct loads are still filling
-  __shared__ __attribute__((aligned(1024))) char lds0[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char lds1[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char lds2[kStageBytes];
-  __shared__ __attribute__((aligned(1024))) char lds3[kStageBytes];
+  // ring of operand tiles; also find_tile's scratch before the K loop and the
+  // output staging after it
+  __shared__ __attribute__((aligned(1024))) char ring[kSlots * kOperandBytes];
   TileCoord tc;
-  if (!find_tile(tokens_per_expert, expert_offsets, e, n_tiles, reinterpret_cast<int64_t *>(lds0), tc)) return;
+  if (!find_tile(tokens_per_expert, expert_offsets, e, n_tiles, reinterpret_cast<int64_t *>(ring), tc)) return;
 
   const int l = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -241,16 +265,16 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   const int blocks_valid = (rows_valid + 31) / 32;
   const int mi_count = blocks_valid > wm ? (blocks_valid - wm + 1) / 2 : 0;
 
-  // direct-load sources: this wave fills tile rows w*64 .. w*64+63 of A and of
-  // B, kLoadRows rows per instruction; lane l writes LDS bytes l*16..l*16+15 of
-  // the instruction's block, i.e. row l / kChunks, position l % kChunks, so it
-  // fetches global chunk position ^ swz(row).  Addresses are a per-tile scalar
-  // base plus a 32-bit per-lane byte offset.
+  // direct-load sources: this wave fills tile rows w*64 .. w*64+63 of each
+  // operand tile, kLoadRows rows per instruction; lane l writes LDS bytes
+  // l*16..l*16+15 of the instruction's 1 KiB, i.e. row l / kChunks, position
+  // l % kChunks, so it fetches global chunk position ^ swz(row).  Addresses are
+  // a per-tile scalar base plus a 32-bit per-lane byte offset.
   const char *a_base = reinterpret_cast<const char *>(A + row0 * K);
   const char *b_base = reinterpret_cast<const char *>(B + (int64_t)te * b_expert_stride);
-  uint32_t a_off[kLoadsPerOperand], b_off[kLoadsPerOperand];
+  uint32_t a_off[kLoads], b_off[kLoads];
 #pragma unroll
-  for (int i = 0; i < kLoadsPerOperand; ++i) {
+  for (int i = 0; i < kLoads; ++i) {
     const int r = w * 64 + i * kLoadRows + l / kChunks;
     const int c = (l % kChunks) ^ swz(r);
     const int ar = r < rows_valid ? r : rows_valid - 1;  // ragged tail: re-read the last row
@@ -265,14 +289,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     }
     b_off[i] = ((uint32_t)br * (uint32_t)K + (uint32_t)(c * 8)) * 2u;  // < 4*I*H bytes
   }
-  auto issue = [&](char *stage, int k0) {
-    const char *ab = a_base + 2 * k0;
-    const char *bb = b_base + 2 * k0;
-    const uint32_t dst = lds_address(stage) + w * 64 * kRowBytes;
-#pragma unroll
-    for (int i = 0; i < kLoadsPerOperand; ++i) dma16(ab + a_off[i], dst + i * 1024);
-#pragma unroll
-    for (int i = 0; i < kLoadsPerOperand; ++i) dma16(bb + b_off[i], dst + kOperandBytes + i * 1024);
+  const uint32_t ring_lds = lds_address(ring) + w * 64 * kRowBytes;
+  // load instruction i (0..7) of this wave for the A (B) tile of step kt into ring slot `slot`
+  auto load_a = [&](int slot, int kt, int i) {
+    dma16(a_base + 2 * kt * kBK, a_off[i], ring_lds + slot * kOperandBytes + i * 1024);
+  };
+  auto load_b = [&](int slot, int kt, int i) {
+    dma16(b_base + 2 * kt * kBK, b_off[i], ring_lds + slot * kOperandBytes + i * 1024);
   };
 
   f32x16 acc[4][4];
@@ -283,82 +306,84 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  // K loop over a ring of kStages LDS buffers, kStages K steps in flight.
-  // Step kt multiplies stage kt slice by slice, reading the fragments of slice
-  // ks+1 while the MFMAs of slice ks run.  Before its last slice it waits for
-  // its own loads of stage kt+1 (at most the kStages-2 younger stages left in
-  // flight), passes a barrier -- after which every wave's loads of stage kt+1
-  // are visible and nobody reads stage kt any more -- refills the buffer of
-  // stage kt with stage kt+kStages, and reads slice 0 of stage kt+1 under the
-  // MFMAs of its last slice.  So no LDS read latency is exposed.  The barrier
-  // orders LDS accesses only (a full workgroup fence would also wait for the
-  // loads in flight).  The loop is unrolled by kStages so every step names its
-  // buffers at compile time.
-  static_assert(kStages == 4, "the unrolled loop below names four stage buffers");
-  constexpr int kSlices = kBK / 16;
-  static_assert(kSlices % 2 == 0, "slice fragments alternate between two register sets");
-  constexpr int kLoadsPerStage = 2 * kLoadsPerOperand;
+  // K loop.  The tiles of step kt sit in ring slots 2kt % 5 (B) and
+  // (2kt+1) % 5 (A).  Step kt multiplies them in four 16-wide slices, reading
+  // the fragments of the next slice under the MFMAs of the current one.
+  // Slices 0 and 1 also load the B tile of step kt+2 (into the slot step kt-1's
+  // A tile held).  After slice 2 every wave waits for its own loads of step
+  // kt+1 (only step kt+2's B tile may stay in flight) and passes a barrier:
+  // then every wave's loads of step kt+1 are visible and no wave reads step
+  // kt's tiles any more (the last slice's fragments are in registers).  Slice
+  // 3 reads the first fragments of step kt+1 and loads the A tile of step kt+2
+  // into the slot of step kt's B tile.  So B tiles are requested about 1.5
+  // steps and A tiles about one step before use; no LDS read latency is
+  // exposed; and the load instructions are spread over the MFMA stream.  The
+  // barrier orders LDS accesses only (a full workgroup fence would also wait
+  // for the loads in flight).
   const int KT = K / kBK;
   bf16x8 fa[2][4], fb[2][4];
-  if (0 < KT) issue(lds0, 0);
-  if (1 < KT) issue(lds1, kBK);
-  if (2 < KT) issue(lds2, 2 * kBK);
-  if (3 < KT) issue(lds3, 3 * kBK);
-  if (KT >= kStages) wait_vmcnt<(kStages - 1) * kLoadsPerStage>();
-  else wait_vmcnt<0>();
-  lds_barrier();
-  load_frags<kSwiGLU>(lds0, 0, wm, wn, l, fa[0], fb[0]);
-#define MOE_K_STEP(CUR, NXT, J, MI)                                                              \
-  {                                                                                          \
-    const int kt = kt0 + (J);                                                                \
-    _Pragma("unroll") for (int ks = 0; ks + 1 < kSlices; ++ks) {                             \
-      load_frags<kSwiGLU>(CUR, ks + 1, wm, wn, l, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);       \
-      mfma_rows<MI>(fa[ks & 1], fb[ks & 1], acc);                                            \
-      if (MI == 4) pin_reads_under_mfmas();                                                  \
-      __builtin_amdgcn_sched_barrier(0);                                                     \
-    }                                                                                        \
-    if (kt + kStages - 1 < KT) wait_vmcnt<(kStages - 2) * kLoadsPerStage>();                 \
-    else wait_vmcnt<0>();                                                                    \
-    lds_barrier();                                                                           \
-    if (kt + kStages < KT) issue(CUR, (kt + kStages) * kBK);                                 \
-    __builtin_amdgcn_sched_barrier(0);                                                       \
-    load_frags<kSwiGLU>(NXT, 0, wm, wn, l, fa[0], fb[0]);                                    \
-    mfma_rows<MI>(fa[(kSlices - 1) & 1], fb[(kSlices - 1) & 1], acc);                        \
-    if (MI == 4) pin_reads_under_mfmas();                                                    \
-    __builtin_amdgcn_sched_barrier(0);                                                       \
-  }
-  // waves whose valid row blocks are at most two (ragged last tile of an
-  // expert) run the loop with half the MFMAs
-  if (mi_count > 2) {
-#define MI_ 4
-  {
-  int kt0 = 0;
-  for (; kt0 + kStages <= KT; kt0 += kStages) {
-    MOE_K_STEP(lds0, lds1, 0, MI_)
-    MOE_K_STEP(lds1, lds2, 1, MI_)
-    MOE_K_STEP(lds2, lds3, 2, MI_)
-    MOE_K_STEP(lds3, lds0, 3, MI_)
-  }
-  if (kt0 < KT) MOE_K_STEP(lds0, lds1, 0, MI_)
-  if (kt0 + 1 < KT) MOE_K_STEP(lds1, lds2, 1, MI_)
-  if (kt0 + 2 < KT) MOE_K_STEP(lds2, lds3, 2, MI_)
-  }
-#undef MI_
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) load_b(0, 0, i);
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) load_a(1, 0, i);
+  if (KT > 1) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) load_b(2, 1, i);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) load_a(3, 1, i);
+    wait_vmcnt<2 * kLoads>();
   } else {
-#define MI_ 2
-  {
-  int kt0 = 0;
-  for (; kt0 + kStages <= KT; kt0 += kStages) {
-    MOE_K_STEP(lds0, lds1, 0, MI_)
-    MOE_K_STEP(lds1, lds2, 1, MI_)
-    MOE_K_STEP(lds2, lds3, 2, MI_)
-    MOE_K_STEP(lds3, lds0, 3, MI_)
+    wait_vmcnt<0>();
   }
-  if (kt0 < KT) MOE_K_STEP(lds0, lds1, 0, MI_)
-  if (kt0 + 1 < KT) MOE_K_STEP(lds1, lds2, 1, MI_)
-  if (kt0 + 2 < KT) MOE_K_STEP(lds2, lds3, 2, MI_)
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  load_frags<kSwiGLU>(ring + kOperandBytes, ring, 0, wm, wn, l, fa[0], fb[0]);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // one K step with MI row blocks per wave; sb, sa: slots of step kt's B and A
+  // tiles; nb, na: of step kt+1's; pb: slot for step kt+2's B tile
+#define MOE_K_STEP(MI)                                                                                   \
+  {                                                                                                     \
+    const int nb = sb + 2 < kSlots ? sb + 2 : sb + 2 - kSlots;                                          \
+    const int na = sa + 2 < kSlots ? sa + 2 : sa + 2 - kSlots;                                          \
+    const int pb = na + 1 < kSlots ? na + 1 : na + 1 - kSlots;                                          \
+    const bool ahead = kt + 2 < KT;                                                                     \
+    const char *as = ring + sa * kOperandBytes;                                                         \
+    const char *bs = ring + sb * kOperandBytes;                                                         \
+    load_frags<kSwiGLU>(as, bs, 1, wm, wn, l, fa[1], fb[1]);                                            \
+    slice<MI>(fa[0], fb[0], acc, [&](int d) {                                                           \
+      if (ahead) load_b(pb, kt + 2, d);                                                                 \
+    });                                                                                                 \
+    load_frags<kSwiGLU>(as, bs, 2, wm, wn, l, fa[0], fb[0]);                                            \
+    slice<MI>(fa[1], fb[1], acc, [&](int d) {                                                           \
+      if (ahead) load_b(pb, kt + 2, 4 + d);                                                             \
+    });                                                                                                 \
+    load_frags<kSwiGLU>(as, bs, 3, wm, wn, l, fa[1], fb[1]);                                            \
+    slice<MI>(fa[0], fb[0], acc, [&](int) {});                                                          \
+    if (ahead) wait_vmcnt<kLoads>();                                                                    \
+    else wait_vmcnt<0>();                                                                               \
+    lds_barrier();                                                                                      \
+    __builtin_amdgcn_sched_barrier(0);                                                                  \
+    load_frags<kSwiGLU>(ring + na * kOperandBytes, ring + nb * kOperandBytes, 0, wm, wn, l, fa[0], fb[0]); \
+    slice<MI>(fa[1], fb[1], acc, [&](int d) {                                                           \
+      if (ahead) {                                                                                      \
+        load_a(sb, kt + 2, 2 * d);                                                                      \
+        load_a(sb, kt + 2, 2 * d + 1);                                                                  \
+      }                                                                                                 \
+    });                                                                                                 \
+    sb = nb;                                                                                            \
+    sa = na;                                                                                            \
   }
-#undef MI_
+  // the ragged last tile of an expert runs the loop with the MFMAs of the row
+  // blocks that hold rows: a quarter or half of them when the waves hold at
+  // most one or two such blocks
+  int sb = 0, sa = 1;
+  if (mi_count > 2) {
+    for (int kt = 0; kt < KT; ++kt) MOE_K_STEP(4)
+  } else if (mi_count == 2) {
+    for (int kt = 0; kt < KT; ++kt) MOE_K_STEP(2)
+  } else {
+    for (int kt = 0; kt < KT; ++kt) MOE_K_STEP(1)
   }
 #undef MOE_K_STEP
   wait_vmcnt<0>();  // no direct load may still be writing LDS when the wave ends
@@ -370,11 +395,11 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   constexpr int kCols = kSwiGLU ? 64 : 128;     // output columns of this wave
   constexpr int kPitch = kCols * 2;             // LDS bytes per staged row
   constexpr int kChunksPerRow = kPitch / 16;
-  static_assert(128 * kPitch <= kStageBytes, "staging fits one stage buffer");
+  static_assert(128 * kPitch <= kOperandBytes, "staging fits one ring slot");
   auto out_pos = [](int r, int c) {             // LDS chunk position of chunk c of staged row r
     return kChunksPerRow == 16 ? (c ^ (r & 15)) : (c ^ ((r & 7) ^ ((r >> 3) & 1)));
   };
-  char *stage = w == 0 ? lds0 : (w == 1 ? lds1 : (w == 2 ? lds2 : lds3));
+  char *stage = ring + w * kOperandBytes;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
     const int r = mi * 32 + (l & 31);
