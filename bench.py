@@ -187,6 +187,17 @@ def counter_pass():
     torch.cuda.synchronize()
 
 
+def gemm_pass():
+    """Short run for rocprofv3 counter passes over the expert GEMM: the qwen3-layer
+    FFN workload, one warm-up call and two measured calls."""
+    import torch
+    import moe_inputs as mi
+    import combine_router_softmax_amd as moe
+    torch.cuda.set_device(0)
+    bench_expert_gemm(moe, mi, torch, 4, 2, 1)
+    torch.cuda.synchronize()
+
+
 def cpu_baseline(mi):
     import numpy as np
     import oracle
@@ -219,7 +230,12 @@ def main():
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--counter-pass", action="store_true",
                     help="short run for rocprofv3 --pmc passes (prints no JSON line)")
+    ap.add_argument("--gemm-pass", action="store_true",
+                    help="short expert-GEMM run for hardware-counter passes (prints nothing)")
     args = ap.parse_args()
+    if args.gemm_pass:
+        gemm_pass()
+        return
     if args.counter_pass:
         counter_pass()
         return
