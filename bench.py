@@ -42,6 +42,12 @@ def median(v):
     return v[len(v) // 2] if v else float("nan")
 
 
+def pct(v, q):
+    """q-th percentile (nearest rank) of v."""
+    v = sorted(v)
+    return v[min(len(v) - 1, max(0, int(round(q / 100.0 * (len(v) - 1)))))] if v else float("nan")
+
+
 def bench_dispatch_combine(moe, mi, torch, steps, warmup):
     import numpy as np
     w = mi.workload(2)
@@ -111,8 +117,41 @@ def bench_dispatch_combine(moe, mi, torch, steps, warmup):
     c1.record()
     torch.cuda.synchronize()
     comb_kernel_ms = c0.elapsed_time(c1) / steps
+    # cold caches: before each timed step, outside the timed region, read 1 GiB
+    # (evicts the 4 MB L2 of every XCD and the 256 MB MALL, which could hold x;
+    # a read leaves clean lines, so no write-back of the flush lands in the step)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    cold = []
+    for i in range(min(steps, 20)):
+        flush.sum()
+        torch.cuda.synchronize()
+        step(cold)
+        torch.cuda.synchronize()
+    cold_route = [r_[0].elapsed_time(r_[1]) for r_ in cold]
+    cold_disp = [r_[1].elapsed_time(r_[2]) for r_ in cold]
+    cold_comb = [r_[2].elapsed_time(r_[3]) for r_ in cold]
+    cold_dc = [r_[1].elapsed_time(r_[3]) for r_ in cold]
+    # a plain device copy of 1 GiB (2.15 GB moved) for the measured-bandwidth fraction
+    dst = torch.empty_like(flush)
+    dst.copy_(flush)
+    torch.cuda.synchronize()
+    k0 = torch.cuda.Event(enable_timing=True)
+    k1 = torch.cuda.Event(enable_timing=True)
+    k0.record()
+    for _ in range(5):
+        dst.copy_(flush)
+    k1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * flush.numel() * 4 / (k0.elapsed_time(k1) / 5 * 1e-3) / 1e9
+    del flush, dst
     return dict(total_ms=total_ms, route_ms=route_ms, dispatch_ms=disp_ms, combine_ms=comb_ms,
-                comb_kernel_ms=comb_kernel_ms, kept=kept,
+                comb_kernel_ms=comb_kernel_ms, kept=kept, copy_gbs=copy_gbs,
+                dc_p10=pct([r_[1].elapsed_time(r_[3]) for r_ in recs], 10),
+                dc_p90=pct([r_[1].elapsed_time(r_[3]) for r_ in recs], 90),
+                cold_route_ms=median(cold_route), cold_dispatch_ms=median(cold_disp),
+                cold_combine_ms=median(cold_comb), cold_dc_ms=median(cold_dc),
+                cold_dc_p10=pct(cold_dc, 10), cold_dc_p90=pct(cold_dc, 90),
                 dispatch_bytes=dispatch_bytes, combine_bytes=combine_bytes, bwd_ms=bwd_ms, bwd_bytes=bwd_bytes,
                 n=n, k=k, e=e, h=h)
 
@@ -287,6 +326,19 @@ def main():
         "combine_us": round(dc["combine_ms"] * 1e3, 2),
         "dispatch_combine_us": round((dc["dispatch_ms"] + dc["combine_ms"]) * 1e3, 2),
         "dispatch_combine_gbs": round(byts / ((dc["dispatch_ms"] + dc["combine_ms"]) * 1e-3) / 1e9, 2),
+        "dispatch_combine_p10_p90_us": [round(dc["dc_p10"] * 1e3, 2), round(dc["dc_p90"] * 1e3, 2)],
+        "cold": {"route_us": round(dc["cold_route_ms"] * 1e3, 2),
+                 "dispatch_us": round(dc["cold_dispatch_ms"] * 1e3, 2),
+                 "combine_us": round(dc["cold_combine_ms"] * 1e3, 2),
+                 "dispatch_combine_us": round(dc["cold_dc_ms"] * 1e3, 2),
+                 "dispatch_combine_p10_p90_us": [round(dc["cold_dc_p10"] * 1e3, 2),
+                                                 round(dc["cold_dc_p90"] * 1e3, 2)],
+                 "dispatch_combine_gbs": round(byts / (dc["cold_dc_ms"] * 1e-3) / 1e9, 2),
+                 "frac_hbm_peak": round(byts / (dc["cold_dc_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                 "note": "median of 20 steps, each after a 1 GiB read that evicts L2 and MALL"},
+        "copy_gbs": round(dc["copy_gbs"], 1),
+        "dispatch_combine_frac_of_copy": round(byts / ((dc["dispatch_ms"] + dc["combine_ms"]) * 1e-3) / 1e9
+                                               / dc["copy_gbs"], 4),
         "combine_bwd_us": round(dc["bwd_ms"] * 1e3, 2),
         "combine_bwd_gbs": round(dc["bwd_bytes"] / (dc["bwd_ms"] * 1e-3) / 1e9, 2),
         "roofline": {"kernel": "combine_kernel<true, 8>", "bound": "hbm", "achieved": round(comb_gbs, 1),
