@@ -59,6 +59,8 @@ def lib():
         L.oracle_combine.argtypes = [i64, i32, i64, i32, p, p, p, p]
         L.oracle_combine.restype = None
         L.oracle_combine_bwd.argtypes = [i64, i32, i64, i32, p, p, p, p, i64, p, i32, p, p]
+        L.oracle_dispatch_bwd.argtypes = [i64, i32, i64, i32, p, p, p]
+        L.oracle_dispatch_bwd.restype = None
         L.oracle_combine_bwd.restype = None
         L.oracle_bf16_round.argtypes = [C.c_double]
         L.oracle_bf16_round.restype = C.c_uint16
@@ -163,6 +165,15 @@ def combine(y: np.ndarray, topk_w: np.ndarray, lay: dict, n: int, k: int):
     out = np.empty((n, h), y.dtype)
     lib().oracle_combine(n, k, h, _dt(y), _p(y), _p(np.ascontiguousarray(topk_w, dtype=np.float32)),
                          _p(lay["assign_row"]), _p(out))
+    return out
+
+
+def dispatch_bwd(grad_x_perm: np.ndarray, lay: dict, n: int, k: int):
+    """Adjoint of the row scatter: grad_x [N, H] = sum of the kept slots' rows."""
+    grad_x_perm = np.ascontiguousarray(grad_x_perm)
+    h = grad_x_perm.shape[1]
+    out = np.empty((n, h), grad_x_perm.dtype)
+    lib().oracle_dispatch_bwd(n, k, h, _dt(grad_x_perm), _p(grad_x_perm), _p(lay["assign_row"]), _p(out))
     return out
 
 

@@ -317,6 +317,28 @@ void oracle_combine(int64_t n, int k, int64_t h, int dt, const void *y, const fl
   }
 }
 
+/* Dispatch backward: the vector-Jacobian product of the row scatter (dispatch
+ * copies token t's row to the rows of its kept slots; the MORI pull request
+ * ROCm/Megatron-LM "Add MORI as a Token Dispatcher" lists the unpermute /
+ * dispatch backward among the paths it fixes).  For each token t:
+ *   grad_x[t, :] = sum over kept slots j, in slot order, of grad_x_perm[assign_row[t,j], :]
+ * fp32 accumulation, one rounding to the activation type; a token with no kept
+ * slot gets a zero row. */
+void oracle_dispatch_bwd(int64_t n, int k, int64_t h, int dt, const void *grad_x_perm, const int32_t *assign_row,
+                         void *grad_x) {
+  for (int64_t t = 0; t < n; ++t) {
+    for (int64_t c = 0; c < h; ++c) {
+      float acc = 0.0f;
+      for (int j = 0; j < k; ++j) {
+        int32_t r = assign_row[t * k + j];
+        if (r < 0) continue;
+        acc = acc + (float)act_load(grad_x_perm, dt, (int64_t)r * h + c);
+      }
+      act_store(grad_x, dt, t * h + c, (double)acc);
+    }
+  }
+}
+
 /* Combine backward (the vector-Jacobian product of the combine above; the MORI
  * commit log's combine backward takes the receiver-side weights and indices).
  * For each kept assignment a = (t, j) in row r:

@@ -357,6 +357,54 @@ def test_scatter_bitwise(dt, capacity):
         assert (xp[pads].view(np.uint8) == 0).all()
 
 
+# ------------------------------------------------------ dispatch backward
+
+def _dispatch_case(dt, capacity, seed, n=41, k=3, e=6, h=24):
+    g = np.random.default_rng(seed)
+    idx = np.stack([g.permutation(e)[:k] for _ in range(n)]).astype(np.int32)
+    idx[g.random(idx.shape) < 0.15] = -1
+    lay = oracle.layout(idx, e, capacity)
+    return g, idx, lay, n, k, h
+
+
+@pytest.mark.parametrize("capacity", [0, 3])
+def test_dispatch_bwd_is_adjoint_of_scatter_exactly(capacity):
+    # small integers: every fp32 sum below is exact, so <dx, x> = <dxp, scatter(x)> holds exactly
+    g, idx, lay, n, k, h = _dispatch_case(mi.DT_F32, capacity, 31)
+    x = g.integers(-8, 9, (n, h)).astype(np.float32)
+    dxp = g.integers(-8, 9, (lay["rows"], h)).astype(np.float32)
+    xp, _ = oracle.scatter(x, k, lay, np.ones((n, k), np.float32), capacity)
+    dx = oracle.dispatch_bwd(dxp, lay, n, k)
+    assert (dx.astype(np.float64) * x).sum() == (dxp.astype(np.float64) * xp).sum()
+
+
+@pytest.mark.parametrize("dt,capacity", [(mi.DT_F32, 0), (mi.DT_BF16, 0), (mi.DT_BF16, 2)])
+def test_dispatch_bwd_dense_matrix(dt, capacity):
+    # brute force: grad_x = M @ grad_x_perm with M[t, r] = number of kept slots of t in row r
+    g, idx, lay, n, k, h = _dispatch_case(dt, capacity, 32 + capacity)
+    dxp = mi.normal_activations((lay["rows"], h), dt, 5, 5)
+    dx = oracle.dispatch_bwd(dxp, lay, n, k)
+    M = np.zeros((n, lay["rows"]))
+    for a, r in enumerate(lay["assign_row"]):
+        if r >= 0:
+            M[a // k, r] += 1.0
+    val = (lambda a: a.astype(np.float64)) if dt == mi.DT_F32 else bf16_vals
+    ref = M @ val(dxp)
+    got = val(dx)
+    tol = (2.0 ** -22 if dt == mi.DT_F32 else 2.0 ** -7) * (M @ np.abs(val(dxp))) + 1e-30
+    assert (np.abs(got - ref) <= tol).all()
+    none_kept = (lay["assign_row"].reshape(n, k) < 0).all(1)
+    assert (dx[none_kept].view(np.uint8) == 0).all()
+
+
+def test_dispatch_bwd_single_slot_is_inverse_permutation():
+    g, idx, lay, n, k, h = _dispatch_case(mi.DT_BF16, 0, 33, k=1)
+    dxp = mi.normal_activations((lay["rows"], h), mi.DT_BF16, 6, 6)
+    dx = oracle.dispatch_bwd(dxp, lay, n, 1)
+    kept = lay["assign_row"] >= 0
+    assert (dx[kept].view(np.uint8) == dxp[lay["assign_row"][kept]].view(np.uint8)).all()
+
+
 # ------------------------------------------------------------------- combine
 
 @pytest.mark.parametrize("dt", [mi.DT_F32, mi.DT_BF16])
