@@ -108,6 +108,19 @@ def bench_dispatch_combine(moe, mi, torch, steps, warmup):
     torch.cuda.synchronize()
     bwd_ms = b0.elapsed_time(b1) / steps
     bwd_bytes = n * row_b + kept * row_b * 2
+    # dispatch backward (grad of the token rows) on the same layout
+    gx = torch.empty_like(x)
+    for _ in range(warmup):
+        moe.moe_dispatch_bwd(gy, lay, out=gx)
+    torch.cuda.synchronize()
+    d0 = torch.cuda.Event(enable_timing=True)
+    d1 = torch.cuda.Event(enable_timing=True)
+    d0.record()
+    for _ in range(steps):
+        moe.moe_dispatch_bwd(gy, lay, out=gx)
+    d1.record()
+    torch.cuda.synchronize()
+    dbwd_ms = d0.elapsed_time(d1) / steps
     # the roofline kernel alone: back-to-back combine launches on the stream
     c0 = torch.cuda.Event(enable_timing=True)
     c1 = torch.cuda.Event(enable_timing=True)
@@ -146,7 +159,7 @@ def bench_dispatch_combine(moe, mi, torch, steps, warmup):
     copy_gbs = 2 * flush.numel() * 4 / (k0.elapsed_time(k1) / 5 * 1e-3) / 1e9
     del flush, dst
     return dict(total_ms=total_ms, route_ms=route_ms, dispatch_ms=disp_ms, combine_ms=comb_ms,
-                comb_kernel_ms=comb_kernel_ms, kept=kept, copy_gbs=copy_gbs,
+                comb_kernel_ms=comb_kernel_ms, kept=kept, copy_gbs=copy_gbs, dbwd_ms=dbwd_ms,
                 dc_p10=pct([r_[1].elapsed_time(r_[3]) for r_ in recs], 10),
                 dc_p90=pct([r_[1].elapsed_time(r_[3]) for r_ in recs], 90),
                 cold_route_ms=median(cold_route), cold_dispatch_ms=median(cold_disp),
@@ -339,6 +352,8 @@ def main():
         "copy_gbs": round(dc["copy_gbs"], 1),
         "dispatch_combine_frac_of_copy": round(byts / ((dc["dispatch_ms"] + dc["combine_ms"]) * 1e-3) / 1e9
                                                / dc["copy_gbs"], 4),
+        "dispatch_bwd_us": round(dc["dbwd_ms"] * 1e3, 2),
+        "dispatch_bwd_gbs": round(dc["combine_bytes"] / (dc["dbwd_ms"] * 1e-3) / 1e9, 2),
         "combine_bwd_us": round(dc["bwd_ms"] * 1e3, 2),
         "combine_bwd_gbs": round(dc["bwd_bytes"] / (dc["bwd_ms"] * 1e-3) / 1e9, 2),
         "roofline": {"kernel": "combine_kernel<true, 8>", "bound": "hbm", "achieved": round(comb_gbs, 1),

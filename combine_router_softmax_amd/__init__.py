@@ -24,7 +24,7 @@ MOE_OP_ROUTE, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE, MOE_OP_COMBINE
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_layout_rows", "moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-           "moe_combine_bwd", "moe_status_string", "moe_version")
+           "moe_dispatch_bwd", "moe_combine_bwd", "moe_status_string", "moe_version")
 
 
 class MoeShape(C.Structure):
@@ -58,7 +58,9 @@ def _load():
     lib.moe_expert_ffn.argtypes = [sp, p, lp, p, p, p, p, C.c_size_t, p]
     lib.moe_combine.argtypes = [sp, p, p, lp, p, p]
     lib.moe_combine_bwd.argtypes = [sp, p, p, p, lp, p, p, p]
-    for f in ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_combine_bwd"):
+    lib.moe_dispatch_bwd.argtypes = [sp, p, lp, p, p]
+    for f in ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_combine_bwd",
+              "moe_dispatch_bwd"):
         getattr(lib, f).restype = i32
     lib.moe_status_string.argtypes = [i32]
     lib.moe_status_string.restype = C.c_char_p
@@ -261,6 +263,20 @@ def moe_combine(y: torch.Tensor, topk_w: torch.Tensor, layout: Layout, *, out: t
     return out
 
 
+def moe_dispatch_bwd(grad_x_perm: torch.Tensor, layout: Layout, *, out: torch.Tensor | None = None):
+    """Backward of the row scatter of moe_dispatch (include/moe.h moe_dispatch_bwd) -> grad_x [N, H]."""
+    _contig(grad_x_perm, "grad_x_perm")
+    h = grad_x_perm.shape[1]
+    dt = _act_dtype(grad_x_perm)
+    if out is None:
+        out = torch.empty((layout.n_tokens, h), dtype=grad_x_perm.dtype, device=grad_x_perm.device)
+    shape = layout.shape(h, dt)
+    lc = layout.c()
+    _check(lib.moe_dispatch_bwd(C.byref(shape), _ptr(grad_x_perm), C.byref(lc), _ptr(out),
+                                _stream(grad_x_perm.device)), "moe_dispatch_bwd")
+    return out
+
+
 def moe_combine_bwd(grad_out: torch.Tensor, y: torch.Tensor, topk_w: torch.Tensor, layout: Layout, *,
                     grad_y: torch.Tensor | None = None, grad_w: torch.Tensor | None = None):
     """Backward of moe_combine (include/moe.h moe_combine_bwd) -> (grad_y [R, H], grad_w fp32 [N, k])."""
@@ -281,5 +297,6 @@ def moe_combine_bwd(grad_out: torch.Tensor, y: torch.Tensor, topk_w: torch.Tenso
     return grad_y, grad_w
 
 
-__all__ = ["moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_combine_bwd", "Layout", "RouteOut",
+__all__ = ["moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_combine_bwd", "moe_dispatch_bwd",
+           "Layout", "RouteOut",
            "MoeError", "make_shape", "workspace_size", "lib", "library_path", "EXPORTS"]

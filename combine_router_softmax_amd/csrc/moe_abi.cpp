@@ -171,6 +171,22 @@ moe_status moe_combine(const moe_shape *s, const void *y, const float *topk_w, c
                                         row_bytes, out, as_stream(stream)));
 }
 
+moe_status moe_dispatch_bwd(const moe_shape *s, const void *grad_x_perm, const moe_layout *layout, void *grad_x,
+                            void *stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  int64_t row_bytes, rows;
+  if ((st = check_rows(s, &row_bytes, &rows)) != MOE_OK) return st;
+  const int64_t n = s->n_tokens;
+  if (!layout) return MOE_ERR_INVALID_ARG;
+  if (n > 0 && (!layout->assign_row || !grad_x || (rows > 0 && !grad_x_perm))) return MOE_ERR_INVALID_ARG;
+  if (!need(grad_x_perm, rows, aligned16) || !need(grad_x, n, aligned16)) return MOE_ERR_MISALIGNED;
+  if (n > 0 && grad_x_perm == grad_x) return MOE_ERR_INVALID_ARG;
+  // the combine with unit weights: same kernel, same slot order
+  return hip_status(moe::launch_combine(s->act_dtype == MOE_DT_BF16, grad_x_perm, nullptr, layout->assign_row, n,
+                                        s->top_k, row_bytes, grad_x, as_stream(stream)));
+}
+
 moe_status moe_combine_bwd(const moe_shape *s, const void *grad_out, const void *y, const float *topk_w,
                            const moe_layout *layout, void *grad_y, float *grad_w, void *stream) {
   moe_status st = check_shape(s);

@@ -24,6 +24,7 @@ hipError_t launch_layout(const int32_t *topk_idx, const float *topk_w, int64_t n
 // ---- row movement (moe_rows.hip); `row_bytes` is a multiple of 16
 hipError_t launch_scatter(const void *x, int64_t n, int k, int64_t row_bytes, const int32_t *assign_row,
                           void *x_perm, int64_t pad_rows, const int32_t *row_src, hipStream_t stream);
+// topk_w may be null: unit weights (the dispatch backward)
 hipError_t launch_combine(bool bf16, const void *y, const float *topk_w, const int32_t *assign_row, int64_t n,
                           int k, int64_t row_bytes, void *out, hipStream_t stream);
 hipError_t launch_combine_bwd(bool bf16, const void *grad_out, const void *y, const float *topk_w,

@@ -94,7 +94,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(const void *__rest
 #pragma unroll
       for (int j = 0; j < KC; ++j) {
         rows[j] = j0 + j < k ? assign_row[t * k + j0 + j] : -1;
-        wts[j] = j0 + j < k ? topk_w[t * k + j0 + j] : 0.0f;
+        wts[j] = j0 + j < k ? (topk_w ? topk_w[t * k + j0 + j] : 1.0f) : 0.0f;  // no weights: unit weights
       }
 #pragma unroll
       for (int j = 0; j < KC; ++j)

@@ -7,6 +7,7 @@
  *   moe_expert_ffn  grouped SwiGLU expert GEMM (bf16 MFMA, fp32 accumulation)
  *   moe_combine     probability-weighted unpermute / combine (fp32 accumulation)
  *   moe_combine_bwd backward of moe_combine (grad of expert rows, grad of weights)
+ *   moe_dispatch_bwd backward of the row scatter (grad of the token rows)
  *
  * The steps follow the four stages of Megatron-Core's MoELayer.forward as laid
  * out on the page "Megatron MoE 实现" (router -> (probs, routing_map);
@@ -170,6 +171,19 @@ moe_status moe_expert_ffn(const moe_shape *s, const void *x_perm, const moe_layo
  * For an identity expert pass x_perm as y.  No workspace. */
 moe_status moe_combine(const moe_shape *s, const void *y, const float *topk_w, const moe_layout *layout,
                        void *out, void *stream);
+
+/* Dispatch backward: the vector-Jacobian product of the row scatter of
+ * moe_dispatch (the unpermute backward of the MORI pull request
+ * ROCm/Megatron-LM "Add MORI as a Token Dispatcher"): for every token t,
+ *   grad_x[t, :] = sum over kept slots j, in slot order, of
+ *                  grad_x_perm[assign_row[t*k + j], :]
+ * with an fp32 accumulator and one rounding to the activation type; a token with
+ * no kept slot gets a zero row.  grad_x_perm: [max_rows, hidden] rows as laid
+ * out by moe_dispatch; grad_x: [n_tokens, hidden]; both in act_dtype, 16-byte
+ * aligned, grad_x must not alias grad_x_perm.  No workspace.  Errors as
+ * moe_combine. */
+moe_status moe_dispatch_bwd(const moe_shape *s, const void *grad_x_perm, const moe_layout *layout, void *grad_x,
+                            void *stream);
 
 /* Combine backward: the vector-Jacobian product of moe_combine (the MORI pull
  * request's combine backward, with receiver-side weights and indices).

@@ -26,7 +26,7 @@ def moe():
 
 def test_library_exports_every_declared_function(moe):
     declared = header_functions()
-    assert len(declared) == 9, declared
+    assert len(declared) == 10, declared
     assert sorted(moe.EXPORTS) == declared
     for name in declared:
         assert hasattr(moe.lib, name), name
@@ -102,4 +102,7 @@ def test_validation_errors_enqueue_nothing(moe):
     assert lib.moe_expert_ffn(C.byref(s), p, C.byref(lay), p, p, p, p, 16, None) == -3
     assert lib.moe_combine(C.byref(s), p, p, C.byref(lay), p, None) == -1     # out aliases y
     assert lib.moe_combine(C.byref(s), odd, p, C.byref(lay), p, None) == -2
+    assert lib.moe_dispatch_bwd(C.byref(s), p, C.byref(lay), p, None) == -1         # grad_x aliases grad_x_perm
+    assert lib.moe_dispatch_bwd(C.byref(s), odd, C.byref(lay), p, None) == -2
+    assert lib.moe_dispatch_bwd(C.byref(s), p, None, C.c_void_p(8192), None) == -1   # no layout
     assert lib.moe_combine_bwd(C.byref(s), p, p, p, C.byref(lay), p, p, None) == -1  # grad_y aliases

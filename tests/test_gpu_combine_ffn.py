@@ -90,6 +90,45 @@ def check_combine_bwd(moe, idx, wts, e, capacity, go, y, max_rows=0):
 
 
 @pytest.mark.parametrize("dt", [mi.DT_F32, mi.DT_BF16])
+@pytest.mark.parametrize("capacity", [0, 5])
+def test_dispatch_bwd_random_rows_with_drops_and_sentinels(moe, dt, capacity):
+    g = np.random.default_rng(60 + capacity + dt)
+    n, k, e, h = 301, 4, 9, 200
+    idx = np.stack([g.permutation(e)[:k] for _ in range(n)]).astype(np.int32)
+    idx[g.random(idx.shape) < 0.2] = -1
+    wts = g.random((n, k)).astype(np.float32)
+    x = mi.normal_activations((n, h), dt, 61, 1)
+    xp, wp, lay = moe.moe_dispatch(dev(x), dev(idx), dev(wts), e, capacity=capacity)
+    lay_h = oracle.layout(idx, e, capacity)
+    gxp = mi.normal_activations((lay_h["rows"], h), dt, 62, 2)
+    got = host(moe.moe_dispatch_bwd(dev(gxp), lay))
+    ref = oracle.dispatch_bwd(gxp, lay_h, n, k)
+    # same fp32 adds in the same slot order, one rounding: bit for bit
+    assert (got.view(np.uint8) == ref.view(np.uint8)).all()
+
+
+@pytest.mark.parametrize("wid", [2, 3])
+def test_dispatch_bwd_full_size(moe, wid):
+    w = mi.workload(wid)
+    idx, wts, _, _ = oracle.route(mi.router_logits(w), w.top_k)
+    lay_h = oracle.layout(idx, w.n_experts, w.capacity)
+    x = mi.activations(w)
+    _, _, lay = moe.moe_dispatch(dev(x), dev(idx), dev(wts), w.n_experts, capacity=w.capacity)
+    gxp = mi.normal_activations((lay_h["rows"], w.hidden), mi.DT_BF16, 63, 3)
+    got = host(moe.moe_dispatch_bwd(dev(gxp), lay))
+    ref = oracle.dispatch_bwd(gxp, lay_h, w.n_tokens, w.top_k)
+    assert (got.view(np.uint8) == ref.view(np.uint8)).all()
+
+
+def test_dispatch_bwd_empty(moe):
+    idx = np.zeros((0, 2), np.int32)
+    x = np.zeros((0, 64), np.float32)
+    _, _, lay = moe.moe_dispatch(dev(x), dev(idx), dev(np.zeros((0, 2), np.float32)), 4)
+    out = moe.moe_dispatch_bwd(dev(np.zeros((0, 64), np.float32)), lay)
+    assert tuple(out.shape) == (0, 64)
+
+
+@pytest.mark.parametrize("dt", [mi.DT_F32, mi.DT_BF16])
 @pytest.mark.parametrize("capacity", [0, 7])
 def test_combine_bwd_small(moe, dt, capacity):
     g = np.random.default_rng(60 + dt + capacity)
