@@ -63,6 +63,8 @@ def lib():
         L.oracle_dispatch_bwd.restype = None
         L.oracle_combine_bwd.restype = None
         L.oracle_bf16_round.argtypes = [C.c_double]
+        L.oracle_bf16_round_array.argtypes = [i64, p, p]
+        L.oracle_bf16_round_array.restype = None
         L.oracle_bf16_round.restype = C.c_uint16
         _lib = L
     return _lib
@@ -193,6 +195,63 @@ def combine_bwd(grad_out: np.ndarray, y: np.ndarray, topk_w: np.ndarray, lay: di
                              _p(np.ascontiguousarray(topk_w, dtype=np.float32)), _p(lay["assign_row"]),
                              rows, _p(lay["row_src"]), capacity, _p(grad_y), _p(grad_w))
     return grad_y, grad_w
+
+
+def bf16_round_array(x: np.ndarray) -> np.ndarray:
+    """double -> bf16 bits (round to nearest, ties to even), element-wise."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    out = np.empty(x.shape, np.uint16)
+    lib().oracle_bf16_round_array(x.size, _p(x), _p(out))
+    return out
+
+
+def _bf16_f64(b: np.ndarray) -> np.ndarray:
+    """bf16 bits -> float64 (exact: the bits are the top half of an fp32)."""
+    return (np.asarray(b, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def expert_ffn_bwd(x_perm, grad_y, lay, w_gate_up, w_down, round_out=True):
+    """Backward of the grouped SwiGLU FFN, per expert segment (rows
+    expert_offsets[e] .. + tokens_per_expert[e]) of the expert-contiguous buffer.
+
+    With G = X Wg^T, U = X Wu^T, s = sigmoid(G), A = G s U, Y = A Wd^T and the
+    incoming dY:
+        dA = dY Wd,  dG = dA U s (1 + G (1 - s)),  dU = dA G s,
+        dX = dG Wg + dU Wu,  dWd = dY^T A,  dWg = dG^T X,  dWu = dU^T X
+    (the chain rule through y = Wd (silu(Wg x) * (Wu x)); silu'(g) = s(1 + g(1 - s))).
+    fp64 numpy matmuls, no intermediate rounding.  Inputs are bf16 bits (or
+    float64 arrays, used as they are).  Returns (grad_x_perm [R, H],
+    grad_w_gate_up [E, 2I, H], grad_w_down [E, H, I]) as bf16 bits, each value
+    rounded once (round_out=False: the float64 values).  Rows outside the
+    segments of grad_x_perm are zero; experts without rows get zero gradients.
+    """
+    e, two_i, h = w_gate_up.shape
+    inter = two_i // 2
+    f64 = lambda a: a if a.dtype == np.float64 else _bf16_f64(a)  # float64 inputs are taken as they are
+    xv, gyv, wgu, wdv = f64(x_perm), f64(grad_y), f64(w_gate_up), f64(w_down)
+    gx = np.zeros((lay["rows"], h))
+    dwgu = np.zeros((e, two_i, h))
+    dwd = np.zeros((e, h, inter))
+    for ex in range(e):
+        o, n = int(lay["expert_offsets"][ex]), int(lay["tokens_per_expert"][ex])
+        if n == 0:
+            continue
+        x, dy = xv[o:o + n], gyv[o:o + n]
+        wg, wu, wd = wgu[ex, :inter], wgu[ex, inter:], wdv[ex]
+        g = x @ wg.T
+        u = x @ wu.T
+        s = 1.0 / (1.0 + np.exp(-g))
+        a = g * s * u
+        da = dy @ wd
+        dg = da * u * s * (1.0 + g * (1.0 - s))
+        du = da * g * s
+        gx[o:o + n] = dg @ wg + du @ wu
+        dwd[ex] = dy.T @ a
+        dwgu[ex, :inter] = dg.T @ x
+        dwgu[ex, inter:] = du.T @ x
+    if not round_out:
+        return gx, dwgu, dwd
+    return bf16_round_array(gx), bf16_round_array(dwgu), bf16_round_array(dwd)
 
 
 def bf16_round(x: float) -> int:

@@ -13,7 +13,9 @@
  *     required "fp32 combine accumulation"), one rounding to the output type;
  *   - expert FFN: double accumulation, bf16 rounding of the SwiGLU intermediate
  *     and of the output (both are bf16 tensors in the method);
- *   - combine backward: double, one rounding per stored value.
+ *   - combine backward: double, one rounding per stored value;
+ *   - expert FFN backward (oracle/__init__.py, numpy fp64 matmuls per expert):
+ *     double throughout, one rounding per stored value.
  * Compiled with -O2 -ffp-contract=off so no fused operation appears that the
  * source does not write.
  *
@@ -371,3 +373,8 @@ void oracle_combine_bwd(int64_t n, int k, int64_t h, int dt, const void *grad_ou
 
 /* Exposed for the tests that pin the number formats. */
 uint16_t oracle_bf16_round(double x) { return bf16_round(x); }
+
+/* Element-wise double -> bf16 (round to nearest, ties to even) of n values. */
+void oracle_bf16_round_array(int64_t n, const double *x, uint16_t *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = bf16_round(x[i]);
+}

@@ -598,3 +598,86 @@ def test_ffn_rows_outside_segments_untouched():
     lay2["tokens_per_expert"][-1] = max(0, lay2["tokens_per_expert"][-1] - 1)
     _, ex = oracle.expert_ffn_rows(rows, xp, lay2, wgu, wd)
     assert ex[0] == -1 and ex[1] >= 0
+
+
+# ------------------------------------------------------- expert FFN backward
+
+def _ffn_forward_f64(x, wgu, wd, lay):
+    """Independent fp64 forward of the grouped SwiGLU FFN (no rounding)."""
+    e, two_i, _ = wgu.shape
+    inter = two_i // 2
+    y = np.zeros((x.shape[0], wd.shape[1]))
+    for ex in range(e):
+        o, n = int(lay["expert_offsets"][ex]), int(lay["tokens_per_expert"][ex])
+        for r in range(o, o + n):
+            gv = wgu[ex, :inter] @ x[r]
+            uv = wgu[ex, inter:] @ x[r]
+            y[r] = wd[ex] @ (gv / (1.0 + np.exp(-gv)) * uv)
+    return y
+
+
+def _ffn_bwd_case(seed=5, capacity=0):
+    g = np.random.default_rng(seed)
+    n, k, e, h, inter = 9, 2, 3, 8, 4
+    idx = np.stack([g.permutation(e)[:k] for _ in range(n)]).astype(np.int32)
+    idx[0, :] = [0, 2]
+    idx[:, :][idx == 1] = 0            # expert 1 receives no rows
+    lay = oracle.layout(idx, e, capacity)
+    x = g.standard_normal((lay["rows"], h))
+    wgu = g.standard_normal((e, 2 * inter, h)) * 0.5
+    wd = g.standard_normal((e, h, inter)) * 0.5
+    dy = g.standard_normal((lay["rows"], h))
+    return lay, x, wgu, wd, dy
+
+
+def test_ffn_bwd_central_finite_differences():
+    lay, x, wgu, wd, dy = _ffn_bwd_case()
+    gx, dwgu, dwd = oracle.expert_ffn_bwd(x, dy, lay, wgu, wd, round_out=False)
+    loss = lambda x_, wgu_, wd_: (_ffn_forward_f64(x_, wgu_, wd_, lay) * dy).sum()
+    g = np.random.default_rng(6)
+    eps = 1e-6
+    in_seg = np.nonzero(lay["pad_mask"] == 0)[0]
+    checks = []
+    for _ in range(12):                # inputs: rows of the segments
+        r, c = int(g.choice(in_seg)), int(g.integers(x.shape[1]))
+        xp, xm = x.copy(), x.copy()
+        xp[r, c] += eps
+        xm[r, c] -= eps
+        checks.append(((loss(xp, wgu, wd) - loss(xm, wgu, wd)) / (2 * eps), gx[r, c]))
+    for _ in range(12):                # gate and up weights of experts 0 and 2
+        ex, i, c = int(g.choice([0, 2])), int(g.integers(wgu.shape[1])), int(g.integers(wgu.shape[2]))
+        wp, wm = wgu.copy(), wgu.copy()
+        wp[ex, i, c] += eps
+        wm[ex, i, c] -= eps
+        checks.append(((loss(x, wp, wd) - loss(x, wm, wd)) / (2 * eps), dwgu[ex, i, c]))
+    for _ in range(12):                # down weights
+        ex, i, c = int(g.choice([0, 2])), int(g.integers(wd.shape[1])), int(g.integers(wd.shape[2]))
+        wp, wm = wd.copy(), wd.copy()
+        wp[ex, i, c] += eps
+        wm[ex, i, c] -= eps
+        checks.append(((loss(x, wgu, wp) - loss(x, wgu, wm)) / (2 * eps), dwd[ex, i, c]))
+    for fd, an in checks:
+        assert abs(fd - an) <= 1e-6 * (1 + abs(fd)), (fd, an)
+
+
+def test_ffn_bwd_euler_in_down_weights_and_empty_expert():
+    lay, x, wgu, wd, dy = _ffn_bwd_case(7)
+    gx, dwgu, dwd = oracle.expert_ffn_bwd(x, dy, lay, wgu, wd, round_out=False)
+    # y is linear in W_down: <grad W_down, W_down> = <dY, Y>
+    y = _ffn_forward_f64(x, wgu, wd, lay)
+    assert abs((dwd * wd).sum() - (dy * y).sum()) <= 1e-9 * (np.abs(dy * y).sum() + 1)
+    assert lay["tokens_per_expert"][1] == 0
+    assert (dwgu[1] == 0).all() and (dwd[1] == 0).all()
+    outside = lay["pad_mask"] != 0
+    assert (gx[outside] == 0).all()
+
+
+def test_ffn_bwd_rounding_is_one_rne_per_value():
+    lay, x, wgu, wd, dy = _ffn_bwd_case(8)
+    exact = oracle.expert_ffn_bwd(x, dy, lay, wgu, wd, round_out=False)
+    rounded = oracle.expert_ffn_bwd(x, dy, lay, wgu, wd)
+    for a, b in zip(exact, rounded):
+        a, b = a.reshape(-1), b.reshape(-1)
+        nz = a != 0                    # the reference rounding covers the normal range
+        assert (bf16_from_double_ref(a[nz]) == b[nz]).all()
+        assert (b[~nz] & 0x7FFF == 0).all()
