@@ -1,5 +1,6 @@
 """MI355X (gfx950) single-GPU Mixture-of-Experts path: route -> dispatch ->
-grouped SwiGLU expert FFN -> combine (+ combine backward).
+grouped SwiGLU expert FFN -> combine (+ the backward of combine, expert FFN and
+dispatch).
 
 A thin ctypes binding over the C ABI of libmoe_mi355x.so (include/moe.h).  It
 only marshals arguments: tensors are passed as device pointers with
@@ -20,11 +21,12 @@ _LIB_PATH = Path(__file__).resolve().parent / "libmoe_mi355x.so"
 
 MOE_DT_F32 = 0
 MOE_DT_BF16 = 1
-MOE_OP_ROUTE, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE, MOE_OP_COMBINE_BWD = range(5)
+MOE_OP_ROUTE, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE, MOE_OP_COMBINE_BWD, MOE_OP_EXPERT_FFN_BWD = range(6)
 
 # Every symbol include/moe.h declares.
-EXPORTS = ("moe_layout_rows", "moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
-           "moe_dispatch_bwd", "moe_combine_bwd", "moe_status_string", "moe_version")
+EXPORTS = ("moe_layout_rows", "moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn",
+           "moe_expert_ffn_bwd", "moe_combine", "moe_dispatch_bwd", "moe_combine_bwd", "moe_status_string",
+           "moe_version")
 
 
 class MoeShape(C.Structure):
@@ -56,11 +58,12 @@ def _load():
     lib.moe_route.argtypes = [sp, p, p, p, p, p, p]
     lib.moe_dispatch.argtypes = [sp, p, p, p, lp, p, p, p, C.c_size_t, p]
     lib.moe_expert_ffn.argtypes = [sp, p, lp, p, p, p, p, C.c_size_t, p]
+    lib.moe_expert_ffn_bwd.argtypes = [sp, p, p, lp, p, p, p, p, p, p, C.c_size_t, p]
     lib.moe_combine.argtypes = [sp, p, p, lp, p, p]
     lib.moe_combine_bwd.argtypes = [sp, p, p, p, lp, p, p, p]
     lib.moe_dispatch_bwd.argtypes = [sp, p, lp, p, p]
-    for f in ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_combine_bwd",
-              "moe_dispatch_bwd"):
+    for f in ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_bwd", "moe_combine",
+              "moe_combine_bwd", "moe_dispatch_bwd"):
         getattr(lib, f).restype = i32
     lib.moe_status_string.argtypes = [i32]
     lib.moe_status_string.restype = C.c_char_p
@@ -248,6 +251,41 @@ def moe_expert_ffn(x_perm: torch.Tensor, layout: Layout, w_gate_up: torch.Tensor
     return y
 
 
+def moe_expert_ffn_bwd(x_perm: torch.Tensor, grad_y: torch.Tensor, layout: Layout, w_gate_up: torch.Tensor,
+                       w_down: torch.Tensor, *, grad_x_perm: torch.Tensor | None = None,
+                       grad_w_gate_up: torch.Tensor | None = None, grad_w_down: torch.Tensor | None = None,
+                       workspace=None):
+    """Backward of the grouped SwiGLU FFN (include/moe.h moe_expert_ffn_bwd)
+    -> (grad_x_perm [R, H], grad_w_gate_up [E, 2I, H], grad_w_down [E, H, I]), all bf16."""
+    for t, name in ((x_perm, "x_perm"), (grad_y, "grad_y"), (w_gate_up, "w_gate_up"), (w_down, "w_down")):
+        _contig(t, name)
+        if t.dtype != torch.bfloat16:
+            raise TypeError(f"{name} must be bfloat16")
+    rows, h = x_perm.shape
+    e, two_i, h2 = w_gate_up.shape
+    inter = two_i // 2
+    if (h2 != h or tuple(w_down.shape) != (e, h, inter) or tuple(grad_y.shape) != (rows, h)
+            or e != layout.n_experts or rows != layout.rows):
+        raise ValueError("inconsistent expert FFN shapes")
+    dev = x_perm.device
+    shape = layout.shape(h, MOE_DT_BF16, inter)
+    if grad_x_perm is None:
+        grad_x_perm = torch.empty_like(x_perm)
+    if grad_w_gate_up is None:
+        grad_w_gate_up = torch.empty_like(w_gate_up)
+    if grad_w_down is None:
+        grad_w_down = torch.empty_like(w_down)
+    if workspace is None:
+        ws, nbytes = _workspace(MOE_OP_EXPERT_FFN_BWD, shape, dev)
+    else:
+        ws, nbytes = workspace, workspace.numel() - 256
+    lc = layout.c()
+    _check(lib.moe_expert_ffn_bwd(C.byref(shape), _ptr(x_perm), _ptr(grad_y), C.byref(lc), _ptr(w_gate_up),
+                                  _ptr(w_down), _ptr(grad_x_perm), _ptr(grad_w_gate_up), _ptr(grad_w_down),
+                                  _ws_ptr(ws), nbytes, _stream(dev)), "moe_expert_ffn_bwd")
+    return grad_x_perm, grad_w_gate_up, grad_w_down
+
+
 def moe_combine(y: torch.Tensor, topk_w: torch.Tensor, layout: Layout, *, out: torch.Tensor | None = None):
     """Probability-weighted combine (include/moe.h moe_combine) -> out [N, H]."""
     _contig(y, "y")
@@ -297,6 +335,7 @@ def moe_combine_bwd(grad_out: torch.Tensor, y: torch.Tensor, topk_w: torch.Tenso
     return grad_y, grad_w
 
 
-__all__ = ["moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_combine_bwd", "moe_dispatch_bwd",
+__all__ = ["moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_bwd", "moe_combine", "moe_combine_bwd",
+           "moe_dispatch_bwd",
            "Layout", "RouteOut",
            "MoeError", "make_shape", "workspace_size", "lib", "library_path", "EXPORTS"]

@@ -59,6 +59,19 @@ bool need(const void *p, int64_t elems, bool (*aligned)(const void *)) {
   return elems == 0 || p == nullptr || aligned(p);
 }
 
+// Checks shared by the forward and backward expert FFN.
+moe_status check_ffn_shape(const moe_shape *s, int64_t *rows) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  int64_t row_bytes;
+  if ((st = check_rows(s, &row_bytes, rows)) != MOE_OK) return st;
+  if (s->act_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
+  if (s->inter < 1) return MOE_ERR_INVALID_ARG;
+  if (s->inter % 64 != 0 || s->hidden % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if (4 * (int64_t)s->inter * s->hidden >= (int64_t)1 << 32) return MOE_ERR_UNSUPPORTED;  // 32-bit weight offsets
+  return MOE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -84,6 +97,10 @@ moe_status moe_workspace_size(moe_op op, const moe_shape *s, size_t *bytes) {
     case MOE_OP_EXPERT_FFN:
       if (s->inter < 1) return MOE_ERR_INVALID_ARG;
       *bytes = moe::ffn_workspace_bytes(rows_of(s), s->inter);
+      return MOE_OK;
+    case MOE_OP_EXPERT_FFN_BWD:
+      if (s->inter < 1) return MOE_ERR_INVALID_ARG;
+      *bytes = moe::ffn_bwd_workspace_bytes(rows_of(s), s->hidden, s->inter, s->n_experts);
       return MOE_OK;
   }
   return MOE_ERR_INVALID_ARG;
@@ -133,14 +150,9 @@ moe_status moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_i
 
 moe_status moe_expert_ffn(const moe_shape *s, const void *x_perm, const moe_layout *layout, const void *w_gate_up,
                           const void *w_down, void *y, void *workspace, size_t workspace_bytes, void *stream) {
-  moe_status st = check_shape(s);
+  int64_t rows;
+  moe_status st = check_ffn_shape(s, &rows);
   if (st != MOE_OK) return st;
-  int64_t row_bytes, rows;
-  if ((st = check_rows(s, &row_bytes, &rows)) != MOE_OK) return st;
-  if (s->act_dtype != MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
-  if (s->inter < 1) return MOE_ERR_INVALID_ARG;
-  if (s->inter % 64 != 0 || s->hidden % 64 != 0) return MOE_ERR_UNSUPPORTED;
-  if (4 * (int64_t)s->inter * s->hidden >= (int64_t)1 << 32) return MOE_ERR_UNSUPPORTED;  // 32-bit weight offsets
   if (!layout || !layout->tokens_per_expert || !layout->expert_offsets || !w_gate_up || !w_down)
     return MOE_ERR_INVALID_ARG;
   if (rows > 0 && (!x_perm || !y)) return MOE_ERR_INVALID_ARG;
@@ -154,6 +166,37 @@ moe_status moe_expert_ffn(const moe_shape *s, const void *x_perm, const moe_layo
                                            layout->expert_offsets, static_cast<const uint16_t *>(w_gate_up),
                                            static_cast<const uint16_t *>(w_down), static_cast<uint16_t *>(y),
                                            workspace, as_stream(stream)));
+}
+
+moe_status moe_expert_ffn_bwd(const moe_shape *s, const void *x_perm, const void *grad_y, const moe_layout *layout,
+                              const void *w_gate_up, const void *w_down, void *grad_x_perm, void *grad_w_gate_up,
+                              void *grad_w_down, void *workspace, size_t workspace_bytes, void *stream) {
+  int64_t rows;
+  moe_status st = check_ffn_shape(s, &rows);
+  if (st != MOE_OK) return st;
+  // 256 rows of a row-transposed operand are addressed with 32-bit byte offsets
+  if (moe::ffn_bwd_seg_ld(rows, s->n_experts) >= (int64_t)1 << 23) return MOE_ERR_UNSUPPORTED;
+  if (!layout || !layout->tokens_per_expert || !layout->expert_offsets || !w_gate_up || !w_down || !grad_w_gate_up ||
+      !grad_w_down)
+    return MOE_ERR_INVALID_ARG;
+  if (rows > 0 && (!x_perm || !grad_y || !grad_x_perm)) return MOE_ERR_INVALID_ARG;
+  if (!need(x_perm, rows, aligned16) || !need(grad_y, rows, aligned16) || !need(grad_x_perm, rows, aligned16) ||
+      !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(grad_w_gate_up) || !aligned16(grad_w_down))
+    return MOE_ERR_MISALIGNED;
+  const void *ins[] = {x_perm, grad_y, w_gate_up, w_down};
+  for (const void *in : ins)
+    if (in && (in == grad_x_perm || in == grad_w_gate_up || in == grad_w_down)) return MOE_ERR_INVALID_ARG;
+  if (grad_w_gate_up == grad_w_down || (grad_x_perm && (grad_x_perm == grad_w_gate_up || grad_x_perm == grad_w_down)))
+    return MOE_ERR_INVALID_ARG;
+  const size_t need_ws = moe::ffn_bwd_workspace_bytes(rows, s->hidden, s->inter, s->n_experts);
+  if (workspace_bytes < need_ws || !workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_expert_ffn_bwd(
+      static_cast<const uint16_t *>(x_perm), static_cast<const uint16_t *>(grad_y), rows, s->hidden, s->inter,
+      s->n_experts, s->capacity, layout->tokens_per_expert, layout->expert_offsets,
+      static_cast<const uint16_t *>(w_gate_up), static_cast<const uint16_t *>(w_down),
+      static_cast<uint16_t *>(grad_x_perm), static_cast<uint16_t *>(grad_w_gate_up),
+      static_cast<uint16_t *>(grad_w_down), workspace, as_stream(stream)));
 }
 
 moe_status moe_combine(const moe_shape *s, const void *y, const float *topk_w, const moe_layout *layout, void *out,

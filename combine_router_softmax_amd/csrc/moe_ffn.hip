@@ -235,29 +235,72 @@ __device__ __forceinline__ void slice(const bf16x8 (&a)[4], const bf16x8 (&b)[4]
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// kSwiGLU: B tile rows 0..127 are gate rows n0.., rows 128..255 the up rows
-// I+n0..; output the [rows, I] SwiGLU intermediate.  Otherwise a plain
-// 256-column tile of y.
-template <bool kSwiGLU>
+// Modes of the grouped GEMM.  kModePlain: per expert segment, C = A B_e^T
+// (y = act W_down^T; also the GEMMs of the backward with pre-transposed
+// weights).  kModeSwiGLU: B tile rows 0..127 are gate rows n0.., rows 128..255
+// the up rows I+n0..; output the [rows, I] SwiGLU intermediate.  kModeWGrad:
+// per expert e, C_e [M, N] = A[:, seg_e] B[:, seg_e]^T, where A [M, ld] and B
+// [N, ld] hold the experts' rows transposed, each expert's segment starting at
+// seg_offp[e] and padded with zero columns to a multiple of 64 -- the weight
+// gradients, the reduction running over the expert's rows.
+constexpr int kModePlain = 0, kModeSwiGLU = 1, kModeWGrad = 2;
+
+template <int kMode>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int64_t b_expert_stride, int K, int N,
     int n_tiles, const int32_t *__restrict__ tokens_per_expert, const int32_t *__restrict__ expert_offsets, int e,
-    uint16_t *__restrict__ C, int64_t ldc) {
+    uint16_t *__restrict__ C, int64_t ldc, int M, int ld, const int32_t *__restrict__ seg_offp, int m_tiles) {
+  constexpr bool kSwiGLU = kMode == kModeSwiGLU, kWGrad = kMode == kModeWGrad;
   // ring of operand tiles; also find_tile's scratch before the K loop and the
   // output staging after it
   __shared__ __attribute__((aligned(1024))) char ring[kSlots * kOperandBytes];
-  TileCoord tc;
-  if (!find_tile(tokens_per_expert, expert_offsets, e, n_tiles, reinterpret_cast<int64_t *>(ring), tc)) return;
 
   const int l = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wm = w >> 1, wn = w & 1;
-  // tile coordinates are the same in every lane: keep them in scalar registers
-  const int te = __builtin_amdgcn_readfirstlane(tc.e);
-  const int n0 = __builtin_amdgcn_readfirstlane(tc.n_tile) * (kSwiGLU ? kBN / 2 : kBN);
-  const int64_t row0 = ((int64_t)__builtin_amdgcn_readfirstlane((int)(tc.row0 >> 32)) << 32) |
-                       (uint32_t)__builtin_amdgcn_readfirstlane((int)tc.row0);
-  const int rows_valid = __builtin_amdgcn_readfirstlane((int)(tc.row_end - tc.row0 < kBM ? tc.row_end - tc.row0 : kBM));
+  // tile coordinates (the same in every lane: kept in scalar registers), the
+  // operand bases and row stride, the K steps and the output base
+  int te, n0, rows_valid, KT, n_lim;
+  uint32_t lda;
+  const char *a_base, *b_base;
+  uint16_t *c_base;
+  int64_t c_ld;
+  if constexpr (kWGrad) {
+    // each XCD (workgroup b runs on XCD b % 8) takes one eighth of every
+    // expert's tiles, m fastest, expert after expert: the experts' different
+    // row counts (the K of these GEMMs) load the XCDs evenly
+    const int per_e = m_tiles * n_tiles, chunk = (per_e + kXcds - 1) / kXcds;
+    const int slot = (int)blockIdx.x / kXcds;
+    te = slot / chunk;
+    const int local = ((int)blockIdx.x % kXcds) * chunk + slot % chunk;
+    if (te >= e || local >= per_e) return;
+    const int m0 = (local % m_tiles) * kBM;
+    n0 = (local / m_tiles) * kBN;
+    rows_valid = M - m0 < kBM ? M - m0 : kBM;
+    const int koff = __builtin_amdgcn_readfirstlane(seg_offp[te]);
+    KT = (__builtin_amdgcn_readfirstlane(seg_offp[te + 1]) - koff) / kBK;
+    lda = (uint32_t)ld;
+    a_base = reinterpret_cast<const char *>(A + (int64_t)m0 * ld + koff);
+    b_base = reinterpret_cast<const char *>(B + (int64_t)n0 * ld + koff);
+    c_ld = N;
+    c_base = C + ((int64_t)te * M + m0) * N;
+    n_lim = N - n0;
+  } else {
+    TileCoord tc;
+    if (!find_tile(tokens_per_expert, expert_offsets, e, n_tiles, reinterpret_cast<int64_t *>(ring), tc)) return;
+    te = __builtin_amdgcn_readfirstlane(tc.e);
+    n0 = __builtin_amdgcn_readfirstlane(tc.n_tile) * (kSwiGLU ? kBN / 2 : kBN);
+    const int64_t row0 = ((int64_t)__builtin_amdgcn_readfirstlane((int)(tc.row0 >> 32)) << 32) |
+                         (uint32_t)__builtin_amdgcn_readfirstlane((int)tc.row0);
+    rows_valid = __builtin_amdgcn_readfirstlane((int)(tc.row_end - tc.row0 < kBM ? tc.row_end - tc.row0 : kBM));
+    KT = K / kBK;
+    lda = (uint32_t)K;
+    a_base = reinterpret_cast<const char *>(A + row0 * K);
+    b_base = reinterpret_cast<const char *>(B + (int64_t)te * b_expert_stride);
+    c_ld = ldc;
+    c_base = C + row0 * ldc;
+    n_lim = N;
+  }
 
   // the tile's 32-row blocks 0..7 alternate between the two row groups of waves
   // (block 2*mi + wm is this wave's block mi); count this wave's blocks that
@@ -270,24 +313,24 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   // l*16..l*16+15 of the instruction's 1 KiB, i.e. row l / kChunks, position
   // l % kChunks, so it fetches global chunk position ^ swz(row).  Addresses are
   // a per-tile scalar base plus a 32-bit per-lane byte offset.
-  const char *a_base = reinterpret_cast<const char *>(A + row0 * K);
-  const char *b_base = reinterpret_cast<const char *>(B + (int64_t)te * b_expert_stride);
   uint32_t a_off[kLoads], b_off[kLoads];
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
     const int r = w * 64 + i * kLoadRows + l / kChunks;
     const int c = (l % kChunks) ^ swz(r);
     const int ar = r < rows_valid ? r : rows_valid - 1;  // ragged tail: re-read the last row
-    a_off[i] = ((uint32_t)ar * (uint32_t)K + (uint32_t)(c * 8)) * 2u;
+    a_off[i] = ((uint32_t)ar * lda + (uint32_t)(c * 8)) * 2u;
     int br;
     if (kSwiGLU) {
       int col = n0 + (r & (kBN / 2 - 1));
       if (col > N - 1) col = N - 1;  // N = I: up rows start at I
       br = (r >= kBN / 2 ? N : 0) + col;
+    } else if (kWGrad) {
+      br = r < n_lim ? r : n_lim - 1;  // the base already points at row n0
     } else {
       br = n0 + r < N ? n0 + r : N - 1;
     }
-    b_off[i] = ((uint32_t)br * (uint32_t)K + (uint32_t)(c * 8)) * 2u;  // < 4*I*H bytes
+    b_off[i] = ((uint32_t)br * lda + (uint32_t)(c * 8)) * 2u;  // < 2^32: checked by the launcher
   }
   const uint32_t ring_lds = lds_address(ring) + w * 64 * kRowBytes;
   // load instruction i (0..7) of this wave for the A (B) tile of step kt into ring slot `slot`
@@ -320,7 +363,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   // exposed; and the load instructions are spread over the MFMA stream.  The
   // barrier orders LDS accesses only (a full workgroup fence would also wait
   // for the loads in flight).
-  const int KT = K / kBK;
+  // (a weight-gradient tile of an expert without rows has no K step: its
+  // accumulators stay zero)
+  if (KT > 0) {
   bf16x8 fa[2][4], fb[2][4];
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) load_b(0, 0, i);
@@ -387,6 +432,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   }
 #undef MOE_K_STEP
   wait_vmcnt<0>();  // no direct load may still be writing LDS when the wave ends
+  }
 
   // epilogue: every real LDS read is done (the last barrier has passed), so
   // each wave stages its bf16 sub-tile in its own LDS buffer -- 128 rows x
@@ -430,14 +476,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   __builtin_amdgcn_wave_barrier();
   constexpr int kRowsPerPass = kWave / kChunksPerRow;
   const int col0 = n0 + wn * kCols;
-  uint16_t *c_base = C + row0 * ldc;
   const int ch = l % kChunksPerRow;
 #pragma unroll 4
   for (int r = l / kChunksPerRow; r < 128; r += kRowsPerPass) {
     const int row = (2 * (r >> 5) + wm) * 32 + (r & 31);  // staged row r is row r%32 of block r/32
     const int col = col0 + ch * 8;
     const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * kPitch + out_pos(r, ch) * 16);
-    if (row < rows_valid && col < N) st16(c_base + (int64_t)row * ldc + col, v);
+    if (row < rows_valid && col < N) st16(c_base + (int64_t)row * c_ld + col, v);
   }
 }
 
@@ -451,7 +496,259 @@ int64_t tile_bound(int64_t rows, int e, int capacity, int n_tiles) {
   return (t + kXcds - 1) / kXcds * kXcds;
 }
 
+// ------------------------------------------------------------------ backward
+//
+// The weight gradients reduce over an expert's rows, so their GEMM operands
+// (dy, x and the two intermediates) are used transposed: [features, rows], each
+// expert's rows a segment of columns padded with zeros to a multiple of kBK and
+// starting at seg_offp[e].  The activation-gradient GEMMs take the weights
+// transposed ([E, I, H] and [E, H, 2I]) so that their operands are K-contiguous
+// like every other operand of the grouped GEMM.
+
+// seg_offp[x] = sum over experts x' < x of tokens_per_expert[x'] rounded up to
+// kBK; seg_offp[e] = the columns in use.
+__global__ __launch_bounds__(kThreads) void seg_offsets_kernel(const int32_t *__restrict__ tokens_per_expert, int e,
+                                                               int32_t *__restrict__ seg_offp) {
+  constexpr int kPer = kMaxExperts / kThreads;
+  __shared__ int32_t part[kThreads];
+  const int tid = threadIdx.x;
+  int32_t local[kPer];
+  int32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int x = tid * kPer + i;
+    const int32_t c = x < e ? tokens_per_expert[x] : 0;
+    local[i] = (c + kBK - 1) / kBK * kBK;
+    s += local[i];
+  }
+  part[tid] = s;
+  __syncthreads();
+  for (int off = 1; off < kThreads; off <<= 1) {
+    const int32_t v = tid >= off ? part[tid - off] : 0;
+    __syncthreads();
+    part[tid] += v;
+    __syncthreads();
+  }
+  int32_t run = part[tid] - s;
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int x = tid * kPer + i;
+    if (x < e) seg_offp[x] = run;
+    run += local[i];
+  }
+  if (tid == kThreads - 1) seg_offp[e] = part[kThreads - 1];
+}
+
+// One 64 x 64 bf16 transpose through LDS: source rows 0..63 (rows >= nv read
+// as zeros), columns 0..63 of `src` (row stride src_ld) become destination rows
+// 0..63, columns 0..63 of `dst` (row stride dst_ld).  The tile is held as
+// 32-bit column pairs, 33 words per source row, so that both the 16-byte row
+// writes and the column reads spread over the LDS banks.
+__device__ __forceinline__ void transpose_tile64(const uint16_t *__restrict__ src, int64_t src_ld, int nv,
+                                                 uint16_t *__restrict__ dst, int64_t dst_ld) {
+  constexpr int kPitch = 33;
+  __shared__ uint32_t tile[64 * kPitch];
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const int j = t / 8 + 32 * p, q = t % 8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (j < nv) v = ld16(src + (int64_t)j * src_ld + 8 * q);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) tile[j * kPitch + 4 * q + d] = v[d];
+  }
+  __syncthreads();
+  const int jg = t % 8, cp = t / 8;  // source rows 8*jg .. 8*jg+7, source columns 2*cp, 2*cp+1
+  uint32_t w[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) w[i] = tile[(8 * jg + i) * kPitch + cp];
+  u32x4 lo, hi;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    lo[i] = (w[2 * i] & 0xFFFFu) | (w[2 * i + 1] << 16);
+    hi[i] = (w[2 * i] >> 16) | (w[2 * i + 1] & 0xFFFF0000u);
+  }
+  st16(dst + (int64_t)(2 * cp) * dst_ld + 8 * jg, lo);
+  st16(dst + (int64_t)(2 * cp + 1) * dst_ld + 8 * jg, hi);
+}
+
+// Batched transpose of expert weights: src [batch, P, Q] -> dst [batch, Q, P];
+// P and Q multiples of 64; grid (P/64, Q/64, batch).
+__global__ __launch_bounds__(kThreads) void weight_transpose_kernel(const uint16_t *__restrict__ src, int P, int Q,
+                                                                    uint16_t *__restrict__ dst) {
+  const int64_t b = blockIdx.z;
+  const int j0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  transpose_tile64(src + (b * P + j0) * Q + c0, Q, 64, dst + (b * Q + c0) * P + j0, P);
+}
+
+// Segment transpose of expert rows: dst [C, ld] column seg_offp[x] + i holds
+// row expert_offsets[x] + i of src [*, C] for i < tokens_per_expert[x] and zero
+// up to the next multiple of 64.  C is a multiple of 64; grid (ld/64, C/64).
+// Every 64-column block lies inside one expert's padded segment.
+__global__ __launch_bounds__(kThreads) void seg_transpose_kernel(
+    const uint16_t *__restrict__ src, int C, const int32_t *__restrict__ seg_offp,
+    const int32_t *__restrict__ tokens_per_expert, const int32_t *__restrict__ expert_offsets, int e,
+    uint16_t *__restrict__ dst, int ld) {
+  const int j0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
+  if (j0 >= seg_offp[e]) return;
+  int lo = 0, hi = e - 1;  // the last expert whose segment starts at or before j0
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (seg_offp[mid] <= j0) lo = mid;
+    else hi = mid - 1;
+  }
+  const int i0 = j0 - seg_offp[lo];
+  const int nv = tokens_per_expert[lo] - i0;
+  transpose_tile64(src + ((int64_t)expert_offsets[lo] + i0) * C + c0, C, nv, dst + (int64_t)c0 * ld + j0, ld);
+}
+
+// SwiGLU backward, in place, 8 features per thread.  For row r and feature i,
+// with g = gu[r, i], u = gu[r, I+i], da = d_act[r, i], s = sigmoid(g):
+//   gu[r, i]     <- bf16(da * u * s * (1 + g * (1 - s)))   (silu'(g) = s (1 + g (1 - s)))
+//   gu[r, I + i] <- bf16(da * g * s)
+//   d_act[r, i]  <- bf16(g * s * u)                          (the activation itself)
+// fp32 arithmetic.  Every element is read and written by the same thread.
+__global__ __launch_bounds__(kThreads) void swiglu_bwd_kernel(uint16_t *__restrict__ gu, uint16_t *__restrict__ d_act,
+                                                              int64_t rows, int inter) {
+  const int per_row = inter / 8;
+  const int64_t n = rows * per_row;
+  for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * kThreads) {
+    const int64_t r = idx / per_row;
+    const int c = (int)(idx % per_row) * 8;
+    uint16_t *pg = gu + r * 2 * inter + c;
+    uint16_t *pu = pg + inter;
+    uint16_t *pa = d_act + r * inter + c;
+    float g[8], u[8], da[8], dg[8], du[8], a[8];
+    Vec16<true>::unpack(ld16(pg), g);
+    Vec16<true>::unpack(ld16(pu), u);
+    Vec16<true>::unpack(ld16(pa), da);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const float sg = 1.0f / (1.0f + __expf(-g[i]));
+      const float gs = g[i] * sg;
+      dg[i] = da[i] * u[i] * (sg * (1.0f + g[i] * (1.0f - sg)));
+      du[i] = da[i] * gs;
+      a[i] = gs * u[i];
+    }
+    st16(pg, Vec16<true>::pack(dg));
+    st16(pu, Vec16<true>::pack(du));
+    st16(pa, Vec16<true>::pack(a));
+  }
+}
+
+int64_t seg_ld(int64_t rows, int e) { return ((rows + kBK - 1) / kBK + e) * kBK; }
+
+struct BwdWorkspace {
+  int32_t *seg_offp;
+  uint16_t *wd_t, *wgu_t, *gu, *dact, *t_h, *t_i;
+};
+
+// Carves the backward workspace; with base == nullptr only counts bytes.
+size_t carve_bwd(char *base, int64_t rows, int64_t hidden, int inter, int e, BwdWorkspace *w) {
+  const int64_t ld = seg_ld(rows, e);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char *p = base ? base + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  BwdWorkspace v;
+  v.seg_offp = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (size_t)(e + 1)));
+  v.wd_t = reinterpret_cast<uint16_t *>(take(2 * (size_t)e * inter * hidden));
+  v.wgu_t = reinterpret_cast<uint16_t *>(take(4 * (size_t)e * inter * hidden));
+  v.gu = reinterpret_cast<uint16_t *>(take(4 * (size_t)rows * inter));
+  v.dact = reinterpret_cast<uint16_t *>(take(2 * (size_t)rows * inter));
+  v.t_h = reinterpret_cast<uint16_t *>(take(2 * (size_t)hidden * ld));
+  v.t_i = reinterpret_cast<uint16_t *>(take(4 * (size_t)inter * ld));
+  if (w) *w = v;
+  return off;
+}
+
+// Plain grouped GEMM over the expert segments: C [rows, N] = A [rows, K] B_e^T.
+hipError_t launch_plain(const uint16_t *A, const uint16_t *B, int64_t b_stride, int K, int N, int64_t rows, int e,
+                        int capacity, const int32_t *tokens_per_expert, const int32_t *expert_offsets, uint16_t *C,
+                        hipStream_t stream) {
+  const int nt = (N + kBN - 1) / kBN;
+  const int64_t g = tile_bound(rows, e, capacity, nt);
+  hipLaunchKernelGGL(grouped_gemm_kernel<kModePlain>, dim3((unsigned)g), dim3(kThreads), 0, stream, A, B, b_stride,
+                     K, N, nt, tokens_per_expert, expert_offsets, e, C, (int64_t)N, 0, 0, nullptr, 0);
+  return hipGetLastError();
+}
+
+// Weight-gradient GEMM: C_e [M, N] = A[:, seg_e] B[:, seg_e]^T for every expert.
+hipError_t launch_wgrad(const uint16_t *A, const uint16_t *B, int M, int N, int ld, const int32_t *seg_offp, int e,
+                        uint16_t *C, hipStream_t stream) {
+  const int mt = (M + kBM - 1) / kBM, nt = (N + kBN - 1) / kBN;
+  const int chunk = (mt * nt + kXcds - 1) / kXcds;
+  hipLaunchKernelGGL(grouped_gemm_kernel<kModeWGrad>, dim3((unsigned)(kXcds * e * chunk)), dim3(kThreads), 0, stream,
+                     A, B, (int64_t)0, 0, N, nt, nullptr, nullptr, e, C, (int64_t)N, M, ld, seg_offp, mt);
+  return hipGetLastError();
+}
+
+hipError_t launch_seg_transpose(const uint16_t *src, int cols, const BwdWorkspace &w, int ld,
+                                const int32_t *tokens_per_expert, const int32_t *expert_offsets, int e,
+                                uint16_t *dst, hipStream_t stream) {
+  hipLaunchKernelGGL(seg_transpose_kernel, dim3((unsigned)(ld / 64), (unsigned)(cols / 64)), dim3(kThreads), 0,
+                     stream, src, cols, w.seg_offp, tokens_per_expert, expert_offsets, e, dst, ld);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+size_t ffn_bwd_workspace_bytes(int64_t rows, int64_t hidden, int inter, int e) {
+  return carve_bwd(nullptr, rows, hidden, inter, e, nullptr);
+}
+
+int64_t ffn_bwd_seg_ld(int64_t rows, int e) { return seg_ld(rows, e); }
+
+hipError_t launch_expert_ffn_bwd(const uint16_t *x_perm, const uint16_t *grad_y, int64_t rows, int64_t hidden,
+                                 int inter, int e, int capacity, const int32_t *tokens_per_expert,
+                                 const int32_t *expert_offsets, const uint16_t *w_gate_up, const uint16_t *w_down,
+                                 uint16_t *grad_x_perm, uint16_t *grad_w_gate_up, uint16_t *grad_w_down,
+                                 void *workspace, hipStream_t stream) {
+  BwdWorkspace w;
+  carve_bwd(static_cast<char *>(workspace), rows, hidden, inter, e, &w);
+  const int ld = (int)seg_ld(rows, e);
+  const int H = (int)hidden, I = inter;
+  hipError_t st;
+#define MOE_TRY(x)                    \
+  if ((st = (x)) != hipSuccess) return st;
+  hipLaunchKernelGGL(seg_offsets_kernel, dim3(1), dim3(kThreads), 0, stream, tokens_per_expert, e, w.seg_offp);
+  MOE_TRY(hipGetLastError());
+  // W_down^T [E, I, H] and W_gate_up^T [E, H, 2I]
+  hipLaunchKernelGGL(weight_transpose_kernel, dim3((unsigned)(H / 64), (unsigned)(I / 64), (unsigned)e),
+                     dim3(kThreads), 0, stream, w_down, H, I, w.wd_t);
+  MOE_TRY(hipGetLastError());
+  hipLaunchKernelGGL(weight_transpose_kernel, dim3((unsigned)(2 * I / 64), (unsigned)(H / 64), (unsigned)e),
+                     dim3(kThreads), 0, stream, w_gate_up, 2 * I, H, w.wgu_t);
+  MOE_TRY(hipGetLastError());
+  if (rows > 0) {
+    // [G | U] = x W_gate_up^T (recomputed), dA = dy W_down
+    MOE_TRY(launch_plain(x_perm, w_gate_up, (int64_t)2 * I * H, H, 2 * I, rows, e, capacity, tokens_per_expert,
+                         expert_offsets, w.gu, stream));
+    MOE_TRY(launch_plain(grad_y, w.wd_t, (int64_t)I * H, H, I, rows, e, capacity, tokens_per_expert, expert_offsets,
+                         w.dact, stream));
+    // [dG | dU] in place of [G | U]; the activation in place of dA
+    const int64_t chunks = rows * (I / 8);
+    int64_t blocks = (chunks + kThreads - 1) / kThreads;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, w.gu, w.dact, rows, I);
+    MOE_TRY(hipGetLastError());
+    // dx = [dG | dU] W_gate_up
+    MOE_TRY(launch_plain(w.gu, w.wgu_t, (int64_t)H * 2 * I, 2 * I, H, rows, e, capacity, tokens_per_expert,
+                         expert_offsets, grad_x_perm, stream));
+  }
+  // dW_down_e = dy_e^T a_e
+  MOE_TRY(launch_seg_transpose(grad_y, H, w, ld, tokens_per_expert, expert_offsets, e, w.t_h, stream));
+  MOE_TRY(launch_seg_transpose(w.dact, I, w, ld, tokens_per_expert, expert_offsets, e, w.t_i, stream));
+  MOE_TRY(launch_wgrad(w.t_h, w.t_i, H, I, ld, w.seg_offp, e, grad_w_down, stream));
+  // [dW_gate; dW_up]_e = [dG | dU]_e^T x_e
+  MOE_TRY(launch_seg_transpose(x_perm, H, w, ld, tokens_per_expert, expert_offsets, e, w.t_h, stream));
+  MOE_TRY(launch_seg_transpose(w.gu, 2 * I, w, ld, tokens_per_expert, expert_offsets, e, w.t_i, stream));
+  MOE_TRY(launch_wgrad(w.t_i, w.t_h, 2 * I, H, ld, w.seg_offp, e, grad_w_gate_up, stream));
+#undef MOE_TRY
+  return hipSuccess;
+}
 
 size_t ffn_workspace_bytes(int64_t rows, int inter) { return align256(sizeof(uint16_t) * (size_t)rows * (size_t)inter); }
 
@@ -463,16 +760,16 @@ hipError_t launch_expert_ffn(const uint16_t *x_perm, int64_t rows, int64_t hidde
   uint16_t *act = static_cast<uint16_t *>(workspace);
   const int n1 = (inter + kBN / 2 - 1) / (kBN / 2);
   const int64_t g1 = tile_bound(rows, e, capacity, n1);
-  hipLaunchKernelGGL(grouped_gemm_kernel<true>, dim3((unsigned)g1), dim3(kThreads), 0, stream, x_perm, w_gate_up,
-                     (int64_t)2 * inter * hidden, (int)hidden, inter, n1, tokens_per_expert, expert_offsets, e, act,
-                     (int64_t)inter);
+  hipLaunchKernelGGL(grouped_gemm_kernel<kModeSwiGLU>, dim3((unsigned)g1), dim3(kThreads), 0, stream, x_perm,
+                     w_gate_up, (int64_t)2 * inter * hidden, (int)hidden, inter, n1, tokens_per_expert, expert_offsets,
+                     e, act, (int64_t)inter, 0, 0, nullptr, 0);
   hipError_t st = hipGetLastError();
   if (st != hipSuccess) return st;
   const int n2 = (int)((hidden + kBN - 1) / kBN);
   const int64_t g2 = tile_bound(rows, e, capacity, n2);
-  hipLaunchKernelGGL(grouped_gemm_kernel<false>, dim3((unsigned)g2), dim3(kThreads), 0, stream, act, w_down,
-                     (int64_t)hidden * inter, inter, (int)hidden, n2, tokens_per_expert, expert_offsets, e, y,
-                     hidden);
+  hipLaunchKernelGGL(grouped_gemm_kernel<kModePlain>, dim3((unsigned)g2), dim3(kThreads), 0, stream, act, w_down,
+                     (int64_t)hidden * inter, inter, (int)hidden, n2, tokens_per_expert, expert_offsets, e, y, hidden,
+                     0, 0, nullptr, 0);
   return hipGetLastError();
 }
 

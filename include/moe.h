@@ -5,6 +5,7 @@
  *   moe_dispatch    per-expert histogram + prefix sum, stable per-expert ordinals,
  *                   capacity drop/pad masks, row scatter into expert-contiguous rows
  *   moe_expert_ffn  grouped SwiGLU expert GEMM (bf16 MFMA, fp32 accumulation)
+ *   moe_expert_ffn_bwd backward of moe_expert_ffn (grads of rows and weights)
  *   moe_combine     probability-weighted unpermute / combine (fp32 accumulation)
  *   moe_combine_bwd backward of moe_combine (grad of expert rows, grad of weights)
  *   moe_dispatch_bwd backward of the row scatter (grad of the token rows)
@@ -60,7 +61,8 @@ typedef enum moe_op {
   MOE_OP_DISPATCH = 1,
   MOE_OP_EXPERT_FFN = 2,
   MOE_OP_COMBINE = 3,
-  MOE_OP_COMBINE_BWD = 4
+  MOE_OP_COMBINE_BWD = 4,
+  MOE_OP_EXPERT_FFN_BWD = 5
 } moe_op;
 
 /* Shapes and options; read on the host only, never kept. */
@@ -157,6 +159,29 @@ moe_status moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_i
 moe_status moe_expert_ffn(const moe_shape *s, const void *x_perm, const moe_layout *layout,
                           const void *w_gate_up, const void *w_down, void *y, void *workspace,
                           size_t workspace_bytes, void *stream);
+
+/* Expert FFN backward: the vector-Jacobian product of moe_expert_ffn (the
+ * experts' backward of MoELayer on "Megatron MoE 实现", with the grouped-GEMM
+ * weight gradients per expert of the MORI and UltraEP pull requests).  Per
+ * expert e and the rows of its segment, with G = x_perm Wg^T, U = x_perm Wu^T
+ * (Wg, Wu: gate and up halves of w_gate_up[e]), s = sigmoid(G), A = G s U and
+ * the incoming grad_y (dY):
+ *   dA = dY w_down[e];  dG = dA U s (1 + G (1 - s));  dU = dA G s
+ *   grad_x_perm = dG Wg + dU Wu
+ *   grad_w_down[e] = dY^T A;  grad_w_gate_up[e] = [dG^T x_perm ; dU^T x_perm]
+ * bf16 operands, fp32 accumulation; G, U, dA, dG, dU and A are recomputed and
+ * held in bf16 between the GEMMs.  An expert with no rows gets zero weight
+ * gradients; rows outside the segments of grad_x_perm are not written.
+ * Shapes as moe_expert_ffn: x_perm, grad_y, grad_x_perm bf16 [R, H];
+ * w_gate_up, grad_w_gate_up bf16 [E, 2I, H]; w_down, grad_w_down bf16 [E, H, I];
+ * outputs must not alias inputs or each other.  Same shape limits as
+ * moe_expert_ffn, and R + 64*E < 2^23.
+ * Workspace: moe_workspace_size(MOE_OP_EXPERT_FFN_BWD) (transposed weights,
+ * the [R, 3I] bf16 intermediates and the row-transposed operands of the weight
+ * gradients). */
+moe_status moe_expert_ffn_bwd(const moe_shape *s, const void *x_perm, const void *grad_y, const moe_layout *layout,
+                              const void *w_gate_up, const void *w_down, void *grad_x_perm, void *grad_w_gate_up,
+                              void *grad_w_down, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Combine: probability-weighted unpermute (DeepSpeed ep_tp_dispatch.py
  * restore_combined: weighted expert rows added into a zeroed [N, H] output by

@@ -44,6 +44,7 @@ STREAM_W_GATE_UP = 2
 STREAM_W_DOWN = 3
 STREAM_GRAD = 4
 STREAM_ROUTING = 5
+STREAM_GRAD_ROWS = 6
 
 DT_F32 = 0
 DT_BF16 = 1
@@ -255,3 +256,8 @@ def activations(w: Workload, seed: int = 0) -> np.ndarray:
 
 def grad_output(w: Workload, seed: int = 0) -> np.ndarray:
     return normal_activations((w.n_tokens, w.hidden), w.dtype, w.wid, STREAM_GRAD, seed)
+
+
+def grad_expert_rows(w: Workload, rows: int, seed: int = 0) -> np.ndarray:
+    """Incoming gradient of the expert outputs: bf16 [rows, H] ~ N(0, 1)."""
+    return normal_activations((rows, w.hidden), DT_BF16, w.wid, STREAM_GRAD_ROWS, seed)

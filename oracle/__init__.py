@@ -254,5 +254,63 @@ def expert_ffn_bwd(x_perm, grad_y, lay, w_gate_up, w_down, round_out=True):
     return bf16_round_array(gx), bf16_round_array(dwgu), bf16_round_array(dwd)
 
 
+def expert_ffn_bwd_entries(x_perm, grad_y, lay, w_gate_up, w_down, rows=(), dwd=(), dwgu=()):
+    """Selected outputs of expert_ffn_bwd, each from the same formulas taken over
+    only the rows and columns it depends on (for shapes where the whole backward
+    takes too long on the host): rows `rows` of grad_x_perm (rows inside the
+    segments), entries (e, h, i) of grad_w_down and entries (e, j, h) of
+    grad_w_gate_up (j < I: gate, j >= I: up).  fp64; each value rounded once to
+    bf16.  Returns (grad_x rows [len(rows), H], dwd values, dwgu values) as bf16 bits.
+    """
+    e, two_i, h = w_gate_up.shape
+    inter = two_i // 2
+    offs = [int(v) for v in lay["expert_offsets"][:e]]
+    cnts = [int(v) for v in lay["tokens_per_expert"][:e]]
+
+    def expert_of(r):
+        for ex in range(e):
+            if offs[ex] <= r < offs[ex] + cnts[ex]:
+                return ex
+        raise ValueError(f"row {r} is outside every expert segment")
+
+    gx = np.zeros((len(rows), h))
+    for n, r in enumerate(rows):
+        ex = expert_of(int(r))
+        x, dy = _bf16_f64(x_perm[r]), _bf16_f64(grad_y[r])
+        wg, wu, wd = _bf16_f64(w_gate_up[ex, :inter]), _bf16_f64(w_gate_up[ex, inter:]), _bf16_f64(w_down[ex])
+        g, u = wg @ x, wu @ x
+        sg = 1.0 / (1.0 + np.exp(-g))
+        da = dy @ wd
+        gx[n] = (da * u * sg * (1.0 + g * (1.0 - sg))) @ wg + (da * g * sg) @ wu
+
+    segs = {}                          # expert -> its rows of x_perm and grad_y in fp64
+
+    def columns(ex, i):
+        """Per row of expert ex's segment: x, dy, g, u, sigmoid(g), dA of intermediate feature i."""
+        if ex not in segs:
+            o, n = offs[ex], cnts[ex]
+            segs[ex] = (_bf16_f64(x_perm[o:o + n]), _bf16_f64(grad_y[o:o + n]))
+        x, dy = segs[ex]
+        g = x @ _bf16_f64(w_gate_up[ex, i])
+        u = x @ _bf16_f64(w_gate_up[ex, inter + i])
+        da = dy @ _bf16_f64(w_down[ex, :, i])
+        return x, dy, g, u, 1.0 / (1.0 + np.exp(-g)), da
+
+    vd = np.zeros(len(dwd))
+    for n, (ex, hh, i) in enumerate(dwd):
+        if cnts[ex] == 0:
+            continue
+        _, dy, g, u, sg, _ = columns(ex, i)
+        vd[n] = dy[:, hh] @ (g * sg * u)
+    vgu = np.zeros(len(dwgu))
+    for n, (ex, j, hh) in enumerate(dwgu):
+        if cnts[ex] == 0:
+            continue
+        x, _, g, u, sg, da = columns(ex, j % inter)
+        col = da * u * sg * (1.0 + g * (1.0 - sg)) if j < inter else da * g * sg
+        vgu[n] = col @ x[:, hh]
+    return bf16_round_array(gx), bf16_round_array(vd), bf16_round_array(vgu)
+
+
 def bf16_round(x: float) -> int:
     return int(lib().oracle_bf16_round(float(x)))

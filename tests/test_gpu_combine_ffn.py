@@ -245,3 +245,96 @@ def test_full_layer_qwen3_shape_sampled_tokens(moe):
         sub_lay["assign_row"] = ref_lay["assign_row"][t * w.top_k:(t + 1) * w.top_k]
         ref = oracle.combine(y_full, wts[t:t + 1], sub_lay, 1, w.top_k)
         assert max_rel_err(out_h[t:t + 1], ref) <= TOL_BF16
+
+
+# ------------------------------------------------------ expert FFN backward
+
+def ffn_bwd_run(moe, w, xp, lay, wgu, wd, seed=0):
+    dy = mi.grad_expert_rows(w, lay.rows, seed)
+    gx, dwgu, dwd = moe.moe_expert_ffn_bwd(xp, dev(dy), lay, dev(wgu), dev(wd))
+    torch.cuda.synchronize()
+    return dy, gx, dwgu, dwd
+
+
+def entries(t: torch.Tensor, idx) -> np.ndarray:
+    """Elements idx (a list of index tuples) of a device tensor, gathered on the device."""
+    cols = [torch.tensor(c, dtype=torch.long, device=t.device) for c in zip(*idx)]
+    return host(t[tuple(cols)].contiguous())
+
+
+@pytest.mark.parametrize("n,e,k,h,inter,cap", [
+    (300, 4, 2, 256, 192, 0),     # several m-tiles per expert, ragged tails
+    (257, 8, 2, 192, 128, 0),     # hidden not a multiple of 128 (masked columns and weight-gradient rows)
+    (1000, 16, 4, 512, 256, 0),
+    (2000, 4, 2, 128, 320, 0),    # long expert segments: many K steps in the weight gradients
+    (600, 8, 2, 256, 64, 1.0),    # capacity layout with drops and pads
+    (5, 4, 1, 64, 64, 0),         # tiny, most experts empty
+])
+def test_expert_ffn_bwd_small_full_compare(moe, n, e, k, h, inter, cap):
+    w, idx, wts, x, wgu, wd, xp, lay, y = ffn_case(moe, n, e, k, h, inter, cap, zero_expert=1 if e > 2 else None)
+    dy, gx, dwgu, dwd = (host(v) if isinstance(v, torch.Tensor) else v for v in ffn_bwd_run(moe, w, xp, lay, wgu, wd))
+    lay_h = layout_host(lay)
+    lay_h["rows"] = lay.rows
+    ref_gx, ref_dwgu, ref_dwd = oracle.expert_ffn_bwd(host(xp), dy, lay_h, wgu, wd)
+    cnt, offs = lay_h["tokens_per_expert"], lay_h["expert_offsets"]
+    in_seg = np.zeros(lay.rows, bool)
+    for ex in range(e):
+        in_seg[offs[ex]:offs[ex] + cnt[ex]] = True
+    assert max_rel_err(gx[in_seg], ref_gx[in_seg]) <= TOL_BF16
+    assert max_rel_err(dwgu, ref_dwgu) <= TOL_BF16
+    assert max_rel_err(dwd, ref_dwd) <= TOL_BF16
+    for ex in np.nonzero(cnt == 0)[0]:          # experts without rows: exactly zero weight gradients
+        assert (dwgu[ex] == 0).all() and (dwd[ex] == 0).all()
+    if e > 2:
+        assert cnt[1] == 0
+
+
+def test_expert_ffn_bwd_repeated_calls_are_identical(moe):
+    """The backward is deterministic: no atomics, fixed reduction order."""
+    w, idx, wts, x, wgu, wd, xp, lay, y = ffn_case(moe, 700, 8, 2, 256, 128)
+    a = ffn_bwd_run(moe, w, xp, lay, wgu, wd)
+    b = ffn_bwd_run(moe, w, xp, lay, wgu, wd)
+    for u, v in zip(a[1:], b[1:]):
+        assert torch.equal(u.view(torch.int16), v.view(torch.int16))
+
+
+def sample_bwd_entries(lay_h: dict, e: int, h: int, inter: int, g: np.random.Generator, per_expert: int = 4):
+    """Weight-gradient entries of the hottest, the coldest non-empty, an empty (if
+    any) and a few random experts."""
+    cnt = lay_h["tokens_per_expert"][:e]
+    nz = np.nonzero(cnt > 0)[0]
+    chosen = {int(np.argmax(cnt)), int(nz[np.argmin(cnt[nz])])}
+    if (cnt == 0).any():
+        chosen.add(int(np.nonzero(cnt == 0)[0][0]))
+    chosen |= {int(v) for v in g.choice(e, size=min(3, e), replace=False)}
+    dwd, dwgu = [], []
+    for ex in sorted(chosen):
+        dwd += [(ex, int(g.integers(h)), int(g.integers(inter))) for _ in range(per_expert)]
+        dwgu += [(ex, int(g.integers(inter)), int(g.integers(h))) for _ in range(per_expert // 2)]
+        dwgu += [(ex, inter + int(g.integers(inter)), int(g.integers(h))) for _ in range(per_expert // 2)]
+    return dwd, dwgu
+
+
+@pytest.mark.parametrize("wid", [4, 5])
+def test_expert_ffn_bwd_full_size_sampled(moe, wid):
+    """Full-size backward (N=8192 H=4096 E=128 k=8 I=1536; the 32-expert H=7168
+    I=2048 share with Zipf loads): sampled rows of grad_x_perm and sampled
+    entries of both weight gradients against the oracle's per-entry backward."""
+    w = mi.workload(wid)
+    idx, wts, logits, x = workload_inputs(w)
+    if idx is None:
+        idx, wts, _, _ = oracle.route(logits, w.top_k)
+    wgu, wd = mi.expert_weights(w)
+    xp, wp, lay = moe.moe_dispatch(dev(x), dev(idx), dev(wts), w.n_experts, max_rows=w.rows)
+    dy, gx, dwgu, dwd = ffn_bwd_run(moe, w, xp, lay, wgu, wd)
+    lay_h = layout_host(lay)
+    g = np.random.default_rng(100 + wid)
+    rows = sample_rows(lay_h, g, per_expert=1, experts=8)
+    d_idx, gu_idx = sample_bwd_entries(lay_h, w.n_experts, w.hidden, w.inter, g)
+    ref_rows, ref_d, ref_gu = oracle.expert_ffn_bwd_entries(host(xp), dy, lay_h, wgu, wd, rows, d_idx, gu_idx)
+    assert max_rel_err(host(gx[torch.as_tensor(rows, device=gx.device)]), ref_rows) <= TOL_BF16
+    assert max_rel_err(entries(dwd, d_idx), ref_d) <= TOL_BF16
+    assert max_rel_err(entries(dwgu, gu_idx), ref_gu) <= TOL_BF16
+    cnt = lay_h["tokens_per_expert"]
+    for ex in np.nonzero(cnt == 0)[0]:
+        assert not dwgu[int(ex)].view(torch.int16).any() and not dwd[int(ex)].view(torch.int16).any()

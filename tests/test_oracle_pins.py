@@ -681,3 +681,23 @@ def test_ffn_bwd_rounding_is_one_rne_per_value():
         nz = a != 0                    # the reference rounding covers the normal range
         assert (bf16_from_double_ref(a[nz]) == b[nz]).all()
         assert (b[~nz] & 0x7FFF == 0).all()
+
+
+def test_ffn_bwd_entries_match_the_whole_backward():
+    """The per-entry backward used at full sizes agrees with the whole-matrix one
+    (itself pinned by finite differences above) on bf16 inputs."""
+    lay, x, wgu, wd, dy = _ffn_bwd_case(9)
+    bits = lambda a: mi.f32_to_bf16_bits(a.astype(np.float32))
+    x, wgu, wd, dy = bits(x), bits(wgu * 0.2), bits(wd * 0.2), bits(dy)
+    gx, dwgu, dwd = oracle.expert_ffn_bwd(x, dy, lay, wgu, wd)
+    rows = np.nonzero(lay["pad_mask"] == 0)[0]
+    e, two_i, h = wgu.shape
+    dwd_idx = [(ex, hh, i) for ex in range(e) for hh in range(h) for i in range(two_i // 2)]
+    dwgu_idx = [(ex, j, hh) for ex in range(e) for j in range(two_i) for hh in range(h)]
+    g_rows, g_dwd, g_dwgu = oracle.expert_ffn_bwd_entries(x, dy, lay, wgu, wd, rows, dwd_idx, dwgu_idx)
+    pairs = [(g_rows, gx[rows]), (g_dwd, np.array([dwd[i] for i in dwd_idx])),
+             (g_dwgu, np.array([dwgu[i] for i in dwgu_idx]))]
+    for got, ref in pairs:
+        got, ref = got.reshape(-1).astype(np.int32), ref.reshape(-1).astype(np.int32)
+        assert (np.abs(got - ref) <= 1).all()      # fp64 sums in another order: at most one bf16 step apart
+        assert (got == ref).mean() > 0.98
