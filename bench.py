@@ -169,7 +169,7 @@ def bench_dispatch_combine(moe, mi, torch, steps, warmup):
                 n=n, k=k, e=e, h=h)
 
 
-def bench_expert_gemm(moe, mi, torch, wid, iters, warmup):
+def bench_expert_gemm(moe, mi, torch, wid, iters, warmup, bwd_iters=0):
     import numpy as np
     w = mi.workload(wid)
     dev = torch.device("cuda")
@@ -202,9 +202,33 @@ def bench_expert_gemm(moe, mi, torch, wid, iters, warmup):
     ms = a.elapsed_time(b) / iters
     rows = int(lay.counters[0].item())
     flops = 2.0 * rows * h * 3 * inter
-    del wgu, wd, x, xp, y, ws
+    out = dict(workload=w.name, rows=rows, ms=ms, tflops=flops / ms / 1e9, flops=flops)
+    del ws
+    if bwd_iters > 0:
+        # backward: dy [R, H] in, grad_x_perm [R, H], grad_w_gate_up, grad_w_down out
+        dy = torch.randn(xp.shape, generator=g, device=dev).to(torch.bfloat16)
+        gx, dwgu, dwd = torch.empty_like(xp), torch.empty_like(wgu), torch.empty_like(wd)
+        ws = torch.empty(moe.workspace_size(moe.MOE_OP_EXPERT_FFN_BWD, shape) + 256, dtype=torch.uint8, device=dev)
+        run = lambda: moe.moe_expert_ffn_bwd(xp, dy, lay, wgu, wd, grad_x_perm=gx, grad_w_gate_up=dwgu,
+                                             grad_w_down=dwd, workspace=ws)
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(bwd_iters):
+            run()
+        b.record()
+        torch.cuda.synchronize()
+        bms = a.elapsed_time(b) / bwd_iters
+        # the backward's own products (dA, dx, dW_down, dW_gate_up): twice the forward's
+        # flops; the recomputed gate/up projection adds 2*rows*H*2I executed flops
+        bflops = 2.0 * rows * h * 6 * inter
+        out.update(bwd_ms=bms, bwd_tflops=bflops / bms / 1e9,
+                   bwd_exec_tflops=(bflops + 2.0 * rows * h * 2 * inter) / bms / 1e9)
+        del dy, gx, dwgu, dwd, ws
+    del wgu, wd, x, xp, y
     torch.cuda.empty_cache()
-    return dict(workload=w.name, rows=rows, ms=ms, tflops=flops / ms / 1e9, flops=flops)
+    return out
 
 
 def recorded_traffic(kernel: str):
@@ -279,6 +303,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--gemm-iters", type=int, default=10)
     ap.add_argument("--skip-gemm", action="store_true")
+    ap.add_argument("--bwd-iters", type=int, default=5, help="expert FFN backward iterations (0: skip)")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--counter-pass", action="store_true",
                     help="short run for rocprofv3 --pmc passes (prints no JSON line)")
@@ -307,7 +332,7 @@ def main():
     if not args.skip_gemm:
         for wid in (4, 5):
             log(f"expert GEMM: workload {mi.workload(wid).name}")
-            gemm.append(bench_expert_gemm(moe, mi, torch, wid, args.gemm_iters, 2))
+            gemm.append(bench_expert_gemm(moe, mi, torch, wid, args.gemm_iters, 2, args.bwd_iters))
     cpu = None
     if not args.skip_cpu:
         log("cpu baseline (oracle)")
@@ -361,7 +386,10 @@ def main():
                      "traffic": traffic, "launch_us": round(dc["comb_kernel_ms"] * 1e3, 2),
                      "algorithmic_bytes": dc["combine_bytes"]},
         "expert_gemm": [{"workload": g["workload"], "rows": g["rows"], "us": round(g["ms"] * 1e3, 1),
-                         "tflops": round(g["tflops"], 1), "frac_bf16_peak": round(g["tflops"] / BF16_PEAK_TFLOPS, 4)}
+                         "tflops": round(g["tflops"], 1), "frac_bf16_peak": round(g["tflops"] / BF16_PEAK_TFLOPS, 4),
+                         **({"bwd_us": round(g["bwd_ms"] * 1e3, 1), "bwd_tflops": round(g["bwd_tflops"], 1),
+                             "bwd_frac_bf16_peak": round(g["bwd_tflops"] / BF16_PEAK_TFLOPS, 4),
+                             "bwd_exec_tflops": round(g["bwd_exec_tflops"], 1)} if "bwd_ms" in g else {})}
                         for g in gemm],
         "cpu_baseline": cpu,
     }

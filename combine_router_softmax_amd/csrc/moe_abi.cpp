@@ -100,7 +100,7 @@ moe_status moe_workspace_size(moe_op op, const moe_shape *s, size_t *bytes) {
       return MOE_OK;
     case MOE_OP_EXPERT_FFN_BWD:
       if (s->inter < 1) return MOE_ERR_INVALID_ARG;
-      *bytes = moe::ffn_bwd_workspace_bytes(rows_of(s), s->hidden, s->inter, s->n_experts);
+      *bytes = moe::ffn_bwd_workspace_bytes(rows_of(s), s->inter);
       return MOE_OK;
   }
   return MOE_ERR_INVALID_ARG;
@@ -174,8 +174,6 @@ moe_status moe_expert_ffn_bwd(const moe_shape *s, const void *x_perm, const void
   int64_t rows;
   moe_status st = check_ffn_shape(s, &rows);
   if (st != MOE_OK) return st;
-  // 256 rows of a row-transposed operand are addressed with 32-bit byte offsets
-  if (moe::ffn_bwd_seg_ld(rows, s->n_experts) >= (int64_t)1 << 23) return MOE_ERR_UNSUPPORTED;
   if (!layout || !layout->tokens_per_expert || !layout->expert_offsets || !w_gate_up || !w_down || !grad_w_gate_up ||
       !grad_w_down)
     return MOE_ERR_INVALID_ARG;
@@ -188,8 +186,8 @@ moe_status moe_expert_ffn_bwd(const moe_shape *s, const void *x_perm, const void
     if (in && (in == grad_x_perm || in == grad_w_gate_up || in == grad_w_down)) return MOE_ERR_INVALID_ARG;
   if (grad_w_gate_up == grad_w_down || (grad_x_perm && (grad_x_perm == grad_w_gate_up || grad_x_perm == grad_w_down)))
     return MOE_ERR_INVALID_ARG;
-  const size_t need_ws = moe::ffn_bwd_workspace_bytes(rows, s->hidden, s->inter, s->n_experts);
-  if (workspace_bytes < need_ws || !workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+  const size_t need_ws = moe::ffn_bwd_workspace_bytes(rows, s->inter);
+  if (workspace_bytes < need_ws || (need_ws > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))))
     return MOE_ERR_WORKSPACE;
   return hip_status(moe::launch_expert_ffn_bwd(
       static_cast<const uint16_t *>(x_perm), static_cast<const uint16_t *>(grad_y), rows, s->hidden, s->inter,

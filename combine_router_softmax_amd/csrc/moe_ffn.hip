@@ -167,22 +167,82 @@ __device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)
 
 __device__ __forceinline__ uint16_t bf16_bits(float v) { return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu); }
 
+// K-major operand tiles (the source stores K as its row index, the tile's 256
+// columns contiguous): 64 rows of 512 bytes per K step, the same 32 KiB as a
+// K-contiguous tile.  The fragments are read with ds_read_b64_tr_b16, which
+// transposes 16-bit elements across each group of 16 lanes: lane i of a group
+// receives, for j = 0..3, element i % 4 of the 8-byte row that lane 4*j + i/4
+// of the group addressed.  When lane r of a group addresses row kb + r/4,
+// columns nb + 4*(r % 4) .. +3, lane i thus receives column nb + i, rows
+// kb .. kb+3: four consecutive K values of one column, half of an MFMA operand.
+constexpr int kTRowBytes = kBN * 2;  // bytes per row of a K-major tile
+
+// LDS position of 16-byte chunk c of row k of a K-major tile is c ^ swz_t(k).
+// Measured on gfx950, the fragment reads below then run as fast as linear
+// 8-byte-per-lane reads; without the permutation they run at about half that.
+__device__ __forceinline__ int swz_t(int k) { return ((k & 3) << 2) | (((k >> 2) & 1) << 4); }
+
+// Byte offset, within a K-major tile, of this lane's transposed read h (K values
+// 4h .. 4h+3 of its eight) of the fragment of 32-column block blk in slice 0;
+// slice ks adds 16*ks rows, which leaves swz_t unchanged.
+__device__ __forceinline__ uint32_t tr_off(int l, int blk, int h) {
+  const int g = l >> 4, i = l & 15;
+  const int k = 8 * (g >> 1) + (i >> 2) + 4 * h;  // lanes 32..63 hold K values 8..15
+  const int n = blk * 32 + 16 * (g & 1) + 4 * (i & 3);
+  return (uint32_t)(k * kTRowBytes + (((n >> 3) ^ swz_t(k)) << 4) + (n & 7) * 2);
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// One MFMA operand (8 consecutive K values of one column) from a K-major tile.
+__device__ __forceinline__ bf16x8 tr_frag(const char *tile, uint32_t off0, uint32_t off1) {
+  const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tile + off0));
+  const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4 *)(tile + off1));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // Fragments of one 16-wide K slice ks from the A tile `as` and the B tile `bs`:
-// A rows (2*mi + wm)*32 + l%32, B rows as below, k-chunk 2*ks + l/32.
-template <bool kSwiGLU>
+// A rows (2*mi + wm)*32 + l%32, B rows as below, k-chunk 2*ks + l/32.  A K-major
+// operand (kAT, kBT) is read through its per-lane offsets ta / tb (block, half).
+template <bool kSwiGLU, bool kAT, bool kBT>
 __device__ __forceinline__ void load_frags(const char *__restrict__ as, const char *__restrict__ bs, int ks, int wm,
-                                           int wn, int l, bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+                                           int wn, int l, bf16x8 (&a)[4], bf16x8 (&b)[4],
+                                           const uint32_t (&ta)[4][2], const uint32_t (&tb)[4][2]) {
   const int r32 = l & 31;
   const int pos = ((2 * ks + (l >> 5)) ^ swz(r32)) * 16;  // every row read is r32 plus a multiple of 32
+  const int tks = ks * 16 * kTRowBytes;
 #pragma unroll
   for (int ni = 0; ni < 4; ++ni) {
-    // SwiGLU: blocks 0,1 are gate columns wn*64 + ni*32, blocks 2,3 the matching up columns
-    const int brow = kSwiGLU ? ((ni >> 1) * (kBN / 2) + wn * 64 + (ni & 1) * 32 + r32) : (wn * 128 + ni * 32 + r32);
-    b[ni] = *reinterpret_cast<const bf16x8 *>(bs + brow * kRowBytes + pos);
+    if constexpr (kBT) {
+      b[ni] = tr_frag(bs + tks, tb[ni][0], tb[ni][1]);
+    } else {
+      // SwiGLU: blocks 0,1 are gate columns wn*64 + ni*32, blocks 2,3 the matching up columns
+      const int brow = kSwiGLU ? ((ni >> 1) * (kBN / 2) + wn * 64 + (ni & 1) * 32 + r32) : (wn * 128 + ni * 32 + r32);
+      b[ni] = *reinterpret_cast<const bf16x8 *>(bs + brow * kRowBytes + pos);
+    }
   }
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-    a[mi] = *reinterpret_cast<const bf16x8 *>(as + ((2 * mi + wm) * 32 + r32) * kRowBytes + pos);
+  for (int mi = 0; mi < 4; ++mi) {
+    if constexpr (kAT) a[mi] = tr_frag(as + tks, ta[mi][0], ta[mi][1]);
+    else a[mi] = *reinterpret_cast<const bf16x8 *>(as + ((2 * mi + wm) * 32 + r32) * kRowBytes + pos);
+  }
+}
+
+// Zeroes the K values >= kvalid (counted from the start of the K step) of the B
+// fragments of slice ks: the ragged last K step of a weight-gradient tile.
+__device__ __forceinline__ void mask_k_tail(bf16x8 (&b)[4], int ks, int kvalid, int l) {
+  const int lim = kvalid - 16 * ks - 8 * (l >> 5);  // this lane's values j < lim are real
+  uint32_t m[4];
+#pragma unroll
+  for (int d = 0; d < 4; ++d) m[d] = (2 * d < lim ? 0xFFFFu : 0u) | (2 * d + 1 < lim ? 0xFFFF0000u : 0u);
+#pragma unroll
+  for (int ni = 0; ni < 4; ++ni) {
+    u32x4 v = __builtin_bit_cast(u32x4, b[ni]);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) v[d] &= m[d];
+    b[ni] = __builtin_bit_cast(bf16x8, v);
+  }
 }
 
 // MFMAs FIRST .. FIRST+COUNT-1 of one 16-wide K slice, numbered row block
@@ -198,13 +258,13 @@ __device__ __forceinline__ void mfma_range(const bf16x8 (&a)[4], const bf16x8 (&
 }
 
 // The 4*MI MFMAs of one K slice for the wave's first MI row blocks.  The
-// fragment reads of the following slice (issued just before, in the same
-// scheduling region) are paired with the first half of the MFMAs; the slice's
-// four direct-load instructions (dma(0..3)) sit between the MFMAs of the
-// second half.  A run of load instructions would stall the wave -- and with it
-// the matrix pipe -- while the address unit works through them; spread out,
-// each load issues while the previous MFMAs run.
-template <int MI, typename Dma>
+// fragment reads of the following slice (kReads LDS reads, issued just before,
+// in the same scheduling region) are paired with the first half of the MFMAs;
+// the slice's four direct-load instructions (dma(0..3)) sit between the MFMAs
+// of the second half.  A run of load instructions would stall the wave -- and
+// with it the matrix pipe -- while the address unit works through them; spread
+// out, each load issues while the previous MFMAs run.
+template <int MI, int kReads, typename Dma>
 __device__ __forceinline__ void slice(const bf16x8 (&a)[4], const bf16x8 (&b)[4], f32x16 (&acc)[4][4],
                                       Dma &&dma) {
   constexpr int kPart = MI / 2;                  // MFMAs between two load slots (MI = 1: none)
@@ -214,7 +274,7 @@ __device__ __forceinline__ void slice(const bf16x8 (&a)[4], const bf16x8 (&b)[4]
 #pragma unroll
   for (int i = 0; i < kHead; ++i) {
     __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kDsRead, 8 / kHead, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, (kReads + kHead - 1) / kHead, 0);
   }
   __builtin_amdgcn_sched_barrier(0);
   mfma_range<kHead, kPart>(a, b, acc);
@@ -236,21 +296,24 @@ __device__ __forceinline__ void slice(const bf16x8 (&a)[4], const bf16x8 (&b)[4]
 }
 
 // Modes of the grouped GEMM.  kModePlain: per expert segment, C = A B_e^T
-// (y = act W_down^T; also the GEMMs of the backward with pre-transposed
-// weights).  kModeSwiGLU: B tile rows 0..127 are gate rows n0.., rows 128..255
-// the up rows I+n0..; output the [rows, I] SwiGLU intermediate.  kModeWGrad:
-// per expert e, C_e [M, N] = A[:, seg_e] B[:, seg_e]^T, where A [M, ld] and B
-// [N, ld] hold the experts' rows transposed, each expert's segment starting at
-// seg_offp[e] and padded with zero columns to a multiple of 64 -- the weight
-// gradients, the reduction running over the expert's rows.
+// (y = act W_down^T, and the backward's products with the weights).
+// kModeSwiGLU: B tile rows 0..127 are gate rows n0.., rows 128..255 the up rows
+// I+n0..; output the [rows, I] SwiGLU intermediate.  kModeWGrad: per expert e,
+// C_e [M, N] = A_e^T B_e with A_e [rows_e, M] and B_e [rows_e, N] the rows of
+// expert e's segment -- the weight gradients, reducing over the expert's rows.
+// kAT / kBT: the operand is K-major (stored [K, M] / [K, N]; row length M / N)
+// instead of K-contiguous ([M, K] / [N, K], row length K).  Plain mode takes
+// only kBT (B = a weight [K, N] of each expert); weight-gradient mode takes both.
 constexpr int kModePlain = 0, kModeSwiGLU = 1, kModeWGrad = 2;
 
-template <int kMode>
+template <int kMode, bool kAT, bool kBT>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
-    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int64_t b_expert_stride, int K, int N,
-    int n_tiles, const int32_t *__restrict__ tokens_per_expert, const int32_t *__restrict__ expert_offsets, int e,
-    uint16_t *__restrict__ C, int64_t ldc, int M, int ld, const int32_t *__restrict__ seg_offp, int m_tiles) {
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int64_t b_expert_stride, int K, int M, int N,
+    int m_tiles, int n_tiles, const int32_t *__restrict__ tokens_per_expert,
+    const int32_t *__restrict__ expert_offsets, int e, uint16_t *__restrict__ C, int64_t ldc) {
   constexpr bool kSwiGLU = kMode == kModeSwiGLU, kWGrad = kMode == kModeWGrad;
+  static_assert(kWGrad ? (kAT && kBT) : !kAT, "operand layouts of the modes");
+  static_assert(!(kSwiGLU && kBT), "the SwiGLU pairing reads K-contiguous weights");
   // ring of operand tiles; also find_tile's scratch before the K loop and the
   // output staging after it
   __shared__ __attribute__((aligned(1024))) char ring[kSlots * kOperandBytes];
@@ -258,49 +321,48 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   const int l = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wm = w >> 1, wn = w & 1;
-  // tile coordinates (the same in every lane: kept in scalar registers), the
-  // operand bases and row stride, the K steps and the output base
-  int te, n0, rows_valid, KT, n_lim;
-  uint32_t lda;
+  // tile coordinates (the same in every lane: kept in scalar registers): n0 the
+  // first output column, rows_valid the output rows of the tile, KT the K steps
+  // and k_len the K extent (ragged only in weight-gradient mode), the operand
+  // bases at K = 0 and the output base
+  int n0, rows_valid, KT, k_len;
   const char *a_base, *b_base;
   uint16_t *c_base;
-  int64_t c_ld;
   if constexpr (kWGrad) {
     // each XCD (workgroup b runs on XCD b % 8) takes one eighth of every
     // expert's tiles, m fastest, expert after expert: the experts' different
     // row counts (the K of these GEMMs) load the XCDs evenly
     const int per_e = m_tiles * n_tiles, chunk = (per_e + kXcds - 1) / kXcds;
     const int slot = (int)blockIdx.x / kXcds;
-    te = slot / chunk;
+    const int te = slot / chunk;
     const int local = ((int)blockIdx.x % kXcds) * chunk + slot % chunk;
     if (te >= e || local >= per_e) return;
     const int m0 = (local % m_tiles) * kBM;
     n0 = (local / m_tiles) * kBN;
     rows_valid = M - m0 < kBM ? M - m0 : kBM;
-    const int koff = __builtin_amdgcn_readfirstlane(seg_offp[te]);
-    KT = (__builtin_amdgcn_readfirstlane(seg_offp[te + 1]) - koff) / kBK;
-    lda = (uint32_t)ld;
-    a_base = reinterpret_cast<const char *>(A + (int64_t)m0 * ld + koff);
-    b_base = reinterpret_cast<const char *>(B + (int64_t)n0 * ld + koff);
-    c_ld = N;
+    k_len = __builtin_amdgcn_readfirstlane(tokens_per_expert[te]);
+    const int64_t r0 = __builtin_amdgcn_readfirstlane(expert_offsets[te]);
+    KT = (k_len + kBK - 1) / kBK;
+    a_base = reinterpret_cast<const char *>(A + r0 * M + m0);
+    b_base = reinterpret_cast<const char *>(B + r0 * N + n0);
     c_base = C + ((int64_t)te * M + m0) * N;
-    n_lim = N - n0;
   } else {
     TileCoord tc;
     if (!find_tile(tokens_per_expert, expert_offsets, e, n_tiles, reinterpret_cast<int64_t *>(ring), tc)) return;
-    te = __builtin_amdgcn_readfirstlane(tc.e);
+    const int te = __builtin_amdgcn_readfirstlane(tc.e);
     n0 = __builtin_amdgcn_readfirstlane(tc.n_tile) * (kSwiGLU ? kBN / 2 : kBN);
     const int64_t row0 = ((int64_t)__builtin_amdgcn_readfirstlane((int)(tc.row0 >> 32)) << 32) |
                          (uint32_t)__builtin_amdgcn_readfirstlane((int)tc.row0);
     rows_valid = __builtin_amdgcn_readfirstlane((int)(tc.row_end - tc.row0 < kBM ? tc.row_end - tc.row0 : kBM));
     KT = K / kBK;
-    lda = (uint32_t)K;
+    k_len = K;
     a_base = reinterpret_cast<const char *>(A + row0 * K);
-    b_base = reinterpret_cast<const char *>(B + (int64_t)te * b_expert_stride);
-    c_ld = ldc;
+    b_base = reinterpret_cast<const char *>(B + (int64_t)te * b_expert_stride + (kBT ? n0 : 0));
     c_base = C + row0 * ldc;
-    n_lim = N;
   }
+  // bytes between the operand tiles of consecutive K steps
+  const int64_t a_step = kAT ? (int64_t)kBK * M * 2 : kRowBytes;
+  const int64_t b_step = kBT ? (int64_t)kBK * N * 2 : kRowBytes;
 
   // the tile's 32-row blocks 0..7 alternate between the two row groups of waves
   // (block 2*mi + wm is this wave's block mi); count this wave's blocks that
@@ -308,38 +370,86 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   const int blocks_valid = (rows_valid + 31) / 32;
   const int mi_count = blocks_valid > wm ? (blocks_valid - wm + 1) / 2 : 0;
 
-  // direct-load sources: this wave fills tile rows w*64 .. w*64+63 of each
-  // operand tile, kLoadRows rows per instruction; lane l writes LDS bytes
+  // direct-load sources: a K-contiguous tile's row r (an output row or column)
+  // holds K values 64*kt .. +63 in 128 bytes; this wave fills rows w*64 ..
+  // w*64+63, kLoadRows rows per instruction; lane l writes LDS bytes
   // l*16..l*16+15 of the instruction's 1 KiB, i.e. row l / kChunks, position
-  // l % kChunks, so it fetches global chunk position ^ swz(row).  Addresses are
-  // a per-tile scalar base plus a 32-bit per-lane byte offset.
+  // l % kChunks, so it fetches global chunk position ^ swz(row).  A K-major
+  // tile's row k holds 256 columns in 512 bytes; this wave fills rows w*16 ..
+  // w*16+15, two per instruction: lane l fills row l / 32, position l % 32 with
+  // chunk position ^ swz_t(row); columns past the operand's end re-read its last
+  // chunk.  Addresses are a per-step scalar base plus a 32-bit per-lane offset.
   uint32_t a_off[kLoads], b_off[kLoads];
+  int a_row[kLoads], b_row[kLoads];  // K-major: the tile row each load instruction fills
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
-    const int r = w * 64 + i * kLoadRows + l / kChunks;
-    const int c = (l % kChunks) ^ swz(r);
-    const int ar = r < rows_valid ? r : rows_valid - 1;  // ragged tail: re-read the last row
-    a_off[i] = ((uint32_t)ar * lda + (uint32_t)(c * 8)) * 2u;
-    int br;
-    if (kSwiGLU) {
-      int col = n0 + (r & (kBN / 2 - 1));
-      if (col > N - 1) col = N - 1;  // N = I: up rows start at I
-      br = (r >= kBN / 2 ? N : 0) + col;
-    } else if (kWGrad) {
-      br = r < n_lim ? r : n_lim - 1;  // the base already points at row n0
+    if constexpr (kAT) {
+      const int k = w * 16 + 2 * i + l / 32;
+      int col = ((l % 32) ^ swz_t(k)) * 8;
+      if (col > rows_valid - 8) col = rows_valid - 8;  // M is a multiple of 64
+      a_row[i] = k;
+      a_off[i] = (uint32_t)col * 2u;
     } else {
-      br = n0 + r < N ? n0 + r : N - 1;
+      const int r = w * 64 + i * kLoadRows + l / kChunks;
+      const int c = (l % kChunks) ^ swz(r);
+      const int ar = r < rows_valid ? r : rows_valid - 1;  // ragged tail: re-read the last row
+      a_row[i] = 0;
+      a_off[i] = ((uint32_t)ar * (uint32_t)K + (uint32_t)(c * 8)) * 2u;
     }
-    b_off[i] = ((uint32_t)br * lda + (uint32_t)(c * 8)) * 2u;  // < 2^32: checked by the launcher
+    if constexpr (kBT) {
+      const int k = w * 16 + 2 * i + l / 32;
+      const int n_lim = N - n0;  // columns of the operand from n0 on
+      int col = ((l % 32) ^ swz_t(k)) * 8;
+      if (col > n_lim - 8) col = n_lim - 8;
+      b_row[i] = k;
+      b_off[i] = (uint32_t)col * 2u;
+    } else {
+      const int r = w * 64 + i * kLoadRows + l / kChunks;
+      const int c = (l % kChunks) ^ swz(r);
+      int br;
+      if (kSwiGLU) {
+        int col = n0 + (r & (kBN / 2 - 1));
+        if (col > N - 1) col = N - 1;  // N = I: up rows start at I
+        br = (r >= kBN / 2 ? N : 0) + col;
+      } else {
+        br = n0 + r < N ? n0 + r : N - 1;
+      }
+      b_row[i] = 0;
+      b_off[i] = ((uint32_t)br * (uint32_t)K + (uint32_t)(c * 8)) * 2u;  // < 4*I*H bytes
+    }
   }
-  const uint32_t ring_lds = lds_address(ring) + w * 64 * kRowBytes;
-  // load instruction i (0..7) of this wave for the A (B) tile of step kt into ring slot `slot`
+  const uint32_t ring_lds = lds_address(ring) + w * 64 * kRowBytes;  // = w * 16 * kTRowBytes
+  // load instruction i (0..7) of this wave for the A (B) tile of step kt into
+  // ring slot `slot`.  K-major rows past the K extent (the ragged last step of
+  // a weight gradient) re-read the extent's last row; mask_k_tail zeroes their
+  // contribution.
   auto load_a = [&](int slot, int kt, int i) {
-    dma16(a_base + 2 * kt * kBK, a_off[i], ring_lds + slot * kOperandBytes + i * 1024);
+    uint32_t off = a_off[i];
+    if constexpr (kAT) {
+      const int last = k_len - 1 - kt * kBK;
+      off += (uint32_t)(a_row[i] < last ? a_row[i] : last) * (uint32_t)M * 2u;
+    }
+    dma16(a_base + kt * a_step, off, ring_lds + slot * kOperandBytes + i * 1024);
   };
   auto load_b = [&](int slot, int kt, int i) {
-    dma16(b_base + 2 * kt * kBK, b_off[i], ring_lds + slot * kOperandBytes + i * 1024);
+    uint32_t off = b_off[i];
+    if constexpr (kBT) {
+      const int last = k_len - 1 - kt * kBK;
+      off += (uint32_t)(b_row[i] < last ? b_row[i] : last) * (uint32_t)N * 2u;
+    }
+    dma16(b_base + kt * b_step, off, ring_lds + slot * kOperandBytes + i * 1024);
   };
+  // per-lane offsets of the transposed fragment reads
+  uint32_t ta[4][2], tb[4][2];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ta[j][h] = kAT ? tr_off(l, 2 * j + wm, h) : 0u;
+      tb[j][h] = kBT ? tr_off(l, 4 * wn + j, h) : 0u;
+    }
+  constexpr int kReads = (kAT ? 8 : 4) + (kBT ? 8 : 4);
+  const int k_tail = k_len - (KT - 1) * kBK;  // K values of the last step (64 unless ragged)
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -382,35 +492,43 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   }
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  load_frags<kSwiGLU>(ring + kOperandBytes, ring, 0, wm, wn, l, fa[0], fb[0]);
+  load_frags<kSwiGLU, kAT, kBT>(ring + kOperandBytes, ring, 0, wm, wn, l, fa[0], fb[0], ta, tb);
   __builtin_amdgcn_sched_barrier(0);
 
   // one K step with MI row blocks per wave; sb, sa: slots of step kt's B and A
-  // tiles; nb, na: of step kt+1's; pb: slot for step kt+2's B tile
+  // tiles; nb, na: of step kt+1's; pb: slot for step kt+2's B tile.  In the
+  // ragged last step of a weight gradient, each slice's B fragments are masked
+  // before use (the first slice's here, the others as they are read).
 #define MOE_K_STEP(MI)                                                                                   \
   {                                                                                                     \
     const int nb = sb + 2 < kSlots ? sb + 2 : sb + 2 - kSlots;                                          \
     const int na = sa + 2 < kSlots ? sa + 2 : sa + 2 - kSlots;                                          \
     const int pb = na + 1 < kSlots ? na + 1 : na + 1 - kSlots;                                          \
     const bool ahead = kt + 2 < KT;                                                                     \
+    const bool tail = kWGrad && kt == KT - 1 && k_tail < kBK;                                           \
     const char *as = ring + sa * kOperandBytes;                                                         \
     const char *bs = ring + sb * kOperandBytes;                                                         \
-    load_frags<kSwiGLU>(as, bs, 1, wm, wn, l, fa[1], fb[1]);                                            \
-    slice<MI>(fa[0], fb[0], acc, [&](int d) {                                                           \
+    if (tail) mask_k_tail(fb[0], 0, k_tail, l);                                                         \
+    load_frags<kSwiGLU, kAT, kBT>(as, bs, 1, wm, wn, l, fa[1], fb[1], ta, tb);                          \
+    if (tail) mask_k_tail(fb[1], 1, k_tail, l);                                                         \
+    slice<MI, kReads>(fa[0], fb[0], acc, [&](int d) {                                                   \
       if (ahead) load_b(pb, kt + 2, d);                                                                 \
     });                                                                                                 \
-    load_frags<kSwiGLU>(as, bs, 2, wm, wn, l, fa[0], fb[0]);                                            \
-    slice<MI>(fa[1], fb[1], acc, [&](int d) {                                                           \
+    load_frags<kSwiGLU, kAT, kBT>(as, bs, 2, wm, wn, l, fa[0], fb[0], ta, tb);                          \
+    if (tail) mask_k_tail(fb[0], 2, k_tail, l);                                                         \
+    slice<MI, kReads>(fa[1], fb[1], acc, [&](int d) {                                                   \
       if (ahead) load_b(pb, kt + 2, 4 + d);                                                             \
     });                                                                                                 \
-    load_frags<kSwiGLU>(as, bs, 3, wm, wn, l, fa[1], fb[1]);                                            \
-    slice<MI>(fa[0], fb[0], acc, [&](int) {});                                                          \
+    load_frags<kSwiGLU, kAT, kBT>(as, bs, 3, wm, wn, l, fa[1], fb[1], ta, tb);                          \
+    if (tail) mask_k_tail(fb[1], 3, k_tail, l);                                                         \
+    slice<MI, kReads>(fa[0], fb[0], acc, [&](int) {});                                                  \
     if (ahead) wait_vmcnt<kLoads>();                                                                    \
     else wait_vmcnt<0>();                                                                               \
     lds_barrier();                                                                                      \
     __builtin_amdgcn_sched_barrier(0);                                                                  \
-    load_frags<kSwiGLU>(ring + na * kOperandBytes, ring + nb * kOperandBytes, 0, wm, wn, l, fa[0], fb[0]); \
-    slice<MI>(fa[1], fb[1], acc, [&](int d) {                                                           \
+    load_frags<kSwiGLU, kAT, kBT>(ring + na * kOperandBytes, ring + nb * kOperandBytes, 0, wm, wn, l,   \
+                                  fa[0], fb[0], ta, tb);                                                \
+    slice<MI, kReads>(fa[1], fb[1], acc, [&](int d) {                                                   \
       if (ahead) {                                                                                      \
         load_a(sb, kt + 2, 2 * d);                                                                      \
         load_a(sb, kt + 2, 2 * d + 1);                                                                  \
@@ -477,6 +595,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   constexpr int kRowsPerPass = kWave / kChunksPerRow;
   const int col0 = n0 + wn * kCols;
   const int ch = l % kChunksPerRow;
+  const int64_t c_ld = kWGrad ? (int64_t)N : ldc;
 #pragma unroll 4
   for (int r = l / kChunksPerRow; r < 128; r += kRowsPerPass) {
     const int row = (2 * (r >> 5) + wm) * 32 + (r & 31);  // staged row r is row r%32 of block r/32
@@ -497,110 +616,6 @@ int64_t tile_bound(int64_t rows, int e, int capacity, int n_tiles) {
 }
 
 // ------------------------------------------------------------------ backward
-//
-// The weight gradients reduce over an expert's rows, so their GEMM operands
-// (dy, x and the two intermediates) are used transposed: [features, rows], each
-// expert's rows a segment of columns padded with zeros to a multiple of kBK and
-// starting at seg_offp[e].  The activation-gradient GEMMs take the weights
-// transposed ([E, I, H] and [E, H, 2I]) so that their operands are K-contiguous
-// like every other operand of the grouped GEMM.
-
-// seg_offp[x] = sum over experts x' < x of tokens_per_expert[x'] rounded up to
-// kBK; seg_offp[e] = the columns in use.
-__global__ __launch_bounds__(kThreads) void seg_offsets_kernel(const int32_t *__restrict__ tokens_per_expert, int e,
-                                                               int32_t *__restrict__ seg_offp) {
-  constexpr int kPer = kMaxExperts / kThreads;
-  __shared__ int32_t part[kThreads];
-  const int tid = threadIdx.x;
-  int32_t local[kPer];
-  int32_t s = 0;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int x = tid * kPer + i;
-    const int32_t c = x < e ? tokens_per_expert[x] : 0;
-    local[i] = (c + kBK - 1) / kBK * kBK;
-    s += local[i];
-  }
-  part[tid] = s;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const int32_t v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int32_t run = part[tid] - s;
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    const int x = tid * kPer + i;
-    if (x < e) seg_offp[x] = run;
-    run += local[i];
-  }
-  if (tid == kThreads - 1) seg_offp[e] = part[kThreads - 1];
-}
-
-// One 64 x 64 bf16 transpose through LDS: source rows 0..63 (rows >= nv read
-// as zeros), columns 0..63 of `src` (row stride src_ld) become destination rows
-// 0..63, columns 0..63 of `dst` (row stride dst_ld).  The tile is held as
-// 32-bit column pairs, 33 words per source row, so that both the 16-byte row
-// writes and the column reads spread over the LDS banks.
-__device__ __forceinline__ void transpose_tile64(const uint16_t *__restrict__ src, int64_t src_ld, int nv,
-                                                 uint16_t *__restrict__ dst, int64_t dst_ld) {
-  constexpr int kPitch = 33;
-  __shared__ uint32_t tile[64 * kPitch];
-  const int t = threadIdx.x;
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const int j = t / 8 + 32 * p, q = t % 8;
-    u32x4 v = {0u, 0u, 0u, 0u};
-    if (j < nv) v = ld16(src + (int64_t)j * src_ld + 8 * q);
-#pragma unroll
-    for (int d = 0; d < 4; ++d) tile[j * kPitch + 4 * q + d] = v[d];
-  }
-  __syncthreads();
-  const int jg = t % 8, cp = t / 8;  // source rows 8*jg .. 8*jg+7, source columns 2*cp, 2*cp+1
-  uint32_t w[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) w[i] = tile[(8 * jg + i) * kPitch + cp];
-  u32x4 lo, hi;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    lo[i] = (w[2 * i] & 0xFFFFu) | (w[2 * i + 1] << 16);
-    hi[i] = (w[2 * i] >> 16) | (w[2 * i + 1] & 0xFFFF0000u);
-  }
-  st16(dst + (int64_t)(2 * cp) * dst_ld + 8 * jg, lo);
-  st16(dst + (int64_t)(2 * cp + 1) * dst_ld + 8 * jg, hi);
-}
-
-// Batched transpose of expert weights: src [batch, P, Q] -> dst [batch, Q, P];
-// P and Q multiples of 64; grid (P/64, Q/64, batch).
-__global__ __launch_bounds__(kThreads) void weight_transpose_kernel(const uint16_t *__restrict__ src, int P, int Q,
-                                                                    uint16_t *__restrict__ dst) {
-  const int64_t b = blockIdx.z;
-  const int j0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-  transpose_tile64(src + (b * P + j0) * Q + c0, Q, 64, dst + (b * Q + c0) * P + j0, P);
-}
-
-// Segment transpose of expert rows: dst [C, ld] column seg_offp[x] + i holds
-// row expert_offsets[x] + i of src [*, C] for i < tokens_per_expert[x] and zero
-// up to the next multiple of 64.  C is a multiple of 64; grid (ld/64, C/64).
-// Every 64-column block lies inside one expert's padded segment.
-__global__ __launch_bounds__(kThreads) void seg_transpose_kernel(
-    const uint16_t *__restrict__ src, int C, const int32_t *__restrict__ seg_offp,
-    const int32_t *__restrict__ tokens_per_expert, const int32_t *__restrict__ expert_offsets, int e,
-    uint16_t *__restrict__ dst, int ld) {
-  const int j0 = blockIdx.x * 64, c0 = blockIdx.y * 64;
-  if (j0 >= seg_offp[e]) return;
-  int lo = 0, hi = e - 1;  // the last expert whose segment starts at or before j0
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (seg_offp[mid] <= j0) lo = mid;
-    else hi = mid - 1;
-  }
-  const int i0 = j0 - seg_offp[lo];
-  const int nv = tokens_per_expert[lo] - i0;
-  transpose_tile64(src + ((int64_t)expert_offsets[lo] + i0) * C + c0, C, nv, dst + (int64_t)c0 * ld + j0, ld);
-}
 
 // SwiGLU backward, in place, 8 features per thread.  For row r and feature i,
 // with g = gu[r, i], u = gu[r, I+i], da = d_act[r, i], s = sigmoid(g):
@@ -636,116 +651,68 @@ __global__ __launch_bounds__(kThreads) void swiglu_bwd_kernel(uint16_t *__restri
   }
 }
 
-int64_t seg_ld(int64_t rows, int e) { return ((rows + kBK - 1) / kBK + e) * kBK; }
-
-struct BwdWorkspace {
-  int32_t *seg_offp;
-  uint16_t *wd_t, *wgu_t, *gu, *dact, *t_h, *t_i;
-};
-
-// Carves the backward workspace; with base == nullptr only counts bytes.
-size_t carve_bwd(char *base, int64_t rows, int64_t hidden, int inter, int e, BwdWorkspace *w) {
-  const int64_t ld = seg_ld(rows, e);
-  size_t off = 0;
-  auto take = [&](size_t bytes) {
-    char *p = base ? base + off : nullptr;
-    off += align256(bytes);
-    return p;
-  };
-  BwdWorkspace v;
-  v.seg_offp = reinterpret_cast<int32_t *>(take(sizeof(int32_t) * (size_t)(e + 1)));
-  v.wd_t = reinterpret_cast<uint16_t *>(take(2 * (size_t)e * inter * hidden));
-  v.wgu_t = reinterpret_cast<uint16_t *>(take(4 * (size_t)e * inter * hidden));
-  v.gu = reinterpret_cast<uint16_t *>(take(4 * (size_t)rows * inter));
-  v.dact = reinterpret_cast<uint16_t *>(take(2 * (size_t)rows * inter));
-  v.t_h = reinterpret_cast<uint16_t *>(take(2 * (size_t)hidden * ld));
-  v.t_i = reinterpret_cast<uint16_t *>(take(4 * (size_t)inter * ld));
-  if (w) *w = v;
-  return off;
-}
-
-// Plain grouped GEMM over the expert segments: C [rows, N] = A [rows, K] B_e^T.
+// Grouped GEMM over the expert segments, C [rows, N] = A [rows, K] B_e^T with
+// B_e [N, K] (kBT false) or B_e [K, N] (kBT true).
+template <bool kBT>
 hipError_t launch_plain(const uint16_t *A, const uint16_t *B, int64_t b_stride, int K, int N, int64_t rows, int e,
                         int capacity, const int32_t *tokens_per_expert, const int32_t *expert_offsets, uint16_t *C,
                         hipStream_t stream) {
   const int nt = (N + kBN - 1) / kBN;
   const int64_t g = tile_bound(rows, e, capacity, nt);
-  hipLaunchKernelGGL(grouped_gemm_kernel<kModePlain>, dim3((unsigned)g), dim3(kThreads), 0, stream, A, B, b_stride,
-                     K, N, nt, tokens_per_expert, expert_offsets, e, C, (int64_t)N, 0, 0, nullptr, 0);
+  hipLaunchKernelGGL((grouped_gemm_kernel<kModePlain, false, kBT>), dim3((unsigned)g), dim3(kThreads), 0, stream, A,
+                     B, b_stride, K, 0, N, 0, nt, tokens_per_expert, expert_offsets, e, C, (int64_t)N);
   return hipGetLastError();
 }
 
-// Weight-gradient GEMM: C_e [M, N] = A[:, seg_e] B[:, seg_e]^T for every expert.
-hipError_t launch_wgrad(const uint16_t *A, const uint16_t *B, int M, int N, int ld, const int32_t *seg_offp, int e,
-                        uint16_t *C, hipStream_t stream) {
+// Weight-gradient GEMM: C_e [M, N] = A_e^T B_e for every expert, A_e [rows_e, M]
+// and B_e [rows_e, N] the rows of expert e's segment.
+hipError_t launch_wgrad(const uint16_t *A, const uint16_t *B, int M, int N, int e, const int32_t *tokens_per_expert,
+                        const int32_t *expert_offsets, uint16_t *C, hipStream_t stream) {
   const int mt = (M + kBM - 1) / kBM, nt = (N + kBN - 1) / kBN;
   const int chunk = (mt * nt + kXcds - 1) / kXcds;
-  hipLaunchKernelGGL(grouped_gemm_kernel<kModeWGrad>, dim3((unsigned)(kXcds * e * chunk)), dim3(kThreads), 0, stream,
-                     A, B, (int64_t)0, 0, N, nt, nullptr, nullptr, e, C, (int64_t)N, M, ld, seg_offp, mt);
-  return hipGetLastError();
-}
-
-hipError_t launch_seg_transpose(const uint16_t *src, int cols, const BwdWorkspace &w, int ld,
-                                const int32_t *tokens_per_expert, const int32_t *expert_offsets, int e,
-                                uint16_t *dst, hipStream_t stream) {
-  hipLaunchKernelGGL(seg_transpose_kernel, dim3((unsigned)(ld / 64), (unsigned)(cols / 64)), dim3(kThreads), 0,
-                     stream, src, cols, w.seg_offp, tokens_per_expert, expert_offsets, e, dst, ld);
+  hipLaunchKernelGGL((grouped_gemm_kernel<kModeWGrad, true, true>), dim3((unsigned)(kXcds * e * chunk)),
+                     dim3(kThreads), 0, stream, A, B, (int64_t)0, 0, M, N, mt, nt, tokens_per_expert, expert_offsets,
+                     e, C, (int64_t)N);
   return hipGetLastError();
 }
 
 }  // namespace
 
-size_t ffn_bwd_workspace_bytes(int64_t rows, int64_t hidden, int inter, int e) {
-  return carve_bwd(nullptr, rows, hidden, inter, e, nullptr);
+size_t ffn_bwd_workspace_bytes(int64_t rows, int inter) {
+  return align256(4 * (size_t)rows * inter) + align256(2 * (size_t)rows * inter);
 }
-
-int64_t ffn_bwd_seg_ld(int64_t rows, int e) { return seg_ld(rows, e); }
 
 hipError_t launch_expert_ffn_bwd(const uint16_t *x_perm, const uint16_t *grad_y, int64_t rows, int64_t hidden,
                                  int inter, int e, int capacity, const int32_t *tokens_per_expert,
                                  const int32_t *expert_offsets, const uint16_t *w_gate_up, const uint16_t *w_down,
                                  uint16_t *grad_x_perm, uint16_t *grad_w_gate_up, uint16_t *grad_w_down,
                                  void *workspace, hipStream_t stream) {
-  BwdWorkspace w;
-  carve_bwd(static_cast<char *>(workspace), rows, hidden, inter, e, &w);
-  const int ld = (int)seg_ld(rows, e);
+  // workspace: [G | U] then [dG | dU] ([rows, 2I]); dA then the activation ([rows, I])
+  uint16_t *gu = static_cast<uint16_t *>(workspace);
+  uint16_t *dact = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + align256(4 * (size_t)rows * inter));
   const int H = (int)hidden, I = inter;
   hipError_t st;
 #define MOE_TRY(x)                    \
   if ((st = (x)) != hipSuccess) return st;
-  hipLaunchKernelGGL(seg_offsets_kernel, dim3(1), dim3(kThreads), 0, stream, tokens_per_expert, e, w.seg_offp);
-  MOE_TRY(hipGetLastError());
-  // W_down^T [E, I, H] and W_gate_up^T [E, H, 2I]
-  hipLaunchKernelGGL(weight_transpose_kernel, dim3((unsigned)(H / 64), (unsigned)(I / 64), (unsigned)e),
-                     dim3(kThreads), 0, stream, w_down, H, I, w.wd_t);
-  MOE_TRY(hipGetLastError());
-  hipLaunchKernelGGL(weight_transpose_kernel, dim3((unsigned)(2 * I / 64), (unsigned)(H / 64), (unsigned)e),
-                     dim3(kThreads), 0, stream, w_gate_up, 2 * I, H, w.wgu_t);
-  MOE_TRY(hipGetLastError());
   if (rows > 0) {
-    // [G | U] = x W_gate_up^T (recomputed), dA = dy W_down
-    MOE_TRY(launch_plain(x_perm, w_gate_up, (int64_t)2 * I * H, H, 2 * I, rows, e, capacity, tokens_per_expert,
-                         expert_offsets, w.gu, stream));
-    MOE_TRY(launch_plain(grad_y, w.wd_t, (int64_t)I * H, H, I, rows, e, capacity, tokens_per_expert, expert_offsets,
-                         w.dact, stream));
+    // [G | U] = x W_gate_up^T (recomputed); dA = dy W_down (W_down [H, I]: K-major)
+    MOE_TRY(launch_plain<false>(x_perm, w_gate_up, (int64_t)2 * I * H, H, 2 * I, rows, e, capacity,
+                                tokens_per_expert, expert_offsets, gu, stream));
+    MOE_TRY(launch_plain<true>(grad_y, w_down, (int64_t)I * H, H, I, rows, e, capacity, tokens_per_expert,
+                               expert_offsets, dact, stream));
     // [dG | dU] in place of [G | U]; the activation in place of dA
     const int64_t chunks = rows * (I / 8);
     int64_t blocks = (chunks + kThreads - 1) / kThreads;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, w.gu, w.dact, rows, I);
+    hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, gu, dact, rows, I);
     MOE_TRY(hipGetLastError());
-    // dx = [dG | dU] W_gate_up
-    MOE_TRY(launch_plain(w.gu, w.wgu_t, (int64_t)H * 2 * I, 2 * I, H, rows, e, capacity, tokens_per_expert,
-                         expert_offsets, grad_x_perm, stream));
+    // dx = [dG | dU] W_gate_up (W_gate_up [2I, H]: K-major)
+    MOE_TRY(launch_plain<true>(gu, w_gate_up, (int64_t)H * 2 * I, 2 * I, H, rows, e, capacity, tokens_per_expert,
+                               expert_offsets, grad_x_perm, stream));
   }
-  // dW_down_e = dy_e^T a_e
-  MOE_TRY(launch_seg_transpose(grad_y, H, w, ld, tokens_per_expert, expert_offsets, e, w.t_h, stream));
-  MOE_TRY(launch_seg_transpose(w.dact, I, w, ld, tokens_per_expert, expert_offsets, e, w.t_i, stream));
-  MOE_TRY(launch_wgrad(w.t_h, w.t_i, H, I, ld, w.seg_offp, e, grad_w_down, stream));
-  // [dW_gate; dW_up]_e = [dG | dU]_e^T x_e
-  MOE_TRY(launch_seg_transpose(x_perm, H, w, ld, tokens_per_expert, expert_offsets, e, w.t_h, stream));
-  MOE_TRY(launch_seg_transpose(w.gu, 2 * I, w, ld, tokens_per_expert, expert_offsets, e, w.t_i, stream));
-  MOE_TRY(launch_wgrad(w.t_i, w.t_h, 2 * I, H, ld, w.seg_offp, e, grad_w_gate_up, stream));
+  // dW_down_e = dy_e^T a_e;  [dW_gate; dW_up]_e = [dG | dU]_e^T x_e  (experts without rows: zeros)
+  MOE_TRY(launch_wgrad(grad_y, dact, H, I, e, tokens_per_expert, expert_offsets, grad_w_down, stream));
+  MOE_TRY(launch_wgrad(gu, x_perm, 2 * I, H, e, tokens_per_expert, expert_offsets, grad_w_gate_up, stream));
 #undef MOE_TRY
   return hipSuccess;
 }
@@ -760,16 +727,16 @@ hipError_t launch_expert_ffn(const uint16_t *x_perm, int64_t rows, int64_t hidde
   uint16_t *act = static_cast<uint16_t *>(workspace);
   const int n1 = (inter + kBN / 2 - 1) / (kBN / 2);
   const int64_t g1 = tile_bound(rows, e, capacity, n1);
-  hipLaunchKernelGGL(grouped_gemm_kernel<kModeSwiGLU>, dim3((unsigned)g1), dim3(kThreads), 0, stream, x_perm,
-                     w_gate_up, (int64_t)2 * inter * hidden, (int)hidden, inter, n1, tokens_per_expert, expert_offsets,
-                     e, act, (int64_t)inter, 0, 0, nullptr, 0);
+  hipLaunchKernelGGL((grouped_gemm_kernel<kModeSwiGLU, false, false>), dim3((unsigned)g1), dim3(kThreads), 0, stream,
+                     x_perm, w_gate_up, (int64_t)2 * inter * hidden, (int)hidden, 0, inter, 0, n1, tokens_per_expert,
+                     expert_offsets, e, act, (int64_t)inter);
   hipError_t st = hipGetLastError();
   if (st != hipSuccess) return st;
   const int n2 = (int)((hidden + kBN - 1) / kBN);
   const int64_t g2 = tile_bound(rows, e, capacity, n2);
-  hipLaunchKernelGGL(grouped_gemm_kernel<kModePlain>, dim3((unsigned)g2), dim3(kThreads), 0, stream, act, w_down,
-                     (int64_t)hidden * inter, inter, (int)hidden, n2, tokens_per_expert, expert_offsets, e, y, hidden,
-                     0, 0, nullptr, 0);
+  hipLaunchKernelGGL((grouped_gemm_kernel<kModePlain, false, false>), dim3((unsigned)g2), dim3(kThreads), 0, stream,
+                     act, w_down, (int64_t)hidden * inter, inter, 0, (int)hidden, 0, n2, tokens_per_expert,
+                     expert_offsets, e, y, hidden);
   return hipGetLastError();
 }
 

@@ -175,10 +175,9 @@ moe_status moe_expert_ffn(const moe_shape *s, const void *x_perm, const moe_layo
  * Shapes as moe_expert_ffn: x_perm, grad_y, grad_x_perm bf16 [R, H];
  * w_gate_up, grad_w_gate_up bf16 [E, 2I, H]; w_down, grad_w_down bf16 [E, H, I];
  * outputs must not alias inputs or each other.  Same shape limits as
- * moe_expert_ffn, and R + 64*E < 2^23.
- * Workspace: moe_workspace_size(MOE_OP_EXPERT_FFN_BWD) (transposed weights,
- * the [R, 3I] bf16 intermediates and the row-transposed operands of the weight
- * gradients). */
+ * moe_expert_ffn.  Deterministic: no atomics, fixed reduction order.
+ * Workspace: moe_workspace_size(MOE_OP_EXPERT_FFN_BWD) (the [R, 3I] bf16
+ * intermediates). */
 moe_status moe_expert_ffn_bwd(const moe_shape *s, const void *x_perm, const void *grad_y, const moe_layout *layout,
                               const void *w_gate_up, const void *w_down, void *grad_x_perm, void *grad_w_gate_up,
                               void *grad_w_down, void *workspace, size_t workspace_bytes, void *stream);

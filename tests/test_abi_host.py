@@ -58,10 +58,7 @@ def test_layout_rows_and_workspace_sizes(moe):
     assert moe.workspace_size(moe.MOE_OP_DISPATCH, s) >= tiles * 32 * 4
     s = moe.make_shape(8192, 4096, 128, 8, inter=1536)
     assert moe.workspace_size(moe.MOE_OP_EXPERT_FFN, s) >= 65536 * 1536 * 2
-    # backward: transposed weights (3*E*I*H), [R, 3I] intermediates, row-transposed operands
-    ld = (65536 // 64 + 128) * 64
-    assert moe.workspace_size(moe.MOE_OP_EXPERT_FFN_BWD, s) >= 2 * (3 * 128 * 1536 * 4096 + 65536 * 3 * 1536
-                                                                     + (4096 + 2 * 1536) * ld)
+    assert moe.workspace_size(moe.MOE_OP_EXPERT_FFN_BWD, s) >= 65536 * 3 * 1536 * 2   # [R, 3I] bf16
     assert moe.workspace_size(moe.MOE_OP_DISPATCH, moe.make_shape(0, 64, 4, 2)) == 0
 
 
@@ -112,8 +109,6 @@ def test_validation_errors_enqueue_nothing(moe):
     assert bwd(C.byref(s), p, p, C.byref(lay), p, p, q, odd, r, p, 1 << 30, None) == -2
     assert bwd(C.byref(s), p, p, None, p, p, q, r, C.c_void_p(16384), p, 1 << 30, None) == -1
     assert bwd(C.byref(s), p, p, C.byref(lay), p, p, q, None, r, p, 1 << 30, None) == -1  # null grad_w_gate_up
-    s_big = moe.make_shape(1 << 23, 64, 8, 1, inter=64)                          # row-transposed operands too wide
-    assert bwd(C.byref(s_big), p, p, C.byref(lay), p, p, q, r, C.c_void_p(16384), p, 1 << 40, None) == -4
     s32 = moe.make_shape(16, 64, 8, 2, inter=64, act_dtype=moe.MOE_DT_F32)
     assert bwd(C.byref(s32), p, p, C.byref(lay), p, p, q, r, C.c_void_p(16384), p, 1 << 30, None) == -4
     assert lib.moe_combine(C.byref(s), p, p, C.byref(lay), p, None) == -1     # out aliases y
