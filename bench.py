@@ -205,27 +205,36 @@ def bench_expert_gemm(moe, mi, torch, wid, iters, warmup, bwd_iters=0):
     out = dict(workload=w.name, rows=rows, ms=ms, tflops=flops / ms / 1e9, flops=flops)
     del ws
     if bwd_iters > 0:
+        def timed(fn, n):
+            for _ in range(warmup):
+                fn()
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(n):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / n
+
+        # training forward: also stores the pre-activations [G | U] for the backward
+        gu = torch.empty((xp.shape[0], 2 * inter), dtype=torch.bfloat16, device=dev)
+        ws = torch.empty(moe.workspace_size(moe.MOE_OP_EXPERT_FFN, shape) + 256, dtype=torch.uint8, device=dev)
+        fms = timed(lambda: moe.moe_expert_ffn(xp, lay, wgu, wd, y=y, gate_up=gu, workspace=ws), iters)
+        del ws
         # backward: dy [R, H] in, grad_x_perm [R, H], grad_w_gate_up, grad_w_down out
         dy = torch.randn(xp.shape, generator=g, device=dev).to(torch.bfloat16)
         gx, dwgu, dwd = torch.empty_like(xp), torch.empty_like(wgu), torch.empty_like(wd)
         ws = torch.empty(moe.workspace_size(moe.MOE_OP_EXPERT_FFN_BWD, shape) + 256, dtype=torch.uint8, device=dev)
-        run = lambda: moe.moe_expert_ffn_bwd(xp, dy, lay, wgu, wd, grad_x_perm=gx, grad_w_gate_up=dwgu,
-                                             grad_w_down=dwd, workspace=ws)
-        for _ in range(warmup):
-            run()
-        torch.cuda.synchronize()
-        a.record()
-        for _ in range(bwd_iters):
-            run()
-        b.record()
-        torch.cuda.synchronize()
-        bms = a.elapsed_time(b) / bwd_iters
-        # the backward's own products (dA, dx, dW_down, dW_gate_up): twice the forward's
-        # flops; the recomputed gate/up projection adds 2*rows*H*2I executed flops
+        bwd = lambda saved: moe.moe_expert_ffn_bwd(xp, dy, lay, wgu, wd, gate_up=saved, grad_x_perm=gx,
+                                                   grad_w_gate_up=dwgu, grad_w_down=dwd, workspace=ws)
+        bms = timed(lambda: bwd(gu), bwd_iters)
+        rms = timed(lambda: bwd(None), bwd_iters)
+        # the backward's products (dA, dx, dW_down, dW_gate_up): twice the forward's
+        # flops; recomputing [G | U] adds 2*rows*H*2I
         bflops = 2.0 * rows * h * 6 * inter
-        out.update(bwd_ms=bms, bwd_tflops=bflops / bms / 1e9,
-                   bwd_exec_tflops=(bflops + 2.0 * rows * h * 2 * inter) / bms / 1e9)
-        del dy, gx, dwgu, dwd, ws
+        out.update(fwd_save_ms=fms, bwd_ms=bms, bwd_tflops=bflops / bms / 1e9, bwd_recompute_ms=rms,
+                   bwd_recompute_tflops=(bflops + 2.0 * rows * h * 2 * inter) / rms / 1e9)
+        del dy, gx, dwgu, dwd, ws, gu
     del wgu, wd, x, xp, y
     torch.cuda.empty_cache()
     return out
@@ -387,9 +396,11 @@ def main():
                      "algorithmic_bytes": dc["combine_bytes"]},
         "expert_gemm": [{"workload": g["workload"], "rows": g["rows"], "us": round(g["ms"] * 1e3, 1),
                          "tflops": round(g["tflops"], 1), "frac_bf16_peak": round(g["tflops"] / BF16_PEAK_TFLOPS, 4),
-                         **({"bwd_us": round(g["bwd_ms"] * 1e3, 1), "bwd_tflops": round(g["bwd_tflops"], 1),
+                         **({"fwd_saving_gate_up_us": round(g["fwd_save_ms"] * 1e3, 1),
+                             "bwd_us": round(g["bwd_ms"] * 1e3, 1), "bwd_tflops": round(g["bwd_tflops"], 1),
                              "bwd_frac_bf16_peak": round(g["bwd_tflops"] / BF16_PEAK_TFLOPS, 4),
-                             "bwd_exec_tflops": round(g["bwd_exec_tflops"], 1)} if "bwd_ms" in g else {})}
+                             "bwd_recompute_us": round(g["bwd_recompute_ms"] * 1e3, 1),
+                             "bwd_recompute_tflops": round(g["bwd_recompute_tflops"], 1)} if "bwd_ms" in g else {})}
                         for g in gemm],
         "cpu_baseline": cpu,
     }

@@ -57,8 +57,8 @@ def _load():
     lib.moe_workspace_size.argtypes = [i32, sp, C.POINTER(C.c_size_t)]
     lib.moe_route.argtypes = [sp, p, p, p, p, p, p]
     lib.moe_dispatch.argtypes = [sp, p, p, p, lp, p, p, p, C.c_size_t, p]
-    lib.moe_expert_ffn.argtypes = [sp, p, lp, p, p, p, p, C.c_size_t, p]
-    lib.moe_expert_ffn_bwd.argtypes = [sp, p, p, lp, p, p, p, p, p, p, C.c_size_t, p]
+    lib.moe_expert_ffn.argtypes = [sp, p, lp, p, p, p, p, p, C.c_size_t, p]
+    lib.moe_expert_ffn_bwd.argtypes = [sp, p, p, p, lp, p, p, p, p, p, p, C.c_size_t, p]
     lib.moe_combine.argtypes = [sp, p, p, lp, p, p]
     lib.moe_combine_bwd.argtypes = [sp, p, p, p, lp, p, p, p]
     lib.moe_dispatch_bwd.argtypes = [sp, p, lp, p, p]
@@ -226,8 +226,11 @@ def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor |
 
 
 def moe_expert_ffn(x_perm: torch.Tensor, layout: Layout, w_gate_up: torch.Tensor, w_down: torch.Tensor, *,
-                   y: torch.Tensor | None = None, workspace=None) -> torch.Tensor:
-    """Grouped SwiGLU FFN (include/moe.h moe_expert_ffn): bf16 x_perm [R, H], w_gate_up [E, 2I, H], w_down [E, H, I]."""
+                   y: torch.Tensor | None = None, gate_up: torch.Tensor | None = None, save_gate_up: bool = False,
+                   workspace=None):
+    """Grouped SwiGLU FFN (include/moe.h moe_expert_ffn): bf16 x_perm [R, H], w_gate_up [E, 2I, H], w_down [E, H, I].
+    Returns y [R, H]; with save_gate_up (or a gate_up buffer [R, 2I]) returns (y, gate_up), the
+    pre-activations moe_expert_ffn_bwd can take."""
     for t, name in ((x_perm, "x_perm"), (w_gate_up, "w_gate_up"), (w_down, "w_down")):
         _contig(t, name)
         if t.dtype != torch.bfloat16:
@@ -246,17 +249,24 @@ def moe_expert_ffn(x_perm: torch.Tensor, layout: Layout, w_gate_up: torch.Tensor
     else:
         ws, nbytes = workspace, workspace.numel() - 256
     lc = layout.c()
+    if save_gate_up and gate_up is None:
+        gate_up = torch.empty((rows, 2 * inter), dtype=torch.bfloat16, device=dev)
+    if gate_up is not None:
+        _contig(gate_up, "gate_up")
+        if gate_up.dtype != torch.bfloat16 or tuple(gate_up.shape) != (rows, 2 * inter):
+            raise ValueError("gate_up must be bfloat16 [R, 2I]")
     _check(lib.moe_expert_ffn(C.byref(shape), _ptr(x_perm), C.byref(lc), _ptr(w_gate_up), _ptr(w_down), _ptr(y),
-                              _ws_ptr(ws), nbytes, _stream(dev)), "moe_expert_ffn")
-    return y
+                              _ptr(gate_up), _ws_ptr(ws), nbytes, _stream(dev)), "moe_expert_ffn")
+    return (y, gate_up) if gate_up is not None else y
 
 
 def moe_expert_ffn_bwd(x_perm: torch.Tensor, grad_y: torch.Tensor, layout: Layout, w_gate_up: torch.Tensor,
-                       w_down: torch.Tensor, *, grad_x_perm: torch.Tensor | None = None,
-                       grad_w_gate_up: torch.Tensor | None = None, grad_w_down: torch.Tensor | None = None,
-                       workspace=None):
+                       w_down: torch.Tensor, *, gate_up: torch.Tensor | None = None,
+                       grad_x_perm: torch.Tensor | None = None, grad_w_gate_up: torch.Tensor | None = None,
+                       grad_w_down: torch.Tensor | None = None, workspace=None):
     """Backward of the grouped SwiGLU FFN (include/moe.h moe_expert_ffn_bwd)
-    -> (grad_x_perm [R, H], grad_w_gate_up [E, 2I, H], grad_w_down [E, H, I]), all bf16."""
+    -> (grad_x_perm [R, H], grad_w_gate_up [E, 2I, H], grad_w_down [E, H, I]), all bf16.
+    gate_up: the pre-activations saved by moe_expert_ffn (None: recomputed)."""
     for t, name in ((x_perm, "x_perm"), (grad_y, "grad_y"), (w_gate_up, "w_gate_up"), (w_down, "w_down")):
         _contig(t, name)
         if t.dtype != torch.bfloat16:
@@ -267,6 +277,10 @@ def moe_expert_ffn_bwd(x_perm: torch.Tensor, grad_y: torch.Tensor, layout: Layou
     if (h2 != h or tuple(w_down.shape) != (e, h, inter) or tuple(grad_y.shape) != (rows, h)
             or e != layout.n_experts or rows != layout.rows):
         raise ValueError("inconsistent expert FFN shapes")
+    if gate_up is not None:
+        _contig(gate_up, "gate_up")
+        if gate_up.dtype != torch.bfloat16 or tuple(gate_up.shape) != (rows, 2 * inter):
+            raise ValueError("gate_up must be bfloat16 [R, 2I]")
     dev = x_perm.device
     shape = layout.shape(h, MOE_DT_BF16, inter)
     if grad_x_perm is None:
@@ -280,9 +294,9 @@ def moe_expert_ffn_bwd(x_perm: torch.Tensor, grad_y: torch.Tensor, layout: Layou
     else:
         ws, nbytes = workspace, workspace.numel() - 256
     lc = layout.c()
-    _check(lib.moe_expert_ffn_bwd(C.byref(shape), _ptr(x_perm), _ptr(grad_y), C.byref(lc), _ptr(w_gate_up),
-                                  _ptr(w_down), _ptr(grad_x_perm), _ptr(grad_w_gate_up), _ptr(grad_w_down),
-                                  _ws_ptr(ws), nbytes, _stream(dev)), "moe_expert_ffn_bwd")
+    _check(lib.moe_expert_ffn_bwd(C.byref(shape), _ptr(x_perm), _ptr(grad_y), _ptr(gate_up), C.byref(lc),
+                                  _ptr(w_gate_up), _ptr(w_down), _ptr(grad_x_perm), _ptr(grad_w_gate_up),
+                                  _ptr(grad_w_down), _ws_ptr(ws), nbytes, _stream(dev)), "moe_expert_ffn_bwd")
     return grad_x_perm, grad_w_gate_up, grad_w_down
 
 

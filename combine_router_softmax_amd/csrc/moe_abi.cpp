@@ -149,15 +149,19 @@ moe_status moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_i
 }
 
 moe_status moe_expert_ffn(const moe_shape *s, const void *x_perm, const moe_layout *layout, const void *w_gate_up,
-                          const void *w_down, void *y, void *workspace, size_t workspace_bytes, void *stream) {
+                          const void *w_down, void *y, void *gate_up, void *workspace, size_t workspace_bytes,
+                          void *stream) {
   int64_t rows;
   moe_status st = check_ffn_shape(s, &rows);
   if (st != MOE_OK) return st;
   if (!layout || !layout->tokens_per_expert || !layout->expert_offsets || !w_gate_up || !w_down)
     return MOE_ERR_INVALID_ARG;
   if (rows > 0 && (!x_perm || !y)) return MOE_ERR_INVALID_ARG;
-  if (!need(x_perm, rows, aligned16) || !need(y, rows, aligned16) || !aligned16(w_gate_up) || !aligned16(w_down))
+  if (!need(x_perm, rows, aligned16) || !need(y, rows, aligned16) || !need(gate_up, rows, aligned16) ||
+      !aligned16(w_gate_up) || !aligned16(w_down))
     return MOE_ERR_MISALIGNED;
+  if (gate_up && (gate_up == x_perm || gate_up == y || gate_up == w_gate_up || gate_up == w_down))
+    return MOE_ERR_INVALID_ARG;
   const size_t need_ws = moe::ffn_workspace_bytes(rows, s->inter);
   if (workspace_bytes < need_ws || (need_ws > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))))
     return MOE_ERR_WORKSPACE;
@@ -165,12 +169,13 @@ moe_status moe_expert_ffn(const moe_shape *s, const void *x_perm, const moe_layo
                                            s->n_experts, s->capacity, layout->tokens_per_expert,
                                            layout->expert_offsets, static_cast<const uint16_t *>(w_gate_up),
                                            static_cast<const uint16_t *>(w_down), static_cast<uint16_t *>(y),
-                                           workspace, as_stream(stream)));
+                                           static_cast<uint16_t *>(gate_up), workspace, as_stream(stream)));
 }
 
-moe_status moe_expert_ffn_bwd(const moe_shape *s, const void *x_perm, const void *grad_y, const moe_layout *layout,
-                              const void *w_gate_up, const void *w_down, void *grad_x_perm, void *grad_w_gate_up,
-                              void *grad_w_down, void *workspace, size_t workspace_bytes, void *stream) {
+moe_status moe_expert_ffn_bwd(const moe_shape *s, const void *x_perm, const void *grad_y, const void *gate_up,
+                              const moe_layout *layout, const void *w_gate_up, const void *w_down, void *grad_x_perm,
+                              void *grad_w_gate_up, void *grad_w_down, void *workspace, size_t workspace_bytes,
+                              void *stream) {
   int64_t rows;
   moe_status st = check_ffn_shape(s, &rows);
   if (st != MOE_OK) return st;
@@ -179,9 +184,10 @@ moe_status moe_expert_ffn_bwd(const moe_shape *s, const void *x_perm, const void
     return MOE_ERR_INVALID_ARG;
   if (rows > 0 && (!x_perm || !grad_y || !grad_x_perm)) return MOE_ERR_INVALID_ARG;
   if (!need(x_perm, rows, aligned16) || !need(grad_y, rows, aligned16) || !need(grad_x_perm, rows, aligned16) ||
-      !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(grad_w_gate_up) || !aligned16(grad_w_down))
+      !need(gate_up, rows, aligned16) || !aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(grad_w_gate_up) ||
+      !aligned16(grad_w_down))
     return MOE_ERR_MISALIGNED;
-  const void *ins[] = {x_perm, grad_y, w_gate_up, w_down};
+  const void *ins[] = {x_perm, grad_y, gate_up, w_gate_up, w_down};
   for (const void *in : ins)
     if (in && (in == grad_x_perm || in == grad_w_gate_up || in == grad_w_down)) return MOE_ERR_INVALID_ARG;
   if (grad_w_gate_up == grad_w_down || (grad_x_perm && (grad_x_perm == grad_w_gate_up || grad_x_perm == grad_w_down)))
@@ -193,7 +199,7 @@ moe_status moe_expert_ffn_bwd(const moe_shape *s, const void *x_perm, const void
       static_cast<const uint16_t *>(x_perm), static_cast<const uint16_t *>(grad_y), rows, s->hidden, s->inter,
       s->n_experts, s->capacity, layout->tokens_per_expert, layout->expert_offsets,
       static_cast<const uint16_t *>(w_gate_up), static_cast<const uint16_t *>(w_down),
-      static_cast<uint16_t *>(grad_x_perm), static_cast<uint16_t *>(grad_w_gate_up),
+      static_cast<const uint16_t *>(gate_up), static_cast<uint16_t *>(grad_x_perm), static_cast<uint16_t *>(grad_w_gate_up),
       static_cast<uint16_t *>(grad_w_down), workspace, as_stream(stream)));
 }
 

@@ -304,13 +304,16 @@ __device__ __forceinline__ void slice(const bf16x8 (&a)[4], const bf16x8 (&b)[4]
 // kAT / kBT: the operand is K-major (stored [K, M] / [K, N]; row length M / N)
 // instead of K-contiguous ([M, K] / [N, K], row length K).  Plain mode takes
 // only kBT (B = a weight [K, N] of each expert); weight-gradient mode takes both.
+// gate_up (SwiGLU mode, nullable): also store the pre-activations [rows, 2I],
+// gate columns then up columns, for the backward.
 constexpr int kModePlain = 0, kModeSwiGLU = 1, kModeWGrad = 2;
 
 template <int kMode, bool kAT, bool kBT>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int64_t b_expert_stride, int K, int M, int N,
     int m_tiles, int n_tiles, const int32_t *__restrict__ tokens_per_expert,
-    const int32_t *__restrict__ expert_offsets, int e, uint16_t *__restrict__ C, int64_t ldc) {
+    const int32_t *__restrict__ expert_offsets, int e, uint16_t *__restrict__ C, int64_t ldc,
+    uint16_t *__restrict__ gate_up) {
   constexpr bool kSwiGLU = kMode == kModeSwiGLU, kWGrad = kMode == kModeWGrad;
   static_assert(kWGrad ? (kAT && kBT) : !kAT, "operand layouts of the modes");
   static_assert(!(kSwiGLU && kBT), "the SwiGLU pairing reads K-contiguous weights");
@@ -327,7 +330,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   // bases at K = 0 and the output base
   int n0, rows_valid, KT, k_len;
   const char *a_base, *b_base;
-  uint16_t *c_base;
+  uint16_t *c_base, *gu_base = nullptr;
   if constexpr (kWGrad) {
     // each XCD (workgroup b runs on XCD b % 8) takes one eighth of every
     // expert's tiles, m fastest, expert after expert: the experts' different
@@ -359,6 +362,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     a_base = reinterpret_cast<const char *>(A + row0 * K);
     b_base = reinterpret_cast<const char *>(B + (int64_t)te * b_expert_stride + (kBT ? n0 : 0));
     c_base = C + row0 * ldc;
+    if (kSwiGLU && gate_up) gu_base = gate_up + row0 * 2 * N;
   }
   // bytes between the operand tiles of consecutive K steps
   const int64_t a_step = kAT ? (int64_t)kBK * M * 2 : kRowBytes;
@@ -553,55 +557,85 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   }
 
   // epilogue: every real LDS read is done (the last barrier has passed), so
-  // each wave stages its bf16 sub-tile in its own LDS buffer -- 128 rows x
-  // (64 SwiGLU features or 128 output columns), 16-byte chunks XOR-swizzled by
-  // row -- and writes it out as whole rows of 16-byte stores.
-  constexpr int kCols = kSwiGLU ? 64 : 128;     // output columns of this wave
-  constexpr int kPitch = kCols * 2;             // LDS bytes per staged row
-  constexpr int kChunksPerRow = kPitch / 16;
-  static_assert(128 * kPitch <= kOperandBytes, "staging fits one ring slot");
-  auto out_pos = [](int r, int c) {             // LDS chunk position of chunk c of staged row r
-    return kChunksPerRow == 16 ? (c ^ (r & 15)) : (c ^ ((r & 7) ^ ((r >> 3) & 1)));
-  };
+  // each wave stages its bf16 sub-tile in its own LDS buffer -- 128 rows x 128
+  // columns (the four accumulator blocks side by side) or, for the SwiGLU
+  // intermediate, 128 rows x 64 features; 16-byte chunks XOR-swizzled by row --
+  // and writes it out as whole rows of 16-byte stores.
   char *stage = ring + w * kOperandBytes;
+  auto pos16 = [](int r, int c) { return c ^ (r & 15); };               // rows of 16 chunks
+  auto pos8 = [](int r, int c) { return c ^ ((r & 7) ^ ((r >> 3) & 1)); };  // rows of 8 chunks
+  auto stage_acc = [&]() {
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-    const int r = mi * 32 + (l & 31);
+    for (int mi = 0; mi < 4; ++mi) {
+      const int r = mi * 32 + (l & 31);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      if (kSwiGLU) {
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          const f32x16 &c = acc[mi][ni];
+          const int f = ni * 32 + 8 * g + 4 * (l >> 5);
+          *reinterpret_cast<uint2 *>(stage + r * 256 + pos16(r, f >> 3) * 16 + (f & 7) * 2) =
+              make_uint2(pack_bf16x2(c[4 * g], c[4 * g + 1]), pack_bf16x2(c[4 * g + 2], c[4 * g + 3]));
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+    __builtin_amdgcn_wave_barrier();
+  };
+  // staged row r is row r%32 of the wave's block r/32
+  auto tile_row = [&](int r) { return (2 * (r >> 5) + wm) * 32 + (r & 31); };
+  if constexpr (kSwiGLU) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int r = mi * 32 + (l & 31);
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni) {
           float v[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) v[i] = silu_f(acc[mi][ni][4 * g + i]) * acc[mi][ni + 2][4 * g + i];
           const int f = ni * 32 + 8 * g + 4 * (l >> 5);
-          *reinterpret_cast<uint2 *>(stage + r * kPitch + out_pos(r, f >> 3) * 16 + (f & 7) * 2) =
+          *reinterpret_cast<uint2 *>(stage + r * 128 + pos8(r, f >> 3) * 16 + (f & 7) * 2) =
               make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
         }
-      } else {
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-          const f32x16 &c = acc[mi][ni];
-          const int f = ni * 32 + 8 * g + 4 * (l >> 5);
-          *reinterpret_cast<uint2 *>(stage + r * kPitch + out_pos(r, f >> 3) * 16 + (f & 7) * 2) =
-              make_uint2(pack_bf16x2(c[4 * g], c[4 * g + 1]), pack_bf16x2(c[4 * g + 2], c[4 * g + 3]));
-        }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_wave_barrier();
+    const int ch = l % 8;
+    const int col = n0 + wn * 64 + ch * 8;
+#pragma unroll 4
+    for (int r = l / 8; r < 128; r += 8) {
+      const int row = tile_row(r);
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * 128 + pos8(r, ch) * 16);
+      if (row < rows_valid && col < N) st16(c_base + (int64_t)row * ldc + col, v);
+    }
+    if (gu_base) {
+      // the pre-activations too: staged columns 0..63 are gate features
+      // n0 + wn*64 .., columns 64..127 the matching up features
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // the reads of the staged intermediate are done
+      __builtin_amdgcn_wave_barrier();
+      stage_acc();
+      const int ch16 = l % 16;
+      const int feat = n0 + wn * 64 + (ch16 & 7) * 8;
+      const int gcol = (ch16 >= 8 ? N : 0) + feat;
+#pragma unroll 4
+      for (int r = l / 16; r < 128; r += 4) {
+        const int row = tile_row(r);
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * 256 + pos16(r, ch16) * 16);
+        if (row < rows_valid && feat < N) st16(gu_base + (int64_t)row * 2 * N + gcol, v);
       }
     }
-  }
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
-  __builtin_amdgcn_wave_barrier();
-  constexpr int kRowsPerPass = kWave / kChunksPerRow;
-  const int col0 = n0 + wn * kCols;
-  const int ch = l % kChunksPerRow;
-  const int64_t c_ld = kWGrad ? (int64_t)N : ldc;
+  } else {
+    stage_acc();
+    const int ch = l % 16;
+    const int col = n0 + wn * 128 + ch * 8;
+    const int64_t c_ld = kWGrad ? (int64_t)N : ldc;
 #pragma unroll 4
-  for (int r = l / kChunksPerRow; r < 128; r += kRowsPerPass) {
-    const int row = (2 * (r >> 5) + wm) * 32 + (r & 31);  // staged row r is row r%32 of block r/32
-    const int col = col0 + ch * 8;
-    const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * kPitch + out_pos(r, ch) * 16);
-    if (row < rows_valid && col < N) st16(c_base + (int64_t)row * c_ld + col, v);
+    for (int r = l / 16; r < 128; r += 4) {
+      const int row = tile_row(r);
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * 256 + pos16(r, ch) * 16);
+      if (row < rows_valid && col < N) st16(c_base + (int64_t)row * c_ld + col, v);
+    }
   }
 }
 
@@ -617,25 +651,26 @@ int64_t tile_bound(int64_t rows, int e, int capacity, int n_tiles) {
 
 // ------------------------------------------------------------------ backward
 
-// SwiGLU backward, in place, 8 features per thread.  For row r and feature i,
-// with g = gu[r, i], u = gu[r, I+i], da = d_act[r, i], s = sigmoid(g):
-//   gu[r, i]     <- bf16(da * u * s * (1 + g * (1 - s)))   (silu'(g) = s (1 + g (1 - s)))
-//   gu[r, I + i] <- bf16(da * g * s)
-//   d_act[r, i]  <- bf16(g * s * u)                          (the activation itself)
-// fp32 arithmetic.  Every element is read and written by the same thread.
-__global__ __launch_bounds__(kThreads) void swiglu_bwd_kernel(uint16_t *__restrict__ gu, uint16_t *__restrict__ d_act,
+// SwiGLU backward, 8 features per thread.  For row r and feature i, with
+// g = gu[r, i], u = gu[r, I+i], da = d_act[r, i], s = sigmoid(g):
+//   dgu[r, i]     = bf16(da * u * s * (1 + g * (1 - s)))   (silu'(g) = s (1 + g (1 - s)))
+//   dgu[r, I + i] = bf16(da * g * s)
+//   d_act[r, i]  <- bf16(g * s * u)                         (the activation itself)
+// fp32 arithmetic.  Every element is read and written by the same thread, so
+// dgu may be gu (in place).
+__global__ __launch_bounds__(kThreads) void swiglu_bwd_kernel(const uint16_t *gu, uint16_t *dgu, uint16_t *d_act,
                                                               int64_t rows, int inter) {
   const int per_row = inter / 8;
   const int64_t n = rows * per_row;
   for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * kThreads) {
     const int64_t r = idx / per_row;
     const int c = (int)(idx % per_row) * 8;
-    uint16_t *pg = gu + r * 2 * inter + c;
-    uint16_t *pu = pg + inter;
+    const uint16_t *pg = gu + r * 2 * inter + c;
+    uint16_t *qg = dgu + r * 2 * inter + c;
     uint16_t *pa = d_act + r * inter + c;
     float g[8], u[8], da[8], dg[8], du[8], a[8];
     Vec16<true>::unpack(ld16(pg), g);
-    Vec16<true>::unpack(ld16(pu), u);
+    Vec16<true>::unpack(ld16(pg + inter), u);
     Vec16<true>::unpack(ld16(pa), da);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -645,8 +680,8 @@ __global__ __launch_bounds__(kThreads) void swiglu_bwd_kernel(uint16_t *__restri
       du[i] = da[i] * gs;
       a[i] = gs * u[i];
     }
-    st16(pg, Vec16<true>::pack(dg));
-    st16(pu, Vec16<true>::pack(du));
+    st16(qg, Vec16<true>::pack(dg));
+    st16(qg + inter, Vec16<true>::pack(du));
     st16(pa, Vec16<true>::pack(a));
   }
 }
@@ -660,7 +695,7 @@ hipError_t launch_plain(const uint16_t *A, const uint16_t *B, int64_t b_stride, 
   const int nt = (N + kBN - 1) / kBN;
   const int64_t g = tile_bound(rows, e, capacity, nt);
   hipLaunchKernelGGL((grouped_gemm_kernel<kModePlain, false, kBT>), dim3((unsigned)g), dim3(kThreads), 0, stream, A,
-                     B, b_stride, K, 0, N, 0, nt, tokens_per_expert, expert_offsets, e, C, (int64_t)N);
+                     B, b_stride, K, 0, N, 0, nt, tokens_per_expert, expert_offsets, e, C, (int64_t)N, nullptr);
   return hipGetLastError();
 }
 
@@ -672,7 +707,7 @@ hipError_t launch_wgrad(const uint16_t *A, const uint16_t *B, int M, int N, int 
   const int chunk = (mt * nt + kXcds - 1) / kXcds;
   hipLaunchKernelGGL((grouped_gemm_kernel<kModeWGrad, true, true>), dim3((unsigned)(kXcds * e * chunk)),
                      dim3(kThreads), 0, stream, A, B, (int64_t)0, 0, M, N, mt, nt, tokens_per_expert, expert_offsets,
-                     e, C, (int64_t)N);
+                     e, C, (int64_t)N, nullptr);
   return hipGetLastError();
 }
 
@@ -685,9 +720,10 @@ size_t ffn_bwd_workspace_bytes(int64_t rows, int inter) {
 hipError_t launch_expert_ffn_bwd(const uint16_t *x_perm, const uint16_t *grad_y, int64_t rows, int64_t hidden,
                                  int inter, int e, int capacity, const int32_t *tokens_per_expert,
                                  const int32_t *expert_offsets, const uint16_t *w_gate_up, const uint16_t *w_down,
-                                 uint16_t *grad_x_perm, uint16_t *grad_w_gate_up, uint16_t *grad_w_down,
-                                 void *workspace, hipStream_t stream) {
-  // workspace: [G | U] then [dG | dU] ([rows, 2I]); dA then the activation ([rows, I])
+                                 const uint16_t *gate_up, uint16_t *grad_x_perm, uint16_t *grad_w_gate_up,
+                                 uint16_t *grad_w_down, void *workspace, hipStream_t stream) {
+  // workspace: [dG | dU] ([rows, 2I], holding the recomputed [G | U] before
+  // when gate_up is null); dA then the activation ([rows, I])
   uint16_t *gu = static_cast<uint16_t *>(workspace);
   uint16_t *dact = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + align256(4 * (size_t)rows * inter));
   const int H = (int)hidden, I = inter;
@@ -695,16 +731,18 @@ hipError_t launch_expert_ffn_bwd(const uint16_t *x_perm, const uint16_t *grad_y,
 #define MOE_TRY(x)                    \
   if ((st = (x)) != hipSuccess) return st;
   if (rows > 0) {
-    // [G | U] = x W_gate_up^T (recomputed); dA = dy W_down (W_down [H, I]: K-major)
-    MOE_TRY(launch_plain<false>(x_perm, w_gate_up, (int64_t)2 * I * H, H, 2 * I, rows, e, capacity,
-                                tokens_per_expert, expert_offsets, gu, stream));
+    // [G | U] = x W_gate_up^T unless saved by the forward; dA = dy W_down (W_down [H, I]: K-major)
+    if (!gate_up)
+      MOE_TRY(launch_plain<false>(x_perm, w_gate_up, (int64_t)2 * I * H, H, 2 * I, rows, e, capacity,
+                                  tokens_per_expert, expert_offsets, gu, stream));
     MOE_TRY(launch_plain<true>(grad_y, w_down, (int64_t)I * H, H, I, rows, e, capacity, tokens_per_expert,
                                expert_offsets, dact, stream));
-    // [dG | dU] in place of [G | U]; the activation in place of dA
+    // [dG | dU] (in place of the recomputed [G | U]); the activation in place of dA
     const int64_t chunks = rows * (I / 8);
     int64_t blocks = (chunks + kThreads - 1) / kThreads;
     if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, gu, dact, rows, I);
+    hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
+                       gate_up ? gate_up : gu, gu, dact, rows, I);
     MOE_TRY(hipGetLastError());
     // dx = [dG | dU] W_gate_up (W_gate_up [2I, H]: K-major)
     MOE_TRY(launch_plain<true>(gu, w_gate_up, (int64_t)H * 2 * I, 2 * I, H, rows, e, capacity, tokens_per_expert,
@@ -721,22 +759,22 @@ size_t ffn_workspace_bytes(int64_t rows, int inter) { return align256(sizeof(uin
 
 hipError_t launch_expert_ffn(const uint16_t *x_perm, int64_t rows, int64_t hidden, int inter, int e, int capacity,
                              const int32_t *tokens_per_expert, const int32_t *expert_offsets,
-                             const uint16_t *w_gate_up, const uint16_t *w_down, uint16_t *y, void *workspace,
-                             hipStream_t stream) {
+                             const uint16_t *w_gate_up, const uint16_t *w_down, uint16_t *y, uint16_t *gate_up,
+                             void *workspace, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   uint16_t *act = static_cast<uint16_t *>(workspace);
   const int n1 = (inter + kBN / 2 - 1) / (kBN / 2);
   const int64_t g1 = tile_bound(rows, e, capacity, n1);
   hipLaunchKernelGGL((grouped_gemm_kernel<kModeSwiGLU, false, false>), dim3((unsigned)g1), dim3(kThreads), 0, stream,
                      x_perm, w_gate_up, (int64_t)2 * inter * hidden, (int)hidden, 0, inter, 0, n1, tokens_per_expert,
-                     expert_offsets, e, act, (int64_t)inter);
+                     expert_offsets, e, act, (int64_t)inter, gate_up);
   hipError_t st = hipGetLastError();
   if (st != hipSuccess) return st;
   const int n2 = (int)((hidden + kBN - 1) / kBN);
   const int64_t g2 = tile_bound(rows, e, capacity, n2);
   hipLaunchKernelGGL((grouped_gemm_kernel<kModePlain, false, false>), dim3((unsigned)g2), dim3(kThreads), 0, stream,
                      act, w_down, (int64_t)hidden * inter, inter, 0, (int)hidden, 0, n2, tokens_per_expert,
-                     expert_offsets, e, y, hidden);
+                     expert_offsets, e, y, hidden, nullptr);
   return hipGetLastError();
 }
 

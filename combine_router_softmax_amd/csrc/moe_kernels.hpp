@@ -35,13 +35,13 @@ hipError_t launch_combine_bwd(bool bf16, const void *grad_out, const void *y, co
 size_t ffn_workspace_bytes(int64_t rows, int inter);
 hipError_t launch_expert_ffn(const uint16_t *x_perm, int64_t rows, int64_t hidden, int inter, int e,
                              int capacity, const int32_t *tokens_per_expert, const int32_t *expert_offsets,
-                             const uint16_t *w_gate_up, const uint16_t *w_down, uint16_t *y, void *workspace,
-                             hipStream_t stream);
+                             const uint16_t *w_gate_up, const uint16_t *w_down, uint16_t *y, uint16_t *gate_up,
+                             void *workspace, hipStream_t stream);
 size_t ffn_bwd_workspace_bytes(int64_t rows, int inter);
 hipError_t launch_expert_ffn_bwd(const uint16_t *x_perm, const uint16_t *grad_y, int64_t rows, int64_t hidden,
                                  int inter, int e, int capacity, const int32_t *tokens_per_expert,
                                  const int32_t *expert_offsets, const uint16_t *w_gate_up, const uint16_t *w_down,
-                                 uint16_t *grad_x_perm, uint16_t *grad_w_gate_up, uint16_t *grad_w_down,
-                                 void *workspace, hipStream_t stream);
+                                 const uint16_t *gate_up, uint16_t *grad_x_perm, uint16_t *grad_w_gate_up,
+                                 uint16_t *grad_w_down, void *workspace, hipStream_t stream);
 
 }  // namespace moe

@@ -155,9 +155,12 @@ moe_status moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_i
  * not written.  Shapes: x_perm bf16 [R, H]; w_gate_up bf16 [E, 2I, H] (gate rows
  * first); w_down bf16 [E, H, I]; y bf16 [R, H].  H and I must be multiples of 64
  * and 4*I*H < 2^32 (one expert's weights are addressed with 32-bit offsets).
+ * gate_up (nullable) bf16 [R, 2I]: when given, the pre-activations are stored
+ * there for moe_expert_ffn_bwd, gate_up[r, i] = bf16(x_perm[r] . w_gate_up[e, i])
+ * for i < 2I (gate columns, then up columns), rows of the segments only.
  * Workspace: moe_workspace_size(MOE_OP_EXPERT_FFN) (holds a [R, I] bf16). */
 moe_status moe_expert_ffn(const moe_shape *s, const void *x_perm, const moe_layout *layout,
-                          const void *w_gate_up, const void *w_down, void *y, void *workspace,
+                          const void *w_gate_up, const void *w_down, void *y, void *gate_up, void *workspace,
                           size_t workspace_bytes, void *stream);
 
 /* Expert FFN backward: the vector-Jacobian product of moe_expert_ffn (the
@@ -169,18 +172,21 @@ moe_status moe_expert_ffn(const moe_shape *s, const void *x_perm, const moe_layo
  *   dA = dY w_down[e];  dG = dA U s (1 + G (1 - s));  dU = dA G s
  *   grad_x_perm = dG Wg + dU Wu
  *   grad_w_down[e] = dY^T A;  grad_w_gate_up[e] = [dG^T x_perm ; dU^T x_perm]
- * bf16 operands, fp32 accumulation; G, U, dA, dG, dU and A are recomputed and
- * held in bf16 between the GEMMs.  An expert with no rows gets zero weight
+ * bf16 operands, fp32 accumulation; G, U, dA, dG, dU and A are held in bf16
+ * between the GEMMs.  gate_up (nullable): the pre-activations [G | U] that
+ * moe_expert_ffn stored; when null they are recomputed (the same values, so
+ * both ways give the same bits).  An expert with no rows gets zero weight
  * gradients; rows outside the segments of grad_x_perm are not written.
- * Shapes as moe_expert_ffn: x_perm, grad_y, grad_x_perm bf16 [R, H];
+ * Shapes as moe_expert_ffn: x_perm, grad_y, grad_x_perm bf16 [R, H]; gate_up [R, 2I];
  * w_gate_up, grad_w_gate_up bf16 [E, 2I, H]; w_down, grad_w_down bf16 [E, H, I];
  * outputs must not alias inputs or each other.  Same shape limits as
  * moe_expert_ffn.  Deterministic: no atomics, fixed reduction order.
  * Workspace: moe_workspace_size(MOE_OP_EXPERT_FFN_BWD) (the [R, 3I] bf16
  * intermediates). */
-moe_status moe_expert_ffn_bwd(const moe_shape *s, const void *x_perm, const void *grad_y, const moe_layout *layout,
-                              const void *w_gate_up, const void *w_down, void *grad_x_perm, void *grad_w_gate_up,
-                              void *grad_w_down, void *workspace, size_t workspace_bytes, void *stream);
+moe_status moe_expert_ffn_bwd(const moe_shape *s, const void *x_perm, const void *grad_y, const void *gate_up,
+                              const moe_layout *layout, const void *w_gate_up, const void *w_down, void *grad_x_perm,
+                              void *grad_w_gate_up, void *grad_w_down, void *workspace, size_t workspace_bytes,
+                              void *stream);
 
 /* Combine: probability-weighted unpermute (DeepSpeed ep_tp_dispatch.py
  * restore_combined: weighted expert rows added into a zeroed [N, H] output by

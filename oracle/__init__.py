@@ -152,6 +152,23 @@ def expert_ffn_rows(rows, x_perm, lay, w_gate_up, w_down):
     return y, ex
 
 
+def expert_gate_up_rows(rows, x_perm, lay, w_gate_up):
+    """Pre-activations of the listed permuted rows (rows inside the segments):
+    [G | U][r, i] = bf16(x_perm[r] . w_gate_up[e, i]) for i < 2I, e the row's
+    expert -- the first GEMM of the SwiGLU FFN before the activation.  fp64 dot
+    products, one rounding.  -> bf16 bits [len(rows), 2I]."""
+    e, two_i, h = w_gate_up.shape
+    offs = [int(v) for v in lay["expert_offsets"][:e]]
+    cnts = [int(v) for v in lay["tokens_per_expert"][:e]]
+    out = np.zeros((len(rows), two_i))
+    for n, r in enumerate(rows):
+        ex = [x for x in range(e) if offs[x] <= int(r) < offs[x] + cnts[x]]
+        if len(ex) != 1:
+            raise ValueError(f"row {r} is not inside exactly one expert segment")
+        out[n] = _bf16_f64(w_gate_up[ex[0]]) @ _bf16_f64(x_perm[r])
+    return bf16_round_array(out)
+
+
 def expert_ffn(x_perm, lay, w_gate_up, w_down):
     """FFN over every kept row; rows outside the segments are returned as zeros."""
     rows = np.nonzero(lay["pad_mask"] == 0)[0]

@@ -96,21 +96,26 @@ def test_validation_errors_enqueue_nothing(moe):
     s = moe.make_shape(16, 64, 8, 2, capacity=4, max_rows=7)                   # max_rows != E*C
     assert lib.moe_dispatch(C.byref(s), p, p, p, C.byref(lay), p, p, p, 1 << 20, None) == -1
     s = moe.make_shape(16, 64, 8, 2, inter=64, act_dtype=moe.MOE_DT_F32)
-    assert lib.moe_expert_ffn(C.byref(s), p, C.byref(lay), p, p, p, p, 1 << 30, None) == -4  # fp32 FFN
+    assert lib.moe_expert_ffn(C.byref(s), p, C.byref(lay), p, p, p, None, p, 1 << 30, None) == -4  # fp32 FFN
     s = moe.make_shape(16, 64, 8, 2, inter=96)
-    assert lib.moe_expert_ffn(C.byref(s), p, C.byref(lay), p, p, p, p, 1 << 30, None) == -4  # I % 64
+    assert lib.moe_expert_ffn(C.byref(s), p, C.byref(lay), p, p, p, None, p, 1 << 30, None) == -4  # I % 64
     s = moe.make_shape(16, 64, 8, 2, inter=64)
-    assert lib.moe_expert_ffn(C.byref(s), p, C.byref(lay), p, p, p, p, 16, None) == -3
+    assert lib.moe_expert_ffn(C.byref(s), p, C.byref(lay), p, p, p, None, p, 16, None) == -3
+    assert lib.moe_expert_ffn(C.byref(s), p, C.byref(lay), p, p, C.c_void_p(8192), odd, p, 1 << 30,
+                              None) == -2                                 # misaligned gate_up
+    assert lib.moe_expert_ffn(C.byref(s), p, C.byref(lay), p, p, C.c_void_p(8192), C.c_void_p(8192), p,
+                              1 << 30, None) == -1                        # gate_up aliases y
     q, r = C.c_void_p(8192), C.c_void_p(12288)
     bwd = lib.moe_expert_ffn_bwd
-    assert bwd(C.byref(s), p, p, C.byref(lay), p, p, q, r, C.c_void_p(16384), p, 16, None) == -3  # small ws
-    assert bwd(C.byref(s), p, p, C.byref(lay), p, p, p, q, r, p, 1 << 30, None) == -1  # grad_x_perm aliases x_perm
-    assert bwd(C.byref(s), p, p, C.byref(lay), p, p, q, r, r, p, 1 << 30, None) == -1  # the weight grads alias
-    assert bwd(C.byref(s), p, p, C.byref(lay), p, p, q, odd, r, p, 1 << 30, None) == -2
-    assert bwd(C.byref(s), p, p, None, p, p, q, r, C.c_void_p(16384), p, 1 << 30, None) == -1
-    assert bwd(C.byref(s), p, p, C.byref(lay), p, p, q, None, r, p, 1 << 30, None) == -1  # null grad_w_gate_up
+    assert bwd(C.byref(s), p, p, None, C.byref(lay), p, p, q, r, C.c_void_p(16384), p, 16, None) == -3  # small ws
+    assert bwd(C.byref(s), p, p, None, C.byref(lay), p, p, p, q, r, p, 1 << 30, None) == -1  # grad_x_perm aliases x_perm
+    assert bwd(C.byref(s), p, p, None, C.byref(lay), p, p, q, r, r, p, 1 << 30, None) == -1  # the weight grads alias
+    assert bwd(C.byref(s), p, p, None, C.byref(lay), p, p, q, odd, r, p, 1 << 30, None) == -2
+    assert bwd(C.byref(s), p, p, None, None, p, p, q, r, C.c_void_p(16384), p, 1 << 30, None) == -1
+    assert bwd(C.byref(s), p, p, None, C.byref(lay), p, p, q, None, r, p, 1 << 30, None) == -1  # null grad_w_gate_up
+    assert bwd(C.byref(s), p, p, q, C.byref(lay), p, p, q, r, C.c_void_p(16384), p, 1 << 30, None) == -1  # gate_up
     s32 = moe.make_shape(16, 64, 8, 2, inter=64, act_dtype=moe.MOE_DT_F32)
-    assert bwd(C.byref(s32), p, p, C.byref(lay), p, p, q, r, C.c_void_p(16384), p, 1 << 30, None) == -4
+    assert bwd(C.byref(s32), p, p, None, C.byref(lay), p, p, q, r, C.c_void_p(16384), p, 1 << 30, None) == -4
     assert lib.moe_combine(C.byref(s), p, p, C.byref(lay), p, None) == -1     # out aliases y
     assert lib.moe_combine(C.byref(s), odd, p, C.byref(lay), p, None) == -2
     assert lib.moe_dispatch_bwd(C.byref(s), p, C.byref(lay), p, None) == -1         # grad_x aliases grad_x_perm

@@ -338,3 +338,32 @@ def test_expert_ffn_bwd_full_size_sampled(moe, wid):
     cnt = lay_h["tokens_per_expert"]
     for ex in np.nonzero(cnt == 0)[0]:
         assert not dwgu[int(ex)].view(torch.int16).any() and not dwd[int(ex)].view(torch.int16).any()
+
+
+@pytest.mark.parametrize("n,e,k,h,inter,cap", [
+    (300, 4, 2, 256, 192, 0),
+    (600, 8, 2, 256, 64, 1.0),
+])
+def test_expert_ffn_saved_gate_up(moe, n, e, k, h, inter, cap):
+    """The forward's stored pre-activations match the oracle, leave y unchanged,
+    and the backward that takes them gives the same bits as the one recomputing them."""
+    w, idx, wts, x, wgu, wd, xp, lay, y = ffn_case(moe, n, e, k, h, inter, cap, zero_expert=1)
+    y2, gu = moe.moe_expert_ffn(xp, lay, dev(wgu), dev(wd), save_gate_up=True)
+    torch.cuda.synchronize()
+    lay_h = layout_host(lay)
+    rows = np.nonzero(lay_h["pad_mask"] == 0)[0]
+    sel = torch.as_tensor(rows, device=y.device)
+    assert torch.equal(y[sel].view(torch.int16), y2[sel].view(torch.int16))   # rows outside the segments: unwritten
+    ref = oracle.expert_gate_up_rows(rows, host(xp), lay_h, wgu)
+    got = host(gu)[rows]
+    assert max_rel_err(got, ref) <= TOL_BF16
+    assert (got == ref).mean() > 0.9
+    dy = dev(mi.grad_expert_rows(w, lay.rows))
+    saved = gu.clone()
+    a = moe.moe_expert_ffn_bwd(xp, dy, lay, dev(wgu), dev(wd))
+    b = moe.moe_expert_ffn_bwd(xp, dy, lay, dev(wgu), dev(wd), gate_up=gu)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0][sel].view(torch.int16), b[0][sel].view(torch.int16))   # grad_x_perm, segment rows
+    for u, v in zip(a[1:], b[1:]):
+        assert torch.equal(u.view(torch.int16), v.view(torch.int16))
+    assert torch.equal(saved.view(torch.int16), gu.view(torch.int16))   # the saved buffer is only read

@@ -701,3 +701,20 @@ def test_ffn_bwd_entries_match_the_whole_backward():
         got, ref = got.reshape(-1).astype(np.int32), ref.reshape(-1).astype(np.int32)
         assert (np.abs(got - ref) <= 1).all()      # fp64 sums in another order: at most one bf16 step apart
         assert (got == ref).mean() > 0.98
+
+
+def test_gate_up_rows_brute_force():
+    """Pre-activations by plain Python loops over a tiny case."""
+    g = np.random.default_rng(12)
+    e, h, inter = 3, 8, 4
+    idx = np.array([[0, 2], [1, 2], [2, 0], [0, 1]], np.int32)
+    lay = oracle.layout(idx, e)
+    x = mi.f32_to_bf16_bits(g.standard_normal((lay["rows"], h)).astype(np.float32))
+    wgu = mi.f32_to_bf16_bits((g.standard_normal((e, 2 * inter, h)) * 0.3).astype(np.float32))
+    rows = list(range(lay["rows"]))
+    got = oracle.expert_gate_up_rows(rows, x, lay, wgu)
+    xv, wv = bf16_vals(x), bf16_vals(wgu)
+    for n, r in enumerate(rows):
+        ex = next(q for q in range(e) if lay["expert_offsets"][q] <= r < lay["expert_offsets"][q] + lay["tokens_per_expert"][q])
+        ref = [sum(float(xv[r, c]) * float(wv[ex, i, c]) for c in range(h)) for i in range(2 * inter)]
+        assert (got[n] == bf16_from_double_ref(np.array(ref))).all()
