@@ -283,6 +283,18 @@ def gemm_pass():
     torch.cuda.synchronize()
 
 
+def bwd_pass():
+    """Short run for rocprofv3 counter passes over the expert FFN backward: the
+    qwen3-layer FFN, forward and training forward twice each, then the backward
+    with saved pre-activations three times and with recomputation three times."""
+    import torch
+    import moe_inputs as mi
+    import combine_router_softmax_amd as moe
+    torch.cuda.set_device(0)
+    bench_expert_gemm(moe, mi, torch, 4, 1, 1, 2)
+    torch.cuda.synchronize()
+
+
 def cpu_baseline(mi):
     import numpy as np
     import oracle
@@ -318,9 +330,14 @@ def main():
                     help="short run for rocprofv3 --pmc passes (prints no JSON line)")
     ap.add_argument("--gemm-pass", action="store_true",
                     help="short expert-GEMM run for hardware-counter passes (prints nothing)")
+    ap.add_argument("--bwd-pass", action="store_true",
+                    help="short expert-FFN backward run for hardware-counter passes (prints nothing)")
     args = ap.parse_args()
     if args.gemm_pass:
         gemm_pass()
+        return
+    if args.bwd_pass:
+        bwd_pass()
         return
     if args.counter_pass:
         counter_pass()
