@@ -104,9 +104,10 @@ static int selected_before(float va, int a, float vb, int b) {
  * probabilities p = softmax over all E logits (double); the k chosen are
  * renormalised, w_j = p_j / sum_j' p_j', and rounded once to fp32; the routing
  * map is the multihot [N, E] row ([MORI] multihot conversion); tokens_per_expert
- * is the column sum of the map. */
-int oracle_route(int64_t n, int e, int k, const float *logits, int32_t *topk_idx, float *topk_w,
-                 uint8_t *routing_map, int32_t *tokens_per_expert) {
+ * is the column sum of the map.  token_mask (nullable): nonzero marks a
+ * padding token, routed nowhere. */
+int oracle_route(int64_t n, int e, int k, const float *logits, const uint8_t *token_mask, int32_t *topk_idx,
+                 float *topk_w, uint8_t *routing_map, int32_t *tokens_per_expert) {
   if (n < 0 || e < 1 || k < 1 || k > e) return -1;
   char *taken = (char *)malloc((size_t)e);
   double *p = (double *)malloc(sizeof(double) * (size_t)e);
@@ -115,6 +116,14 @@ int oracle_route(int64_t n, int e, int k, const float *logits, int32_t *topk_idx
   for (int64_t t = 0; t < n; ++t) {
     const float *l = logits + t * e;
     memset(taken, 0, (size_t)e);
+    if (token_mask && token_mask[t]) {
+      /* a padding token takes part in no routing [MORI router: padding tokens
+       * masked out of routing and dispatch]: every slot is the -1 sentinel with
+       * weight 0, its map row is empty and it is not counted */
+      for (int j = 0; j < k; ++j) { topk_idx[t * k + j] = -1; topk_w[t * k + j] = 0.0f; }
+      if (routing_map) memset(routing_map + t * e, 0, (size_t)e);
+      continue;
+    }
     for (int j = 0; j < k; ++j) {
       int best = -1;
       for (int x = 0; x < e; ++x) {

@@ -235,6 +235,41 @@ def test_route_closed_forms():
     assert np.allclose(w[:, 0], 1.0) and (w[:, 1:] < 1e-25).all()
 
 
+@pytest.mark.parametrize("trial", range(20))
+def test_route_token_mask_brute_force(trial):
+    """Padding tokens route nowhere; the other tokens route exactly as the brute
+    force does, and the counts are the column sums over the unmasked tokens only."""
+    g = np.random.default_rng(2000 + trial)
+    e = int(g.integers(1, 17))
+    k = int(g.integers(1, e + 1))
+    n = int(g.integers(1, 40))
+    logits = g.standard_normal((n, e)).astype(np.float32)
+    mask = (g.random(n) < 0.3).astype(np.uint8)
+    mask[0] = 1 if trial % 3 == 0 else mask[0]
+    if trial == 1:
+        mask[:] = 1                                   # every token is padding
+    idx, w, rmap, tpe = oracle.route(logits, k, mask)
+    counts = np.zeros(e, np.int64)
+    for t in range(n):
+        if mask[t]:
+            assert (idx[t] == -1).all() and (w[t] == 0).all() and (rmap[t] == 0).all()
+            continue
+        sel = bf_topk(logits[t], k)
+        assert list(idx[t]) == sel
+        ref = bf_weights(logits[t], sel)
+        assert np.all(np.abs(w[t].astype(np.float64) - ref) <= f32_ulp(np.float32(ref)) * 1.0001)
+        counts[sel] += 1
+        mrow = np.zeros(e, np.uint8)
+        mrow[sel] = 1
+        np.testing.assert_array_equal(rmap[t], mrow)
+    np.testing.assert_array_equal(tpe, counts)
+    # the masked routing dispatches no padding token: its rows stay out of the layout
+    lay = oracle.layout(idx, e)
+    assert lay["counters"][0] == (1 - mask).sum() * k and lay["counters"][3] == 0
+    placed = lay["assign_row"].reshape(n, k)
+    assert (placed[mask == 1] == -1).all() and (placed[mask == 0] >= 0).all()
+
+
 def test_route_invariants_uniform_workload():
     w = mi.workload(2)
     logits = mi.router_logits(w)
