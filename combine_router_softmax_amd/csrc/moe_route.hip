@@ -10,6 +10,9 @@
 // wave max-reduction select the top-k in order; the chosen key is zeroed.
 // Weights use the identity softmax(l)[i] / sum_chosen softmax(l) =
 // exp(l_i - l_max) / sum_chosen exp(l_j - l_max), with l_max the slot-0 logit.
+// A token marked in the optional padding mask routes nowhere (the router of
+// "Add MORI as a Token Dispatcher" masks padding tokens out of routing and
+// dispatch).
 // Counts: when the routing map is written (E % 16 == 0), a second kernel takes
 // its column sums in a few dozen workgroups, one global atomic per expert and
 // workgroup; otherwise each router workgroup adds its LDS histogram with global
@@ -77,7 +80,8 @@ __global__ __launch_bounds__(kRouteThreads) void count_map_kernel(const uint8_t 
 }
 
 template <int VPL>
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(const float *__restrict__ logits, int64_t n, int e,
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const float *__restrict__ logits,
+                                                              const uint8_t *__restrict__ token_mask, int64_t n, int e,
                                                               int k, int32_t *__restrict__ topk_idx,
                                                               float *__restrict__ topk_w,
                                                               uint8_t *__restrict__ routing_map,
@@ -98,7 +102,17 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float *__res
   __syncthreads();
 
   const int64_t t = (int64_t)blockIdx.x * kRouteTokensPerBlock + w;
-  if (t < n) {
+  // a padding token (nonzero mask byte) takes part in no routing: -1 slots,
+  // weight 0, an empty map row, no count
+  const bool pad = t < n && token_mask && token_mask[t];
+  if (pad) {
+    for (int j = l; j < k; j += kWave) {
+      topk_idx[t * k + j] = -1;
+      topk_w[t * k + j] = 0.0f;
+    }
+    if (routing_map)
+      for (int x = l; x < e; x += kWave) routing_map[t * e + x] = 0;
+  } else if (t < n) {
     const float *row = logits + t * e;
     uint64_t key[VPL];
 #pragma unroll
@@ -155,20 +169,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float *__res
 }
 
 template <int VPL>
-hipError_t launch_route_vpl(const float *logits, int64_t n, int e, int k, int32_t *topk_idx, float *topk_w,
-                            uint8_t *routing_map, int32_t *tokens_per_expert, int32_t *zero_counts,
-                            hipStream_t stream) {
+hipError_t launch_route_vpl(const float *logits, const uint8_t *token_mask, int64_t n, int e, int k,
+                            int32_t *topk_idx, float *topk_w, uint8_t *routing_map, int32_t *tokens_per_expert,
+                            int32_t *zero_counts, hipStream_t stream) {
   const int64_t blocks = (n + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock;
   const size_t lds = sizeof(uint32_t) * (2 * kRouteTokensPerBlock * (size_t)k + (size_t)e);
-  hipLaunchKernelGGL(route_kernel<VPL>, dim3((unsigned)blocks), dim3(kRouteThreads), lds, stream, logits, n, e, k,
-                     topk_idx, topk_w, routing_map, tokens_per_expert, zero_counts);
+  hipLaunchKernelGGL(route_kernel<VPL>, dim3((unsigned)blocks), dim3(kRouteThreads), lds, stream, logits, token_mask,
+                     n, e, k, topk_idx, topk_w, routing_map, tokens_per_expert, zero_counts);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_route(const float *logits, int64_t n, int e, int k, int32_t *topk_idx, float *topk_w,
-                        uint8_t *routing_map, int32_t *tokens_per_expert, hipStream_t stream) {
+hipError_t launch_route(const float *logits, const uint8_t *token_mask, int64_t n, int e, int k, int32_t *topk_idx,
+                        float *topk_w, uint8_t *routing_map, int32_t *tokens_per_expert, hipStream_t stream) {
   const bool map_counts = n > 0 && tokens_per_expert && routing_map && e % 16 == 0 &&
                           (reinterpret_cast<uintptr_t>(routing_map) & 15u) == 0;
   if (tokens_per_expert && !map_counts) {  // the router kernel adds into zeroed counts
@@ -182,7 +196,7 @@ hipError_t launch_route(const float *logits, int64_t n, int e, int k, int32_t *t
   int32_t *zero_counts = map_counts ? tokens_per_expert : nullptr;
   hipError_t st;
 #define MOE_ROUTE(V) \
-  launch_route_vpl<V>(logits, n, e, k, topk_idx, topk_w, routing_map, kernel_counts, zero_counts, stream)
+  launch_route_vpl<V>(logits, token_mask, n, e, k, topk_idx, topk_w, routing_map, kernel_counts, zero_counts, stream)
   if (e <= 64) st = MOE_ROUTE(1);
   else if (e <= 128) st = MOE_ROUTE(2);
   else if (e <= 256) st = MOE_ROUTE(4);

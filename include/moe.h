@@ -117,11 +117,16 @@ moe_status moe_workspace_size(moe_op op, const moe_shape *s, size_t *bytes);
  *     (fp32; equal to the softmax over the k chosen logits);
  *   routing_map[t, e] = 1 if e was chosen else 0 (nullable, uint8 [N, E]);
  *   tokens_per_expert[e] = number of tokens choosing e (nullable, int32 [E]).
+ * token_mask (nullable, uint8 [N]): a nonzero byte marks a padding token, which
+ *   takes part in no routing (the pull request's router masks padding tokens out
+ *   of routing and dispatch): its slots are -1 with weight 0, its map row is
+ *   empty and it is not counted; moe_dispatch then skips it and moe_combine
+ *   gives it a zero row.
  * Inputs: logits fp32 [N, E].  Outputs: topk_idx int32 [N, k], topk_w fp32 [N, k].
  * Infinite logits are unsupported (their weights are NaN).  k <= E <= 1024.
  * No workspace. */
-moe_status moe_route(const moe_shape *s, const float *logits, int32_t *topk_idx, float *topk_w,
-                     uint8_t *routing_map, int32_t *tokens_per_expert, void *stream);
+moe_status moe_route(const moe_shape *s, const float *logits, const uint8_t *token_mask, int32_t *topk_idx,
+                     float *topk_w, uint8_t *routing_map, int32_t *tokens_per_expert, void *stream);
 
 /* Dispatch: local permutation of token rows into expert-contiguous rows
  * ("Megatron MoE 实现", dispatch_preprocess / dispatch_postprocess ->

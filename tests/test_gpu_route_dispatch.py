@@ -10,7 +10,7 @@ import torch
 
 import moe_inputs as mi
 import oracle
-from parity_util import TOL_F32, assert_layout_equal, dev, host, layout_host, max_rel_err, workload_inputs
+from parity_util import TOL_BF16, TOL_F32, assert_layout_equal, dev, host, layout_host, max_rel_err, workload_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -50,6 +50,48 @@ def test_route_shapes_ties_signed_zero_nan(moe, e, k):
     vals = np.array([-1.0, -0.0, 0.0, 1.0, np.nan], np.float32)
     ties = g.choice(vals, size=(n, e), p=[0.25, 0.2, 0.2, 0.25, 0.1]).astype(np.float32)
     check_route(moe, ties, k)
+
+
+@pytest.mark.parametrize("e,k,with_map", [(8, 2, True), (100, 7, True), (256, 8, True), (256, 8, False), (1024, 16, True)])
+def test_route_token_mask(moe, e, k, with_map):
+    """Padding tokens route nowhere; both counting paths (map column sums, and the
+    router's own histogram when there is no map or E % 16 != 0)."""
+    g = np.random.default_rng(e + k)
+    n = 777
+    logits = g.standard_normal((n, e)).astype(np.float32)
+    mask = (g.random(n) < 0.25).astype(np.uint8)
+    r = moe.moe_route(dev(logits), k, token_mask=dev(mask), routing_map=with_map)
+    torch.cuda.synchronize()
+    idx, w, rmap, tpe = oracle.route(logits, k, mask)
+    np.testing.assert_array_equal(host(r.topk_idx), idx)
+    if with_map:
+        np.testing.assert_array_equal(host(r.routing_map), rmap)
+    np.testing.assert_array_equal(host(r.tokens_per_expert), tpe)
+    got_w = host(r.topk_w)
+    assert (got_w[mask == 1] == 0).all()
+    assert max_rel_err(got_w, w) <= TOL_F32
+
+
+def test_route_token_mask_through_the_layer(moe):
+    """masked route -> dispatch -> combine: padding tokens are not dispatched and get zero rows."""
+    w = mi.workload(2, n_tokens=512)
+    logits = mi.router_logits(w)
+    x = mi.activations(w)
+    mask = np.zeros(w.n_tokens, np.uint8)
+    mask[::3] = 1
+    r = moe.moe_route(dev(logits), w.top_k, token_mask=dev(mask))
+    xp, wp, lay = moe.moe_dispatch(dev(x), r.topk_idx, r.topk_w, w.n_experts)
+    out = moe.moe_combine(xp, r.topk_w, lay)
+    torch.cuda.synchronize()
+    idx, wts, _, _ = oracle.route(logits, w.top_k, mask)
+    ref_lay = oracle.layout(idx, w.n_experts)
+    assert_layout_equal(layout_host(lay), ref_lay)
+    assert int(host(lay.counters)[0]) == (1 - mask).sum() * w.top_k
+    out_h = host(out)
+    assert (out_h[mask == 1] == 0).all()
+    xp_ref, _ = oracle.scatter(x, w.top_k, ref_lay, wts)
+    ref = oracle.combine(xp_ref, wts, ref_lay, w.n_tokens, w.top_k)
+    assert max_rel_err(out_h, ref) <= TOL_BF16
 
 
 def test_route_empty(moe):
