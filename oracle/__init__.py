@@ -48,17 +48,17 @@ def lib():
         p, i64, i32 = C.c_void_p, C.c_int64, C.c_int
         L.oracle_route.argtypes = [i64, i32, i32, p, p, p, p, p, p]
         L.oracle_route.restype = i32
-        L.oracle_layout_rows.argtypes = [i64, i32, i32, i32, i64]
+        L.oracle_layout_rows.argtypes = [i64, i32, i32, i32, i64, i32]
         L.oracle_layout_rows.restype = i64
-        L.oracle_layout.argtypes = [i64, i32, i32, i32, i64, p, p, p, p, p, p, p, p, p]
+        L.oracle_layout.argtypes = [i64, i32, i32, i32, i64, i32, p, p, p, p, p, p, p, p, p]
         L.oracle_layout.restype = i32
-        L.oracle_scatter.argtypes = [i64, i32, i64, p, p, p, i64, p, i32, p, p]
+        L.oracle_scatter.argtypes = [i64, i32, i64, p, p, p, i64, p, i64, p, p]
         L.oracle_scatter.restype = None
         L.oracle_expert_ffn_rows.argtypes = [i64, p, i32, i64, i64, p, p, p, p, p, p, p]
         L.oracle_expert_ffn_rows.restype = None
         L.oracle_combine.argtypes = [i64, i32, i64, i32, p, p, p, p]
         L.oracle_combine.restype = None
-        L.oracle_combine_bwd.argtypes = [i64, i32, i64, i32, p, p, p, p, i64, p, i32, p, p]
+        L.oracle_combine_bwd.argtypes = [i64, i32, i64, i32, p, p, p, p, i64, p, i64, p, p]
         L.oracle_dispatch_bwd.argtypes = [i64, i32, i64, i32, p, p, p]
         L.oracle_dispatch_bwd.restype = None
         L.oracle_combine_bwd.restype = None
@@ -102,11 +102,11 @@ def route(logits: np.ndarray, k: int, token_mask=None):
     return idx, w, rmap, tpe
 
 
-def layout(topk_idx: np.ndarray, n_experts: int, capacity: int = 0, max_rows: int = 0) -> dict:
+def layout(topk_idx: np.ndarray, n_experts: int, capacity: int = 0, max_rows: int = 0, row_align: int = 0) -> dict:
     """Dispatch layout; returns a dict of numpy arrays (see moe_oracle.c oracle_layout)."""
     topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
     n, k = topk_idx.shape
-    rows = lib().oracle_layout_rows(n, k, n_experts, capacity, max_rows)
+    rows = lib().oracle_layout_rows(n, k, n_experts, capacity, max_rows, row_align)
     out = dict(
         tokens_per_expert=np.empty(n_experts, np.int32),
         expert_offsets=np.empty(n_experts + 1, np.int32),
@@ -117,7 +117,7 @@ def layout(topk_idx: np.ndarray, n_experts: int, capacity: int = 0, max_rows: in
         pad_mask=np.empty(rows, np.uint8),
         counters=np.empty(4, np.int32),
     )
-    rc = lib().oracle_layout(n, k, n_experts, capacity, max_rows, _p(topk_idx),
+    rc = lib().oracle_layout(n, k, n_experts, capacity, max_rows, row_align, _p(topk_idx),
                              *[_p(out[f]) for f in ("tokens_per_expert", "expert_offsets", "ordinal",
                                                     "assign_row", "row_src", "drop_mask", "pad_mask", "counters")])
     if rc != 0:
@@ -126,9 +126,10 @@ def layout(topk_idx: np.ndarray, n_experts: int, capacity: int = 0, max_rows: in
     return out
 
 
-def scatter(x: np.ndarray, k: int, lay: dict, topk_w: np.ndarray, capacity: int = 0, x_perm=None):
-    """Permuted rows and weights: -> (x_perm [rows, H], w_perm [rows]).  Rows of an
-    unused dropless tail keep what `x_perm` held (zeros if not given)."""
+def scatter(x: np.ndarray, k: int, lay: dict, topk_w: np.ndarray, x_perm=None):
+    """Permuted rows and weights: -> (x_perm [rows, H], w_perm [rows]).  Pad rows (below
+    the end of the last segment, holding nothing) are zero; rows of an unused dropless
+    tail keep what `x_perm` held (zeros if not given)."""
     x = np.ascontiguousarray(x)
     n, h = x.shape
     rows = lay["rows"]
@@ -137,7 +138,7 @@ def scatter(x: np.ndarray, k: int, lay: dict, topk_w: np.ndarray, capacity: int 
     w_perm = np.empty(rows, np.float32)
     topk_w = np.ascontiguousarray(topk_w, dtype=np.float32)
     lib().oracle_scatter(n, k, h * x.itemsize, _p(x), _p(lay["assign_row"]), _p(topk_w), rows,
-                         _p(lay["row_src"]), capacity, _p(x_perm), _p(w_perm))
+                         _p(lay["row_src"]), int(lay["expert_offsets"][-1]), _p(x_perm), _p(w_perm))
     return x_perm, w_perm
 
 
@@ -201,8 +202,7 @@ def dispatch_bwd(grad_x_perm: np.ndarray, lay: dict, n: int, k: int):
     return out
 
 
-def combine_bwd(grad_out: np.ndarray, y: np.ndarray, topk_w: np.ndarray, lay: dict, k: int,
-                capacity: int = 0, grad_y=None):
+def combine_bwd(grad_out: np.ndarray, y: np.ndarray, topk_w: np.ndarray, lay: dict, k: int, grad_y=None):
     """-> (grad_y [rows, H], grad_w fp32 [N, k]).  Unused dropless tail rows keep what
     `grad_y` held (zeros if not given)."""
     grad_out = np.ascontiguousarray(grad_out)
@@ -215,7 +215,7 @@ def combine_bwd(grad_out: np.ndarray, y: np.ndarray, topk_w: np.ndarray, lay: di
     grad_w = np.empty((n, k), np.float32)
     lib().oracle_combine_bwd(n, k, h, _dt(y), _p(grad_out), _p(y),
                              _p(np.ascontiguousarray(topk_w, dtype=np.float32)), _p(lay["assign_row"]),
-                             rows, _p(lay["row_src"]), capacity, _p(grad_y), _p(grad_w))
+                             rows, _p(lay["row_src"]), int(lay["expert_offsets"][-1]), _p(grad_y), _p(grad_w))
     return grad_y, grad_w
 
 

@@ -153,9 +153,11 @@ int oracle_route(int64_t n, int e, int k, const float *logits, const uint8_t *to
 
 /* Rows of the permuted buffer: E*C with a capacity, else max_rows if given,
  * else one row per assignment. */
-int64_t oracle_layout_rows(int64_t n, int k, int e, int capacity, int64_t max_rows) {
+int64_t oracle_layout_rows(int64_t n, int k, int e, int capacity, int64_t max_rows, int row_align) {
   if (capacity > 0) return (int64_t)e * capacity;
-  return max_rows > 0 ? max_rows : n * k;
+  if (max_rows > 0) return max_rows;
+  /* every segment rounded up to row_align rows adds at most row_align - 1 pad rows */
+  return n * k + (row_align > 1 ? (int64_t)e * (row_align - 1) : 0);
 }
 
 /* Dispatch layout [MEG dispatch_preprocess / dispatch_postprocess; DS
@@ -167,19 +169,23 @@ int64_t oracle_layout_rows(int64_t n, int k, int e, int capacity, int64_t max_ro
  *    of the stably expert-sorted list).
  *  - capacity C > 0: segment of expert e starts at e*C, the first C assignments
  *    (by ordinal) are kept, the rest dropped; slots kept_e..C-1 are pad rows.
- *    C <= 0: segments are the exclusive scan of the counts, clipped to the row
- *    budget; assignments past the budget are dropped.
+ *    C <= 0: segments are the exclusive scan of the counts, each rounded up to
+ *    a multiple of row_align rows when row_align > 1 ([MORI] padding routing
+ *    maps / FP8 padding: every expert's segment starts on an aligned row),
+ *    clipped to the row budget; assignments past the budget are dropped; the
+ *    rows between an expert's kept rows and the next segment are pad rows.
  *  - assign_row[a] = offset[e] + ordinal[a] when kept, else -1.
  *  - row_src[r] = the assignment placed in row r, else -1; pad_mask[r] = 1 for
  *    every row that holds no assignment (capacity pad or unused tail).
- *  - counters = {kept, dropped, capacity pad rows, invalid ids}. */
-int oracle_layout(int64_t n, int k, int e, int capacity, int64_t max_rows, const int32_t *topk_idx,
+ *  - counters = {kept, dropped, pad rows (capacity or alignment), invalid ids}. */
+int oracle_layout(int64_t n, int k, int e, int capacity, int64_t max_rows, int row_align, const int32_t *topk_idx,
                   int32_t *tokens_per_expert, int32_t *expert_offsets, int32_t *ordinal,
                   int32_t *assign_row, int32_t *row_src, uint8_t *drop_mask, uint8_t *pad_mask,
                   int32_t *counters) {
   if (n < 0 || k < 1 || e < 1) return -1;
   int64_t a_total = n * k;
-  int64_t rows = oracle_layout_rows(n, k, e, capacity, max_rows);
+  int64_t rows = oracle_layout_rows(n, k, e, capacity, max_rows, row_align);
+  const int64_t align = row_align > 1 ? row_align : 1;
   int64_t *count = (int64_t *)calloc((size_t)e, sizeof(int64_t));
   int64_t *seen = (int64_t *)calloc((size_t)e, sizeof(int64_t));
   int64_t *kept = (int64_t *)calloc((size_t)e, sizeof(int64_t));
@@ -201,10 +207,13 @@ int oracle_layout(int64_t n, int k, int e, int capacity, int64_t max_rows, const
     int64_t off = 0;
     for (int x = 0; x < e; ++x) {
       expert_offsets[x] = (int32_t)(off < rows ? off : rows);
-      off += count[x];
+      off += (count[x] + align - 1) / align * align;
     }
     expert_offsets[e] = (int32_t)(off < rows ? off : rows);
-    for (int x = 0; x < e; ++x) kept[x] = expert_offsets[x + 1] - expert_offsets[x];
+    for (int x = 0; x < e; ++x) {
+      const int64_t room = rows - expert_offsets[x];
+      kept[x] = count[x] < room ? count[x] : room;
+    }
   }
   for (int64_t r = 0; r < rows; ++r) { row_src[r] = -1; pad_mask[r] = 1; }
   int64_t dropped = 0, kept_total = 0;
@@ -229,7 +238,7 @@ int oracle_layout(int64_t n, int k, int e, int capacity, int64_t max_rows, const
   for (int x = 0; x < e; ++x) tokens_per_expert[x] = (int32_t)kept[x];
   counters[0] = (int32_t)kept_total;
   counters[1] = (int32_t)dropped;
-  counters[2] = capacity > 0 ? (int32_t)(rows - kept_total) : 0;
+  counters[2] = (int32_t)(expert_offsets[e] - kept_total);  /* rows below the used end holding nothing */
   counters[3] = (int32_t)invalid;
   free(count);
   free(seen);
@@ -241,12 +250,13 @@ int oracle_layout(int64_t n, int k, int e, int capacity, int64_t max_rows, const
 
 /* Row scatter [MEG dispatch_preprocess permutes hidden states and probs; HT
  * Validation: the dispatched copy is exact].  Each kept assignment's token row
- * is copied bit for bit into its row; its weight goes to w_perm.  With a
- * capacity, pad rows are all-zero bits with weight 0 ([MORI] masked tails are
- * filled with 0).  Rows of an unused dropless tail get weight 0 and keep their
- * data. */
+ * is copied bit for bit into its row; its weight goes to w_perm.  Pad rows --
+ * rows below pad_limit (expert_offsets[E]: the end of the last segment) that
+ * hold no assignment, i.e. capacity or alignment pads -- are all-zero bits
+ * with weight 0 ([MORI] masked tails are filled with 0).  Rows of an unused
+ * dropless tail get weight 0 and keep their data. */
 void oracle_scatter(int64_t n, int k, int64_t row_bytes, const uint8_t *x, const int32_t *assign_row,
-                    const float *topk_w, int64_t rows, const int32_t *row_src, int capacity,
+                    const float *topk_w, int64_t rows, const int32_t *row_src, int64_t pad_limit,
                     uint8_t *x_perm, float *w_perm) {
   for (int64_t a = 0; a < n * k; ++a) {
     int32_t r = assign_row[a];
@@ -256,7 +266,7 @@ void oracle_scatter(int64_t n, int k, int64_t row_bytes, const uint8_t *x, const
   }
   for (int64_t r = 0; r < rows; ++r) {
     if (row_src[r] >= 0) continue;
-    if (capacity > 0) memset(x_perm + r * row_bytes, 0, (size_t)row_bytes);
+    if (r < pad_limit) memset(x_perm + r * row_bytes, 0, (size_t)row_bytes);
     if (w_perm) w_perm[r] = 0.0f;
   }
 }
@@ -355,11 +365,12 @@ void oracle_dispatch_bwd(int64_t n, int k, int64_t h, int dt, const void *grad_x
  * For each kept assignment a = (t, j) in row r:
  *   grad_y[r, :] = w[t,j] * g[t, :]        (one rounding to the activation type)
  *   grad_w[t, j] = sum_h g[t,h] * y[r,h]   (double, one rounding to fp32)
- * grad_w is 0 for dropped, sentinel and invalid slots; capacity pad rows of
- * grad_y are 0; rows of an unused dropless tail are not written. */
+ * grad_w is 0 for dropped, sentinel and invalid slots; pad rows of grad_y
+ * (rows below pad_limit holding no assignment) are 0; rows of an unused
+ * dropless tail are not written. */
 void oracle_combine_bwd(int64_t n, int k, int64_t h, int dt, const void *grad_out, const void *y,
                         const float *topk_w, const int32_t *assign_row, int64_t rows,
-                        const int32_t *row_src, int capacity, void *grad_y, float *grad_w) {
+                        const int32_t *row_src, int64_t pad_limit, void *grad_y, float *grad_w) {
   for (int64_t t = 0; t < n; ++t) {
     for (int j = 0; j < k; ++j) {
       int64_t a = t * k + j;
@@ -374,8 +385,7 @@ void oracle_combine_bwd(int64_t n, int k, int64_t h, int dt, const void *grad_ou
       grad_w[a] = (float)dot;
     }
   }
-  if (capacity > 0)
-    for (int64_t r = 0; r < rows; ++r)
+  for (int64_t r = 0; r < rows && r < pad_limit; ++r)
       if (row_src[r] < 0)
         for (int64_t c = 0; c < h; ++c) act_store(grad_y, dt, r * h + c, 0.0);
 }

@@ -80,7 +80,7 @@ def check_combine_bwd(moe, idx, wts, e, capacity, go, y, max_rows=0):
     _, _, lay = moe.moe_dispatch(dev(x_dummy), dev(idx), dev(wts), e, capacity=capacity, max_rows=max_rows)
     gy, gw = moe.moe_combine_bwd(dev(go), dev(y), dev(wts), lay)
     gy_h, gw_h = host(gy), host(gw)
-    ref_gy, ref_gw = oracle.combine_bwd(go, y, wts, ref_lay, k, capacity, grad_y=gy_h.copy())
+    ref_gy, ref_gw = oracle.combine_bwd(go, y, wts, ref_lay, k, grad_y=gy_h.copy())
     written = ref_lay["row_src"] >= 0
     if capacity:
         written[:] = True

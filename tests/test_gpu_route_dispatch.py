@@ -121,7 +121,7 @@ def check_dispatch(moe, x, idx, wts, e, capacity=0, max_rows=0):
     if capacity > 0:
         pads = np.nonzero(ref["row_src"] < 0)[0]
         assert (xp_h[pads].view(np.uint8) == 0).all()
-    ref_xp, ref_wp = oracle.scatter(x, k, ref, wts, capacity, x_perm=xp_h.copy())
+    ref_xp, ref_wp = oracle.scatter(x, k, ref, wts, x_perm=xp_h.copy())
     np.testing.assert_array_equal(host(wp), ref_wp)
     assert (xp_h.view(np.uint8) == ref_xp.view(np.uint8)).all()
     return xp, wp, lay, ref

@@ -49,9 +49,10 @@ def bf_weights(row: np.ndarray, sel):
     return [x / s for x in ex]
 
 
-def bf_layout(idx: np.ndarray, e: int, capacity: int, max_rows: int):
+def bf_layout(idx: np.ndarray, e: int, capacity: int, max_rows: int, row_align: int = 0):
     """Permutation by a comparison sort on (expert, assignment); ordinals by the
-    segment-start / running-max construction over the expert-sorted list."""
+    segment-start / running-max construction over the expert-sorted list; with a
+    row alignment A, dropless segments are the counts rounded up to multiples of A."""
     flat = idx.reshape(-1)
     a_total = flat.size
     valid = [a for a in range(a_total) if 0 <= flat[a] < e]
@@ -75,9 +76,11 @@ def bf_layout(idx: np.ndarray, e: int, capacity: int, max_rows: int):
         offsets = np.arange(e + 1) * capacity
         kept = np.minimum(counts, capacity)
     else:
-        rows = max_rows if max_rows > 0 else a_total
-        offsets = np.minimum(np.concatenate([[0], np.cumsum(counts)]), rows)
-        kept = np.diff(offsets)
+        al = max(row_align, 1)
+        rows = max_rows if max_rows > 0 else a_total + e * (al - 1)
+        padded = [-(-int(c) // al) * al for c in counts]
+        offsets = np.minimum(np.concatenate([[0], np.cumsum(padded, dtype=np.int64)]), rows)
+        kept = np.minimum(counts, rows - offsets[:-1])
     assign_row = np.full(a_total, -1, np.int64)
     drop = np.zeros(a_total, np.uint8)
     for a in valid:
@@ -93,8 +96,7 @@ def bf_layout(idx: np.ndarray, e: int, capacity: int, max_rows: int):
     invalid = int(sum(1 for v in flat if v < -1 or v >= e))
     return dict(ordinal=ordinal, assign_row=assign_row, drop_mask=drop, row_src=row_src,
                 pad_mask=(row_src < 0).astype(np.uint8), tokens_per_expert=kept,
-                expert_offsets=offsets, counters=np.array([kept.sum(), drop.sum(),
-                                                           (rows - kept.sum()) if capacity > 0 else 0,
+                expert_offsets=offsets, counters=np.array([kept.sum(), drop.sum(), offsets[-1] - kept.sum(),
                                                            invalid]))
 
 
@@ -291,9 +293,9 @@ def test_route_invariants_uniform_workload():
 
 # -------------------------------------------------------------------- layout
 
-def _check_layout(idx, e, capacity=0, max_rows=0):
-    got = oracle.layout(idx, e, capacity, max_rows)
-    ref = bf_layout(idx, e, capacity, max_rows)
+def _check_layout(idx, e, capacity=0, max_rows=0, row_align=0):
+    got = oracle.layout(idx, e, capacity, max_rows, row_align)
+    ref = bf_layout(idx, e, capacity, max_rows, row_align)
     for f in ("ordinal", "assign_row", "drop_mask", "row_src", "pad_mask", "tokens_per_expert",
               "expert_offsets", "counters"):
         np.testing.assert_array_equal(got[f], ref[f], err_msg=f)
@@ -314,6 +316,43 @@ def test_layout_brute_force_random(trial):
     capacity = int(g.integers(1, 6)) if mode == 1 else 0
     max_rows = int(g.integers(0, n * k + 1)) if mode == 2 else 0
     _check_layout(idx, e, capacity, max_rows)
+
+
+@pytest.mark.parametrize("trial", range(30))
+def test_layout_row_align_brute_force_random(trial):
+    """Alignment-padded dropless segments, with and without a row budget."""
+    g = np.random.default_rng(3000 + trial)
+    e = int(g.integers(1, 17))
+    k = int(g.integers(1, 5))
+    n = int(g.integers(0, 65))
+    al = int(g.choice([2, 4, 16, 64]))
+    idx = g.integers(-1, e, size=(n, k)).astype(np.int32)
+    max_rows = int(g.integers(0, n * k + e * al + 1)) if trial % 2 else 0
+    got = _check_layout(idx, e, 0, max_rows, al)
+    off, kept = got["expert_offsets"], got["tokens_per_expert"]
+    rows = got["rows"]
+    for x in range(e):
+        if off[x] < rows:
+            assert off[x] % al == 0                                   # aligned starts
+        end = min(off[x] + -(-int(kept[x]) // al) * al, rows)
+        assert (got["pad_mask"][off[x] + kept[x]:end] == 1).all()    # alignment pads
+    if not max_rows:
+        assert rows == n * k + e * (al - 1) and got["counters"][1] == 0
+        assert got["counters"][2] == sum(-(-int(c) // al) * al - int(c) for c in kept)
+
+
+def test_layout_row_align_closed_forms():
+    # counts 5, 0, 3 with alignment 4: segments [0, 8), [8, 8), [8, 12)
+    idx = np.array([[0], [0], [2], [0], [2], [0], [0], [2]], np.int32)
+    got = _check_layout(idx, 3, row_align=4)
+    assert got["expert_offsets"].tolist() == [0, 8, 8, 12]
+    assert got["tokens_per_expert"].tolist() == [5, 0, 3]
+    assert got["counters"].tolist() == [8, 0, 4, 0]
+    assert got["pad_mask"][:12].tolist() == [0] * 5 + [1] * 3 + [0] * 3 + [1]
+    # alignment 1 is no alignment
+    for al in (0, 1):
+        np.testing.assert_array_equal(oracle.layout(idx, 3, row_align=al)["assign_row"],
+                                      oracle.layout(idx, 3)["assign_row"])
 
 
 def test_layout_all_to_one_expert_and_capacity_one():
@@ -374,22 +413,32 @@ def test_layout_matches_brute_force_on_uniform_workload_sample():
 # ------------------------------------------------------------------- scatter
 
 @pytest.mark.parametrize("dt,capacity", [(mi.DT_F32, 0), (mi.DT_BF16, 0), (mi.DT_BF16, 3), (mi.DT_F32, 2)])
-def test_scatter_bitwise(dt, capacity):
+def test_scatter_bitwise(dt, capacity, row_align=0):
     g = np.random.default_rng(7)
     n, k, e, h = 37, 3, 6, 24
     idx = np.stack([g.permutation(e)[:k] for _ in range(n)]).astype(np.int32)
     idx[g.random(idx.shape) < 0.15] = -1
     wts = g.random((n, k)).astype(np.float32)
     x = mi.normal_activations((n, h), dt, 99, 1)
-    lay = oracle.layout(idx, e, capacity)
-    xp, wp = oracle.scatter(x, k, lay, wts, capacity)
+    lay = oracle.layout(idx, e, capacity, row_align=row_align)
+    fill = np.full((lay["rows"], h), 7, x.dtype)    # rows the scatter does not write keep this
+    xp, wp = oracle.scatter(x, k, lay, wts, x_perm=fill.copy())
     kept = np.nonzero(lay["assign_row"] >= 0)[0]
     assert (xp[lay["assign_row"][kept]].view(np.uint8) == x[kept // k].view(np.uint8)).all()
     assert (wp[lay["assign_row"][kept]] == wts.reshape(-1)[kept]).all()
     pads = lay["row_src"] < 0
     assert (wp[pads] == 0).all()
+    used = np.arange(lay["rows"]) < lay["expert_offsets"][-1]
+    assert (xp[pads & used].view(np.uint8) == 0).all()          # capacity or alignment pads: zero
+    assert (xp[pads & ~used] == fill[pads & ~used]).all()        # the unused dropless tail: untouched
     if capacity:
-        assert (xp[pads].view(np.uint8) == 0).all()
+        assert used.all()
+    if row_align > 1:
+        assert (pads & used).sum() == lay["counters"][2] > 0
+
+
+def test_scatter_bitwise_row_align():
+    test_scatter_bitwise(mi.DT_BF16, 0, row_align=8)
 
 
 # ------------------------------------------------------ dispatch backward
@@ -408,7 +457,7 @@ def test_dispatch_bwd_is_adjoint_of_scatter_exactly(capacity):
     g, idx, lay, n, k, h = _dispatch_case(mi.DT_F32, capacity, 31)
     x = g.integers(-8, 9, (n, h)).astype(np.float32)
     dxp = g.integers(-8, 9, (lay["rows"], h)).astype(np.float32)
-    xp, _ = oracle.scatter(x, k, lay, np.ones((n, k), np.float32), capacity)
+    xp, _ = oracle.scatter(x, k, lay, np.ones((n, k), np.float32))
     dx = oracle.dispatch_bwd(dxp, lay, n, k)
     assert (dx.astype(np.float64) * x).sum() == (dxp.astype(np.float64) * xp).sum()
 
@@ -500,7 +549,7 @@ def test_combine_capacity_reduces_to_kept_weights():
     idx, wts, _, _ = oracle.route(mi.router_logits(w), w.top_k)
     lay = oracle.layout(idx, w.n_experts, w.capacity)
     x = mi.normal_activations((w.n_tokens, w.hidden), mi.DT_F32, 3, 1)
-    xp, _ = oracle.scatter(x, w.top_k, lay, wts, w.capacity)
+    xp, _ = oracle.scatter(x, w.top_k, lay, wts)
     out = oracle.combine(xp, wts, lay, w.n_tokens, w.top_k)
     kept_w = np.where(lay["assign_row"].reshape(w.n_tokens, w.top_k) >= 0, wts, 0).astype(np.float64).sum(1)
     np.testing.assert_allclose(out, x * kept_w[:, None], rtol=1e-5, atol=1e-6)
@@ -517,7 +566,7 @@ def test_combine_bwd_adjoint_euler_and_finite_differences(dt):
     lay = oracle.layout(idx, e, cap)
     y = mi.normal_activations((lay["rows"], h), dt, 8, 8)
     go = mi.normal_activations((n, h), dt, 9, 9)
-    gy, gw = oracle.combine_bwd(go, y, wts, lay, k, cap)
+    gy, gw = oracle.combine_bwd(go, y, wts, lay, k)
     val = (lambda a: a.astype(np.float64)) if dt == mi.DT_F32 else bf16_vals
     yv, gv, gyv = val(y), val(go), val(gy)
     M = dense_combine_matrix(n, k, lay["rows"], wts, lay["assign_row"])
