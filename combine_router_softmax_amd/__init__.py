@@ -32,7 +32,7 @@ EXPORTS = ("moe_layout_rows", "moe_workspace_size", "moe_route", "moe_dispatch",
 class MoeShape(C.Structure):
     _fields_ = [("n_tokens", C.c_int64), ("hidden", C.c_int64), ("n_experts", C.c_int32), ("top_k", C.c_int32),
                 ("capacity", C.c_int32), ("inter", C.c_int32), ("max_rows", C.c_int64), ("act_dtype", C.c_int32),
-                ("reserved", C.c_int32)]
+                ("row_align", C.c_int32)]
 
 
 class MoeLayoutC(C.Structure):
@@ -107,9 +107,10 @@ def _contig(t: torch.Tensor, name: str):
     return t
 
 
-def make_shape(n_tokens, hidden, n_experts, top_k, capacity=0, inter=0, max_rows=0, act_dtype=MOE_DT_BF16):
+def make_shape(n_tokens, hidden, n_experts, top_k, capacity=0, inter=0, max_rows=0, act_dtype=MOE_DT_BF16,
+               row_align=0):
     return MoeShape(int(n_tokens), int(hidden), int(n_experts), int(top_k), int(capacity), int(inter), int(max_rows),
-                    int(act_dtype), 0)
+                    int(act_dtype), int(row_align))
 
 
 def workspace_size(op: int, shape: MoeShape) -> int:
@@ -156,15 +157,17 @@ class Layout:
     drop_mask: torch.Tensor
     pad_mask: torch.Tensor
     counters: torch.Tensor
+    row_align: int = 0
 
     @staticmethod
-    def empty(n_tokens, top_k, n_experts, capacity, rows, device) -> "Layout":
+    def empty(n_tokens, top_k, n_experts, capacity, rows, device, row_align=0) -> "Layout":
         i32 = dict(dtype=torch.int32, device=device)
         u8 = dict(dtype=torch.uint8, device=device)
         a = n_tokens * top_k
         return Layout(n_tokens, top_k, n_experts, capacity, rows, torch.empty(n_experts, **i32),
                       torch.empty(n_experts + 1, **i32), torch.empty(a, **i32), torch.empty(a, **i32),
-                      torch.empty(rows, **i32), torch.empty(a, **u8), torch.empty(rows, **u8), torch.empty(4, **i32))
+                      torch.empty(rows, **i32), torch.empty(a, **u8), torch.empty(rows, **u8), torch.empty(4, **i32),
+                      row_align)
 
     def c(self) -> MoeLayoutC:
         return MoeLayoutC(*[t.data_ptr() for t in (self.tokens_per_expert, self.expert_offsets, self.ordinal,
@@ -173,7 +176,7 @@ class Layout:
 
     def shape(self, hidden, act_dtype, inter=0) -> MoeShape:
         return make_shape(self.n_tokens, hidden, self.n_experts, self.top_k, self.capacity, inter,
-                          0 if self.capacity > 0 else self.rows, act_dtype)
+                          0 if self.capacity > 0 else self.rows, act_dtype, self.row_align)
 
 
 def moe_route(logits: torch.Tensor, top_k: int, *, token_mask: torch.Tensor | None = None, routing_map: bool = True,
@@ -203,21 +206,23 @@ def moe_route(logits: torch.Tensor, top_k: int, *, token_mask: torch.Tensor | No
 
 
 def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor | None, n_experts: int, *,
-                 capacity: int = 0, max_rows: int = 0, w_perm: bool = True, layout: Layout | None = None,
-                 x_perm: torch.Tensor | None = None, w_perm_out: torch.Tensor | None = None, workspace=None):
-    """Layout + row scatter (include/moe.h moe_dispatch) -> (x_perm, w_perm, layout)."""
+                 capacity: int = 0, max_rows: int = 0, row_align: int = 0, w_perm: bool = True,
+                 layout: Layout | None = None, x_perm: torch.Tensor | None = None,
+                 w_perm_out: torch.Tensor | None = None, workspace=None):
+    """Layout + row scatter (include/moe.h moe_dispatch) -> (x_perm, w_perm, layout).
+    row_align: dropless segments rounded up to multiples of this many rows (0: none)."""
     _contig(x, "x")
     _contig(topk_idx, "topk_idx")
     n, h = x.shape
     k = topk_idx.shape[1]
     dev = x.device
     dt = _act_dtype(x)
-    shape = make_shape(n, h, n_experts, k, capacity, 0, max_rows, dt)
+    shape = make_shape(n, h, n_experts, k, capacity, 0, max_rows, dt, row_align)
     rows = int(lib.moe_layout_rows(C.byref(shape)))
     if rows < 0:
         _check(-1, "moe_dispatch")
     if layout is None:
-        layout = Layout.empty(n, k, n_experts, capacity, rows, dev)
+        layout = Layout.empty(n, k, n_experts, capacity, rows, dev, row_align)
     if x_perm is None:
         x_perm = torch.empty((rows, h), dtype=x.dtype, device=dev)
     if w_perm and w_perm_out is None:

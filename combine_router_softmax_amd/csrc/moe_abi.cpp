@@ -11,6 +11,7 @@ namespace {
 
 constexpr int kMaxExperts = 1024;
 constexpr int64_t kMaxIndex = 0x7FFFFFFFll;  // row and assignment indices are int32
+constexpr int kMaxRowAlign = 1024;
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
@@ -22,7 +23,8 @@ moe_status check_shape(const moe_shape *s) {
   if (!s) return MOE_ERR_INVALID_ARG;
   if (s->n_tokens < 0 || s->hidden < 1 || s->n_experts < 1 || s->top_k < 1 || s->max_rows < 0) return MOE_ERR_INVALID_ARG;
   if (s->act_dtype != MOE_DT_F32 && s->act_dtype != MOE_DT_BF16) return MOE_ERR_INVALID_ARG;
-  if (s->reserved != 0) return MOE_ERR_INVALID_ARG;
+  if (s->row_align < 0 || s->row_align > kMaxRowAlign || (s->row_align & (s->row_align - 1)) != 0)
+    return MOE_ERR_INVALID_ARG;
   if (s->n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
   if (s->n_tokens > kMaxIndex / s->top_k) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
@@ -30,7 +32,9 @@ moe_status check_shape(const moe_shape *s) {
 
 int64_t rows_of(const moe_shape *s) {
   if (s->capacity > 0) return (int64_t)s->n_experts * s->capacity;
-  return s->max_rows > 0 ? s->max_rows : s->n_tokens * s->top_k;
+  if (s->max_rows > 0) return s->max_rows;
+  // every aligned segment adds at most row_align - 1 pad rows
+  return s->n_tokens * s->top_k + (s->row_align > 1 ? (int64_t)s->n_experts * (s->row_align - 1) : 0);
 }
 
 // Row geometry and the rows of the permuted buffer.
@@ -41,6 +45,10 @@ moe_status check_rows(const moe_shape *s, int64_t *row_bytes, int64_t *rows) {
     const int64_t ec = (int64_t)s->n_experts * s->capacity;
     if (s->max_rows != 0 && s->max_rows != ec) return MOE_ERR_INVALID_ARG;
     if (ec > kMaxIndex) return MOE_ERR_UNSUPPORTED;
+    if (s->row_align > 1 && s->capacity % s->row_align != 0) return MOE_ERR_UNSUPPORTED;  // segments are e*C
+  } else if (s->row_align > 1 &&
+             s->n_tokens * s->top_k + (int64_t)s->n_experts * (s->row_align - 1) > kMaxIndex) {
+    return MOE_ERR_UNSUPPORTED;  // the aligned offsets are int32
   }
   const int64_t r = rows_of(s);
   if (r > kMaxIndex) return MOE_ERR_UNSUPPORTED;
@@ -138,13 +146,16 @@ moe_status moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_i
   if (workspace_bytes < need_ws || (need_ws > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))))
     return MOE_ERR_WORKSPACE;
   hipStream_t hs = as_stream(stream);
-  hipError_t e = moe::launch_layout(topk_idx, topk_w, n, s->top_k, s->n_experts, s->capacity, rows,
+  hipError_t e = moe::launch_layout(topk_idx, topk_w, n, s->top_k, s->n_experts, s->capacity, s->row_align, rows,
                                     layout->tokens_per_expert, layout->expert_offsets, layout->ordinal,
                                     layout->assign_row, layout->row_src, layout->drop_mask, layout->pad_mask,
                                     layout->counters, w_perm, workspace, hs);
   if (e != hipSuccess) return MOE_ERR_HIP;
-  const int64_t pad_rows = s->capacity > 0 ? rows : 0;
-  return hip_status(moe::launch_scatter(x, n, s->top_k, row_bytes, layout->assign_row, x_perm, pad_rows,
+  // pad rows to zero: capacity pads (every row without an assignment), or the
+  // pads of aligned segments (those below the end of the last segment)
+  const int64_t pad_rows = (s->capacity > 0 || s->row_align > 1) ? rows : 0;
+  const int32_t *pad_limit = s->capacity > 0 ? nullptr : layout->expert_offsets + s->n_experts;
+  return hip_status(moe::launch_scatter(x, n, s->top_k, row_bytes, layout->assign_row, x_perm, pad_rows, pad_limit,
                                         layout->row_src, hs));
 }
 
@@ -244,15 +255,17 @@ moe_status moe_combine_bwd(const moe_shape *s, const void *grad_out, const void 
   if (!layout) return MOE_ERR_INVALID_ARG;
   if (n > 0 && (!grad_out || !topk_w || !layout->assign_row || !grad_w || (rows > 0 && (!y || !grad_y))))
     return MOE_ERR_INVALID_ARG;
-  if (s->capacity > 0 && rows > 0 && (!layout->row_src || !grad_y)) return MOE_ERR_INVALID_ARG;
+  if ((s->capacity > 0 || s->row_align > 1) && rows > 0 && (!layout->row_src || !grad_y || !layout->expert_offsets))
+    return MOE_ERR_INVALID_ARG;
   if (!need(grad_out, n, aligned16) || !need(y, rows, aligned16) || !need(grad_y, rows, aligned16) ||
       !need(grad_w, n, aligned4))
     return MOE_ERR_MISALIGNED;
   if (rows > 0 && grad_y && (grad_y == y || grad_y == grad_out)) return MOE_ERR_INVALID_ARG;
-  const int64_t pad_rows = s->capacity > 0 ? rows : 0;
+  const int64_t pad_rows = (s->capacity > 0 || s->row_align > 1) ? rows : 0;
+  const int32_t *pad_limit = s->capacity > 0 ? nullptr : layout->expert_offsets + s->n_experts;
   return hip_status(moe::launch_combine_bwd(s->act_dtype == MOE_DT_BF16, grad_out, y, topk_w, layout->assign_row, n,
-                                            s->top_k, row_bytes, grad_y, grad_w, pad_rows, layout->row_src,
-                                            as_stream(stream)));
+                                            s->top_k, row_bytes, grad_y, grad_w, pad_rows, pad_limit,
+                                            layout->row_src, as_stream(stream)));
 }
 
 const char *moe_status_string(moe_status st) {

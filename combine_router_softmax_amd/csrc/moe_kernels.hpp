@@ -17,19 +17,23 @@ constexpr int kLayoutTile = 2048;  // assignments per layout tile
 inline int64_t layout_tiles(int64_t assignments) { return (assignments + kLayoutTile - 1) / kLayoutTile; }
 size_t layout_workspace_bytes(int64_t assignments, int e);
 hipError_t launch_layout(const int32_t *topk_idx, const float *topk_w, int64_t n, int k, int e, int capacity,
-                         int64_t rows, int32_t *tokens_per_expert, int32_t *expert_offsets, int32_t *ordinal,
+                         int row_align, int64_t rows, int32_t *tokens_per_expert, int32_t *expert_offsets, int32_t *ordinal,
                          int32_t *assign_row, int32_t *row_src, uint8_t *drop_mask, uint8_t *pad_mask,
                          int32_t *counters, float *w_perm, void *workspace, hipStream_t stream);
 
-// ---- row movement (moe_rows.hip); `row_bytes` is a multiple of 16
+// ---- row movement (moe_rows.hip); `row_bytes` is a multiple of 16.  Pad rows
+// (row_src < 0) below pad_rows, and below *pad_limit when pad_limit is given,
+// are zero-filled.
 hipError_t launch_scatter(const void *x, int64_t n, int k, int64_t row_bytes, const int32_t *assign_row,
-                          void *x_perm, int64_t pad_rows, const int32_t *row_src, hipStream_t stream);
+                          void *x_perm, int64_t pad_rows, const int32_t *pad_limit, const int32_t *row_src,
+                          hipStream_t stream);
 // topk_w may be null: unit weights (the dispatch backward)
 hipError_t launch_combine(bool bf16, const void *y, const float *topk_w, const int32_t *assign_row, int64_t n,
                           int k, int64_t row_bytes, void *out, hipStream_t stream);
 hipError_t launch_combine_bwd(bool bf16, const void *grad_out, const void *y, const float *topk_w,
                               const int32_t *assign_row, int64_t n, int k, int64_t row_bytes, void *grad_y,
-                              float *grad_w, int64_t pad_rows, const int32_t *row_src, hipStream_t stream);
+                              float *grad_w, int64_t pad_rows, const int32_t *pad_limit, const int32_t *row_src,
+                              hipStream_t stream);
 
 // ---- grouped SwiGLU FFN (moe_ffn.hip); bf16 operands as uint16_t bit patterns
 size_t ffn_workspace_bytes(int64_t rows, int inter);

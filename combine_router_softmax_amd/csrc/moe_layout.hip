@@ -8,7 +8,10 @@
 // tokens_per_expert, ROCm/Megatron-LM "Add MORI as a Token Dispatcher"):
 //   ordinal[a]    = #{a' < a : id[a'] = id[a]}          (stable counting sort)
 //   expert offset = e*C with a capacity, else the exclusive scan of the counts
-//                   clipped to the row budget R
+//                   (each rounded up to a multiple of the row alignment A, so
+//                   that every segment starts on an aligned row: the padded
+//                   routing maps of the MORI pull request) clipped to the row
+//                   budget R
 //   assign_row[a] = offset[id[a]] + ordinal[a] if kept, else -1
 //
 // How (two launches, no host synchronisation, no atomics on the ordering
@@ -114,7 +117,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count(const int32_t *__
 
 __global__ __launch_bounds__(kLayoutThreads) void layout_place(
     const int32_t *__restrict__ topk_idx, const float *__restrict__ topk_w, int64_t a_total, int64_t tiles, int e,
-    int id_bits, int capacity, int64_t rows, const int32_t *__restrict__ tile_counts,
+    int id_bits, int capacity, int row_align, int64_t rows, const int32_t *__restrict__ tile_counts,
     const int32_t *__restrict__ tile_invalid, int32_t *__restrict__ tokens_per_expert,
     int32_t *__restrict__ expert_offsets, int32_t *__restrict__ counters, int32_t *__restrict__ ordinal,
     int32_t *__restrict__ assign_row, int32_t *__restrict__ row_src, uint8_t *__restrict__ drop_mask,
@@ -202,16 +205,24 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place(
     if (tid == 0) off[e] = (int32_t)rows;
     __syncthreads();
   } else {
-    block_exclusive_scan(total, off, e);
-    for (int x = tid; x < e; x += kLayoutThreads) {
-      const int64_t s0 = off[x] < rows ? off[x] : rows;
-      const int64_t s1 = (int64_t)off[x] + total[x];
-      kept[x] = (int32_t)((s1 < rows ? s1 : rows) - s0);
+    // segment lengths rounded up to the alignment (kept[] as scratch), their
+    // exclusive scan, then each start and kept count clipped to the budget
+    __shared__ int32_t used_end;
+    for (int x = tid; x < e; x += kLayoutThreads) kept[x] = (total[x] + row_align - 1) / row_align * row_align;
+    __syncthreads();
+    block_exclusive_scan(kept, off, e);
+    if (tid == 0) {
+      const int64_t end = (int64_t)off[e - 1] + kept[e - 1];
+      used_end = (int32_t)(end < rows ? end : rows);
     }
     __syncthreads();
-    for (int x = tid; x < e; x += kLayoutThreads) off[x] = off[x] < rows ? off[x] : (int32_t)rows;
-    __syncthreads();
-    if (tid == 0) off[e] = off[e - 1] + kept[e - 1];
+    for (int x = tid; x < e; x += kLayoutThreads) {
+      const int32_t s0 = off[x] < rows ? off[x] : (int32_t)rows;
+      const int64_t room = rows - s0;
+      kept[x] = (int32_t)(total[x] < room ? total[x] : room);
+      off[x] = s0;
+    }
+    if (tid == 0) off[e] = used_end;
     __syncthreads();
   }
 
@@ -243,7 +254,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place(
       }
       counters[0] = ks;
       counters[1] = ts - ks;
-      counters[2] = capacity > 0 ? (int32_t)(rows - ks) : 0;
+      counters[2] = off[e] - ks;  // rows below the end of the last segment holding nothing: pads
       counters[3] = is;
     }
   }
@@ -304,7 +315,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place(
     }
   }
 
-  // rows that receive no assignment: capacity pads and the unused dropless tail
+  // rows that receive no assignment: capacity or alignment pads and the unused
+  // dropless tail
   for (int64_t r = (int64_t)blockIdx.x * kLayoutThreads + tid; r < rows; r += (int64_t)gridDim.x * kLayoutThreads) {
     int x;
     if (capacity > 0) {
@@ -333,7 +345,7 @@ size_t layout_workspace_bytes(int64_t assignments, int e) {
 }
 
 hipError_t launch_layout(const int32_t *topk_idx, const float *topk_w, int64_t n, int k, int e, int capacity,
-                         int64_t rows, int32_t *tokens_per_expert, int32_t *expert_offsets, int32_t *ordinal,
+                         int row_align, int64_t rows, int32_t *tokens_per_expert, int32_t *expert_offsets, int32_t *ordinal,
                          int32_t *assign_row, int32_t *row_src, uint8_t *drop_mask, uint8_t *pad_mask,
                          int32_t *counters, float *w_perm, void *workspace, hipStream_t stream) {
   const int64_t a_total = n * k;
@@ -354,7 +366,8 @@ hipError_t launch_layout(const int32_t *topk_idx, const float *topk_w, int64_t n
   const int id_bits = e <= 1 ? 0 : 32 - __builtin_clz((unsigned)(e - 1));
   const size_t lds = sizeof(int32_t) * ((size_t)kLayoutWaves * e + 4 * (size_t)e + 1);
   hipLaunchKernelGGL(layout_place, dim3((unsigned)blocks), dim3(kLayoutThreads), lds, stream, topk_idx, topk_w,
-                     a_total, tiles, e, id_bits, capacity, rows, tile_counts, tile_invalid, tokens_per_expert,
+                     a_total, tiles, e, id_bits, capacity, row_align > 1 ? row_align : 1, rows, tile_counts,
+                     tile_invalid, tokens_per_expert,
                      expert_offsets, counters, ordinal, assign_row, row_src, drop_mask, pad_mask, w_perm);
   return hipGetLastError();
 }

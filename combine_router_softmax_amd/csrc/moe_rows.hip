@@ -37,12 +37,16 @@ __device__ __forceinline__ const char *row_ptr(const void *base, int64_t row, in
   return static_cast<const char *>(base) + row * row_bytes;
 }
 
-// Zero-fill rows r < pad_rows with row_src[r] < 0 (capacity pad slots).
-__device__ __forceinline__ void zero_pad_rows(void *dst, int64_t pad_rows, const int32_t *row_src,
-                                              int64_t row_bytes, int64_t pad_block, int64_t pad_blocks) {
+// Zero-fill the pad rows: rows r < pad_rows (and r < *pad_limit when given: the
+// end of the last expert segment) with row_src[r] < 0 -- capacity pads, or the
+// pads of alignment-padded segments.
+__device__ __forceinline__ void zero_pad_rows(void *dst, int64_t pad_rows, const int32_t *pad_limit,
+                                              const int32_t *row_src, int64_t row_bytes, int64_t pad_block,
+                                              int64_t pad_blocks) {
   const u32x4 z = {0u, 0u, 0u, 0u};
   const int64_t vpr = row_bytes / 16;
-  for (int64_t r = pad_block; r < pad_rows; r += pad_blocks) {
+  const int64_t lim = pad_limit && *pad_limit < pad_rows ? *pad_limit : pad_rows;
+  for (int64_t r = pad_block; r < lim; r += pad_blocks) {
     if (row_src[r] >= 0) continue;
     char *d = row_ptr(dst, r, row_bytes);
     for (int64_t v = threadIdx.x; v < vpr; v += kRowThreads) st16_stream(d + v * 16, z);
@@ -53,10 +57,11 @@ template <int KC>
 __global__ __launch_bounds__(kRowThreads) void scatter_kernel(const void *__restrict__ x, int64_t n, int k,
                                                               int64_t row_bytes, const int32_t *__restrict__ assign_row,
                                                               void *__restrict__ x_perm, int64_t pad_rows,
+                                                              const int32_t *__restrict__ pad_limit,
                                                               const int32_t *__restrict__ row_src, int64_t pad_blocks) {
   const int64_t b = blockIdx.x;
   if (b >= n) {
-    zero_pad_rows(x_perm, pad_rows, row_src, row_bytes, b - n, pad_blocks);
+    zero_pad_rows(x_perm, pad_rows, pad_limit, row_src, row_bytes, b - n, pad_blocks);
     return;
   }
   const int64_t vpr = row_bytes / 16;
@@ -116,14 +121,15 @@ template <bool BF16, int KC>
 __global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
     const void *__restrict__ grad_out, const void *__restrict__ y, const float *__restrict__ topk_w,
     const int32_t *__restrict__ assign_row, int64_t n, int k, int64_t row_bytes, void *__restrict__ grad_y,
-    float *__restrict__ grad_w, int64_t pad_rows, const int32_t *__restrict__ row_src, int64_t pad_blocks) {
+    float *__restrict__ grad_w, int64_t pad_rows, const int32_t *__restrict__ pad_limit,
+    const int32_t *__restrict__ row_src, int64_t pad_blocks) {
   using V = Vec16<BF16>;
   constexpr int EL = V::kElems;
   constexpr int kWaves = kRowThreads / kWave;
   __shared__ float part[kWaves][KC];
   const int64_t t = blockIdx.x;
   if (t >= n) {
-    zero_pad_rows(grad_y, pad_rows, row_src, row_bytes, t - n, pad_blocks);
+    zero_pad_rows(grad_y, pad_rows, pad_limit, row_src, row_bytes, t - n, pad_blocks);
     return;
   }
   const int64_t vpr = row_bytes / 16;
@@ -184,16 +190,17 @@ inline int64_t pad_block_count(int64_t pad_rows) {
 }  // namespace
 
 hipError_t launch_scatter(const void *x, int64_t n, int k, int64_t row_bytes, const int32_t *assign_row,
-                          void *x_perm, int64_t pad_rows, const int32_t *row_src, hipStream_t stream) {
+                          void *x_perm, int64_t pad_rows, const int32_t *pad_limit, const int32_t *row_src,
+                          hipStream_t stream) {
   const int64_t pb = pad_block_count(pad_rows);
   const int64_t blocks = n + pb;
   if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(kRowThreads);
   switch (slot_chunk(k)) {
-    case 1: hipLaunchKernelGGL(scatter_kernel<1>, grid, block, 0, stream, x, n, k, row_bytes, assign_row, x_perm, pad_rows, row_src, pb); break;
-    case 2: hipLaunchKernelGGL(scatter_kernel<2>, grid, block, 0, stream, x, n, k, row_bytes, assign_row, x_perm, pad_rows, row_src, pb); break;
-    case 4: hipLaunchKernelGGL(scatter_kernel<4>, grid, block, 0, stream, x, n, k, row_bytes, assign_row, x_perm, pad_rows, row_src, pb); break;
-    default: hipLaunchKernelGGL(scatter_kernel<8>, grid, block, 0, stream, x, n, k, row_bytes, assign_row, x_perm, pad_rows, row_src, pb); break;
+    case 1: hipLaunchKernelGGL(scatter_kernel<1>, grid, block, 0, stream, x, n, k, row_bytes, assign_row, x_perm, pad_rows, pad_limit, row_src, pb); break;
+    case 2: hipLaunchKernelGGL(scatter_kernel<2>, grid, block, 0, stream, x, n, k, row_bytes, assign_row, x_perm, pad_rows, pad_limit, row_src, pb); break;
+    case 4: hipLaunchKernelGGL(scatter_kernel<4>, grid, block, 0, stream, x, n, k, row_bytes, assign_row, x_perm, pad_rows, pad_limit, row_src, pb); break;
+    default: hipLaunchKernelGGL(scatter_kernel<8>, grid, block, 0, stream, x, n, k, row_bytes, assign_row, x_perm, pad_rows, pad_limit, row_src, pb); break;
   }
   return hipGetLastError();
 }
@@ -221,12 +228,13 @@ hipError_t launch_combine(bool bf16, const void *y, const float *topk_w, const i
 template <bool BF16>
 static hipError_t launch_combine_bwd_t(const void *grad_out, const void *y, const float *topk_w,
                                        const int32_t *assign_row, int64_t n, int k, int64_t row_bytes, void *grad_y,
-                                       float *grad_w, int64_t pad_rows, const int32_t *row_src, hipStream_t stream) {
+                                       float *grad_w, int64_t pad_rows, const int32_t *pad_limit,
+                                       const int32_t *row_src, hipStream_t stream) {
   const int64_t pb = pad_block_count(pad_rows);
   const dim3 grid((unsigned)(n + pb)), block(kRowThreads);
 #define MOE_CBWD(KC)                                                                                         \
   hipLaunchKernelGGL((combine_bwd_kernel<BF16, KC>), grid, block, 0, stream, grad_out, y, topk_w, assign_row, n, \
-                     k, row_bytes, grad_y, grad_w, pad_rows, row_src, pb)
+                     k, row_bytes, grad_y, grad_w, pad_rows, pad_limit, row_src, pb)
   switch (slot_chunk(k)) {
     case 1: MOE_CBWD(1); break;
     case 2: MOE_CBWD(2); break;
@@ -239,12 +247,13 @@ static hipError_t launch_combine_bwd_t(const void *grad_out, const void *y, cons
 
 hipError_t launch_combine_bwd(bool bf16, const void *grad_out, const void *y, const float *topk_w,
                               const int32_t *assign_row, int64_t n, int k, int64_t row_bytes, void *grad_y,
-                              float *grad_w, int64_t pad_rows, const int32_t *row_src, hipStream_t stream) {
+                              float *grad_w, int64_t pad_rows, const int32_t *pad_limit, const int32_t *row_src,
+                              hipStream_t stream) {
   if (n + pad_block_count(pad_rows) == 0) return hipSuccess;
   return bf16 ? launch_combine_bwd_t<true>(grad_out, y, topk_w, assign_row, n, k, row_bytes, grad_y, grad_w, pad_rows,
-                                           row_src, stream)
+                                           pad_limit, row_src, stream)
               : launch_combine_bwd_t<false>(grad_out, y, topk_w, assign_row, n, k, row_bytes, grad_y, grad_w,
-                                            pad_rows, row_src, stream);
+                                            pad_rows, pad_limit, row_src, stream);
 }
 
 }  // namespace moe

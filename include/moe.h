@@ -76,7 +76,14 @@ typedef struct moe_shape {
   int64_t max_rows;  /* R: rows of the permuted buffer; 0 = default (E*C with a
                         capacity, else N*k).  With a capacity R must be E*C or 0. */
   int32_t act_dtype; /* moe_dtype of the activations */
-  int32_t reserved;  /* must be 0 */
+  int32_t row_align; /* A: 0 or 1 = none; else a power of two <= 1024.  Without a
+                        capacity, every expert segment is rounded up to a multiple
+                        of A rows, so that each starts on an aligned row (the
+                        padded routing maps of the MORI pull request, for
+                        tile- or FP8-block-aligned expert GEMMs); the rows between
+                        an expert's kept rows and the next segment are pad rows.
+                        Default R becomes N*k + E*(A-1).  With a capacity, C must
+                        be a multiple of A (segments are e*C already). */
 } moe_shape;
 
 /* The dispatch layout ("handle"): written by moe_dispatch, read by the other
@@ -86,16 +93,19 @@ typedef struct moe_layout {
   int32_t *tokens_per_expert; /* [E]   rows kept per expert */
   int32_t *expert_offsets;    /* [E+1] first row of each expert segment; E*C
                                  spacing with a capacity, else the exclusive scan
-                                 of the counts clipped to R; [E] = rows used */
+                                 of the counts (rounded up to A when aligned)
+                                 clipped to R; [E] = end of the last segment */
   int32_t *ordinal;           /* [A]   stable per-expert ordinal (number of earlier
                                  assignments to the same expert), -1 for -1 /
                                  invalid ids; dropped assignments keep theirs */
   int32_t *assign_row;        /* [A]   row of assignment a, -1 if not placed */
   int32_t *row_src;           /* [R]   assignment placed in the row, -1 if none */
   uint8_t *drop_mask;         /* [A]   1 = valid id but over capacity / R */
-  uint8_t *pad_mask;          /* [R]   1 = row holds no assignment (capacity pad
-                                 or unused dropless tail) */
-  int32_t *counters;          /* [4]   kept, dropped, capacity pad rows, invalid ids */
+  uint8_t *pad_mask;          /* [R]   1 = row holds no assignment (capacity or
+                                 alignment pad, or unused dropless tail) */
+  int32_t *counters;          /* [4]   kept, dropped, pad rows (capacity or
+                                 alignment: rows below expert_offsets[E] holding
+                                 nothing), invalid ids */
 } moe_layout;
 
 /* Rows R of the permuted buffer for this shape (E*C, max_rows or N*k). */
@@ -138,9 +148,9 @@ moe_status moe_route(const moe_shape *s, const float *logits, const uint8_t *tok
  * Inputs: x [N, H] activations; topk_idx int32 [N, k] expert ids (-1 = skip;
  *   < -1 or >= E: invalid, skipped, counted in counters[3]); topk_w fp32 [N, k].
  * Outputs: every array of *layout (see moe_layout); x_perm [R, H]: row
- *   assign_row[a] = x[a / k] bit for bit, capacity pad rows all-zero, unused
- *   dropless tail rows not written; w_perm fp32 [R] (nullable): topk_w[a] in
- *   row assign_row[a], 0 in every other row.
+ *   assign_row[a] = x[a / k] bit for bit, pad rows (capacity or alignment)
+ *   all-zero, unused dropless tail rows not written; w_perm fp32 [R]
+ *   (nullable): topk_w[a] in row assign_row[a], 0 in every other row.
  * Stability: within an expert, rows follow assignment order a = t*k + j.
  * With a capacity C the first C assignments of each expert (by ordinal) are
  * kept; without one, assignments past row R are dropped.
@@ -225,8 +235,8 @@ moe_status moe_dispatch_bwd(const moe_shape *s, const void *grad_x_perm, const m
  * For every kept assignment a = (t, j) in row r = assign_row[a]:
  *   grad_y[r, :] = topk_w[t, j] * grad_out[t, :]     (rounded to the activation type)
  *   grad_w[t, j] = sum_h grad_out[t, h] * y[r, h]    (fp32 accumulation)
- * grad_w = 0 for dropped, -1 and invalid slots; capacity pad rows of grad_y are
- * zero; unused dropless tail rows are not written.  grad_y must not alias y or
+ * grad_w = 0 for dropped, -1 and invalid slots; pad rows of grad_y (capacity or
+ * alignment) are zero; unused dropless tail rows are not written.  grad_y must not alias y or
  * grad_out.  No workspace. */
 moe_status moe_combine_bwd(const moe_shape *s, const void *grad_out, const void *y, const float *topk_w,
                            const moe_layout *layout, void *grad_y, float *grad_w, void *stream);

@@ -100,16 +100,17 @@ def test_route_empty(moe):
     assert (host(r.tokens_per_expert) == 0).all()
 
 
-def run_dispatch(moe, x: np.ndarray, idx: np.ndarray, wts: np.ndarray, e: int, capacity=0, max_rows=0):
+def run_dispatch(moe, x: np.ndarray, idx: np.ndarray, wts: np.ndarray, e: int, capacity=0, max_rows=0, row_align=0):
     x_d = dev(x)
-    xp, wp, lay = moe.moe_dispatch(x_d, dev(idx), dev(wts), e, capacity=capacity, max_rows=max_rows)
+    xp, wp, lay = moe.moe_dispatch(x_d, dev(idx), dev(wts), e, capacity=capacity, max_rows=max_rows,
+                                   row_align=row_align)
     torch.cuda.synchronize()
     return xp, wp, lay
 
 
-def check_dispatch(moe, x, idx, wts, e, capacity=0, max_rows=0):
-    xp, wp, lay = run_dispatch(moe, x, idx, wts, e, capacity, max_rows)
-    ref = oracle.layout(idx, e, capacity, max_rows)
+def check_dispatch(moe, x, idx, wts, e, capacity=0, max_rows=0, row_align=0):
+    xp, wp, lay = run_dispatch(moe, x, idx, wts, e, capacity, max_rows, row_align)
+    ref = oracle.layout(idx, e, capacity, max_rows, row_align)
     got = layout_host(lay)
     assert_layout_equal(got, ref)
     xp_h = host(xp)
@@ -118,8 +119,8 @@ def check_dispatch(moe, x, idx, wts, e, capacity=0, max_rows=0):
     rows = ref["assign_row"][kept]
     # dispatched rows: bit-exact copies; capacity pads: all-zero bits
     assert (xp_h[rows].view(np.uint8) == x[kept // k].view(np.uint8)).all()
-    if capacity > 0:
-        pads = np.nonzero(ref["row_src"] < 0)[0]
+    if capacity > 0 or row_align > 1:   # capacity or alignment pads: all-zero bits
+        pads = np.nonzero(ref["row_src"][:ref["expert_offsets"][-1]] < 0)[0]
         assert (xp_h[pads].view(np.uint8) == 0).all()
     ref_xp, ref_wp = oracle.scatter(x, k, ref, wts, x_perm=xp_h.copy())
     np.testing.assert_array_equal(host(wp), ref_wp)
@@ -137,24 +138,28 @@ def test_dispatch_workloads_full_size(moe, wid):
 
 
 EDGE_CASES = ["ragged", "capacity", "clip_rows", "invalid_ids", "one_expert", "all_to_one", "capacity_one", "k1",
-              "e1024", "sentinels"]
+              "e1024", "sentinels", "align64", "align16_clip_rows", "align256_e1024", "align8_capacity"]
 
 
 @pytest.mark.parametrize("case", EDGE_CASES)
 def test_dispatch_edge_cases(moe, case):
     g = np.random.default_rng(100 + EDGE_CASES.index(case))
-    n, e, k, h, cap, max_rows = 1001, 256, 8, 512, 0, 0
+    n, e, k, h, cap, max_rows, align = 1001, 256, 8, 512, 0, 0, 0
     if case == "one_expert":
         e, k = 1, 1
     if case == "k1":
         k = 1
-    if case == "e1024":
+    if case in ("e1024", "align256_e1024"):
         e = 1024
+    if case.startswith("align"):
+        align = int(case[5:].split("_")[0])
     idx = np.stack([g.permutation(e)[:k] for _ in range(n)]).astype(np.int32)
     if case == "capacity":
         cap = 30
-    if case == "clip_rows":
+    if case in ("clip_rows", "align16_clip_rows"):
         max_rows = n * k - 777
+    if case == "align8_capacity":
+        cap = 24
     if case == "invalid_ids":
         bad = g.random(idx.shape) < 0.05
         idx[bad] = g.choice([-5, e, e + 100, -2], size=bad.sum())
@@ -167,7 +172,36 @@ def test_dispatch_edge_cases(moe, case):
         idx[g.random(idx.shape) < 0.75] = -1
     wts = g.random((n, k)).astype(np.float32)
     x = mi.normal_activations((n, h), mi.DT_BF16, 77, 1)
-    check_dispatch(moe, x, idx, wts, e, cap, max_rows)
+    check_dispatch(moe, x, idx, wts, e, cap, max_rows, align)
+
+
+@pytest.mark.parametrize("align", [16, 256])
+def test_aligned_segments_through_ffn_and_combine_bwd(moe, align):
+    """Aligned segments feed the grouped FFN unchanged (its rows are the kept
+    rows); combine backward zeroes the alignment pads of grad_y."""
+    w = mi.workload(4, n_tokens=512, hidden=256, n_experts=16, inter=128)
+    logits = mi.router_logits(w)
+    idx, wts, _, _ = oracle.route(logits, w.top_k)
+    x = mi.activations(w)
+    xp, wp, lay = moe.moe_dispatch(dev(x), dev(idx), dev(wts), w.n_experts, row_align=align)
+    wgu, wd = mi.expert_weights(w)
+    y = moe.moe_expert_ffn(xp, lay, dev(wgu), dev(wd))
+    go = mi.grad_output(w)
+    gy, gw = moe.moe_combine_bwd(dev(go), y, dev(wts), lay)
+    torch.cuda.synchronize()
+    ref_lay = oracle.layout(idx, w.n_experts, row_align=align)
+    ref_lay["rows"] = lay.rows
+    assert_layout_equal(layout_host(lay), ref_lay)
+    kept = ref_lay["pad_mask"] == 0
+    ref_y = oracle.expert_ffn(host(xp), ref_lay, wgu, wd)
+    y_h = host(y)
+    assert max_rel_err(y_h[kept], ref_y[kept]) <= TOL_BF16
+    ref_gy, ref_gw = oracle.combine_bwd(go, y_h, wts, ref_lay, w.top_k, grad_y=host(gy).copy())
+    used = np.arange(lay.rows) < ref_lay["expert_offsets"][-1]
+    gy_h = host(gy)
+    assert (gy_h[used & ~kept] == 0).all()                      # alignment pads of grad_y
+    assert max_rel_err(gy_h[kept], ref_gy[kept]) <= TOL_BF16
+    assert max_rel_err(host(gw), ref_gw) <= TOL_F32
 
 
 def test_dispatch_fp32_tiny_and_empty(moe):
