@@ -8,6 +8,10 @@
 //          intermediate reaches memory.
 //   GEMM2  [rows, I] x [I, H] -> y = bf16(acc).
 // Both operands are K-contiguous (weights stored [out, in]), fp32 accumulation.
+// The backward (moe_expert_ffn_bwd) runs the same kernel with K-major operands
+// -- the weights as stored, for dA and dx, and the expert's rows themselves for
+// the weight gradients, which reduce over the rows of each segment -- read
+// through LDS transpose loads, plus one elementwise SwiGLU-backward kernel.
 // ("Megatron MoE 实现": experts(dispatched_input, tokens_per_expert, ...); the
 // grouped-GEMM paths of ROCm/Megatron-LM "Add MORI as a Token Dispatcher" and
 // xtuner "Integrate UltraEP Runtime" take per-expert row counts; here the
