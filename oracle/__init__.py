@@ -46,7 +46,7 @@ def lib():
             build()
         L = C.CDLL(str(_LIB))
         p, i64, i32 = C.c_void_p, C.c_int64, C.c_int
-        L.oracle_route.argtypes = [i64, i32, i32, p, p, p, p, p, p]
+        L.oracle_route.argtypes = [i64, i32, i32, p, p, p, p, p, p, p]
         L.oracle_route.restype = i32
         L.oracle_layout_rows.argtypes = [i64, i32, i32, i32, i64, i32]
         L.oracle_layout_rows.restype = i64
@@ -85,9 +85,10 @@ def _dt(a: np.ndarray) -> int:
     raise TypeError(f"activations must be float32 or bf16 bits (uint16), got {a.dtype}")
 
 
-def route(logits: np.ndarray, k: int, token_mask=None):
+def route(logits: np.ndarray, k: int, token_mask=None, expert_bias=None):
     """-> topk_idx int32 [N,k], topk_w fp32 [N,k], routing_map uint8 [N,E], tokens_per_expert int32 [E].
-    token_mask (uint8 [N], optional): nonzero marks a padding token, routed nowhere (-1 slots, weight 0)."""
+    token_mask (uint8 [N], optional): nonzero marks a padding token, routed nowhere (-1 slots, weight 0).
+    expert_bias (fp32 [E], optional): selection-only bias (rank by logit + bias, weights from the logits)."""
     logits = np.ascontiguousarray(logits, dtype=np.float32)
     n, e = logits.shape
     idx = np.empty((n, k), np.int32)
@@ -96,7 +97,9 @@ def route(logits: np.ndarray, k: int, token_mask=None):
     tpe = np.empty(e, np.int32)
     mask = None if token_mask is None else np.ascontiguousarray(token_mask, dtype=np.uint8)
     assert mask is None or mask.shape == (n,)
-    rc = lib().oracle_route(n, e, k, _p(logits), _p(mask), _p(idx), _p(w), _p(rmap), _p(tpe))
+    bias = None if expert_bias is None else np.ascontiguousarray(expert_bias, dtype=np.float32)
+    assert bias is None or bias.shape == (e,)
+    rc = lib().oracle_route(n, e, k, _p(logits), _p(bias), _p(mask), _p(idx), _p(w), _p(rmap), _p(tpe))
     if rc != 0:
         raise ValueError(f"oracle_route: bad arguments (rc={rc})")
     return idx, w, rmap, tpe

@@ -105,13 +105,18 @@ static int selected_before(float va, int a, float vb, int b) {
  * renormalised, w_j = p_j / sum_j' p_j', and rounded once to fp32; the routing
  * map is the multihot [N, E] row ([MORI] multihot conversion); tokens_per_expert
  * is the column sum of the map.  token_mask (nullable): nonzero marks a
- * padding token, routed nowhere. */
-int oracle_route(int64_t n, int e, int k, const float *logits, const uint8_t *token_mask, int32_t *topk_idx,
-                 float *topk_w, uint8_t *routing_map, int32_t *tokens_per_expert) {
+ * padding token, routed nowhere.  expert_bias (nullable, [E]): a
+ * selection-only bias -- experts are ranked by logit + bias (fp32), the
+ * weights still come from the logits alone (the load-balancing expert bias
+ * of Megatron's router that the UltraEP pull request lists as not yet
+ * supported there). */
+int oracle_route(int64_t n, int e, int k, const float *logits, const float *expert_bias, const uint8_t *token_mask,
+                 int32_t *topk_idx, float *topk_w, uint8_t *routing_map, int32_t *tokens_per_expert) {
   if (n < 0 || e < 1 || k < 1 || k > e) return -1;
   char *taken = (char *)malloc((size_t)e);
   double *p = (double *)malloc(sizeof(double) * (size_t)e);
-  if (!taken || !p) { free(taken); free(p); return -2; }
+  float *sc = (float *)malloc(sizeof(float) * (size_t)e);
+  if (!taken || !p || !sc) { free(taken); free(p); free(sc); return -2; }
   if (tokens_per_expert) memset(tokens_per_expert, 0, sizeof(int32_t) * (size_t)e);
   for (int64_t t = 0; t < n; ++t) {
     const float *l = logits + t * e;
@@ -124,11 +129,14 @@ int oracle_route(int64_t n, int e, int k, const float *logits, const uint8_t *to
       if (routing_map) memset(routing_map + t * e, 0, (size_t)e);
       continue;
     }
+    /* selection score: the logit, plus the expert's bias when one is given
+     * (an fp32 sum); the weights below use the logits alone */
+    for (int x = 0; x < e; ++x) sc[x] = expert_bias ? l[x] + expert_bias[x] : l[x];
     for (int j = 0; j < k; ++j) {
       int best = -1;
       for (int x = 0; x < e; ++x) {
         if (taken[x]) continue;
-        if (best < 0 || selected_before(l[x], x, l[best], best)) best = x;
+        if (best < 0 || selected_before(sc[x], x, sc[best], best)) best = x;
       }
       taken[best] = 1;
       topk_idx[t * k + j] = best;
@@ -146,6 +154,7 @@ int oracle_route(int64_t n, int e, int k, const float *logits, const uint8_t *to
   }
   free(taken);
   free(p);
+  free(sc);
   return 0;
 }
 

@@ -272,6 +272,42 @@ def test_route_token_mask_brute_force(trial):
     assert (placed[mask == 1] == -1).all() and (placed[mask == 0] >= 0).all()
 
 
+@pytest.mark.parametrize("trial", range(20))
+def test_route_expert_bias_brute_force(trial):
+    """Selection by logit + bias (an fp32 sum), weights from the logits of the chosen experts."""
+    g = np.random.default_rng(4000 + trial)
+    e = int(g.integers(1, 17))
+    k = int(g.integers(1, e + 1))
+    n = int(g.integers(1, 40))
+    logits = g.standard_normal((n, e)).astype(np.float32)
+    bias = (g.standard_normal(e) * 0.7).astype(np.float32)
+    if trial % 4 == 0:
+        bias[:] = np.round(bias)                      # many ties between biased scores
+        logits[:] = np.round(logits * 2) / 2
+    idx, w, rmap, tpe = oracle.route(logits, k, expert_bias=bias)
+    for t in range(n):
+        sel = bf_topk((logits[t] + bias).astype(np.float32), k)
+        assert list(idx[t]) == sel
+        ref = bf_weights(logits[t], sel)
+        assert np.all(np.abs(w[t].astype(np.float64) - ref) <= f32_ulp(np.float32(ref)) * 1.0001)
+    np.testing.assert_array_equal(tpe, rmap.sum(0))
+
+
+def test_route_expert_bias_closed_forms():
+    g = np.random.default_rng(5)
+    logits = g.standard_normal((64, 12)).astype(np.float32)
+    ref = oracle.route(logits, 3)
+    zero = oracle.route(logits, 3, expert_bias=np.zeros(12, np.float32))
+    for a, b in zip(ref, zero):                        # a zero bias changes nothing
+        np.testing.assert_array_equal(a, b)
+    big = np.zeros(12, np.float32)
+    big[7] = 100.0                                     # expert 7 is selected by every token, in slot 0
+    idx, w, _, tpe = oracle.route(logits, 3, expert_bias=big)
+    assert (idx[:, 0] == 7).all() and tpe[7] == 64
+    for t in range(64):                                # its weight still comes from its logit
+        np.testing.assert_allclose(w[t], bf_weights(logits[t], list(idx[t])), rtol=2 ** -22)
+
+
 def test_route_invariants_uniform_workload():
     w = mi.workload(2)
     logits = mi.router_logits(w)
