@@ -55,7 +55,7 @@ def _load():
     lib.moe_layout_rows.argtypes = [sp]
     lib.moe_layout_rows.restype = C.c_int64
     lib.moe_workspace_size.argtypes = [i32, sp, C.POINTER(C.c_size_t)]
-    lib.moe_route.argtypes = [sp, p, p, p, p, p, p, p]
+    lib.moe_route.argtypes = [sp, p, p, p, p, p, p, p, p]
     lib.moe_dispatch.argtypes = [sp, p, p, p, lp, p, p, p, C.c_size_t, p]
     lib.moe_expert_ffn.argtypes = [sp, p, lp, p, p, p, p, p, C.c_size_t, p]
     lib.moe_expert_ffn_bwd.argtypes = [sp, p, p, p, lp, p, p, p, p, p, p, C.c_size_t, p]
@@ -179,14 +179,20 @@ class Layout:
                           0 if self.capacity > 0 else self.rows, act_dtype, self.row_align)
 
 
-def moe_route(logits: torch.Tensor, top_k: int, *, token_mask: torch.Tensor | None = None, routing_map: bool = True,
-              counts: bool = True, out: RouteOut | None = None) -> RouteOut:
+def moe_route(logits: torch.Tensor, top_k: int, *, expert_bias: torch.Tensor | None = None,
+              token_mask: torch.Tensor | None = None, routing_map: bool = True, counts: bool = True,
+              out: RouteOut | None = None) -> RouteOut:
     """Router softmax / top-k (include/moe.h moe_route).  logits fp32 [N, E] on the GPU;
+    expert_bias (optional, fp32 [E]): selection-only bias;
     token_mask (optional, uint8 or bool [N]): nonzero marks a padding token, routed nowhere."""
     _contig(logits, "logits")
     if logits.dtype != torch.float32 or logits.dim() != 2:
         raise TypeError("logits must be a float32 [N, E] tensor")
     n, e = logits.shape
+    if expert_bias is not None:
+        _contig(expert_bias, "expert_bias")
+        if expert_bias.dtype != torch.float32 or tuple(expert_bias.shape) != (e,):
+            raise TypeError("expert_bias must be a float32 [E] tensor")
     if token_mask is not None:
         if token_mask.dtype == torch.bool:
             token_mask = token_mask.view(torch.uint8)
@@ -200,8 +206,9 @@ def moe_route(logits: torch.Tensor, top_k: int, *, token_mask: torch.Tensor | No
                        torch.empty((n, e), dtype=torch.uint8, device=dev) if routing_map else None,
                        torch.empty(e, dtype=torch.int32, device=dev) if counts else None)
     shape = make_shape(n, 1, e, top_k, act_dtype=MOE_DT_F32)
-    _check(lib.moe_route(C.byref(shape), _ptr(logits), _ptr(token_mask), _ptr(out.topk_idx), _ptr(out.topk_w),
-                         _ptr(out.routing_map), _ptr(out.tokens_per_expert), _stream(dev)), "moe_route")
+    _check(lib.moe_route(C.byref(shape), _ptr(logits), _ptr(expert_bias), _ptr(token_mask), _ptr(out.topk_idx),
+                         _ptr(out.topk_w), _ptr(out.routing_map), _ptr(out.tokens_per_expert), _stream(dev)),
+           "moe_route")
     return out
 
 

@@ -12,7 +12,10 @@
 // exp(l_i - l_max) / sum_chosen exp(l_j - l_max), with l_max the slot-0 logit.
 // A token marked in the optional padding mask routes nowhere (the router of
 // "Add MORI as a Token Dispatcher" masks padding tokens out of routing and
-// dispatch).
+// dispatch).  An optional per-expert bias enters the selection only: experts
+// are ranked by logit + bias, the weights come from the logits (Megatron's
+// load-balancing expert bias, which "Integrate UltraEP Runtime" lists as not
+// yet supported there).
 // Counts: when the routing map is written (E % 16 == 0), a second kernel takes
 // its column sums in a few dozen workgroups, one global atomic per expert and
 // workgroup; otherwise each router workgroup adds its LDS histogram with global
@@ -81,6 +84,7 @@ __global__ __launch_bounds__(kRouteThreads) void count_map_kernel(const uint8_t 
 
 template <int VPL>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float *__restrict__ logits,
+                                                              const float *__restrict__ expert_bias,
                                                               const uint8_t *__restrict__ token_mask, int64_t n, int e,
                                                               int k, int32_t *__restrict__ topk_idx,
                                                               float *__restrict__ topk_w,
@@ -118,7 +122,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float *__res
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
       const int x = l + kWave * i;
-      key[i] = x < e ? ((uint64_t)logit_key(row[x]) << 32) | (uint32_t)~(uint32_t)x : 0ull;
+      // selection score: the logit, plus the expert's bias when one is given
+      const float sc = x < e ? (expert_bias ? row[x] + expert_bias[x] : row[x]) : 0.0f;
+      key[i] = x < e ? ((uint64_t)logit_key(sc) << 32) | (uint32_t)~(uint32_t)x : 0ull;
     }
     uint32_t taken = 0;
     for (int j = 0; j < k; ++j) {
@@ -140,13 +146,30 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float *__res
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    const float lmax = key_logit(sel_key[0]);
-    float part = 0.0f;
-    for (int j = l; j < k; j += kWave) part += expf(key_logit(sel_key[j]) - lmax);
-    const float denom = wave_sum_f32(part);
-    for (int j = l; j < k; j += kWave) {
-      topk_idx[t * k + j] = sel_idx[j];
-      topk_w[t * k + j] = expf(key_logit(sel_key[j]) - lmax) / denom;
+    if (!expert_bias) {
+      // the chosen logits are the selection keys; slot 0 holds the largest
+      const float lmax = key_logit(sel_key[0]);
+      float part = 0.0f;
+      for (int j = l; j < k; j += kWave) part += expf(key_logit(sel_key[j]) - lmax);
+      const float denom = wave_sum_f32(part);
+      for (int j = l; j < k; j += kWave) {
+        topk_idx[t * k + j] = sel_idx[j];
+        topk_w[t * k + j] = expf(key_logit(sel_key[j]) - lmax) / denom;
+      }
+    } else {
+      // the bias only selects: the weights come from the chosen experts' logits,
+      // relative to the largest of them
+      float lmax = -INFINITY;
+      for (int j = l; j < k; j += kWave) lmax = fmaxf(lmax, row[sel_idx[j]]);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, off, kWave));
+      float part = 0.0f;
+      for (int j = l; j < k; j += kWave) part += expf(row[sel_idx[j]] - lmax);
+      const float denom = wave_sum_f32(part);
+      for (int j = l; j < k; j += kWave) {
+        topk_idx[t * k + j] = sel_idx[j];
+        topk_w[t * k + j] = expf(row[sel_idx[j]] - lmax) / denom;
+      }
     }
     if (routing_map) {
 #pragma unroll
@@ -169,20 +192,21 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float *__res
 }
 
 template <int VPL>
-hipError_t launch_route_vpl(const float *logits, const uint8_t *token_mask, int64_t n, int e, int k,
-                            int32_t *topk_idx, float *topk_w, uint8_t *routing_map, int32_t *tokens_per_expert,
-                            int32_t *zero_counts, hipStream_t stream) {
+hipError_t launch_route_vpl(const float *logits, const float *expert_bias, const uint8_t *token_mask, int64_t n,
+                            int e, int k, int32_t *topk_idx, float *topk_w, uint8_t *routing_map,
+                            int32_t *tokens_per_expert, int32_t *zero_counts, hipStream_t stream) {
   const int64_t blocks = (n + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock;
   const size_t lds = sizeof(uint32_t) * (2 * kRouteTokensPerBlock * (size_t)k + (size_t)e);
-  hipLaunchKernelGGL(route_kernel<VPL>, dim3((unsigned)blocks), dim3(kRouteThreads), lds, stream, logits, token_mask,
-                     n, e, k, topk_idx, topk_w, routing_map, tokens_per_expert, zero_counts);
+  hipLaunchKernelGGL(route_kernel<VPL>, dim3((unsigned)blocks), dim3(kRouteThreads), lds, stream, logits,
+                     expert_bias, token_mask, n, e, k, topk_idx, topk_w, routing_map, tokens_per_expert, zero_counts);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_route(const float *logits, const uint8_t *token_mask, int64_t n, int e, int k, int32_t *topk_idx,
-                        float *topk_w, uint8_t *routing_map, int32_t *tokens_per_expert, hipStream_t stream) {
+hipError_t launch_route(const float *logits, const float *expert_bias, const uint8_t *token_mask, int64_t n, int e,
+                        int k, int32_t *topk_idx, float *topk_w, uint8_t *routing_map, int32_t *tokens_per_expert,
+                        hipStream_t stream) {
   const bool map_counts = n > 0 && tokens_per_expert && routing_map && e % 16 == 0 &&
                           (reinterpret_cast<uintptr_t>(routing_map) & 15u) == 0;
   if (tokens_per_expert && !map_counts) {  // the router kernel adds into zeroed counts
@@ -196,7 +220,8 @@ hipError_t launch_route(const float *logits, const uint8_t *token_mask, int64_t 
   int32_t *zero_counts = map_counts ? tokens_per_expert : nullptr;
   hipError_t st;
 #define MOE_ROUTE(V) \
-  launch_route_vpl<V>(logits, token_mask, n, e, k, topk_idx, topk_w, routing_map, kernel_counts, zero_counts, stream)
+  launch_route_vpl<V>(logits, expert_bias, token_mask, n, e, k, topk_idx, topk_w, routing_map, kernel_counts, \
+                      zero_counts, stream)
   if (e <= 64) st = MOE_ROUTE(1);
   else if (e <= 128) st = MOE_ROUTE(2);
   else if (e <= 256) st = MOE_ROUTE(4);

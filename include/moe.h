@@ -127,6 +127,11 @@ moe_status moe_workspace_size(moe_op op, const moe_shape *s, size_t *bytes);
  *     (fp32; equal to the softmax over the k chosen logits);
  *   routing_map[t, e] = 1 if e was chosen else 0 (nullable, uint8 [N, E]);
  *   tokens_per_expert[e] = number of tokens choosing e (nullable, int32 [E]).
+ * expert_bias (nullable, fp32 [E]): a selection-only bias: experts are ranked by
+ *   the fp32 sum logits[t, e] + expert_bias[e] (same order and tie rules), while
+ *   topk_w stays the renormalised softmax of the chosen experts' logits (the
+ *   load-balancing expert bias of Megatron's router, which the UltraEP pull
+ *   request "Integrate UltraEP Runtime" lists as not yet supported there).
  * token_mask (nullable, uint8 [N]): a nonzero byte marks a padding token, which
  *   takes part in no routing (the pull request's router masks padding tokens out
  *   of routing and dispatch): its slots are -1 with weight 0, its map row is
@@ -135,8 +140,9 @@ moe_status moe_workspace_size(moe_op op, const moe_shape *s, size_t *bytes);
  * Inputs: logits fp32 [N, E].  Outputs: topk_idx int32 [N, k], topk_w fp32 [N, k].
  * Infinite logits are unsupported (their weights are NaN).  k <= E <= 1024.
  * No workspace. */
-moe_status moe_route(const moe_shape *s, const float *logits, const uint8_t *token_mask, int32_t *topk_idx,
-                     float *topk_w, uint8_t *routing_map, int32_t *tokens_per_expert, void *stream);
+moe_status moe_route(const moe_shape *s, const float *logits, const float *expert_bias, const uint8_t *token_mask,
+                     int32_t *topk_idx, float *topk_w, uint8_t *routing_map, int32_t *tokens_per_expert,
+                     void *stream);
 
 /* Dispatch: local permutation of token rows into expert-contiguous rows
  * ("Megatron MoE 实现", dispatch_preprocess / dispatch_postprocess ->

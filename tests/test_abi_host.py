@@ -84,11 +84,12 @@ def test_validation_errors_enqueue_nothing(moe):
     p = C.c_void_p(4096)          # a fake, 16-byte-aligned "device" address: never dereferenced
     odd = C.c_void_p(4096 + 2)
     s = moe.make_shape(16, 64, 8, 9, act_dtype=moe.MOE_DT_F32)
-    assert lib.moe_route(C.byref(s), p, None, p, p, None, None, None) == -1    # k > E
+    assert lib.moe_route(C.byref(s), p, None, None, p, p, None, None, None) == -1    # k > E
     s = moe.make_shape(16, 64, 8, 2, act_dtype=moe.MOE_DT_F32)
-    assert lib.moe_route(C.byref(s), None, None, p, p, None, None, None) == -1  # null logits
-    assert lib.moe_route(C.byref(s), odd, None, p, p, None, None, None) == -2   # misaligned
-    assert lib.moe_route(None, p, None, p, p, None, None, None) == -1
+    assert lib.moe_route(C.byref(s), None, None, None, p, p, None, None, None) == -1  # null logits
+    assert lib.moe_route(C.byref(s), odd, None, None, p, p, None, None, None) == -2   # misaligned
+    assert lib.moe_route(C.byref(s), p, odd, None, p, p, None, None, None) == -2     # misaligned bias
+    assert lib.moe_route(None, p, None, None, p, p, None, None, None) == -1
     lay = moe.MoeLayoutC(*([4096] * 8))
     s = moe.make_shape(16, 60, 8, 2, act_dtype=moe.MOE_DT_BF16)                # 120-byte rows
     assert lib.moe_dispatch(C.byref(s), p, p, p, C.byref(lay), p, p, p, 1 << 20, None) == -2

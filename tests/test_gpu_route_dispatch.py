@@ -72,6 +72,43 @@ def test_route_token_mask(moe, e, k, with_map):
     assert max_rel_err(got_w, w) <= TOL_F32
 
 
+@pytest.mark.parametrize("e,k,ties", [(8, 2, False), (100, 7, True), (256, 8, False), (256, 8, True), (1000, 70, False)])
+def test_route_expert_bias(moe, e, k, ties):
+    """Selection by logit + bias, weights from the logits; with ties between biased scores."""
+    g = np.random.default_rng(7 * e + k)
+    n = 513
+    logits = g.standard_normal((n, e)).astype(np.float32)
+    bias = (g.standard_normal(e) * 0.5).astype(np.float32)
+    if ties:
+        logits = (np.round(logits * 2) / 2).astype(np.float32)
+        bias = np.round(bias).astype(np.float32)
+    mask = (g.random(n) < 0.1).astype(np.uint8)
+    r = moe.moe_route(dev(logits), k, expert_bias=dev(bias), token_mask=dev(mask))
+    torch.cuda.synchronize()
+    idx, w, rmap, tpe = oracle.route(logits, k, mask, bias)
+    np.testing.assert_array_equal(host(r.topk_idx), idx)
+    np.testing.assert_array_equal(host(r.routing_map), rmap)
+    np.testing.assert_array_equal(host(r.tokens_per_expert), tpe)
+    assert max_rel_err(host(r.topk_w), w) <= TOL_F32
+
+
+def test_route_expert_bias_balances_skewed_logits(moe):
+    """The Zipf-skewed workload's logits with the negated per-expert mean offset as
+    the bias: the load evens out (selection), the weights keep the skewed logits."""
+    w = mi.workload(3)
+    logits = mi.router_logits(w)
+    col = logits.astype(np.float64).mean(0)
+    bias = (-(col - col.mean())).astype(np.float32)       # undoes the calibrated per-expert skew
+    r = moe.moe_route(dev(logits), w.top_k, expert_bias=dev(bias))
+    torch.cuda.synchronize()
+    idx, wts, _, tpe = oracle.route(logits, w.top_k, expert_bias=bias)
+    np.testing.assert_array_equal(host(r.topk_idx), idx)
+    np.testing.assert_array_equal(host(r.tokens_per_expert), tpe)
+    assert max_rel_err(host(r.topk_w), wts) <= TOL_F32
+    skewed = oracle.route(logits, w.top_k)[3]
+    assert tpe.max() < skewed.max() / 4                  # 4096 for the hottest expert without the bias
+
+
 def test_route_token_mask_through_the_layer(moe):
     """masked route -> dispatch -> combine: padding tokens are not dispatched and get zero rows."""
     w = mi.workload(2, n_tokens=512)
