@@ -48,6 +48,10 @@ def lib():
         p, i64, i32 = C.c_void_p, C.c_int64, C.c_int
         L.oracle_route.argtypes = [i64, i32, i32, p, p, p, p, p, p, p]
         L.oracle_route.restype = i32
+        L.oracle_philox4x32_10.argtypes = [p, p, p]
+        L.oracle_philox4x32_10.restype = None
+        L.oracle_random_logits.argtypes = [i64, i32, C.c_uint64, p]
+        L.oracle_random_logits.restype = None
         L.oracle_layout_rows.argtypes = [i64, i32, i32, i32, i64, i32]
         L.oracle_layout_rows.restype = i64
         L.oracle_layout.argtypes = [i64, i32, i32, i32, i64, i32, p, p, p, p, p, p, p, p, p]
@@ -103,6 +107,27 @@ def route(logits: np.ndarray, k: int, token_mask=None, expert_bias=None):
     if rc != 0:
         raise ValueError(f"oracle_route: bad arguments (rc={rc})")
     return idx, w, rmap, tpe
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32-10 (Salmon et al., SC 2011) of one counter (4 words) and key (2 words)."""
+    c = np.ascontiguousarray(ctr, dtype=np.uint32)
+    k = np.ascontiguousarray(key, dtype=np.uint32)
+    out = np.empty(4, np.uint32)
+    lib().oracle_philox4x32_10(_p(c), _p(k), _p(out))
+    return out
+
+
+def random_logits(n: int, e: int, seed: int) -> np.ndarray:
+    """The force-balanced mode's router logits, fp32 [N, E] uniform in [0, 1) (moe_oracle.c)."""
+    out = np.empty((n, e), np.float32)
+    lib().oracle_random_logits(n, e, seed, _p(out))
+    return out
+
+
+def route_random(n: int, e: int, k: int, seed: int, token_mask=None, expert_bias=None):
+    """Force-balanced routing: route() over random_logits(n, e, seed)."""
+    return route(random_logits(n, e, seed), k, token_mask, expert_bias)
 
 
 def layout(topk_idx: np.ndarray, n_experts: int, capacity: int = 0, max_rows: int = 0, row_align: int = 0) -> dict:

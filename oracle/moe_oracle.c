@@ -158,6 +158,41 @@ int oracle_route(int64_t n, int e, int k, const float *logits, const float *expe
   return 0;
 }
 
+/* ---------------------------------------------- random (balanced) logits */
+
+/* Philox4x32-10, the counter-based generator of Salmon, Moraes, Dror and Shaw,
+ * "Parallel Random Numbers: As Easy as 1, 2, 3" (SC 2011): ten rounds of two
+ * 32x32 -> 64-bit multiplications (multipliers 0xD2511F53 and 0xCD9E8D57),
+ * the key bumped by the Weyl constants 0x9E3779B9 and 0xBB67AE85 between
+ * rounds.  out = Philox(counter ctr[4], key key[2]). */
+void oracle_philox4x32_10(const uint32_t ctr[4], const uint32_t key[2], uint32_t out[4]) {
+  uint32_t c0 = ctr[0], c1 = ctr[1], c2 = ctr[2], c3 = ctr[3], k0 = key[0], k1 = key[1];
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) { k0 += 0x9E3779B9u; k1 += 0xBB67AE85u; }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0, p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0, n1 = (uint32_t)p1;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1, n3 = (uint32_t)p0;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* Random router logits for the force-balanced benchmark mode (the UltraEP pull
+ * request "Integrate UltraEP Runtime": random-logits routing for balanced
+ * benchmark runs).  logit[t, x] = (w >> 8) * 2^-24, a uniform number in [0, 1)
+ * exact in fp32, where w is word x % 4 of Philox4x32-10 with counter
+ * (x / 4, t mod 2^32, t / 2^32, 0) and key (seed mod 2^32, seed / 2^32). */
+void oracle_random_logits(int64_t n, int e, uint64_t seed, float *logits) {
+  const uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  for (int64_t t = 0; t < n; ++t)
+    for (int x = 0; x < e; ++x) {
+      const uint32_t ctr[4] = {(uint32_t)(x / 4), (uint32_t)t, (uint32_t)((uint64_t)t >> 32), 0u};
+      uint32_t w[4];
+      oracle_philox4x32_10(ctr, key, w);
+      logits[t * e + x] = (float)(w[x % 4] >> 8) * (1.0f / 16777216.0f);
+    }
+}
+
 /* ------------------------------------------------------------------ layout */
 
 /* Rows of the permuted buffer: E*C with a capacity, else max_rows if given,

@@ -308,6 +308,33 @@ def test_route_expert_bias_closed_forms():
         np.testing.assert_allclose(w[t], bf_weights(logits[t], list(idx[t])), rtol=2 ** -22)
 
 
+def test_philox_known_answers():
+    """Philox4x32-10 known-answer vectors published with the Random123 library."""
+    cases = [((0, 0, 0, 0), (0, 0), (0x6627e8d5, 0xe169c58d, 0xbc57ac4c, 0x9b00dbd8)),
+             ((0xffffffff,) * 4, (0xffffffff,) * 2, (0x408f276d, 0x41c83b0e, 0xa20bc7c6, 0x6d5451fd)),
+             ((0x243f6a88, 0x85a308d3, 0x13198a2e, 0x03707344), (0xa4093822, 0x299f31d0),
+              (0xd16cfe09, 0x94fdcceb, 0x5001e420, 0x24126ea1))]
+    for ctr, key, out in cases:
+        assert oracle.philox4x32_10(ctr, key).tolist() == list(out)
+
+
+def test_random_logits_definition_and_balance():
+    n, e, seed = 4096, 256, 0x0123456789ABCDEF
+    lg = oracle.random_logits(n, e, seed)
+    assert lg.dtype == np.float32 and (lg >= 0).all() and (lg < 1).all()
+    # spot values from the definition: word x % 4 of Philox((x/4, t, 0, 0), seed), top 24 bits
+    for t, x in ((0, 0), (1, 5), (4095, 255), (77, 130)):
+        w = oracle.philox4x32_10((x // 4, t, 0, 0), (seed & 0xffffffff, seed >> 32))[x % 4]
+        assert lg[t, x] == np.float32((int(w) >> 8) / 16777216.0)
+    # uniform logits balance the experts: counts near N*k/E = 128, weights near 1/k
+    idx, w, _, tpe = oracle.route_random(n, e, 8, seed)
+    assert tpe.sum() == n * 8 and abs(tpe.mean() - 128) < 1e-9
+    assert tpe.min() > 128 - 6 * np.sqrt(128) and tpe.max() < 128 + 6 * np.sqrt(128)
+    assert np.abs(w - 0.125).max() < 0.05
+    # another seed, other logits
+    assert (oracle.random_logits(8, e, seed + 1) != lg[:8]).mean() > 0.99
+
+
 def test_route_invariants_uniform_workload():
     w = mi.workload(2)
     logits = mi.router_logits(w)
