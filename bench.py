@@ -130,6 +130,17 @@ def bench_dispatch_combine(moe, mi, torch, steps, warmup):
     c1.record()
     torch.cuda.synchronize()
     comb_kernel_ms = c0.elapsed_time(c1) / steps
+    # the force-balanced router (random logits drawn on the device) at the same shape
+    rr = moe.moe_route_random(n, e, k, 7, device=dev)
+    for _ in range(warmup):
+        moe.moe_route_random(n, e, k, 7, device=dev, out=rr)
+    torch.cuda.synchronize()
+    c0.record()
+    for _ in range(steps):
+        moe.moe_route_random(n, e, k, 7, device=dev, out=rr)
+    c1.record()
+    torch.cuda.synchronize()
+    route_random_ms = c0.elapsed_time(c1) / steps
     # cold caches: before each timed step, outside the timed region, read 1 GiB
     # (evicts the 4 MB L2 of every XCD and the 256 MB MALL, which could hold x;
     # a read leaves clean lines, so no write-back of the flush lands in the step)
@@ -160,6 +171,7 @@ def bench_dispatch_combine(moe, mi, torch, steps, warmup):
     del flush, dst
     return dict(total_ms=total_ms, route_ms=route_ms, dispatch_ms=disp_ms, combine_ms=comb_ms,
                 comb_kernel_ms=comb_kernel_ms, kept=kept, copy_gbs=copy_gbs, dbwd_ms=dbwd_ms,
+                route_random_ms=route_random_ms,
                 dc_p10=pct([r_[1].elapsed_time(r_[3]) for r_ in recs], 10),
                 dc_p90=pct([r_[1].elapsed_time(r_[3]) for r_ in recs], 90),
                 cold_route_ms=median(cold_route), cold_dispatch_ms=median(cold_disp),
@@ -203,7 +215,25 @@ def bench_expert_gemm(moe, mi, torch, wid, iters, warmup, bwd_iters=0):
     rows = int(lay.counters[0].item())
     flops = 2.0 * rows * h * 3 * inter
     out = dict(workload=w.name, rows=rows, ms=ms, tflops=flops / ms / 1e9, flops=flops)
-    del ws
+    # the same FFN over force-balanced routing (random logits, moe_route_random): every
+    # expert gets about rows/E rows -- the reference point the skew is measured against
+    n_bal, k_bal = (w.n_tokens, w.top_k) if w.has_router else (rows // 2, 2)
+    rb = moe.moe_route_random(n_bal, e, k_bal, 1234 + wid, device=dev, routing_map=False, counts=False)
+    xb = torch.randn((n_bal, h), generator=g, device=dev).to(torch.bfloat16)
+    xpb, _, layb = moe.moe_dispatch(xb, rb.topk_idx, rb.topk_w, e, w_perm=False)
+    yb = torch.empty_like(xpb)
+    for _ in range(warmup):
+        moe.moe_expert_ffn(xpb, layb, wgu, wd, y=yb, workspace=ws)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(iters):
+        moe.moe_expert_ffn(xpb, layb, wgu, wd, y=yb, workspace=ws)
+    b.record()
+    torch.cuda.synchronize()
+    bal_ms = a.elapsed_time(b) / iters
+    bal_rows = int(layb.counters[0].item())
+    out.update(balanced_ms=bal_ms, balanced_tflops=2.0 * bal_rows * h * 3 * inter / bal_ms / 1e9, balanced_rows=bal_rows)
+    del rb, xb, xpb, layb, yb, ws
     if bwd_iters > 0:
         def timed(fn, n):
             for _ in range(warmup):
@@ -403,6 +433,7 @@ def main():
         "copy_gbs": round(dc["copy_gbs"], 1),
         "dispatch_combine_frac_of_copy": round(byts / ((dc["dispatch_ms"] + dc["combine_ms"]) * 1e-3) / 1e9
                                                / dc["copy_gbs"], 4),
+        "route_force_balanced_us": round(dc["route_random_ms"] * 1e3, 2),
         "dispatch_bwd_us": round(dc["dbwd_ms"] * 1e3, 2),
         "dispatch_bwd_gbs": round(dc["combine_bytes"] / (dc["dbwd_ms"] * 1e-3) / 1e9, 2),
         "combine_bwd_us": round(dc["bwd_ms"] * 1e3, 2),
@@ -413,6 +444,8 @@ def main():
                      "algorithmic_bytes": dc["combine_bytes"]},
         "expert_gemm": [{"workload": g["workload"], "rows": g["rows"], "us": round(g["ms"] * 1e3, 1),
                          "tflops": round(g["tflops"], 1), "frac_bf16_peak": round(g["tflops"] / BF16_PEAK_TFLOPS, 4),
+                         "force_balanced_tflops": round(g["balanced_tflops"], 1),
+                         "frac_of_force_balanced": round(g["tflops"] / g["balanced_tflops"], 4),
                          **({"fwd_saving_gate_up_us": round(g["fwd_save_ms"] * 1e3, 1),
                              "bwd_us": round(g["bwd_ms"] * 1e3, 1), "bwd_tflops": round(g["bwd_tflops"], 1),
                              "bwd_frac_bf16_peak": round(g["bwd_tflops"] / BF16_PEAK_TFLOPS, 4),

@@ -24,7 +24,7 @@ MOE_DT_BF16 = 1
 MOE_OP_ROUTE, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE, MOE_OP_COMBINE_BWD, MOE_OP_EXPERT_FFN_BWD = range(6)
 
 # Every symbol include/moe.h declares.
-EXPORTS = ("moe_layout_rows", "moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn",
+EXPORTS = ("moe_layout_rows", "moe_workspace_size", "moe_route", "moe_route_random", "moe_dispatch", "moe_expert_ffn",
            "moe_expert_ffn_bwd", "moe_combine", "moe_dispatch_bwd", "moe_combine_bwd", "moe_status_string",
            "moe_version")
 
@@ -56,13 +56,14 @@ def _load():
     lib.moe_layout_rows.restype = C.c_int64
     lib.moe_workspace_size.argtypes = [i32, sp, C.POINTER(C.c_size_t)]
     lib.moe_route.argtypes = [sp, p, p, p, p, p, p, p, p]
+    lib.moe_route_random.argtypes = [sp, C.c_uint64, p, p, p, p, p, p, p]
     lib.moe_dispatch.argtypes = [sp, p, p, p, lp, p, p, p, C.c_size_t, p]
     lib.moe_expert_ffn.argtypes = [sp, p, lp, p, p, p, p, p, C.c_size_t, p]
     lib.moe_expert_ffn_bwd.argtypes = [sp, p, p, p, lp, p, p, p, p, p, p, C.c_size_t, p]
     lib.moe_combine.argtypes = [sp, p, p, lp, p, p]
     lib.moe_combine_bwd.argtypes = [sp, p, p, p, lp, p, p, p]
     lib.moe_dispatch_bwd.argtypes = [sp, p, lp, p, p]
-    for f in ("moe_workspace_size", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_bwd", "moe_combine",
+    for f in ("moe_workspace_size", "moe_route", "moe_route_random", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_bwd", "moe_combine",
               "moe_combine_bwd", "moe_dispatch_bwd"):
         getattr(lib, f).restype = i32
     lib.moe_status_string.argtypes = [i32]
@@ -209,6 +210,35 @@ def moe_route(logits: torch.Tensor, top_k: int, *, expert_bias: torch.Tensor | N
     _check(lib.moe_route(C.byref(shape), _ptr(logits), _ptr(expert_bias), _ptr(token_mask), _ptr(out.topk_idx),
                          _ptr(out.topk_w), _ptr(out.routing_map), _ptr(out.tokens_per_expert), _stream(dev)),
            "moe_route")
+    return out
+
+
+def moe_route_random(n_tokens: int, n_experts: int, top_k: int, seed: int, *, device="cuda",
+                     expert_bias: torch.Tensor | None = None, token_mask: torch.Tensor | None = None,
+                     routing_map: bool = True, counts: bool = True, out: RouteOut | None = None) -> RouteOut:
+    """Force-balanced router (include/moe.h moe_route_random): moe_route over uniform random
+    logits drawn from `seed` on the device."""
+    dev = torch.device(device)
+    n, e = int(n_tokens), int(n_experts)
+    if expert_bias is not None:
+        _contig(expert_bias, "expert_bias")
+        if expert_bias.dtype != torch.float32 or tuple(expert_bias.shape) != (e,):
+            raise TypeError("expert_bias must be a float32 [E] tensor")
+    if token_mask is not None:
+        if token_mask.dtype == torch.bool:
+            token_mask = token_mask.view(torch.uint8)
+        _contig(token_mask, "token_mask")
+        if token_mask.dtype != torch.uint8 or tuple(token_mask.shape) != (n,):
+            raise TypeError("token_mask must be a uint8 or bool [N] tensor")
+    if out is None:
+        out = RouteOut(torch.empty((n, top_k), dtype=torch.int32, device=dev),
+                       torch.empty((n, top_k), dtype=torch.float32, device=dev),
+                       torch.empty((n, e), dtype=torch.uint8, device=dev) if routing_map else None,
+                       torch.empty(e, dtype=torch.int32, device=dev) if counts else None)
+    shape = make_shape(n, 1, e, top_k, act_dtype=MOE_DT_F32)
+    _check(lib.moe_route_random(C.byref(shape), C.c_uint64(seed & (2 ** 64 - 1)), _ptr(expert_bias),
+                                _ptr(token_mask), _ptr(out.topk_idx), _ptr(out.topk_w), _ptr(out.routing_map),
+                                _ptr(out.tokens_per_expert), _stream(dev)), "moe_route_random")
     return out
 
 
@@ -368,7 +398,7 @@ def moe_combine_bwd(grad_out: torch.Tensor, y: torch.Tensor, topk_w: torch.Tenso
     return grad_y, grad_w
 
 
-__all__ = ["moe_route", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_bwd", "moe_combine", "moe_combine_bwd",
+__all__ = ["moe_route", "moe_route_random", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_bwd", "moe_combine", "moe_combine_bwd",
            "moe_dispatch_bwd",
            "Layout", "RouteOut",
            "MoeError", "make_shape", "workspace_size", "lib", "library_path", "EXPORTS"]

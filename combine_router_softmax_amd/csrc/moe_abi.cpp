@@ -125,8 +125,23 @@ moe_status moe_route(const moe_shape *s, const float *logits, const float *exper
   if (n > 0 && (!aligned4(logits) || !aligned4(topk_idx) || !aligned4(topk_w))) return MOE_ERR_MISALIGNED;
   if (tokens_per_expert && !aligned4(tokens_per_expert)) return MOE_ERR_MISALIGNED;
   if (expert_bias && !aligned4(expert_bias)) return MOE_ERR_MISALIGNED;
-  return hip_status(moe::launch_route(logits, expert_bias, token_mask, n, s->n_experts, s->top_k, topk_idx, topk_w, routing_map,
+  return hip_status(moe::launch_route(logits, 0, expert_bias, token_mask, n, s->n_experts, s->top_k, topk_idx, topk_w, routing_map,
                                       tokens_per_expert, as_stream(stream)));
+}
+
+moe_status moe_route_random(const moe_shape *s, uint64_t seed, const float *expert_bias, const uint8_t *token_mask,
+                            int32_t *topk_idx, float *topk_w, uint8_t *routing_map, int32_t *tokens_per_expert,
+                            void *stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (s->top_k > s->n_experts) return MOE_ERR_INVALID_ARG;
+  const int64_t n = s->n_tokens;
+  if (n > 0 && (!topk_idx || !topk_w)) return MOE_ERR_INVALID_ARG;
+  if (n > 0 && (!aligned4(topk_idx) || !aligned4(topk_w))) return MOE_ERR_MISALIGNED;
+  if (tokens_per_expert && !aligned4(tokens_per_expert)) return MOE_ERR_MISALIGNED;
+  if (expert_bias && !aligned4(expert_bias)) return MOE_ERR_MISALIGNED;
+  return hip_status(moe::launch_route(nullptr, seed, expert_bias, token_mask, n, s->n_experts, s->top_k, topk_idx,
+                                      topk_w, routing_map, tokens_per_expert, as_stream(stream)));
 }
 
 moe_status moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_idx, const float *topk_w,

@@ -9,9 +9,10 @@
 namespace moe {
 
 // ---- route (moe_route.hip)
-hipError_t launch_route(const float *logits, const float *expert_bias, const uint8_t *token_mask, int64_t n, int e,
-                        int k, int32_t *topk_idx, float *topk_w, uint8_t *routing_map, int32_t *tokens_per_expert,
-                        hipStream_t stream);
+// logits == nullptr: uniform random logits drawn from `seed` (force-balanced mode)
+hipError_t launch_route(const float *logits, uint64_t seed, const float *expert_bias, const uint8_t *token_mask,
+                        int64_t n, int e, int k, int32_t *topk_idx, float *topk_w, uint8_t *routing_map,
+                        int32_t *tokens_per_expert, hipStream_t stream);
 
 // ---- layout (moe_layout.hip)
 constexpr int kLayoutTile = 2048;  // assignments per layout tile

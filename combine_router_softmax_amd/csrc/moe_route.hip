@@ -15,7 +15,9 @@
 // dispatch).  An optional per-expert bias enters the selection only: experts
 // are ranked by logit + bias, the weights come from the logits (Megatron's
 // load-balancing expert bias, which "Integrate UltraEP Runtime" lists as not
-// yet supported there).
+// yet supported there).  Without logits, the force-balanced benchmark mode of
+// "Integrate UltraEP Runtime" routes by uniform random logits drawn from a
+// counter-based generator (Philox4x32-10) keyed by a seed.
 // Counts: when the routing map is written (E % 16 == 0), a second kernel takes
 // its column sums in a few dozen workgroups, one global atomic per expert and
 // workgroup; otherwise each router workgroup adds its LDS histogram with global
@@ -41,6 +43,39 @@ __device__ __forceinline__ uint32_t logit_key(float v) {
 __device__ __forceinline__ float key_logit(uint32_t key) {
   if (key == 0u) return __uint_as_float(0x7FC00000u);
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel Random Numbers: As
+// Easy as 1, 2, 3", SC 2011): ten rounds of two 32x32 -> 64-bit products, the
+// key bumped by two Weyl constants between rounds.  Returns word `word` of the
+// output block of counter (c0, c1, c2, 0) under key (k0, k1).
+__device__ __forceinline__ uint32_t philox_word(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t k0, uint32_t k1,
+                                                int word) {
+  uint32_t c3 = 0u;
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = 0xD2511F53u * c0, hi0 = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo1 = 0xCD9E8D57u * c2, hi1 = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo1;
+    c2 = n2;
+    c3 = lo0;
+  }
+  return word == 0 ? c0 : word == 1 ? c1 : word == 2 ? c2 : c3;
+}
+
+// Force-balanced mode: the logit of token t and expert x is the uniform number
+// (w >> 8) * 2^-24 in [0, 1), exact in fp32, w = word x % 4 of the Philox block
+// of counter (x / 4, t mod 2^32, t / 2^32) under the 64-bit seed.
+__device__ __forceinline__ float random_logit(int64_t t, int x, uint64_t seed) {
+  const uint32_t w = philox_word((uint32_t)(x >> 2), (uint32_t)t, (uint32_t)((uint64_t)t >> 32), (uint32_t)seed,
+                                 (uint32_t)(seed >> 32), x & 3);
+  return (float)(w >> 8) * (1.0f / 16777216.0f);
 }
 
 __global__ void fill_i32(int32_t *p, int64_t n, int32_t v) {
@@ -83,7 +118,8 @@ __global__ __launch_bounds__(kRouteThreads) void count_map_kernel(const uint8_t 
 }
 
 template <int VPL>
-__global__ __launch_bounds__(kRouteThreads) void route_kernel(const float *__restrict__ logits,
+// logits == nullptr: the force-balanced mode, logits drawn from `seed`.
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const float *__restrict__ logits, uint64_t seed,
                                                               const float *__restrict__ expert_bias,
                                                               const uint8_t *__restrict__ token_mask, int64_t n, int e,
                                                               int k, int32_t *__restrict__ topk_idx,
@@ -117,13 +153,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float *__res
     if (routing_map)
       for (int x = l; x < e; x += kWave) routing_map[t * e + x] = 0;
   } else if (t < n) {
-    const float *row = logits + t * e;
+    const float *row = logits ? logits + t * e : nullptr;
+    auto logit = [&](int x) { return row ? row[x] : random_logit(t, x, seed); };
     uint64_t key[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
       const int x = l + kWave * i;
       // selection score: the logit, plus the expert's bias when one is given
-      const float sc = x < e ? (expert_bias ? row[x] + expert_bias[x] : row[x]) : 0.0f;
+      const float lx = x < e ? logit(x) : 0.0f;
+      const float sc = expert_bias && x < e ? lx + expert_bias[x] : lx;
       key[i] = x < e ? ((uint64_t)logit_key(sc) << 32) | (uint32_t)~(uint32_t)x : 0ull;
     }
     uint32_t taken = 0;
@@ -160,15 +198,15 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float *__res
       // the bias only selects: the weights come from the chosen experts' logits,
       // relative to the largest of them
       float lmax = -INFINITY;
-      for (int j = l; j < k; j += kWave) lmax = fmaxf(lmax, row[sel_idx[j]]);
+      for (int j = l; j < k; j += kWave) lmax = fmaxf(lmax, logit(sel_idx[j]));
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) lmax = fmaxf(lmax, __shfl_xor(lmax, off, kWave));
       float part = 0.0f;
-      for (int j = l; j < k; j += kWave) part += expf(row[sel_idx[j]] - lmax);
+      for (int j = l; j < k; j += kWave) part += expf(logit(sel_idx[j]) - lmax);
       const float denom = wave_sum_f32(part);
       for (int j = l; j < k; j += kWave) {
         topk_idx[t * k + j] = sel_idx[j];
-        topk_w[t * k + j] = expf(row[sel_idx[j]] - lmax) / denom;
+        topk_w[t * k + j] = expf(logit(sel_idx[j]) - lmax) / denom;
       }
     }
     if (routing_map) {
@@ -192,21 +230,21 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float *__res
 }
 
 template <int VPL>
-hipError_t launch_route_vpl(const float *logits, const float *expert_bias, const uint8_t *token_mask, int64_t n,
-                            int e, int k, int32_t *topk_idx, float *topk_w, uint8_t *routing_map,
+hipError_t launch_route_vpl(const float *logits, uint64_t seed, const float *expert_bias, const uint8_t *token_mask,
+                            int64_t n, int e, int k, int32_t *topk_idx, float *topk_w, uint8_t *routing_map,
                             int32_t *tokens_per_expert, int32_t *zero_counts, hipStream_t stream) {
   const int64_t blocks = (n + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock;
   const size_t lds = sizeof(uint32_t) * (2 * kRouteTokensPerBlock * (size_t)k + (size_t)e);
-  hipLaunchKernelGGL(route_kernel<VPL>, dim3((unsigned)blocks), dim3(kRouteThreads), lds, stream, logits,
+  hipLaunchKernelGGL(route_kernel<VPL>, dim3((unsigned)blocks), dim3(kRouteThreads), lds, stream, logits, seed,
                      expert_bias, token_mask, n, e, k, topk_idx, topk_w, routing_map, tokens_per_expert, zero_counts);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_route(const float *logits, const float *expert_bias, const uint8_t *token_mask, int64_t n, int e,
-                        int k, int32_t *topk_idx, float *topk_w, uint8_t *routing_map, int32_t *tokens_per_expert,
-                        hipStream_t stream) {
+hipError_t launch_route(const float *logits, uint64_t seed, const float *expert_bias, const uint8_t *token_mask,
+                        int64_t n, int e, int k, int32_t *topk_idx, float *topk_w, uint8_t *routing_map,
+                        int32_t *tokens_per_expert, hipStream_t stream) {
   const bool map_counts = n > 0 && tokens_per_expert && routing_map && e % 16 == 0 &&
                           (reinterpret_cast<uintptr_t>(routing_map) & 15u) == 0;
   if (tokens_per_expert && !map_counts) {  // the router kernel adds into zeroed counts
@@ -220,7 +258,7 @@ hipError_t launch_route(const float *logits, const float *expert_bias, const uin
   int32_t *zero_counts = map_counts ? tokens_per_expert : nullptr;
   hipError_t st;
 #define MOE_ROUTE(V) \
-  launch_route_vpl<V>(logits, expert_bias, token_mask, n, e, k, topk_idx, topk_w, routing_map, kernel_counts, \
+  launch_route_vpl<V>(logits, seed, expert_bias, token_mask, n, e, k, topk_idx, topk_w, routing_map, kernel_counts, \
                       zero_counts, stream)
   if (e <= 64) st = MOE_ROUTE(1);
   else if (e <= 128) st = MOE_ROUTE(2);

@@ -2,6 +2,7 @@
  * moe.h -- C ABI of the MI355X (gfx950) single-GPU Mixture-of-Experts path:
  *
  *   moe_route       router softmax / top-k / renormalise / multihot map / counts
+ *   moe_route_random the same over random logits (force-balanced benchmark mode)
  *   moe_dispatch    per-expert histogram + prefix sum, stable per-expert ordinals,
  *                   capacity drop/pad masks, row scatter into expert-contiguous rows
  *   moe_expert_ffn  grouped SwiGLU expert GEMM (bf16 MFMA, fp32 accumulation)
@@ -143,6 +144,20 @@ moe_status moe_workspace_size(moe_op op, const moe_shape *s, size_t *bytes);
 moe_status moe_route(const moe_shape *s, const float *logits, const float *expert_bias, const uint8_t *token_mask,
                      int32_t *topk_idx, float *topk_w, uint8_t *routing_map, int32_t *tokens_per_expert,
                      void *stream);
+
+/* Force-balanced router: moe_route with random instead of given logits (the
+ * force-balanced router benchmark mode of the UltraEP pull request "Integrate
+ * UltraEP Runtime": random-logits routing, so that every expert receives about
+ * N*k/E assignments, the reference point of its throughput tables).  The logit
+ * of token t and expert x is (w >> 8) * 2^-24, uniform in [0, 1) and exact in
+ * fp32, where w is 32-bit word x % 4 of the Philox4x32-10 block (Salmon et al.,
+ * "Parallel Random Numbers: As Easy as 1, 2, 3") of counter
+ * (x / 4, t mod 2^32, t / 2^32, 0) under key (seed mod 2^32, seed / 2^32).
+ * Everything else -- selection, weights, map, counts, expert_bias, token_mask,
+ * errors -- is as moe_route. */
+moe_status moe_route_random(const moe_shape *s, uint64_t seed, const float *expert_bias, const uint8_t *token_mask,
+                            int32_t *topk_idx, float *topk_w, uint8_t *routing_map, int32_t *tokens_per_expert,
+                            void *stream);
 
 /* Dispatch: local permutation of token rows into expert-contiguous rows
  * ("Megatron MoE 实现", dispatch_preprocess / dispatch_postprocess ->

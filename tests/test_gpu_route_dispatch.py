@@ -109,6 +109,35 @@ def test_route_expert_bias_balances_skewed_logits(moe):
     assert tpe.max() < skewed.max() / 4                  # 4096 for the hottest expert without the bias
 
 
+@pytest.mark.parametrize("n,e,k,seed", [(4096, 256, 8, 1), (8192, 128, 8, 2 ** 40 + 3), (777, 100, 7, 0),
+                                         (64, 8, 2, 2 ** 64 - 1), (300, 1000, 70, 5)])
+def test_route_random_force_balanced(moe, n, e, k, seed):
+    """The device-drawn logits and everything derived from them equal the oracle's."""
+    r = moe.moe_route_random(n, e, k, seed)
+    torch.cuda.synchronize()
+    idx, w, rmap, tpe = oracle.route_random(n, e, k, seed)
+    np.testing.assert_array_equal(host(r.topk_idx), idx)
+    np.testing.assert_array_equal(host(r.routing_map), rmap)
+    np.testing.assert_array_equal(host(r.tokens_per_expert), tpe)
+    assert max_rel_err(host(r.topk_w), w) <= TOL_F32
+    if n * k >= 32 * e:                                  # balanced: no expert far from N*k/E
+        m = n * k / e
+        assert tpe.max() < m + 6 * np.sqrt(m) and tpe.min() > m - 6 * np.sqrt(m)
+
+
+def test_route_random_with_bias_and_mask(moe):
+    g = np.random.default_rng(3)
+    n, e, k = 1000, 64, 4
+    bias = (g.standard_normal(e) * 0.1).astype(np.float32)
+    mask = (g.random(n) < 0.2).astype(np.uint8)
+    r = moe.moe_route_random(n, e, k, 99, expert_bias=dev(bias), token_mask=dev(mask))
+    torch.cuda.synchronize()
+    idx, w, rmap, tpe = oracle.route_random(n, e, k, 99, mask, bias)
+    np.testing.assert_array_equal(host(r.topk_idx), idx)
+    np.testing.assert_array_equal(host(r.tokens_per_expert), tpe)
+    assert max_rel_err(host(r.topk_w), w) <= TOL_F32
+
+
 def test_route_token_mask_through_the_layer(moe):
     """masked route -> dispatch -> combine: padding tokens are not dispatched and get zero rows."""
     w = mi.workload(2, n_tokens=512)
