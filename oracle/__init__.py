@@ -54,7 +54,7 @@ def lib():
         L.oracle_random_logits.restype = None
         L.oracle_layout_rows.argtypes = [i64, i32, i32, i32, i64, i32]
         L.oracle_layout_rows.restype = i64
-        L.oracle_layout.argtypes = [i64, i32, i32, i32, i64, i32, p, p, p, p, p, p, p, p, p]
+        L.oracle_layout.argtypes = [i64, i32, i32, i32, i64, i32, i32, p, p, p, p, p, p, p, p, p, p]
         L.oracle_layout.restype = i32
         L.oracle_scatter.argtypes = [i64, i32, i64, p, p, p, i64, p, i64, p, p]
         L.oracle_scatter.restype = None
@@ -130,9 +130,14 @@ def route_random(n: int, e: int, k: int, seed: int, token_mask=None, expert_bias
     return route(random_logits(n, e, seed), k, token_mask, expert_bias)
 
 
-def layout(topk_idx: np.ndarray, n_experts: int, capacity: int = 0, max_rows: int = 0, row_align: int = 0) -> dict:
-    """Dispatch layout; returns a dict of numpy arrays (see moe_oracle.c oracle_layout)."""
+def layout(topk_idx: np.ndarray, n_experts: int, capacity: int = 0, max_rows: int = 0, row_align: int = 0,
+           drop_policy: int = 0, topk_w=None) -> dict:
+    """Dispatch layout; returns a dict of numpy arrays (see moe_oracle.c oracle_layout).
+    drop_policy 1 (capacity only) keeps each expert's C largest weights topk_w."""
     topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    w = None if topk_w is None else np.ascontiguousarray(topk_w, dtype=np.float32)
+    if drop_policy == 1 and capacity > 0:
+        assert w is not None and w.shape == topk_idx.shape
     n, k = topk_idx.shape
     rows = lib().oracle_layout_rows(n, k, n_experts, capacity, max_rows, row_align)
     out = dict(
@@ -145,7 +150,7 @@ def layout(topk_idx: np.ndarray, n_experts: int, capacity: int = 0, max_rows: in
         pad_mask=np.empty(rows, np.uint8),
         counters=np.empty(4, np.int32),
     )
-    rc = lib().oracle_layout(n, k, n_experts, capacity, max_rows, row_align, _p(topk_idx),
+    rc = lib().oracle_layout(n, k, n_experts, capacity, max_rows, row_align, drop_policy, _p(topk_idx), _p(w),
                              *[_p(out[f]) for f in ("tokens_per_expert", "expert_offsets", "ordinal",
                                                     "assign_row", "row_src", "drop_mask", "pad_mask", "counters")])
     if rc != 0:

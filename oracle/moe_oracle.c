@@ -218,12 +218,32 @@ int64_t oracle_layout_rows(int64_t n, int k, int e, int capacity, int64_t max_ro
  *    maps / FP8 padding: every expert's segment starts on an aligned row),
  *    clipped to the row budget; assignments past the budget are dropped; the
  *    rows between an expert's kept rows and the next segment are pad rows.
- *  - assign_row[a] = offset[e] + ordinal[a] when kept, else -1.
+ *  - drop_policy (capacity only): 0 keeps the first C assignments of an
+ *    expert by position, as above; 1 keeps the C with the largest weights
+ *    topk_w[a] (ties: the earlier assignment; NaN below every number),
+ *    Megatron's "probs" token-drop policy.
+ *  - assign_row[a] = offset[e] + (the number of kept assignments of e before a)
+ *    when kept, else -1 (= offset[e] + ordinal[a] under the position policy).
  *  - row_src[r] = the assignment placed in row r, else -1; pad_mask[r] = 1 for
  *    every row that holds no assignment (capacity pad or unused tail).
  *  - counters = {kept, dropped, pad rows (capacity or alignment), invalid ids}. */
-int oracle_layout(int64_t n, int k, int e, int capacity, int64_t max_rows, int row_align, const int32_t *topk_idx,
-                  int32_t *tokens_per_expert, int32_t *expert_offsets, int32_t *ordinal,
+/* Drop-policy order of two assignments of one expert: the larger weight first,
+ * NaN after every number, -0.0 == +0.0; equal weights keep position order. */
+static const float *g_sort_w;
+static int by_weight_desc(const void *pa, const void *pb) {
+  const int64_t a = *(const int64_t *)pa, b = *(const int64_t *)pb;
+  const float va = g_sort_w[a], vb = g_sort_w[b];
+  const int na = isnan(va), nb = isnan(vb);
+  if (na != nb) return na ? 1 : -1;
+  if (!na) {
+    if (va > vb) return -1;
+    if (va < vb) return 1;
+  }
+  return a < b ? -1 : (a > b ? 1 : 0);
+}
+
+int oracle_layout(int64_t n, int k, int e, int capacity, int64_t max_rows, int row_align, int drop_policy,
+                  const int32_t *topk_idx, const float *topk_w, int32_t *tokens_per_expert, int32_t *expert_offsets, int32_t *ordinal,
                   int32_t *assign_row, int32_t *row_src, uint8_t *drop_mask, uint8_t *pad_mask,
                   int32_t *counters) {
   if (n < 0 || k < 1 || e < 1) return -1;
@@ -259,6 +279,25 @@ int oracle_layout(int64_t n, int k, int e, int capacity, int64_t max_rows, int r
       kept[x] = count[x] < room ? count[x] : room;
     }
   }
+  /* keep[a]: under the probs policy, sort each over-full expert's assignments
+   * by weight and keep the first C; otherwise keep by position (ordinal < kept) */
+  uint8_t *keep = NULL;
+  if (capacity > 0 && drop_policy == 1) {
+    keep = (uint8_t *)calloc((size_t)(a_total > 0 ? a_total : 1), 1);
+    int64_t *list = (int64_t *)malloc(sizeof(int64_t) * (size_t)(a_total > 0 ? a_total : 1));
+    if (!keep || !list) { free(keep); free(list); free(count); free(seen); free(kept); return -2; }
+    g_sort_w = topk_w;
+    for (int x = 0; x < e; ++x) {
+      int64_t m = 0;
+      for (int64_t a = 0; a < a_total; ++a)
+        if (topk_idx[a] == x) list[m++] = a;
+      if (m > capacity) qsort(list, (size_t)m, sizeof(int64_t), by_weight_desc);
+      for (int64_t i = 0; i < m && i < capacity; ++i) keep[list[i]] = 1;
+    }
+    free(list);
+  }
+  int64_t *placed = (int64_t *)calloc((size_t)e, sizeof(int64_t));
+  if (!placed) { free(keep); free(count); free(seen); free(kept); return -2; }
   for (int64_t r = 0; r < rows; ++r) { row_src[r] = -1; pad_mask[r] = 1; }
   int64_t dropped = 0, kept_total = 0;
   for (int64_t a = 0; a < a_total; ++a) {
@@ -267,8 +306,8 @@ int oracle_layout(int64_t n, int k, int e, int capacity, int64_t max_rows, int r
     if (x < 0 || x >= e) { ordinal[a] = -1; assign_row[a] = -1; continue; }
     int64_t o = seen[x]++;
     ordinal[a] = (int32_t)o;
-    if (o < kept[x]) {
-      int64_t r = expert_offsets[x] + o;
+    if (keep ? keep[a] : o < kept[x]) {
+      int64_t r = expert_offsets[x] + placed[x]++;
       assign_row[a] = (int32_t)r;
       row_src[r] = (int32_t)a;
       pad_mask[r] = 0;
@@ -279,6 +318,8 @@ int oracle_layout(int64_t n, int k, int e, int capacity, int64_t max_rows, int r
       ++dropped;
     }
   }
+  free(keep);
+  free(placed);
   for (int x = 0; x < e; ++x) tokens_per_expert[x] = (int32_t)kept[x];
   counters[0] = (int32_t)kept_total;
   counters[1] = (int32_t)dropped;

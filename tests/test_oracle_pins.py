@@ -49,7 +49,7 @@ def bf_weights(row: np.ndarray, sel):
     return [x / s for x in ex]
 
 
-def bf_layout(idx: np.ndarray, e: int, capacity: int, max_rows: int, row_align: int = 0):
+def bf_layout(idx: np.ndarray, e: int, capacity: int, max_rows: int, row_align: int = 0, probs=None):
     """Permutation by a comparison sort on (expert, assignment); ordinals by the
     segment-start / running-max construction over the expert-sorted list; with a
     row alignment A, dropless segments are the counts rounded up to multiples of A."""
@@ -83,12 +83,30 @@ def bf_layout(idx: np.ndarray, e: int, capacity: int, max_rows: int, row_align: 
         kept = np.minimum(counts, rows - offsets[:-1])
     assign_row = np.full(a_total, -1, np.int64)
     drop = np.zeros(a_total, np.uint8)
-    for a in valid:
-        ex = flat[a]
-        if ordinal[a] < kept[ex]:
-            assign_row[a] = offsets[ex] + ordinal[a]
-        else:
-            drop[a] = 1
+    if probs is not None and capacity > 0:
+        # keep each expert's C largest weights (NaN last, ties by position), rows in position order
+        wf = probs.reshape(-1)
+        keepset = set()
+        for ex in range(e):
+            mine = [a for a in valid if flat[a] == ex]
+            rank = sorted(mine, key=lambda a: (1 if math.isnan(wf[a]) else 0,
+                                               0.0 if math.isnan(wf[a]) else -(float(wf[a]) + 0.0), a))
+            keepset |= set(rank[:capacity])
+        placed = np.zeros(e, np.int64)
+        for a in valid:
+            ex = flat[a]
+            if a in keepset:
+                assign_row[a] = offsets[ex] + placed[ex]
+                placed[ex] += 1
+            else:
+                drop[a] = 1
+    else:
+        for a in valid:
+            ex = flat[a]
+            if ordinal[a] < kept[ex]:
+                assign_row[a] = offsets[ex] + ordinal[a]
+            else:
+                drop[a] = 1
     row_src = np.full(rows, -1, np.int64)
     for a in valid:
         if assign_row[a] >= 0:
@@ -416,6 +434,64 @@ def test_layout_row_align_closed_forms():
     for al in (0, 1):
         np.testing.assert_array_equal(oracle.layout(idx, 3, row_align=al)["assign_row"],
                                       oracle.layout(idx, 3)["assign_row"])
+
+
+@pytest.mark.parametrize("trial", range(30))
+def test_layout_probs_drop_policy_brute_force(trial):
+    """Capacity with the probability drop policy: each expert keeps its C largest weights."""
+    g = np.random.default_rng(6000 + trial)
+    e = int(g.integers(1, 9))
+    k = int(g.integers(1, min(e, 4) + 1))
+    n = int(g.integers(0, 65))
+    idx = np.stack([g.permutation(e)[:k] for _ in range(n)]).astype(np.int32).reshape(n, k)
+    if n:
+        idx[g.random(idx.shape) < 0.1] = -1
+    w = g.random((n, k)).astype(np.float32)
+    if trial % 3 == 0 and n:
+        w = np.round(w * 4).astype(np.float32) / 4       # many equal weights: position breaks the ties
+    if trial % 5 == 0 and n:
+        w[g.random(w.shape) < 0.1] = np.nan
+    cap = int(g.integers(1, 6))
+    got = oracle.layout(idx, e, cap, drop_policy=1, topk_w=w)
+    ref = bf_layout(idx, e, cap, 0, probs=w)
+    for f in ("ordinal", "assign_row", "drop_mask", "row_src", "pad_mask", "tokens_per_expert",
+              "expert_offsets", "counters"):
+        np.testing.assert_array_equal(got[f], ref[f], err_msg=f)
+    # the same counts, offsets and pads as the position policy; only which assignments are kept differs
+    pos = oracle.layout(idx, e, cap)
+    for f in ("tokens_per_expert", "expert_offsets", "counters", "pad_mask", "ordinal"):
+        np.testing.assert_array_equal(got[f], pos[f], err_msg=f)
+
+
+def test_layout_probs_drop_policy_skewed_workload_invariants():
+    """Zipf-skewed routing with capacity 160: every over-full expert's kept weights are
+    all at least its dropped ones, and the kept rows stay in assignment order."""
+    w = mi.workload(3)
+    idx, wts, _, _ = oracle.route(mi.router_logits(w), w.top_k)
+    got = oracle.layout(idx, w.n_experts, w.capacity, drop_policy=1, topk_w=wts)
+    flat, wf = idx.reshape(-1), wts.reshape(-1)
+    kept = got["assign_row"] >= 0
+    for ex in range(w.n_experts):
+        mine = flat == ex
+        if mine.sum() <= w.capacity:
+            assert kept[mine].all()
+            continue
+        assert kept[mine].sum() == w.capacity
+        assert wf[mine & kept].min() >= wf[mine & ~kept].max()
+        seg = got["row_src"][ex * w.capacity:(ex + 1) * w.capacity]
+        assert (np.diff(seg) > 0).all()
+
+
+def test_layout_probs_drop_policy_closed_form():
+    # one expert, capacity 2, weights 0.1 0.9 0.5 0.9: keeps assignments 1 and 3 (ties by position)
+    idx = np.zeros((4, 1), np.int32)
+    w = np.array([[0.1], [0.9], [0.5], [0.9]], np.float32)
+    got = oracle.layout(idx, 1, 2, drop_policy=1, topk_w=w)
+    assert got["assign_row"].tolist() == [-1, 0, -1, 1] and got["drop_mask"].tolist() == [1, 0, 1, 0]
+    assert got["row_src"].tolist() == [1, 3] and got["ordinal"].tolist() == [0, 1, 2, 3]
+    # under capacity every assignment is kept, as with the position policy
+    got = oracle.layout(idx, 1, 4, drop_policy=1, topk_w=w)
+    assert got["assign_row"].tolist() == [0, 1, 2, 3]
 
 
 def test_layout_all_to_one_expert_and_capacity_one():
