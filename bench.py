@@ -181,6 +181,46 @@ def bench_dispatch_combine(moe, mi, torch, steps, warmup):
                 n=n, k=k, e=e, h=h)
 
 
+def bench_skewed_capacity(moe, mi, torch, steps, warmup):
+    """Dispatch + combine at the Zipf-skewed workload with capacity 160 (many drops and
+    pads), dropping by position and by weight: -> dict of us and algorithmic bytes."""
+    import numpy as np
+    w = mi.workload(3)
+    logits = torch.from_numpy(mi.router_logits(w)).cuda()
+    x_np = mi.activations(w)
+    x = torch.from_numpy(x_np.view(np.int16)).cuda().view(torch.bfloat16)
+    n, k, e, h = w.n_tokens, w.top_k, w.n_experts, w.hidden
+    r = moe.moe_route(logits, k)
+    out = torch.empty_like(x)
+    res = {}
+    for name, policy in (("position", moe.MOE_DROP_POSITION), ("probs", moe.MOE_DROP_PROBS)):
+        xp, wp, lay = moe.moe_dispatch(x, r.topk_idx, r.topk_w, e, capacity=w.capacity, drop_policy=policy)
+        shape = lay.shape(h, moe.MOE_DT_BF16)
+        ws = torch.empty(moe.workspace_size(moe.MOE_OP_DISPATCH, shape) + 256, dtype=torch.uint8, device=x.device)
+        run_d = lambda: moe.moe_dispatch(x, r.topk_idx, r.topk_w, e, capacity=w.capacity, drop_policy=policy,
+                                         layout=lay, x_perm=xp, w_perm_out=wp, workspace=ws)
+        for _ in range(warmup):
+            run_d()
+            moe.moe_combine(xp, r.topk_w, lay, out=out)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        ev[0].record()
+        for _ in range(steps):
+            run_d()
+        ev[1].record()
+        for _ in range(steps):
+            moe.moe_combine(xp, r.topk_w, lay, out=out)
+        ev[2].record()
+        torch.cuda.synchronize()
+        cnt = lay.counters.cpu().tolist()
+        kept, pads = cnt[0], cnt[2]
+        row_b = h * 2
+        res[name] = dict(dispatch_us=ev[0].elapsed_time(ev[1]) / steps * 1e3,
+                         combine_us=ev[1].elapsed_time(ev[2]) / steps * 1e3, kept=kept, dropped=cnt[1], pads=pads,
+                         dispatch_bytes=n * row_b + (kept + pads) * row_b, combine_bytes=kept * row_b + n * row_b)
+    return res
+
+
 def bench_expert_gemm(moe, mi, torch, wid, iters, warmup, bwd_iters=0):
     import numpy as np
     w = mi.workload(wid)
@@ -384,6 +424,8 @@ def main():
     torch.cuda.set_device(0)
     log("dispatch+combine: uniform workload N=4096 H=7168 E=256 k=8")
     dc = bench_dispatch_combine(moe, mi, torch, args.steps, args.warmup)
+    log("dispatch+combine: Zipf-skewed workload with capacity 160, both drop policies")
+    skew = bench_skewed_capacity(moe, mi, torch, 20, 3)
     gemm = []
     if not args.skip_gemm:
         for wid in (4, 5):
@@ -434,6 +476,11 @@ def main():
         "dispatch_combine_frac_of_copy": round(byts / ((dc["dispatch_ms"] + dc["combine_ms"]) * 1e-3) / 1e9
                                                / dc["copy_gbs"], 4),
         "route_force_balanced_us": round(dc["route_random_ms"] * 1e3, 2),
+        "zipf_capacity": {p: {"dispatch_us": round(v["dispatch_us"], 2), "combine_us": round(v["combine_us"], 2),
+                              "dispatch_gbs": round(v["dispatch_bytes"] / v["dispatch_us"] / 1e3, 1),
+                              "combine_gbs": round(v["combine_bytes"] / v["combine_us"] / 1e3, 1),
+                              "kept": v["kept"], "dropped": v["dropped"], "pad_rows": v["pads"]}
+                          for p, v in skew.items()},
         "dispatch_bwd_us": round(dc["dbwd_ms"] * 1e3, 2),
         "dispatch_bwd_gbs": round(dc["combine_bytes"] / (dc["dbwd_ms"] * 1e-3) / 1e9, 2),
         "combine_bwd_us": round(dc["bwd_ms"] * 1e3, 2),

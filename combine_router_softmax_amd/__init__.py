@@ -21,6 +21,7 @@ _LIB_PATH = Path(__file__).resolve().parent / "libmoe_mi355x.so"
 
 MOE_DT_F32 = 0
 MOE_DT_BF16 = 1
+MOE_DROP_POSITION, MOE_DROP_PROBS = 0, 1
 MOE_OP_ROUTE, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE, MOE_OP_COMBINE_BWD, MOE_OP_EXPERT_FFN_BWD = range(6)
 
 # Every symbol include/moe.h declares.
@@ -32,7 +33,7 @@ EXPORTS = ("moe_layout_rows", "moe_workspace_size", "moe_route", "moe_route_rand
 class MoeShape(C.Structure):
     _fields_ = [("n_tokens", C.c_int64), ("hidden", C.c_int64), ("n_experts", C.c_int32), ("top_k", C.c_int32),
                 ("capacity", C.c_int32), ("inter", C.c_int32), ("max_rows", C.c_int64), ("act_dtype", C.c_int32),
-                ("row_align", C.c_int32)]
+                ("row_align", C.c_int32), ("drop_policy", C.c_int32), ("reserved", C.c_int32)]
 
 
 class MoeLayoutC(C.Structure):
@@ -109,9 +110,9 @@ def _contig(t: torch.Tensor, name: str):
 
 
 def make_shape(n_tokens, hidden, n_experts, top_k, capacity=0, inter=0, max_rows=0, act_dtype=MOE_DT_BF16,
-               row_align=0):
+               row_align=0, drop_policy=MOE_DROP_POSITION):
     return MoeShape(int(n_tokens), int(hidden), int(n_experts), int(top_k), int(capacity), int(inter), int(max_rows),
-                    int(act_dtype), int(row_align))
+                    int(act_dtype), int(row_align), int(drop_policy), 0)
 
 
 def workspace_size(op: int, shape: MoeShape) -> int:
@@ -159,16 +160,18 @@ class Layout:
     pad_mask: torch.Tensor
     counters: torch.Tensor
     row_align: int = 0
+    drop_policy: int = MOE_DROP_POSITION
 
     @staticmethod
-    def empty(n_tokens, top_k, n_experts, capacity, rows, device, row_align=0) -> "Layout":
+    def empty(n_tokens, top_k, n_experts, capacity, rows, device, row_align=0,
+              drop_policy=MOE_DROP_POSITION) -> "Layout":
         i32 = dict(dtype=torch.int32, device=device)
         u8 = dict(dtype=torch.uint8, device=device)
         a = n_tokens * top_k
         return Layout(n_tokens, top_k, n_experts, capacity, rows, torch.empty(n_experts, **i32),
                       torch.empty(n_experts + 1, **i32), torch.empty(a, **i32), torch.empty(a, **i32),
                       torch.empty(rows, **i32), torch.empty(a, **u8), torch.empty(rows, **u8), torch.empty(4, **i32),
-                      row_align)
+                      row_align, drop_policy)
 
     def c(self) -> MoeLayoutC:
         return MoeLayoutC(*[t.data_ptr() for t in (self.tokens_per_expert, self.expert_offsets, self.ordinal,
@@ -177,7 +180,7 @@ class Layout:
 
     def shape(self, hidden, act_dtype, inter=0) -> MoeShape:
         return make_shape(self.n_tokens, hidden, self.n_experts, self.top_k, self.capacity, inter,
-                          0 if self.capacity > 0 else self.rows, act_dtype, self.row_align)
+                          0 if self.capacity > 0 else self.rows, act_dtype, self.row_align, self.drop_policy)
 
 
 def moe_route(logits: torch.Tensor, top_k: int, *, expert_bias: torch.Tensor | None = None,
@@ -243,23 +246,24 @@ def moe_route_random(n_tokens: int, n_experts: int, top_k: int, seed: int, *, de
 
 
 def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor | None, n_experts: int, *,
-                 capacity: int = 0, max_rows: int = 0, row_align: int = 0, w_perm: bool = True,
-                 layout: Layout | None = None, x_perm: torch.Tensor | None = None,
+                 capacity: int = 0, max_rows: int = 0, row_align: int = 0, drop_policy: int = MOE_DROP_POSITION,
+                 w_perm: bool = True, layout: Layout | None = None, x_perm: torch.Tensor | None = None,
                  w_perm_out: torch.Tensor | None = None, workspace=None):
     """Layout + row scatter (include/moe.h moe_dispatch) -> (x_perm, w_perm, layout).
-    row_align: dropless segments rounded up to multiples of this many rows (0: none)."""
+    row_align: dropless segments rounded up to multiples of this many rows (0: none);
+    drop_policy: which assignments an over-full expert keeps with a capacity."""
     _contig(x, "x")
     _contig(topk_idx, "topk_idx")
     n, h = x.shape
     k = topk_idx.shape[1]
     dev = x.device
     dt = _act_dtype(x)
-    shape = make_shape(n, h, n_experts, k, capacity, 0, max_rows, dt, row_align)
+    shape = make_shape(n, h, n_experts, k, capacity, 0, max_rows, dt, row_align, drop_policy)
     rows = int(lib.moe_layout_rows(C.byref(shape)))
     if rows < 0:
         _check(-1, "moe_dispatch")
     if layout is None:
-        layout = Layout.empty(n, k, n_experts, capacity, rows, dev, row_align)
+        layout = Layout.empty(n, k, n_experts, capacity, rows, dev, row_align, drop_policy)
     if x_perm is None:
         x_perm = torch.empty((rows, h), dtype=x.dtype, device=dev)
     if w_perm and w_perm_out is None:

@@ -25,10 +25,15 @@ moe_status check_shape(const moe_shape *s) {
   if (s->act_dtype != MOE_DT_F32 && s->act_dtype != MOE_DT_BF16) return MOE_ERR_INVALID_ARG;
   if (s->row_align < 0 || s->row_align > kMaxRowAlign || (s->row_align & (s->row_align - 1)) != 0)
     return MOE_ERR_INVALID_ARG;
+  if ((s->drop_policy != MOE_DROP_POSITION && s->drop_policy != MOE_DROP_PROBS) || s->reserved != 0)
+    return MOE_ERR_INVALID_ARG;
   if (s->n_experts > kMaxExperts) return MOE_ERR_UNSUPPORTED;
   if (s->n_tokens > kMaxIndex / s->top_k) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
+
+// Capacity drops by weight (else by position).
+bool by_weight(const moe_shape *s) { return s->capacity > 0 && s->drop_policy == MOE_DROP_PROBS; }
 
 int64_t rows_of(const moe_shape *s) {
   if (s->capacity > 0) return (int64_t)s->n_experts * s->capacity;
@@ -100,7 +105,7 @@ moe_status moe_workspace_size(moe_op op, const moe_shape *s, size_t *bytes) {
       *bytes = 0;
       return MOE_OK;
     case MOE_OP_DISPATCH:
-      *bytes = moe::layout_workspace_bytes(s->n_tokens * s->top_k, s->n_experts);
+      *bytes = moe::layout_workspace_bytes(s->n_tokens * s->top_k, s->n_experts, by_weight(s));
       return MOE_OK;
     case MOE_OP_EXPERT_FFN:
       if (s->inter < 1) return MOE_ERR_INVALID_ARG;
@@ -159,11 +164,13 @@ moe_status moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_i
       (w_perm && a > 0 && !topk_w))
     return MOE_ERR_INVALID_ARG;
   if (!need(x, n, aligned16) || !need(x_perm, rows, aligned16)) return MOE_ERR_MISALIGNED;
-  const size_t need_ws = moe::layout_workspace_bytes(a, s->n_experts);
+  if (by_weight(s) && a > 0 && !topk_w) return MOE_ERR_INVALID_ARG;  // the policy ranks the weights
+  const size_t need_ws = moe::layout_workspace_bytes(a, s->n_experts, by_weight(s));
   if (workspace_bytes < need_ws || (need_ws > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))))
     return MOE_ERR_WORKSPACE;
   hipStream_t hs = as_stream(stream);
-  hipError_t e = moe::launch_layout(topk_idx, topk_w, n, s->top_k, s->n_experts, s->capacity, s->row_align, rows,
+  hipError_t e = moe::launch_layout(topk_idx, topk_w, n, s->top_k, s->n_experts, s->capacity, s->row_align,
+                                    by_weight(s), rows,
                                     layout->tokens_per_expert, layout->expert_offsets, layout->ordinal,
                                     layout->assign_row, layout->row_src, layout->drop_mask, layout->pad_mask,
                                     layout->counters, w_perm, workspace, hs);

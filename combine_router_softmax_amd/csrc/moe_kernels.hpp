@@ -17,11 +17,13 @@ hipError_t launch_route(const float *logits, uint64_t seed, const float *expert_
 // ---- layout (moe_layout.hip)
 constexpr int kLayoutTile = 2048;  // assignments per layout tile
 inline int64_t layout_tiles(int64_t assignments) { return (assignments + kLayoutTile - 1) / kLayoutTile; }
-size_t layout_workspace_bytes(int64_t assignments, int e);
+size_t layout_workspace_bytes(int64_t assignments, int e, bool drop_by_weight);
+// drop_by_weight (with a capacity): keep each expert's `capacity` largest weights
 hipError_t launch_layout(const int32_t *topk_idx, const float *topk_w, int64_t n, int k, int e, int capacity,
-                         int row_align, int64_t rows, int32_t *tokens_per_expert, int32_t *expert_offsets, int32_t *ordinal,
-                         int32_t *assign_row, int32_t *row_src, uint8_t *drop_mask, uint8_t *pad_mask,
-                         int32_t *counters, float *w_perm, void *workspace, hipStream_t stream);
+                         int row_align, bool drop_by_weight, int64_t rows, int32_t *tokens_per_expert,
+                         int32_t *expert_offsets, int32_t *ordinal, int32_t *assign_row, int32_t *row_src,
+                         uint8_t *drop_mask, uint8_t *pad_mask, int32_t *counters, float *w_perm, void *workspace,
+                         hipStream_t stream);
 
 // ---- row movement (moe_rows.hip); `row_bytes` is a multiple of 16.  Pad rows
 // (row_src < 0) below pad_rows, and below *pad_limit when pad_limit is given,

@@ -29,6 +29,9 @@
 //      tile's base plus the counts of the earlier waves of the tile.  The same
 //      launch marks every row that receives no assignment (pad or tail), and
 //      workgroup 0 writes the counts, offsets and counters.
+// With a capacity and the drop-by-weight policy, layout_place lists every
+// assignment by expert instead of placing it, and capacity_select_kernel keeps
+// each expert's largest weights (see there).
 // Re-scanning the count matrix in every workgroup replaces a separate scan
 // launch: the matrix is tiles x E ints (16 x 256 for 4096 tokens, top-8, 256
 // experts), and a dependent kernel-to-kernel round trip costs more than
@@ -118,7 +121,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_count(const int32_t *__
 __global__ __launch_bounds__(kLayoutThreads) void layout_place(
     const int32_t *__restrict__ topk_idx, const float *__restrict__ topk_w, int64_t a_total, int64_t tiles, int e,
     int id_bits, int capacity, int row_align, int64_t rows, const int32_t *__restrict__ tile_counts,
-    const int32_t *__restrict__ tile_invalid, int32_t *__restrict__ tokens_per_expert,
+    const int32_t *__restrict__ tile_invalid, int32_t *__restrict__ full_list, int32_t *__restrict__ full_off,
+    int32_t *__restrict__ tokens_per_expert,
     int32_t *__restrict__ expert_offsets, int32_t *__restrict__ counters, int32_t *__restrict__ ordinal,
     int32_t *__restrict__ assign_row, int32_t *__restrict__ row_src, uint8_t *__restrict__ drop_mask,
     uint8_t *__restrict__ pad_mask, float *__restrict__ w_perm) {
@@ -128,6 +132,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place(
   int32_t *kept = off + e + 1;            // [e]
   int32_t *base = kept + e;               // [e] this tile's base (counts of earlier tiles)
   int32_t *total = base + e;              // [e] expert counts over all tiles
+  int32_t *full = total + e;              // [e + 1] (drop by weight) starts of the experts' full lists
   __shared__ int32_t part[2][kLayoutThreads];
   __shared__ int32_t red[3][kLayoutWaves];
   const int tid = threadIdx.x;
@@ -195,6 +200,16 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place(
     }
   }
   __syncthreads();
+
+  // drop by weight (full_list given): every assignment is listed, expert by
+  // expert in assignment order, for capacity_select_kernel to choose from
+  if (full_list) {
+    block_exclusive_scan(total, full, e);
+    if (tid == 0) full[e] = full[e - 1] + total[e - 1];
+    __syncthreads();
+    if (blockIdx.x == 0)
+      for (int x = tid; x <= e; x += kLayoutThreads) full_off[x] = full[x];
+  }
 
   // ---- segment offsets and kept counts
   if (capacity > 0) {
@@ -295,7 +310,9 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place(
         if (rank == 0) run[w * e + x] = b + __popcll(peers);
         const int32_t o = b + rank;
         ordinal[a] = o;
-        if (o < kept[x]) {
+        if (full_list) {
+          full_list[full[x] + o] = (int32_t)a;  // kept or dropped: capacity_select_kernel decides
+        } else if (o < kept[x]) {
           const int32_t r = off[x] + o;
           assign_row[a] = r;
           drop_mask[a] = 0;
@@ -337,22 +354,160 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place(
   }
 }
 
+// Order-preserving key of a weight for the drop-by-weight policy: a larger
+// number gets a larger key, -0.0 == +0.0, NaN gets 0 (below every number).
+__device__ __forceinline__ uint32_t weight_key(float v) {
+  uint32_t u = __float_as_uint(v);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0u;
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+constexpr int kSelectThreads = 1024;
+constexpr int kSelectWaves = kSelectThreads / kWave;
+constexpr int kSelectLdsKeys = 32768;  // weight keys of an expert held in LDS (128 KiB); the rest re-read
+
+// Exclusive prefix of a per-thread flag over the block in thread order, and the
+// block total (every thread calls it; `wave_tot` holds kSelectWaves ints).
+__device__ __forceinline__ int32_t block_flag_scan(bool f, int32_t *wave_tot, int32_t &total) {
+  const int w = threadIdx.x / kWave;
+  const uint64_t bal = ballot(f);
+  const int32_t below = __popcll(bal & lanes_below_mask());
+  if (lane_id() == 0) wave_tot[w] = __popcll(bal);
+  __syncthreads();
+  int32_t before = 0, all = 0;
+#pragma unroll
+  for (int i = 0; i < kSelectWaves; ++i) {
+    before += i < w ? wave_tot[i] : 0;
+    all += wave_tot[i];
+  }
+  __syncthreads();
+  total = all;
+  return before + below;
+}
+
+// Drop by weight (Megatron's "probs" token-drop policy), one workgroup per
+// expert: of the expert's assignments (full_list, in assignment order) keep the
+// `capacity` with the largest weights -- ties to the earlier assignment, NaN
+// below every number -- and place the kept ones in the expert's rows in
+// assignment order.  The weight threshold comes from a radix select over the
+// 32-bit weight keys (held in LDS), one byte per pass from the top: a
+// histogram of the next byte among the keys that match the bytes chosen so far
+// gives the byte of the C-th largest key (each of 256 threads sums the bins
+// above its own) and how many keys above it are kept.  A last, ordered pass
+// keeps every key above the threshold and the first `need` keys equal to it.
+__global__ __launch_bounds__(kSelectThreads) void capacity_select_kernel(
+    const int32_t *__restrict__ full_list, const int32_t *__restrict__ full_off, const float *__restrict__ topk_w,
+    int capacity, int32_t *__restrict__ assign_row, uint8_t *__restrict__ drop_mask, int32_t *__restrict__ row_src,
+    uint8_t *__restrict__ pad_mask, float *__restrict__ w_perm) {
+  extern __shared__ uint32_t keys[];  // [kSelectLdsKeys]
+  __shared__ uint32_t hist[256];
+  __shared__ uint32_t sh_prefix;
+  __shared__ int32_t sh_need;
+  __shared__ int32_t wave_tot[kSelectWaves];
+  const int x = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int32_t c0 = full_off[x];
+  const int32_t c = full_off[x + 1] - c0;
+  const int32_t *list = full_list + c0;
+  const bool select = c > capacity;
+  auto key_of = [&](int32_t i) { return i < kSelectLdsKeys ? keys[i] : weight_key(topk_w[list[i]]); };
+  uint32_t thr = 0;
+  int32_t need = capacity;
+  if (select) {
+    const int32_t cached = c < kSelectLdsKeys ? c : kSelectLdsKeys;
+    for (int32_t i = tid; i < cached; i += kSelectThreads) keys[i] = weight_key(topk_w[list[i]]);
+    uint32_t prefix = 0, mask = 0;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      if (tid < 256) hist[tid] = 0;
+      __syncthreads();
+      for (int32_t i = tid; i < c; i += kSelectThreads) {
+        const uint32_t kk = key_of(i);
+        if ((kk & mask) == prefix) atomicAdd(&hist[(kk >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      // the bin holding the need-th largest matching key: thread t < 256 takes
+      // bin b = 255 - t, an inclusive scan over those threads gives the number
+      // of keys in bins b and above
+      int32_t incl = 0;
+      if (tid < 256) {
+        const int32_t hb = (int32_t)hist[255 - tid];
+        incl = wave_incl_scan(hb);
+        if (lane_id() == kWave - 1) wave_tot[tid / kWave] = incl;
+      }
+      __syncthreads();
+      if (tid < 256) {
+        for (int i = 0; i < tid / kWave; ++i) incl += wave_tot[i];
+        const int32_t hb = (int32_t)hist[255 - tid];
+        if (incl - hb < need && incl >= need) {
+          sh_need = need - (incl - hb);
+          sh_prefix = prefix | ((uint32_t)(255 - tid) << shift);
+        }
+      }
+      __syncthreads();
+      need = sh_need;
+      prefix = sh_prefix;
+      mask |= 255u << shift;
+      __syncthreads();
+    }
+    thr = prefix;
+  }
+  int32_t run_tie = 0, run_keep = 0;
+  for (int32_t b0 = 0; b0 < c; b0 += kSelectThreads) {
+    const int32_t i = b0 + tid;
+    const bool valid = i < c;
+    const int32_t a = valid ? list[i] : -1;
+    const uint32_t kk = valid && select ? key_of(i) : 0u;
+    const bool tie = valid && select && kk == thr;
+    int32_t n_tie, n_keep;
+    const int32_t tie_rank = run_tie + block_flag_scan(tie, wave_tot, n_tie);
+    const bool keep = valid && (!select || kk > thr || (tie && tie_rank < need));
+    const int32_t slot = run_keep + block_flag_scan(keep, wave_tot, n_keep);
+    if (keep) {
+      const int32_t r = x * capacity + slot;
+      assign_row[a] = r;
+      drop_mask[a] = 0;
+      row_src[r] = a;
+      pad_mask[r] = 0;
+      if (w_perm) w_perm[r] = topk_w[a];
+    } else if (valid) {
+      assign_row[a] = -1;
+      drop_mask[a] = 1;
+    }
+    run_tie += n_tie;
+    run_keep += n_keep;
+  }
+}
+
 }  // namespace
 
-size_t layout_workspace_bytes(int64_t assignments, int e) {
+size_t layout_workspace_bytes(int64_t assignments, int e, bool drop_by_weight) {
   const int64_t tiles = layout_tiles(assignments);
-  return align256(sizeof(int32_t) * (size_t)tiles * (size_t)e) + align256(sizeof(int32_t) * (size_t)tiles);
+  size_t b = align256(sizeof(int32_t) * (size_t)tiles * (size_t)e) + align256(sizeof(int32_t) * (size_t)tiles);
+  if (drop_by_weight)  // every assignment listed by expert, and the list offsets
+    b += align256(sizeof(int32_t) * (size_t)assignments) + align256(sizeof(int32_t) * (size_t)(e + 1));
+  return b;
 }
 
 hipError_t launch_layout(const int32_t *topk_idx, const float *topk_w, int64_t n, int k, int e, int capacity,
-                         int row_align, int64_t rows, int32_t *tokens_per_expert, int32_t *expert_offsets, int32_t *ordinal,
-                         int32_t *assign_row, int32_t *row_src, uint8_t *drop_mask, uint8_t *pad_mask,
-                         int32_t *counters, float *w_perm, void *workspace, hipStream_t stream) {
+                         int row_align, bool drop_by_weight, int64_t rows, int32_t *tokens_per_expert,
+                         int32_t *expert_offsets, int32_t *ordinal, int32_t *assign_row, int32_t *row_src,
+                         uint8_t *drop_mask, uint8_t *pad_mask, int32_t *counters, float *w_perm, void *workspace,
+                         hipStream_t stream) {
   const int64_t a_total = n * k;
   const int64_t tiles = layout_tiles(a_total);
-  int32_t *tile_counts = static_cast<int32_t *>(workspace);
-  int32_t *tile_invalid = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) +
-                                                      align256(sizeof(int32_t) * (size_t)tiles * (size_t)e));
+  char *ws = static_cast<char *>(workspace);
+  int32_t *tile_counts = reinterpret_cast<int32_t *>(ws);
+  ws += align256(sizeof(int32_t) * (size_t)tiles * (size_t)e);
+  int32_t *tile_invalid = reinterpret_cast<int32_t *>(ws);
+  ws += align256(sizeof(int32_t) * (size_t)tiles);
+  const bool by_weight = drop_by_weight && capacity > 0;
+  int32_t *full_list = nullptr, *full_off = nullptr;
+  if (by_weight) {
+    full_list = reinterpret_cast<int32_t *>(ws);
+    ws += align256(sizeof(int32_t) * (size_t)a_total);
+    full_off = reinterpret_cast<int32_t *>(ws);
+  }
   if (tiles > 0) {
     hipLaunchKernelGGL(layout_count, dim3((unsigned)tiles), dim3(kLayoutThreads), sizeof(int32_t) * (e + 1), stream,
                        topk_idx, a_total, e, tile_counts, tile_invalid);
@@ -364,11 +519,16 @@ hipError_t launch_layout(const int32_t *topk_idx, const float *topk_w, int64_t n
   int64_t blocks = tiles > row_blocks ? tiles : row_blocks;
   if (blocks == 0) blocks = 1;  // workgroup 0 still writes counts, offsets and counters
   const int id_bits = e <= 1 ? 0 : 32 - __builtin_clz((unsigned)(e - 1));
-  const size_t lds = sizeof(int32_t) * ((size_t)kLayoutWaves * e + 4 * (size_t)e + 1);
+  const size_t lds = sizeof(int32_t) * ((size_t)kLayoutWaves * e + 5 * (size_t)e + 2);
   hipLaunchKernelGGL(layout_place, dim3((unsigned)blocks), dim3(kLayoutThreads), lds, stream, topk_idx, topk_w,
                      a_total, tiles, e, id_bits, capacity, row_align > 1 ? row_align : 1, rows, tile_counts,
-                     tile_invalid, tokens_per_expert,
-                     expert_offsets, counters, ordinal, assign_row, row_src, drop_mask, pad_mask, w_perm);
+                     tile_invalid, full_list, full_off, tokens_per_expert, expert_offsets, counters, ordinal,
+                     assign_row, row_src, drop_mask, pad_mask, w_perm);
+  hipError_t st = hipGetLastError();
+  if (st != hipSuccess || !by_weight) return st;
+  hipLaunchKernelGGL(capacity_select_kernel, dim3((unsigned)e), dim3(kSelectThreads),
+                     sizeof(uint32_t) * kSelectLdsKeys, stream, full_list, full_off, topk_w, capacity, assign_row,
+                     drop_mask, row_src, pad_mask, w_perm);
   return hipGetLastError();
 }
 

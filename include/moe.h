@@ -57,6 +57,12 @@ typedef enum moe_status {
 
 typedef enum moe_dtype { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype;
 
+/* Which assignments an over-full expert keeps when there is a capacity. */
+typedef enum moe_drop_policy {
+  MOE_DROP_POSITION = 0, /* the first C by assignment order */
+  MOE_DROP_PROBS = 1     /* the C with the largest routing weights (Megatron's "probs" drop policy) */
+} moe_drop_policy;
+
 typedef enum moe_op {
   MOE_OP_ROUTE = 0,
   MOE_OP_DISPATCH = 1,
@@ -85,6 +91,8 @@ typedef struct moe_shape {
                         an expert's kept rows and the next segment are pad rows.
                         Default R becomes N*k + E*(A-1).  With a capacity, C must
                         be a multiple of A (segments are e*C already). */
+  int32_t drop_policy; /* moe_drop_policy, used with a capacity only */
+  int32_t reserved;    /* must be 0 */
 } moe_shape;
 
 /* The dispatch layout ("handle"): written by moe_dispatch, read by the other
@@ -173,8 +181,12 @@ moe_status moe_route_random(const moe_shape *s, uint64_t seed, const float *expe
  *   all-zero, unused dropless tail rows not written; w_perm fp32 [R]
  *   (nullable): topk_w[a] in row assign_row[a], 0 in every other row.
  * Stability: within an expert, rows follow assignment order a = t*k + j.
- * With a capacity C the first C assignments of each expert (by ordinal) are
- * kept; without one, assignments past row R are dropped.
+ * With a capacity C, MOE_DROP_POSITION keeps the first C assignments of each
+ * expert (by ordinal); MOE_DROP_PROBS keeps the C with the largest topk_w
+ * (ties to the earlier assignment, NaN below every number; topk_w required),
+ * still placed in assignment order, so assign_row - offset is the rank among
+ * the kept, and ordinal stays the position among all of the expert's
+ * assignments.  Without a capacity, assignments past row R are dropped.
  * Workspace: moe_workspace_size(MOE_OP_DISPATCH). */
 moe_status moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_idx, const float *topk_w,
                         const moe_layout *layout, void *x_perm, float *w_perm, void *workspace,

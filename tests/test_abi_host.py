@@ -60,6 +60,11 @@ def test_layout_rows_and_workspace_sizes(moe):
     assert moe.workspace_size(moe.MOE_OP_EXPERT_FFN, s) >= 65536 * 1536 * 2
     assert moe.workspace_size(moe.MOE_OP_EXPERT_FFN_BWD, s) >= 65536 * 3 * 1536 * 2   # [R, 3I] bf16
     assert moe.workspace_size(moe.MOE_OP_DISPATCH, moe.make_shape(0, 64, 4, 2)) == 0
+    # dropping by weight lists every assignment by expert: room for N*k ints more
+    pos = moe.workspace_size(moe.MOE_OP_DISPATCH, moe.make_shape(4096, 7168, 256, 8, capacity=160))
+    probs = moe.workspace_size(moe.MOE_OP_DISPATCH, moe.make_shape(4096, 7168, 256, 8, capacity=160,
+                                                                  drop_policy=moe.MOE_DROP_PROBS))
+    assert probs >= pos + 4096 * 8 * 4 + 257 * 4
     # aligned dropless segments: room for E * (A - 1) pad rows; a row budget or a capacity fixes R
     assert moe.lib.moe_layout_rows(C.byref(moe.make_shape(4096, 7168, 256, 8, row_align=64))) == 32768 + 256 * 63
     assert moe.lib.moe_layout_rows(C.byref(moe.make_shape(4096, 7168, 256, 8, row_align=1))) == 32768
@@ -69,6 +74,7 @@ def test_layout_rows_and_workspace_sizes(moe):
 @pytest.mark.parametrize("field,value,status", [
     ("n_tokens", -1, -1), ("hidden", 0, -1), ("n_experts", 0, -1), ("n_experts", 1025, -4), ("top_k", 0, -1),
     ("act_dtype", 7, -1), ("row_align", 3, -1), ("row_align", 2048, -1), ("row_align", -2, -1), ("max_rows", -5, -1),
+    ("drop_policy", 2, -1), ("drop_policy", -1, -1), ("reserved", 1, -1),
 ])
 def test_bad_shapes_are_rejected(moe, field, value, status):
     s = moe.make_shape(16, 64, 8, 2)
@@ -98,6 +104,8 @@ def test_validation_errors_enqueue_nothing(moe):
     assert lib.moe_dispatch(C.byref(s), p, p, p, C.byref(lay), p, p, p, 0, None) == -3       # no workspace
     assert lib.moe_dispatch(C.byref(s), p, p, p, C.byref(lay), p, p, odd, 1 << 20, None) == -3  # unaligned ws
     assert lib.moe_dispatch(C.byref(s), p, p, p, None, p, p, p, 1 << 20, None) == -1
+    s = moe.make_shape(16, 64, 8, 2, capacity=4, drop_policy=moe.MOE_DROP_PROBS)  # the policy needs topk_w
+    assert lib.moe_dispatch(C.byref(s), p, p, None, C.byref(lay), p, None, p, 1 << 20, None) == -1
     s = moe.make_shape(16, 64, 8, 2, capacity=6, row_align=4)                   # C not a multiple of A
     assert lib.moe_dispatch(C.byref(s), p, p, p, C.byref(lay), p, p, p, 1 << 20, None) == -4
     s = moe.make_shape(16, 64, 8, 2, capacity=4, max_rows=7)                   # max_rows != E*C

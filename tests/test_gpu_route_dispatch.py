@@ -166,17 +166,18 @@ def test_route_empty(moe):
     assert (host(r.tokens_per_expert) == 0).all()
 
 
-def run_dispatch(moe, x: np.ndarray, idx: np.ndarray, wts: np.ndarray, e: int, capacity=0, max_rows=0, row_align=0):
+def run_dispatch(moe, x: np.ndarray, idx: np.ndarray, wts: np.ndarray, e: int, capacity=0, max_rows=0, row_align=0,
+                 drop_policy=0):
     x_d = dev(x)
     xp, wp, lay = moe.moe_dispatch(x_d, dev(idx), dev(wts), e, capacity=capacity, max_rows=max_rows,
-                                   row_align=row_align)
+                                   row_align=row_align, drop_policy=drop_policy)
     torch.cuda.synchronize()
     return xp, wp, lay
 
 
-def check_dispatch(moe, x, idx, wts, e, capacity=0, max_rows=0, row_align=0):
-    xp, wp, lay = run_dispatch(moe, x, idx, wts, e, capacity, max_rows, row_align)
-    ref = oracle.layout(idx, e, capacity, max_rows, row_align)
+def check_dispatch(moe, x, idx, wts, e, capacity=0, max_rows=0, row_align=0, drop_policy=0):
+    xp, wp, lay = run_dispatch(moe, x, idx, wts, e, capacity, max_rows, row_align, drop_policy)
+    ref = oracle.layout(idx, e, capacity, max_rows, row_align, drop_policy, wts)
     got = layout_host(lay)
     assert_layout_equal(got, ref)
     xp_h = host(xp)
@@ -192,6 +193,42 @@ def check_dispatch(moe, x, idx, wts, e, capacity=0, max_rows=0, row_align=0):
     np.testing.assert_array_equal(host(wp), ref_wp)
     assert (xp_h.view(np.uint8) == ref_xp.view(np.uint8)).all()
     return xp, wp, lay, ref
+
+
+@pytest.mark.parametrize("case", ["random", "ties", "nan", "one_hot_expert", "under_capacity"])
+def test_dispatch_drop_by_weight(moe, case):
+    """Capacity with the drop-by-weight policy: the radix select keeps each
+    expert's largest weights, ties to the earlier assignment."""
+    g = np.random.default_rng(["random", "ties", "nan", "one_hot_expert", "under_capacity"].index(case))
+    n, e, k, h, cap = 2000, 64, 4, 256, 96
+    idx = np.stack([g.permutation(e)[:k] for _ in range(n)]).astype(np.int32)
+    wts = g.random((n, k)).astype(np.float32)
+    if case == "ties":
+        wts = (np.round(wts * 8) / 8).astype(np.float32)
+    if case == "nan":
+        wts[g.random(wts.shape) < 0.05] = np.nan
+        wts[g.random(wts.shape) < 0.05] = -0.0
+    if case == "one_hot_expert":
+        idx[:, 0] = 5                                   # expert 5 receives every token: 2000 rows for 96 slots
+    if case == "under_capacity":
+        cap = 400                                       # nobody over capacity: same as the position policy
+    x = mi.normal_activations((n, h), mi.DT_BF16, 78, 1)
+    xp, wp, lay, ref = check_dispatch(moe, x, idx, wts, e, cap, drop_policy=1)
+    if case == "under_capacity":
+        assert_layout_equal(layout_host(lay), oracle.layout(idx, e, cap))
+
+
+def test_dispatch_drop_by_weight_zipf_workload(moe):
+    w = mi.workload(3)
+    logits = mi.router_logits(w)
+    idx, wts, _, _ = oracle.route(logits, w.top_k)
+    x = mi.activations(w)
+    xp, wp, lay, ref = check_dispatch(moe, x, idx, wts, w.n_experts, w.capacity, drop_policy=1)
+    # the kept mass: dropping by weight keeps at least as much routing weight as dropping by position
+    kept_w = np.nansum(np.where(ref["assign_row"].reshape(idx.shape) >= 0, wts, 0))
+    pos = oracle.layout(idx, w.n_experts, w.capacity)
+    kept_pos = np.nansum(np.where(pos["assign_row"].reshape(idx.shape) >= 0, wts, 0))
+    assert kept_w > kept_pos
 
 
 @pytest.mark.parametrize("wid", [1, 2, 3, 5])
