@@ -40,6 +40,41 @@ __device__ __forceinline__ uint32_t logit_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Wave-wide max of a 64-bit key with DPP row operations instead of LDS
+// permutes: four row_shr steps leave each row's max in its lane 15, two row
+// broadcasts carry it to lane 63, which is read back into every lane.  The
+// top-k loop makes k of these reductions in a row, so their latency matters.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  // lanes without a source (or outside ROW_MASK) keep their own value
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v, CTRL, ROW_MASK, 0xF,
+                                                            false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(v >> 32), (int)(uint32_t)(v >> 32), CTRL,
+                                                            ROW_MASK, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
+  constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
+  constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+  uint64_t t;
+  t = dpp_u64<kRowShr1, 0xF>(v);
+  v = t > v ? t : v;
+  t = dpp_u64<kRowShr2, 0xF>(v);
+  v = t > v ? t : v;
+  t = dpp_u64<kRowShr4, 0xF>(v);
+  v = t > v ? t : v;
+  t = dpp_u64<kRowShr8, 0xF>(v);
+  v = t > v ? t : v;
+  t = dpp_u64<kRowBcast15, 0xA>(v);
+  v = t > v ? t : v;
+  t = dpp_u64<kRowBcast31, 0xC>(v);
+  v = t > v ? t : v;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, kWave - 1);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), kWave - 1);
+  return ((uint64_t)hi << 32) | lo;
+}
+
 __device__ __forceinline__ float key_logit(uint32_t key) {
   if (key == 0u) return __uint_as_float(0x7FC00000u);
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
@@ -169,7 +204,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float *__res
       uint64_t best = key[0];
 #pragma unroll
       for (int i = 1; i < VPL; ++i) best = key[i] > best ? key[i] : best;
-      best = wave_max_u64(best);
+      best = wave_max_u64_dpp(best);
       const uint32_t x = ~(uint32_t)best;
 #pragma unroll
       for (int i = 0; i < VPL; ++i)
