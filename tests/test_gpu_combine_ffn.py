@@ -289,6 +289,39 @@ def test_expert_ffn_bwd_small_full_compare(moe, n, e, k, h, inter, cap):
         assert cnt[1] == 0
 
 
+def test_expert_ffn_and_bwd_empty(moe):
+    """No rows: the forward writes nothing, the backward gives zero weight gradients."""
+    e, h, inter = 4, 128, 64
+    x = torch.empty((0, h), dtype=torch.bfloat16, device="cuda")
+    idx = torch.empty((0, 2), dtype=torch.int32, device="cuda")
+    wts = torch.empty((0, 2), dtype=torch.float32, device="cuda")
+    xp, wp, lay = moe.moe_dispatch(x, idx, wts, e)
+    g = torch.Generator(device="cuda").manual_seed(0)
+    wgu = torch.randn((e, 2 * inter, h), generator=g, device="cuda").to(torch.bfloat16)
+    wd = torch.randn((e, h, inter), generator=g, device="cuda").to(torch.bfloat16)
+    y = moe.moe_expert_ffn(xp, lay, wgu, wd)
+    gx, dwgu, dwd = moe.moe_expert_ffn_bwd(xp, torch.empty_like(xp), lay, wgu, wd,
+                                           grad_w_gate_up=torch.full_like(wgu, 3.0), grad_w_down=torch.full_like(wd, 3.0))
+    torch.cuda.synchronize()
+    assert y.shape == (0, h) and gx.shape == (0, h)
+    assert not dwgu.view(torch.int16).any() and not dwd.view(torch.int16).any()
+
+
+def test_expert_ffn_and_bwd_1024_experts(moe):
+    """The most experts the tile scan takes, most of them empty, a few with ragged rows."""
+    n, e, k, h, inter = 600, 1024, 2, 128, 64
+    w, idx, wts, x, wgu, wd, xp, lay, y = ffn_case(moe, n, e, k, h, inter)
+    lay_h = layout_host(lay)
+    lay_h["rows"] = lay.rows
+    ref = oracle.expert_ffn(host(xp), lay_h, wgu, wd)
+    kept = lay_h["pad_mask"] == 0
+    assert max_rel_err(host(y)[kept], ref[kept]) <= TOL_BF16
+    dy, gx, dwgu, dwd = (host(v) if isinstance(v, torch.Tensor) else v for v in ffn_bwd_run(moe, w, xp, lay, wgu, wd))
+    ref_gx, ref_dwgu, ref_dwd = oracle.expert_ffn_bwd(host(xp), dy, lay_h, wgu, wd)
+    assert max_rel_err(gx[kept], ref_gx[kept]) <= TOL_BF16
+    assert max_rel_err(dwgu, ref_dwgu) <= TOL_BF16 and max_rel_err(dwd, ref_dwd) <= TOL_BF16
+
+
 def test_expert_ffn_bwd_repeated_calls_are_identical(moe):
     """The backward is deterministic: no atomics, fixed reduction order."""
     w, idx, wts, x, wgu, wd, xp, lay, y = ffn_case(moe, 700, 8, 2, 256, 128)
