@@ -109,59 +109,77 @@ struct TileCoord {
 };
 
 // Maps blockIdx.x to an output tile; returns false for surplus workgroups.
-// `scratch` (LDS) must hold kMaxExperts + kThreads int64 and is free again on
-// return.
+// `scratch` (LDS) must hold 3 * kMaxExperts + kThreads / kWave int32 and is
+// free again on return.  The experts' row counts and offsets are read in one
+// round of loads and kept in LDS; the tile counts are scanned with wave scans
+// and one barrier.  Tile counts fit in int32: their total bounds the grid.
 __device__ bool find_tile(const int32_t *__restrict__ tokens_per_expert, const int32_t *__restrict__ expert_offsets,
-                          int e, int n_tiles, int64_t *scratch, TileCoord &tc) {
+                          int e, int n_tiles, int32_t *scratch, TileCoord &tc) {
   constexpr int kPer = kMaxExperts / kThreads;  // experts per thread
-  int64_t *part = scratch + kMaxExperts;
+  int32_t *pre = scratch;                       // [kMaxExperts] first tile of each expert
+  int32_t *rows_s = pre + kMaxExperts;          // [kMaxExperts]
+  int32_t *offs_s = rows_s + kMaxExperts;       // [kMaxExperts]
+  int32_t *wave_tot = offs_s + kMaxExperts;     // [kThreads / kWave]
   const int tid = threadIdx.x;
-  int64_t local[kPer];
-  int64_t s = 0;
+  int32_t rows[kPer], offs[kPer];
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int x = tid * kPer + i;
-    const int64_t rows = x < e ? tokens_per_expert[x] : 0;
-    local[i] = ((rows + kBM - 1) / kBM) * n_tiles;
-    s += local[i];
+    rows[i] = x < e ? tokens_per_expert[x] : 0;
+    offs[i] = x < e ? expert_offsets[x] : 0;
   }
-  part[tid] = s;
-  __syncthreads();
-  for (int off = 1; off < kThreads; off <<= 1) {
-    const int64_t v = tid >= off ? part[tid - off] : 0;
-    __syncthreads();
-    part[tid] += v;
-    __syncthreads();
-  }
-  int64_t run = part[tid] - s;  // exclusive prefix of this thread's experts
+  int32_t local[kPer];
+  int32_t s = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    scratch[tid * kPer + i] = run;
+    const int x = tid * kPer + i;
+    local[i] = ((rows[i] + kBM - 1) / kBM) * n_tiles;
+    s += local[i];
+    rows_s[x] = rows[i];
+    offs_s[x] = offs[i];
+  }
+  const int l = lane_id(), wv = tid / kWave;
+  int32_t incl = s;  // inclusive scan over the wave
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int32_t o = __shfl_up(incl, off, kWave);
+    if (l >= off) incl += o;
+  }
+  if (l == kWave - 1) wave_tot[wv] = incl;
+  __syncthreads();
+  int32_t run = incl - s, total = 0;
+#pragma unroll
+  for (int i = 0; i < kThreads / kWave; ++i) {
+    run += i < wv ? wave_tot[i] : 0;
+    total += wave_tot[i];
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    pre[tid * kPer + i] = run;
     run += local[i];
   }
-  const int64_t total = part[kThreads - 1];
   __syncthreads();
 
-  const int64_t bid = blockIdx.x;
-  const int64_t share = (total + kXcds - 1) / kXcds;
-  const int64_t slot = bid / kXcds;
-  const int64_t logical = (bid % kXcds) * share + slot;
+  const int32_t bid = blockIdx.x;
+  const int32_t share = (total + kXcds - 1) / kXcds;
+  const int32_t slot = bid / kXcds;
+  const int32_t logical = (bid % kXcds) * share + slot;
   bool ok = slot < share && logical < total;
   if (ok) {
     int lo = 0, hi = e - 1;  // last expert whose first tile is <= logical
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (scratch[mid] <= logical) lo = mid;
+      if (pre[mid] <= logical) lo = mid;
       else hi = mid - 1;
     }
-    const int64_t rows = tokens_per_expert[lo];
-    const int64_t mt = (rows + kBM - 1) / kBM;
-    const int64_t local_id = logical - scratch[lo];
-    const int64_t m_tile = local_id % mt;
+    const int32_t nrows = rows_s[lo];
+    const int32_t mt = (nrows + kBM - 1) / kBM;
+    const int32_t local_id = logical - pre[lo];
+    const int32_t m_tile = local_id % mt;
     tc.e = lo;
-    tc.n_tile = (int)(local_id / mt);
-    tc.row0 = expert_offsets[lo] + m_tile * kBM;
-    tc.row_end = (int64_t)expert_offsets[lo] + rows;
+    tc.n_tile = local_id / mt;
+    tc.row0 = (int64_t)offs_s[lo] + (int64_t)m_tile * kBM;
+    tc.row_end = (int64_t)offs_s[lo] + nrows;
   }
   __syncthreads();
   return ok;
@@ -355,7 +373,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     c_base = C + ((int64_t)te * M + m0) * N;
   } else {
     TileCoord tc;
-    if (!find_tile(tokens_per_expert, expert_offsets, e, n_tiles, reinterpret_cast<int64_t *>(ring), tc)) return;
+    if (!find_tile(tokens_per_expert, expert_offsets, e, n_tiles, reinterpret_cast<int32_t *>(ring), tc)) return;
     const int te = __builtin_amdgcn_readfirstlane(tc.e);
     n0 = __builtin_amdgcn_readfirstlane(tc.n_tile) * (kSwiGLU ? kBN / 2 : kBN);
     const int64_t row0 = ((int64_t)__builtin_amdgcn_readfirstlane((int)(tc.row0 >> 32)) << 32) |
@@ -650,7 +668,7 @@ int64_t tile_bound(int64_t rows, int e, int capacity, int n_tiles) {
     if (cap_m < m) m = cap_m;
   }
   const int64_t t = m * n_tiles;
-  return (t + kXcds - 1) / kXcds * kXcds;
+  return (t + kXcds - 1) / kXcds * kXcds;  // the launchers reject a grid past INT32_MAX (tile ids are int32)
 }
 
 // ------------------------------------------------------------------ backward
@@ -698,6 +716,7 @@ hipError_t launch_plain(const uint16_t *A, const uint16_t *B, int64_t b_stride, 
                         hipStream_t stream) {
   const int nt = (N + kBN - 1) / kBN;
   const int64_t g = tile_bound(rows, e, capacity, nt);
+  if (g > INT32_MAX) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((grouped_gemm_kernel<kModePlain, false, kBT>), dim3((unsigned)g), dim3(kThreads), 0, stream, A,
                      B, b_stride, K, 0, N, 0, nt, tokens_per_expert, expert_offsets, e, C, (int64_t)N, nullptr);
   return hipGetLastError();
@@ -769,13 +788,14 @@ hipError_t launch_expert_ffn(const uint16_t *x_perm, int64_t rows, int64_t hidde
   uint16_t *act = static_cast<uint16_t *>(workspace);
   const int n1 = (inter + kBN / 2 - 1) / (kBN / 2);
   const int64_t g1 = tile_bound(rows, e, capacity, n1);
+  const int64_t g2 = tile_bound(rows, e, capacity, (int)((hidden + kBN - 1) / kBN));
+  if (g1 > INT32_MAX || g2 > INT32_MAX) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((grouped_gemm_kernel<kModeSwiGLU, false, false>), dim3((unsigned)g1), dim3(kThreads), 0, stream,
                      x_perm, w_gate_up, (int64_t)2 * inter * hidden, (int)hidden, 0, inter, 0, n1, tokens_per_expert,
                      expert_offsets, e, act, (int64_t)inter, gate_up);
   hipError_t st = hipGetLastError();
   if (st != hipSuccess) return st;
   const int n2 = (int)((hidden + kBN - 1) / kBN);
-  const int64_t g2 = tile_bound(rows, e, capacity, n2);
   hipLaunchKernelGGL((grouped_gemm_kernel<kModePlain, false, false>), dim3((unsigned)g2), dim3(kThreads), 0, stream,
                      act, w_down, (int64_t)hidden * inter, inter, 0, (int)hidden, 0, n2, tokens_per_expert,
                      expert_offsets, e, y, hidden, nullptr);
