@@ -90,6 +90,26 @@ def bench_dispatch_combine(moe, mi, torch, steps, warmup):
     route_ms = median([r_[0].elapsed_time(r_[1]) for r_ in recs])
     disp_ms = median([r_[1].elapsed_time(r_[2]) for r_ in recs])
     comb_ms = median([r_[2].elapsed_time(r_[3]) for r_ in recs])
+    # the same step captured once in a HIP graph and replayed (no launch overhead on the host)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(steps):
+        graph.replay()
+    t1.record()
+    torch.cuda.synchronize()
+    graph_ms = t0.elapsed_time(t1) / steps
+    del graph
     counters = lay.counters.cpu().tolist()
     kept = counters[0]
     row_b = h * 2
@@ -171,7 +191,7 @@ def bench_dispatch_combine(moe, mi, torch, steps, warmup):
     del flush, dst
     return dict(total_ms=total_ms, route_ms=route_ms, dispatch_ms=disp_ms, combine_ms=comb_ms,
                 comb_kernel_ms=comb_kernel_ms, kept=kept, copy_gbs=copy_gbs, dbwd_ms=dbwd_ms,
-                route_random_ms=route_random_ms,
+                route_random_ms=route_random_ms, graph_ms=graph_ms,
                 dc_p10=pct([r_[1].elapsed_time(r_[3]) for r_ in recs], 10),
                 dc_p90=pct([r_[1].elapsed_time(r_[3]) for r_ in recs], 90),
                 cold_route_ms=median(cold_route), cold_dispatch_ms=median(cold_disp),
@@ -475,6 +495,8 @@ def main():
         "copy_gbs": round(dc["copy_gbs"], 1),
         "dispatch_combine_frac_of_copy": round(byts / ((dc["dispatch_ms"] + dc["combine_ms"]) * 1e-3) / 1e9
                                                / dc["copy_gbs"], 4),
+        "graph_step_us": round(dc["graph_ms"] * 1e3, 2),
+        "graph_step_gbs": round(byts / (dc["graph_ms"] * 1e-3) / 1e9, 2),
         "route_force_balanced_us": round(dc["route_random_ms"] * 1e3, 2),
         "zipf_capacity": {p: {"dispatch_us": round(v["dispatch_us"], 2), "combine_us": round(v["combine_us"], 2),
                               "dispatch_gbs": round(v["dispatch_bytes"] / v["dispatch_us"] / 1e3, 1),

@@ -400,3 +400,54 @@ def test_expert_ffn_saved_gate_up(moe, n, e, k, h, inter, cap):
     for u, v in zip(a[1:], b[1:]):
         assert torch.equal(u.view(torch.int16), v.view(torch.int16))
     assert torch.equal(saved.view(torch.int16), gu.view(torch.int16))   # the saved buffer is only read
+
+
+def test_layer_step_replays_in_a_hip_graph(moe):
+    """route -> dispatch -> grouped FFN -> combine captured once in a HIP graph (the
+    library launches kernels only: no memsets, allocations or host synchronisation)
+    and replayed three times, with other work and synchronisation in between; every
+    replay equals the eager step bit for bit."""
+    n, e, k, h, inter = 512, 16, 4, 256, 128
+    w = mi.workload(4, n_tokens=n, hidden=h, n_experts=e, top_k=k, inter=inter)
+    logits, x = dev(mi.router_logits(w)), dev(mi.activations(w))
+    wgu, wd = (dev(a) for a in mi.expert_weights(w))
+    r = moe.moe_route(logits, k)
+    xp, wp, lay = moe.moe_dispatch(x, r.topk_idx, r.topk_w, e)
+    y = torch.empty_like(xp)
+    out = torch.empty_like(x)
+    shape_d = moe.make_shape(n, h, e, k)
+    ws_d = torch.empty(moe.workspace_size(moe.MOE_OP_DISPATCH, shape_d) + 256, dtype=torch.uint8, device="cuda")
+    ws_f = torch.empty(moe.workspace_size(moe.MOE_OP_EXPERT_FFN, lay.shape(h, moe.MOE_DT_BF16, inter)) + 256,
+                       dtype=torch.uint8, device="cuda")
+
+    def step():
+        moe.moe_route(logits, k, out=r)
+        moe.moe_dispatch(x, r.topk_idx, r.topk_w, e, layout=lay, x_perm=xp, w_perm_out=wp, workspace=ws_d)
+        moe.moe_expert_ffn(xp, lay, wgu, wd, y=y, workspace=ws_f)
+        moe.moe_combine(y, r.topk_w, lay, out=out)
+
+    step()
+    torch.cuda.synchronize()
+    ref_out = out.clone()
+    ref_idx = r.topk_idx.clone()
+    ref_rows = lay.assign_row.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for i in range(3):
+        out.fill_(7.0)
+        lay.assign_row.fill_(-5)
+        r.topk_idx.fill_(-5)
+        torch.randn(1 << 20, device="cuda").sum()       # other work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref_out.view(torch.int16)), i
+        assert torch.equal(r.topk_idx, ref_idx) and torch.equal(lay.assign_row, ref_rows), i
