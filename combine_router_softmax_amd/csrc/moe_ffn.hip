@@ -185,7 +185,9 @@ __device__ bool find_tile(const int32_t *__restrict__ tokens_per_expert, const i
   return ok;
 }
 
-__device__ __forceinline__ float silu_f(float g) { return g / (1.0f + __expf(-g)); }
+// silu(g) = g * sigmoid(g), with the hardware reciprocal (v_rcp_f32, about one
+// ulp) in place of a correctly rounded division: the result is rounded to bf16.
+__device__ __forceinline__ float silu_f(float g) { return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)); }
 
 __device__ __forceinline__ uint16_t bf16_bits(float v) { return (uint16_t)(pack_bf16x2(v, 0.0f) & 0xFFFFu); }
 
