@@ -70,6 +70,12 @@ def lib():
         L.oracle_bf16_round_array.argtypes = [i64, p, p]
         L.oracle_bf16_round_array.restype = None
         L.oracle_bf16_round.restype = C.c_uint16
+        L.oracle_mx_quantize.argtypes = [i64, i64, p, p, p]
+        L.oracle_mx_quantize.restype = None
+        L.oracle_e4m3_encode_array.argtypes = [i64, p, p]
+        L.oracle_e4m3_encode_array.restype = None
+        L.oracle_e4m3_decode_array.argtypes = [i64, p, p]
+        L.oracle_e4m3_decode_array.restype = None
         _lib = L
     return _lib
 
@@ -173,6 +179,53 @@ def scatter(x: np.ndarray, k: int, lay: dict, topk_w: np.ndarray, x_perm=None):
     lib().oracle_scatter(n, k, h * x.itemsize, _p(x), _p(lay["assign_row"]), _p(topk_w), rows,
                          _p(lay["row_src"]), int(lay["expert_offsets"][-1]), _p(x_perm), _p(w_perm))
     return x_perm, w_perm
+
+
+def mx_quantize(x: np.ndarray):
+    """MXFP8 of bf16 rows (uint16 bits [n, H], H % 32 == 0) -> (q uint8 [n, H] E4M3
+    codes, scale uint8 [n, H/32] E8M0 codes); the OCP MX v1.0 conversion."""
+    x = np.ascontiguousarray(x, dtype=np.uint16)
+    n, h = x.shape
+    if h % 32:
+        raise ValueError("row length must be a multiple of 32")
+    q = np.empty((n, h), np.uint8)
+    sc = np.empty((n, h // 32), np.uint8)
+    lib().oracle_mx_quantize(n, h, _p(x), _p(q), _p(sc))
+    return q, sc
+
+
+def e4m3_encode(v: np.ndarray) -> np.ndarray:
+    """double -> E4M3 codes (clamped to +-448, nearest, ties to even), element-wise."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    out = np.empty(v.shape, np.uint8)
+    lib().oracle_e4m3_encode_array(v.size, _p(v), _p(out))
+    return out
+
+
+def e4m3_decode(c: np.ndarray) -> np.ndarray:
+    """E4M3 codes -> float64 values (NaN for 0x7F / 0xFF)."""
+    c = np.ascontiguousarray(c, dtype=np.uint8)
+    out = np.empty(c.shape, np.float64)
+    lib().oracle_e4m3_decode_array(c.size, _p(c), _p(out))
+    return out
+
+
+def mx_dequantize(q: np.ndarray, scale: np.ndarray) -> np.ndarray:
+    """Values of MXFP8 rows: E4M3 value times 2^(scale code - 127), float64."""
+    q = np.asarray(q, np.uint8)
+    n, h = q.shape
+    s = np.repeat(np.asarray(scale, np.int64).reshape(n, h // 32) - 127, 32, axis=1)
+    return np.ldexp(e4m3_decode(q), s)
+
+
+def dispatch_mxfp8(x: np.ndarray, k: int, lay: dict, topk_w: np.ndarray, x_perm_q=None, x_perm_scale=None):
+    """MXFP8 dispatch: each token row quantised (mx_quantize), then its codes and
+    scales permuted like scatter() permutes bf16 rows -> (x_perm_q [rows, H],
+    x_perm_scale [rows, H/32], w_perm [rows]); pad rows are all-zero bytes."""
+    q, sc = mx_quantize(x)
+    pq, w_perm = scatter(q, k, lay, topk_w, x_perm_q)
+    ps, _ = scatter(sc, k, lay, topk_w, x_perm_scale)
+    return pq, ps, w_perm
 
 
 def expert_ffn_rows(rows, x_perm, lay, w_gate_up, w_down):

@@ -356,6 +356,79 @@ void oracle_scatter(int64_t n, int k, int64_t row_bytes, const uint8_t *x, const
   }
 }
 
+/* -------------------------------------------------------- MXFP8 dispatch */
+
+/* FP8 dispatch ([MORI] commit log: optional FP8 dispatch, a per-token scale
+ * tensor beside the quantised rows; the ROCm Megatron training script's MXFP8
+ * recipe).  Read as MXFP8 as the OCP "Microscaling (MX) Formats Specification"
+ * v1.0 defines it: each run of 32 consecutive elements of a row shares one
+ * E8M0 scale X = 2^s (code s + 127, s in [-127, 127]); element i is stored as
+ * the FP8 E4M3 code P_i of V_i / X.  The scale follows the specification's
+ * conversion: s = floor(log2(max_i |V_i|)) - 8 (8 = the largest E4M3 exponent),
+ * clipped to [-127, 127]; V_i / X is rounded to the nearest E4M3 value, ties
+ * to even, and magnitudes above the largest finite E4M3 value (448) are
+ * clamped to it.  An all-zero block is not covered by the formula (log2 0);
+ * read: code 0, the smallest scale (every element is 0 under any scale).
+ * Inputs must be finite. */
+
+/* Value of the non-negative E4M3 code c (0 .. 0x7E; 0x7F is NaN): exponent
+ * field e = c >> 3 (bias 7), mantissa m = c & 7; e = 0 is subnormal,
+ * m/8 * 2^-6, else (1 + m/8) * 2^(e-7). */
+static double e4m3_value(int c) {
+  const int e = c >> 3, m = c & 7;
+  return e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+}
+
+/* E4M3 code of v: |v| clamped to 448, then the nearest code by value (the
+ * codes 0 .. 0x7E ascend in value), ties to the even code; sign bit = sign of v. */
+static uint8_t e4m3_encode(double v) {
+  double a = fabs(v);
+  if (a > 448.0) a = 448.0;
+  int c = 0;
+  while (c < 0x7E && e4m3_value(c + 1) <= a) ++c; /* largest code not above a */
+  if (c < 0x7E) {
+    const double below = a - e4m3_value(c), above = e4m3_value(c + 1) - a;
+    if (above < below || (above == below && (c & 1))) ++c;
+  }
+  return (uint8_t)(c | (signbit(v) ? 0x80 : 0));
+}
+
+/* MXFP8 quantisation of `rows` bf16 rows of h elements (h a multiple of 32):
+ * q [rows, h] E4M3 codes, scale [rows, h/32] E8M0 codes. */
+void oracle_mx_quantize(int64_t rows, int64_t h, const uint16_t *x, uint8_t *q, uint8_t *scale) {
+  for (int64_t r = 0; r < rows; ++r)
+    for (int64_t b = 0; b < h / 32; ++b) {
+      const uint16_t *v = x + r * h + 32 * b;
+      double amax = 0.0;
+      for (int i = 0; i < 32; ++i)
+        if (fabs(bf16_value(v[i])) > amax) amax = fabs(bf16_value(v[i]));
+      int s = -127;
+      if (amax > 0.0) {
+        int ex;
+        frexp(amax, &ex); /* amax = f * 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1 */
+        s = ex - 1 - 8;
+        if (s < -127) s = -127;
+        if (s > 127) s = 127;
+      }
+      scale[r * (h / 32) + b] = (uint8_t)(s + 127);
+      for (int i = 0; i < 32; ++i) q[r * h + 32 * b + i] = e4m3_encode(ldexp(bf16_value(v[i]), -s));
+    }
+}
+
+/* Element-wise E4M3 encoding of n doubles (the element step alone, scale 1). */
+void oracle_e4m3_encode_array(int64_t n, const double *v, uint8_t *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = e4m3_encode(v[i]);
+}
+
+/* Values of n E4M3 codes (0x7F / 0xFF give NaN). */
+void oracle_e4m3_decode_array(int64_t n, const uint8_t *c, double *out) {
+  for (int64_t i = 0; i < n; ++i) {
+    const int m = c[i] & 0x7F;
+    const double v = m == 0x7F ? NAN : e4m3_value(m);
+    out[i] = (c[i] & 0x80) ? -v : v;
+  }
+}
+
 /* ------------------------------------------------------------- expert FFN */
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
