@@ -141,6 +141,25 @@ def bench_dispatch_combine(moe, mi, torch, steps, warmup):
     d1.record()
     torch.cuda.synchronize()
     dbwd_ms = d0.elapsed_time(d1) / steps
+    # MXFP8 dispatch (rows quantised to E4M3 + one E8M0 scale per 32 elements on the way)
+    q8 = torch.empty((xp.shape[0], h), dtype=torch.uint8, device=dev)
+    s8 = torch.empty((xp.shape[0], h // 32), dtype=torch.uint8, device=dev)
+    lay8 = moe.Layout.empty(n, k, e, 0, xp.shape[0], dev)
+
+    def mx_dispatch():
+        moe.moe_dispatch_mxfp8(x, r.topk_idx, r.topk_w, e, layout=lay8, x_perm_q=q8, x_perm_scale=s8,
+                               w_perm_out=wp, workspace=ws)
+
+    for _ in range(warmup):
+        mx_dispatch()
+    torch.cuda.synchronize()
+    d0.record()
+    for _ in range(steps):
+        mx_dispatch()
+    d1.record()
+    torch.cuda.synchronize()
+    mx_ms = d0.elapsed_time(d1) / steps
+    mx_bytes = n * row_b + kept * (h + h // 32)
     # the roofline kernel alone: back-to-back combine launches on the stream
     c0 = torch.cuda.Event(enable_timing=True)
     c1 = torch.cuda.Event(enable_timing=True)
@@ -198,6 +217,7 @@ def bench_dispatch_combine(moe, mi, torch, steps, warmup):
                 cold_combine_ms=median(cold_comb), cold_dc_ms=median(cold_dc),
                 cold_dc_p10=pct(cold_dc, 10), cold_dc_p90=pct(cold_dc, 90),
                 dispatch_bytes=dispatch_bytes, combine_bytes=combine_bytes, bwd_ms=bwd_ms, bwd_bytes=bwd_bytes,
+                mx_ms=mx_ms, mx_bytes=mx_bytes,
                 n=n, k=k, e=e, h=h)
 
 
@@ -505,6 +525,8 @@ def main():
                           for p, v in skew.items()},
         "dispatch_bwd_us": round(dc["dbwd_ms"] * 1e3, 2),
         "dispatch_bwd_gbs": round(dc["combine_bytes"] / (dc["dbwd_ms"] * 1e-3) / 1e9, 2),
+        "dispatch_mxfp8_us": round(dc["mx_ms"] * 1e3, 2),
+        "dispatch_mxfp8_gbs": round(dc["mx_bytes"] / (dc["mx_ms"] * 1e-3) / 1e9, 2),
         "combine_bwd_us": round(dc["bwd_ms"] * 1e3, 2),
         "combine_bwd_gbs": round(dc["bwd_bytes"] / (dc["bwd_ms"] * 1e-3) / 1e9, 2),
         "roofline": {"kernel": "combine_kernel<true, 8>", "bound": "hbm", "achieved": round(comb_gbs, 1),

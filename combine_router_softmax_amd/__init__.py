@@ -25,7 +25,8 @@ MOE_DROP_POSITION, MOE_DROP_PROBS = 0, 1
 MOE_OP_ROUTE, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE, MOE_OP_COMBINE_BWD, MOE_OP_EXPERT_FFN_BWD = range(6)
 
 # Every symbol include/moe.h declares.
-EXPORTS = ("moe_layout_rows", "moe_workspace_size", "moe_route", "moe_route_random", "moe_dispatch", "moe_expert_ffn",
+EXPORTS = ("moe_layout_rows", "moe_workspace_size", "moe_route", "moe_route_random", "moe_dispatch",
+           "moe_dispatch_mxfp8", "moe_expert_ffn",
            "moe_expert_ffn_bwd", "moe_combine", "moe_dispatch_bwd", "moe_combine_bwd", "moe_status_string",
            "moe_version")
 
@@ -59,12 +60,13 @@ def _load():
     lib.moe_route.argtypes = [sp, p, p, p, p, p, p, p, p]
     lib.moe_route_random.argtypes = [sp, C.c_uint64, p, p, p, p, p, p, p]
     lib.moe_dispatch.argtypes = [sp, p, p, p, lp, p, p, p, C.c_size_t, p]
+    lib.moe_dispatch_mxfp8.argtypes = [sp, p, p, p, lp, p, p, p, p, C.c_size_t, p]
     lib.moe_expert_ffn.argtypes = [sp, p, lp, p, p, p, p, p, C.c_size_t, p]
     lib.moe_expert_ffn_bwd.argtypes = [sp, p, p, p, lp, p, p, p, p, p, p, C.c_size_t, p]
     lib.moe_combine.argtypes = [sp, p, p, lp, p, p]
     lib.moe_combine_bwd.argtypes = [sp, p, p, p, lp, p, p, p]
     lib.moe_dispatch_bwd.argtypes = [sp, p, lp, p, p]
-    for f in ("moe_workspace_size", "moe_route", "moe_route_random", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_bwd", "moe_combine",
+    for f in ("moe_workspace_size", "moe_route", "moe_route_random", "moe_dispatch", "moe_dispatch_mxfp8", "moe_expert_ffn", "moe_expert_ffn_bwd", "moe_combine",
               "moe_combine_bwd", "moe_dispatch_bwd"):
         getattr(lib, f).restype = i32
     lib.moe_status_string.argtypes = [i32]
@@ -278,6 +280,48 @@ def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor |
     return x_perm, (w_perm_out if w_perm else None), layout
 
 
+def moe_dispatch_mxfp8(x: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor | None, n_experts: int, *,
+                       capacity: int = 0, max_rows: int = 0, row_align: int = 0,
+                       drop_policy: int = MOE_DROP_POSITION, w_perm: bool = True, layout: Layout | None = None,
+                       x_perm_q: torch.Tensor | None = None, x_perm_scale: torch.Tensor | None = None,
+                       w_perm_out: torch.Tensor | None = None, workspace=None):
+    """Layout + row scatter with MXFP8 quantisation (include/moe.h moe_dispatch_mxfp8):
+    bf16 x [N, H], H % 32 == 0 -> (x_perm_q uint8 [R, H] E4M3 codes, x_perm_scale uint8
+    [R, H/32] E8M0 codes, w_perm, layout).  Options as moe_dispatch."""
+    _contig(x, "x")
+    _contig(topk_idx, "topk_idx")
+    if x.dtype != torch.bfloat16:
+        raise TypeError("x must be bfloat16")
+    n, h = x.shape
+    k = topk_idx.shape[1]
+    dev = x.device
+    shape = make_shape(n, h, n_experts, k, capacity, 0, max_rows, MOE_DT_BF16, row_align, drop_policy)
+    rows = int(lib.moe_layout_rows(C.byref(shape)))
+    if rows < 0:
+        _check(-1, "moe_dispatch_mxfp8")
+    if layout is None:
+        layout = Layout.empty(n, k, n_experts, capacity, rows, dev, row_align, drop_policy)
+    if x_perm_q is None:
+        x_perm_q = torch.empty((rows, h), dtype=torch.uint8, device=dev)
+    if x_perm_scale is None:
+        x_perm_scale = torch.empty((rows, h // 32), dtype=torch.uint8, device=dev)
+    for t, name in ((x_perm_q, "x_perm_q"), (x_perm_scale, "x_perm_scale")):
+        _contig(t, name)
+        if t.dtype != torch.uint8:
+            raise TypeError(f"{name} must be uint8")
+    if w_perm and w_perm_out is None:
+        w_perm_out = torch.empty(rows, dtype=torch.float32, device=dev)
+    if workspace is None:
+        ws, nbytes = _workspace(MOE_OP_DISPATCH, shape, dev)
+    else:
+        ws, nbytes = workspace, workspace.numel() - 256
+    lc = layout.c()
+    _check(lib.moe_dispatch_mxfp8(C.byref(shape), _ptr(x), _ptr(topk_idx), _ptr(topk_w), C.byref(lc),
+                                  _ptr(x_perm_q), _ptr(x_perm_scale), _ptr(w_perm_out if w_perm else None),
+                                  _ws_ptr(ws), nbytes, _stream(dev)), "moe_dispatch_mxfp8")
+    return x_perm_q, x_perm_scale, (w_perm_out if w_perm else None), layout
+
+
 def moe_expert_ffn(x_perm: torch.Tensor, layout: Layout, w_gate_up: torch.Tensor, w_down: torch.Tensor, *,
                    y: torch.Tensor | None = None, gate_up: torch.Tensor | None = None, save_gate_up: bool = False,
                    workspace=None):
@@ -402,7 +446,7 @@ def moe_combine_bwd(grad_out: torch.Tensor, y: torch.Tensor, topk_w: torch.Tenso
     return grad_y, grad_w
 
 
-__all__ = ["moe_route", "moe_route_random", "moe_dispatch", "moe_expert_ffn", "moe_expert_ffn_bwd", "moe_combine", "moe_combine_bwd",
+__all__ = ["moe_route", "moe_route_random", "moe_dispatch", "moe_dispatch_mxfp8", "moe_expert_ffn", "moe_expert_ffn_bwd", "moe_combine", "moe_combine_bwd",
            "moe_dispatch_bwd",
            "Layout", "RouteOut",
            "MoeError", "make_shape", "workspace_size", "lib", "library_path", "EXPORTS"]

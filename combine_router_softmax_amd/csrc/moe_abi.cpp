@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <initializer_list>
+
 #include "moe_kernels.hpp"
 
 namespace {
@@ -149,6 +151,45 @@ moe_status moe_route_random(const moe_shape *s, uint64_t seed, const float *expe
                                       topk_w, routing_map, tokens_per_expert, as_stream(stream)));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Validation and layout launch shared by the bf16 and MXFP8 dispatch; `outs`
+// are the permuted-row outputs (each must be non-null when rows > 0).
+moe_status dispatch_layout(const moe_shape *s, int64_t rows, const void *x, const int32_t *topk_idx,
+                           const float *topk_w, const moe_layout *layout, std::initializer_list<const void *> outs,
+                           float *w_perm, void *workspace, size_t workspace_bytes, hipStream_t hs) {
+  if (!layout) return MOE_ERR_INVALID_ARG;
+  const int64_t n = s->n_tokens, a = n * s->top_k;
+  if (!layout->tokens_per_expert || !layout->expert_offsets || !layout->counters) return MOE_ERR_INVALID_ARG;
+  if ((a > 0 && (!topk_idx || !layout->ordinal || !layout->assign_row || !layout->drop_mask)) ||
+      (rows > 0 && (!layout->row_src || !layout->pad_mask)) || (n > 0 && !x) || (w_perm && a > 0 && !topk_w))
+    return MOE_ERR_INVALID_ARG;
+  for (const void *o : outs)
+    if (rows > 0 && !o) return MOE_ERR_INVALID_ARG;
+  if (!need(x, n, aligned16)) return MOE_ERR_MISALIGNED;
+  if (by_weight(s) && a > 0 && !topk_w) return MOE_ERR_INVALID_ARG;  // the policy ranks the weights
+  const size_t need_ws = moe::layout_workspace_bytes(a, s->n_experts, by_weight(s));
+  if (workspace_bytes < need_ws || (need_ws > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))))
+    return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_layout(topk_idx, topk_w, n, s->top_k, s->n_experts, s->capacity, s->row_align,
+                                       by_weight(s), rows, layout->tokens_per_expert, layout->expert_offsets,
+                                       layout->ordinal, layout->assign_row, layout->row_src, layout->drop_mask,
+                                       layout->pad_mask, layout->counters, w_perm, workspace, hs));
+}
+
+// Pad rows to zero: capacity pads (every row without an assignment), or the
+// pads of aligned segments (those below the end of the last segment).
+int64_t pad_rows_of(const moe_shape *s, int64_t rows) { return (s->capacity > 0 || s->row_align > 1) ? rows : 0; }
+const int32_t *pad_limit_of(const moe_shape *s, const moe_layout *layout) {
+  return s->capacity > 0 ? nullptr : layout->expert_offsets + s->n_experts;
+}
+
+}  // namespace
+
+extern "C" {
+
 moe_status moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_idx, const float *topk_w,
                         const moe_layout *layout, void *x_perm, float *w_perm, void *workspace,
                         size_t workspace_bytes, void *stream) {
@@ -156,31 +197,32 @@ moe_status moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_i
   if (st != MOE_OK) return st;
   int64_t row_bytes, rows;
   if ((st = check_rows(s, &row_bytes, &rows)) != MOE_OK) return st;
-  if (!layout) return MOE_ERR_INVALID_ARG;
-  const int64_t n = s->n_tokens, a = n * s->top_k;
-  if (!layout->tokens_per_expert || !layout->expert_offsets || !layout->counters) return MOE_ERR_INVALID_ARG;
-  if ((a > 0 && (!topk_idx || !layout->ordinal || !layout->assign_row || !layout->drop_mask)) ||
-      (rows > 0 && (!layout->row_src || !layout->pad_mask || !x_perm)) || (n > 0 && !x) ||
-      (w_perm && a > 0 && !topk_w))
-    return MOE_ERR_INVALID_ARG;
-  if (!need(x, n, aligned16) || !need(x_perm, rows, aligned16)) return MOE_ERR_MISALIGNED;
-  if (by_weight(s) && a > 0 && !topk_w) return MOE_ERR_INVALID_ARG;  // the policy ranks the weights
-  const size_t need_ws = moe::layout_workspace_bytes(a, s->n_experts, by_weight(s));
-  if (workspace_bytes < need_ws || (need_ws > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))))
-    return MOE_ERR_WORKSPACE;
+  if (!need(x_perm, rows, aligned16)) return MOE_ERR_MISALIGNED;
   hipStream_t hs = as_stream(stream);
-  hipError_t e = moe::launch_layout(topk_idx, topk_w, n, s->top_k, s->n_experts, s->capacity, s->row_align,
-                                    by_weight(s), rows,
-                                    layout->tokens_per_expert, layout->expert_offsets, layout->ordinal,
-                                    layout->assign_row, layout->row_src, layout->drop_mask, layout->pad_mask,
-                                    layout->counters, w_perm, workspace, hs);
-  if (e != hipSuccess) return MOE_ERR_HIP;
-  // pad rows to zero: capacity pads (every row without an assignment), or the
-  // pads of aligned segments (those below the end of the last segment)
-  const int64_t pad_rows = (s->capacity > 0 || s->row_align > 1) ? rows : 0;
-  const int32_t *pad_limit = s->capacity > 0 ? nullptr : layout->expert_offsets + s->n_experts;
-  return hip_status(moe::launch_scatter(x, n, s->top_k, row_bytes, layout->assign_row, x_perm, pad_rows, pad_limit,
-                                        layout->row_src, hs));
+  if ((st = dispatch_layout(s, rows, x, topk_idx, topk_w, layout, {x_perm}, w_perm, workspace, workspace_bytes, hs)) !=
+      MOE_OK)
+    return st;
+  return hip_status(moe::launch_scatter(x, s->n_tokens, s->top_k, row_bytes, layout->assign_row, x_perm,
+                                        pad_rows_of(s, rows), pad_limit_of(s, layout), layout->row_src, hs));
+}
+
+moe_status moe_dispatch_mxfp8(const moe_shape *s, const void *x, const int32_t *topk_idx, const float *topk_w,
+                              const moe_layout *layout, uint8_t *x_perm_q, uint8_t *x_perm_scale, float *w_perm,
+                              void *workspace, size_t workspace_bytes, void *stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  int64_t row_bytes, rows;
+  if ((st = check_rows(s, &row_bytes, &rows)) != MOE_OK) return st;
+  if (s->act_dtype != MOE_DT_BF16 || s->hidden % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  if (!need(x_perm_q, rows, aligned16)) return MOE_ERR_MISALIGNED;
+  if (rows > 0 && x_perm_q && x_perm_q == x_perm_scale) return MOE_ERR_INVALID_ARG;
+  hipStream_t hs = as_stream(stream);
+  if ((st = dispatch_layout(s, rows, x, topk_idx, topk_w, layout, {x_perm_q, x_perm_scale}, w_perm, workspace,
+                            workspace_bytes, hs)) != MOE_OK)
+    return st;
+  return hip_status(moe::launch_scatter_mxfp8(static_cast<const uint16_t *>(x), s->n_tokens, s->top_k, s->hidden,
+                                              layout->assign_row, x_perm_q, x_perm_scale, pad_rows_of(s, rows),
+                                              pad_limit_of(s, layout), layout->row_src, hs));
 }
 
 moe_status moe_expert_ffn(const moe_shape *s, const void *x_perm, const moe_layout *layout, const void *w_gate_up,

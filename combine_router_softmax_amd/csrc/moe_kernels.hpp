@@ -39,6 +39,12 @@ hipError_t launch_combine_bwd(bool bf16, const void *grad_out, const void *y, co
                               float *grad_w, int64_t pad_rows, const int32_t *pad_limit, const int32_t *row_src,
                               hipStream_t stream);
 
+// ---- MXFP8 dispatch (moe_mxfp8.hip): x bf16 [n, h], h % 32 == 0; q [rows, h]
+// E4M3 codes, scale [rows, h/32] E8M0 codes; pad rows as launch_scatter.
+hipError_t launch_scatter_mxfp8(const uint16_t *x, int64_t n, int k, int64_t h, const int32_t *assign_row,
+                                uint8_t *q, uint8_t *scale, int64_t pad_rows, const int32_t *pad_limit,
+                                const int32_t *row_src, hipStream_t stream);
+
 // ---- grouped SwiGLU FFN (moe_ffn.hip); bf16 operands as uint16_t bit patterns
 size_t ffn_workspace_bytes(int64_t rows, int inter);
 hipError_t launch_expert_ffn(const uint16_t *x_perm, int64_t rows, int64_t hidden, int inter, int e,

@@ -5,6 +5,7 @@
  *   moe_route_random the same over random logits (force-balanced benchmark mode)
  *   moe_dispatch    per-expert histogram + prefix sum, stable per-expert ordinals,
  *                   capacity drop/pad masks, row scatter into expert-contiguous rows
+ *   moe_dispatch_mxfp8 the same, the permuted rows quantised to MXFP8 (E4M3 + E8M0)
  *   moe_expert_ffn  grouped SwiGLU expert GEMM (bf16 MFMA, fp32 accumulation)
  *   moe_expert_ffn_bwd backward of moe_expert_ffn (grads of rows and weights)
  *   moe_combine     probability-weighted unpermute / combine (fp32 accumulation)
@@ -191,6 +192,30 @@ moe_status moe_route_random(const moe_shape *s, uint64_t seed, const float *expe
 moe_status moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_idx, const float *topk_w,
                         const moe_layout *layout, void *x_perm, float *w_perm, void *workspace,
                         size_t workspace_bytes, void *stream);
+
+/* MXFP8 dispatch: moe_dispatch with the permuted rows quantised to MXFP8 on the
+ * way (the optional FP8 dispatch of the MORI token dispatcher, ROCm/Megatron-LM
+ * "Add MORI as a Token Dispatcher": quantised rows plus a per-token scale
+ * tensor; MXFP8 as in the ROCm Megatron MXFP8 training recipe).  The format is
+ * the OCP "Microscaling (MX) Formats Specification" v1.0, blocks of 32
+ * consecutive elements of a row:
+ *   x_perm_scale[r, b] = s + 127 (E8M0), s = floor(log2(max_i |x_i|)) - 8
+ *     clipped to [-127, 127]; an all-zero block has code 0;
+ *   x_perm_q[r, 32b + i] = the FP8 E4M3 (OCP E4M3FN: bias 7, no infinities)
+ *     code of x_i / 2^s, rounded to nearest, ties to even, magnitudes above
+ *     448 clamped to 448 (the sign of x_i is kept, also for zero);
+ * with x_i the elements of block b of token row assign_row^-1(r).  Every other
+ * field, layout output, w_perm, stability and drop rule is as moe_dispatch.
+ * Pad rows are all-zero bytes in both outputs (a zero row quantised); rows of
+ * an unused dropless tail are not written.
+ * Shapes: x bf16 [N, H] (act_dtype must be MOE_DT_BF16 and H % 32 == 0, else
+ * MOE_ERR_UNSUPPORTED), 16-byte aligned; x_perm_q uint8 [R, H], 16-byte
+ * aligned; x_perm_scale uint8 [R, H/32], any alignment.  Inputs must be finite
+ * (a block holding an infinity or NaN gets unspecified codes).
+ * Workspace: moe_workspace_size(MOE_OP_DISPATCH). */
+moe_status moe_dispatch_mxfp8(const moe_shape *s, const void *x, const int32_t *topk_idx, const float *topk_w,
+                              const moe_layout *layout, uint8_t *x_perm_q, uint8_t *x_perm_scale, float *w_perm,
+                              void *workspace, size_t workspace_bytes, void *stream);
 
 /* Grouped SwiGLU expert FFN over the expert segments of a dispatch layout
  * ("Megatron MoE 实现", experts(dispatched_input, tokens_per_expert, ...), one

@@ -26,7 +26,7 @@ def moe():
 
 def test_library_exports_every_declared_function(moe):
     declared = header_functions()
-    assert len(declared) == 12, declared
+    assert len(declared) == 13, declared
     assert sorted(moe.EXPORTS) == declared
     for name in declared:
         assert hasattr(moe.lib, name), name
@@ -110,6 +110,19 @@ def test_validation_errors_enqueue_nothing(moe):
     assert lib.moe_dispatch(C.byref(s), p, p, p, C.byref(lay), p, p, p, 1 << 20, None) == -4
     s = moe.make_shape(16, 64, 8, 2, capacity=4, max_rows=7)                   # max_rows != E*C
     assert lib.moe_dispatch(C.byref(s), p, p, p, C.byref(lay), p, p, p, 1 << 20, None) == -1
+    mx = lib.moe_dispatch_mxfp8
+    q8, s8 = C.c_void_p(8192), C.c_void_p(12288)
+    s = moe.make_shape(16, 64, 8, 2, act_dtype=moe.MOE_DT_F32)                 # fp32 input
+    assert mx(C.byref(s), p, p, p, C.byref(lay), q8, s8, p, p, 1 << 20, None) == -4
+    s = moe.make_shape(16, 48, 8, 2)                                           # H % 32 != 0
+    assert mx(C.byref(s), p, p, p, C.byref(lay), q8, s8, p, p, 1 << 20, None) == -4
+    s = moe.make_shape(16, 64, 8, 2)
+    assert mx(C.byref(s), p, p, p, C.byref(lay), C.c_void_p(8200), s8, p, p, 1 << 20, None) == -2  # q misaligned
+    assert mx(C.byref(s), p, p, p, C.byref(lay), q8, None, p, p, 1 << 20, None) == -1   # no scale buffer
+    assert mx(C.byref(s), p, p, p, C.byref(lay), q8, q8, p, p, 1 << 20, None) == -1     # scales alias codes
+    assert mx(C.byref(s), odd, p, p, C.byref(lay), q8, s8, p, p, 1 << 20, None) == -2  # x misaligned
+    assert mx(C.byref(s), p, p, p, C.byref(lay), q8, s8, p, p, 0, None) == -3          # no workspace
+    assert mx(C.byref(s), p, p, p, None, q8, s8, p, p, 1 << 20, None) == -1
     s = moe.make_shape(16, 64, 8, 2, inter=64, act_dtype=moe.MOE_DT_F32)
     assert lib.moe_expert_ffn(C.byref(s), p, C.byref(lay), p, p, p, None, p, 1 << 30, None) == -4  # fp32 FFN
     s = moe.make_shape(16, 64, 8, 2, inter=96)

@@ -1,0 +1,149 @@
+"""GPU parity of moe_dispatch_mxfp8 against the CPU oracle, through the C ABI.
+Bit-exact: every layout array, every E4M3 code byte and E8M0 scale byte of the
+permuted rows, the permuted weights, and the zeroed pad rows."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+from parity_util import assert_layout_equal, dev, host, layout_host, values, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import combine_router_softmax_amd as m
+    return m
+
+
+def check_mx_dispatch(moe, x, idx, wts, e, capacity=0, max_rows=0, row_align=0, drop_policy=0):
+    q, sc, wp, lay = moe.moe_dispatch_mxfp8(dev(x), dev(idx), dev(wts), e, capacity=capacity, max_rows=max_rows,
+                                            row_align=row_align, drop_policy=drop_policy)
+    torch.cuda.synchronize()
+    ref = oracle.layout(idx, e, capacity, max_rows, row_align, drop_policy, wts)
+    assert_layout_equal(layout_host(lay), ref)
+    q_h, sc_h = host(q), host(sc)
+    # rows of an unused dropless tail are not written: the oracle keeps what the GPU left there
+    ref_q, ref_sc, ref_wp = oracle.dispatch_mxfp8(x, idx.shape[1], ref, wts, x_perm_q=q_h.copy(),
+                                                  x_perm_scale=sc_h.copy())
+    np.testing.assert_array_equal(sc_h, ref_sc)
+    np.testing.assert_array_equal(q_h, ref_q)
+    np.testing.assert_array_equal(host(wp), ref_wp)
+    return q_h, sc_h, ref
+
+
+@pytest.mark.parametrize("n,h,e,k", [(300, 256, 16, 4), (1001, 7168, 256, 8), (513, 4096, 128, 8), (77, 32, 3, 2),
+                                     (129, 9216, 8, 1), (64, 11264, 64, 12)])
+def test_mx_dispatch_shapes(moe, n, h, e, k):
+    """Several tiles of blocks per row, rows longer than one workgroup's 256
+    blocks (H = 9216, 11264), k not a multiple of the slot chunk."""
+    g = np.random.default_rng(n + h + e + k)
+    idx = np.stack([g.permutation(e)[:k] for _ in range(n)]).astype(np.int32)
+    wts = g.random((n, k)).astype(np.float32)
+    x = mi.normal_activations((n, h), mi.DT_BF16, 91, n)
+    check_mx_dispatch(moe, x, idx, wts, e)
+
+
+@pytest.mark.parametrize("order", ["shuffled", "by_magnitude"])
+def test_mx_dispatch_every_bf16_value(moe, order):
+    """Every finite bf16 bit pattern, in blocks of mixed magnitudes (small
+    elements rounded into E4M3's subnormals or to signed zero) and in blocks of
+    similar magnitudes (every scale code, the clipped smallest scale included)."""
+    b = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    b = b[((b >> 7) & 0xFF) != 0xFF]                                # 65280 finite patterns
+    if order == "shuffled":
+        b = np.random.default_rng(3).permutation(b)
+    else:
+        b = b[np.argsort(b & 0x7FFF, kind="stable")]
+    x = b.reshape(-1, 256)                                          # 255 token rows
+    n = x.shape[0]
+    idx = np.stack([np.arange(n) % 5, (np.arange(n) + 2) % 5], axis=1).astype(np.int32)
+    wts = np.ones((n, 2), np.float32)
+    q, sc, ref = check_mx_dispatch(moe, x, idx, wts, 5)
+    if order == "by_magnitude":
+        assert {0, 1, 119, 127} <= set(np.unique(sc).tolist())
+
+
+@pytest.mark.parametrize("case", ["capacity", "capacity_by_weight", "align64", "align16_clip_rows", "sentinels",
+                                  "invalid_ids", "clip_rows", "zero_rows"])
+def test_mx_dispatch_edge_cases(moe, case):
+    g = np.random.default_rng(200 + len(case))
+    n, e, k, h, cap, max_rows, align, policy = 1001, 64, 8, 512, 0, 0, 0, 0
+    idx = np.stack([g.permutation(e)[:k] for _ in range(n)]).astype(np.int32)
+    if case.startswith("capacity"):
+        cap = 128                                                   # about 125 per expert: drops and pads
+        policy = 1 if case.endswith("by_weight") else 0
+    if case.startswith("align"):
+        align = int(case[5:].split("_")[0])
+    if case.endswith("clip_rows"):
+        max_rows = n * k - 555
+    if case == "sentinels":
+        idx[g.random(idx.shape) < 0.75] = -1
+    if case == "invalid_ids":
+        bad = g.random(idx.shape) < 0.05
+        idx[bad] = g.choice([-5, e, e + 100, -2], size=bad.sum())
+    wts = g.random((n, k)).astype(np.float32)
+    x = mi.normal_activations((n, h), mi.DT_BF16, 92, 1)
+    if case == "zero_rows":
+        x[::3] = 0
+        x[1::3, :64] = 0x8000                                       # -0.0: code 0x80, scale code 0
+    q, sc, ref = check_mx_dispatch(moe, x, idx, wts, e, cap, max_rows, align, policy)
+    if cap or align:
+        pads = np.nonzero(ref["row_src"][:ref["expert_offsets"][-1]] < 0)[0]
+        assert pads.size and not q[pads].any() and not sc[pads].any()
+    if cap:
+        assert ref["counters"][1] > 0                               # some assignments dropped
+
+
+def test_mx_dispatch_empty(moe):
+    x = np.zeros((0, 256), np.uint16)
+    idx = np.zeros((0, 2), np.int32)
+    wts = np.zeros((0, 2), np.float32)
+    check_mx_dispatch(moe, x, idx, wts, 8)
+    q, sc, ref = check_mx_dispatch(moe, x, idx, wts, 8, capacity=3)
+    assert not q.any() and not sc.any()
+
+
+@pytest.mark.parametrize("wid", [2, 3, 5])
+def test_mx_dispatch_full_size(moe, wid):
+    """Full-size workloads (uniform dropless; Zipf with capacity; the expert
+    share with -1 sentinels and a row limit): the layout equals the bf16
+    dispatch's, every kept row equals the oracle's quantisation of its token
+    row byte for byte, and the dequantised rows lie within half an E4M3 grid
+    step of the bf16 rows of moe_dispatch (clamped elements within their clamp
+    distance)."""
+    w = mi.workload(wid)
+    idx, wts, logits, x = workload_inputs(w)
+    if idx is None:
+        idx, wts, _, _ = oracle.route(logits, w.top_k)
+    x_d, idx_d, w_d = dev(x), dev(idx), dev(wts)
+    q, sc, wp, lay = moe.moe_dispatch_mxfp8(x_d, idx_d, w_d, w.n_experts, capacity=w.capacity, max_rows=w.rows)
+    xp, wp16, lay16 = moe.moe_dispatch(x_d, idx_d, w_d, w.n_experts, capacity=w.capacity, max_rows=w.rows)
+    torch.cuda.synchronize()
+    got = layout_host(lay)
+    assert_layout_equal(got, layout_host(lay16))
+    assert torch.equal(wp, wp16)
+    k = w.top_k
+    ref_q, ref_sc = oracle.mx_quantize(x)
+    rows = np.nonzero(got["row_src"] >= 0)[0]
+    tok = got["row_src"][rows] // k
+    q_h, sc_h = host(q), host(sc)
+    bad = np.nonzero((q_h[rows] != ref_q[tok]).any(axis=1) | (sc_h[rows] != ref_sc[tok]).any(axis=1))[0]
+    assert bad.size == 0, f"{bad.size} rows differ, first rows {rows[bad[:8]]} (tokens {tok[bad[:8]]})"
+    pads = np.nonzero(got["row_src"][:got["expert_offsets"][-1]] < 0)[0]
+    assert not q_h[pads].any() and not sc_h[pads].any()
+    g = np.random.default_rng(wid)
+    sample = g.choice(rows, 256, replace=False)
+    v = values(host(xp)[sample])
+    deq = oracle.mx_dequantize(q_h[sample], sc_h[sample])
+    s = np.repeat(sc_h[sample].astype(np.int64) - 127, 32, axis=1)
+    a = np.abs(v) / 2.0 ** s
+    e = np.maximum(np.floor(np.log2(np.where(a > 0, a, 1.0))), -6)
+    bound = np.where(a > 448, np.abs(v) - 448 * 2.0 ** s, 2.0 ** (s + e - 4))
+    assert (np.abs(deq - v) <= bound).all()
