@@ -71,6 +71,14 @@ def lib():
         L.oracle_bf16_round_array.restype = None
         L.oracle_bf16_round.restype = C.c_uint16
         L.oracle_mx_quantize.argtypes = [i64, i64, p, p, p]
+        L.oracle_replica_plan.argtypes = [i32, p, i32, p]
+        L.oracle_replica_plan.restype = None
+        L.oracle_reroute.argtypes = [i64, i32, i32, p, i32, p, p]
+        L.oracle_reroute.restype = None
+        L.oracle_replica_sync.argtypes = [i32, p, i64, p, p]
+        L.oracle_replica_sync.restype = None
+        L.oracle_replica_grad_reduce.argtypes = [i32, i32, p, i64, p, p]
+        L.oracle_replica_grad_reduce.restype = None
         L.oracle_mx_quantize.restype = None
         L.oracle_e4m3_encode_array.argtypes = [i64, p, p]
         L.oracle_e4m3_encode_array.restype = None
@@ -226,6 +234,44 @@ def dispatch_mxfp8(x: np.ndarray, k: int, lay: dict, topk_w: np.ndarray, x_perm_
     pq, w_perm = scatter(q, k, lay, topk_w, x_perm_q)
     ps, _ = scatter(sc, k, lay, topk_w, x_perm_scale)
     return pq, ps, w_perm
+
+
+def replica_plan(counts: np.ndarray, r: int) -> np.ndarray:
+    """Hot-expert placement: logical expert of each of r replica slots."""
+    counts = np.ascontiguousarray(counts, dtype=np.int32)
+    out = np.empty(r, np.int32)
+    lib().oracle_replica_plan(counts.size, _p(counts), r, _p(out))
+    return out
+
+
+def reroute(topk_idx: np.ndarray, n_experts: int, replica_of: np.ndarray) -> np.ndarray:
+    """Logical -> physical expert ids [N, k] (physical E + i = replica slot i)."""
+    idx = np.ascontiguousarray(topk_idx, dtype=np.int32)
+    rep = np.ascontiguousarray(replica_of, dtype=np.int32)
+    out = np.empty_like(idx)
+    n, k = idx.shape
+    lib().oracle_reroute(n, k, n_experts, _p(idx), rep.size, _p(rep), _p(out))
+    return out
+
+
+def replica_sync(master: np.ndarray, replica_of: np.ndarray) -> np.ndarray:
+    """Replica weights [R, ...] copied from the masters [E, ...] (bf16 bits)."""
+    master = np.ascontiguousarray(master, dtype=np.uint16)
+    rep = np.ascontiguousarray(replica_of, dtype=np.int32)
+    out = np.empty((rep.size,) + master.shape[1:], np.uint16)
+    elems = int(np.prod(master.shape[1:]))
+    lib().oracle_replica_sync(rep.size, _p(rep), elems, _p(master), _p(out))
+    return out
+
+
+def replica_grad_reduce(grad_master: np.ndarray, grad_replica: np.ndarray, replica_of: np.ndarray) -> np.ndarray:
+    """Master gradients [E, ...] plus their replicas' [R, ...] (bf16 bits, one rounding)."""
+    gm = np.ascontiguousarray(grad_master, dtype=np.uint16).copy()
+    gr = np.ascontiguousarray(grad_replica, dtype=np.uint16)
+    rep = np.ascontiguousarray(replica_of, dtype=np.int32)
+    elems = int(np.prod(gm.shape[1:]))
+    lib().oracle_replica_grad_reduce(gm.shape[0], rep.size, _p(rep), elems, _p(gr), _p(gm))
+    return gm
 
 
 def expert_ffn_rows(rows, x_perm, lay, w_gate_up, w_down):

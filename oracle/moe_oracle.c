@@ -429,6 +429,87 @@ void oracle_e4m3_decode_array(int64_t n, const uint8_t *c, double *out) {
   }
 }
 
+/* ------------------------------------------------ hot-expert replication */
+
+/* [UEP] InternLM/xtuner pull request "Integrate UltraEP Runtime": replicas of
+ * hot experts created from the current load, part of their tokens rerouted to
+ * the replica slots (logical -> physical placement and reroute), replica
+ * weights synchronised from the masters, one grouped GEMM over master and
+ * replica experts (weights from two storage bases), replica weight gradients
+ * written to a replica buffer and reduced into the masters'.  The pages give
+ * no placement or split rule; readings:
+ *   placement: R slots filled one at a time, each going to the logical expert
+ *     with the largest load per copy, count_e / (1 + slots_e) (ties: lowest e);
+ *   reroute: expert e's count_e assignments, in assignment order, are cut into
+ *     m_e = 1 + slots_e consecutive runs as equal as the count allows (run j
+ *     holds ordinals ceil(j count/m) .. ceil((j+1) count/m) - 1); run 0 stays
+ *     on the master, run j >= 1 goes to e's j-th slot in slot order.
+ * Physical expert p < E is the master of logical expert p, p = E + i is slot i. */
+
+/* Placement: replica_of[i] = logical expert of slot i, i = 0 .. r-1. */
+void oracle_replica_plan(int e, const int32_t *counts, int r, int32_t *replica_of) {
+  int *slots = calloc((size_t)e, sizeof(int));
+  for (int i = 0; i < r; ++i) {
+    int best = 0;
+    for (int x = 1; x < e; ++x) /* counts[x]/(1+slots[x]) > counts[best]/(1+slots[best]), exactly */
+      if ((int64_t)counts[x] * (1 + slots[best]) > (int64_t)counts[best] * (1 + slots[x])) best = x;
+    replica_of[i] = best;
+    ++slots[best];
+  }
+  free(slots);
+}
+
+/* Reroute of logical ids idx [n*k] to physical ids phys [n*k]: -1 stays -1,
+ * an id outside [0, E) becomes -2 (still invalid for the E + r physical
+ * experts), a valid id goes to the copy whose run holds its ordinal. */
+void oracle_reroute(int64_t n, int k, int e, const int32_t *idx, int r, const int32_t *replica_of, int32_t *phys) {
+  const int64_t a_n = n * k;
+  int64_t *count = calloc((size_t)e, sizeof(int64_t)), *seen = calloc((size_t)e, sizeof(int64_t));
+  for (int64_t a = 0; a < a_n; ++a)
+    if (idx[a] >= 0 && idx[a] < e) ++count[idx[a]];
+  for (int64_t a = 0; a < a_n; ++a) {
+    const int32_t x = idx[a];
+    if (x == -1) { phys[a] = -1; continue; }
+    if (x < 0 || x >= e) { phys[a] = -2; continue; }
+    int m = 1;
+    for (int i = 0; i < r; ++i) m += replica_of[i] == x;
+    const int64_t o = seen[x]++;
+    int run = 0; /* the run whose ordinal range [ceil(j c/m), ceil((j+1) c/m)) holds o */
+    while (!(o >= (run * count[x] + m - 1) / m && o < ((run + 1) * count[x] + m - 1) / m)) ++run;
+    if (run == 0) { phys[a] = x; continue; }
+    int slot = -1, found = 0; /* e's run-th slot, in slot order */
+    for (int i = 0; i < r && found < run; ++i)
+      if (replica_of[i] == x && ++found == run) slot = i;
+    phys[a] = e + slot;
+  }
+  free(count);
+  free(seen);
+}
+
+/* Replica weight sync: slot i's weights [elems] = its master's. */
+void oracle_replica_sync(int r, const int32_t *replica_of, int64_t elems, const uint16_t *master, uint16_t *replica) {
+  for (int i = 0; i < r; ++i)
+    memcpy(replica + (int64_t)i * elems, master + (int64_t)replica_of[i] * elems, (size_t)elems * 2);
+}
+
+/* Replica gradient reduce: for every expert with slots, grad_master[e] =
+ * bf16(grad_master[e] + the sum of its slots' gradients), the sum exact
+ * (double; a handful of bf16 terms), one rounding. */
+void oracle_replica_grad_reduce(int e, int r, const int32_t *replica_of, int64_t elems, const uint16_t *grad_replica,
+                                uint16_t *grad_master) {
+  for (int x = 0; x < e; ++x) {
+    int any = 0;
+    for (int i = 0; i < r; ++i) any |= replica_of[i] == x;
+    if (!any) continue;
+    for (int64_t v = 0; v < elems; ++v) {
+      double acc = bf16_value(grad_master[(int64_t)x * elems + v]);
+      for (int i = 0; i < r; ++i)
+        if (replica_of[i] == x) acc += bf16_value(grad_replica[(int64_t)i * elems + v]);
+      grad_master[(int64_t)x * elems + v] = bf16_round(acc);
+    }
+  }
+}
+
 /* ------------------------------------------------------------- expert FFN */
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
