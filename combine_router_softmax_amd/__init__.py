@@ -22,13 +22,15 @@ _LIB_PATH = Path(__file__).resolve().parent / "libmoe_mi355x.so"
 MOE_DT_F32 = 0
 MOE_DT_BF16 = 1
 MOE_DROP_POSITION, MOE_DROP_PROBS = 0, 1
-MOE_OP_ROUTE, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE, MOE_OP_COMBINE_BWD, MOE_OP_EXPERT_FFN_BWD = range(6)
+(MOE_OP_ROUTE, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE, MOE_OP_COMBINE_BWD, MOE_OP_EXPERT_FFN_BWD,
+ MOE_OP_REROUTE) = range(7)
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_layout_rows", "moe_workspace_size", "moe_route", "moe_route_random", "moe_dispatch",
            "moe_dispatch_mxfp8", "moe_expert_ffn",
            "moe_expert_ffn_bwd", "moe_combine", "moe_dispatch_bwd", "moe_combine_bwd", "moe_status_string",
-           "moe_version")
+           "moe_version", "moe_replica_plan", "moe_reroute", "moe_replica_sync", "moe_replica_grad_reduce",
+           "moe_expert_ffn_replicas", "moe_expert_ffn_bwd_replicas")
 
 
 class MoeShape(C.Structure):
@@ -66,8 +68,15 @@ def _load():
     lib.moe_combine.argtypes = [sp, p, p, lp, p, p]
     lib.moe_combine_bwd.argtypes = [sp, p, p, p, lp, p, p, p]
     lib.moe_dispatch_bwd.argtypes = [sp, p, lp, p, p]
+    lib.moe_replica_plan.argtypes = [sp, p, i32, p, p]
+    lib.moe_reroute.argtypes = [sp, p, p, i32, p, p, C.c_size_t, p]
+    lib.moe_replica_sync.argtypes = [sp, p, i32, p, p, p, p, p]
+    lib.moe_replica_grad_reduce.argtypes = [sp, p, i32, p, p, p, p, p]
+    lib.moe_expert_ffn_replicas.argtypes = [sp, i32, p, lp, p, p, p, p, p, p, p, C.c_size_t, p]
+    lib.moe_expert_ffn_bwd_replicas.argtypes = [sp, i32, p, p, p, lp, p, p, p, p, p, p, p, p, p, p, C.c_size_t, p]
     for f in ("moe_workspace_size", "moe_route", "moe_route_random", "moe_dispatch", "moe_dispatch_mxfp8", "moe_expert_ffn", "moe_expert_ffn_bwd", "moe_combine",
-              "moe_combine_bwd", "moe_dispatch_bwd"):
+              "moe_combine_bwd", "moe_dispatch_bwd", "moe_replica_plan", "moe_reroute", "moe_replica_sync",
+              "moe_replica_grad_reduce", "moe_expert_ffn_replicas", "moe_expert_ffn_bwd_replicas"):
         getattr(lib, f).restype = i32
     lib.moe_status_string.argtypes = [i32]
     lib.moe_status_string.restype = C.c_char_p
@@ -322,21 +331,34 @@ def moe_dispatch_mxfp8(x: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Te
     return x_perm_q, x_perm_scale, (w_perm_out if w_perm else None), layout
 
 
-def moe_expert_ffn(x_perm: torch.Tensor, layout: Layout, w_gate_up: torch.Tensor, w_down: torch.Tensor, *,
-                   y: torch.Tensor | None = None, gate_up: torch.Tensor | None = None, save_gate_up: bool = False,
-                   workspace=None):
-    """Grouped SwiGLU FFN (include/moe.h moe_expert_ffn): bf16 x_perm [R, H], w_gate_up [E, 2I, H], w_down [E, H, I].
-    Returns y [R, H]; with save_gate_up (or a gate_up buffer [R, 2I]) returns (y, gate_up), the
-    pre-activations moe_expert_ffn_bwd can take."""
-    for t, name in ((x_perm, "x_perm"), (w_gate_up, "w_gate_up"), (w_down, "w_down")):
+def _bf16(*named):
+    for t, name in named:
         _contig(t, name)
         if t.dtype != torch.bfloat16:
             raise TypeError(f"{name} must be bfloat16")
+
+
+def _ffn_shapes(x_perm, layout, w_gate_up, w_down, w_gate_up_replica, w_down_replica):
+    """(rows, H, I, R) of a grouped FFN call; the masters and the R replica slots
+    together are the layout's experts."""
+    _bf16((x_perm, "x_perm"), (w_gate_up, "w_gate_up"), (w_down, "w_down"))
     rows, h = x_perm.shape
     e, two_i, h2 = w_gate_up.shape
     inter = two_i // 2
-    if h2 != h or tuple(w_down.shape) != (e, h, inter) or e != layout.n_experts or rows != layout.rows:
+    r = 0
+    if w_gate_up_replica is not None or w_down_replica is not None:
+        _bf16((w_gate_up_replica, "w_gate_up_replica"), (w_down_replica, "w_down_replica"))
+        r = w_gate_up_replica.shape[0]
+        if (tuple(w_gate_up_replica.shape) != (r, two_i, h) or tuple(w_down_replica.shape) != (r, h, inter)):
+            raise ValueError("replica weights must be [R, 2I, H] and [R, H, I]")
+    if h2 != h or tuple(w_down.shape) != (e, h, inter) or e + r != layout.n_experts or rows != layout.rows:
         raise ValueError("inconsistent expert FFN shapes")
+    return rows, h, inter, r
+
+
+def _expert_ffn(x_perm, layout, w_gate_up, w_down, w_gate_up_replica, w_down_replica, y, gate_up, save_gate_up,
+                workspace):
+    rows, h, inter, r = _ffn_shapes(x_perm, layout, w_gate_up, w_down, w_gate_up_replica, w_down_replica)
     dev = x_perm.device
     shape = layout.shape(h, MOE_DT_BF16, inter)
     if y is None:
@@ -352,27 +374,42 @@ def moe_expert_ffn(x_perm: torch.Tensor, layout: Layout, w_gate_up: torch.Tensor
         _contig(gate_up, "gate_up")
         if gate_up.dtype != torch.bfloat16 or tuple(gate_up.shape) != (rows, 2 * inter):
             raise ValueError("gate_up must be bfloat16 [R, 2I]")
-    _check(lib.moe_expert_ffn(C.byref(shape), _ptr(x_perm), C.byref(lc), _ptr(w_gate_up), _ptr(w_down), _ptr(y),
-                              _ptr(gate_up), _ws_ptr(ws), nbytes, _stream(dev)), "moe_expert_ffn")
+    if r == 0 and w_gate_up_replica is None:
+        _check(lib.moe_expert_ffn(C.byref(shape), _ptr(x_perm), C.byref(lc), _ptr(w_gate_up), _ptr(w_down), _ptr(y),
+                                  _ptr(gate_up), _ws_ptr(ws), nbytes, _stream(dev)), "moe_expert_ffn")
+    else:
+        _check(lib.moe_expert_ffn_replicas(C.byref(shape), r, _ptr(x_perm), C.byref(lc), _ptr(w_gate_up),
+                                           _ptr(w_down), _ptr(w_gate_up_replica), _ptr(w_down_replica), _ptr(y),
+                                           _ptr(gate_up), _ws_ptr(ws), nbytes, _stream(dev)),
+               "moe_expert_ffn_replicas")
     return (y, gate_up) if gate_up is not None else y
 
 
-def moe_expert_ffn_bwd(x_perm: torch.Tensor, grad_y: torch.Tensor, layout: Layout, w_gate_up: torch.Tensor,
-                       w_down: torch.Tensor, *, gate_up: torch.Tensor | None = None,
-                       grad_x_perm: torch.Tensor | None = None, grad_w_gate_up: torch.Tensor | None = None,
-                       grad_w_down: torch.Tensor | None = None, workspace=None):
-    """Backward of the grouped SwiGLU FFN (include/moe.h moe_expert_ffn_bwd)
-    -> (grad_x_perm [R, H], grad_w_gate_up [E, 2I, H], grad_w_down [E, H, I]), all bf16.
-    gate_up: the pre-activations saved by moe_expert_ffn (None: recomputed)."""
-    for t, name in ((x_perm, "x_perm"), (grad_y, "grad_y"), (w_gate_up, "w_gate_up"), (w_down, "w_down")):
-        _contig(t, name)
-        if t.dtype != torch.bfloat16:
-            raise TypeError(f"{name} must be bfloat16")
-    rows, h = x_perm.shape
-    e, two_i, h2 = w_gate_up.shape
-    inter = two_i // 2
-    if (h2 != h or tuple(w_down.shape) != (e, h, inter) or tuple(grad_y.shape) != (rows, h)
-            or e != layout.n_experts or rows != layout.rows):
+def moe_expert_ffn(x_perm: torch.Tensor, layout: Layout, w_gate_up: torch.Tensor, w_down: torch.Tensor, *,
+                   y: torch.Tensor | None = None, gate_up: torch.Tensor | None = None, save_gate_up: bool = False,
+                   workspace=None):
+    """Grouped SwiGLU FFN (include/moe.h moe_expert_ffn): bf16 x_perm [R, H], w_gate_up [E, 2I, H], w_down [E, H, I].
+    Returns y [R, H]; with save_gate_up (or a gate_up buffer [R, 2I]) returns (y, gate_up), the
+    pre-activations moe_expert_ffn_bwd can take."""
+    return _expert_ffn(x_perm, layout, w_gate_up, w_down, None, None, y, gate_up, save_gate_up, workspace)
+
+
+def moe_expert_ffn_replicas(x_perm: torch.Tensor, layout: Layout, w_gate_up: torch.Tensor, w_down: torch.Tensor,
+                            w_gate_up_replica: torch.Tensor, w_down_replica: torch.Tensor, *,
+                            y: torch.Tensor | None = None, gate_up: torch.Tensor | None = None,
+                            save_gate_up: bool = False, workspace=None):
+    """moe_expert_ffn over physical experts (include/moe.h moe_expert_ffn_replicas): the layout's
+    last R experts are replica slots with weights w_gate_up_replica [R, 2I, H], w_down_replica [R, H, I]."""
+    return _expert_ffn(x_perm, layout, w_gate_up, w_down, w_gate_up_replica, w_down_replica, y, gate_up,
+                       save_gate_up, workspace)
+
+
+def _expert_ffn_bwd(x_perm, grad_y, layout, w_gate_up, w_down, w_gate_up_replica, w_down_replica, gate_up,
+                    grad_x_perm, grad_w_gate_up, grad_w_down, grad_w_gate_up_replica, grad_w_down_replica,
+                    workspace):
+    rows, h, inter, r = _ffn_shapes(x_perm, layout, w_gate_up, w_down, w_gate_up_replica, w_down_replica)
+    _bf16((grad_y, "grad_y"))
+    if tuple(grad_y.shape) != (rows, h):
         raise ValueError("inconsistent expert FFN shapes")
     if gate_up is not None:
         _contig(gate_up, "gate_up")
@@ -391,10 +428,113 @@ def moe_expert_ffn_bwd(x_perm: torch.Tensor, grad_y: torch.Tensor, layout: Layou
     else:
         ws, nbytes = workspace, workspace.numel() - 256
     lc = layout.c()
-    _check(lib.moe_expert_ffn_bwd(C.byref(shape), _ptr(x_perm), _ptr(grad_y), _ptr(gate_up), C.byref(lc),
-                                  _ptr(w_gate_up), _ptr(w_down), _ptr(grad_x_perm), _ptr(grad_w_gate_up),
-                                  _ptr(grad_w_down), _ws_ptr(ws), nbytes, _stream(dev)), "moe_expert_ffn_bwd")
-    return grad_x_perm, grad_w_gate_up, grad_w_down
+    if w_gate_up_replica is None:
+        _check(lib.moe_expert_ffn_bwd(C.byref(shape), _ptr(x_perm), _ptr(grad_y), _ptr(gate_up), C.byref(lc),
+                                      _ptr(w_gate_up), _ptr(w_down), _ptr(grad_x_perm), _ptr(grad_w_gate_up),
+                                      _ptr(grad_w_down), _ws_ptr(ws), nbytes, _stream(dev)), "moe_expert_ffn_bwd")
+        return grad_x_perm, grad_w_gate_up, grad_w_down
+    if grad_w_gate_up_replica is None:
+        grad_w_gate_up_replica = torch.empty_like(w_gate_up_replica)
+    if grad_w_down_replica is None:
+        grad_w_down_replica = torch.empty_like(w_down_replica)
+    _check(lib.moe_expert_ffn_bwd_replicas(C.byref(shape), r, _ptr(x_perm), _ptr(grad_y), _ptr(gate_up), C.byref(lc),
+                                           _ptr(w_gate_up), _ptr(w_down), _ptr(w_gate_up_replica),
+                                           _ptr(w_down_replica), _ptr(grad_x_perm), _ptr(grad_w_gate_up),
+                                           _ptr(grad_w_down), _ptr(grad_w_gate_up_replica),
+                                           _ptr(grad_w_down_replica), _ws_ptr(ws), nbytes, _stream(dev)),
+           "moe_expert_ffn_bwd_replicas")
+    return grad_x_perm, grad_w_gate_up, grad_w_down, grad_w_gate_up_replica, grad_w_down_replica
+
+
+def moe_expert_ffn_bwd(x_perm: torch.Tensor, grad_y: torch.Tensor, layout: Layout, w_gate_up: torch.Tensor,
+                       w_down: torch.Tensor, *, gate_up: torch.Tensor | None = None,
+                       grad_x_perm: torch.Tensor | None = None, grad_w_gate_up: torch.Tensor | None = None,
+                       grad_w_down: torch.Tensor | None = None, workspace=None):
+    """Backward of the grouped SwiGLU FFN (include/moe.h moe_expert_ffn_bwd)
+    -> (grad_x_perm [R, H], grad_w_gate_up [E, 2I, H], grad_w_down [E, H, I]), all bf16.
+    gate_up: the pre-activations saved by moe_expert_ffn (None: recomputed)."""
+    return _expert_ffn_bwd(x_perm, grad_y, layout, w_gate_up, w_down, None, None, gate_up, grad_x_perm,
+                           grad_w_gate_up, grad_w_down, None, None, workspace)
+
+
+def moe_expert_ffn_bwd_replicas(x_perm: torch.Tensor, grad_y: torch.Tensor, layout: Layout, w_gate_up: torch.Tensor,
+                                w_down: torch.Tensor, w_gate_up_replica: torch.Tensor, w_down_replica: torch.Tensor,
+                                *, gate_up: torch.Tensor | None = None, grad_x_perm: torch.Tensor | None = None,
+                                grad_w_gate_up: torch.Tensor | None = None, grad_w_down: torch.Tensor | None = None,
+                                grad_w_gate_up_replica: torch.Tensor | None = None,
+                                grad_w_down_replica: torch.Tensor | None = None, workspace=None):
+    """Backward with replica slots (include/moe.h moe_expert_ffn_bwd_replicas) -> (grad_x_perm,
+    grad_w_gate_up, grad_w_down, grad_w_gate_up_replica, grad_w_down_replica)."""
+    return _expert_ffn_bwd(x_perm, grad_y, layout, w_gate_up, w_down, w_gate_up_replica, w_down_replica, gate_up,
+                           grad_x_perm, grad_w_gate_up, grad_w_down, grad_w_gate_up_replica, grad_w_down_replica,
+                           workspace)
+
+
+def moe_replica_plan(tokens_per_expert: torch.Tensor, n_replicas: int, *, out: torch.Tensor | None = None):
+    """Hot-expert placement (include/moe.h moe_replica_plan) -> replica_of int32 [n_replicas]."""
+    _contig(tokens_per_expert, "tokens_per_expert")
+    e = tokens_per_expert.numel()
+    dev = tokens_per_expert.device
+    if out is None:
+        out = torch.empty(n_replicas, dtype=torch.int32, device=dev)
+    shape = make_shape(0, 1, e, 1)
+    _check(lib.moe_replica_plan(C.byref(shape), _ptr(tokens_per_expert), n_replicas, _ptr(out), _stream(dev)),
+           "moe_replica_plan")
+    return out
+
+
+def moe_reroute(topk_idx: torch.Tensor, n_experts: int, replica_of: torch.Tensor, *, out: torch.Tensor | None = None,
+                workspace=None):
+    """Logical -> physical expert ids (include/moe.h moe_reroute) -> phys_idx int32 [N, k]."""
+    _contig(topk_idx, "topk_idx")
+    _contig(replica_of, "replica_of")
+    n, k = topk_idx.shape
+    dev = topk_idx.device
+    if out is None:
+        out = torch.empty_like(topk_idx)
+    shape = make_shape(n, 1, n_experts, k)
+    if workspace is None:
+        ws, nbytes = _workspace(MOE_OP_REROUTE, shape, dev)
+    else:
+        ws, nbytes = workspace, workspace.numel() - 256
+    _check(lib.moe_reroute(C.byref(shape), _ptr(topk_idx), _ptr(replica_of), replica_of.numel(), _ptr(out),
+                           _ws_ptr(ws), nbytes, _stream(dev)), "moe_reroute")
+    return out
+
+
+def moe_replica_sync(w_gate_up: torch.Tensor, w_down: torch.Tensor, replica_of: torch.Tensor, *,
+                     w_gate_up_replica: torch.Tensor | None = None, w_down_replica: torch.Tensor | None = None):
+    """Replica weight sync (include/moe.h moe_replica_sync) -> (w_gate_up_replica [R, 2I, H],
+    w_down_replica [R, H, I])."""
+    _bf16((w_gate_up, "w_gate_up"), (w_down, "w_down"))
+    _contig(replica_of, "replica_of")
+    e, two_i, h = w_gate_up.shape
+    r = replica_of.numel()
+    if w_gate_up_replica is None:
+        w_gate_up_replica = torch.empty((r, two_i, h), dtype=torch.bfloat16, device=w_gate_up.device)
+    if w_down_replica is None:
+        w_down_replica = torch.empty((r, h, two_i // 2), dtype=torch.bfloat16, device=w_gate_up.device)
+    shape = make_shape(0, h, e, 1, inter=two_i // 2)
+    _check(lib.moe_replica_sync(C.byref(shape), _ptr(replica_of), r, _ptr(w_gate_up), _ptr(w_down),
+                                _ptr(w_gate_up_replica), _ptr(w_down_replica), _stream(w_gate_up.device)),
+           "moe_replica_sync")
+    return w_gate_up_replica, w_down_replica
+
+
+def moe_replica_grad_reduce(grad_w_gate_up: torch.Tensor, grad_w_down: torch.Tensor,
+                            grad_w_gate_up_replica: torch.Tensor, grad_w_down_replica: torch.Tensor,
+                            replica_of: torch.Tensor):
+    """Adds the replica slots' weight gradients into their masters' (include/moe.h
+    moe_replica_grad_reduce), in place -> (grad_w_gate_up, grad_w_down)."""
+    _bf16((grad_w_gate_up, "grad_w_gate_up"), (grad_w_down, "grad_w_down"),
+          (grad_w_gate_up_replica, "grad_w_gate_up_replica"), (grad_w_down_replica, "grad_w_down_replica"))
+    _contig(replica_of, "replica_of")
+    e, two_i, h = grad_w_gate_up.shape
+    shape = make_shape(0, h, e, 1, inter=two_i // 2)
+    _check(lib.moe_replica_grad_reduce(C.byref(shape), _ptr(replica_of), replica_of.numel(),
+                                       _ptr(grad_w_gate_up_replica), _ptr(grad_w_down_replica), _ptr(grad_w_gate_up),
+                                       _ptr(grad_w_down), _stream(grad_w_gate_up.device)), "moe_replica_grad_reduce")
+    return grad_w_gate_up, grad_w_down
 
 
 def moe_combine(y: torch.Tensor, topk_w: torch.Tensor, layout: Layout, *, out: torch.Tensor | None = None):
@@ -446,7 +586,8 @@ def moe_combine_bwd(grad_out: torch.Tensor, y: torch.Tensor, topk_w: torch.Tenso
     return grad_y, grad_w
 
 
-__all__ = ["moe_route", "moe_route_random", "moe_dispatch", "moe_dispatch_mxfp8", "moe_expert_ffn", "moe_expert_ffn_bwd", "moe_combine", "moe_combine_bwd",
+__all__ = ["moe_route", "moe_route_random", "moe_dispatch", "moe_dispatch_mxfp8", "moe_replica_plan", "moe_reroute",
+           "moe_replica_sync", "moe_replica_grad_reduce", "moe_expert_ffn_replicas", "moe_expert_ffn_bwd_replicas", "moe_expert_ffn", "moe_expert_ffn_bwd", "moe_combine", "moe_combine_bwd",
            "moe_dispatch_bwd",
            "Layout", "RouteOut",
            "MoeError", "make_shape", "workspace_size", "lib", "library_path", "EXPORTS"]

@@ -17,7 +17,7 @@ PKG = Path(__file__).resolve().parent
 CSRC = PKG / "csrc"
 BUILD = PKG / "_build"
 LIB = PKG / "libmoe_mi355x.so"
-SOURCES = ["moe_abi.cpp", "moe_route.hip", "moe_layout.hip", "moe_rows.hip", "moe_mxfp8.hip", "moe_ffn.hip"]
+SOURCES = ["moe_abi.cpp", "moe_route.hip", "moe_layout.hip", "moe_rows.hip", "moe_mxfp8.hip", "moe_ffn.hip", "moe_replica.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

@@ -113,6 +113,9 @@ moe_status moe_workspace_size(moe_op op, const moe_shape *s, size_t *bytes) {
       if (s->inter < 1) return MOE_ERR_INVALID_ARG;
       *bytes = moe::ffn_workspace_bytes(rows_of(s), s->inter);
       return MOE_OK;
+    case MOE_OP_REROUTE:
+      *bytes = moe::reroute_workspace_bytes(s->n_tokens * s->top_k, s->n_experts);
+      return MOE_OK;
     case MOE_OP_EXPERT_FFN_BWD:
       if (s->inter < 1) return MOE_ERR_INVALID_ARG;
       *bytes = moe::ffn_bwd_workspace_bytes(rows_of(s), s->inter);
@@ -225,9 +228,13 @@ moe_status moe_dispatch_mxfp8(const moe_shape *s, const void *x, const int32_t *
                                               pad_limit_of(s, layout), layout->row_src, hs));
 }
 
-moe_status moe_expert_ffn(const moe_shape *s, const void *x_perm, const moe_layout *layout, const void *w_gate_up,
-                          const void *w_down, void *y, void *gate_up, void *workspace, size_t workspace_bytes,
-                          void *stream) {
+}  // extern "C"
+
+namespace {
+
+moe_status expert_ffn(const moe_shape *s, const void *x_perm, const moe_layout *layout, const void *w_gate_up,
+                      const void *w_down, void *y, void *gate_up, const moe::ReplicaBases *rep, void *workspace,
+                      size_t workspace_bytes, void *stream) {
   int64_t rows;
   moe_status st = check_ffn_shape(s, &rows);
   if (st != MOE_OK) return st;
@@ -246,13 +253,13 @@ moe_status moe_expert_ffn(const moe_shape *s, const void *x_perm, const moe_layo
                                            s->n_experts, s->capacity, layout->tokens_per_expert,
                                            layout->expert_offsets, static_cast<const uint16_t *>(w_gate_up),
                                            static_cast<const uint16_t *>(w_down), static_cast<uint16_t *>(y),
-                                           static_cast<uint16_t *>(gate_up), workspace, as_stream(stream)));
+                                           static_cast<uint16_t *>(gate_up), rep, workspace, as_stream(stream)));
 }
 
-moe_status moe_expert_ffn_bwd(const moe_shape *s, const void *x_perm, const void *grad_y, const void *gate_up,
-                              const moe_layout *layout, const void *w_gate_up, const void *w_down, void *grad_x_perm,
-                              void *grad_w_gate_up, void *grad_w_down, void *workspace, size_t workspace_bytes,
-                              void *stream) {
+moe_status expert_ffn_bwd(const moe_shape *s, const void *x_perm, const void *grad_y, const void *gate_up,
+                          const moe_layout *layout, const void *w_gate_up, const void *w_down, void *grad_x_perm,
+                          void *grad_w_gate_up, void *grad_w_down, const moe::ReplicaBases *rep, void *workspace,
+                          size_t workspace_bytes, void *stream) {
   int64_t rows;
   moe_status st = check_ffn_shape(s, &rows);
   if (st != MOE_OK) return st;
@@ -277,8 +284,169 @@ moe_status moe_expert_ffn_bwd(const moe_shape *s, const void *x_perm, const void
       s->n_experts, s->capacity, layout->tokens_per_expert, layout->expert_offsets,
       static_cast<const uint16_t *>(w_gate_up), static_cast<const uint16_t *>(w_down),
       static_cast<const uint16_t *>(gate_up), static_cast<uint16_t *>(grad_x_perm), static_cast<uint16_t *>(grad_w_gate_up),
-      static_cast<uint16_t *>(grad_w_down), workspace, as_stream(stream)));
+      static_cast<uint16_t *>(grad_w_down), rep, workspace, as_stream(stream)));
 }
+
+// Replica slots of the grouped FFN: the last n_replicas of the shape's experts.
+moe_status replica_bases(const moe_shape *s, int32_t n_replicas, const void *w_gate_up_replica,
+                         const void *w_down_replica, void *grad_w_gate_up_replica, void *grad_w_down_replica,
+                         bool backward, moe::ReplicaBases *out) {
+  if (n_replicas < 0 || n_replicas >= s->n_experts) return MOE_ERR_INVALID_ARG;
+  if (n_replicas > 0 && (!w_gate_up_replica || !w_down_replica ||
+                         (backward && (!grad_w_gate_up_replica || !grad_w_down_replica))))
+    return MOE_ERR_INVALID_ARG;
+  if (!aligned16(w_gate_up_replica) || !aligned16(w_down_replica) || !aligned16(grad_w_gate_up_replica) ||
+      !aligned16(grad_w_down_replica))
+    return MOE_ERR_MISALIGNED;
+  if (n_replicas > 0 && grad_w_gate_up_replica && grad_w_gate_up_replica == grad_w_down_replica)
+    return MOE_ERR_INVALID_ARG;
+  out->e_master = s->n_experts - n_replicas;
+  out->w_gate_up = static_cast<const uint16_t *>(w_gate_up_replica);
+  out->w_down = static_cast<const uint16_t *>(w_down_replica);
+  out->grad_w_gate_up = static_cast<uint16_t *>(grad_w_gate_up_replica);
+  out->grad_w_down = static_cast<uint16_t *>(grad_w_down_replica);
+  return MOE_OK;
+}
+
+// Shape checks of the replication calls on logical experts: 0 <= R <= 1024.
+moe_status check_replicas(const moe_shape *s, int32_t n_replicas, const int32_t *replica_of) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (n_replicas < 0) return MOE_ERR_INVALID_ARG;
+  if (n_replicas > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  if (n_replicas > 0 && !replica_of) return MOE_ERR_INVALID_ARG;
+  if (replica_of && !aligned4(replica_of)) return MOE_ERR_MISALIGNED;
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_expert_ffn(const moe_shape *s, const void *x_perm, const moe_layout *layout, const void *w_gate_up,
+                          const void *w_down, void *y, void *gate_up, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+  return expert_ffn(s, x_perm, layout, w_gate_up, w_down, y, gate_up, nullptr, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_expert_ffn_bwd(const moe_shape *s, const void *x_perm, const void *grad_y, const void *gate_up,
+                              const moe_layout *layout, const void *w_gate_up, const void *w_down, void *grad_x_perm,
+                              void *grad_w_gate_up, void *grad_w_down, void *workspace, size_t workspace_bytes,
+                              void *stream) {
+  return expert_ffn_bwd(s, x_perm, grad_y, gate_up, layout, w_gate_up, w_down, grad_x_perm, grad_w_gate_up,
+                        grad_w_down, nullptr, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_expert_ffn_replicas(const moe_shape *s, int32_t n_replicas, const void *x_perm, const moe_layout *layout,
+                                   const void *w_gate_up, const void *w_down, const void *w_gate_up_replica,
+                                   const void *w_down_replica, void *y, void *gate_up, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+  if (!s) return MOE_ERR_INVALID_ARG;
+  moe::ReplicaBases rep;
+  moe_status st = replica_bases(s, n_replicas, w_gate_up_replica, w_down_replica, nullptr, nullptr, false, &rep);
+  if (st != MOE_OK) return st;
+  const void *ins[] = {x_perm, w_gate_up, w_down};
+  for (const void *in : ins)
+    if (n_replicas > 0 && in && (in == w_gate_up_replica || in == w_down_replica)) return MOE_ERR_INVALID_ARG;
+  return expert_ffn(s, x_perm, layout, w_gate_up, w_down, y, gate_up, &rep, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_expert_ffn_bwd_replicas(const moe_shape *s, int32_t n_replicas, const void *x_perm, const void *grad_y,
+                                       const void *gate_up, const moe_layout *layout, const void *w_gate_up,
+                                       const void *w_down, const void *w_gate_up_replica, const void *w_down_replica,
+                                       void *grad_x_perm, void *grad_w_gate_up, void *grad_w_down,
+                                       void *grad_w_gate_up_replica, void *grad_w_down_replica, void *workspace,
+                                       size_t workspace_bytes, void *stream) {
+  if (!s) return MOE_ERR_INVALID_ARG;
+  moe::ReplicaBases rep;
+  moe_status st = replica_bases(s, n_replicas, w_gate_up_replica, w_down_replica, grad_w_gate_up_replica,
+                                grad_w_down_replica, true, &rep);
+  if (st != MOE_OK) return st;
+  if (n_replicas > 0) {
+    const void *outs[] = {grad_w_gate_up_replica, grad_w_down_replica};
+    const void *others[] = {x_perm, grad_y, gate_up, w_gate_up, w_down, w_gate_up_replica, w_down_replica, grad_x_perm,
+                            grad_w_gate_up, grad_w_down};
+    for (const void *o : outs)
+      for (const void *in : others)
+        if (in && in == o) return MOE_ERR_INVALID_ARG;
+  }
+  return expert_ffn_bwd(s, x_perm, grad_y, gate_up, layout, w_gate_up, w_down, grad_x_perm, grad_w_gate_up,
+                        grad_w_down, &rep, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_replica_plan(const moe_shape *s, const int32_t *tokens_per_expert, int32_t n_replicas,
+                            int32_t *replica_of, void *stream) {
+  moe_status st = check_replicas(s, n_replicas, replica_of);
+  if (st != MOE_OK) return st;
+  if (!tokens_per_expert) return MOE_ERR_INVALID_ARG;
+  if (!aligned4(tokens_per_expert)) return MOE_ERR_MISALIGNED;
+  return hip_status(moe::launch_replica_plan(tokens_per_expert, s->n_experts, n_replicas, replica_of,
+                                             as_stream(stream)));
+}
+
+moe_status moe_reroute(const moe_shape *s, const int32_t *topk_idx, const int32_t *replica_of, int32_t n_replicas,
+                       int32_t *phys_idx, void *workspace, size_t workspace_bytes, void *stream) {
+  moe_status st = check_replicas(s, n_replicas, replica_of);
+  if (st != MOE_OK) return st;
+  if (s->n_experts + n_replicas > kMaxExperts) return MOE_ERR_UNSUPPORTED;  // the physical experts
+  const int64_t a = s->n_tokens * s->top_k;
+  if (a > 0 && (!topk_idx || !phys_idx)) return MOE_ERR_INVALID_ARG;
+  if (a > 0 && (!aligned4(topk_idx) || !aligned4(phys_idx))) return MOE_ERR_MISALIGNED;
+  const size_t need_ws = moe::reroute_workspace_bytes(a, s->n_experts);
+  if (a > 0 && (workspace_bytes < need_ws || !workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u)))
+    return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_reroute(topk_idx, s->n_tokens, s->top_k, s->n_experts, replica_of, n_replicas,
+                                        phys_idx, workspace, as_stream(stream)));
+}
+
+moe_status moe_replica_sync(const moe_shape *s, const int32_t *replica_of, int32_t n_replicas, const void *w_gate_up,
+                            const void *w_down, void *w_gate_up_replica, void *w_down_replica, void *stream) {
+  moe_status st = check_replicas(s, n_replicas, replica_of);
+  if (st != MOE_OK) return st;
+  int64_t rows;
+  if ((st = check_ffn_shape(s, &rows)) != MOE_OK) return st;
+  if (n_replicas == 0) return MOE_OK;
+  if (!w_gate_up || !w_down || !w_gate_up_replica || !w_down_replica) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(w_gate_up) || !aligned16(w_down) || !aligned16(w_gate_up_replica) || !aligned16(w_down_replica))
+    return MOE_ERR_MISALIGNED;
+  if (w_gate_up_replica == w_down_replica || w_gate_up_replica == w_gate_up || w_gate_up_replica == w_down ||
+      w_down_replica == w_gate_up || w_down_replica == w_down)
+    return MOE_ERR_INVALID_ARG;
+  const int64_t hi = s->hidden * s->inter;
+  hipStream_t hs = as_stream(stream);
+  hipError_t e = moe::launch_replica_sync(w_gate_up, w_gate_up_replica, replica_of, n_replicas, s->n_experts,
+                                          2 * hi * 2, hs);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_replica_sync(w_down, w_down_replica, replica_of, n_replicas, s->n_experts, hi * 2, hs));
+}
+
+moe_status moe_replica_grad_reduce(const moe_shape *s, const int32_t *replica_of, int32_t n_replicas,
+                                   const void *grad_w_gate_up_replica, const void *grad_w_down_replica,
+                                   void *grad_w_gate_up, void *grad_w_down, void *stream) {
+  moe_status st = check_replicas(s, n_replicas, replica_of);
+  if (st != MOE_OK) return st;
+  int64_t rows;
+  if ((st = check_ffn_shape(s, &rows)) != MOE_OK) return st;
+  if (n_replicas == 0) return MOE_OK;
+  if (!grad_w_gate_up_replica || !grad_w_down_replica || !grad_w_gate_up || !grad_w_down) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(grad_w_gate_up_replica) || !aligned16(grad_w_down_replica) || !aligned16(grad_w_gate_up) ||
+      !aligned16(grad_w_down))
+    return MOE_ERR_MISALIGNED;
+  if (grad_w_gate_up == grad_w_down || grad_w_gate_up == grad_w_gate_up_replica ||
+      grad_w_gate_up == grad_w_down_replica || grad_w_down == grad_w_gate_up_replica ||
+      grad_w_down == grad_w_down_replica)
+    return MOE_ERR_INVALID_ARG;
+  const int64_t hi = s->hidden * s->inter;
+  hipStream_t hs = as_stream(stream);
+  hipError_t e = moe::launch_replica_grad_reduce(static_cast<uint16_t *>(grad_w_gate_up),
+                                                 static_cast<const uint16_t *>(grad_w_gate_up_replica), replica_of,
+                                                 n_replicas, s->n_experts, 2 * hi, hs);
+  if (e != hipSuccess) return MOE_ERR_HIP;
+  return hip_status(moe::launch_replica_grad_reduce(static_cast<uint16_t *>(grad_w_down),
+                                                    static_cast<const uint16_t *>(grad_w_down_replica), replica_of,
+                                                    n_replicas, s->n_experts, hi, hs));
+}
+
 
 moe_status moe_combine(const moe_shape *s, const void *y, const float *topk_w, const moe_layout *layout, void *out,
                        void *stream) {

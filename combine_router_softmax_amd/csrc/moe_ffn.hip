@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int64_t b_expert_stride, int K, int M, int N,
     int m_tiles, int n_tiles, const int32_t *__restrict__ tokens_per_expert,
     const int32_t *__restrict__ expert_offsets, int e, uint16_t *__restrict__ C, int64_t ldc,
-    uint16_t *__restrict__ gate_up) {
+    uint16_t *__restrict__ gate_up, const uint16_t *__restrict__ B_rep, uint16_t *__restrict__ C_rep, int e_master) {
   constexpr bool kSwiGLU = kMode == kModeSwiGLU, kWGrad = kMode == kModeWGrad;
   static_assert(kWGrad ? (kAT && kBT) : !kAT, "operand layouts of the modes");
   static_assert(!(kSwiGLU && kBT), "the SwiGLU pairing reads K-contiguous weights");
@@ -372,7 +372,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     KT = (k_len + kBK - 1) / kBK;
     a_base = reinterpret_cast<const char *>(A + r0 * M + m0);
     b_base = reinterpret_cast<const char *>(B + r0 * N + n0);
-    c_base = C + ((int64_t)te * M + m0) * N;
+    // replica slots (experts from e_master on) write to the replica buffer
+    c_base = (te < e_master ? C + (int64_t)te * M * N : C_rep + (int64_t)(te - e_master) * M * N) + (int64_t)m0 * N;
   } else {
     TileCoord tc;
     if (!find_tile(tokens_per_expert, expert_offsets, e, n_tiles, reinterpret_cast<int32_t *>(ring), tc)) return;
@@ -384,7 +385,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     KT = K / kBK;
     k_len = K;
     a_base = reinterpret_cast<const char *>(A + row0 * K);
-    b_base = reinterpret_cast<const char *>(B + (int64_t)te * b_expert_stride + (kBT ? n0 : 0));
+    // replica slots (experts from e_master on) read the replica weights
+    const uint16_t *b_e = te < e_master ? B + (int64_t)te * b_expert_stride : B_rep + (int64_t)(te - e_master) * b_expert_stride;
+    b_base = reinterpret_cast<const char *>(b_e + (kBT ? n0 : 0));
     c_base = C + row0 * ldc;
     if (kSwiGLU && gate_up) gu_base = gate_up + row0 * 2 * N;
   }
@@ -713,26 +716,27 @@ __global__ __launch_bounds__(kThreads) void swiglu_bwd_kernel(const uint16_t *gu
 // Grouped GEMM over the expert segments, C [rows, N] = A [rows, K] B_e^T with
 // B_e [N, K] (kBT false) or B_e [K, N] (kBT true).
 template <bool kBT>
-hipError_t launch_plain(const uint16_t *A, const uint16_t *B, int64_t b_stride, int K, int N, int64_t rows, int e,
-                        int capacity, const int32_t *tokens_per_expert, const int32_t *expert_offsets, uint16_t *C,
-                        hipStream_t stream) {
+hipError_t launch_plain(const uint16_t *A, const uint16_t *B, const uint16_t *B_rep, int e_master, int64_t b_stride,
+                        int K, int N, int64_t rows, int e, int capacity, const int32_t *tokens_per_expert,
+                        const int32_t *expert_offsets, uint16_t *C, hipStream_t stream) {
   const int nt = (N + kBN - 1) / kBN;
   const int64_t g = tile_bound(rows, e, capacity, nt);
   if (g > INT32_MAX) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((grouped_gemm_kernel<kModePlain, false, kBT>), dim3((unsigned)g), dim3(kThreads), 0, stream, A,
-                     B, b_stride, K, 0, N, 0, nt, tokens_per_expert, expert_offsets, e, C, (int64_t)N, nullptr);
+                     B, b_stride, K, 0, N, 0, nt, tokens_per_expert, expert_offsets, e, C, (int64_t)N, nullptr, B_rep,
+                     nullptr, e_master);
   return hipGetLastError();
 }
 
 // Weight-gradient GEMM: C_e [M, N] = A_e^T B_e for every expert, A_e [rows_e, M]
 // and B_e [rows_e, N] the rows of expert e's segment.
 hipError_t launch_wgrad(const uint16_t *A, const uint16_t *B, int M, int N, int e, const int32_t *tokens_per_expert,
-                        const int32_t *expert_offsets, uint16_t *C, hipStream_t stream) {
+                        const int32_t *expert_offsets, uint16_t *C, uint16_t *C_rep, int e_master, hipStream_t stream) {
   const int mt = (M + kBM - 1) / kBM, nt = (N + kBN - 1) / kBN;
   const int chunk = (mt * nt + kXcds - 1) / kXcds;
   hipLaunchKernelGGL((grouped_gemm_kernel<kModeWGrad, true, true>), dim3((unsigned)(kXcds * e * chunk)),
                      dim3(kThreads), 0, stream, A, B, (int64_t)0, 0, M, N, mt, nt, tokens_per_expert, expert_offsets,
-                     e, C, (int64_t)N, nullptr);
+                     e, C, (int64_t)N, nullptr, nullptr, C_rep, e_master);
   return hipGetLastError();
 }
 
@@ -746,7 +750,11 @@ hipError_t launch_expert_ffn_bwd(const uint16_t *x_perm, const uint16_t *grad_y,
                                  int inter, int e, int capacity, const int32_t *tokens_per_expert,
                                  const int32_t *expert_offsets, const uint16_t *w_gate_up, const uint16_t *w_down,
                                  const uint16_t *gate_up, uint16_t *grad_x_perm, uint16_t *grad_w_gate_up,
-                                 uint16_t *grad_w_down, void *workspace, hipStream_t stream) {
+                                 uint16_t *grad_w_down, const ReplicaBases *rep, void *workspace,
+                                 hipStream_t stream) {
+  const int em = rep ? rep->e_master : e;
+  const uint16_t *wgu_r = rep ? rep->w_gate_up : nullptr, *wd_r = rep ? rep->w_down : nullptr;
+  uint16_t *gwgu_r = rep ? rep->grad_w_gate_up : nullptr, *gwd_r = rep ? rep->grad_w_down : nullptr;
   // workspace: [dG | dU] ([rows, 2I], holding the recomputed [G | U] before
   // when gate_up is null); dA then the activation ([rows, I])
   uint16_t *gu = static_cast<uint16_t *>(workspace);
@@ -758,9 +766,9 @@ hipError_t launch_expert_ffn_bwd(const uint16_t *x_perm, const uint16_t *grad_y,
   if (rows > 0) {
     // [G | U] = x W_gate_up^T unless saved by the forward; dA = dy W_down (W_down [H, I]: K-major)
     if (!gate_up)
-      MOE_TRY(launch_plain<false>(x_perm, w_gate_up, (int64_t)2 * I * H, H, 2 * I, rows, e, capacity,
+      MOE_TRY(launch_plain<false>(x_perm, w_gate_up, wgu_r, em, (int64_t)2 * I * H, H, 2 * I, rows, e, capacity,
                                   tokens_per_expert, expert_offsets, gu, stream));
-    MOE_TRY(launch_plain<true>(grad_y, w_down, (int64_t)I * H, H, I, rows, e, capacity, tokens_per_expert,
+    MOE_TRY(launch_plain<true>(grad_y, w_down, wd_r, em, (int64_t)I * H, H, I, rows, e, capacity, tokens_per_expert,
                                expert_offsets, dact, stream));
     // [dG | dU] (in place of the recomputed [G | U]); the activation in place of dA
     const int64_t chunks = rows * (I / 8);
@@ -770,12 +778,13 @@ hipError_t launch_expert_ffn_bwd(const uint16_t *x_perm, const uint16_t *grad_y,
                        gate_up ? gate_up : gu, gu, dact, rows, I);
     MOE_TRY(hipGetLastError());
     // dx = [dG | dU] W_gate_up (W_gate_up [2I, H]: K-major)
-    MOE_TRY(launch_plain<true>(gu, w_gate_up, (int64_t)H * 2 * I, 2 * I, H, rows, e, capacity, tokens_per_expert,
-                               expert_offsets, grad_x_perm, stream));
+    MOE_TRY(launch_plain<true>(gu, w_gate_up, wgu_r, em, (int64_t)H * 2 * I, 2 * I, H, rows, e, capacity,
+                               tokens_per_expert, expert_offsets, grad_x_perm, stream));
   }
   // dW_down_e = dy_e^T a_e;  [dW_gate; dW_up]_e = [dG | dU]_e^T x_e  (experts without rows: zeros)
-  MOE_TRY(launch_wgrad(grad_y, dact, H, I, e, tokens_per_expert, expert_offsets, grad_w_down, stream));
-  MOE_TRY(launch_wgrad(gu, x_perm, 2 * I, H, e, tokens_per_expert, expert_offsets, grad_w_gate_up, stream));
+  MOE_TRY(launch_wgrad(grad_y, dact, H, I, e, tokens_per_expert, expert_offsets, grad_w_down, gwd_r, em, stream));
+  MOE_TRY(launch_wgrad(gu, x_perm, 2 * I, H, e, tokens_per_expert, expert_offsets, grad_w_gate_up, gwgu_r, em,
+                       stream));
 #undef MOE_TRY
   return hipSuccess;
 }
@@ -785,8 +794,9 @@ size_t ffn_workspace_bytes(int64_t rows, int inter) { return align256(sizeof(uin
 hipError_t launch_expert_ffn(const uint16_t *x_perm, int64_t rows, int64_t hidden, int inter, int e, int capacity,
                              const int32_t *tokens_per_expert, const int32_t *expert_offsets,
                              const uint16_t *w_gate_up, const uint16_t *w_down, uint16_t *y, uint16_t *gate_up,
-                             void *workspace, hipStream_t stream) {
+                             const ReplicaBases *rep, void *workspace, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
+  const int em = rep ? rep->e_master : e;
   uint16_t *act = static_cast<uint16_t *>(workspace);
   const int n1 = (inter + kBN / 2 - 1) / (kBN / 2);
   const int64_t g1 = tile_bound(rows, e, capacity, n1);
@@ -794,13 +804,13 @@ hipError_t launch_expert_ffn(const uint16_t *x_perm, int64_t rows, int64_t hidde
   if (g1 > INT32_MAX || g2 > INT32_MAX) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((grouped_gemm_kernel<kModeSwiGLU, false, false>), dim3((unsigned)g1), dim3(kThreads), 0, stream,
                      x_perm, w_gate_up, (int64_t)2 * inter * hidden, (int)hidden, 0, inter, 0, n1, tokens_per_expert,
-                     expert_offsets, e, act, (int64_t)inter, gate_up);
+                     expert_offsets, e, act, (int64_t)inter, gate_up, rep ? rep->w_gate_up : nullptr, nullptr, em);
   hipError_t st = hipGetLastError();
   if (st != hipSuccess) return st;
   const int n2 = (int)((hidden + kBN - 1) / kBN);
   hipLaunchKernelGGL((grouped_gemm_kernel<kModePlain, false, false>), dim3((unsigned)g2), dim3(kThreads), 0, stream,
                      act, w_down, (int64_t)hidden * inter, inter, 0, (int)hidden, 0, n2, tokens_per_expert,
-                     expert_offsets, e, y, hidden, nullptr);
+                     expert_offsets, e, y, hidden, nullptr, rep ? rep->w_down : nullptr, nullptr, em);
   return hipGetLastError();
 }
 

@@ -46,16 +46,41 @@ hipError_t launch_scatter_mxfp8(const uint16_t *x, int64_t n, int k, int64_t h, 
                                 const int32_t *row_src, hipStream_t stream);
 
 // ---- grouped SwiGLU FFN (moe_ffn.hip); bf16 operands as uint16_t bit patterns
+// Replica weight slots: experts from e_master on take their weights from (and
+// write their weight gradients to) the replica buffers, slot e - e_master.
+struct ReplicaBases {
+  int e_master;
+  const uint16_t *w_gate_up;  // [R, 2I, H]
+  const uint16_t *w_down;     // [R, H, I]
+  uint16_t *grad_w_gate_up;   // [R, 2I, H] (backward)
+  uint16_t *grad_w_down;      // [R, H, I] (backward)
+};
 size_t ffn_workspace_bytes(int64_t rows, int inter);
+// rep: nullable (no replica slots)
 hipError_t launch_expert_ffn(const uint16_t *x_perm, int64_t rows, int64_t hidden, int inter, int e,
                              int capacity, const int32_t *tokens_per_expert, const int32_t *expert_offsets,
                              const uint16_t *w_gate_up, const uint16_t *w_down, uint16_t *y, uint16_t *gate_up,
-                             void *workspace, hipStream_t stream);
+                             const ReplicaBases *rep, void *workspace, hipStream_t stream);
 size_t ffn_bwd_workspace_bytes(int64_t rows, int inter);
 hipError_t launch_expert_ffn_bwd(const uint16_t *x_perm, const uint16_t *grad_y, int64_t rows, int64_t hidden,
                                  int inter, int e, int capacity, const int32_t *tokens_per_expert,
                                  const int32_t *expert_offsets, const uint16_t *w_gate_up, const uint16_t *w_down,
                                  const uint16_t *gate_up, uint16_t *grad_x_perm, uint16_t *grad_w_gate_up,
-                                 uint16_t *grad_w_down, void *workspace, hipStream_t stream);
+                                 uint16_t *grad_w_down, const ReplicaBases *rep, void *workspace,
+                                 hipStream_t stream);
+
+// ---- hot-expert replication (moe_replica.hip)
+// placement: replica_of[i] = logical expert of slot i (greedy by load per copy)
+hipError_t launch_replica_plan(const int32_t *counts, int e, int r, int32_t *replica_of, hipStream_t stream);
+size_t reroute_workspace_bytes(int64_t assignments, int e);
+hipError_t launch_reroute(const int32_t *topk_idx, int64_t n, int k, int e, const int32_t *replica_of, int r,
+                          int32_t *phys_idx, void *workspace, hipStream_t stream);
+// replica[i] = master[replica_of[i]], `bytes` per expert (a multiple of 16);
+// slots naming no expert in [0, e) are skipped
+hipError_t launch_replica_sync(const void *master, void *replica, const int32_t *replica_of, int r, int e,
+                               int64_t bytes, hipStream_t stream);
+// grad_master[x] = bf16(fp32 sum of grad_master[x] and its slots' gradients in slot order)
+hipError_t launch_replica_grad_reduce(uint16_t *grad_master, const uint16_t *grad_replica, const int32_t *replica_of,
+                                      int r, int e, int64_t elems, hipStream_t stream);
 
 }  // namespace moe

@@ -11,6 +11,11 @@
  *   moe_combine     probability-weighted unpermute / combine (fp32 accumulation)
  *   moe_combine_bwd backward of moe_combine (grad of expert rows, grad of weights)
  *   moe_dispatch_bwd backward of the row scatter (grad of the token rows)
+ *   moe_replica_plan / moe_replica_sync / moe_reroute / moe_expert_ffn_replicas /
+ *   moe_expert_ffn_bwd_replicas / moe_replica_grad_reduce
+ *                   hot-expert replication on one GPU (placement, weight sync,
+ *                   logical -> physical reroute, FFN with replica weight slots,
+ *                   replica gradient reduce)
  *
  * The steps follow the four stages of Megatron-Core's MoELayer.forward as laid
  * out on the page "Megatron MoE 实现" (router -> (probs, routing_map);
@@ -70,7 +75,8 @@ typedef enum moe_op {
   MOE_OP_EXPERT_FFN = 2,
   MOE_OP_COMBINE = 3,
   MOE_OP_COMBINE_BWD = 4,
-  MOE_OP_EXPERT_FFN_BWD = 5
+  MOE_OP_EXPERT_FFN_BWD = 5,
+  MOE_OP_REROUTE = 6
 } moe_op;
 
 /* Shapes and options; read on the host only, never kept. */
@@ -260,6 +266,84 @@ moe_status moe_expert_ffn_bwd(const moe_shape *s, const void *x_perm, const void
                               const moe_layout *layout, const void *w_gate_up, const void *w_down, void *grad_x_perm,
                               void *grad_w_gate_up, void *grad_w_down, void *workspace, size_t workspace_bytes,
                               void *stream);
+
+/* Hot-expert replication, the part of one GPU (InternLM/xtuner pull request
+ * "Integrate UltraEP Runtime": replicas of hot experts created from the current
+ * load, part of their tokens rerouted to replica slots, master/replica weight
+ * sync, one grouped GEMM over master and replica experts with the weights at
+ * two storage bases, replica weight gradients in a replica buffer reduced into
+ * the masters').  The router and its outputs keep logical expert ids; the
+ * dispatch, FFN and combine run on physical ids: physical expert p < E is the
+ * master of logical expert p, p = E + i is replica slot i, a copy of logical
+ * expert replica_of[i].  Sequence: moe_route -> moe_replica_plan ->
+ * moe_replica_sync -> moe_reroute -> moe_dispatch (E + R experts) ->
+ * moe_expert_ffn_replicas -> moe_combine; backward moe_combine_bwd ->
+ * moe_expert_ffn_bwd_replicas -> moe_replica_grad_reduce -> moe_dispatch_bwd.
+ * Replica slot contents are device data: a slot naming no expert in [0, E) is
+ * never used as an address (the sync and the reduce skip it; the reroute sends
+ * nothing to it). */
+
+/* Placement: replica_of[i] (int32 [n_replicas]) = the logical expert that slot
+ * i copies.  Slots are filled in order, each going to the expert with the
+ * largest load per copy tokens_per_expert[e] / (1 + slots given to e so far),
+ * compared exactly, ties to the lower id.  s->n_experts = E (logical);
+ * tokens_per_expert int32 [E] (moe_route's counts); 0 <= n_replicas <= 1024.
+ * One wavefront; no workspace. */
+moe_status moe_replica_plan(const moe_shape *s, const int32_t *tokens_per_expert, int32_t n_replicas,
+                            int32_t *replica_of, void *stream);
+
+/* Reroute: phys_idx [N, k] = the physical expert of every routed slot.  For a
+ * logical expert e with c assignments (valid slots, in assignment order
+ * a = t*k + j, ordinal o = its position among them) and m = 1 + (its number of
+ * slots) copies, the assignment with ordinal o goes to run floor(o * m / c):
+ * run 0 stays on the master e, run j >= 1 goes to e's j-th slot (slots in
+ * increasing index), so every copy receives floor(c/m) or ceil(c/m) of them
+ * in assignment order.  -1 stays -1; an id outside [0, E) becomes -2 (invalid
+ * for the physical dispatch as well).  s->n_experts = E (logical), E +
+ * n_replicas <= 1024; topk_idx and phys_idx int32 [N, k] (may be the same
+ * array).  Workspace: moe_workspace_size(MOE_OP_REROUTE) (a dropless layout of
+ * the logical ids, for the ordinals and counts). */
+moe_status moe_reroute(const moe_shape *s, const int32_t *topk_idx, const int32_t *replica_of, int32_t n_replicas,
+                       int32_t *phys_idx, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Replica weight sync: w_gate_up_replica[i] = w_gate_up[replica_of[i]] and
+ * w_down_replica[i] = w_down[replica_of[i]] (bit copies).  s->n_experts = E
+ * (logical), hidden, inter as moe_expert_ffn; replica buffers bf16
+ * [R, 2I, H] and [R, H, I], 16-byte aligned, distinct from the masters. */
+moe_status moe_replica_sync(const moe_shape *s, const int32_t *replica_of, int32_t n_replicas, const void *w_gate_up,
+                            const void *w_down, void *w_gate_up_replica, void *w_down_replica, void *stream);
+
+/* Replica gradient reduce: for every logical expert x with slots,
+ *   grad_w_gate_up[x] = bf16(grad_w_gate_up[x] + sum over x's slots i, in slot
+ *                       order, of grad_w_gate_up_replica[i])   (fp32 sum)
+ * and the same for grad_w_down; experts without slots are untouched.  Shapes
+ * as moe_replica_sync. */
+moe_status moe_replica_grad_reduce(const moe_shape *s, const int32_t *replica_of, int32_t n_replicas,
+                                   const void *grad_w_gate_up_replica, const void *grad_w_down_replica,
+                                   void *grad_w_gate_up, void *grad_w_down, void *stream);
+
+/* moe_expert_ffn over physical experts with replica slots: s->n_experts = P,
+ * the layout's experts (E masters then n_replicas slots, 0 <= n_replicas < P);
+ * physical expert p < P - n_replicas takes w_gate_up[p], w_down[p]; slot
+ * p - (P - n_replicas) takes w_gate_up_replica[.], w_down_replica[.] (bf16
+ * [R, 2I, H], [R, H, I]), in the same grouped GEMM launches.  Everything else
+ * as moe_expert_ffn, whose workspace size it takes. */
+moe_status moe_expert_ffn_replicas(const moe_shape *s, int32_t n_replicas, const void *x_perm, const moe_layout *layout,
+                                   const void *w_gate_up, const void *w_down, const void *w_gate_up_replica,
+                                   const void *w_down_replica, void *y, void *gate_up, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
+/* moe_expert_ffn_bwd over physical experts with replica slots (as
+ * moe_expert_ffn_replicas): the weight gradients of the slots go to
+ * grad_w_gate_up_replica / grad_w_down_replica ([R, 2I, H], [R, H, I]), those
+ * of the masters to grad_w_gate_up / grad_w_down ([P - R, ...]);
+ * moe_replica_grad_reduce then adds the former into the latter. */
+moe_status moe_expert_ffn_bwd_replicas(const moe_shape *s, int32_t n_replicas, const void *x_perm, const void *grad_y,
+                                       const void *gate_up, const moe_layout *layout, const void *w_gate_up,
+                                       const void *w_down, const void *w_gate_up_replica, const void *w_down_replica,
+                                       void *grad_x_perm, void *grad_w_gate_up, void *grad_w_down,
+                                       void *grad_w_gate_up_replica, void *grad_w_down_replica, void *workspace,
+                                       size_t workspace_bytes, void *stream);
 
 /* Combine: probability-weighted unpermute (DeepSpeed ep_tp_dispatch.py
  * restore_combined: weighted expert rows added into a zeroed [N, H] output by

@@ -26,7 +26,7 @@ def moe():
 
 def test_library_exports_every_declared_function(moe):
     declared = header_functions()
-    assert len(declared) == 13, declared
+    assert len(declared) == 19, declared
     assert sorted(moe.EXPORTS) == declared
     for name in declared:
         assert hasattr(moe.lib, name), name
@@ -123,6 +123,43 @@ def test_validation_errors_enqueue_nothing(moe):
     assert mx(C.byref(s), odd, p, p, C.byref(lay), q8, s8, p, p, 1 << 20, None) == -2  # x misaligned
     assert mx(C.byref(s), p, p, p, C.byref(lay), q8, s8, p, p, 0, None) == -3          # no workspace
     assert mx(C.byref(s), p, p, p, None, q8, s8, p, p, 1 << 20, None) == -1
+    # hot-expert replication
+    s = moe.make_shape(16, 64, 8, 2, inter=64)
+    rep, tpe = C.c_void_p(4096), C.c_void_p(8192)
+    assert lib.moe_replica_plan(C.byref(s), tpe, 4, None, None) == -1           # no replica_of
+    assert lib.moe_replica_plan(C.byref(s), None, 4, rep, None) == -1           # no counts
+    assert lib.moe_replica_plan(C.byref(s), tpe, -1, rep, None) == -1
+    assert lib.moe_replica_plan(C.byref(s), tpe, 1025, rep, None) == -4
+    assert lib.moe_replica_plan(C.byref(s), C.c_void_p(8194), 4, rep, None) == -2
+    assert lib.moe_reroute(C.byref(s), p, rep, 4, p, p, 0, None) == -3         # no workspace
+    assert lib.moe_reroute(C.byref(s), p, rep, 1020, p, p, 1 << 20, None) == -4  # E + R > 1024
+    assert lib.moe_reroute(C.byref(s), None, rep, 4, p, p, 1 << 20, None) == -1
+    assert lib.moe_reroute(C.byref(s), odd, rep, 4, p, p, 1 << 20, None) == -2
+    w1, w2, w3, w4 = (C.c_void_p(v) for v in (1 << 16, 1 << 17, 1 << 18, 1 << 19))
+    assert lib.moe_replica_sync(C.byref(s), rep, 2, w1, w2, w3, w3, None) == -1   # replica buffers alias
+    assert lib.moe_replica_sync(C.byref(s), rep, 2, w1, w2, w1, w4, None) == -1   # replica aliases a master
+    assert lib.moe_replica_sync(C.byref(s), rep, 2, w1, w2, odd, w4, None) == -2
+    assert lib.moe_replica_sync(C.byref(s), rep, 2, w1, None, w3, w4, None) == -1
+    assert lib.moe_replica_sync(C.byref(s), rep, 0, None, None, None, None, None) == 0  # nothing to do
+    assert lib.moe_replica_grad_reduce(C.byref(s), rep, 2, w3, w4, w1, w1, None) == -1  # masters alias
+    assert lib.moe_replica_grad_reduce(C.byref(s), rep, 2, w3, w4, w3, w2, None) == -1  # master aliases a replica
+    assert lib.moe_replica_grad_reduce(C.byref(s), None, 2, w3, w4, w1, w2, None) == -1
+    s96 = moe.make_shape(16, 64, 8, 2, inter=96)
+    assert lib.moe_replica_sync(C.byref(s96), rep, 2, w1, w2, w3, w4, None) == -4     # I % 64
+    ffr = lib.moe_expert_ffn_replicas
+    assert ffr(C.byref(s), 8, p, C.byref(lay), w1, w2, w3, w4, p, None, p, 1 << 30, None) == -1  # R >= P
+    assert ffr(C.byref(s), 2, p, C.byref(lay), w1, w2, None, w4, p, None, p, 1 << 30, None) == -1
+    assert ffr(C.byref(s), 2, p, C.byref(lay), w1, w2, odd, w4, p, None, p, 1 << 30, None) == -2
+    assert ffr(C.byref(s), 2, p, C.byref(lay), w1, w2, w1, w4, p, None, p, 1 << 30, None) == -1  # aliases
+    bwr = lib.moe_expert_ffn_bwd_replicas
+    g1, g2 = C.c_void_p(1 << 20), C.c_void_p(1 << 21)
+    q, r = C.c_void_p(8192), C.c_void_p(12288)
+    assert bwr(C.byref(s), 2, p, p, None, C.byref(lay), w1, w2, w3, w4, q, r, C.c_void_p(16384), None, g2, p,
+               1 << 30, None) == -1                                             # no replica grad buffer
+    assert bwr(C.byref(s), 2, p, p, None, C.byref(lay), w1, w2, w3, w4, q, r, C.c_void_p(16384), g1, g1, p,
+               1 << 30, None) == -1                                             # replica grads alias
+    assert bwr(C.byref(s), 2, p, p, None, C.byref(lay), w1, w2, w3, w4, q, r, C.c_void_p(16384), g1, w4, p,
+               1 << 30, None) == -1                                             # replica grad aliases a weight
     s = moe.make_shape(16, 64, 8, 2, inter=64, act_dtype=moe.MOE_DT_F32)
     assert lib.moe_expert_ffn(C.byref(s), p, C.byref(lay), p, p, p, None, p, 1 << 30, None) == -4  # fp32 FFN
     s = moe.make_shape(16, 64, 8, 2, inter=96)
