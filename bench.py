@@ -261,7 +261,7 @@ def bench_skewed_capacity(moe, mi, torch, steps, warmup):
     return res
 
 
-def bench_expert_gemm(moe, mi, torch, wid, iters, warmup, bwd_iters=0):
+def bench_expert_gemm(moe, mi, torch, wid, iters, warmup, bwd_iters=0, replicas=0):
     import numpy as np
     w = mi.workload(wid)
     dev = torch.device("cuda")
@@ -313,18 +313,44 @@ def bench_expert_gemm(moe, mi, torch, wid, iters, warmup, bwd_iters=0):
     bal_ms = a.elapsed_time(b) / iters
     bal_rows = int(layb.counters[0].item())
     out.update(balanced_ms=bal_ms, balanced_tflops=2.0 * bal_rows * h * 3 * inter / bal_ms / 1e9, balanced_rows=bal_rows)
-    del rb, xb, xpb, layb, yb, ws
+    del rb, xb, xpb, layb, yb
+
+    def timed(fn, n):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(n):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+
+    if replicas > 0:
+        # hot-expert replication: placement from the expert counts, weight sync,
+        # reroute, and the FFN over masters + replica slots
+        counts = lay.tokens_per_expert
+        rep = moe.moe_replica_plan(counts, replicas)
+        wgu_r, wd_r = moe.moe_replica_sync(wgu, wd, rep)
+        phys = moe.moe_reroute(idx, e, rep)
+        xp_r, _, lay_r = moe.moe_dispatch(x, phys, wts, e + replicas, max_rows=w.rows)
+        y_r = torch.empty_like(xp_r)
+        rr_shape = moe.make_shape(idx.shape[0], h, e, idx.shape[1])
+        ws_rr = torch.empty(moe.workspace_size(moe.MOE_OP_REROUTE, rr_shape) + 256, dtype=torch.uint8, device=dev)
+        plan_ms = timed(lambda: moe.moe_replica_plan(counts, replicas, out=rep), iters)
+        sync_ms = timed(lambda: moe.moe_replica_sync(wgu, wd, rep, w_gate_up_replica=wgu_r, w_down_replica=wd_r), iters)
+        rr_ms = timed(lambda: moe.moe_reroute(idx, e, rep, out=phys, workspace=ws_rr), iters)
+        ffn_r_ms = timed(lambda: moe.moe_expert_ffn_replicas(xp_r, lay_r, wgu, wd, wgu_r, wd_r, y=y_r, workspace=ws),
+                         iters)
+        sync_bytes = 2 * replicas * 3 * inter * h * 2          # read and write each replica's weights
+        out.update(replication=dict(n_replicas=replicas, plan_us=plan_ms * 1e3, reroute_us=rr_ms * 1e3,
+                                    sync_us=sync_ms * 1e3, sync_gbs=sync_bytes / sync_ms / 1e6,
+                                    ffn_us=ffn_r_ms * 1e3, ffn_tflops=flops / ffn_r_ms / 1e9,
+                                    max_rows_per_expert=int(counts.max().item()),
+                                    max_rows_per_copy=int(lay_r.tokens_per_expert.max().item())))
+        del wgu_r, wd_r, phys, xp_r, lay_r, y_r, ws_rr
+    del ws
     if bwd_iters > 0:
-        def timed(fn, n):
-            for _ in range(warmup):
-                fn()
-            torch.cuda.synchronize()
-            a.record()
-            for _ in range(n):
-                fn()
-            b.record()
-            torch.cuda.synchronize()
-            return a.elapsed_time(b) / n
 
         # training forward: also stores the pre-activations [G | U] for the backward
         gu = torch.empty((xp.shape[0], 2 * inter), dtype=torch.bfloat16, device=dev)
@@ -470,7 +496,8 @@ def main():
     if not args.skip_gemm:
         for wid in (4, 5):
             log(f"expert GEMM: workload {mi.workload(wid).name}")
-            gemm.append(bench_expert_gemm(moe, mi, torch, wid, args.gemm_iters, 2, args.bwd_iters))
+            gemm.append(bench_expert_gemm(moe, mi, torch, wid, args.gemm_iters, 2, args.bwd_iters,
+                                          replicas=8 if wid == 5 else 0))
     cpu = None
     if not args.skip_cpu:
         log("cpu baseline (oracle)")
@@ -541,7 +568,9 @@ def main():
                              "bwd_us": round(g["bwd_ms"] * 1e3, 1), "bwd_tflops": round(g["bwd_tflops"], 1),
                              "bwd_frac_bf16_peak": round(g["bwd_tflops"] / BF16_PEAK_TFLOPS, 4),
                              "bwd_recompute_us": round(g["bwd_recompute_ms"] * 1e3, 1),
-                             "bwd_recompute_tflops": round(g["bwd_recompute_tflops"], 1)} if "bwd_ms" in g else {})}
+                             "bwd_recompute_tflops": round(g["bwd_recompute_tflops"], 1)} if "bwd_ms" in g else {}),
+                         **({"replication": {k_: (round(v, 2) if isinstance(v, float) else v)
+                                             for k_, v in g["replication"].items()}} if "replication" in g else {})}
                         for g in gemm],
         "cpu_baseline": cpu,
     }
