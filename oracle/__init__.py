@@ -71,6 +71,8 @@ def lib():
         L.oracle_bf16_round_array.restype = None
         L.oracle_bf16_round.restype = C.c_uint16
         L.oracle_mx_quantize.argtypes = [i64, i64, p, p, p]
+        L.oracle_expert_ffn_mxfp8_rows.argtypes = [i64, p, i32, i64, i64, p, p, p, p, p, p, p, p, p, p]
+        L.oracle_expert_ffn_mxfp8_rows.restype = None
         L.oracle_replica_plan.argtypes = [i32, p, i32, p]
         L.oracle_replica_plan.restype = None
         L.oracle_reroute.argtypes = [i64, i32, i32, p, i32, p, p]
@@ -224,6 +226,25 @@ def mx_dequantize(q: np.ndarray, scale: np.ndarray) -> np.ndarray:
     n, h = q.shape
     s = np.repeat(np.asarray(scale, np.int64).reshape(n, h // 32) - 127, 32, axis=1)
     return np.ldexp(e4m3_decode(q), s)
+
+
+def expert_ffn_mxfp8_rows(rows, xq, xs, lay, wguq, wgus, wdq, wds):
+    """SwiGLU FFN over MXFP8 operands for the listed permuted rows -> (y_rows bf16 bits [len, H],
+    expert_of).  xq [R, H] / xs [R, H/32]; wguq [E, 2I, H] / wgus [E, 2I, H/32]; wdq [E, H, I] /
+    wds [E, H, I/32]."""
+    rows = np.ascontiguousarray(rows, dtype=np.int64)
+    e, two_i, h = wguq.shape
+    inter = two_i // 2
+    assert wdq.shape == (e, h, inter) and wgus.shape == (e, two_i, h // 32) and wds.shape == (e, h, inter // 32)
+    y = np.zeros((rows.size, h), np.uint16)
+    ex = np.empty(rows.size, np.int32)
+    c = np.ascontiguousarray
+    lib().oracle_expert_ffn_mxfp8_rows(rows.size, _p(rows), e, h, inter, _p(c(xq, dtype=np.uint8)),
+                                       _p(c(xs, dtype=np.uint8)), _p(lay["expert_offsets"]),
+                                       _p(lay["tokens_per_expert"]), _p(c(wguq, dtype=np.uint8)),
+                                       _p(c(wgus, dtype=np.uint8)), _p(c(wdq, dtype=np.uint8)),
+                                       _p(c(wds, dtype=np.uint8)), _p(y), _p(ex))
+    return y, ex
 
 
 def dispatch_mxfp8(x: np.ndarray, k: int, lay: dict, topk_w: np.ndarray, x_perm_q=None, x_perm_scale=None):

@@ -356,6 +356,8 @@ void oracle_scatter(int64_t n, int k, int64_t row_bytes, const uint8_t *x, const
   }
 }
 
+static double silu(double z);
+
 /* -------------------------------------------------------- MXFP8 dispatch */
 
 /* FP8 dispatch ([MORI] commit log: optional FP8 dispatch, a per-token scale
@@ -393,12 +395,10 @@ static uint8_t e4m3_encode(double v) {
   return (uint8_t)(c | (signbit(v) ? 0x80 : 0));
 }
 
-/* MXFP8 quantisation of `rows` bf16 rows of h elements (h a multiple of 32):
- * q [rows, h] E4M3 codes, scale [rows, h/32] E8M0 codes. */
-void oracle_mx_quantize(int64_t rows, int64_t h, const uint16_t *x, uint8_t *q, uint8_t *scale) {
-  for (int64_t r = 0; r < rows; ++r)
-    for (int64_t b = 0; b < h / 32; ++b) {
-      const uint16_t *v = x + r * h + 32 * b;
+/* MXFP8 of one bf16 row of h elements (h a multiple of 32). */
+static void mx_quantize_row(int64_t h, const uint16_t *x, uint8_t *q, uint8_t *scale) {
+  for (int64_t b = 0; b < h / 32; ++b) {
+      const uint16_t *v = x + 32 * b;
       double amax = 0.0;
       for (int i = 0; i < 32; ++i)
         if (fabs(bf16_value(v[i])) > amax) amax = fabs(bf16_value(v[i]));
@@ -410,9 +410,75 @@ void oracle_mx_quantize(int64_t rows, int64_t h, const uint16_t *x, uint8_t *q, 
         if (s < -127) s = -127;
         if (s > 127) s = 127;
       }
-      scale[r * (h / 32) + b] = (uint8_t)(s + 127);
-      for (int i = 0; i < 32; ++i) q[r * h + 32 * b + i] = e4m3_encode(ldexp(bf16_value(v[i]), -s));
+      scale[b] = (uint8_t)(s + 127);
+      for (int i = 0; i < 32; ++i) q[32 * b + i] = e4m3_encode(ldexp(bf16_value(v[i]), -s));
+  }
+}
+
+/* MXFP8 quantisation of `rows` bf16 rows of h elements (h a multiple of 32):
+ * q [rows, h] E4M3 codes, scale [rows, h/32] E8M0 codes. */
+void oracle_mx_quantize(int64_t rows, int64_t h, const uint16_t *x, uint8_t *q, uint8_t *scale) {
+  for (int64_t r = 0; r < rows; ++r) mx_quantize_row(h, x + r * h, q + r * h, scale + r * (h / 32));
+}
+
+/* Value of element i of an MXFP8 row: E4M3 code times 2^(scale code - 127). */
+static double mx_value(const uint8_t *q, const uint8_t *scale, int64_t i) {
+  const int c = q[i] & 0x7F;
+  const double v = ldexp(e4m3_value(c), (int)scale[i / 32] - 127);
+  return (q[i] & 0x80) ? -v : v;
+}
+
+/* The SwiGLU expert over MXFP8 operands (the expert FFN with FP8 grouped
+ * experts: the dispatched rows as moe_dispatch_mxfp8 writes them, the weights
+ * MXFP8 along their K dimension).  For a row r of expert e's segment, with
+ * every operand value the exact value of its code and scale:
+ *   g_i, u_i = sum_h x[r,h] W_gu[e, i, h], sum_h x[r,h] W_gu[e, I+i, h]  (double)
+ *   a_i      = bf16(silu(g_i) * u_i)            (the bf16 intermediate)
+ *   a'       = MXFP8 of the row a (blocks of 32 along I), dequantised
+ *   y[r, c]  = bf16(sum_i a'_i W_d[e, c, i])                          (double)
+ * The same listed-rows interface as oracle_expert_ffn_rows; xq [.., h], xs
+ * [.., h/32]; wguq [E, 2I, h], wgus [E, 2I, h/32]; wdq [E, h, I], wds [E, h, I/32]. */
+void oracle_expert_ffn_mxfp8_rows(int64_t nrows, const int64_t *rows, int e, int64_t h, int64_t inter,
+                                  const uint8_t *xq, const uint8_t *xs, const int32_t *offsets,
+                                  const int32_t *counts, const uint8_t *wguq, const uint8_t *wgus,
+                                  const uint8_t *wdq, const uint8_t *wds, uint16_t *y_rows, int32_t *expert_of) {
+  double *x = malloc(sizeof(double) * (size_t)h);
+  uint16_t *a = malloc(sizeof(uint16_t) * (size_t)inter);
+  uint8_t *aq = malloc((size_t)inter), *as = malloc((size_t)(inter / 32));
+  for (int64_t j = 0; j < nrows; ++j) {
+    const int64_t r = rows[j];
+    int ex = -1;
+    for (int x_ = 0; x_ < e; ++x_)
+      if (r >= offsets[x_] && r < (int64_t)offsets[x_] + counts[x_]) ex = x_;
+    expert_of[j] = ex;
+    if (ex < 0) {
+      memset(y_rows + j * h, 0, sizeof(uint16_t) * (size_t)h);
+      continue;
     }
+    for (int64_t c = 0; c < h; ++c) x[c] = mx_value(xq + r * h, xs + r * (h / 32), c);
+    const int64_t gu_row = 2 * inter;
+    for (int64_t i = 0; i < inter; ++i) {
+      double g = 0.0, u = 0.0;
+      const int64_t gi = (int64_t)ex * gu_row + i, ui = (int64_t)ex * gu_row + inter + i;
+      for (int64_t c = 0; c < h; ++c) {
+        g += x[c] * mx_value(wguq + gi * h, wgus + gi * (h / 32), c);
+        u += x[c] * mx_value(wguq + ui * h, wgus + ui * (h / 32), c);
+      }
+      a[i] = bf16_round(silu(g) * u);
+    }
+    mx_quantize_row(inter, a, aq, as);
+    for (int64_t c = 0; c < h; ++c) {
+      const int64_t di = (int64_t)ex * h + c;
+      double acc = 0.0;
+      for (int64_t i = 0; i < inter; ++i)
+        acc += mx_value(aq, as, i) * mx_value(wdq + di * inter, wds + di * (inter / 32), i);
+      y_rows[j * h + c] = bf16_round(acc);
+    }
+  }
+  free(x);
+  free(a);
+  free(aq);
+  free(as);
 }
 
 /* Element-wise E4M3 encoding of n doubles (the element step alone, scale 1). */

@@ -199,3 +199,52 @@ def test_dispatch_mxfp8_rows_are_quantised_token_rows(capacity, row_align):
     for r in range(lay["rows"]):
         if lay["row_src"][r] < 0 and r < end:
             assert not pq[r].any() and not ps[r].any() and wp[r] == 0
+
+
+# ------------------------------------------------------------ MXFP8 expert FFN
+
+def _mx(shape, scale_sigma, rng):
+    x = mi.f32_to_bf16_bits((rng.standard_normal(shape) * scale_sigma).astype(np.float32))
+    q, s = oracle.mx_quantize(x.reshape(-1, shape[-1]))
+    return q.reshape(shape), s.reshape(shape[:-1] + (shape[-1] // 32,))
+
+
+def test_expert_ffn_mxfp8_matches_composed_pinned_steps():
+    """The MXFP8 FFN oracle equals its definition composed from independently
+    pinned pieces: MX dequantisation, numpy fp64 matmuls, the bf16 rounding, the
+    MX quantisation of the intermediate."""
+    rng = np.random.default_rng(77)
+    e, h, inter, rows = 3, 64, 64, 20
+    xq, xs = _mx((rows, h), 1.0, rng)
+    gq, gs = _mx((e, 2 * inter, h), 0.1, rng)
+    dq, ds = _mx((e, h, inter), 0.1, rng)
+    lay = {"expert_offsets": np.array([0, 6, 6, 17], np.int32), "tokens_per_expert": np.array([6, 0, 11], np.int32)}
+    got, ex = oracle.expert_ffn_mxfp8_rows(np.arange(rows), xq, xs, lay, gq, gs, dq, ds)
+    x = oracle.mx_dequantize(xq, xs)
+    wgu = oracle.mx_dequantize(gq.reshape(-1, h), gs.reshape(-1, h // 32)).reshape(e, 2 * inter, h)
+    wd = oracle.mx_dequantize(dq.reshape(-1, inter), ds.reshape(-1, inter // 32)).reshape(e, h, inter)
+    for r in range(rows):
+        x_e = {0: 0, 1: 0, 2: 0, 3: 0, 4: 0, 5: 0}.get(r, 2 if 6 <= r < 17 else -1)
+        assert ex[r] == x_e
+        if x_e < 0:
+            assert not got[r].any()
+            continue
+        gu = wgu[x_e] @ x[r]
+        g, u = gu[:inter], gu[inter:]
+        a = oracle.bf16_round_array(g / (1 + np.exp(-g)) * u)
+        aq, as_ = oracle.mx_quantize(a[None, :])
+        y = wd[x_e] @ oracle.mx_dequantize(aq, as_)[0]
+        np.testing.assert_array_equal(got[r], oracle.bf16_round_array(y))
+
+
+def test_expert_ffn_mxfp8_zero_gate():
+    """Zero gate weights give exactly zero rows (silu(0) = 0)."""
+    rng = np.random.default_rng(5)
+    e, h, inter, rows = 2, 64, 32, 8
+    xq, xs = _mx((rows, h), 1.0, rng)
+    gq, gs = _mx((e, 2 * inter, h), 0.1, rng)
+    dq, ds = _mx((e, h, inter), 0.1, rng)
+    gq[:, :inter] = 0
+    lay = {"expert_offsets": np.array([0, 4, 8], np.int32), "tokens_per_expert": np.array([4, 4], np.int32)}
+    got, _ = oracle.expert_ffn_mxfp8_rows(np.arange(rows), xq, xs, lay, gq, gs, dq, ds)
+    assert not got.any()
