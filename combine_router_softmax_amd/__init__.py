@@ -23,14 +23,14 @@ MOE_DT_F32 = 0
 MOE_DT_BF16 = 1
 MOE_DROP_POSITION, MOE_DROP_PROBS = 0, 1
 (MOE_OP_ROUTE, MOE_OP_DISPATCH, MOE_OP_EXPERT_FFN, MOE_OP_COMBINE, MOE_OP_COMBINE_BWD, MOE_OP_EXPERT_FFN_BWD,
- MOE_OP_REROUTE) = range(7)
+ MOE_OP_REROUTE, MOE_OP_EXPERT_FFN_MXFP8) = range(8)
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_layout_rows", "moe_workspace_size", "moe_route", "moe_route_random", "moe_dispatch",
            "moe_dispatch_mxfp8", "moe_expert_ffn",
            "moe_expert_ffn_bwd", "moe_combine", "moe_dispatch_bwd", "moe_combine_bwd", "moe_status_string",
            "moe_version", "moe_replica_plan", "moe_reroute", "moe_replica_sync", "moe_replica_grad_reduce",
-           "moe_expert_ffn_replicas", "moe_expert_ffn_bwd_replicas")
+           "moe_expert_ffn_replicas", "moe_expert_ffn_bwd_replicas", "moe_mx_quantize", "moe_expert_ffn_mxfp8")
 
 
 class MoeShape(C.Structure):
@@ -69,6 +69,8 @@ def _load():
     lib.moe_combine_bwd.argtypes = [sp, p, p, p, lp, p, p, p]
     lib.moe_dispatch_bwd.argtypes = [sp, p, lp, p, p]
     lib.moe_replica_plan.argtypes = [sp, p, i32, p, p]
+    lib.moe_mx_quantize.argtypes = [C.c_int64, C.c_int64, p, p, p, p]
+    lib.moe_expert_ffn_mxfp8.argtypes = [sp, p, p, lp, p, p, p, p, p, p, C.c_size_t, p]
     lib.moe_reroute.argtypes = [sp, p, p, i32, p, p, C.c_size_t, p]
     lib.moe_replica_sync.argtypes = [sp, p, i32, p, p, p, p, p]
     lib.moe_replica_grad_reduce.argtypes = [sp, p, i32, p, p, p, p, p]
@@ -76,7 +78,8 @@ def _load():
     lib.moe_expert_ffn_bwd_replicas.argtypes = [sp, i32, p, p, p, lp, p, p, p, p, p, p, p, p, p, p, C.c_size_t, p]
     for f in ("moe_workspace_size", "moe_route", "moe_route_random", "moe_dispatch", "moe_dispatch_mxfp8", "moe_expert_ffn", "moe_expert_ffn_bwd", "moe_combine",
               "moe_combine_bwd", "moe_dispatch_bwd", "moe_replica_plan", "moe_reroute", "moe_replica_sync",
-              "moe_replica_grad_reduce", "moe_expert_ffn_replicas", "moe_expert_ffn_bwd_replicas"):
+              "moe_replica_grad_reduce", "moe_expert_ffn_replicas", "moe_expert_ffn_bwd_replicas", "moe_mx_quantize",
+              "moe_expert_ffn_mxfp8"):
         getattr(lib, f).restype = i32
     lib.moe_status_string.argtypes = [i32]
     lib.moe_status_string.restype = C.c_char_p
@@ -470,6 +473,53 @@ def moe_expert_ffn_bwd_replicas(x_perm: torch.Tensor, grad_y: torch.Tensor, layo
                            workspace)
 
 
+def moe_mx_quantize(x: torch.Tensor, *, q: torch.Tensor | None = None, scale: torch.Tensor | None = None):
+    """MXFP8 of a bf16 matrix along its rows (include/moe.h moe_mx_quantize): x [..., cols]
+    -> (q uint8 [..., cols] E4M3 codes, scale uint8 [..., cols/32] E8M0 codes)."""
+    _bf16((x, "x"))
+    cols = x.shape[-1]
+    rows = x.numel() // cols if cols else 0
+    if q is None:
+        q = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    if scale is None:
+        scale = torch.empty(x.shape[:-1] + (cols // 32,), dtype=torch.uint8, device=x.device)
+    _check(lib.moe_mx_quantize(rows, cols, _ptr(x), _ptr(q), _ptr(scale), _stream(x.device)), "moe_mx_quantize")
+    return q, scale
+
+
+def moe_expert_ffn_mxfp8(x_perm_q: torch.Tensor, x_perm_scale: torch.Tensor, layout: Layout,
+                         w_gate_up_q: torch.Tensor, w_gate_up_scale: torch.Tensor, w_down_q: torch.Tensor,
+                         w_down_scale: torch.Tensor, *, y: torch.Tensor | None = None, workspace=None):
+    """Grouped SwiGLU FFN over MXFP8 operands (include/moe.h moe_expert_ffn_mxfp8): x_perm_q [R, H] +
+    x_perm_scale [R, H/32] (moe_dispatch_mxfp8), weights from moe_mx_quantize: w_gate_up_q
+    [E, 2I, H] + [E, 2I, H/32], w_down_q [E, H, I] + [E, H, I/32] -> y bf16 [R, H]."""
+    for t, name in ((x_perm_q, "x_perm_q"), (x_perm_scale, "x_perm_scale"), (w_gate_up_q, "w_gate_up_q"),
+                    (w_gate_up_scale, "w_gate_up_scale"), (w_down_q, "w_down_q"), (w_down_scale, "w_down_scale")):
+        _contig(t, name)
+        if t.dtype != torch.uint8:
+            raise TypeError(f"{name} must be uint8")
+    rows, h = x_perm_q.shape
+    e, two_i, h2 = w_gate_up_q.shape
+    inter = two_i // 2
+    if (h2 != h or tuple(w_down_q.shape) != (e, h, inter) or tuple(x_perm_scale.shape) != (rows, h // 32)
+            or tuple(w_gate_up_scale.shape) != (e, two_i, h // 32) or tuple(w_down_scale.shape) != (e, h, inter // 32)
+            or e != layout.n_experts or rows != layout.rows):
+        raise ValueError("inconsistent MXFP8 expert FFN shapes")
+    dev = x_perm_q.device
+    shape = layout.shape(h, MOE_DT_BF16, inter)
+    if y is None:
+        y = torch.empty((rows, h), dtype=torch.bfloat16, device=dev)
+    if workspace is None:
+        ws, nbytes = _workspace(MOE_OP_EXPERT_FFN_MXFP8, shape, dev)
+    else:
+        ws, nbytes = workspace, workspace.numel() - 256
+    lc = layout.c()
+    _check(lib.moe_expert_ffn_mxfp8(C.byref(shape), _ptr(x_perm_q), _ptr(x_perm_scale), C.byref(lc), _ptr(w_gate_up_q),
+                                    _ptr(w_gate_up_scale), _ptr(w_down_q), _ptr(w_down_scale), _ptr(y), _ws_ptr(ws),
+                                    nbytes, _stream(dev)), "moe_expert_ffn_mxfp8")
+    return y
+
+
 def moe_replica_plan(tokens_per_expert: torch.Tensor, n_replicas: int, *, out: torch.Tensor | None = None):
     """Hot-expert placement (include/moe.h moe_replica_plan) -> replica_of int32 [n_replicas]."""
     _contig(tokens_per_expert, "tokens_per_expert")
@@ -586,7 +636,8 @@ def moe_combine_bwd(grad_out: torch.Tensor, y: torch.Tensor, topk_w: torch.Tenso
     return grad_y, grad_w
 
 
-__all__ = ["moe_route", "moe_route_random", "moe_dispatch", "moe_dispatch_mxfp8", "moe_replica_plan", "moe_reroute",
+__all__ = ["moe_route", "moe_route_random", "moe_dispatch", "moe_dispatch_mxfp8", "moe_mx_quantize",
+           "moe_expert_ffn_mxfp8", "moe_replica_plan", "moe_reroute",
            "moe_replica_sync", "moe_replica_grad_reduce", "moe_expert_ffn_replicas", "moe_expert_ffn_bwd_replicas", "moe_expert_ffn", "moe_expert_ffn_bwd", "moe_combine", "moe_combine_bwd",
            "moe_dispatch_bwd",
            "Layout", "RouteOut",

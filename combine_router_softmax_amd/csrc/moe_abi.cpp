@@ -113,6 +113,10 @@ moe_status moe_workspace_size(moe_op op, const moe_shape *s, size_t *bytes) {
       if (s->inter < 1) return MOE_ERR_INVALID_ARG;
       *bytes = moe::ffn_workspace_bytes(rows_of(s), s->inter);
       return MOE_OK;
+    case MOE_OP_EXPERT_FFN_MXFP8:
+      if (s->inter < 1) return MOE_ERR_INVALID_ARG;
+      *bytes = moe::ffn_mxfp8_workspace_bytes(rows_of(s), s->inter);
+      return MOE_OK;
     case MOE_OP_REROUTE:
       *bytes = moe::reroute_workspace_bytes(s->n_tokens * s->top_k, s->n_experts);
       return MOE_OK;
@@ -372,6 +376,44 @@ moe_status moe_expert_ffn_bwd_replicas(const moe_shape *s, int32_t n_replicas, c
   }
   return expert_ffn_bwd(s, x_perm, grad_y, gate_up, layout, w_gate_up, w_down, grad_x_perm, grad_w_gate_up,
                         grad_w_down, &rep, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_mx_quantize(int64_t rows, int64_t cols, const void *x, uint8_t *q, uint8_t *scale, void *stream) {
+  if (rows < 0 || cols < 1) return MOE_ERR_INVALID_ARG;
+  if (cols % 32 != 0) return MOE_ERR_UNSUPPORTED;
+  if (rows > kMaxIndex) return MOE_ERR_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!x || !q || !scale || q == scale) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(q)) return MOE_ERR_MISALIGNED;
+  return hip_status(moe::launch_scatter_mxfp8(static_cast<const uint16_t *>(x), rows, 1, cols, nullptr, q, scale, 0,
+                                              nullptr, nullptr, as_stream(stream)));
+}
+
+moe_status moe_expert_ffn_mxfp8(const moe_shape *s, const uint8_t *x_perm_q, const uint8_t *x_perm_scale,
+                                const moe_layout *layout, const uint8_t *w_gate_up_q, const uint8_t *w_gate_up_scale,
+                                const uint8_t *w_down_q, const uint8_t *w_down_scale, void *y, void *workspace,
+                                size_t workspace_bytes, void *stream) {
+  int64_t rows;
+  moe_status st = check_ffn_shape(s, &rows);
+  if (st != MOE_OK) return st;
+  if (s->hidden % 512 != 0 || s->inter % 512 != 0) return MOE_ERR_UNSUPPORTED;  // scale groups of 4 K steps
+  if (!layout || !layout->tokens_per_expert || !layout->expert_offsets) return MOE_ERR_INVALID_ARG;
+  if (!w_gate_up_q || !w_gate_up_scale || !w_down_q || !w_down_scale) return MOE_ERR_INVALID_ARG;
+  if (rows > 0 && (!x_perm_q || !x_perm_scale || !y)) return MOE_ERR_INVALID_ARG;
+  // codes 16-byte aligned; scale rows are multiples of 16 bytes (H/32, I/32)
+  const void *al[] = {x_perm_q, x_perm_scale, w_gate_up_q, w_gate_up_scale, w_down_q, w_down_scale, y};
+  for (const void *ptr : al)
+    if (ptr && !aligned16(ptr)) return MOE_ERR_MISALIGNED;
+  const void *ins[] = {x_perm_q, x_perm_scale, w_gate_up_q, w_gate_up_scale, w_down_q, w_down_scale};
+  for (const void *in : ins)
+    if (in && in == y) return MOE_ERR_INVALID_ARG;
+  const size_t need_ws = moe::ffn_mxfp8_workspace_bytes(rows, s->inter);
+  if (workspace_bytes < need_ws || (need_ws > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))))
+    return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_expert_ffn_mxfp8(x_perm_q, x_perm_scale, rows, s->hidden, s->inter, s->n_experts,
+                                                 s->capacity, layout->tokens_per_expert, layout->expert_offsets,
+                                                 w_gate_up_q, w_gate_up_scale, w_down_q, w_down_scale,
+                                                 static_cast<uint16_t *>(y), workspace, as_stream(stream)));
 }
 
 moe_status moe_replica_plan(const moe_shape *s, const int32_t *tokens_per_expert, int32_t n_replicas,

@@ -38,12 +38,15 @@
 // of an expert's segment re-read its last row and are not stored.
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
+#include "moe_mx.hpp"
 
 namespace moe {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int kBM = 256;
 constexpr int kBN = 256;
@@ -58,6 +61,12 @@ constexpr int kThreads = 256;
 constexpr int kXcds = 8;
 constexpr int kMaxExperts = 1024;
 static_assert(kSlots * kOperandBytes <= 160 * 1024, "LDS budget");
+// MXFP8 operands (E4M3 codes, 128 per K step in the same 128-byte tile rows):
+// a ring of four operand tiles and the E8M0 scales of two groups of four K
+// steps, each group 16 bytes per tile row for each operand.
+constexpr int kSlots8 = 4;
+constexpr int kScaleGroupBytes = 2 * kBM * 16;  // A and B scales of one group of 4 K steps
+static_assert(kSlots8 * kOperandBytes + 2 * kScaleGroupBytes <= 160 * 1024, "LDS budget (MXFP8)");
 static_assert(kLoads == 8, "load schedule below: 8 load instructions per wave per operand tile");
 
 // LDS position of 16-byte chunk c of tile row r is c ^ swz(r).  A fragment
@@ -319,6 +328,74 @@ __device__ __forceinline__ void slice(const bf16x8 (&a)[4], const bf16x8 (&b)[4]
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// MXFP8 fragments: the MFMA v_mfma_scale_f32_32x32x64_f8f6f4 takes, in lane l
+// (h = l/32), K values 16h .. 16h+15 and 32+16h .. 32+16h+15 of row l%32 as its
+// 32 operand bytes (measured with an in-bounds probe) -- in a tile row of 128
+// codes, slice i's chunks 4i+h and 4i+2+h, which are the chunks the bf16
+// fragment reads of slices 2i and 2i+1 fetch.  So a slice-i MXFP8 fragment is
+// those two bf16 reads side by side.
+template <bool kSwiGLU>
+__device__ __forceinline__ void load_frags_fp8(const char *__restrict__ as, const char *__restrict__ bs, int i, int wm,
+                                               int wn, int l, i32x8 (&a)[4], i32x8 (&b)[4]) {
+  bf16x8 a0[4], b0[4], a1[4], b1[4];
+  const uint32_t none[4][2] = {};
+  load_frags<kSwiGLU, false, false>(as, bs, 2 * i, wm, wn, l, a0, b0, none, none);
+  load_frags<kSwiGLU, false, false>(as, bs, 2 * i + 1, wm, wn, l, a1, b1, none, none);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const i32x4 x0 = __builtin_bit_cast(i32x4, a0[j]), x1 = __builtin_bit_cast(i32x4, a1[j]);
+    const i32x4 y0 = __builtin_bit_cast(i32x4, b0[j]), y1 = __builtin_bit_cast(i32x4, b1[j]);
+    a[j] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+    b[j] = __builtin_shufflevector(y0, y1, 0, 1, 2, 3, 4, 5, 6, 7);
+  }
+}
+
+// MXFP8 MFMAs FIRST .. FIRST+COUNT-1 of one 64-wide K slice, numbered as in
+// mfma_range.  Lane l's scale operand covers its row and 32-value block l/32 of
+// the slice: the lane's scale words hold the K step's four block codes shifted
+// right by 8*(l/32), so byte 2*slice (the op_sel) is its block.
+template <int FIRST, int COUNT, int kOpsel>
+__device__ __forceinline__ void mfma8_range(const i32x8 (&a)[4], const i32x8 (&b)[4], const uint32_t (&sa)[4],
+                                            const uint32_t (&sb)[4], f32x16 (&acc)[4][4]) {
+#pragma unroll
+  for (int i = FIRST; i < FIRST + COUNT; ++i)
+    acc[i / 4][i % 4] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+        b[i % 4], a[i / 4], acc[i / 4][i % 4], 0, 0, kOpsel, (int)sb[i % 4], kOpsel, (int)sa[i / 4]);
+}
+
+// One MXFP8 K slice (as slice(): the reads of what comes next paired with the
+// first MFMAs, the four load slots between the later ones).
+template <int MI, int kReads, int kOpsel, typename Dma>
+__device__ __forceinline__ void slice_fp8(const i32x8 (&a)[4], const i32x8 (&b)[4], const uint32_t (&sa)[4],
+                                          const uint32_t (&sb)[4], f32x16 (&acc)[4][4], Dma &&dma) {
+  constexpr int kPart = MI / 2;
+  constexpr int kHead = 4 * MI - 4 * kPart;
+  constexpr int kDsRead = 0x100, kMfma = 0x008;
+  mfma8_range<0, kHead, kOpsel>(a, b, sa, sb, acc);
+#pragma unroll
+  for (int i = 0; i < kHead; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kDsRead, (kReads + kHead - 1) / kHead, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  mfma8_range<kHead, kPart, kOpsel>(a, b, sa, sb, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  dma(0);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma8_range<kHead + kPart, kPart, kOpsel>(a, b, sa, sb, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  dma(1);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma8_range<kHead + 2 * kPart, kPart, kOpsel>(a, b, sa, sb, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  dma(2);
+  __builtin_amdgcn_sched_barrier(0);
+  mfma8_range<kHead + 3 * kPart, kPart, kOpsel>(a, b, sa, sb, acc);
+  __builtin_amdgcn_sched_barrier(0);
+  dma(3);
+  __builtin_amdgcn_sched_barrier(0);
+}
+
 // Modes of the grouped GEMM.  kModePlain: per expert segment, C = A B_e^T
 // (y = act W_down^T, and the backward's products with the weights).
 // kModeSwiGLU: B tile rows 0..127 are gate rows n0.., rows 128..255 the up rows
@@ -330,20 +407,29 @@ __device__ __forceinline__ void slice(const bf16x8 (&a)[4], const bf16x8 (&b)[4]
 // only kBT (B = a weight [K, N] of each expert); weight-gradient mode takes both.
 // gate_up (SwiGLU mode, nullable): also store the pre-activations [rows, 2I],
 // gate columns then up columns, for the backward.
+// kFp8: A and B are MXFP8 (E4M3 codes [.., K] with E8M0 scales A_scale [rows,
+// K/32], B_scale [E, N rows, K/32]; K a multiple of 512); plain mode writes
+// bf16 C, SwiGLU mode writes the intermediate as MXFP8 (codes into C as bytes
+// [rows, ldc], scales into C_scale [rows, ldc/32]).
 constexpr int kModePlain = 0, kModeSwiGLU = 1, kModeWGrad = 2;
 
-template <int kMode, bool kAT, bool kBT>
+template <int kMode, bool kAT, bool kBT, bool kFp8 = false>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int64_t b_expert_stride, int K, int M, int N,
     int m_tiles, int n_tiles, const int32_t *__restrict__ tokens_per_expert,
     const int32_t *__restrict__ expert_offsets, int e, uint16_t *__restrict__ C, int64_t ldc,
-    uint16_t *__restrict__ gate_up, const uint16_t *__restrict__ B_rep, uint16_t *__restrict__ C_rep, int e_master) {
+    uint16_t *__restrict__ gate_up, const uint16_t *__restrict__ B_rep, uint16_t *__restrict__ C_rep, int e_master,
+    const uint8_t *__restrict__ A_scale, const uint8_t *__restrict__ B_scale, uint8_t *__restrict__ C_scale) {
   constexpr bool kSwiGLU = kMode == kModeSwiGLU, kWGrad = kMode == kModeWGrad;
   static_assert(kWGrad ? (kAT && kBT) : !kAT, "operand layouts of the modes");
   static_assert(!(kSwiGLU && kBT), "the SwiGLU pairing reads K-contiguous weights");
-  // ring of operand tiles; also find_tile's scratch before the K loop and the
-  // output staging after it
-  __shared__ __attribute__((aligned(1024))) char ring[kSlots * kOperandBytes];
+  static_assert(!kFp8 || (!kAT && !kBT && !kWGrad), "MXFP8 operands: K-contiguous forward GEMMs");
+  constexpr int kEsz = kFp8 ? 1 : 2;            // bytes per operand element
+  constexpr int kStepK = kRowBytes / kEsz;      // K values per step
+  // ring of operand tiles (MXFP8: and the scale groups after it); also
+  // find_tile's scratch before the K loop and the output staging after it
+  __shared__ __attribute__((aligned(1024))) char ring[kFp8 ? kSlots8 * kOperandBytes + 2 * kScaleGroupBytes
+                                                            : kSlots * kOperandBytes];
 
   const int l = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -354,6 +440,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   // bases at K = 0 and the output base
   int n0, rows_valid, KT, k_len;
   const char *a_base, *b_base;
+  const uint8_t *as_base = nullptr, *bs_base = nullptr;  // MXFP8 scale rows of the tile at K = 0
+  uint8_t *q_base = nullptr, *qs_base = nullptr;        // MXFP8 intermediate: codes and scales of row0
   uint16_t *c_base, *gu_base = nullptr;
   if constexpr (kWGrad) {
     // each XCD (workgroup b runs on XCD b % 8) takes one eighth of every
@@ -382,12 +470,22 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     const int64_t row0 = ((int64_t)__builtin_amdgcn_readfirstlane((int)(tc.row0 >> 32)) << 32) |
                          (uint32_t)__builtin_amdgcn_readfirstlane((int)tc.row0);
     rows_valid = __builtin_amdgcn_readfirstlane((int)(tc.row_end - tc.row0 < kBM ? tc.row_end - tc.row0 : kBM));
-    KT = K / kBK;
+    KT = K / kStepK;
     k_len = K;
-    a_base = reinterpret_cast<const char *>(A + row0 * K);
+    a_base = reinterpret_cast<const char *>(A) + row0 * K * kEsz;
     // replica slots (experts from e_master on) read the replica weights
-    const uint16_t *b_e = te < e_master ? B + (int64_t)te * b_expert_stride : B_rep + (int64_t)(te - e_master) * b_expert_stride;
-    b_base = reinterpret_cast<const char *>(b_e + (kBT ? n0 : 0));
+    const char *b_e = te < e_master
+                          ? reinterpret_cast<const char *>(B) + (int64_t)te * b_expert_stride * kEsz
+                          : reinterpret_cast<const char *>(B_rep) + (int64_t)(te - e_master) * b_expert_stride * kEsz;
+    b_base = b_e + (kBT ? n0 * 2 : 0);
+    if constexpr (kFp8) {
+      as_base = A_scale + row0 * (K / 32);
+      bs_base = B_scale + (int64_t)te * (b_expert_stride / 32);
+      if constexpr (kSwiGLU) {
+        q_base = reinterpret_cast<uint8_t *>(C) + row0 * ldc;
+        qs_base = C_scale + row0 * (ldc / 32);
+      }
+    }
     c_base = C + row0 * ldc;
     if (kSwiGLU && gate_up) gu_base = gate_up + row0 * 2 * N;
   }
@@ -425,7 +523,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
       const int c = (l % kChunks) ^ swz(r);
       const int ar = r < rows_valid ? r : rows_valid - 1;  // ragged tail: re-read the last row
       a_row[i] = 0;
-      a_off[i] = ((uint32_t)ar * (uint32_t)K + (uint32_t)(c * 8)) * 2u;
+      a_off[i] = (uint32_t)ar * (uint32_t)(K * kEsz) + (uint32_t)(c * 16);
     }
     if constexpr (kBT) {
       const int k = w * 16 + 2 * i + l / 32;
@@ -446,7 +544,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
         br = n0 + r < N ? n0 + r : N - 1;
       }
       b_row[i] = 0;
-      b_off[i] = ((uint32_t)br * (uint32_t)K + (uint32_t)(c * 8)) * 2u;  // < 4*I*H bytes
+      b_off[i] = (uint32_t)br * (uint32_t)(K * kEsz) + (uint32_t)(c * 16);  // < 4*I*H bytes
     }
   }
   const uint32_t ring_lds = lds_address(ring) + w * 64 * kRowBytes;  // = w * 16 * kTRowBytes
@@ -506,7 +604,109 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   // for the loads in flight).
   // (a weight-gradient tile of an expert without rows has no K step: its
   // accumulators stay zero)
-  if (KT > 0) {
+  if constexpr (kFp8) {
+    // MXFP8 K loop: 128 codes per step in two 64-wide slices.  Four ring slots:
+    // step kt's B and A tiles in slots (2kt) % 4 and (2kt) % 4 + 1.  Slice 0
+    // runs under the reads of slice 1's fragments; then every wave waits for
+    // its loads of step kt+1 and passes a barrier (no wave reads step kt's
+    // tiles any more); slice 1 runs under the reads of step kt+1's first
+    // fragments and scales and loads step kt+2's tiles into step kt's slots.
+    // The E8M0 scales come in groups of four K steps (16 bytes per tile row per
+    // operand) into two LDS buffers: group g+1 is loaded in step 4g, after its
+    // buffer's previous group was last read (in step 4g-2), and is waited for
+    // with the tiles before its first read (in step 4g+3).
+    if (KT > 0) {
+      char *sbuf = ring + kSlots8 * kOperandBytes;
+      const int sr = w * 64 + l;  // the tile row whose scales this lane fetches
+      const int sar = sr < rows_valid ? sr : rows_valid - 1;
+      int sbr;
+      if (kSwiGLU) {
+        int col = n0 + (sr & (kBN / 2 - 1));
+        if (col > N - 1) col = N - 1;
+        sbr = (sr >= kBN / 2 ? N : 0) + col;
+      } else {
+        sbr = n0 + sr < N ? n0 + sr : N - 1;
+      }
+      const uint32_t sa_off = (uint32_t)sar * (uint32_t)(K / 32), sb_off = (uint32_t)sbr * (uint32_t)(K / 32);
+      const uint32_t sbuf_lds = lds_address(sbuf) + w * 1024;
+      auto load_scales = [&](int g) {
+        const uint32_t dst = sbuf_lds + (g & 1) * kScaleGroupBytes;
+        dma16(as_base + g * 16, sa_off, dst);
+        dma16(bs_base + g * 16, sb_off, dst + kBM * 16);
+      };
+      const int r32 = l & 31, half = l >> 5;
+      // step kt's scale words of the lane's four A and four B fragment rows,
+      // shifted so that byte 2*slice is the lane's block (op_sel 0 and 2)
+      auto read_scales = [&](int kt, uint32_t (&sa)[4], uint32_t (&sb)[4]) {
+        const char *base = sbuf + ((kt >> 2) & 1) * kScaleGroupBytes + (kt & 3) * 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int brow = kSwiGLU ? ((j >> 1) * (kBN / 2) + wn * 64 + (j & 1) * 32 + r32) : (wn * 128 + j * 32 + r32);
+          sa[j] = *reinterpret_cast<const uint32_t *>(base + ((2 * j + wm) * 32 + r32) * 16) >> (8 * half);
+          sb[j] = *reinterpret_cast<const uint32_t *>(base + kBM * 16 + brow * 16) >> (8 * half);
+        }
+      };
+      i32x8 fa[2][4], fb[2][4];
+      uint32_t sa_c[4], sb_c[4], sa_n[4], sb_n[4];
+      load_scales(0);
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) load_b(0, 0, i);
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) load_a(1, 0, i);
+      if (KT > 1) {
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) load_b(2, 1, i);
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) load_a(3, 1, i);
+        wait_vmcnt<2 * kLoads>();
+      } else {
+        wait_vmcnt<0>();
+      }
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      load_frags_fp8<kSwiGLU>(ring + kOperandBytes, ring, 0, wm, wn, l, fa[0], fb[0]);
+      read_scales(0, sa_c, sb_c);
+      __builtin_amdgcn_sched_barrier(0);
+#define MOE_K_STEP8(MI)                                                                               \
+  {                                                                                                   \
+    const int sbt = (2 * kt) & 3; /* step kt's B tile; its A tile is in the next slot */              \
+    const char *bs = ring + sbt * kOperandBytes;                                                      \
+    const char *nbs = ring + (sbt ^ 2) * kOperandBytes;                                               \
+    const bool ahead = kt + 2 < KT;                                                                   \
+    const bool scales_ahead = (kt & 3) == 0 && kt + 4 < KT;                                           \
+    load_frags_fp8<kSwiGLU>(bs + kOperandBytes, bs, 1, wm, wn, l, fa[1], fb[1]);                      \
+    slice_fp8<MI, 16, 0>(fa[0], fb[0], sa_c, sb_c, acc, [&](int) {});                                 \
+    wait_vmcnt<0>();                                                                                  \
+    lds_barrier();                                                                                    \
+    __builtin_amdgcn_sched_barrier(0);                                                                \
+    /* the last step reads stale slots here; those values are not used */                           \
+    load_frags_fp8<kSwiGLU>(nbs + kOperandBytes, nbs, 0, wm, wn, l, fa[0], fb[0]);                    \
+    read_scales(kt + 1, sa_n, sb_n);                                                                  \
+    slice_fp8<MI, 24, 2>(fa[1], fb[1], sa_c, sb_c, acc, [&](int d) {                                  \
+      if (ahead) {                                                                                    \
+        load_b(sbt, kt + 2, 2 * d);                                                                   \
+        load_b(sbt, kt + 2, 2 * d + 1);                                                               \
+        load_a(sbt + 1, kt + 2, 2 * d);                                                               \
+        load_a(sbt + 1, kt + 2, 2 * d + 1);                                                           \
+      }                                                                                               \
+      if (d == 0 && scales_ahead) load_scales((kt >> 2) + 1);                                         \
+    });                                                                                               \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) {                                                   \
+      sa_c[j] = sa_n[j];                                                                              \
+      sb_c[j] = sb_n[j];                                                                              \
+    }                                                                                                 \
+  }
+      if (mi_count > 2) {
+        for (int kt = 0; kt < KT; ++kt) MOE_K_STEP8(4)
+      } else if (mi_count == 2) {
+        for (int kt = 0; kt < KT; ++kt) MOE_K_STEP8(2)
+      } else {
+        for (int kt = 0; kt < KT; ++kt) MOE_K_STEP8(1)
+      }
+#undef MOE_K_STEP8
+      wait_vmcnt<0>();  // no direct load may still be writing LDS when the wave ends
+    }
+  } else if (KT > 0) {
   bf16x8 fa[2][4], fb[2][4];
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) load_b(0, 0, i);
@@ -630,11 +830,28 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     __builtin_amdgcn_wave_barrier();
     const int ch = l % 8;
     const int col = n0 + wn * 64 + ch * 8;
+    if constexpr (kFp8) {
+      // the bf16 intermediate quantised to MXFP8 on the way out: the four lanes
+      // ch 0..3 (4..7) of a row hold one 32-feature block (N % 512 == 0, so
+      // every column exists); all lanes quantise, the rows inside the tile store
 #pragma unroll 4
-    for (int r = l / 8; r < 128; r += 8) {
-      const int row = tile_row(r);
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * 128 + pos8(r, ch) * 16);
-      if (row < rows_valid && col < N) st16(c_base + (int64_t)row * ldc + col, v);
+      for (int r = l / 8; r < 128; r += 8) {
+        const int row = tile_row(r);
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * 128 + pos8(r, ch) * 16);
+        u32x2 q;
+        const uint32_t code = mx_quad(v, q);
+        if (row < rows_valid) {
+          *reinterpret_cast<u32x2 *>(q_base + (int64_t)row * ldc + col) = q;
+          if ((ch & 3) == 0) qs_base[(int64_t)row * (ldc / 32) + col / 32] = (uint8_t)code;
+        }
+      }
+    } else {
+#pragma unroll 4
+      for (int r = l / 8; r < 128; r += 8) {
+        const int row = tile_row(r);
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * 128 + pos8(r, ch) * 16);
+        if (row < rows_valid && col < N) st16(c_base + (int64_t)row * ldc + col, v);
+      }
     }
     if (gu_base) {
       // the pre-activations too: staged columns 0..63 are gate features
@@ -724,7 +941,7 @@ hipError_t launch_plain(const uint16_t *A, const uint16_t *B, const uint16_t *B_
   if (g > INT32_MAX) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((grouped_gemm_kernel<kModePlain, false, kBT>), dim3((unsigned)g), dim3(kThreads), 0, stream, A,
                      B, b_stride, K, 0, N, 0, nt, tokens_per_expert, expert_offsets, e, C, (int64_t)N, nullptr, B_rep,
-                     nullptr, e_master);
+                     nullptr, e_master, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -736,7 +953,7 @@ hipError_t launch_wgrad(const uint16_t *A, const uint16_t *B, int M, int N, int 
   const int chunk = (mt * nt + kXcds - 1) / kXcds;
   hipLaunchKernelGGL((grouped_gemm_kernel<kModeWGrad, true, true>), dim3((unsigned)(kXcds * e * chunk)),
                      dim3(kThreads), 0, stream, A, B, (int64_t)0, 0, M, N, mt, nt, tokens_per_expert, expert_offsets,
-                     e, C, (int64_t)N, nullptr, nullptr, C_rep, e_master);
+                     e, C, (int64_t)N, nullptr, nullptr, C_rep, e_master, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -804,13 +1021,47 @@ hipError_t launch_expert_ffn(const uint16_t *x_perm, int64_t rows, int64_t hidde
   if (g1 > INT32_MAX || g2 > INT32_MAX) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((grouped_gemm_kernel<kModeSwiGLU, false, false>), dim3((unsigned)g1), dim3(kThreads), 0, stream,
                      x_perm, w_gate_up, (int64_t)2 * inter * hidden, (int)hidden, 0, inter, 0, n1, tokens_per_expert,
-                     expert_offsets, e, act, (int64_t)inter, gate_up, rep ? rep->w_gate_up : nullptr, nullptr, em);
+                     expert_offsets, e, act, (int64_t)inter, gate_up, rep ? rep->w_gate_up : nullptr, nullptr, em,
+                     nullptr, nullptr, nullptr);
   hipError_t st = hipGetLastError();
   if (st != hipSuccess) return st;
   const int n2 = (int)((hidden + kBN - 1) / kBN);
   hipLaunchKernelGGL((grouped_gemm_kernel<kModePlain, false, false>), dim3((unsigned)g2), dim3(kThreads), 0, stream,
                      act, w_down, (int64_t)hidden * inter, inter, 0, (int)hidden, 0, n2, tokens_per_expert,
-                     expert_offsets, e, y, hidden, nullptr, rep ? rep->w_down : nullptr, nullptr, em);
+                     expert_offsets, e, y, hidden, nullptr, rep ? rep->w_down : nullptr, nullptr, em, nullptr, nullptr,
+                     nullptr);
+  return hipGetLastError();
+}
+
+size_t ffn_mxfp8_workspace_bytes(int64_t rows, int inter) {
+  return align256((size_t)rows * (size_t)inter) + align256((size_t)rows * (size_t)(inter / 32));
+}
+
+hipError_t launch_expert_ffn_mxfp8(const uint8_t *x_q, const uint8_t *x_s, int64_t rows, int64_t hidden, int inter,
+                                   int e, int capacity, const int32_t *tokens_per_expert,
+                                   const int32_t *expert_offsets, const uint8_t *w_gate_up_q,
+                                   const uint8_t *w_gate_up_s, const uint8_t *w_down_q, const uint8_t *w_down_s,
+                                   uint16_t *y, void *workspace, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  // workspace: the MXFP8 intermediate, codes [rows, I] then scales [rows, I/32]
+  uint8_t *act_q = static_cast<uint8_t *>(workspace);
+  uint8_t *act_s = act_q + align256((size_t)rows * (size_t)inter);
+  const int n1 = (inter + kBN / 2 - 1) / (kBN / 2);
+  const int n2 = (int)((hidden + kBN - 1) / kBN);
+  const int64_t g1 = tile_bound(rows, e, capacity, n1);
+  const int64_t g2 = tile_bound(rows, e, capacity, n2);
+  if (g1 > INT32_MAX || g2 > INT32_MAX) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((grouped_gemm_kernel<kModeSwiGLU, false, false, true>), dim3((unsigned)g1), dim3(kThreads), 0,
+                     stream, reinterpret_cast<const uint16_t *>(x_q), reinterpret_cast<const uint16_t *>(w_gate_up_q),
+                     (int64_t)2 * inter * hidden, (int)hidden, 0, inter, 0, n1, tokens_per_expert, expert_offsets, e,
+                     reinterpret_cast<uint16_t *>(act_q), (int64_t)inter, nullptr, nullptr, nullptr, e, x_s,
+                     w_gate_up_s, act_s);
+  hipError_t st = hipGetLastError();
+  if (st != hipSuccess) return st;
+  hipLaunchKernelGGL((grouped_gemm_kernel<kModePlain, false, false, true>), dim3((unsigned)g2), dim3(kThreads), 0,
+                     stream, reinterpret_cast<const uint16_t *>(act_q), reinterpret_cast<const uint16_t *>(w_down_q),
+                     (int64_t)hidden * inter, inter, 0, (int)hidden, 0, n2, tokens_per_expert, expert_offsets, e, y,
+                     hidden, nullptr, nullptr, nullptr, e, act_s, w_down_s, nullptr);
   return hipGetLastError();
 }
 

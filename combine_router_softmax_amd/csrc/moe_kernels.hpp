@@ -41,6 +41,7 @@ hipError_t launch_combine_bwd(bool bf16, const void *grad_out, const void *y, co
 
 // ---- MXFP8 dispatch (moe_mxfp8.hip): x bf16 [n, h], h % 32 == 0; q [rows, h]
 // E4M3 codes, scale [rows, h/32] E8M0 codes; pad rows as launch_scatter.
+// assign_row null: row t of x goes to row t (k = 1), the plain quantisation.
 hipError_t launch_scatter_mxfp8(const uint16_t *x, int64_t n, int k, int64_t h, const int32_t *assign_row,
                                 uint8_t *q, uint8_t *scale, int64_t pad_rows, const int32_t *pad_limit,
                                 const int32_t *row_src, hipStream_t stream);
@@ -68,6 +69,15 @@ hipError_t launch_expert_ffn_bwd(const uint16_t *x_perm, const uint16_t *grad_y,
                                  const uint16_t *gate_up, uint16_t *grad_x_perm, uint16_t *grad_w_gate_up,
                                  uint16_t *grad_w_down, const ReplicaBases *rep, void *workspace,
                                  hipStream_t stream);
+
+// MXFP8 operands (E4M3 codes and E8M0 scales per 32 values along K; H and I
+// multiples of 512): y bf16 [rows, H]; the workspace holds the MXFP8 intermediate
+size_t ffn_mxfp8_workspace_bytes(int64_t rows, int inter);
+hipError_t launch_expert_ffn_mxfp8(const uint8_t *x_q, const uint8_t *x_s, int64_t rows, int64_t hidden, int inter,
+                                   int e, int capacity, const int32_t *tokens_per_expert,
+                                   const int32_t *expert_offsets, const uint8_t *w_gate_up_q,
+                                   const uint8_t *w_gate_up_s, const uint8_t *w_down_q, const uint8_t *w_down_s,
+                                   uint16_t *y, void *workspace, hipStream_t stream);
 
 // ---- hot-expert replication (moe_replica.hip)
 // placement: replica_of[i] = logical expert of slot i (greedy by load per copy)

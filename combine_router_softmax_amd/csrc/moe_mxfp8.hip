@@ -15,6 +15,7 @@
 // per kept copy -- about half the bytes the bf16 scatter writes.
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
+#include "moe_mx.hpp"
 
 namespace moe {
 namespace {
@@ -22,23 +23,6 @@ namespace {
 constexpr int kMxThreads = 256;
 constexpr int kMxBlock = 32;  // elements per MX block
 constexpr int kMaxPadBlocks = 2048;
-
-// E4M3 code of q (|q| < 2^10, finite).  Magnitudes below 2^-6 sit on the
-// subnormal grid of step 2^-9: a * 512 is exact and rintf rounds it to the
-// nearest integer, ties to even -- the code itself (8 = 0x08 = 2^-6 when it
-// rounds up into the normal range).  From 2^-6 up, rounding the fp32 mantissa
-// to its top 3 bits with ties to even (add 0x7FFFF plus the lowest kept bit,
-// then shift) gives exponent field and mantissa together, a carry moving into
-// the exponent; the fp32 exponent bias 127 becomes E4M3's 7 by subtracting
-// 120 << 3.  The clamp to 448 (0x7E) comes first, so no code reaches 0x7F.
-__device__ __forceinline__ uint32_t e4m3_code(float q) {
-  const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
-  const float a = fminf(fabsf(q), 448.0f);
-  const uint32_t ab = __float_as_uint(a);
-  const uint32_t normal = ((ab + 0x7FFFFu + ((ab >> 20) & 1u)) >> 20) - (120u << 3);
-  const uint32_t sub = (uint32_t)__builtin_rintf(a * 512.0f);
-  return (a < 0x1p-6f ? sub : normal) | sign;
-}
 
 // Lane l of a row pass owns 16 consecutive elements, half an MX block, read
 // as two 16-byte vectors; the two lanes of a block exchange their maxima with
@@ -99,7 +83,7 @@ __global__ __launch_bounds__(kMxThreads) void scatter_mxfp8_kernel(
     for (int j0 = 0; j0 < k; j0 += KC) {
       int32_t rows[KC];
 #pragma unroll
-      for (int j = 0; j < KC; ++j) rows[j] = j0 + j < k ? assign_row[b * k + j0 + j] : -1;
+      for (int j = 0; j < KC; ++j) rows[j] = j0 + j < k ? (assign_row ? assign_row[b * k + j0 + j] : (int32_t)b) : -1;
 #pragma unroll
       for (int j = 0; j < KC; ++j) {
         if (rows[j] < 0) continue;

@@ -11,6 +11,9 @@
  *   moe_combine     probability-weighted unpermute / combine (fp32 accumulation)
  *   moe_combine_bwd backward of moe_combine (grad of expert rows, grad of weights)
  *   moe_dispatch_bwd backward of the row scatter (grad of the token rows)
+ *   moe_mx_quantize / moe_expert_ffn_mxfp8
+ *                   MXFP8 quantisation of a matrix; the expert FFN over MXFP8
+ *                   rows and weights (scaled fp8 MFMA)
  *   moe_replica_plan / moe_replica_sync / moe_reroute / moe_expert_ffn_replicas /
  *   moe_expert_ffn_bwd_replicas / moe_replica_grad_reduce
  *                   hot-expert replication on one GPU (placement, weight sync,
@@ -76,7 +79,8 @@ typedef enum moe_op {
   MOE_OP_COMBINE = 3,
   MOE_OP_COMBINE_BWD = 4,
   MOE_OP_EXPERT_FFN_BWD = 5,
-  MOE_OP_REROUTE = 6
+  MOE_OP_REROUTE = 6,
+  MOE_OP_EXPERT_FFN_MXFP8 = 7
 } moe_op;
 
 /* Shapes and options; read on the host only, never kept. */
@@ -266,6 +270,34 @@ moe_status moe_expert_ffn_bwd(const moe_shape *s, const void *x_perm, const void
                               const moe_layout *layout, const void *w_gate_up, const void *w_down, void *grad_x_perm,
                               void *grad_w_gate_up, void *grad_w_down, void *workspace, size_t workspace_bytes,
                               void *stream);
+
+/* MXFP8 quantisation of a bf16 matrix along its rows (the format of
+ * moe_dispatch_mxfp8): x bf16 [rows, cols] (16-byte aligned, cols % 32 == 0)
+ * -> q uint8 [rows, cols] E4M3 codes (16-byte aligned), scale uint8
+ * [rows, cols/32] E8M0 codes.  The expert weights of moe_expert_ffn_mxfp8 are
+ * quantised with it along K: w_gate_up [E*2I, H] and w_down [E*H, I]. */
+moe_status moe_mx_quantize(int64_t rows, int64_t cols, const void *x, uint8_t *q, uint8_t *scale, void *stream);
+
+/* Grouped SwiGLU expert FFN over MXFP8 operands (the grouped expert GEMM with
+ * FP8 grouped experts, which the UltraEP pull request lists as a follow-up, fed
+ * by the MXFP8 dispatch; MXFP8 as in the ROCm Megatron MXFP8 recipe).  For every
+ * row r of expert e's segment, every operand value being its E4M3 code times
+ * its block's E8M0 scale:
+ *   a[r, i] = bf16( silu(x[r] . w_gate_up[e, i]) * (x[r] . w_gate_up[e, I + i]) )
+ *   a'      = MXFP8 of the row a[r] (blocks of 32 along I, as moe_mx_quantize)
+ *   y[r, c] = bf16( a'[r] . w_down[e, c] )
+ * with fp32 accumulation on the CDNA4 scaled MFMA (v_mfma_scale_f32_32x32x64_
+ * f8f6f4).  Shapes: x_perm_q [R, H] + x_perm_scale [R, H/32] (from
+ * moe_dispatch_mxfp8); w_gate_up_q [E, 2I, H] + w_gate_up_scale [E, 2I, H/32];
+ * w_down_q [E, H, I] + w_down_scale [E, H, I/32]; y bf16 [R, H].  H and I must
+ * be multiples of 512 (MOE_ERR_UNSUPPORTED otherwise); every array 16-byte
+ * aligned.  Rows outside the segments of y are not written.  Forward only.
+ * Workspace: moe_workspace_size(MOE_OP_EXPERT_FFN_MXFP8) (the MXFP8
+ * intermediate). */
+moe_status moe_expert_ffn_mxfp8(const moe_shape *s, const uint8_t *x_perm_q, const uint8_t *x_perm_scale,
+                                const moe_layout *layout, const uint8_t *w_gate_up_q, const uint8_t *w_gate_up_scale,
+                                const uint8_t *w_down_q, const uint8_t *w_down_scale, void *y, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /* Hot-expert replication, the part of one GPU (InternLM/xtuner pull request
  * "Integrate UltraEP Runtime": replicas of hot experts created from the current

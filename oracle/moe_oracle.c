@@ -386,8 +386,12 @@ static double e4m3_value(int c) {
 static uint8_t e4m3_encode(double v) {
   double a = fabs(v);
   if (a > 448.0) a = 448.0;
-  int c = 0;
-  while (c < 0x7E && e4m3_value(c + 1) <= a) ++c; /* largest code not above a */
+  int c = 0, hi = 0x7E; /* bisection for the largest code not above a */
+  while (c < hi) {
+    const int mid = (c + hi + 1) / 2;
+    if (e4m3_value(mid) <= a) c = mid;
+    else hi = mid - 1;
+  }
   if (c < 0x7E) {
     const double below = a - e4m3_value(c), above = e4m3_value(c + 1) - a;
     if (above < below || (above == below && (c & 1))) ++c;

@@ -26,7 +26,7 @@ def moe():
 
 def test_library_exports_every_declared_function(moe):
     declared = header_functions()
-    assert len(declared) == 19, declared
+    assert len(declared) == 21, declared
     assert sorted(moe.EXPORTS) == declared
     for name in declared:
         assert hasattr(moe.lib, name), name
@@ -160,6 +160,23 @@ def test_validation_errors_enqueue_nothing(moe):
                1 << 30, None) == -1                                             # replica grads alias
     assert bwr(C.byref(s), 2, p, p, None, C.byref(lay), w1, w2, w3, w4, q, r, C.c_void_p(16384), g1, w4, p,
                1 << 30, None) == -1                                             # replica grad aliases a weight
+    # MXFP8 quantisation and FFN
+    assert lib.moe_mx_quantize(4, 48, p, q, r, None) == -4                  # cols % 32
+    assert lib.moe_mx_quantize(-1, 64, p, q, r, None) == -1
+    assert lib.moe_mx_quantize(4, 64, odd, q, r, None) == -2
+    assert lib.moe_mx_quantize(4, 64, p, q, q, None) == -1                  # scales alias codes
+    assert lib.moe_mx_quantize(0, 64, None, None, None, None) == 0          # empty
+    mxf = lib.moe_expert_ffn_mxfp8
+    s = moe.make_shape(16, 512, 8, 2, inter=512)
+    b1, b2, b3, b4, b5 = (C.c_void_p(v) for v in (1 << 16, 1 << 17, 1 << 18, 1 << 19, 1 << 22))
+    assert mxf(C.byref(s), p, q, C.byref(lay), b1, b2, b3, b4, b5, p, 0, None) == -3       # no workspace
+    assert mxf(C.byref(s), p, q, C.byref(lay), b1, b2, b3, None, b5, p, 1 << 30, None) == -1
+    assert mxf(C.byref(s), p, C.c_void_p(12289), C.byref(lay), b1, b2, b3, b4, b5, p, 1 << 30, None) == -2
+    assert mxf(C.byref(s), p, q, C.byref(lay), b1, b2, b3, b4, b1, p, 1 << 30, None) == -1  # y aliases a weight
+    s_bad = moe.make_shape(16, 448, 8, 2, inter=512)                                      # H % 512
+    assert mxf(C.byref(s_bad), p, q, C.byref(lay), b1, b2, b3, b4, b5, p, 1 << 30, None) == -4
+    s_bad = moe.make_shape(16, 512, 8, 2, inter=1536 - 64)                                # I % 512
+    assert mxf(C.byref(s_bad), p, q, C.byref(lay), b1, b2, b3, b4, b5, p, 1 << 30, None) == -4
     s = moe.make_shape(16, 64, 8, 2, inter=64, act_dtype=moe.MOE_DT_F32)
     assert lib.moe_expert_ffn(C.byref(s), p, C.byref(lay), p, p, p, None, p, 1 << 30, None) == -4  # fp32 FFN
     s = moe.make_shape(16, 64, 8, 2, inter=96)

@@ -9,7 +9,7 @@ import torch
 
 import moe_inputs as mi
 import oracle
-from parity_util import assert_layout_equal, dev, host, layout_host, values, workload_inputs
+from parity_util import TOL_BF16, assert_layout_equal, dev, host, layout_host, max_rel_err, values, workload_inputs
 
 pytestmark = pytest.mark.gpu
 
@@ -147,3 +147,95 @@ def test_mx_dispatch_full_size(moe, wid):
     e = np.maximum(np.floor(np.log2(np.where(a > 0, a, 1.0))), -6)
     bound = np.where(a > 448, np.abs(v) - 448 * 2.0 ** s, 2.0 ** (s + e - 4))
     assert (np.abs(deq - v) <= bound).all()
+
+
+# ------------------------------------------------------------ MXFP8 expert FFN
+
+@pytest.mark.parametrize("rows,cols", [(1, 32), (300, 7168), (1024, 4096), (77, 544)])
+def test_mx_quantize(moe, rows, cols):
+    g = np.random.default_rng(rows + cols)
+    x = mi.f32_to_bf16_bits((g.standard_normal((rows, cols)) * np.exp(g.uniform(-10, 10, (rows, 1)))).astype(np.float32))
+    x[0, :32] = 0
+    q, s = moe.moe_mx_quantize(dev(x))
+    torch.cuda.synchronize()
+    ref_q, ref_s = oracle.mx_quantize(x)
+    np.testing.assert_array_equal(host(s), ref_s)
+    np.testing.assert_array_equal(host(q), ref_q)
+
+
+def mx_ffn_case(moe, w, n_sample, seed=0, experts=None):
+    """Route, MXFP8 dispatch and MXFP8 FFN on the GPU; the oracle on sampled rows
+    of the given experts (its own layout, dispatch and weight quantisation)."""
+    logits = mi.router_logits(w, seed)
+    x = mi.activations(w, seed)
+    wgu, wd = mi.expert_weights(w, seed)
+    e, h, inter, k = w.n_experts, w.hidden, w.inter, w.top_k
+    idx, wts, _, _ = oracle.route(logits, k)
+    q, sc, _, lay = moe.moe_dispatch_mxfp8(dev(x), dev(idx), dev(wts), e)
+    gq, gs = moe.moe_mx_quantize(dev(wgu))
+    dq, ds = moe.moe_mx_quantize(dev(wd))
+    y = moe.moe_expert_ffn_mxfp8(q, sc, lay, gq, gs, dq, ds)
+    torch.cuda.synchronize()
+    ref_lay = oracle.layout(idx, e)
+    ref_q, ref_s, _ = oracle.dispatch_mxfp8(x, k, ref_lay, wts)
+    np.testing.assert_array_equal(host(q), ref_q)
+    np.testing.assert_array_equal(host(sc), ref_s)
+    g = np.random.default_rng(seed + 1)
+    if experts is None:
+        experts = np.nonzero(ref_lay["tokens_per_expert"] > 0)[0]
+    cand = np.concatenate([np.arange(ref_lay["expert_offsets"][x_], ref_lay["expert_offsets"][x_]
+                                     + ref_lay["tokens_per_expert"][x_]) for x_ in experts])
+    rows = np.sort(g.choice(cand, min(n_sample, cand.size), replace=False))
+    # the weights of the sampled rows' experts, quantised by the oracle (checked against the GPU's)
+    rq_gu = np.zeros((e, 2 * inter, h), np.uint8); rs_gu = np.zeros((e, 2 * inter, h // 32), np.uint8)
+    rq_d = np.zeros((e, h, inter), np.uint8); rs_d = np.zeros((e, h, inter // 32), np.uint8)
+    for x_ in experts:
+        rq_gu[x_], rs_gu[x_] = oracle.mx_quantize(wgu[x_])
+        rq_d[x_], rs_d[x_] = oracle.mx_quantize(wd[x_])
+        np.testing.assert_array_equal(host(gq[x_]), rq_gu[x_])
+        np.testing.assert_array_equal(host(gs[x_]), rs_gu[x_])
+        np.testing.assert_array_equal(host(dq[x_]), rq_d[x_])
+        np.testing.assert_array_equal(host(ds[x_]), rs_d[x_])
+    ref_y, ex = oracle.expert_ffn_mxfp8_rows(rows, ref_q, ref_s, ref_lay, rq_gu, rs_gu, rq_d, rs_d)
+    assert (ex >= 0).all()
+    got = host(y)[rows]
+    err = max_rel_err(got, ref_y)
+    assert err <= TOL_BF16, err
+    return err
+
+
+def test_mx_ffn_small_ragged(moe):
+    """Several experts with ragged last tiles (2 tiles of 512 features, 2 K groups)."""
+    w = mi.workload(4, n_tokens=400, hidden=512, n_experts=8, top_k=2, inter=512)
+    mx_ffn_case(moe, w, 96)
+
+
+def test_mx_ffn_qwen3_layer_sampled(moe):
+    """The Qwen3-like layer (H=4096, I=1536): sampled rows of three experts."""
+    w = mi.workload(4)
+    mx_ffn_case(moe, w, 12, experts=[0, 57, 127])
+
+
+def test_mx_ffn_dsv3_shape_sampled(moe):
+    """H=7168, I=2048 (the DeepSeek-like expert shape): 32 experts, top-8 routing."""
+    w = mi.workload(4, n_tokens=2048, hidden=7168, n_experts=32, top_k=8, inter=2048)
+    mx_ffn_case(moe, w, 8, experts=[3, 30])
+
+
+def test_mx_ffn_empty_and_empty_experts(moe):
+    w = mi.workload(4, n_tokens=64, hidden=512, n_experts=16, top_k=1, inter=512)
+    logits = mi.router_logits(w)
+    logits[:, 8:] -= 100.0                                 # experts 8..15 receive nothing
+    x = mi.activations(w)
+    idx, wts, _, _ = oracle.route(logits, 1)
+    q, sc, _, lay = moe.moe_dispatch_mxfp8(dev(x), dev(idx), dev(wts), 16)
+    wgu, wd = mi.expert_weights(w)
+    gq, gs = moe.moe_mx_quantize(dev(wgu))
+    dq, ds = moe.moe_mx_quantize(dev(wd))
+    y = moe.moe_expert_ffn_mxfp8(q, sc, lay, gq, gs, dq, ds)
+    torch.cuda.synchronize()
+    assert np.isfinite(mi.bf16_bits_to_f32(host(y))).all()                # every row is kept (top-1, dropless)
+    q0, s0, _, lay0 = moe.moe_dispatch_mxfp8(dev(x[:0]), dev(idx[:0]), dev(wts[:0]), 16)
+    y0 = moe.moe_expert_ffn_mxfp8(q0, s0, lay0, gq, gs, dq, ds)
+    torch.cuda.synchronize()
+    assert y0.numel() == 0
