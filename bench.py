@@ -27,6 +27,7 @@ sys.path.insert(0, str(ROOT))
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 BF16_PEAK_TFLOPS = 2516.6      # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk/CU)
+FP8_PEAK_TFLOPS = 5033.2       # MI355X dense fp8 MFMA (twice the bf16 rate)
 
 
 def log(*a):
@@ -295,6 +296,31 @@ def bench_expert_gemm(moe, mi, torch, wid, iters, warmup, bwd_iters=0, replicas=
     rows = int(lay.counters[0].item())
     flops = 2.0 * rows * h * 3 * inter
     out = dict(workload=w.name, rows=rows, ms=ms, tflops=flops / ms / 1e9, flops=flops)
+    # the same FFN over MXFP8 operands: rows from the MXFP8 dispatch, weights
+    # quantised along K by moe_mx_quantize (timed too: a once-per-weight-update cost)
+    if h % 512 == 0 and inter % 512 == 0:
+        q8, s8, _, lay8 = moe.moe_dispatch_mxfp8(x, idx, wts, e, max_rows=w.rows)
+        gq, gs = moe.moe_mx_quantize(wgu)
+        dq, ds = moe.moe_mx_quantize(wd)
+        y8 = torch.empty_like(xp)
+        ws8 = torch.empty(moe.workspace_size(moe.MOE_OP_EXPERT_FFN_MXFP8, shape) + 256, dtype=torch.uint8,
+                          device=dev)
+        for _ in range(warmup):
+            moe.moe_expert_ffn_mxfp8(q8, s8, lay8, gq, gs, dq, ds, y=y8, workspace=ws8)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(iters):
+            moe.moe_expert_ffn_mxfp8(q8, s8, lay8, gq, gs, dq, ds, y=y8, workspace=ws8)
+        b.record()
+        torch.cuda.synchronize()
+        ms8 = a.elapsed_time(b) / iters
+        a.record()
+        moe.moe_mx_quantize(wgu, q=gq, scale=gs)
+        moe.moe_mx_quantize(wd, q=dq, scale=ds)
+        b.record()
+        torch.cuda.synchronize()
+        out.update(mxfp8_ms=ms8, mxfp8_tflops=flops / ms8 / 1e9, mxfp8_weight_quant_ms=a.elapsed_time(b))
+        del q8, s8, lay8, gq, gs, dq, ds, y8, ws8
     # the same FFN over force-balanced routing (random logits, moe_route_random): every
     # expert gets about rows/E rows -- the reference point the skew is measured against
     n_bal, k_bal = (w.n_tokens, w.top_k) if w.has_router else (rows // 2, 2)
@@ -569,6 +595,11 @@ def main():
                              "bwd_frac_bf16_peak": round(g["bwd_tflops"] / BF16_PEAK_TFLOPS, 4),
                              "bwd_recompute_us": round(g["bwd_recompute_ms"] * 1e3, 1),
                              "bwd_recompute_tflops": round(g["bwd_recompute_tflops"], 1)} if "bwd_ms" in g else {}),
+                         **({"mxfp8_us": round(g["mxfp8_ms"] * 1e3, 1), "mxfp8_tflops": round(g["mxfp8_tflops"], 1),
+                             "mxfp8_frac_fp8_peak": round(g["mxfp8_tflops"] / FP8_PEAK_TFLOPS, 4),
+                             "mxfp8_speedup_vs_bf16": round(g["ms"] / g["mxfp8_ms"], 3),
+                             "mxfp8_weight_quant_us": round(g["mxfp8_weight_quant_ms"] * 1e3, 1)}
+                            if "mxfp8_ms" in g else {}),
                          **({"replication": {k_: (round(v, 2) if isinstance(v, float) else v)
                                              for k_, v in g["replication"].items()}} if "replication" in g else {})}
                         for g in gemm],
