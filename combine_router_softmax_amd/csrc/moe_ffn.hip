@@ -610,7 +610,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     // runs under the reads of slice 1's fragments; then every wave waits for
     // its loads of step kt+1 and passes a barrier (no wave reads step kt's
     // tiles any more); slice 1 runs under the reads of step kt+1's first
-    // fragments and scales and loads step kt+2's tiles into step kt's slots.
+    // fragments and scales and loads step kt+2's tiles into step kt's slots,
+    // all sixteen load instructions at its start (measured 2-4 % faster than
+    // spreading them over the slice: with four slots a tile is requested only
+    // about one step before use, so every cycle of lead counts).
     // The E8M0 scales come in groups of four K steps (16 bytes per tile row per
     // operand) into two LDS buffers: group g+1 is loaded in step 4g, after its
     // buffer's previous group was last read (in step 4g-2), and is waited for
@@ -683,11 +686,9 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     load_frags_fp8<kSwiGLU>(nbs + kOperandBytes, nbs, 0, wm, wn, l, fa[0], fb[0]);                    \
     read_scales(kt + 1, sa_n, sb_n);                                                                  \
     slice_fp8<MI, 24, 2>(fa[1], fb[1], sa_c, sb_c, acc, [&](int d) {                                  \
-      if (ahead) {                                                                                    \
-        load_b(sbt, kt + 2, 2 * d);                                                                   \
-        load_b(sbt, kt + 2, 2 * d + 1);                                                               \
-        load_a(sbt + 1, kt + 2, 2 * d);                                                               \
-        load_a(sbt + 1, kt + 2, 2 * d + 1);                                                           \
+      if (ahead && d == 0) { /* all at the first slot: the four-slot ring prefetches only a step */     \
+        _Pragma("unroll") for (int q = 0; q < kLoads; ++q) load_b(sbt, kt + 2, q);                    \
+        _Pragma("unroll") for (int q = 0; q < kLoads; ++q) load_a(sbt + 1, kt + 2, q);                \
       }                                                                                               \
       if (d == 0 && scales_ahead) load_scales((kt >> 2) + 1);                                         \
     });                                                                                               \
