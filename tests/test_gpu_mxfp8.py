@@ -163,21 +163,23 @@ def test_mx_quantize(moe, rows, cols):
     np.testing.assert_array_equal(host(q), ref_q)
 
 
-def mx_ffn_case(moe, w, n_sample, seed=0, experts=None):
+def mx_ffn_case(moe, w, n_sample, seed=0, experts=None, capacity=0, row_align=0, logits=None):
     """Route, MXFP8 dispatch and MXFP8 FFN on the GPU; the oracle on sampled rows
     of the given experts (its own layout, dispatch and weight quantisation)."""
-    logits = mi.router_logits(w, seed)
+    if logits is None:
+        logits = mi.router_logits(w, seed)
     x = mi.activations(w, seed)
     wgu, wd = mi.expert_weights(w, seed)
     e, h, inter, k = w.n_experts, w.hidden, w.inter, w.top_k
     idx, wts, _, _ = oracle.route(logits, k)
-    q, sc, _, lay = moe.moe_dispatch_mxfp8(dev(x), dev(idx), dev(wts), e)
+    q, sc, _, lay = moe.moe_dispatch_mxfp8(dev(x), dev(idx), dev(wts), e, capacity=capacity, row_align=row_align)
     gq, gs = moe.moe_mx_quantize(dev(wgu))
     dq, ds = moe.moe_mx_quantize(dev(wd))
     y = moe.moe_expert_ffn_mxfp8(q, sc, lay, gq, gs, dq, ds)
     torch.cuda.synchronize()
-    ref_lay = oracle.layout(idx, e)
-    ref_q, ref_s, _ = oracle.dispatch_mxfp8(x, k, ref_lay, wts)
+    ref_lay = oracle.layout(idx, e, capacity, 0, row_align)
+    # rows of an unused dropless tail are not written: the oracle keeps what the GPU left there
+    ref_q, ref_s, _ = oracle.dispatch_mxfp8(x, k, ref_lay, wts, x_perm_q=host(q).copy(), x_perm_scale=host(sc).copy())
     np.testing.assert_array_equal(host(q), ref_q)
     np.testing.assert_array_equal(host(sc), ref_s)
     g = np.random.default_rng(seed + 1)
@@ -220,6 +222,22 @@ def test_mx_ffn_dsv3_shape_sampled(moe):
     """H=7168, I=2048 (the DeepSeek-like expert shape): 32 experts, top-8 routing."""
     w = mi.workload(4, n_tokens=2048, hidden=7168, n_experts=32, top_k=8, inter=2048)
     mx_ffn_case(moe, w, 8, experts=[3, 30])
+
+
+@pytest.mark.parametrize("capacity,row_align", [(96, 0), (128, 32), (0, 32), (0, 256)])
+def test_mx_ffn_capacity_and_aligned_segments(moe, capacity, row_align):
+    """Capacity segments with zero pad rows, and alignment-padded dropless
+    segments (the FP8 padding of the routing maps): the pads are all-zero MXFP8
+    rows and the FFN computes the kept rows only."""
+    w = mi.workload(4, n_tokens=512, hidden=512, n_experts=8, top_k=2, inter=512)
+    logits = mi.router_logits(w) + np.log(np.arange(1, 9) ** -1.0).astype(np.float32)  # uneven loads
+    mx_ffn_case(moe, w, 64, capacity=capacity, row_align=row_align, logits=logits.astype(np.float32))
+
+
+def test_mx_ffn_many_experts(moe):
+    """1024 experts with a few rows each (most m-tiles ragged, many experts empty)."""
+    w = mi.workload(4, n_tokens=600, hidden=512, n_experts=1024, top_k=4, inter=512)
+    mx_ffn_case(moe, w, 24, experts=[0, 511, 1023])
 
 
 def test_mx_ffn_empty_and_empty_experts(moe):
