@@ -556,6 +556,6 @@ const char *moe_status_string(moe_status st) {
   return "unknown status";
 }
 
-const char *moe_version(void) { return "0.1.0"; }
+const char *moe_version(void) { return "0.2.0"; }
 
 }  // extern "C"
