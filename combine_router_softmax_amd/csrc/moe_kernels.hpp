@@ -15,7 +15,7 @@ hipError_t launch_route(const float *logits, uint64_t seed, const float *expert_
                         int32_t *tokens_per_expert, hipStream_t stream);
 
 // ---- layout (moe_layout.hip)
-constexpr int kLayoutTile = 2048;  // assignments per layout tile
+constexpr int kLayoutTile = 512;  // assignments per layout tile
 inline int64_t layout_tiles(int64_t assignments) { return (assignments + kLayoutTile - 1) / kLayoutTile; }
 size_t layout_workspace_bytes(int64_t assignments, int e, bool drop_by_weight);
 // drop_by_weight (with a capacity): keep each expert's `capacity` largest weights
