@@ -505,7 +505,7 @@ def main():
         counter_pass()
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (the expert-parallel all-to-all is out "
+        print("bench.py measures one GPU: the library has no multi-GPU path (the expert-parallel all-to-all is out "
               "of scope); run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
