@@ -204,3 +204,41 @@ def test_validation_errors_enqueue_nothing(moe):
     assert lib.moe_dispatch_bwd(C.byref(s), odd, C.byref(lay), p, None) == -2
     assert lib.moe_dispatch_bwd(C.byref(s), p, None, C.c_void_p(8192), None) == -1   # no layout
     assert lib.moe_combine_bwd(C.byref(s), p, p, p, C.byref(lay), p, p, None) == -1  # grad_y aliases
+
+
+C_PROGRAM = r"""
+#include "moe.h"
+#include <stdio.h>
+int main(void) {
+  moe_shape s = {4096, 7168, 256, 8, 0, 0, 0, MOE_DT_BF16, 0, MOE_DROP_POSITION, 0};
+  size_t b = 0;
+  moe_status st = moe_workspace_size(MOE_OP_DISPATCH, &s, &b);
+  s.capacity = 160;
+  printf("%s %s %lld %lld %d\n", moe_version(), moe_status_string(st), (long long)moe_layout_rows(&s),
+         (long long)(b > 0), (int)moe_dispatch(&s, 0, 0, 0, 0, 0, 0, 0, 0, 0));
+  return st == MOE_OK ? 0 : 1;
+}
+"""
+
+
+def test_header_is_plain_c_and_links(tmp_path, moe):
+    """include/moe.h compiles as pedantic C99 with warnings as errors, and a C
+    program links against the library and calls its host-side functions."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    src = tmp_path / "t.c"
+    src.write_text(C_PROGRAM)
+    libdir = str(Path(moe.library_path).parent)
+    exe = tmp_path / "t"
+    r = subprocess.run([gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", str(ROOT / "include"),
+                        str(src), "-L", libdir, "-lmoe_mi355x", f"-Wl,-rpath,{libdir}", "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    out = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert out.returncode == 0, out.stderr
+    version, status, rows, has_ws, null_layout = out.stdout.split()
+    assert version == moe.lib.moe_version().decode() and status == "ok"
+    assert int(rows) == 256 * 160 and has_ws == "1" and int(null_layout) == -1   # null layout: invalid argument

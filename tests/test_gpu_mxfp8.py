@@ -1,6 +1,8 @@
-"""GPU parity of moe_dispatch_mxfp8 against the CPU oracle, through the C ABI.
-Bit-exact: every layout array, every E4M3 code byte and E8M0 scale byte of the
-permuted rows, the permuted weights, and the zeroed pad rows."""
+"""GPU parity of the MXFP8 calls against the CPU oracle, through the C ABI.
+moe_dispatch_mxfp8 and moe_mx_quantize bit-exact (every layout array, every
+E4M3 code byte and E8M0 scale byte, the permuted weights, the zeroed pad rows);
+moe_expert_ffn_mxfp8 within the bf16 tolerance on sampled rows; graph replay of
+the MXFP8 and the replicated layer steps bit for bit."""
 from __future__ import annotations
 
 import numpy as np
@@ -257,3 +259,74 @@ def test_mx_ffn_empty_and_empty_experts(moe):
     y0 = moe.moe_expert_ffn_mxfp8(q0, s0, lay0, gq, gs, dq, ds)
     torch.cuda.synchronize()
     assert y0.numel() == 0
+
+
+def test_mxfp8_and_replicated_steps_replay_in_a_hip_graph(moe):
+    """route -> MXFP8 dispatch -> MXFP8 FFN -> combine, and route -> replica plan
+    -> weight sync -> reroute -> dispatch -> FFN with replica slots -> combine,
+    each captured once in a HIP graph and replayed three times with other work in
+    between: every replay equals the eager step bit for bit (the new entry points
+    launch kernels only)."""
+    n, e, k, h, inter, r_ = 512, 16, 4, 512, 512, 3
+    w = mi.workload(4, n_tokens=n, hidden=h, n_experts=e, top_k=k, inter=inter)
+    logits = dev((mi.router_logits(w) + np.log(np.arange(1, e + 1) ** -1.5).astype(np.float32) * 3).astype(np.float32))
+    x = dev(mi.activations(w))
+    wgu, wd = (dev(a) for a in mi.expert_weights(w))
+    gq, gs = moe.moe_mx_quantize(wgu)
+    dq, ds = moe.moe_mx_quantize(wd)
+    rt = moe.moe_route(logits, k)
+    q8, s8, _, lay8 = moe.moe_dispatch_mxfp8(x, rt.topk_idx, rt.topk_w, e)
+    y8 = torch.empty((lay8.rows, h), dtype=torch.bfloat16, device="cuda")
+    out8 = torch.empty_like(x)
+    rep = moe.moe_replica_plan(rt.tokens_per_expert, r_)
+    wgu_r, wd_r = moe.moe_replica_sync(wgu, wd, rep)
+    phys = moe.moe_reroute(rt.topk_idx, e, rep)
+    xp, wp, lay = moe.moe_dispatch(x, phys, rt.topk_w, e + r_)
+    y = torch.empty_like(xp)
+    out = torch.empty_like(x)
+    ws_d = torch.empty(moe.workspace_size(moe.MOE_OP_DISPATCH, moe.make_shape(n, h, e + r_, k)) + 256,
+                       dtype=torch.uint8, device="cuda")
+    ws_8 = torch.empty(moe.workspace_size(moe.MOE_OP_EXPERT_FFN_MXFP8, lay8.shape(h, moe.MOE_DT_BF16, inter)) + 256,
+                       dtype=torch.uint8, device="cuda")
+    ws_f = torch.empty(moe.workspace_size(moe.MOE_OP_EXPERT_FFN, lay.shape(h, moe.MOE_DT_BF16, inter)) + 256,
+                       dtype=torch.uint8, device="cuda")
+    ws_r = torch.empty(moe.workspace_size(moe.MOE_OP_REROUTE, moe.make_shape(n, 1, e, k)) + 256, dtype=torch.uint8,
+                       device="cuda")
+
+    def step():
+        moe.moe_route(logits, k, out=rt)
+        moe.moe_dispatch_mxfp8(x, rt.topk_idx, rt.topk_w, e, layout=lay8, x_perm_q=q8, x_perm_scale=s8,
+                               w_perm=False, workspace=ws_d)
+        moe.moe_expert_ffn_mxfp8(q8, s8, lay8, gq, gs, dq, ds, y=y8, workspace=ws_8)
+        moe.moe_combine(y8, rt.topk_w, lay8, out=out8)
+        moe.moe_replica_plan(rt.tokens_per_expert, r_, out=rep)
+        moe.moe_replica_sync(wgu, wd, rep, w_gate_up_replica=wgu_r, w_down_replica=wd_r)
+        moe.moe_reroute(rt.topk_idx, e, rep, out=phys, workspace=ws_r)
+        moe.moe_dispatch(x, phys, rt.topk_w, e + r_, layout=lay, x_perm=xp, w_perm_out=wp, workspace=ws_d)
+        moe.moe_expert_ffn_replicas(xp, lay, wgu, wd, wgu_r, wd_r, y=y, workspace=ws_f)
+        moe.moe_combine(y, rt.topk_w, lay, out=out)
+
+    step()
+    torch.cuda.synchronize()
+    ref8, ref, ref_phys = out8.clone(), out.clone(), phys.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for _ in range(3):
+        out8.fill_(7.0)
+        out.fill_(7.0)
+        phys.fill_(-5)
+        q8.fill_(0)
+        torch.randn(1 << 20, device="cuda").sum()           # other work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out8, ref8) and torch.equal(out, ref) and torch.equal(phys, ref_phys)
+    del g
