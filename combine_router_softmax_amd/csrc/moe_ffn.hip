@@ -500,7 +500,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   const int mi_count = blocks_valid > wm ? (blocks_valid - wm + 1) / 2 : 0;
 
   // direct-load sources: a K-contiguous tile's row r (an output row or column)
-  // holds K values 64*kt .. +63 in 128 bytes; this wave fills rows w*64 ..
+  // holds K step kt in 128 bytes (64 bf16 or 128 E4M3 values); this wave fills rows w*64 ..
   // w*64+63, kLoadRows rows per instruction; lane l writes LDS bytes
   // l*16..l*16+15 of the instruction's 1 KiB, i.e. row l / kChunks, position
   // l % kChunks, so it fetches global chunk position ^ swz(row).  A K-major
