@@ -482,8 +482,8 @@ def cpu_baseline(mi):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--gemm-iters", type=int, default=10)
     ap.add_argument("--skip-gemm", action="store_true")
     ap.add_argument("--bwd-iters", type=int, default=5, help="expert FFN backward iterations (0: skip)")
