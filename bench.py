@@ -66,31 +66,50 @@ def bench_dispatch_combine(moe, mi, torch, steps, warmup):
     gy = torch.empty_like(xp)
     gw = torch.empty((n, k), dtype=torch.float32, device=dev)
 
-    def step(rec=None):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if rec is not None else None
-        if ev: ev[0].record()
-        moe.moe_route(logits, k, out=r)
-        if ev: ev[1].record()
-        moe.moe_dispatch(x, r.topk_idx, r.topk_w, e, layout=lay, x_perm=xp, w_perm_out=wp, workspace=ws)
-        if ev: ev[2].record()
-        moe.moe_combine(xp, r.topk_w, lay, out=out)
-        if ev: ev[3].record(); rec.append(ev)
+    route = lambda: moe.moe_route(logits, k, out=r)
+    dispatch = lambda: moe.moe_dispatch(x, r.topk_idx, r.topk_w, e, layout=lay, x_perm=xp, w_perm_out=wp,
+                                        workspace=ws)
+    combine = lambda: moe.moe_combine(xp, r.topk_w, lay, out=out)
 
+    def step():
+        route()
+        dispatch()
+        combine()
+
+    # The timed steps carry no event markers between the calls: a recorded event
+    # costs the stream several microseconds of idle time (measured 8.6 us for an
+    # empty pair), so per-call times come from runs of back-to-back calls below.
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    recs = []
     t0.record()
     for _ in range(steps):
-        step(recs)
+        step()
     t1.record()
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
-    route_ms = median([r_[0].elapsed_time(r_[1]) for r_ in recs])
-    disp_ms = median([r_[1].elapsed_time(r_[2]) for r_ in recs])
-    comb_ms = median([r_[2].elapsed_time(r_[3]) for r_ in recs])
+
+    def b2b_ms(fns, n):
+        """Mean time of n rounds of the calls fns, back to back on the stream."""
+        for _ in range(warmup):
+            for f in fns: f()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(n):
+            for f in fns: f()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / n
+
+    route_ms = b2b_ms([route], steps)
+    disp_ms = b2b_ms([dispatch], steps)
+    comb_ms = b2b_ms([combine], steps)
+    # dispatch then combine, in batches (one event pair per batch) for the spread
+    batch = max(1, steps // 10)
+    dc_batches = [b2b_ms([dispatch, combine], batch) for _ in range(10)]
+    dc_ms = median(dc_batches)
     # the same step captured once in a HIP graph and replayed (no launch overhead on the host)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
@@ -161,15 +180,8 @@ def bench_dispatch_combine(moe, mi, torch, steps, warmup):
     torch.cuda.synchronize()
     mx_ms = d0.elapsed_time(d1) / steps
     mx_bytes = n * row_b + kept * (h + h // 32)
-    # the roofline kernel alone: back-to-back combine launches on the stream
     c0 = torch.cuda.Event(enable_timing=True)
     c1 = torch.cuda.Event(enable_timing=True)
-    c0.record()
-    for _ in range(steps):
-        moe.moe_combine(xp, r.topk_w, lay, out=out)
-    c1.record()
-    torch.cuda.synchronize()
-    comb_kernel_ms = c0.elapsed_time(c1) / steps
     # the force-balanced router (random logits drawn on the device) at the same shape
     rr = moe.moe_route_random(n, e, k, 7, device=dev)
     for _ in range(warmup):
@@ -186,16 +198,31 @@ def bench_dispatch_combine(moe, mi, torch, steps, warmup):
     # a read leaves clean lines, so no write-back of the flush lands in the step)
     flush = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
-    cold = []
-    for i in range(min(steps, 20)):
-        flush.sum()
-        torch.cuda.synchronize()
-        step(cold)
-        torch.cuda.synchronize()
+    # cold dispatch + combine: one event pair around the two calls; the split
+    # between them comes from a second pass with a marker in between
+    def cold_pass(split):
+        res = []
+        for _ in range(min(steps, 20)):
+            flush.sum()
+            torch.cuda.synchronize()
+            ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+            ev[0].record()
+            route()
+            ev[1].record()
+            dispatch()
+            if split:
+                ev[2].record()
+            combine()
+            ev[3].record()
+            torch.cuda.synchronize()
+            res.append(ev)
+        return res
+    cold = cold_pass(False)
     cold_route = [r_[0].elapsed_time(r_[1]) for r_ in cold]
+    cold_dc = [r_[1].elapsed_time(r_[3]) for r_ in cold]
+    cold = cold_pass(True)
     cold_disp = [r_[1].elapsed_time(r_[2]) for r_ in cold]
     cold_comb = [r_[2].elapsed_time(r_[3]) for r_ in cold]
-    cold_dc = [r_[1].elapsed_time(r_[3]) for r_ in cold]
     # a plain device copy of 1 GiB (2.15 GB moved) for the measured-bandwidth fraction
     dst = torch.empty_like(flush)
     dst.copy_(flush)
@@ -210,10 +237,9 @@ def bench_dispatch_combine(moe, mi, torch, steps, warmup):
     copy_gbs = 2 * flush.numel() * 4 / (k0.elapsed_time(k1) / 5 * 1e-3) / 1e9
     del flush, dst
     return dict(total_ms=total_ms, route_ms=route_ms, dispatch_ms=disp_ms, combine_ms=comb_ms,
-                comb_kernel_ms=comb_kernel_ms, kept=kept, copy_gbs=copy_gbs, dbwd_ms=dbwd_ms,
+                comb_kernel_ms=comb_ms, kept=kept, copy_gbs=copy_gbs, dbwd_ms=dbwd_ms,
                 route_random_ms=route_random_ms, graph_ms=graph_ms,
-                dc_p10=pct([r_[1].elapsed_time(r_[3]) for r_ in recs], 10),
-                dc_p90=pct([r_[1].elapsed_time(r_[3]) for r_ in recs], 90),
+                dc_ms=dc_ms, dc_p10=pct(dc_batches, 10), dc_p90=pct(dc_batches, 90),
                 cold_route_ms=median(cold_route), cold_dispatch_ms=median(cold_disp),
                 cold_combine_ms=median(cold_comb), cold_dc_ms=median(cold_dc),
                 cold_dc_p10=pct(cold_dc, 10), cold_dc_p90=pct(cold_dc, 90),
@@ -421,8 +447,9 @@ def recorded_traffic(kernel: str):
 
 
 def counter_pass():
-    """Short run for rocprofv3 counter passes: three uniform-workload steps, then one
-    1 GiB device-to-device copy as the calibration kernel of known size."""
+    """Short run for rocprofv3 counter passes: the uniform-workload loops with three
+    timed calls each, then one 1 GiB device-to-device copy as the calibration
+    kernel of known size."""
     import torch
     import moe_inputs as mi
     import combine_router_softmax_amd as moe
@@ -553,9 +580,12 @@ def main():
         "route_us": round(dc["route_ms"] * 1e3, 2),
         "dispatch_us": round(dc["dispatch_ms"] * 1e3, 2),
         "combine_us": round(dc["combine_ms"] * 1e3, 2),
-        "dispatch_combine_us": round((dc["dispatch_ms"] + dc["combine_ms"]) * 1e3, 2),
-        "dispatch_combine_gbs": round(byts / ((dc["dispatch_ms"] + dc["combine_ms"]) * 1e-3) / 1e9, 2),
+        "dispatch_combine_us": round(dc["dc_ms"] * 1e3, 2),
+        "dispatch_combine_gbs": round(byts / (dc["dc_ms"] * 1e-3) / 1e9, 2),
+        "dispatch_combine_frac_hbm_peak": round(byts / (dc["dc_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "dispatch_combine_p10_p90_us": [round(dc["dc_p10"] * 1e3, 2), round(dc["dc_p90"] * 1e3, 2)],
+        "timing": "route/dispatch/combine_us: means of back-to-back calls of each; dispatch_combine_us: median "
+                  "of 10 batches of dispatch->combine pairs, one event pair per batch",
         "cold": {"route_us": round(dc["cold_route_ms"] * 1e3, 2),
                  "dispatch_us": round(dc["cold_dispatch_ms"] * 1e3, 2),
                  "combine_us": round(dc["cold_combine_ms"] * 1e3, 2),
@@ -564,10 +594,10 @@ def main():
                                                  round(dc["cold_dc_p90"] * 1e3, 2)],
                  "dispatch_combine_gbs": round(byts / (dc["cold_dc_ms"] * 1e-3) / 1e9, 2),
                  "frac_hbm_peak": round(byts / (dc["cold_dc_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                 "note": "median of 20 steps, each after a 1 GiB read that evicts L2 and MALL"},
+                 "note": "median of 20 steps, each after a 1 GiB read that evicts L2 and MALL; the split "
+                         "from 20 more with an event between the two calls"},
         "copy_gbs": round(dc["copy_gbs"], 1),
-        "dispatch_combine_frac_of_copy": round(byts / ((dc["dispatch_ms"] + dc["combine_ms"]) * 1e-3) / 1e9
-                                               / dc["copy_gbs"], 4),
+        "dispatch_combine_frac_of_copy": round(byts / (dc["dc_ms"] * 1e-3) / 1e9 / dc["copy_gbs"], 4),
         "graph_step_us": round(dc["graph_ms"] * 1e3, 2),
         "graph_step_gbs": round(byts / (dc["graph_ms"] * 1e-3) / 1e9, 2),
         "route_force_balanced_us": round(dc["route_random_ms"] * 1e3, 2),
