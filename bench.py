@@ -484,6 +484,74 @@ def bwd_pass():
     torch.cuda.synchronize()
 
 
+def power_pass():
+    """Five-second phases for reading board power and shader clock from outside
+    (rocm-smi / amd-smi sampled by the caller): idle, the bf16 expert FFN, the
+    vendor library's batched GEMM on the uniform version of its gate/up GEMM
+    (128 x [512 x 4096] x [4096 x 3072]), the MXFP8 expert FFN, and the
+    uniform-workload combine.  Prints one PHASE line per phase with its wall-clock
+    start and end (seconds since the epoch) and its time per call."""
+    import numpy as np
+    import torch
+    import moe_inputs as mi
+    import combine_router_softmax_amd as moe
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda")
+    w = mi.workload(4)
+    g = torch.Generator(device=dev).manual_seed(5)
+    e, h, inter = w.n_experts, w.hidden, w.inter
+    wgu = (torch.randn((e, 2 * inter, h), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    wd = (torch.randn((e, h, inter), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    x = torch.randn((w.n_tokens, h), generator=g, device=dev).to(torch.bfloat16)
+    r = moe.moe_route(torch.from_numpy(mi.router_logits(w)).cuda(), w.top_k)
+    xp, _, lay = moe.moe_dispatch(x, r.topk_idx, r.topk_w, e, max_rows=w.rows)
+    y = torch.empty_like(xp)
+    shape = lay.shape(h, moe.MOE_DT_BF16, inter)
+    ws = torch.empty(moe.workspace_size(moe.MOE_OP_EXPERT_FFN, shape) + 256, dtype=torch.uint8, device=dev)
+    q8, s8, _, lay8 = moe.moe_dispatch_mxfp8(x, r.topk_idx, r.topk_w, e, max_rows=w.rows)
+    gq, gs = moe.moe_mx_quantize(wgu)
+    dq, ds = moe.moe_mx_quantize(wd)
+    ws8 = torch.empty(moe.workspace_size(moe.MOE_OP_EXPERT_FFN_MXFP8, shape) + 256, dtype=torch.uint8, device=dev)
+    xa = torch.randn((e, 512, h), generator=g, device=dev).to(torch.bfloat16)
+    wb = wgu.transpose(1, 2).contiguous()  # contiguous right operand for torch.bmm
+    yb = torch.empty((e, 512, 2 * inter), dtype=torch.bfloat16, device=dev)
+    w2 = mi.workload(2)
+    x2 = torch.from_numpy(mi.activations(w2).view(np.int16)).cuda().view(torch.bfloat16)
+    r2 = moe.moe_route(torch.from_numpy(mi.router_logits(w2)).cuda(), w2.top_k)
+    xp2, _, lay2 = moe.moe_dispatch(x2, r2.topk_idx, r2.topk_w, w2.n_experts)
+    out2 = torch.empty_like(x2)
+    rows = int(lay.counters[0].item())
+    ffn_flops = 2.0 * rows * h * 3 * inter
+
+    def phase(name, fn, secs, flops=None):
+        torch.cuda.synchronize()
+        t0 = time.time()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        n = 0
+        a.record()
+        while time.time() - t0 < secs:
+            for _ in range(4):
+                fn()
+            n += 4
+            torch.cuda.synchronize()
+        b.record()
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) / n * 1e3
+        rate = f" {flops / us / 1e6:.0f} TFLOP/s" if flops else ""
+        print(f"PHASE {name} {t0:.3f} {time.time():.3f} calls {n} {us:.1f} us/call{rate}", flush=True)
+        time.sleep(2)
+
+    torch.cuda.synchronize()
+    t = time.time()
+    time.sleep(2)
+    print(f"PHASE idle {t:.3f} {time.time():.3f}", flush=True)
+    phase("expert_ffn_bf16", lambda: moe.moe_expert_ffn(xp, lay, wgu, wd, y=y, workspace=ws), 5, ffn_flops)
+    phase("vendor_bmm_gate_up", lambda: torch.bmm(xa, wb, out=yb), 5, 2.0 * e * 512 * h * 2 * inter)
+    phase("expert_ffn_mxfp8", lambda: moe.moe_expert_ffn_mxfp8(q8, s8, lay8, gq, gs, dq, ds, y=y, workspace=ws8), 5,
+          ffn_flops)
+    phase("combine_uniform", lambda: moe.moe_combine(xp2, r2.topk_w, lay2, out=out2), 5)
+
+
 def cpu_baseline(mi):
     import numpy as np
     import oracle
@@ -521,7 +589,12 @@ def main():
                     help="short expert-GEMM run for hardware-counter passes (prints nothing)")
     ap.add_argument("--bwd-pass", action="store_true",
                     help="short expert-FFN backward run for hardware-counter passes (prints nothing)")
+    ap.add_argument("--power-pass", action="store_true",
+                    help="five-second phases for sampling board power and clock from outside (PHASE lines)")
     args = ap.parse_args()
+    if args.power_pass:
+        power_pass()
+        return
     if args.gemm_pass:
         gemm_pass()
         return
