@@ -552,26 +552,36 @@ def power_pass():
     phase("combine_uniform", lambda: moe.moe_combine(xp2, r2.topk_w, lay2, out=out2), 5)
 
 
-def cpu_baseline(mi):
-    import numpy as np
+def cpu_baseline(mi, min_seconds=10.0):
+    """The oracle on the host, single thread: full uniform-workload steps (route,
+    layout, scatter, combine) repeated until at least min_seconds have passed."""
     import oracle
     w = mi.workload(2)
     logits = mi.router_logits(w)
     x = mi.activations(w)
-    t0 = time.perf_counter()
-    idx, wts, _, _ = oracle.route(logits, w.top_k)
-    t1 = time.perf_counter()
-    lay = oracle.layout(idx, w.n_experts)
-    xp, _ = oracle.scatter(x, w.top_k, lay, wts)
-    t2 = time.perf_counter()
-    oracle.combine(xp, wts, lay, w.n_tokens, w.top_k)
-    t3 = time.perf_counter()
-    kept = int(lay["counters"][0])
+    parts = [0.0, 0.0, 0.0]
+    steps = 0
+    kept = 0
+    start = time.perf_counter()
+    while steps == 0 or time.perf_counter() - start < min_seconds:
+        t0 = time.perf_counter()
+        idx, wts, _, _ = oracle.route(logits, w.top_k)
+        t1 = time.perf_counter()
+        lay = oracle.layout(idx, w.n_experts)
+        xp, _ = oracle.scatter(x, w.top_k, lay, wts)
+        t2 = time.perf_counter()
+        oracle.combine(xp, wts, lay, w.n_tokens, w.top_k)
+        t3 = time.perf_counter()
+        parts = [parts[0] + t1 - t0, parts[1] + t2 - t1, parts[2] + t3 - t2]
+        kept = int(lay["counters"][0])
+        steps += 1
     row_b = w.hidden * 2
     byts = (w.n_tokens + kept) * row_b * 2
-    return dict(value=byts / (t3 - t0) / 1e9, unit="GB/s", cores=1, kind="oracle",
-                sample=f"one full step (route+layout+scatter+combine) of the uniform workload, single thread: "
-                       f"route {1e3*(t1-t0):.0f} ms, dispatch {1e3*(t2-t1):.0f} ms, combine {1e3*(t3-t2):.0f} ms")
+    per_step = sum(parts) / steps
+    return dict(value=byts / per_step / 1e9, unit="GB/s", cores=1, kind="oracle",
+                sample=f"{steps} full steps (route+layout+scatter+combine) of the uniform workload, single thread, "
+                       f"{sum(parts):.1f} s in all; per step: route {1e3 * parts[0] / steps:.0f} ms, "
+                       f"dispatch {1e3 * parts[1] / steps:.0f} ms, combine {1e3 * parts[2] / steps:.0f} ms")
 
 
 def main():
