@@ -236,7 +236,26 @@ def bench_dispatch_combine(moe, mi, torch, steps, warmup):
     torch.cuda.synchronize()
     copy_gbs = 2 * flush.numel() * 4 / (k0.elapsed_time(k1) / 5 * 1e-3) / 1e9
     del flush, dst
+    # router and layout options at the same shape, back to back: a selection-only
+    # expert bias, a padding-token mask (every tenth token), and dropless segments
+    # aligned to 128 rows (the zeroed pad rows between segments are written too)
+    g = torch.Generator(device=dev).manual_seed(11)
+    bias = torch.randn(e, generator=g, device=dev) * 0.1
+    rb = moe.moe_route(logits, k, expert_bias=bias)
+    mask = (torch.arange(n, device=dev) % 10 == 0).to(torch.uint8)
+    rm = moe.moe_route(logits, k, token_mask=mask)
+    route_bias_ms = b2b_ms([lambda: moe.moe_route(logits, k, expert_bias=bias, out=rb)], steps)
+    route_mask_ms = b2b_ms([lambda: moe.moe_route(logits, k, token_mask=mask, out=rm)], steps)
+    xpa, wpa, laya = moe.moe_dispatch(x, r.topk_idx, r.topk_w, e, row_align=128)
+    shape_a = laya.shape(h, moe.MOE_DT_BF16)
+    ws_a = torch.empty(moe.workspace_size(moe.MOE_OP_DISPATCH, shape_a) + 256, dtype=torch.uint8, device=dev)
+    aligned_ms = b2b_ms([lambda: moe.moe_dispatch(x, r.topk_idx, r.topk_w, e, row_align=128, layout=laya, x_perm=xpa,
+                                                  w_perm_out=wpa, workspace=ws_a)], steps)
+    aligned_rows = int(laya.expert_offsets[e].item())
+    del xpa, wpa, laya, ws_a
     return dict(total_ms=total_ms, route_ms=route_ms, dispatch_ms=disp_ms, combine_ms=comb_ms,
+                route_bias_ms=route_bias_ms, route_mask_ms=route_mask_ms, aligned_ms=aligned_ms,
+                aligned_rows=aligned_rows,
                 comb_kernel_ms=comb_ms, kept=kept, copy_gbs=copy_gbs, dbwd_ms=dbwd_ms,
                 route_random_ms=route_random_ms, graph_ms=graph_ms,
                 dc_ms=dc_ms, dc_p10=pct(dc_batches, 10), dc_p90=pct(dc_batches, 90),
@@ -684,6 +703,11 @@ def main():
         "graph_step_us": round(dc["graph_ms"] * 1e3, 2),
         "graph_step_gbs": round(byts / (dc["graph_ms"] * 1e-3) / 1e9, 2),
         "route_force_balanced_us": round(dc["route_random_ms"] * 1e3, 2),
+        "route_expert_bias_us": round(dc["route_bias_ms"] * 1e3, 2),
+        "route_token_mask_us": round(dc["route_mask_ms"] * 1e3, 2),
+        "dispatch_row_align_128": {"us": round(dc["aligned_ms"] * 1e3, 2), "rows": dc["aligned_rows"],
+                                   "gbs": round((dc["n"] + dc["aligned_rows"]) * dc["h"] * 2
+                                                / (dc["aligned_ms"] * 1e-3) / 1e9, 1)},
         "zipf_capacity": {p: {"dispatch_us": round(v["dispatch_us"], 2), "combine_us": round(v["combine_us"], 2),
                               "dispatch_gbs": round(v["dispatch_bytes"] / v["dispatch_us"] / 1e3, 1),
                               "combine_gbs": round(v["combine_bytes"] / v["combine_us"] / 1e3, 1),
