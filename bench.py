@@ -49,7 +49,7 @@ def pct(v, q):
     return v[min(len(v) - 1, max(0, int(round(q / 100.0 * (len(v) - 1)))))] if v else float("nan")
 
 
-def bench_dispatch_combine(moe, mi, torch, steps, warmup):
+def bench_dispatch_combine(moe, mi, torch, steps, warmup, options=True):
     import numpy as np
     w = mi.workload(2)
     logits = torch.from_numpy(mi.router_logits(w)).cuda()
@@ -236,6 +236,8 @@ def bench_dispatch_combine(moe, mi, torch, steps, warmup):
     torch.cuda.synchronize()
     copy_gbs = 2 * flush.numel() * 4 / (k0.elapsed_time(k1) / 5 * 1e-3) / 1e9
     del flush, dst
+    if not options:
+        return dict(total_ms=total_ms, kept=kept)
     # router and layout options at the same shape, back to back: a selection-only
     # expert bias, a padding-token mask (every tenth token), and dropless segments
     # aligned to 128 rows (the zeroed pad rows between segments are written too)
@@ -473,7 +475,7 @@ def counter_pass():
     import moe_inputs as mi
     import combine_router_softmax_amd as moe
     torch.cuda.set_device(0)
-    bench_dispatch_combine(moe, mi, torch, 3, 1)
+    bench_dispatch_combine(moe, mi, torch, 3, 1, options=False)
     a = torch.empty(1 << 29, dtype=torch.bfloat16, device="cuda").fill_(1.0)
     b = torch.empty_like(a)
     b.copy_(a)
