@@ -328,6 +328,29 @@ def expert_gate_up_rows(rows, x_perm, lay, w_gate_up):
     return bf16_round_array(out)
 
 
+def expert_ffn_segments(x_perm, lay, w_gate_up, w_down, experts=None):
+    """The grouped SwiGLU FFN of oracle_expert_ffn_rows taken one expert segment
+    at a time with fp64 matrix products (a library matmul: every product of two
+    bf16 values is exact in fp64 and the sums are fp64, in the library's order
+    rather than the C loop's) and the same two bf16 roundings:
+        a = bf16(silu(x . w_gate) * (x . w_up)),  y = bf16(a . w_down),
+    silu(z) = z / (1 + e^-z).  For full-size checks of every row, where the C
+    loop takes too long.  Yields (expert, first row, y rows [count, H] as bf16
+    bits) for every non-empty segment among `experts` (default: all)."""
+    e, two_i, h = w_gate_up.shape
+    inter = two_i // 2
+    for ex in (range(e) if experts is None else experts):
+        o, n = int(lay["expert_offsets"][ex]), int(lay["tokens_per_expert"][ex])
+        if n == 0:
+            continue
+        x = _bf16_f64(x_perm[o:o + n])
+        g = x @ _bf16_f64(w_gate_up[ex, :inter]).T
+        u = x @ _bf16_f64(w_gate_up[ex, inter:]).T
+        a = _bf16_f64(bf16_round_array(g / (1.0 + np.exp(-g)) * u))
+        del g, u
+        yield ex, o, bf16_round_array(a @ _bf16_f64(w_down[ex]).T)
+
+
 def expert_ffn(x_perm, lay, w_gate_up, w_down):
     """FFN over every kept row; rows outside the segments are returned as zeros."""
     rows = np.nonzero(lay["pad_mask"] == 0)[0]
@@ -402,8 +425,6 @@ def expert_ffn_bwd(x_perm, grad_y, lay, w_gate_up, w_down, round_out=True):
     """
     e, two_i, h = w_gate_up.shape
     inter = two_i // 2
-    f64 = lambda a: a if a.dtype == np.float64 else _bf16_f64(a)  # float64 inputs are taken as they are
-    xv, gyv, wgu, wdv = f64(x_perm), f64(grad_y), f64(w_gate_up), f64(w_down)
     gx = np.zeros((lay["rows"], h))
     dwgu = np.zeros((e, two_i, h))
     dwd = np.zeros((e, h, inter))
@@ -411,19 +432,34 @@ def expert_ffn_bwd(x_perm, grad_y, lay, w_gate_up, w_down, round_out=True):
         o, n = int(lay["expert_offsets"][ex]), int(lay["tokens_per_expert"][ex])
         if n == 0:
             continue
-        x, dy = xv[o:o + n], gyv[o:o + n]
-        wg, wu, wd = wgu[ex, :inter], wgu[ex, inter:], wdv[ex]
-        g = x @ wg.T
-        u = x @ wu.T
-        s = 1.0 / (1.0 + np.exp(-g))
-        a = g * s * u
-        da = dy @ wd
-        dg = da * u * s * (1.0 + g * (1.0 - s))
-        du = da * g * s
-        gx[o:o + n] = dg @ wg + du @ wu
-        dwd[ex] = dy.T @ a
-        dwgu[ex, :inter] = dg.T @ x
-        dwgu[ex, inter:] = du.T @ x
+        gx[o:o + n], dwgu[ex], dwd[ex] = expert_ffn_bwd_expert(x_perm, grad_y, lay, w_gate_up, w_down, ex,
+                                                               round_out=False)
+    if not round_out:
+        return gx, dwgu, dwd
+    return bf16_round_array(gx), bf16_round_array(dwgu), bf16_round_array(dwd)
+
+
+def expert_ffn_bwd_expert(x_perm, grad_y, lay, w_gate_up, w_down, ex, round_out=True):
+    """expert_ffn_bwd for the one expert `ex` (the same formulas over its segment
+    only), so that full-size checks can take experts one at a time.  Returns
+    (grad_x_perm rows of the segment [count, H], grad_w_gate_up[ex] [2I, H],
+    grad_w_down[ex] [H, I]); bf16 bits rounded once, or the float64 values."""
+    e, two_i, h = w_gate_up.shape
+    inter = two_i // 2
+    f64 = lambda a: a if a.dtype == np.float64 else _bf16_f64(a)  # float64 inputs are taken as they are
+    o, n = int(lay["expert_offsets"][ex]), int(lay["tokens_per_expert"][ex])
+    x, dy = f64(x_perm[o:o + n]), f64(grad_y[o:o + n])
+    wg, wu, wd = f64(w_gate_up[ex, :inter]), f64(w_gate_up[ex, inter:]), f64(w_down[ex])
+    g = x @ wg.T
+    u = x @ wu.T
+    s = 1.0 / (1.0 + np.exp(-g))
+    a = g * s * u
+    da = dy @ wd
+    dg = da * u * s * (1.0 + g * (1.0 - s))
+    du = da * g * s
+    gx = dg @ wg + du @ wu
+    dwd = dy.T @ a
+    dwgu = np.concatenate([dg.T @ x, du.T @ x])
     if not round_out:
         return gx, dwgu, dwd
     return bf16_round_array(gx), bf16_round_array(dwgu), bf16_round_array(dwd)

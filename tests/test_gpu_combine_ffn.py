@@ -43,7 +43,8 @@ def test_combine_identity_expert_full_size(moe, wid):
     ref_lay = layout_host(lay)
     ref_lay["rows"] = lay.rows
     ref = oracle.combine(host(xp), wts, ref_lay, w.n_tokens, w.top_k)
-    assert max_rel_err(got, ref) <= tol_for(ref)
+    # the kernel takes the oracle's fp32 fused multiply-adds in slot order: equal bits
+    np.testing.assert_array_equal(got, ref)
     if wid == 2:
         # identity expert, renormalised weights, nothing dropped: combine(dispatch(x)) == x bit for bit
         assert (got == x).all()
@@ -66,7 +67,7 @@ def test_combine_random_rows_with_drops_and_sentinels(moe, dt, capacity):
     ref_lay = oracle.layout(idx, e, capacity)
     ref = oracle.combine(y, wts, ref_lay, n, k)
     got = host(out)
-    assert max_rel_err(got, ref) <= tol_for(ref)
+    np.testing.assert_array_equal(got, ref)   # same fp32 fused multiply-adds in slot order
     none = (ref_lay["assign_row"].reshape(n, k) < 0).all(1)
     assert (got[none].view(np.uint8) == 0).all()
 
@@ -187,66 +188,6 @@ def test_expert_ffn_small_full_compare(moe, n, e, k, h, inter, cap):
     assert (got[kept] == ref[kept]).mean() > 0.9
 
 
-def sample_rows(lay_h: dict, g: np.random.Generator, per_expert: int = 2, experts: int = 16):
-    e = lay_h["tokens_per_expert"].size
-    chosen = g.choice(e, size=min(experts, e), replace=False)
-    rows = []
-    for x in chosen:
-        o, c = int(lay_h["expert_offsets"][x]), int(lay_h["tokens_per_expert"][x])
-        if c == 0:
-            continue
-        rows += [o, o + c - 1] + list(o + g.integers(0, c, size=per_expert))
-    return np.unique(np.array(rows, np.int64))
-
-
-@pytest.mark.parametrize("wid", [4, 5])
-def test_expert_ffn_full_size_sampled_rows(moe, wid):
-    w = mi.workload(wid)
-    idx, wts, logits, x = workload_inputs(w)
-    if idx is None:
-        idx, wts, _, _ = oracle.route(logits, w.top_k)
-    wgu, wd = mi.expert_weights(w)
-    xp, wp, lay = moe.moe_dispatch(dev(x), dev(idx), dev(wts), w.n_experts, max_rows=w.rows)
-    y = moe.moe_expert_ffn(xp, lay, dev(wgu), dev(wd))
-    torch.cuda.synchronize()
-    lay_h = layout_host(lay)
-    rows = sample_rows(lay_h, np.random.default_rng(wid), per_expert=1, experts=12)
-    xp_h = host(xp)
-    ref, ex = oracle.expert_ffn_rows(rows, xp_h, lay_h, wgu, wd)
-    assert (ex >= 0).all()
-    got = host(y)[rows]
-    assert max_rel_err(got, ref) <= TOL_BF16
-    assert (got == ref).mean() > 0.9
-
-
-def test_full_layer_qwen3_shape_sampled_tokens(moe):
-    """route -> dispatch -> grouped SwiGLU FFN -> combine at N=8192 H=4096 E=128 k=8 I=1536;
-    sampled output tokens against the oracle's route, layout, FFN rows and combine."""
-    w = mi.workload(4)
-    logits = mi.router_logits(w)
-    x = mi.activations(w)
-    wgu, wd = mi.expert_weights(w)
-    r = moe.moe_route(dev(logits), w.top_k)
-    xp, wp, lay = moe.moe_dispatch(dev(x), r.topk_idx, r.topk_w, w.n_experts)
-    y = moe.moe_expert_ffn(xp, lay, dev(wgu), dev(wd))
-    out = moe.moe_combine(y, r.topk_w, lay)
-    torch.cuda.synchronize()
-    idx, wts, _, _ = oracle.route(logits, w.top_k)
-    ref_lay = oracle.layout(idx, w.n_experts)
-    toks = np.random.default_rng(9).choice(w.n_tokens, size=6, replace=False)
-    xp_ref, _ = oracle.scatter(x, w.top_k, ref_lay, wts)
-    out_h = host(out)
-    for t in toks:
-        rows = ref_lay["assign_row"][t * w.top_k:(t + 1) * w.top_k].astype(np.int64)
-        y_rows, _ = oracle.expert_ffn_rows(rows, xp_ref, ref_lay, wgu, wd)
-        y_full = np.zeros((ref_lay["rows"], w.hidden), np.uint16)
-        y_full[rows] = y_rows
-        sub_lay = dict(ref_lay)
-        sub_lay["assign_row"] = ref_lay["assign_row"][t * w.top_k:(t + 1) * w.top_k]
-        ref = oracle.combine(y_full, wts[t:t + 1], sub_lay, 1, w.top_k)
-        assert max_rel_err(out_h[t:t + 1], ref) <= TOL_BF16
-
-
 # ------------------------------------------------------ expert FFN backward
 
 def ffn_bwd_run(moe, w, xp, lay, wgu, wd, seed=0):
@@ -329,48 +270,6 @@ def test_expert_ffn_bwd_repeated_calls_are_identical(moe):
     b = ffn_bwd_run(moe, w, xp, lay, wgu, wd)
     for u, v in zip(a[1:], b[1:]):
         assert torch.equal(u.view(torch.int16), v.view(torch.int16))
-
-
-def sample_bwd_entries(lay_h: dict, e: int, h: int, inter: int, g: np.random.Generator, per_expert: int = 4):
-    """Weight-gradient entries of the hottest, the coldest non-empty, an empty (if
-    any) and a few random experts."""
-    cnt = lay_h["tokens_per_expert"][:e]
-    nz = np.nonzero(cnt > 0)[0]
-    chosen = {int(np.argmax(cnt)), int(nz[np.argmin(cnt[nz])])}
-    if (cnt == 0).any():
-        chosen.add(int(np.nonzero(cnt == 0)[0][0]))
-    chosen |= {int(v) for v in g.choice(e, size=min(3, e), replace=False)}
-    dwd, dwgu = [], []
-    for ex in sorted(chosen):
-        dwd += [(ex, int(g.integers(h)), int(g.integers(inter))) for _ in range(per_expert)]
-        dwgu += [(ex, int(g.integers(inter)), int(g.integers(h))) for _ in range(per_expert // 2)]
-        dwgu += [(ex, inter + int(g.integers(inter)), int(g.integers(h))) for _ in range(per_expert // 2)]
-    return dwd, dwgu
-
-
-@pytest.mark.parametrize("wid", [4, 5])
-def test_expert_ffn_bwd_full_size_sampled(moe, wid):
-    """Full-size backward (N=8192 H=4096 E=128 k=8 I=1536; the 32-expert H=7168
-    I=2048 share with Zipf loads): sampled rows of grad_x_perm and sampled
-    entries of both weight gradients against the oracle's per-entry backward."""
-    w = mi.workload(wid)
-    idx, wts, logits, x = workload_inputs(w)
-    if idx is None:
-        idx, wts, _, _ = oracle.route(logits, w.top_k)
-    wgu, wd = mi.expert_weights(w)
-    xp, wp, lay = moe.moe_dispatch(dev(x), dev(idx), dev(wts), w.n_experts, max_rows=w.rows)
-    dy, gx, dwgu, dwd = ffn_bwd_run(moe, w, xp, lay, wgu, wd)
-    lay_h = layout_host(lay)
-    g = np.random.default_rng(100 + wid)
-    rows = sample_rows(lay_h, g, per_expert=1, experts=8)
-    d_idx, gu_idx = sample_bwd_entries(lay_h, w.n_experts, w.hidden, w.inter, g)
-    ref_rows, ref_d, ref_gu = oracle.expert_ffn_bwd_entries(host(xp), dy, lay_h, wgu, wd, rows, d_idx, gu_idx)
-    assert max_rel_err(host(gx[torch.as_tensor(rows, device=gx.device)]), ref_rows) <= TOL_BF16
-    assert max_rel_err(entries(dwd, d_idx), ref_d) <= TOL_BF16
-    assert max_rel_err(entries(dwgu, gu_idx), ref_gu) <= TOL_BF16
-    cnt = lay_h["tokens_per_expert"]
-    for ex in np.nonzero(cnt == 0)[0]:
-        assert not dwgu[int(ex)].view(torch.int16).any() and not dwd[int(ex)].view(torch.int16).any()
 
 
 @pytest.mark.parametrize("n,e,k,h,inter,cap", [

@@ -1,0 +1,169 @@
+"""Full-size GPU parity of the whole path, forward and backward, at the two
+expert-FFN workloads, through the C ABI:
+
+  qwen3_layer  N=8192 tokens, H=4096, E=128, top-8, SwiGLU I=1536 (router ->
+               dispatch -> grouped FFN -> combine, 65536 rows)
+  dsv3_share   16384 received tokens x 8 slots (2 local ids, 6 sentinels),
+               32 experts with Zipf(1.2) counts 10573 ... 165, H=7168,
+               I=2048, 32768 rows
+
+and the backward chain combine_bwd -> expert_ffn_bwd -> dispatch_bwd.
+
+Bit-exact: routing, every layout field, dispatched rows and weights, the
+combine over EVERY token (kernel and oracle take the same fp32 fused
+multiply-adds in slot order, so the bits agree), the dispatch backward.
+Tolerance (max|got - ref| / max|ref| per tensor): the FFN output on EVERY row
+(the oracle's segment-wise fp64 products with the two bf16 roundings), the
+combine backward, and the FFN backward of whole experts -- the hottest, the
+coldest non-empty one and the two with the most ragged last 256-row tile.
+Each oracle input is the oracle's own value where one exists (route, layout,
+scatter) and otherwise the GPU output that the previous test proved."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle
+from parity_util import TOL_BF16, TOL_F32, assert_layout_equal, dev, host, layout_host, max_rel_err, values
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import combine_router_softmax_amd as m
+    return m
+
+
+@pytest.fixture(scope="module", params=[4, 5], ids=["qwen3_layer", "dsv3_share"])
+def layer(request, moe):
+    """One full-size forward and backward pass on the GPU and the host inputs."""
+    w = mi.workload(request.param)
+    print(f"\n[full size] {w.name}: N={w.n_tokens} H={w.hidden} E={w.n_experts} k={w.top_k} I={w.inter}", flush=True)
+    x = mi.activations(w)
+    if w.has_router:
+        logits = mi.router_logits(w)
+        r = moe.moe_route(dev(logits), w.top_k)
+        idx, wts, rmap, tpe = oracle.route(logits, w.top_k)
+        route_gpu = (host(r.topk_idx), host(r.topk_w), host(r.routing_map), host(r.tokens_per_expert))
+        idx_d, wts_d = r.topk_idx, r.topk_w
+        route_ref = (idx, wts, rmap, tpe)
+    else:
+        idx, wts = mi.received_routing(w)
+        idx_d, wts_d = dev(idx), dev(wts)
+        route_gpu = route_ref = None
+    max_rows = w.rows if w.rows else 0
+    wgu, wd = mi.expert_weights(w)
+    wgu_d, wd_d = dev(wgu), dev(wd)
+    go = mi.grad_output(w)
+    xp, wp, lay = moe.moe_dispatch(dev(x), idx_d, wts_d, w.n_experts, max_rows=max_rows)
+    y = moe.moe_expert_ffn(xp, lay, wgu_d, wd_d)
+    out = moe.moe_combine(y, wts_d, lay)
+    gy, gw = moe.moe_combine_bwd(dev(go), y, wts_d, lay)
+    gxp, dwgu, dwd = moe.moe_expert_ffn_bwd(xp, gy, lay, wgu_d, wd_d)
+    gx = moe.moe_dispatch_bwd(gxp, lay)
+    torch.cuda.synchronize()
+    ref_lay = oracle.layout(idx, w.n_experts, 0, max_rows)
+    d = dict(w=w, x=x, idx=idx, wts=wts, wgu=wgu, wd=wd, go=go, route_gpu=route_gpu, route_ref=route_ref,
+             ref_lay=ref_lay, lay=layout_host(lay), xp=host(xp), wp=host(wp), y=host(y), out=host(out), gy=host(gy),
+             gw=host(gw), gxp=host(gxp), gx=host(gx), dwgu_d=dwgu, dwd_d=dwd)
+    yield d
+    d.clear()
+    torch.cuda.empty_cache()
+
+
+def test_route_and_dispatch_bit_exact(layer):
+    w = layer["w"]
+    if layer["route_ref"] is not None:
+        gi, gwt, gm, gt = layer["route_gpu"]
+        idx, wts, rmap, tpe = layer["route_ref"]
+        np.testing.assert_array_equal(gi, idx)
+        np.testing.assert_array_equal(gm, rmap)
+        np.testing.assert_array_equal(gt, tpe)
+        assert max_rel_err(gwt, wts) <= TOL_F32
+    ref = layer["ref_lay"]
+    assert_layout_equal(layer["lay"], ref)
+    xp_ref, wp_ref = oracle.scatter(layer["x"], w.top_k, ref, layer["wts"], x_perm=layer["xp"].copy())
+    assert (layer["xp"].view(np.uint8) == xp_ref.view(np.uint8)).all()
+    np.testing.assert_array_equal(layer["wp"], wp_ref)
+    # rows follow the expert segments, stable in assignment order
+    kept = ref["assign_row"] >= 0
+    assert int(kept.sum()) == int(ref["counters"][0]) == w.n_tokens * w.top_k - int((layer["idx"] < 0).sum())
+
+
+def test_ffn_every_row(layer):
+    """Every kept row of y against the segment-wise fp64 oracle; also the share of
+    bit-identical values (the kernel's fp32 sums round like the oracle's fp64 ones
+    almost everywhere)."""
+    w = layer["w"]
+    ref_lay = layer["ref_lay"]
+    xp_ref, _ = oracle.scatter(layer["x"], w.top_k, ref_lay, layer["wts"])
+    y = layer["y"]
+    worst, scale, same, total, seen = 0.0, 0.0, 0, 0, 0
+    for ex, o, ref in oracle.expert_ffn_segments(xp_ref, ref_lay, layer["wgu"], layer["wd"]):
+        got = y[o:o + ref.shape[0]]
+        worst = max(worst, float(np.abs(values(got) - values(ref)).max()))
+        scale = max(scale, float(np.abs(values(ref)).max()))
+        same += int((got == ref).sum())
+        total += ref.size
+        seen += ref.shape[0]
+    assert seen == int(ref_lay["counters"][0])
+    print(f"[full size] {w.name}: FFN max rel err {worst / scale:.3e}, identical values {same / total:.4f}")
+    assert worst <= TOL_BF16 * scale
+    assert same / total > 0.9
+
+
+def test_combine_every_token_bit_exact(layer):
+    w = layer["w"]
+    ref = oracle.combine(layer["y"], layer["wts"], layer["ref_lay"], w.n_tokens, w.top_k)
+    np.testing.assert_array_equal(layer["out"], ref)
+
+
+def test_combine_bwd_full(layer):
+    w = layer["w"]
+    ref_lay = dict(layer["ref_lay"])
+    ref_gy, ref_gw = oracle.combine_bwd(layer["go"], layer["y"], layer["wts"], ref_lay, w.top_k,
+                                        grad_y=layer["gy"].copy())
+    kept = ref_lay["pad_mask"] == 0
+    assert max_rel_err(layer["gy"][kept], ref_gy[kept]) <= TOL_BF16
+    assert max_rel_err(layer["gw"], ref_gw) <= TOL_F32
+    assert (layer["gw"].reshape(-1)[ref_lay["assign_row"] < 0] == 0).all()
+
+
+def bwd_experts(cnt: np.ndarray):
+    """The hottest expert, the coldest non-empty one and the two whose last 256-row
+    tile is the most ragged (fewest rows in it)."""
+    nz = np.nonzero(cnt > 0)[0]
+    pick = {int(np.argmax(cnt)), int(nz[np.argmin(cnt[nz])])}
+    tail = (cnt[nz] - 1) % 256 + 1
+    for i in np.argsort(tail, kind="stable")[:2]:
+        pick.add(int(nz[i]))
+    return sorted(pick)
+
+
+def test_ffn_bwd_whole_experts(layer):
+    w = layer["w"]
+    ref_lay = layer["ref_lay"]
+    xp_ref, _ = oracle.scatter(layer["x"], w.top_k, ref_lay, layer["wts"])
+    cnt = ref_lay["tokens_per_expert"]
+    for ex in bwd_experts(cnt):
+        o, c = int(ref_lay["expert_offsets"][ex]), int(cnt[ex])
+        r_gx, r_dwgu, r_dwd = oracle.expert_ffn_bwd_expert(xp_ref, layer["gy"], ref_lay, layer["wgu"], layer["wd"], ex)
+        g_dwgu, g_dwd = host(layer["dwgu_d"][ex]), host(layer["dwd_d"][ex])
+        errs = (max_rel_err(layer["gxp"][o:o + c], r_gx), max_rel_err(g_dwgu, r_dwgu), max_rel_err(g_dwd, r_dwd))
+        print(f"[full size] {w.name}: expert {ex} ({c} rows) FFN backward max rel err dX {errs[0]:.2e} "
+              f"dW_gate_up {errs[1]:.2e} dW_down {errs[2]:.2e}")
+        assert max(errs) <= TOL_BF16, (ex, c, errs)
+    for ex in np.nonzero(cnt == 0)[0]:
+        assert not layer["dwgu_d"][int(ex)].view(torch.int16).any()
+        assert not layer["dwd_d"][int(ex)].view(torch.int16).any()
+
+
+def test_dispatch_bwd_bit_exact(layer):
+    w = layer["w"]
+    ref = oracle.dispatch_bwd(layer["gxp"], layer["ref_lay"], w.n_tokens, w.top_k)
+    assert (layer["gx"].view(np.uint8) == ref.view(np.uint8)).all()

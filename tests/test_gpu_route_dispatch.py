@@ -231,7 +231,7 @@ def test_dispatch_drop_by_weight_zipf_workload(moe):
     assert kept_w > kept_pos
 
 
-@pytest.mark.parametrize("wid", [1, 2, 3, 5])
+@pytest.mark.parametrize("wid", [1, 2, 3, 4, 5])
 def test_dispatch_workloads_full_size(moe, wid):
     w = mi.workload(wid)
     idx, wts, logits, x = workload_inputs(w)

@@ -785,6 +785,29 @@ def test_ffn_matches_numpy_matmul_per_expert():
         assert np.abs(bf16_vals(got) - bf16_vals(ref)).max() <= 2e-2 * np.abs(bf16_vals(ref)).max()
 
 
+def test_ffn_segments_match_the_row_loop():
+    """The segment-wise fp64 FFN (library matmuls) against the C row loop and the
+    numpy form above: the same two roundings, sums in another order, so equal bits
+    but for rare rounding boundaries, and never more than one bf16 step apart."""
+    for seed, e, n, h, inter in ((0, 3, 40, 48, 32), (1, 5, 300, 128, 96), (2, 1, 70, 64, 64)):
+        w, idx, wts, lay, x, xp, wgu, wd = _small_ffn_case(e=e, n=n, k=min(2, e), h=h, inter=inter, seed=seed)
+        ref = oracle.expert_ffn(xp, lay, wgu, wd)
+        seen = 0
+        for ex, o, y in oracle.expert_ffn_segments(xp, lay, wgu, wd):
+            c = int(lay["tokens_per_expert"][ex])
+            assert o == lay["expert_offsets"][ex] and y.shape == (c, h)
+            got, want = y, ref[o:o + c]
+            assert (got == want).mean() > 0.97
+            assert np.abs(bf16_vals(got) - bf16_vals(want)).max() <= 2.0 ** -7 * np.abs(bf16_vals(want)).max()
+            np_ref = ffn_numpy(bf16_vals(xp[o:o + c]), bf16_vals(wgu[ex, :inter]), bf16_vals(wgu[ex, inter:]),
+                               bf16_vals(wd[ex]))
+            assert (got == np_ref).mean() > 0.97
+            seen += c
+        assert seen == int(lay["tokens_per_expert"].sum())
+    only = list(oracle.expert_ffn_segments(xp, lay, wgu, wd, experts=[0]))
+    assert [v[0] for v in only] == ([0] if lay["tokens_per_expert"][0] else [])
+
+
 def test_ffn_single_expert_is_plain_gemm_pair():
     w, idx, wts, lay, x, xp, wgu, wd = _small_ffn_case(e=1, k=1, n=30)
     y = oracle.expert_ffn(xp, lay, wgu, wd)
