@@ -60,7 +60,7 @@ def bench_dispatch_combine(moe, mi, torch, steps, warmup, options=True):
     r = moe.moe_route(logits, k)
     xp, wp, lay = moe.moe_dispatch(x, r.topk_idx, r.topk_w, e)
     shape = moe.make_shape(n, h, e, k, act_dtype=moe.MOE_DT_BF16)
-    ws = torch.empty(moe.workspace_size(moe.MOE_OP_DISPATCH, shape) + 256, dtype=torch.uint8, device=dev)
+    ws = moe.alloc_workspace(moe.MOE_OP_DISPATCH, shape, dev)
     out = torch.empty_like(x)
     go = torch.randn(x.shape, generator=torch.Generator(device=dev).manual_seed(4), device=dev).to(torch.bfloat16)
     gy = torch.empty_like(xp)
@@ -250,7 +250,7 @@ def bench_dispatch_combine(moe, mi, torch, steps, warmup, options=True):
     route_mask_ms = b2b_ms([lambda: moe.moe_route(logits, k, token_mask=mask, out=rm)], steps)
     xpa, wpa, laya = moe.moe_dispatch(x, r.topk_idx, r.topk_w, e, row_align=128)
     shape_a = laya.shape(h, moe.MOE_DT_BF16)
-    ws_a = torch.empty(moe.workspace_size(moe.MOE_OP_DISPATCH, shape_a) + 256, dtype=torch.uint8, device=dev)
+    ws_a = moe.alloc_workspace(moe.MOE_OP_DISPATCH, shape_a, dev)
     aligned_ms = b2b_ms([lambda: moe.moe_dispatch(x, r.topk_idx, r.topk_w, e, row_align=128, layout=laya, x_perm=xpa,
                                                   w_perm_out=wpa, workspace=ws_a)], steps)
     aligned_rows = int(laya.expert_offsets[e].item())
@@ -284,7 +284,7 @@ def bench_skewed_capacity(moe, mi, torch, steps, warmup):
     for name, policy in (("position", moe.MOE_DROP_POSITION), ("probs", moe.MOE_DROP_PROBS)):
         xp, wp, lay = moe.moe_dispatch(x, r.topk_idx, r.topk_w, e, capacity=w.capacity, drop_policy=policy)
         shape = lay.shape(h, moe.MOE_DT_BF16)
-        ws = torch.empty(moe.workspace_size(moe.MOE_OP_DISPATCH, shape) + 256, dtype=torch.uint8, device=x.device)
+        ws = moe.alloc_workspace(moe.MOE_OP_DISPATCH, shape, x.device)
         run_d = lambda: moe.moe_dispatch(x, r.topk_idx, r.topk_w, e, capacity=w.capacity, drop_policy=policy,
                                          layout=lay, x_perm=xp, w_perm_out=wp, workspace=ws)
         for _ in range(warmup):
@@ -328,7 +328,7 @@ def bench_expert_gemm(moe, mi, torch, wid, iters, warmup, bwd_iters=0, replicas=
     xp, wp, lay = moe.moe_dispatch(x, idx, wts, e, max_rows=w.rows)
     y = torch.empty_like(xp)
     shape = lay.shape(h, moe.MOE_DT_BF16, inter)
-    ws = torch.empty(moe.workspace_size(moe.MOE_OP_EXPERT_FFN, shape) + 256, dtype=torch.uint8, device=dev)
+    ws = moe.alloc_workspace(moe.MOE_OP_EXPERT_FFN, shape, dev)
     for _ in range(warmup):
         moe.moe_expert_ffn(xp, lay, wgu, wd, y=y, workspace=ws)
     torch.cuda.synchronize()
@@ -350,8 +350,7 @@ def bench_expert_gemm(moe, mi, torch, wid, iters, warmup, bwd_iters=0, replicas=
         gq, gs = moe.moe_mx_quantize(wgu)
         dq, ds = moe.moe_mx_quantize(wd)
         y8 = torch.empty_like(xp)
-        ws8 = torch.empty(moe.workspace_size(moe.MOE_OP_EXPERT_FFN_MXFP8, shape) + 256, dtype=torch.uint8,
-                          device=dev)
+        ws8 = moe.alloc_workspace(moe.MOE_OP_EXPERT_FFN_MXFP8, shape, dev)
         for _ in range(warmup):
             moe.moe_expert_ffn_mxfp8(q8, s8, lay8, gq, gs, dq, ds, y=y8, workspace=ws8)
         torch.cuda.synchronize()
@@ -409,7 +408,7 @@ def bench_expert_gemm(moe, mi, torch, wid, iters, warmup, bwd_iters=0, replicas=
         xp_r, _, lay_r = moe.moe_dispatch(x, phys, wts, e + replicas, max_rows=w.rows)
         y_r = torch.empty_like(xp_r)
         rr_shape = moe.make_shape(idx.shape[0], h, e, idx.shape[1])
-        ws_rr = torch.empty(moe.workspace_size(moe.MOE_OP_REROUTE, rr_shape) + 256, dtype=torch.uint8, device=dev)
+        ws_rr = moe.alloc_workspace(moe.MOE_OP_REROUTE, rr_shape, dev)
         plan_ms = timed(lambda: moe.moe_replica_plan(counts, replicas, out=rep), iters)
         sync_ms = timed(lambda: moe.moe_replica_sync(wgu, wd, rep, w_gate_up_replica=wgu_r, w_down_replica=wd_r), iters)
         rr_ms = timed(lambda: moe.moe_reroute(idx, e, rep, out=phys, workspace=ws_rr), iters)
@@ -427,13 +426,13 @@ def bench_expert_gemm(moe, mi, torch, wid, iters, warmup, bwd_iters=0, replicas=
 
         # training forward: also stores the pre-activations [G | U] for the backward
         gu = torch.empty((xp.shape[0], 2 * inter), dtype=torch.bfloat16, device=dev)
-        ws = torch.empty(moe.workspace_size(moe.MOE_OP_EXPERT_FFN, shape) + 256, dtype=torch.uint8, device=dev)
+        ws = moe.alloc_workspace(moe.MOE_OP_EXPERT_FFN, shape, dev)
         fms = timed(lambda: moe.moe_expert_ffn(xp, lay, wgu, wd, y=y, gate_up=gu, workspace=ws), iters)
         del ws
         # backward: dy [R, H] in, grad_x_perm [R, H], grad_w_gate_up, grad_w_down out
         dy = torch.randn(xp.shape, generator=g, device=dev).to(torch.bfloat16)
         gx, dwgu, dwd = torch.empty_like(xp), torch.empty_like(wgu), torch.empty_like(wd)
-        ws = torch.empty(moe.workspace_size(moe.MOE_OP_EXPERT_FFN_BWD, shape) + 256, dtype=torch.uint8, device=dev)
+        ws = moe.alloc_workspace(moe.MOE_OP_EXPERT_FFN_BWD, shape, dev)
         bwd = lambda saved: moe.moe_expert_ffn_bwd(xp, dy, lay, wgu, wd, gate_up=saved, grad_x_perm=gx,
                                                    grad_w_gate_up=dwgu, grad_w_down=dwd, workspace=ws)
         bms = timed(lambda: bwd(gu), bwd_iters)
@@ -528,11 +527,11 @@ def power_pass():
     xp, _, lay = moe.moe_dispatch(x, r.topk_idx, r.topk_w, e, max_rows=w.rows)
     y = torch.empty_like(xp)
     shape = lay.shape(h, moe.MOE_DT_BF16, inter)
-    ws = torch.empty(moe.workspace_size(moe.MOE_OP_EXPERT_FFN, shape) + 256, dtype=torch.uint8, device=dev)
+    ws = moe.alloc_workspace(moe.MOE_OP_EXPERT_FFN, shape, dev)
     q8, s8, _, lay8 = moe.moe_dispatch_mxfp8(x, r.topk_idx, r.topk_w, e, max_rows=w.rows)
     gq, gs = moe.moe_mx_quantize(wgu)
     dq, ds = moe.moe_mx_quantize(wd)
-    ws8 = torch.empty(moe.workspace_size(moe.MOE_OP_EXPERT_FFN_MXFP8, shape) + 256, dtype=torch.uint8, device=dev)
+    ws8 = moe.alloc_workspace(moe.MOE_OP_EXPERT_FFN_MXFP8, shape, dev)
     xa = torch.randn((e, 512, h), generator=g, device=dev).to(torch.bfloat16)
     wb = wgu.transpose(1, 2).contiguous()  # contiguous right operand for torch.bmm
     yb = torch.empty((e, 512, 2 * inter), dtype=torch.bfloat16, device=dev)

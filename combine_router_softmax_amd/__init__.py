@@ -135,11 +135,20 @@ def workspace_size(op: int, shape: MoeShape) -> int:
     return int(out.value)
 
 
-def _workspace(op, shape, device):
+def alloc_workspace(op: int, shape: MoeShape, device) -> torch.Tensor | None:
+    """A device workspace for `op` at `shape` (include/moe.h moe_workspace_size), with
+    256 bytes of slack for the 256-byte alignment the calls take.  Zero-filled: the
+    dispatch and reroute workspaces must start with a zero header, which every call
+    leaves zero again, so one workspace serves any number of calls in stream order."""
     n = workspace_size(op, shape)
     if n == 0:
-        return None, 0
-    return torch.empty(n + 256, dtype=torch.uint8, device=device), n
+        return None
+    return torch.zeros(n + 256, dtype=torch.uint8, device=device)
+
+
+def _workspace(op, shape, device):
+    ws = alloc_workspace(op, shape, device)
+    return ws, (0 if ws is None else ws.numel() - 256)
 
 
 def _ws_ptr(ws):

@@ -166,7 +166,8 @@ namespace {
 // are the permuted-row outputs (each must be non-null when rows > 0).
 moe_status dispatch_layout(const moe_shape *s, int64_t rows, const void *x, const int32_t *topk_idx,
                            const float *topk_w, const moe_layout *layout, std::initializer_list<const void *> outs,
-                           float *w_perm, void *workspace, size_t workspace_bytes, hipStream_t hs) {
+                           float *w_perm, void *workspace, size_t workspace_bytes, hipStream_t hs,
+                           bool place_in_scatter) {
   if (!layout) return MOE_ERR_INVALID_ARG;
   const int64_t n = s->n_tokens, a = n * s->top_k;
   if (!layout->tokens_per_expert || !layout->expert_offsets || !layout->counters) return MOE_ERR_INVALID_ARG;
@@ -178,8 +179,12 @@ moe_status dispatch_layout(const moe_shape *s, int64_t rows, const void *x, cons
   if (!need(x, n, aligned16)) return MOE_ERR_MISALIGNED;
   if (by_weight(s) && a > 0 && !topk_w) return MOE_ERR_INVALID_ARG;  // the policy ranks the weights
   const size_t need_ws = moe::layout_workspace_bytes(a, s->n_experts, by_weight(s));
-  if (workspace_bytes < need_ws || (need_ws > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))))
+  if (workspace_bytes < need_ws || !workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return MOE_ERR_WORKSPACE;
+  if (place_in_scatter)  // the scan alone; the scatter places the rows
+    return hip_status(moe::launch_layout_scan(topk_idx, n, s->top_k, s->n_experts, s->capacity, s->row_align, rows,
+                                              layout->tokens_per_expert, layout->expert_offsets, layout->ordinal,
+                                              layout->counters, workspace, hs));
   return hip_status(moe::launch_layout(topk_idx, topk_w, n, s->top_k, s->n_experts, s->capacity, s->row_align,
                                        by_weight(s), rows, layout->tokens_per_expert, layout->expert_offsets,
                                        layout->ordinal, layout->assign_row, layout->row_src, layout->drop_mask,
@@ -206,9 +211,18 @@ moe_status moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_i
   if ((st = check_rows(s, &row_bytes, &rows)) != MOE_OK) return st;
   if (!need(x_perm, rows, aligned16)) return MOE_ERR_MISALIGNED;
   hipStream_t hs = as_stream(stream);
-  if ((st = dispatch_layout(s, rows, x, topk_idx, topk_w, layout, {x_perm}, w_perm, workspace, workspace_bytes, hs)) !=
-      MOE_OK)
+  // the position policy places rows in the scatter; dropping by weight selects first
+  const bool place_in_scatter = !by_weight(s);
+  if ((st = dispatch_layout(s, rows, x, topk_idx, topk_w, layout, {x_perm}, w_perm, workspace, workspace_bytes, hs,
+                            place_in_scatter)) != MOE_OK)
     return st;
+  if (place_in_scatter) {
+    const moe::PlaceArgs p = moe::place_args(topk_idx, topk_w, layout->ordinal, layout->tokens_per_expert,
+                                             layout->expert_offsets, s->n_experts, s->capacity, s->row_align, rows,
+                                             layout->assign_row, layout->drop_mask, layout->row_src, layout->pad_mask,
+                                             w_perm);
+    return hip_status(moe::launch_scatter_placing(x, s->n_tokens, s->top_k, row_bytes, p, x_perm, hs));
+  }
   return hip_status(moe::launch_scatter(x, s->n_tokens, s->top_k, row_bytes, layout->assign_row, x_perm,
                                         pad_rows_of(s, rows), pad_limit_of(s, layout), layout->row_src, hs));
 }
@@ -225,7 +239,7 @@ moe_status moe_dispatch_mxfp8(const moe_shape *s, const void *x, const int32_t *
   if (rows > 0 && x_perm_q && x_perm_q == x_perm_scale) return MOE_ERR_INVALID_ARG;
   hipStream_t hs = as_stream(stream);
   if ((st = dispatch_layout(s, rows, x, topk_idx, topk_w, layout, {x_perm_q, x_perm_scale}, w_perm, workspace,
-                            workspace_bytes, hs)) != MOE_OK)
+                            workspace_bytes, hs, false)) != MOE_OK)
     return st;
   return hip_status(moe::launch_scatter_mxfp8(static_cast<const uint16_t *>(x), s->n_tokens, s->top_k, s->hidden,
                                               layout->assign_row, x_perm_q, x_perm_scale, pad_rows_of(s, rows),

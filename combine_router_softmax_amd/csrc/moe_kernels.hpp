@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "moe_place.hpp"
+
 namespace moe {
 
 // ---- route (moe_route.hip)
@@ -15,9 +17,22 @@ hipError_t launch_route(const float *logits, uint64_t seed, const float *expert_
                         int32_t *tokens_per_expert, hipStream_t stream);
 
 // ---- layout (moe_layout.hip)
-constexpr int kLayoutTile = 512;  // assignments per layout tile
-inline int64_t layout_tiles(int64_t assignments) { return (assignments + kLayoutTile - 1) / kLayoutTile; }
+constexpr int kLayoutTile = 2048;  // assignments per layout tile
+inline int64_t layout_tiles(int64_t assignments) {
+  return assignments <= 0 ? 1 : (assignments + kLayoutTile - 1) / kLayoutTile;
+}
+// Workspace of the layout: a 256-byte header that must be zero before the
+// workspace's first use (every call leaves it zero), then the scan's status
+// words (and, dropping by weight, the per-expert assignment lists).
 size_t layout_workspace_bytes(int64_t assignments, int e, bool drop_by_weight);
+// zero the header of a layout workspace (a kernel, so that it can be captured)
+hipError_t clear_layout_header(void *workspace, hipStream_t stream);
+// the scan alone: ordinal, tokens_per_expert, expert_offsets, counters; rows
+// are then placed by launch_scatter_placing (or not at all: the reroute)
+hipError_t launch_layout_scan(const int32_t *topk_idx, int64_t n, int k, int e, int capacity, int row_align,
+                              int64_t rows, int32_t *tokens_per_expert, int32_t *expert_offsets, int32_t *ordinal,
+                              int32_t *counters, void *workspace, hipStream_t stream);
+// the whole layout with the rows placed in a launch of their own;
 // drop_by_weight (with a capacity): keep each expert's `capacity` largest weights
 hipError_t launch_layout(const int32_t *topk_idx, const float *topk_w, int64_t n, int k, int e, int capacity,
                          int row_align, bool drop_by_weight, int64_t rows, int32_t *tokens_per_expert,
@@ -31,6 +46,11 @@ hipError_t launch_layout(const int32_t *topk_idx, const float *topk_w, int64_t n
 hipError_t launch_scatter(const void *x, int64_t n, int k, int64_t row_bytes, const int32_t *assign_row,
                           void *x_perm, int64_t pad_rows, const int32_t *pad_limit, const int32_t *row_src,
                           hipStream_t stream);
+// The scatter that also places the rows after launch_layout_scan (the
+// position policy): each slot's row from its ordinal, kept count and offset,
+// the layout's row maps and masks written on the way, pad rows zeroed.
+hipError_t launch_scatter_placing(const void *x, int64_t n, int k, int64_t row_bytes, const PlaceArgs &place,
+                                  void *x_perm, hipStream_t stream);
 // topk_w may be null: unit weights (the dispatch backward)
 hipError_t launch_combine(bool bf16, const void *y, const float *topk_w, const int32_t *assign_row, int64_t n,
                           int k, int64_t row_bytes, void *out, hipStream_t stream);

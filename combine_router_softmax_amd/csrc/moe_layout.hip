@@ -14,45 +14,117 @@
 //                   budget R
 //   assign_row[a] = offset[id[a]] + ordinal[a] if kept, else -1
 //
-// How (two launches, no host synchronisation, no atomics on the ordering
-// path, so the result does not depend on scheduling):
-//   1. layout_count: one workgroup per tile of 512 assignments builds an LDS
-//      histogram of the tile's ids -> tile_counts[tile][e] (a small matrix).
-//   2. layout_place: every workgroup reads the whole tile_counts matrix once (a
-//      single round of independent loads) and scans it in LDS: per expert, the
-//      sum over earlier tiles (this tile's base) and over all tiles (the
-//      expert's count); a block scan over experts gives the segment offsets.
-//      Then each wave walks its 64-assignment chunks of the tile in order;
-//      lanes holding the same expert find each other with one ballot per bit of
-//      the expert id (a wave64 "match"), rank = popcount(peers below the lane);
-//      the per-wave running count per expert lives in LDS and starts at the
-//      tile's base plus the counts of the earlier waves of the tile.  The same
-//      launch marks every row that receives no assignment (pad or tail), and
-//      workgroup 0 writes the counts, offsets and counters.
-// With a capacity and the drop-by-weight policy, layout_place lists every
-// assignment by expert instead of placing it, and capacity_select_kernel keeps
-// each expert's largest weights (see there).
-// Re-scanning the count matrix in every workgroup replaces a separate scan
-// launch: the matrix is tiles x E ints (64 x 256 for 4096 tokens, top-8, 256
-// experts), and a dependent kernel-to-kernel round trip costs more than
-// re-reading it.  Tiles of 512 assignments (one 64-assignment chunk per wave)
-// give 64 placing workgroups at that shape; 2048-assignment tiles (16
-// workgroups, four chunks per wave) measured 3 us slower.
+// How: one single-pass scan kernel, no host synchronisation.
+//   layout_scan: one workgroup per tile of 2048 assignments.  A workgroup takes
+//   its tile number from an atomic ticket, so every earlier tile belongs to a
+//   workgroup that is already running (or done) and waiting on it cannot
+//   deadlock.  It builds per-wave LDS histograms of its ids, publishes the
+//   tile's per-expert counts, then finds the counts of all earlier tiles by a
+//   decoupled look-back (Merrill and Garland, "Single-pass Parallel Prefix Scan
+//   with Decoupled Look-back", 2016): walking back over the earlier tiles'
+//   published words -- a tile's own count (AGG) or its inclusive prefix (INCL),
+//   which ends the walk -- sixteen words in flight per round.  It publishes its
+//   inclusive prefix, and ranks its assignments: lanes holding the same expert
+//   find each other with one ballot per bit of the expert id (a wave64 match),
+//   ordinal = earlier tiles + earlier waves + rank among the peers below.  The
+//   tile with the last ticket holds the totals and writes the counts, segment
+//   offsets and counters.  Ordinals never depend on atomic order: the tiles are
+//   scanned in assignment order whatever order they run in.
+//   Rows are then placed from (ordinal, kept, offset) alone (moe_place.hpp):
+//   by the scatter as it copies the rows, or by layout_finish where no scatter
+//   follows.
+// Status words are 64-bit: [63:34] the call's epoch, [33:32] the flag, [31:0]
+// the count, written and read with device-scope atomics, so one word carries
+// flag and value together.  The workspace header holds the ticket, a done
+// counter and the epoch; the last workgroup to finish resets ticket and done
+// and advances the epoch, so words left by an earlier call never look ready
+// and the workspace needs no clearing between calls -- only the header must be
+// zero before its first use.  A wait that runs past a bound (a header that was
+// not zeroed, two calls sharing one workspace) gives up, and the call reports
+// it with counters[3] = -1 instead of hanging.
+// With a capacity and the drop-by-weight policy, layout_finish lists every
+// assignment by expert and capacity_select_kernel keeps each expert's largest
+// weights (see there).
 #include "moe_device.hpp"
 #include "moe_kernels.hpp"
+#include "moe_place.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kLayoutThreads = 512;
-constexpr int kLayoutWaves = kLayoutThreads / kWave;
-constexpr int kChunksPerWave = kLayoutTile / kLayoutThreads;  // 64-assignment chunks per wave
-static_assert(kLayoutTile % kLayoutThreads == 0, "tile must be a multiple of the block");
+constexpr int kScanThreads = 512;
+constexpr int kScanWaves = kScanThreads / kWave;
+constexpr int kScanChunks = kLayoutTile / kScanThreads;  // 64-assignment chunks per wave
+static_assert(kLayoutTile % kScanThreads == 0, "tile must be a multiple of the block");
 constexpr int kMaxExperts = 1024;
+constexpr int kLookback = 16;                // status words in flight per thread and round
+constexpr uint32_t kSpinLimit = 1u << 17;    // polls of one word before giving up (~0.1 s)
+constexpr uint64_t kFlagAgg = 1, kFlagIncl = 2;
+constexpr uint32_t kEpochMask = 0x3FFFFFFFu;
 
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+struct ScanHeader {
+  uint32_t ticket;  // next tile number
+  uint32_t done;    // tiles finished
+  uint32_t epoch;   // tags this call's status words
+  uint32_t fault;   // a wait gave up
+};
+constexpr size_t kHeaderBytes = 256;
+
 __device__ __forceinline__ bool valid_id(int32_t x, int e) { return x >= 0 && x < e; }
+
+__global__ void fill_u32(uint32_t *p, int64_t n, uint32_t v) {
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) p[i] = v;
+}
+
+__device__ __forceinline__ uint64_t status_word(uint32_t epoch, uint64_t flag, uint32_t v) {
+  return ((uint64_t)(epoch & kEpochMask) << 34) | (flag << 32) | v;
+}
+__device__ __forceinline__ bool status_ready(uint64_t w, uint32_t epoch) {
+  return (uint32_t)(w >> 34) == (epoch & kEpochMask) && ((w >> 32) & 3u) != 0;
+}
+__device__ __forceinline__ uint64_t ld_status(const uint64_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_status(uint64_t *p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Poll a status word until it carries this call's epoch; past the bound, record
+// the fault and return an empty inclusive word (ends the walk).
+__device__ uint64_t wait_status(const uint64_t *p, uint32_t epoch, ScanHeader *hdr) {
+  for (uint32_t it = 0; it < kSpinLimit; ++it) {
+    const uint64_t w = ld_status(p);
+    if (status_ready(w, epoch)) return w;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  __hip_atomic_store(&hdr->fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return status_word(epoch, kFlagIncl, 0);
+}
+
+// Sum of bin x over the tiles before `tile`: walk back over their status words,
+// kLookback at a time, adding counts until an inclusive prefix.
+__device__ uint32_t look_back(const uint64_t *status, int64_t tile, int nbins, int x, uint32_t epoch, ScanHeader *hdr) {
+  uint32_t sum = 0;
+  for (int64_t p = tile - 1; p >= 0; p -= kLookback) {
+    uint64_t w[kLookback];
+#pragma unroll
+    for (int i = 0; i < kLookback; ++i) w[i] = p - i >= 0 ? ld_status(status + (p - i) * nbins + x) : 0ull;
+    bool stop = false;
+#pragma unroll
+    for (int i = 0; i < kLookback; ++i) {
+      if (!stop && p - i >= 0) {
+        uint64_t v = w[i];
+        if (!status_ready(v, epoch)) v = wait_status(status + (p - i) * nbins + x, epoch, hdr);
+        sum += (uint32_t)v;
+        stop = ((v >> 32) & 3u) == kFlagIncl;
+      }
+    }
+    if (stop) break;
+  }
+  return sum;
+}
 
 __device__ __forceinline__ int32_t wave_incl_scan(int32_t v) {
   const int l = lane_id();
@@ -72,8 +144,8 @@ __device__ __forceinline__ int32_t wave_sum_i32(int32_t v) {
 
 // Exclusive scan of in[0..n) (n <= 1024) into out[]; every thread of the block calls it.
 __device__ void block_exclusive_scan(const int32_t *in, int32_t *out, int n) {
-  __shared__ int32_t wave_tot[kLayoutWaves];
-  constexpr int kPer = kMaxExperts / kLayoutThreads;
+  __shared__ int32_t wave_tot[kScanWaves];
+  constexpr int kPer = kMaxExperts / kScanThreads;
   const int t = threadIdx.x;
   int32_t v[kPer];
   int32_t s = 0;
@@ -97,206 +169,84 @@ __device__ void block_exclusive_scan(const int32_t *in, int32_t *out, int n) {
   __syncthreads();
 }
 
-__global__ __launch_bounds__(kLayoutThreads) void layout_count(const int32_t *__restrict__ topk_idx, int64_t a_total,
-                                                               int e, int32_t *__restrict__ tile_counts,
-                                                               int32_t *__restrict__ tile_invalid) {
-  extern __shared__ int32_t cnt[];  // [e + 1], cnt[e] = invalid ids
-  for (int x = threadIdx.x; x <= e; x += kLayoutThreads) cnt[x] = 0;
-  __syncthreads();
-  const int64_t a0 = (int64_t)blockIdx.x * kLayoutTile;
-  int32_t ids[kChunksPerWave];
-#pragma unroll
-  for (int i = 0; i < kChunksPerWave; ++i) {
-    const int64_t a = a0 + threadIdx.x + i * kLayoutThreads;
-    ids[i] = a < a_total ? topk_idx[a] : -1;
-  }
-#pragma unroll
-  for (int i = 0; i < kChunksPerWave; ++i) {
-    if (valid_id(ids[i], e)) atomicAdd(&cnt[ids[i]], 1);
-    else if (ids[i] != -1) atomicAdd(&cnt[e], 1);
-  }
-  __syncthreads();
-  for (int x = threadIdx.x; x < e; x += kLayoutThreads) tile_counts[(int64_t)blockIdx.x * e + x] = cnt[x];
-  if (threadIdx.x == 0) tile_invalid[blockIdx.x] = cnt[e];
-}
-
-__global__ __launch_bounds__(kLayoutThreads) void layout_place(
-    const int32_t *__restrict__ topk_idx, const float *__restrict__ topk_w, int64_t a_total, int64_t tiles, int e,
-    int id_bits, int capacity, int row_align, int64_t rows, const int32_t *__restrict__ tile_counts,
-    const int32_t *__restrict__ tile_invalid, int32_t *__restrict__ full_list, int32_t *__restrict__ full_off,
-    int32_t *__restrict__ tokens_per_expert,
-    int32_t *__restrict__ expert_offsets, int32_t *__restrict__ counters, int32_t *__restrict__ ordinal,
-    int32_t *__restrict__ assign_row, int32_t *__restrict__ row_src, uint8_t *__restrict__ drop_mask,
-    uint8_t *__restrict__ pad_mask, float *__restrict__ w_perm) {
+// One workgroup per tile of kLayoutTile assignments (see the file comment).
+// Wave w owns the tile's assignments w*256 .. w*256+255, in four 64-wide
+// chunks; bin e (E + 1 bins) counts the invalid ids (neither -1 nor an expert).
+__global__ __launch_bounds__(kScanThreads) void layout_scan(
+    const int32_t *__restrict__ topk_idx, int64_t a_total, int64_t tiles, int e, int id_bits, int capacity,
+    int row_align, int64_t rows, ScanHeader *hdr, uint64_t *status, int32_t *__restrict__ ordinal,
+    int32_t *__restrict__ tokens_per_expert, int32_t *__restrict__ expert_offsets, int32_t *__restrict__ counters,
+    int32_t *__restrict__ full_off) {
   extern __shared__ int32_t sm[];
-  int32_t *run = sm;                      // [waves][e] running per-expert count of each wave
-  int32_t *off = run + kLayoutWaves * e;  // [e + 1] segment starts
-  int32_t *kept = off + e + 1;            // [e]
-  int32_t *base = kept + e;               // [e] this tile's base (counts of earlier tiles)
-  int32_t *total = base + e;              // [e] expert counts over all tiles
-  int32_t *full = total + e;              // [e + 1] (drop by weight) starts of the experts' full lists
-  __shared__ int32_t part[2][kLayoutThreads];
-  __shared__ int32_t red[3][kLayoutWaves];
+  const int nb = e + 1;
+  int32_t *run = sm;                  // [waves][nb] per-wave counts, then running bases
+  int32_t *agg = run + kScanWaves * nb;  // [nb] this tile's counts
+  int32_t *base = agg + nb;           // [nb] counts of the earlier tiles
+  int32_t *kept = base + nb;          // [e] (last tile)
+  int32_t *off = kept + e;            // [e + 1] (last tile)
+  __shared__ uint32_t sh_ticket, sh_epoch;
+  __shared__ int32_t red[3][kScanWaves];
   const int tid = threadIdx.x;
   const int w = tid / kWave;
   const int l = lane_id();
-  const int64_t tile = blockIdx.x;
 
-  // this tile's expert ids, loaded first so they arrive while the count matrix is read
-  const int64_t a_wave = tile * kLayoutTile + (int64_t)w * kChunksPerWave * kWave;
-  int32_t ids[kChunksPerWave];
-#pragma unroll
-  for (int c = 0; c < kChunksPerWave; ++c) {
-    const int64_t a = a_wave + c * kWave + l;
-    ids[c] = (tile < tiles && a < a_total) ? topk_idx[a] : -1;
+  if (tid == 0) {
+    sh_ticket = __hip_atomic_fetch_add(&hdr->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh_epoch = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-
-  // ---- per-expert sums over tiles: before this tile, and over all tiles
-  if (e <= kLayoutThreads) {
-    // thread (g, x): expert x, tiles g, g+G, g+2G, ...  (G groups of e threads)
-    const int groups = kLayoutThreads / e;
-    const int g = tid / e, x = tid % e;
-    if (g < groups) {
-      int32_t before = 0, all = 0;
-      for (int64_t t0 = g; t0 < tiles; t0 += 16 * (int64_t)groups) {
-        int32_t c[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          const int64_t t = t0 + (int64_t)u * groups;
-          c[u] = t < tiles ? tile_counts[t * e + x] : 0;
-        }
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          all += c[u];
-          if (t0 + (int64_t)u * groups < tile) before += c[u];
-        }
-      }
-      part[0][tid] = before;
-      part[1][tid] = all;
-    }
-    __syncthreads();
-    if (tid < e) {
-      int32_t b = 0, a = 0;
-      for (int gg = 0; gg < groups; ++gg) {
-        b += part[0][gg * e + tid];
-        a += part[1][gg * e + tid];
-      }
-      base[tid] = b;
-      total[tid] = a;
-    }
-  } else {
-    for (int x = tid; x < e; x += kLayoutThreads) {
-      int32_t before = 0, all = 0;
-      for (int64_t t0 = 0; t0 < tiles; t0 += 16) {
-        int32_t c[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) c[u] = t0 + u < tiles ? tile_counts[(t0 + u) * e + x] : 0;
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-          all += c[u];
-          if (t0 + u < tile) before += c[u];
-        }
-      }
-      base[x] = before;
-      total[x] = all;
-    }
-  }
+  for (int x = tid; x < kScanWaves * nb; x += kScanThreads) run[x] = 0;
   __syncthreads();
+  const int64_t tile = sh_ticket;
+  const uint32_t epoch = sh_epoch;
 
-  // drop by weight (full_list given): every assignment is listed, expert by
-  // expert in assignment order, for capacity_select_kernel to choose from
-  if (full_list) {
-    block_exclusive_scan(total, full, e);
-    if (tid == 0) full[e] = full[e - 1] + total[e - 1];
-    __syncthreads();
-    if (blockIdx.x == 0)
-      for (int x = tid; x <= e; x += kLayoutThreads) full_off[x] = full[x];
-  }
-
-  // ---- segment offsets and kept counts
-  if (capacity > 0) {
-    for (int x = tid; x < e; x += kLayoutThreads) {
-      off[x] = x * capacity;
-      kept[x] = total[x] < capacity ? total[x] : capacity;
-    }
-    if (tid == 0) off[e] = (int32_t)rows;
-    __syncthreads();
-  } else {
-    // segment lengths rounded up to the alignment (kept[] as scratch), their
-    // exclusive scan, then each start and kept count clipped to the budget
-    __shared__ int32_t used_end;
-    for (int x = tid; x < e; x += kLayoutThreads) kept[x] = (total[x] + row_align - 1) / row_align * row_align;
-    __syncthreads();
-    block_exclusive_scan(kept, off, e);
-    if (tid == 0) {
-      const int64_t end = (int64_t)off[e - 1] + kept[e - 1];
-      used_end = (int32_t)(end < rows ? end : rows);
-    }
-    __syncthreads();
-    for (int x = tid; x < e; x += kLayoutThreads) {
-      const int32_t s0 = off[x] < rows ? off[x] : (int32_t)rows;
-      const int64_t room = rows - s0;
-      kept[x] = (int32_t)(total[x] < room ? total[x] : room);
-      off[x] = s0;
-    }
-    if (tid == 0) off[e] = used_end;
-    __syncthreads();
-  }
-
-  if (blockIdx.x == 0) {  // the expert counts, offsets and counters
-    int32_t k_sum = 0, t_sum = 0, inv = 0;
-    for (int x = tid; x < e; x += kLayoutThreads) {
-      tokens_per_expert[x] = kept[x];
-      expert_offsets[x] = off[x];
-      k_sum += kept[x];
-      t_sum += total[x];
-    }
-    if (tid == 0) expert_offsets[e] = off[e];
-    for (int64_t t = tid; t < tiles; t += kLayoutThreads) inv += tile_invalid[t];
-    k_sum = wave_sum_i32(k_sum);
-    t_sum = wave_sum_i32(t_sum);
-    inv = wave_sum_i32(inv);
-    if (l == 0) {
-      red[0][w] = k_sum;
-      red[1][w] = t_sum;
-      red[2][w] = inv;
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int32_t ks = 0, ts = 0, is = 0;
-      for (int ww = 0; ww < kLayoutWaves; ++ww) {
-        ks += red[0][ww];
-        ts += red[1][ww];
-        is += red[2][ww];
-      }
-      counters[0] = ks;
-      counters[1] = ts - ks;
-      counters[2] = off[e] - ks;  // rows below the end of the last segment holding nothing: pads
-      counters[3] = is;
-    }
-  }
-
-  if (tile < tiles) {  // block-uniform
-    for (int x = tid; x < kLayoutWaves * e; x += kLayoutThreads) run[x] = 0;
-    __syncthreads();
+  if (tile < tiles) {  // block-uniform; a larger ticket only comes from a header that was not zeroed
+    const int64_t a_wave = tile * kLayoutTile + (int64_t)w * kScanChunks * kWave;
+    int32_t ids[kScanChunks];
 #pragma unroll
-    for (int c = 0; c < kChunksPerWave; ++c)
-      if (valid_id(ids[c], e)) atomicAdd(&run[w * e + ids[c]], 1);
+    for (int c = 0; c < kScanChunks; ++c) {
+      const int64_t a = a_wave + c * kWave + l;
+      ids[c] = a < a_total ? topk_idx[a] : -1;
+    }
+#pragma unroll
+    for (int c = 0; c < kScanChunks; ++c) {
+      if (valid_id(ids[c], e)) atomicAdd(&run[w * nb + ids[c]], 1);
+      else if (ids[c] != -1) atomicAdd(&run[w * nb + e], 1);
+    }
     __syncthreads();
-    // exclusive prefix over the waves of this tile, on top of the tile's base
-    for (int x = tid; x < e; x += kLayoutThreads) {
+
+    // this tile's counts, published at once (tile 0's are already inclusive)
+    uint64_t *mine = status + tile * nb;
+    for (int x = tid; x < nb; x += kScanThreads) {
+      int32_t s = 0;
+#pragma unroll
+      for (int ww = 0; ww < kScanWaves; ++ww) s += run[ww * nb + x];
+      agg[x] = s;
+      st_status(mine + x, status_word(epoch, tile == 0 ? kFlagIncl : kFlagAgg, (uint32_t)s));
+    }
+    // the earlier tiles' counts by look-back, then this tile's inclusive prefix
+    for (int x = tid; x < nb; x += kScanThreads) {
+      const int32_t b = tile == 0 ? 0 : (int32_t)look_back(status, tile, nb, x, epoch, hdr);
+      base[x] = b;
+      if (tile > 0) st_status(mine + x, status_word(epoch, kFlagIncl, (uint32_t)(b + agg[x])));
+    }
+    __syncthreads();
+
+    // running base of each wave: earlier tiles + earlier waves of this tile
+    for (int x = tid; x < e; x += kScanThreads) {
       int32_t b = base[x];
 #pragma unroll
-      for (int ww = 0; ww < kLayoutWaves; ++ww) {
-        const int32_t c = run[ww * e + x];
-        run[ww * e + x] = b;
+      for (int ww = 0; ww < kScanWaves; ++ww) {
+        const int32_t c = run[ww * nb + x];
+        run[ww * nb + x] = b;
         b += c;
       }
     }
     __syncthreads();
+
+    // stable ranks: chunks in order, peers found by a ballot per id bit
     const uint64_t below = lanes_below_mask();
 #pragma unroll
-    for (int c = 0; c < kChunksPerWave; ++c) {
+    for (int c = 0; c < kScanChunks; ++c) {
       const int64_t a = a_wave + c * kWave + l;
       const int32_t x = ids[c];
       const bool valid = valid_id(x, e);
@@ -308,51 +258,140 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_place(
       }
       if (valid) {
         const int rank = __popcll(peers & below);
-        const int32_t b = run[w * e + x];
-        if (rank == 0) run[w * e + x] = b + __popcll(peers);
-        const int32_t o = b + rank;
-        ordinal[a] = o;
-        if (full_list) {
-          full_list[full[x] + o] = (int32_t)a;  // kept or dropped: capacity_select_kernel decides
-        } else if (o < kept[x]) {
-          const int32_t r = off[x] + o;
-          assign_row[a] = r;
-          drop_mask[a] = 0;
-          row_src[r] = (int32_t)a;
-          pad_mask[r] = 0;
-          if (w_perm) w_perm[r] = topk_w[a];
-        } else {
-          assign_row[a] = -1;
-          drop_mask[a] = 1;
-        }
+        const int32_t b = run[w * nb + x];
+        if (rank == 0) run[w * nb + x] = b + __popcll(peers);
+        ordinal[a] = b + rank;
       } else if (a < a_total) {
         ordinal[a] = -1;
-        assign_row[a] = -1;
-        drop_mask[a] = 0;
       }
       __builtin_amdgcn_wave_barrier();
     }
+
+    if (tile == tiles - 1) {  // the totals: counts, segment offsets, counters
+      int32_t *total = agg;   // reused: total = base + this tile's count
+      __syncthreads();
+      for (int x = tid; x < nb; x += kScanThreads) total[x] += base[x];
+      __syncthreads();
+      if (full_off) {  // drop by weight: where each expert's list of assignments starts
+        block_exclusive_scan(total, off, e);
+        for (int x = tid; x < e; x += kScanThreads) full_off[x] = off[x];
+        if (tid == 0) full_off[e] = off[e - 1] + total[e - 1];
+        __syncthreads();
+      }
+      if (capacity > 0) {
+        for (int x = tid; x < e; x += kScanThreads) {
+          off[x] = x * capacity;
+          kept[x] = total[x] < capacity ? total[x] : capacity;
+        }
+        if (tid == 0) off[e] = (int32_t)rows;
+        __syncthreads();
+      } else {
+        // segment lengths rounded up to the alignment (kept[] as scratch), their
+        // exclusive scan, then each start and kept count clipped to the budget
+        __shared__ int32_t used_end;
+        for (int x = tid; x < e; x += kScanThreads) kept[x] = (total[x] + row_align - 1) / row_align * row_align;
+        __syncthreads();
+        block_exclusive_scan(kept, off, e);
+        if (tid == 0) {
+          const int64_t end = (int64_t)off[e - 1] + kept[e - 1];
+          used_end = (int32_t)(end < rows ? end : rows);
+        }
+        __syncthreads();
+        for (int x = tid; x < e; x += kScanThreads) {
+          const int32_t s0 = off[x] < rows ? off[x] : (int32_t)rows;
+          const int64_t room = rows - s0;
+          kept[x] = (int32_t)(total[x] < room ? total[x] : room);
+          off[x] = s0;
+        }
+        if (tid == 0) off[e] = used_end;
+        __syncthreads();
+      }
+      int32_t k_sum = 0, t_sum = 0;
+      for (int x = tid; x < e; x += kScanThreads) {
+        tokens_per_expert[x] = kept[x];
+        expert_offsets[x] = off[x];
+        k_sum += kept[x];
+        t_sum += total[x];
+      }
+      if (tid == 0) expert_offsets[e] = off[e];
+      k_sum = wave_sum_i32(k_sum);
+      t_sum = wave_sum_i32(t_sum);
+      if (l == 0) {
+        red[0][w] = k_sum;
+        red[1][w] = t_sum;
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int32_t ks = 0, ts = 0;
+        for (int ww = 0; ww < kScanWaves; ++ww) {
+          ks += red[0][ww];
+          ts += red[1][ww];
+        }
+        // device-scope stores: the last workgroup to finish may overwrite counters[3]
+        __hip_atomic_store(&counters[0], ks, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&counters[1], ts - ks, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&counters[2], off[e] - ks, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&counters[3], total[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  } else if (tid == 0) {
+    __hip_atomic_store(&hdr->fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // rows that receive no assignment: capacity or alignment pads and the unused
-  // dropless tail
-  for (int64_t r = (int64_t)blockIdx.x * kLayoutThreads + tid; r < rows; r += (int64_t)gridDim.x * kLayoutThreads) {
-    int x;
-    if (capacity > 0) {
-      x = (int)(r / capacity);
-    } else {  // last expert whose segment starts at or before r
-      int lo = 0, hi = e;  // off[lo] <= r always holds (off[0] == 0)
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (off[mid] <= r) lo = mid;
-        else hi = mid - 1;
-      }
-      x = lo;
+  // the last workgroup to finish leaves the header ready for the next call
+  __syncthreads();
+  if (tid == 0) {
+    const uint32_t d = __hip_atomic_fetch_add(&hdr->done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (d + 1 == (uint32_t)tiles) {
+      if (__hip_atomic_load(&hdr->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+        __hip_atomic_store(&counters[3], -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&hdr->fault, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&hdr->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&hdr->epoch, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (x < e && r - off[x] < kept[x]) continue;  // written by the assignment pass
-    row_src[r] = -1;
-    pad_mask[r] = 1;
-    if (w_perm) w_perm[r] = 0.0f;
+  }
+}
+
+// Placement where no scatter follows (the MXFP8 dispatch and the drop-by-weight
+// policy place rows in their own launch): blocks below `assign_blocks` take 256
+// assignments each, the others take the rows that no assignment fills.
+// list_full (drop by weight): valid assignments are listed by expert for
+// capacity_select_kernel instead of placed; their rows are written there.
+__global__ __launch_bounds__(256) void layout_finish(PlaceArgs p, int64_t a_total, int64_t assign_blocks,
+                                                     int32_t *__restrict__ full_list,
+                                                     const int32_t *__restrict__ full_off) {
+  __shared__ int32_t off_lds[kPlaceMaxExperts + 1];
+  const int64_t b = blockIdx.x;
+  if (b < assign_blocks) {
+    const int64_t a = b * 256 + threadIdx.x;
+    if (a >= a_total) return;
+    if (full_list) {
+      const int32_t x = p.topk_idx[a];
+      if (valid_id(x, p.e)) {
+        const int64_t i = (int64_t)full_off[x] + p.ordinal[a];
+        if (i >= 0 && i < a_total) full_list[i] = (int32_t)a;  // always, unless the scan gave up
+      } else {
+        p.assign_row[a] = -1;
+        p.drop_mask[a] = 0;
+      }
+      return;
+    }
+    bool dropped;
+    const int32_t r = placed_row(p, a, &dropped);
+    write_assignment(p, a, r, dropped);
+    return;
+  }
+  for (int x = threadIdx.x; x <= p.e; x += 256) off_lds[x] = p.off[x];
+  __syncthreads();
+  const int64_t used = used_rows(p, off_lds[p.e]);
+  const int64_t stride = (gridDim.x - assign_blocks) * 256;
+  for (int64_t r = (b - assign_blocks) * 256 + threadIdx.x + (p.has_pads ? 0 : used); r < p.rows; r += stride) {
+    if (r < used) {
+      const int x = segment_of(off_lds, p.e, p.capacity, r);
+      if (r - off_lds[x] < p.kept[x]) continue;  // a kept row: written by its assignment
+    }
+    write_empty_row(p, r);
   }
 }
 
@@ -400,7 +439,7 @@ __device__ __forceinline__ int32_t block_flag_scan(bool f, int32_t *wave_tot, in
 // keeps every key above the threshold and the first `need` keys equal to it.
 __global__ __launch_bounds__(kSelectThreads) void capacity_select_kernel(
     const int32_t *__restrict__ full_list, const int32_t *__restrict__ full_off, const float *__restrict__ topk_w,
-    int capacity, int32_t *__restrict__ assign_row, uint8_t *__restrict__ drop_mask, int32_t *__restrict__ row_src,
+    int64_t a_total, int capacity, int32_t *__restrict__ assign_row, uint8_t *__restrict__ drop_mask, int32_t *__restrict__ row_src,
     uint8_t *__restrict__ pad_mask, float *__restrict__ w_perm) {
   extern __shared__ uint32_t keys[];  // [kSelectLdsKeys]
   __shared__ uint32_t hist[256];
@@ -409,16 +448,28 @@ __global__ __launch_bounds__(kSelectThreads) void capacity_select_kernel(
   __shared__ int32_t wave_tot[kSelectWaves];
   const int x = blockIdx.x;
   const int tid = threadIdx.x;
-  const int32_t c0 = full_off[x];
-  const int32_t c = full_off[x + 1] - c0;
+  // list bounds and entries are checked, so that a scan that gave up (see
+  // layout_scan) cannot send a read or write outside the arrays
+  auto clamp_a = [&](int32_t v) { return v < 0 ? 0 : (v > a_total ? (int32_t)a_total : v); };
+  const int32_t c0 = clamp_a(full_off[x]);
+  const int32_t c1 = clamp_a(full_off[x + 1]);
+  const int32_t c = c1 > c0 ? c1 - c0 : 0;
   const int32_t *list = full_list + c0;
+  auto entry = [&](int32_t i) {
+    const int32_t a = list[i];
+    return a >= 0 && a < a_total ? a : -1;
+  };
+  auto key_at = [&](int32_t i) {
+    const int32_t a = entry(i);
+    return a >= 0 ? weight_key(topk_w[a]) : 0u;
+  };
   const bool select = c > capacity;
-  auto key_of = [&](int32_t i) { return i < kSelectLdsKeys ? keys[i] : weight_key(topk_w[list[i]]); };
+  auto key_of = [&](int32_t i) { return i < kSelectLdsKeys ? keys[i] : key_at(i); };
   uint32_t thr = 0;
   int32_t need = capacity;
   if (select) {
     const int32_t cached = c < kSelectLdsKeys ? c : kSelectLdsKeys;
-    for (int32_t i = tid; i < cached; i += kSelectThreads) keys[i] = weight_key(topk_w[list[i]]);
+    for (int32_t i = tid; i < cached; i += kSelectThreads) keys[i] = key_at(i);
     uint32_t prefix = 0, mask = 0;
     for (int shift = 24; shift >= 0; shift -= 8) {
       if (tid < 256) hist[tid] = 0;
@@ -457,8 +508,8 @@ __global__ __launch_bounds__(kSelectThreads) void capacity_select_kernel(
   int32_t run_tie = 0, run_keep = 0;
   for (int32_t b0 = 0; b0 < c; b0 += kSelectThreads) {
     const int32_t i = b0 + tid;
-    const bool valid = i < c;
-    const int32_t a = valid ? list[i] : -1;
+    const int32_t a = i < c ? entry(i) : -1;
+    const bool valid = a >= 0;
     const uint32_t kk = valid && select ? key_of(i) : 0u;
     const bool tie = valid && select && kk == thr;
     int32_t n_tie, n_keep;
@@ -485,10 +536,62 @@ __global__ __launch_bounds__(kSelectThreads) void capacity_select_kernel(
 
 size_t layout_workspace_bytes(int64_t assignments, int e, bool drop_by_weight) {
   const int64_t tiles = layout_tiles(assignments);
-  size_t b = align256(sizeof(int32_t) * (size_t)tiles * (size_t)e) + align256(sizeof(int32_t) * (size_t)tiles);
+  size_t b = kHeaderBytes + align256(sizeof(uint64_t) * (size_t)tiles * (size_t)(e + 1));
   if (drop_by_weight)  // every assignment listed by expert, and the list offsets
     b += align256(sizeof(int32_t) * (size_t)assignments) + align256(sizeof(int32_t) * (size_t)(e + 1));
   return b;
+}
+
+namespace {
+
+struct LayoutWorkspace {
+  ScanHeader *hdr;
+  uint64_t *status;
+  int32_t *full_list;  // drop by weight only
+  int32_t *full_off;
+};
+
+LayoutWorkspace carve(void *workspace, int64_t a_total, int e, bool by_weight) {
+  char *ws = static_cast<char *>(workspace);
+  LayoutWorkspace w{};
+  w.hdr = reinterpret_cast<ScanHeader *>(ws);
+  ws += kHeaderBytes;
+  w.status = reinterpret_cast<uint64_t *>(ws);
+  ws += align256(sizeof(uint64_t) * (size_t)layout_tiles(a_total) * (size_t)(e + 1));
+  if (by_weight) {
+    w.full_list = reinterpret_cast<int32_t *>(ws);
+    ws += align256(sizeof(int32_t) * (size_t)a_total);
+    w.full_off = reinterpret_cast<int32_t *>(ws);
+  }
+  return w;
+}
+
+hipError_t scan(const int32_t *topk_idx, int64_t a_total, int e, int capacity, int row_align, int64_t rows,
+                int32_t *tokens_per_expert, int32_t *expert_offsets, int32_t *ordinal, int32_t *counters,
+                const LayoutWorkspace &w, hipStream_t stream) {
+  const int64_t tiles = layout_tiles(a_total);
+  const int id_bits = e <= 1 ? 0 : 32 - __builtin_clz((unsigned)(e - 1));
+  const size_t lds = sizeof(int32_t) * ((size_t)(kScanWaves + 2) * (e + 1) + 2 * (size_t)e + 1);
+  hipLaunchKernelGGL(layout_scan, dim3((unsigned)tiles), dim3(kScanThreads), lds, stream, topk_idx, a_total, tiles, e,
+                     id_bits, capacity, row_align > 1 ? row_align : 1, rows, w.hdr, w.status, ordinal,
+                     tokens_per_expert, expert_offsets, counters, w.full_off);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t clear_layout_header(void *workspace, hipStream_t stream) {
+  hipLaunchKernelGGL(fill_u32, dim3(1), dim3(64), 0, stream, static_cast<uint32_t *>(workspace),
+                     (int64_t)(kHeaderBytes / 4), 0u);
+  return hipGetLastError();
+}
+
+hipError_t launch_layout_scan(const int32_t *topk_idx, int64_t n, int k, int e, int capacity, int row_align,
+                              int64_t rows, int32_t *tokens_per_expert, int32_t *expert_offsets, int32_t *ordinal,
+                              int32_t *counters, void *workspace, hipStream_t stream) {
+  const int64_t a_total = n * k;
+  return scan(topk_idx, a_total, e, capacity, row_align, rows, tokens_per_expert, expert_offsets, ordinal, counters,
+              carve(workspace, a_total, e, false), stream);
 }
 
 hipError_t launch_layout(const int32_t *topk_idx, const float *topk_w, int64_t n, int k, int e, int capacity,
@@ -497,39 +600,24 @@ hipError_t launch_layout(const int32_t *topk_idx, const float *topk_w, int64_t n
                          uint8_t *drop_mask, uint8_t *pad_mask, int32_t *counters, float *w_perm, void *workspace,
                          hipStream_t stream) {
   const int64_t a_total = n * k;
-  const int64_t tiles = layout_tiles(a_total);
-  char *ws = static_cast<char *>(workspace);
-  int32_t *tile_counts = reinterpret_cast<int32_t *>(ws);
-  ws += align256(sizeof(int32_t) * (size_t)tiles * (size_t)e);
-  int32_t *tile_invalid = reinterpret_cast<int32_t *>(ws);
-  ws += align256(sizeof(int32_t) * (size_t)tiles);
   const bool by_weight = drop_by_weight && capacity > 0;
-  int32_t *full_list = nullptr, *full_off = nullptr;
-  if (by_weight) {
-    full_list = reinterpret_cast<int32_t *>(ws);
-    ws += align256(sizeof(int32_t) * (size_t)a_total);
-    full_off = reinterpret_cast<int32_t *>(ws);
-  }
-  if (tiles > 0) {
-    hipLaunchKernelGGL(layout_count, dim3((unsigned)tiles), dim3(kLayoutThreads), sizeof(int32_t) * (e + 1), stream,
-                       topk_idx, a_total, e, tile_counts, tile_invalid);
-    hipError_t st = hipGetLastError();
-    if (st != hipSuccess) return st;
-  }
-  int64_t row_blocks = (rows + kLayoutThreads - 1) / kLayoutThreads;
+  const LayoutWorkspace w = carve(workspace, a_total, e, by_weight);
+  hipError_t st = scan(topk_idx, a_total, e, capacity, row_align, rows, tokens_per_expert, expert_offsets, ordinal,
+                       counters, w, stream);
+  if (st != hipSuccess) return st;
+  const PlaceArgs p = place_args(topk_idx, topk_w, ordinal, tokens_per_expert, expert_offsets, e, capacity,
+                                 row_align, rows, assign_row, drop_mask, row_src, pad_mask, w_perm);
+  const int64_t assign_blocks = (a_total + 255) / 256;
+  int64_t row_blocks = (rows + 255) / 256;
   if (row_blocks > 256) row_blocks = 256;
-  int64_t blocks = tiles > row_blocks ? tiles : row_blocks;
-  if (blocks == 0) blocks = 1;  // workgroup 0 still writes counts, offsets and counters
-  const int id_bits = e <= 1 ? 0 : 32 - __builtin_clz((unsigned)(e - 1));
-  const size_t lds = sizeof(int32_t) * ((size_t)kLayoutWaves * e + 5 * (size_t)e + 2);
-  hipLaunchKernelGGL(layout_place, dim3((unsigned)blocks), dim3(kLayoutThreads), lds, stream, topk_idx, topk_w,
-                     a_total, tiles, e, id_bits, capacity, row_align > 1 ? row_align : 1, rows, tile_counts,
-                     tile_invalid, full_list, full_off, tokens_per_expert, expert_offsets, counters, ordinal,
-                     assign_row, row_src, drop_mask, pad_mask, w_perm);
-  hipError_t st = hipGetLastError();
-  if (st != hipSuccess || !by_weight) return st;
+  if (assign_blocks + row_blocks > 0) {
+    hipLaunchKernelGGL(layout_finish, dim3((unsigned)(assign_blocks + row_blocks)), dim3(256), 0, stream, p, a_total,
+                       assign_blocks, by_weight ? w.full_list : nullptr, by_weight ? w.full_off : nullptr);
+    if ((st = hipGetLastError()) != hipSuccess) return st;
+  }
+  if (!by_weight) return hipSuccess;
   hipLaunchKernelGGL(capacity_select_kernel, dim3((unsigned)e), dim3(kSelectThreads),
-                     sizeof(uint32_t) * kSelectLdsKeys, stream, full_list, full_off, topk_w, capacity, assign_row,
+                     sizeof(uint32_t) * kSelectLdsKeys, stream, w.full_list, w.full_off, topk_w, a_total, capacity, assign_row,
                      drop_mask, row_src, pad_mask, w_perm);
   return hipGetLastError();
 }

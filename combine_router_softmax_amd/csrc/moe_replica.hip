@@ -155,16 +155,18 @@ hipError_t launch_replica_plan(const int32_t *counts, int e, int r, int32_t *rep
 
 // Workspace: a dropless layout of the logical ids (counts, offsets, ordinals,
 // rows, row sources, masks, counters) and that layout's own workspace.
+// The layout workspace comes first, so that its header (zero before first use)
+// is the reroute workspace's header.
 size_t reroute_workspace_bytes(int64_t a, int e) {
-  return 2 * align256(4 * (size_t)(e + 1)) + 3 * align256(4 * (size_t)a) + 2 * align256((size_t)a) + align256(16) +
-         layout_workspace_bytes(a, e, false);
+  return layout_workspace_bytes(a, e, false) + 2 * align256(4 * (size_t)(e + 1)) + align256(4 * (size_t)a) +
+         align256(16);
 }
 
 hipError_t launch_reroute(const int32_t *topk_idx, int64_t n, int k, int e, const int32_t *replica_of, int r,
                           int32_t *phys_idx, void *workspace, hipStream_t stream) {
   const int64_t a = n * k;
   if (a == 0) return hipSuccess;
-  char *w = static_cast<char *>(workspace);
+  char *w = static_cast<char *>(workspace) + layout_workspace_bytes(a, e, false);
   auto take = [&](size_t bytes) {
     char *p = w;
     w += align256(bytes);
@@ -173,13 +175,9 @@ hipError_t launch_reroute(const int32_t *topk_idx, int64_t n, int k, int e, cons
   int32_t *tpe = reinterpret_cast<int32_t *>(take(4 * (size_t)(e + 1)));
   int32_t *off = reinterpret_cast<int32_t *>(take(4 * (size_t)(e + 1)));
   int32_t *ord = reinterpret_cast<int32_t *>(take(4 * (size_t)a));
-  int32_t *row = reinterpret_cast<int32_t *>(take(4 * (size_t)a));
-  int32_t *src = reinterpret_cast<int32_t *>(take(4 * (size_t)a));
-  uint8_t *drop = reinterpret_cast<uint8_t *>(take((size_t)a));
-  uint8_t *pad = reinterpret_cast<uint8_t *>(take((size_t)a));
   int32_t *ctr = reinterpret_cast<int32_t *>(take(16));
-  hipError_t st = launch_layout(topk_idx, nullptr, n, k, e, 0, 0, false, a, tpe, off, ord, row, src, drop, pad, ctr,
-                                nullptr, w, stream);
+  // the layout scan alone gives the ordinals and counts of the logical ids
+  hipError_t st = launch_layout_scan(topk_idx, n, k, e, 0, 0, a, tpe, off, ord, ctr, workspace, stream);
   if (st != hipSuccess) return st;
   hipLaunchKernelGGL(reroute_kernel, dim3(grid_for(a, 4096)), dim3(kThreads), 0, stream, topk_idx, a, e, ord, tpe,
                      replica_of, r, phys_idx);

@@ -81,6 +81,73 @@ __global__ __launch_bounds__(kRowThreads) void scatter_kernel(const void *__rest
   }
 }
 
+// The rows no assignment fills, for the scatter that places rows: pad rows
+// (capacity or alignment, below the end of the last segment: zero data and
+// metadata, one row per block and step) and the unused tail past it (metadata
+// only, one row per thread).  Whether a row below the end is kept follows from
+// its segment's kept count alone (moe_place.hpp).
+__device__ __forceinline__ void place_empty_rows(const PlaceArgs &p, void *dst, int64_t row_bytes, int64_t pb,
+                                                 int64_t pad_blocks) {
+  __shared__ int32_t off_lds[kPlaceMaxExperts + 1];
+  __shared__ int32_t kept_lds[kPlaceMaxExperts];
+  for (int x = threadIdx.x; x <= p.e; x += kRowThreads) {
+    off_lds[x] = p.off[x];
+    if (x < p.e) kept_lds[x] = p.kept[x];
+  }
+  __syncthreads();
+  const int64_t used = used_rows(p, off_lds[p.e]);
+  if (p.has_pads) {
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    const int64_t vpr = row_bytes / 16;
+    for (int64_t r = pb; r < used; r += pad_blocks) {
+      const int x = segment_of(off_lds, p.e, p.capacity, r);
+      if (r - off_lds[x] < kept_lds[x]) continue;  // block-uniform: a kept row
+      char *d = row_ptr(dst, r, row_bytes);
+      for (int64_t v = threadIdx.x; v < vpr; v += kRowThreads) st16_stream(d + v * 16, z);
+      if (threadIdx.x == 0) write_empty_row(p, r);
+    }
+  }
+  for (int64_t r = used + pb * kRowThreads + threadIdx.x; r < p.rows; r += pad_blocks * kRowThreads)
+    write_empty_row(p, r);
+}
+
+// Scatter after the layout scan: token block t computes the row of each of its
+// slots from the scan's ordinal, the expert's kept count and segment start,
+// writes the slot's layout entries (assign_row, drop_mask, and for a kept slot
+// row_src, pad_mask, w_perm) and copies the token row to the kept rows.  Blocks
+// from n on write the rows no assignment fills.
+template <int KC>
+__global__ __launch_bounds__(kRowThreads) void scatter_place_kernel(const void *__restrict__ x, int64_t n, int k,
+                                                                    int64_t row_bytes, PlaceArgs p,
+                                                                    void *__restrict__ x_perm, int64_t pad_blocks) {
+  const int64_t b = blockIdx.x;
+  if (b >= n) {
+    place_empty_rows(p, x_perm, row_bytes, b - n, pad_blocks);
+    return;
+  }
+  const int64_t vpr = row_bytes / 16;
+  const char *src = row_ptr(x, b, row_bytes);
+  for (int j0 = 0; j0 < k; j0 += KC) {
+    int32_t rows[KC];
+#pragma unroll
+    for (int j = 0; j < KC; ++j) {
+      rows[j] = -1;
+      if (j0 + j < k) {
+        const int64_t a = b * k + j0 + j;
+        bool dropped;
+        rows[j] = placed_row(p, a, &dropped);
+        if (threadIdx.x == j) write_assignment(p, a, rows[j], dropped);
+      }
+    }
+    for (int64_t v = threadIdx.x; v < vpr; v += kRowThreads) {
+      const u32x4 val = ld16(src + v * 16);
+#pragma unroll
+      for (int j = 0; j < KC; ++j)
+        if (rows[j] >= 0) st16_stream(row_ptr(x_perm, rows[j], row_bytes) + v * 16, val);
+    }
+  }
+}
+
 template <bool BF16, int KC>
 __global__ __launch_bounds__(kRowThreads) void combine_kernel(const void *__restrict__ y, const float *__restrict__ topk_w,
                                                               const int32_t *__restrict__ assign_row, int64_t n, int k,
@@ -216,6 +283,27 @@ hipError_t launch_scatter(const void *x, int64_t n, int k, int64_t row_bytes, co
     case 4: hipLaunchKernelGGL(scatter_kernel<4>, grid, block, 0, stream, x, n, k, row_bytes, assign_row, x_perm, pad_rows, pad_limit, row_src, pb); break;
     default: hipLaunchKernelGGL(scatter_kernel<8>, grid, block, 0, stream, x, n, k, row_bytes, assign_row, x_perm, pad_rows, pad_limit, row_src, pb); break;
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_placing(const void *x, int64_t n, int k, int64_t row_bytes, const PlaceArgs &place,
+                                  void *x_perm, hipStream_t stream) {
+  // empty-row blocks: one per pad row up to kMaxPadBlocks with pads, else enough
+  // for one tail row per thread up to 256 blocks
+  int64_t pb = place.has_pads ? pad_block_count(place.rows) : (place.rows + kRowThreads - 1) / kRowThreads;
+  if (!place.has_pads && pb > 256) pb = 256;
+  const int64_t blocks = n + pb;
+  if (blocks == 0) return hipSuccess;
+  const dim3 grid((unsigned)blocks), block(kRowThreads);
+#define MOE_SCATTER_PLACE(KC) \
+  hipLaunchKernelGGL(scatter_place_kernel<KC>, grid, block, 0, stream, x, n, k, row_bytes, place, x_perm, pb)
+  switch (slot_chunk(k)) {
+    case 1: MOE_SCATTER_PLACE(1); break;
+    case 2: MOE_SCATTER_PLACE(2); break;
+    case 4: MOE_SCATTER_PLACE(4); break;
+    default: MOE_SCATTER_PLACE(8); break;
+  }
+#undef MOE_SCATTER_PLACE
   return hipGetLastError();
 }
 

@@ -315,9 +315,8 @@ def test_layer_step_replays_in_a_hip_graph(moe):
     y = torch.empty_like(xp)
     out = torch.empty_like(x)
     shape_d = moe.make_shape(n, h, e, k)
-    ws_d = torch.empty(moe.workspace_size(moe.MOE_OP_DISPATCH, shape_d) + 256, dtype=torch.uint8, device="cuda")
-    ws_f = torch.empty(moe.workspace_size(moe.MOE_OP_EXPERT_FFN, lay.shape(h, moe.MOE_DT_BF16, inter)) + 256,
-                       dtype=torch.uint8, device="cuda")
+    ws_d = moe.alloc_workspace(moe.MOE_OP_DISPATCH, shape_d, "cuda")
+    ws_f = moe.alloc_workspace(moe.MOE_OP_EXPERT_FFN, lay.shape(h, moe.MOE_DT_BF16, inter), "cuda")
 
     def step():
         moe.moe_route(logits, k, out=r)

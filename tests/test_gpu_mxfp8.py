@@ -284,14 +284,10 @@ def test_mxfp8_and_replicated_steps_replay_in_a_hip_graph(moe):
     xp, wp, lay = moe.moe_dispatch(x, phys, rt.topk_w, e + r_)
     y = torch.empty_like(xp)
     out = torch.empty_like(x)
-    ws_d = torch.empty(moe.workspace_size(moe.MOE_OP_DISPATCH, moe.make_shape(n, h, e + r_, k)) + 256,
-                       dtype=torch.uint8, device="cuda")
-    ws_8 = torch.empty(moe.workspace_size(moe.MOE_OP_EXPERT_FFN_MXFP8, lay8.shape(h, moe.MOE_DT_BF16, inter)) + 256,
-                       dtype=torch.uint8, device="cuda")
-    ws_f = torch.empty(moe.workspace_size(moe.MOE_OP_EXPERT_FFN, lay.shape(h, moe.MOE_DT_BF16, inter)) + 256,
-                       dtype=torch.uint8, device="cuda")
-    ws_r = torch.empty(moe.workspace_size(moe.MOE_OP_REROUTE, moe.make_shape(n, 1, e, k)) + 256, dtype=torch.uint8,
-                       device="cuda")
+    ws_d = moe.alloc_workspace(moe.MOE_OP_DISPATCH, moe.make_shape(n, h, e + r_, k), "cuda")
+    ws_8 = moe.alloc_workspace(moe.MOE_OP_EXPERT_FFN_MXFP8, lay8.shape(h, moe.MOE_DT_BF16, inter), "cuda")
+    ws_f = moe.alloc_workspace(moe.MOE_OP_EXPERT_FFN, lay.shape(h, moe.MOE_DT_BF16, inter), "cuda")
+    ws_r = moe.alloc_workspace(moe.MOE_OP_REROUTE, moe.make_shape(n, 1, e, k), "cuda")
 
     def step():
         moe.moe_route(logits, k, out=rt)
