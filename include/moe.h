@@ -132,7 +132,15 @@ typedef struct moe_layout {
 int64_t moe_layout_rows(const moe_shape *s);
 
 /* Bytes of device workspace `op` needs for shape `s` (0 is a valid answer).
- * Workspace must be 256-byte aligned; its contents need no initialisation. */
+ * Workspace must be 256-byte aligned.  The dispatch and reroute workspaces
+ * (MOE_OP_DISPATCH, MOE_OP_REROUTE) start with a 256-byte header, the state of
+ * the single-pass layout scan, which must be zero before the workspace is
+ * first used (zero-fill it once when it is allocated); every call leaves it
+ * zero again, so the workspace then serves any number of calls in stream
+ * order.  Two calls in flight at once must not share a workspace.  No other
+ * workspace needs initialisation.  A dispatch whose header was not zero does
+ * not hang or write outside its arrays: its scan gives up after a bounded wait
+ * and reports counters[3] = -1. */
 moe_status moe_workspace_size(moe_op op, const moe_shape *s, size_t *bytes);
 
 /* Router: the routing stage of MoELayer.forward ("Megatron MoE 实现",
