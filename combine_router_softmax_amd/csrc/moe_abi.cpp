@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <initializer_list>
+#include <mutex>
 
 #include "moe_kernels.hpp"
 
@@ -200,11 +201,13 @@ const int32_t *pad_limit_of(const moe_shape *s, const moe_layout *layout) {
 
 }  // namespace
 
-extern "C" {
+namespace {
 
-moe_status moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_idx, const float *topk_w,
-                        const moe_layout *layout, void *x_perm, float *w_perm, void *workspace,
-                        size_t workspace_bytes, void *stream) {
+// moe_dispatch with the workspace given (the caller's, or the no-allocation
+// entry point's static scratch).
+moe_status dispatch_impl(const moe_shape *s, const void *x, const int32_t *topk_idx, const float *topk_w,
+                         const moe_layout *layout, void *x_perm, float *w_perm, void *workspace,
+                         size_t workspace_bytes, void *stream) {
   moe_status st = check_shape(s);
   if (st != MOE_OK) return st;
   int64_t row_bytes, rows;
@@ -225,6 +228,55 @@ moe_status moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_i
   }
   return hip_status(moe::launch_scatter(x, s->n_tokens, s->top_k, row_bytes, layout->assign_row, x_perm,
                                         pad_rows_of(s, rows), pad_limit_of(s, layout), layout->row_src, hs));
+}
+
+// Scratch of moe_dispatch_noalloc: one array per GPU (each device holds its own
+// copy at its own address), kept until the process ends.  Host code never uses
+// the array's name as an address: the device address comes from
+// hipGetSymbolAddress, once per device, below.
+constexpr size_t kNoallocScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once known
+
+// The current device's scratch address; on the first call on a device, look it
+// up and zero the layout header at its start (the scan's state, which every
+// call leaves zero again), enqueued on `hs` ahead of the call's kernels.
+moe_status noalloc_scratch(hipStream_t hs, void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_ERR_HIP;
+    if (moe::clear_layout_header(ptr, hs) != hipSuccess) return MOE_ERR_HIP;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_idx, const float *topk_w,
+                        const moe_layout *layout, void *x_perm, float *w_perm, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+  return dispatch_impl(s, x, topk_idx, topk_w, layout, x_perm, w_perm, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_dispatch_noalloc(const moe_shape *s, const void *x, const int32_t *topk_idx, const float *topk_w,
+                                const moe_layout *layout, void *x_perm, float *w_perm, void *stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  if (moe::layout_workspace_bytes(s->n_tokens * s->top_k, s->n_experts, by_weight(s)) > kNoallocScratchBytes)
+    return MOE_ERR_WORKSPACE;  // more scratch than the static array holds
+  void *ws = nullptr;
+  if ((st = noalloc_scratch(as_stream(stream), &ws)) != MOE_OK) return st;
+  return dispatch_impl(s, x, topk_idx, topk_w, layout, x_perm, w_perm, ws, kNoallocScratchBytes, stream);
 }
 
 moe_status moe_dispatch_mxfp8(const moe_shape *s, const void *x, const int32_t *topk_idx, const float *topk_w,

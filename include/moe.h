@@ -5,6 +5,7 @@
  *   moe_route_random the same over random logits (force-balanced benchmark mode)
  *   moe_dispatch    per-expert histogram + prefix sum, stable per-expert ordinals,
  *                   capacity drop/pad masks, row scatter into expert-contiguous rows
+ *   moe_dispatch_noalloc the same with library-owned scratch (no workspace)
  *   moe_dispatch_mxfp8 the same, the permuted rows quantised to MXFP8 (E4M3 + E8M0)
  *   moe_expert_ffn  grouped SwiGLU expert GEMM (bf16 MFMA, fp32 accumulation)
  *   moe_expert_ffn_bwd backward of moe_expert_ffn (grads of rows and weights)
@@ -210,6 +211,27 @@ moe_status moe_route_random(const moe_shape *s, uint64_t seed, const float *expe
 moe_status moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_idx, const float *topk_w,
                         const moe_layout *layout, void *x_perm, float *w_perm, void *workspace,
                         size_t workspace_bytes, void *stream);
+
+/* Bytes of the static scratch of moe_dispatch_noalloc (per GPU). */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)
+
+/* moe_dispatch for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  It
+ * takes no workspace: its scratch is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES owned by the library, one per GPU it runs on, held
+ * until the process ends (found with hipGetSymbolAddress at the first call on
+ * a device, which also enqueues the clearing of its header on `stream`).  The
+ * call allocates nothing: no hipMalloc, no hipFree, no allocating library
+ * routine.  A shape whose dispatch workspace (moe_workspace_size with
+ * MOE_OP_DISPATCH) exceeds MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_WORKSPACE
+ * with nothing enqueued (8 MiB holds, for example, 2M assignments over 256
+ * experts, or 1M assignments dropped by weight).  Every call on a GPU shares that
+ * GPU's array, which keeps the last call's state: calls in stream order are
+ * fine, calls that overlap in time on one GPU (several streams or threads)
+ * race and must not be made.  Inputs, outputs, results and errors are
+ * moe_dispatch's. */
+moe_status moe_dispatch_noalloc(const moe_shape *s, const void *x, const int32_t *topk_idx, const float *topk_w,
+                                const moe_layout *layout, void *x_perm, float *w_perm, void *stream);
 
 /* MXFP8 dispatch: moe_dispatch with the permuted rows quantised to MXFP8 on the
  * way (the optional FP8 dispatch of the MORI token dispatcher, ROCm/Megatron-LM

@@ -26,7 +26,7 @@ def moe():
 
 def test_library_exports_every_declared_function(moe):
     declared = header_functions()
-    assert len(declared) == 21, declared
+    assert len(declared) == 22, declared
     assert sorted(moe.EXPORTS) == declared
     for name in declared:
         assert hasattr(moe.lib, name), name
@@ -84,6 +84,17 @@ def test_bad_shapes_are_rejected(moe, field, value, status):
     out = C.c_size_t(0)
     assert moe.lib.moe_workspace_size(moe.MOE_OP_DISPATCH, C.byref(s), C.byref(out)) == status
     assert moe.lib.moe_layout_rows(C.byref(s)) == -1
+
+
+def test_noalloc_dispatch_rejects_shapes_beyond_its_scratch(moe):
+    """moe_dispatch_noalloc checks its scratch need on the host, before any HIP call."""
+    s = moe.make_shape(5_000_000, 64, 256, 8)      # 40M assignments: far more status words than 8 MiB
+    p = C.c_void_p(4096)
+    lay = moe.MoeLayoutC(*([4096] * 8))
+    need = moe.workspace_size(moe.MOE_OP_DISPATCH, s)
+    assert need > 8 << 20
+    assert moe.lib.moe_dispatch_noalloc(C.byref(s), p, p, p, C.byref(lay), p, None, None) == -3
+    assert moe.lib.moe_dispatch_noalloc(None, p, p, p, C.byref(lay), p, None, None) == -1
 
 
 def test_validation_errors_enqueue_nothing(moe):
