@@ -223,7 +223,7 @@ moe_status dispatch_impl(const moe_shape *s, const void *x, const int32_t *topk_
     const moe::PlaceArgs p = moe::place_args(topk_idx, topk_w, layout->ordinal, layout->tokens_per_expert,
                                              layout->expert_offsets, s->n_experts, s->capacity, s->row_align, rows,
                                              layout->assign_row, layout->drop_mask, layout->row_src, layout->pad_mask,
-                                             w_perm);
+                                             w_perm, workspace, layout->counters);
     return hip_status(moe::launch_scatter_placing(x, s->n_tokens, s->top_k, row_bytes, p, x_perm, hs));
   }
   return hip_status(moe::launch_scatter(x, s->n_tokens, s->top_k, row_bytes, layout->assign_row, x_perm,

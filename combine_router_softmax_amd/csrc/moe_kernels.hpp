@@ -28,7 +28,8 @@ size_t layout_workspace_bytes(int64_t assignments, int e, bool drop_by_weight);
 // zero the header of a layout workspace (a kernel, so that it can be captured)
 hipError_t clear_layout_header(void *workspace, hipStream_t stream);
 // the scan alone: ordinal, tokens_per_expert, expert_offsets, counters; rows
-// are then placed by launch_scatter_placing (or not at all: the reroute)
+// are then placed by launch_scatter_placing (or not at all: the reroute).  The
+// next kernel of the call must run finish_scan on the workspace header.
 hipError_t launch_layout_scan(const int32_t *topk_idx, int64_t n, int k, int e, int capacity, int row_align,
                               int64_t rows, int32_t *tokens_per_expert, int32_t *expert_offsets, int32_t *ordinal,
                               int32_t *counters, void *workspace, hipStream_t stream);

@@ -35,13 +35,13 @@
 //   follows.
 // Status words are 64-bit: [63:34] the call's epoch, [33:32] the flag, [31:0]
 // the count, written and read with device-scope atomics, so one word carries
-// flag and value together.  The workspace header holds the ticket, a done
-// counter and the epoch; the last workgroup to finish resets ticket and done
-// and advances the epoch, so words left by an earlier call never look ready
-// and the workspace needs no clearing between calls -- only the header must be
-// zero before its first use.  A wait that runs past a bound (a header that was
-// not zeroed, two calls sharing one workspace) gives up, and the call reports
-// it with counters[3] = -1 instead of hanging.
+// flag and value together.  The workspace header holds the ticket and the
+// epoch; the kernel that follows the scan in the same call resets the ticket
+// and advances the epoch (finish_scan), so words left by an earlier call never
+// look ready and the workspace needs no clearing between calls -- only the
+// header must be zero before its first use.  A wait that runs past a bound (a
+// header that was not zeroed, two calls sharing one workspace) gives up, and
+// the call reports it with counters[3] = -1 instead of hanging.
 // With a capacity and the drop-by-weight policy, layout_finish lists every
 // assignment by expert and capacity_select_kernel keeps each expert's largest
 // weights (see there).
@@ -64,13 +64,7 @@ constexpr uint32_t kEpochMask = 0x3FFFFFFFu;
 
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
-struct ScanHeader {
-  uint32_t ticket;  // next tile number
-  uint32_t done;    // tiles finished
-  uint32_t epoch;   // tags this call's status words
-  uint32_t fault;   // a wait gave up
-};
-constexpr size_t kHeaderBytes = 256;
+constexpr size_t kHeaderBytes = 256;  // ScanHeader (moe_place.hpp), padded
 
 __device__ __forceinline__ bool valid_id(int32_t x, int e) { return x >= 0 && x < e; }
 
@@ -194,6 +188,15 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan(
     sh_ticket = __hip_atomic_fetch_add(&hdr->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     sh_epoch = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+  // the ids of tile blockIdx.x are requested while the ticket is on its way
+  // (tickets mostly follow dispatch order); another ticket reloads them
+  const int64_t guess = blockIdx.x;
+  int32_t ids[kScanChunks];
+#pragma unroll
+  for (int c = 0; c < kScanChunks; ++c) {
+    const int64_t a = guess * kLayoutTile + (int64_t)w * kScanChunks * kWave + c * kWave + l;
+    ids[c] = a < a_total ? topk_idx[a] : -1;
+  }
   for (int x = tid; x < kScanWaves * nb; x += kScanThreads) run[x] = 0;
   __syncthreads();
   const int64_t tile = sh_ticket;
@@ -201,11 +204,12 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan(
 
   if (tile < tiles) {  // block-uniform; a larger ticket only comes from a header that was not zeroed
     const int64_t a_wave = tile * kLayoutTile + (int64_t)w * kScanChunks * kWave;
-    int32_t ids[kScanChunks];
+    if (tile != guess) {
 #pragma unroll
-    for (int c = 0; c < kScanChunks; ++c) {
-      const int64_t a = a_wave + c * kWave + l;
-      ids[c] = a < a_total ? topk_idx[a] : -1;
+      for (int c = 0; c < kScanChunks; ++c) {
+        const int64_t a = a_wave + c * kWave + l;
+        ids[c] = a < a_total ? topk_idx[a] : -1;
+      }
     }
 #pragma unroll
     for (int c = 0; c < kScanChunks; ++c) {
@@ -327,30 +331,16 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan(
           ks += red[0][ww];
           ts += red[1][ww];
         }
-        // device-scope stores: the last workgroup to finish may overwrite counters[3]
-        __hip_atomic_store(&counters[0], ks, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&counters[1], ts - ks, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&counters[2], off[e] - ks, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&counters[3], total[e], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        counters[0] = ks;
+        counters[1] = ts - ks;
+        counters[2] = off[e] - ks;
+        counters[3] = total[e];
       }
     }
   } else if (tid == 0) {
     __hip_atomic_store(&hdr->fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-
-  // the last workgroup to finish leaves the header ready for the next call
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t d = __hip_atomic_fetch_add(&hdr->done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (d + 1 == (uint32_t)tiles) {
-      if (__hip_atomic_load(&hdr->fault, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
-        __hip_atomic_store(&counters[3], -1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&hdr->fault, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&hdr->ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&hdr->epoch, epoch + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&hdr->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  // the header is reset by the kernel that follows (finish_scan)
 }
 
 // Placement where no scatter follows (the MXFP8 dispatch and the drop-by-weight
@@ -363,6 +353,7 @@ __global__ __launch_bounds__(256) void layout_finish(PlaceArgs p, int64_t a_tota
                                                      const int32_t *__restrict__ full_off) {
   __shared__ int32_t off_lds[kPlaceMaxExperts + 1];
   const int64_t b = blockIdx.x;
+  if (b == 0 && threadIdx.x == 0) finish_scan(p.hdr, p.counters);
   if (b < assign_blocks) {
     const int64_t a = b * 256 + threadIdx.x;
     if (a >= a_total) return;
@@ -606,15 +597,15 @@ hipError_t launch_layout(const int32_t *topk_idx, const float *topk_w, int64_t n
                        counters, w, stream);
   if (st != hipSuccess) return st;
   const PlaceArgs p = place_args(topk_idx, topk_w, ordinal, tokens_per_expert, expert_offsets, e, capacity,
-                                 row_align, rows, assign_row, drop_mask, row_src, pad_mask, w_perm);
+                                 row_align, rows, assign_row, drop_mask, row_src, pad_mask, w_perm, workspace,
+                                 counters);
   const int64_t assign_blocks = (a_total + 255) / 256;
   int64_t row_blocks = (rows + 255) / 256;
   if (row_blocks > 256) row_blocks = 256;
-  if (assign_blocks + row_blocks > 0) {
-    hipLaunchKernelGGL(layout_finish, dim3((unsigned)(assign_blocks + row_blocks)), dim3(256), 0, stream, p, a_total,
-                       assign_blocks, by_weight ? w.full_list : nullptr, by_weight ? w.full_off : nullptr);
-    if ((st = hipGetLastError()) != hipSuccess) return st;
-  }
+  if (row_blocks < 1) row_blocks = 1;  // at least one block: it resets the scan header
+  hipLaunchKernelGGL(layout_finish, dim3((unsigned)(assign_blocks + row_blocks)), dim3(256), 0, stream, p, a_total,
+                     assign_blocks, by_weight ? w.full_list : nullptr, by_weight ? w.full_off : nullptr);
+  if ((st = hipGetLastError()) != hipSuccess) return st;
   if (!by_weight) return hipSuccess;
   hipLaunchKernelGGL(capacity_select_kernel, dim3((unsigned)e), dim3(kSelectThreads),
                      sizeof(uint32_t) * kSelectLdsKeys, stream, w.full_list, w.full_off, topk_w, a_total, capacity, assign_row,

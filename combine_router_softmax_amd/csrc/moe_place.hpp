@@ -21,6 +21,29 @@ namespace moe {
 
 constexpr int kPlaceMaxExperts = 1024;
 
+// State of the single-pass layout scan at the start of its workspace (256 bytes
+// reserved): the next tile ticket, the epoch that tags this call's status
+// words, and a flag set when a wait gave up.  Zero before the workspace's first
+// use; the kernel that follows the scan in the same call (it runs after the
+// scan has finished) reports a fault and resets the header with finish_scan.
+struct ScanHeader {
+  uint32_t ticket;
+  uint32_t epoch;
+  uint32_t fault;
+  uint32_t unused;
+};
+
+// One thread of the kernel that follows the scan: a fault becomes
+// counters[3] = -1; ticket and fault return to zero and the epoch advances,
+// so the status words of this call never look ready to the next one.
+__device__ __forceinline__ void finish_scan(ScanHeader *hdr, int32_t *counters) {
+  volatile ScanHeader *h = hdr;
+  if (h->fault) counters[3] = -1;
+  h->fault = 0;
+  h->ticket = 0;
+  h->epoch = h->epoch + 1;
+}
+
 struct PlaceArgs {
   const int32_t *topk_idx;  // [A]
   const float *topk_w;      // [A] (nullable when w_perm is null)
@@ -36,13 +59,18 @@ struct PlaceArgs {
   int32_t *row_src;         // [R]
   uint8_t *pad_mask;        // [R]
   float *w_perm;            // [R] (nullable)
+  ScanHeader *hdr;          // the scan's header, reset by the placing kernel
+  int32_t *counters;        // [4]
 };
 
+// `workspace`: the layout workspace, whose header the placing kernel resets.
 inline PlaceArgs place_args(const int32_t *topk_idx, const float *topk_w, const int32_t *ordinal, const int32_t *kept,
                             const int32_t *off, int e, int capacity, int row_align, int64_t rows, int32_t *assign_row,
-                            uint8_t *drop_mask, int32_t *row_src, uint8_t *pad_mask, float *w_perm) {
-  return PlaceArgs{topk_idx, topk_w,    ordinal, kept,    off,      e,      capacity, capacity > 0 || row_align > 1,
-                   rows,     assign_row, drop_mask, row_src, pad_mask, w_perm};
+                            uint8_t *drop_mask, int32_t *row_src, uint8_t *pad_mask, float *w_perm, void *workspace,
+                            int32_t *counters) {
+  return PlaceArgs{topk_idx, topk_w,    ordinal,   kept,    off,      e,      capacity,
+                   capacity > 0 || row_align > 1,       rows,    assign_row, drop_mask, row_src,
+                   pad_mask, w_perm,    static_cast<ScanHeader *>(workspace), counters};
 }
 
 // Row of assignment a, -1 if it is not placed (sentinel, invalid id, dropped).

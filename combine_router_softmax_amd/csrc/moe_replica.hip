@@ -72,8 +72,10 @@ __global__ __launch_bounds__(kThreads) void reroute_kernel(const int32_t *__rest
                                                            const int32_t *__restrict__ ordinal,
                                                            const int32_t *__restrict__ count,
                                                            const int32_t *__restrict__ replica_of, int r,
-                                                           int32_t *__restrict__ phys) {
+                                                           int32_t *__restrict__ phys, ScanHeader *hdr,
+                                                           int32_t *counters) {
   __shared__ int32_t slots[kMaxSlots];
+  if (blockIdx.x == 0 && threadIdx.x == 0) finish_scan(hdr, counters);  // the layout scan's header
   for (int i = threadIdx.x; i < r; i += kThreads) slots[i] = replica_of[i];
   __syncthreads();
   for (int64_t a = (int64_t)blockIdx.x * kThreads + threadIdx.x; a < a_n; a += (int64_t)gridDim.x * kThreads) {
@@ -180,7 +182,7 @@ hipError_t launch_reroute(const int32_t *topk_idx, int64_t n, int k, int e, cons
   hipError_t st = launch_layout_scan(topk_idx, n, k, e, 0, 0, a, tpe, off, ord, ctr, workspace, stream);
   if (st != hipSuccess) return st;
   hipLaunchKernelGGL(reroute_kernel, dim3(grid_for(a, 4096)), dim3(kThreads), 0, stream, topk_idx, a, e, ord, tpe,
-                     replica_of, r, phys_idx);
+                     replica_of, r, phys_idx, static_cast<ScanHeader *>(workspace), ctr);
   return hipGetLastError();
 }
 

@@ -31,6 +31,8 @@ namespace {
 
 constexpr int kRowThreads = 256;
 constexpr int kMaxPadBlocks = 2048;
+constexpr int kScatterAhead = 4;  // row segments per thread loaded ahead (a 14 KiB row at 256 threads)
+constexpr int kStageIters = (kPlaceMaxExperts + 1 + kRowThreads - 1) / kRowThreads;  // expert table per thread
 
 __device__ __forceinline__ char *row_ptr(void *base, int64_t row, int64_t row_bytes) {
   return static_cast<char *>(base) + row * row_bytes;
@@ -116,35 +118,127 @@ __device__ __forceinline__ void place_empty_rows(const PlaceArgs &p, void *dst, 
 // writes the slot's layout entries (assign_row, drop_mask, and for a kept slot
 // row_src, pad_mask, w_perm) and copies the token row to the kept rows.  Blocks
 // from n on write the rows no assignment fills.
+// Latency: the slot ids and ordinals (scalar loads) and the token row's leading
+// segments are requested together; the experts' kept counts and starts follow
+// as scalar loads, so the rows are known about when the row data arrives.  The
+// layout entries of a chunk of slots are one vector store per field from its
+// first lanes.
+// The read-only layout inputs are also passed as restrict-qualified pointers,
+// which lets the uniform ids, ordinals, kept counts and starts come through
+// scalar loads.
 template <int KC>
-__global__ __launch_bounds__(kRowThreads) void scatter_place_kernel(const void *__restrict__ x, int64_t n, int k,
-                                                                    int64_t row_bytes, PlaceArgs p,
-                                                                    void *__restrict__ x_perm, int64_t pad_blocks) {
+__global__ __launch_bounds__(kRowThreads) void scatter_place_kernel(
+    const void *__restrict__ x, int64_t n, int k, int64_t row_bytes, PlaceArgs p, const int32_t *__restrict__ topk_idx,
+    const int32_t *__restrict__ ordinal, const int32_t *__restrict__ kept, const int32_t *__restrict__ off,
+    const float *__restrict__ topk_w, int32_t *__restrict__ assign_row, uint8_t *__restrict__ drop_mask,
+    int32_t *__restrict__ row_src, uint8_t *__restrict__ pad_mask, float *__restrict__ w_perm,
+    void *__restrict__ x_perm, int64_t pad_blocks) {
   const int64_t b = blockIdx.x;
+  if (b == 0 && threadIdx.x == 0) finish_scan(p.hdr, p.counters);
   if (b >= n) {
     place_empty_rows(p, x_perm, row_bytes, b - n, pad_blocks);
     return;
   }
+  __shared__ int32_t off_lds[kPlaceMaxExperts + 1];
+  __shared__ int32_t kept_lds[kPlaceMaxExperts];
   const int64_t vpr = row_bytes / 16;
   const char *src = row_ptr(x, b, row_bytes);
-  for (int j0 = 0; j0 < k; j0 += KC) {
-    int32_t rows[KC];
-#pragma unroll
-    for (int j = 0; j < KC; ++j) {
-      rows[j] = -1;
-      if (j0 + j < k) {
-        const int64_t a = b * k + j0 + j;
-        bool dropped;
-        rows[j] = placed_row(p, a, &dropped);
-        if (threadIdx.x == j) write_assignment(p, a, rows[j], dropped);
+  const int lane = lane_id();
+  const uint32_t n_rows = (uint32_t)p.rows;  // R < 2^31 (checked on the host)
+  const float *w_src = w_perm ? topk_w : reinterpret_cast<const float *>(topk_idx);  // a valid address either way
+
+  // Lane j of every wave holds slot j0 + j.  Its id, ordinal and weight are
+  // requested first, then the expert's start and kept count; the layout
+  // entries are written by the first wave; the rows are made uniform with
+  // readlane.  Every address is clamped, so no branch separates the loads.
+  struct Slot {
+    int64_t a;
+    int32_t id, ord;
+    float w;
+  };
+  auto load_slot = [&](int j0) {
+    const int js = j0 + (lane < KC ? lane : 0);
+    Slot sl;
+    sl.a = b * k + (js < k ? js : k - 1);
+    sl.id = topk_idx[sl.a];
+    sl.ord = ordinal[sl.a];
+    sl.w = w_src[sl.a];
+    return sl;
+  };
+  auto place_slots = [&](int j0, const Slot &sl, int32_t (&rows)[KC]) {
+    const int js = j0 + lane;
+    const int32_t ex = sl.id < 0 ? 0 : (sl.id >= p.e ? p.e - 1 : sl.id);
+    const int32_t start = off_lds[ex];
+    const int32_t cap = kept_lds[ex];
+    const bool valid = (lane < KC) & (js < k) & (sl.id >= 0) & (sl.id < p.e);
+    const uint32_t r = (uint32_t)start + (uint32_t)sl.ord;
+    // checked against [0, R) too (see placed_row); an unsigned r >= R covers r < 0
+    const bool keep = valid & (sl.ord >= 0) & (sl.ord < cap) & (r < n_rows);
+    const int32_t my_row = keep ? (int32_t)r : -1;
+    if (threadIdx.x < KC && js < k) {
+      assign_row[sl.a] = my_row;
+      drop_mask[sl.a] = (valid & !keep) ? 1 : 0;
+      if (keep) {
+        row_src[r] = (int32_t)sl.a;
+        pad_mask[r] = 0;
+        if (w_perm) w_perm[r] = sl.w;
       }
     }
-    for (int64_t v = threadIdx.x; v < vpr; v += kRowThreads) {
+#pragma unroll
+    for (int j = 0; j < KC; ++j) rows[j] = __builtin_amdgcn_readlane(my_row, j);
+  };
+  auto copy_from = [&](int64_t v_first, const int32_t (&rows)[KC]) {
+    for (int64_t v = v_first; v < vpr; v += kRowThreads) {
       const u32x4 val = ld16(src + v * 16);
 #pragma unroll
       for (int j = 0; j < KC; ++j)
         if (rows[j] >= 0) st16_stream(row_ptr(x_perm, rows[j], row_bytes) + v * 16, val);
     }
+  };
+
+  // first chunk: the experts' starts and kept counts (into LDS), the slots and
+  // the row's leading segments are all requested at once: one memory round
+  // trip, then an LDS lookup, before the stores
+  {
+    int32_t st_v[kStageIters], kp_v[kStageIters];
+#pragma unroll
+    for (int i = 0; i < kStageIters; ++i) {
+      const int x_ = threadIdx.x + i * kRowThreads;
+      st_v[i] = off[x_ <= p.e ? x_ : p.e];
+      kp_v[i] = kept[x_ < p.e ? x_ : p.e - 1];
+    }
+    const Slot sl = load_slot(0);
+    u32x4 ahead[kScatterAhead];
+#pragma unroll
+    for (int i = 0; i < kScatterAhead; ++i) {
+      const int64_t v = threadIdx.x + (int64_t)i * kRowThreads;
+      ahead[i] = ld16(src + (v < vpr ? v : vpr - 1) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < kStageIters; ++i) {
+      const int x_ = threadIdx.x + i * kRowThreads;
+      if (x_ <= p.e) off_lds[x_] = st_v[i];
+      if (x_ < p.e) kept_lds[x_] = kp_v[i];
+    }
+    __syncthreads();
+    int32_t rows[KC];
+    place_slots(0, sl, rows);
+#pragma unroll
+    for (int i = 0; i < kScatterAhead; ++i) {
+      const int64_t v = threadIdx.x + (int64_t)i * kRowThreads;
+      if (v < vpr) {
+#pragma unroll
+        for (int j = 0; j < KC; ++j)
+          if (rows[j] >= 0) st16_stream(row_ptr(x_perm, rows[j], row_bytes) + v * 16, ahead[i]);
+      }
+    }
+    copy_from(threadIdx.x + (int64_t)kScatterAhead * kRowThreads, rows);
+  }
+  for (int j0 = KC; j0 < k; j0 += KC) {  // more than KC slots (the LDS stage stays)
+    const Slot sl = load_slot(j0);
+    int32_t rows[KC];
+    place_slots(j0, sl, rows);
+    copy_from(threadIdx.x, rows);
   }
 }
 
@@ -292,11 +386,13 @@ hipError_t launch_scatter_placing(const void *x, int64_t n, int k, int64_t row_b
   // for one tail row per thread up to 256 blocks
   int64_t pb = place.has_pads ? pad_block_count(place.rows) : (place.rows + kRowThreads - 1) / kRowThreads;
   if (!place.has_pads && pb > 256) pb = 256;
+  if (n + pb == 0) pb = 1;  // at least one block: block 0 resets the scan header
   const int64_t blocks = n + pb;
-  if (blocks == 0) return hipSuccess;
   const dim3 grid((unsigned)blocks), block(kRowThreads);
-#define MOE_SCATTER_PLACE(KC) \
-  hipLaunchKernelGGL(scatter_place_kernel<KC>, grid, block, 0, stream, x, n, k, row_bytes, place, x_perm, pb)
+#define MOE_SCATTER_PLACE(KC)                                                                                     \
+  hipLaunchKernelGGL(scatter_place_kernel<KC>, grid, block, 0, stream, x, n, k, row_bytes, place, place.topk_idx,     \
+                     place.ordinal, place.kept, place.off, place.topk_w, place.assign_row, place.drop_mask,           \
+                     place.row_src, place.pad_mask, place.w_perm, x_perm, pb)
   switch (slot_chunk(k)) {
     case 1: MOE_SCATTER_PLACE(1); break;
     case 2: MOE_SCATTER_PLACE(2); break;
