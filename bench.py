@@ -201,10 +201,12 @@ def bench_dispatch_combine(moe, mi, torch, steps, warmup, options=True):
     # cold dispatch + combine: one event pair around the two calls; the split
     # between them comes from a second pass with a marker in between
     def cold_pass(split):
+        # the flush is queued without a host synchronisation, so the host has
+        # enqueued the whole step before the GPU reaches it: the events time the
+        # GPU, not the host's launch latency
         res = []
         for _ in range(min(steps, 20)):
             flush.sum()
-            torch.cuda.synchronize()
             ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
             ev[0].record()
             route()
@@ -267,6 +269,121 @@ def bench_dispatch_combine(moe, mi, torch, steps, warmup, options=True):
                 dispatch_bytes=dispatch_bytes, combine_bytes=combine_bytes, bwd_ms=bwd_ms, bwd_bytes=bwd_bytes,
                 mx_ms=mx_ms, mx_bytes=mx_bytes,
                 n=n, k=k, e=e, h=h)
+
+
+def dispatch_combine_at(moe, mi, torch, wid, steps, warmup, flush):
+    """Dispatch -> combine (identity expert: the combine reads the dispatched rows) at
+    workload `wid`, warm (back-to-back pairs) and cold (each pair after a 1 GiB read,
+    queued without a host synchronisation) -> dict.  The tiny fp32 workload also
+    times its whole step (route -> dispatch -> combine), eagerly and as a replayed
+    HIP graph: it is bound by launch latency."""
+    import numpy as np
+    w = mi.workload(wid)
+    dev = torch.device("cuda")
+    xn = mi.activations(w)
+    x = torch.from_numpy(xn.view(np.int16)).cuda().view(torch.bfloat16) if xn.dtype == np.uint16 else \
+        torch.from_numpy(xn).cuda()
+    n, k, e, h = w.n_tokens, w.top_k, w.n_experts, w.hidden
+    if w.has_router:
+        logits = torch.from_numpy(mi.router_logits(w)).cuda()
+        r = moe.moe_route(logits, k)
+        idx, wts = r.topk_idx, r.topk_w
+    else:
+        idx_np, w_np = mi.received_routing(w)
+        idx, wts = torch.from_numpy(idx_np).cuda(), torch.from_numpy(w_np).cuda()
+    max_rows = w.rows if w.rows else 0
+    xp, wp, lay = moe.moe_dispatch(x, idx, wts, e, max_rows=max_rows)
+    ws = moe.alloc_workspace(moe.MOE_OP_DISPATCH, lay.shape(h, moe.MOE_DT_BF16 if x.dtype == torch.bfloat16 else
+                                                             moe.MOE_DT_F32), dev)
+    out = torch.empty_like(x)
+    disp = lambda: moe.moe_dispatch(x, idx, wts, e, max_rows=max_rows, layout=lay, x_perm=xp, w_perm_out=wp,
+                                    workspace=ws)
+    comb = lambda: moe.moe_combine(xp, wts, lay, out=out)
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def b2b_ms(fns, reps):
+        for _ in range(warmup):
+            for f in fns: f()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(reps):
+            for f in fns: f()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / reps
+
+    batch = max(1, steps // 10)
+    warm = sorted(b2b_ms([disp, comb], batch) for _ in range(10))
+    cold = []
+    for _ in range(20):
+        flush.sum()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        disp()
+        comb()
+        b.record()
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    cold.sort()
+    kept = int(lay.counters[0].item())
+    eb = x.element_size()
+    res = dict(workload=w.name, warm_ms=warm[5], cold_ms=cold[10], cold_p10=cold[2], cold_p90=cold[18],
+               dispatch_bytes=(n + kept) * h * eb, combine_bytes=(kept + n) * h * eb, kept=kept)
+    if wid == 1:
+        step = lambda: (moe.moe_route(logits, k, out=r), disp(), comb())
+        res["step_ms"] = b2b_ms([step], steps)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        res["graph_step_ms"] = b2b_ms([graph.replay], steps)
+        del graph
+    if w.backward:   # combine backward on this layout
+        go = torch.from_numpy(mi.grad_output(w).view(np.int16)).cuda().view(torch.bfloat16)
+        gy = torch.empty_like(xp)
+        gw = torch.empty((n, k), dtype=torch.float32, device=dev)
+        cb = lambda: moe.moe_combine_bwd(go, xp, wts, lay, grad_y=gy, grad_w=gw)
+        res["combine_bwd_ms"] = b2b_ms([cb], steps)
+        cbc = []
+        for _ in range(20):
+            flush.sum()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            cb()
+            b.record()
+            torch.cuda.synchronize()
+            cbc.append(a.elapsed_time(b))
+        res["combine_bwd_cold_ms"] = sorted(cbc)[10]
+        res["combine_bwd_bytes"] = (n + 2 * kept) * h * eb
+    return res
+
+
+def bench_layout_sizes(moe, torch, steps, warmup, sizes=(4096, 32768, 65536)):
+    """moe_build_layout (the single-pass scan and the row placement, no row copy) at
+    N tokens, 256 experts, top-8 over force-balanced random routing -> {N: us}."""
+    dev = torch.device("cuda")
+    res = {}
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for n in sizes:
+        r = moe.moe_route_random(n, 256, 8, 31 + n, device=dev)
+        wp, lay = moe.moe_build_layout(r.topk_idx, r.topk_w, 256)
+        ws = moe.alloc_workspace(moe.MOE_OP_DISPATCH, lay.shape(8, moe.MOE_DT_BF16), dev)
+        run = lambda: moe.moe_build_layout(r.topk_idx, r.topk_w, 256, layout=lay, w_perm_out=wp, workspace=ws)
+        for _ in range(warmup):
+            run()
+        torch.cuda.synchronize()
+        t0.record()
+        for _ in range(steps):
+            run()
+        t1.record()
+        torch.cuda.synchronize()
+        res[n] = t0.elapsed_time(t1) / steps * 1e3
+    return res
 
 
 def bench_skewed_capacity(moe, mi, torch, steps, warmup):
@@ -572,36 +689,134 @@ def power_pass():
     phase("combine_uniform", lambda: moe.moe_combine(xp2, r2.topk_w, lay2, out=out2), 5)
 
 
-def cpu_baseline(mi, min_seconds=10.0):
-    """The oracle on the host, single thread: full uniform-workload steps (route,
-    layout, scatter, combine) repeated until at least min_seconds have passed."""
+def host_cpu():
+    """(threads this process may run, host CPU model name)."""
+    n = len(os.sched_getaffinity(0))
+    omp = os.environ.get("OMP_NUM_THREADS")
+    if omp and omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return n, model
+
+
+def cpu_baseline(mi, min_seconds=8.0):
+    """The oracle as it stands on the host, on full uniform-workload steps (route,
+    layout, scatter, combine): one step on one thread, then steps on every thread
+    the process may run until min_seconds have passed -- route, scatter and combine
+    split over token ranges (tokens are independent, so no per-token arithmetic is
+    reordered), the layout's counting sort whole (it is sequential).  The combine
+    backward of the same shape is timed once each way beside it."""
+    from concurrent.futures import ThreadPoolExecutor
+    import numpy as np
     import oracle
+    threads, model = host_cpu()
+    lib = oracle.lib()
+    p = oracle._p
     w = mi.workload(2)
+    n, k, e, h = w.n_tokens, w.top_k, w.n_experts, w.hidden
     logits = mi.router_logits(w)
     x = mi.activations(w)
-    parts = [0.0, 0.0, 0.0]
-    steps = 0
-    kept = 0
+    go = mi.grad_output(w)
+    row_b = h * 2
+    ranges = [(n * i // threads, n * (i + 1) // threads) for i in range(threads)]
+    pool = ThreadPoolExecutor(threads)
+
+    def par(fn):
+        return list(pool.map(lambda r: fn(*r), ranges))
+
+    def step(parallel):
+        t = [time.perf_counter()]
+        if parallel:
+            parts = par(lambda a, b: oracle.route(logits[a:b], k)[:2])
+            idx = np.concatenate([q[0] for q in parts])
+            wts = np.concatenate([q[1] for q in parts])
+        else:
+            idx, wts, _, _ = oracle.route(logits, k)
+        t.append(time.perf_counter())
+        lay = oracle.layout(idx, e)
+        t.append(time.perf_counter())
+        rows = lay["rows"]
+        xp = np.empty((rows, h), np.uint16)
+        ar = lay["assign_row"]
+        if parallel:   # rows of distinct tokens never overlap; no pads in a dropless layout
+            par(lambda a, b: lib.oracle_scatter(b - a, k, row_b, p(x[a:b]), p(ar[a * k:b * k]), p(wts[a:b]), 0,
+                                                None, 0, p(xp), None))
+        else:
+            oracle.scatter(x, k, lay, wts, x_perm=xp)
+        t.append(time.perf_counter())
+        out = np.empty((n, h), np.uint16)
+        if parallel:
+            par(lambda a, b: lib.oracle_combine(b - a, k, h, oracle.DT_BF16, p(xp), p(wts[a:b]), p(ar[a * k:b * k]),
+                                                p(out[a:b])))
+        else:
+            out = oracle.combine(xp, wts, lay, n, k)
+        t.append(time.perf_counter())
+        return np.diff(t), lay, xp, wts
+
+    one, lay, xp, wts = step(False)
+    kept = int(lay["counters"][0])
+    byts = (n + kept) * row_b * 2
+    steps, tot = 0, np.zeros(4)
     start = time.perf_counter()
     while steps == 0 or time.perf_counter() - start < min_seconds:
-        t0 = time.perf_counter()
-        idx, wts, _, _ = oracle.route(logits, w.top_k)
-        t1 = time.perf_counter()
-        lay = oracle.layout(idx, w.n_experts)
-        xp, _ = oracle.scatter(x, w.top_k, lay, wts)
-        t2 = time.perf_counter()
-        oracle.combine(xp, wts, lay, w.n_tokens, w.top_k)
-        t3 = time.perf_counter()
-        parts = [parts[0] + t1 - t0, parts[1] + t2 - t1, parts[2] + t3 - t2]
-        kept = int(lay["counters"][0])
+        d, _, _, _ = step(True)
+        tot += d
         steps += 1
-    row_b = w.hidden * 2
-    byts = (w.n_tokens + kept) * row_b * 2
-    per_step = sum(parts) / steps
-    return dict(value=byts / per_step / 1e9, unit="GB/s", cores=1, kind="oracle",
-                sample=f"{steps} full steps (route+layout+scatter+combine) of the uniform workload, single thread, "
-                       f"{sum(parts):.1f} s in all; per step: route {1e3 * parts[0] / steps:.0f} ms, "
-                       f"dispatch {1e3 * parts[1] / steps:.0f} ms, combine {1e3 * parts[2] / steps:.0f} ms")
+    per = tot / steps
+    # combine backward: read g and the kept rows, write grad_y, grad_w (double accumulation)
+    ar = lay["assign_row"]
+    gy = np.empty_like(xp)
+    gw = np.empty((n, k), np.float32)
+    t0 = time.perf_counter()
+    lib.oracle_combine_bwd(n, k, h, oracle.DT_BF16, p(go), p(xp), p(wts), p(ar), 0, None, 0, p(gy), p(gw))
+    t1 = time.perf_counter()
+    par(lambda a, b: lib.oracle_combine_bwd(b - a, k, h, oracle.DT_BF16, p(go[a:b]), p(xp), p(wts[a:b]),
+                                            p(ar[a * k:b * k]), 0, None, 0, p(gy), p(gw[a:b])))
+    t2 = time.perf_counter()
+    pool.shutdown()
+    bwd_bytes = (n + 2 * kept) * row_b
+    ms = lambda v: f"{1e3 * v:.0f} ms"
+    return dict(value=round(byts / per.sum() / 1e9, 3), unit="GB/s", cores=threads, kind="oracle",
+                cpu_model=model, nproc=os.cpu_count(),
+                single_thread_gbs=round(byts / one.sum() / 1e9, 3),
+                combine_bwd_gbs=round(bwd_bytes / (t2 - t1) / 1e9, 3),
+                combine_bwd_single_thread_gbs=round(bwd_bytes / (t1 - t0) / 1e9, 3),
+                sample=f"uniform workload (4096 tokens, hidden 7168, 256 experts, top-8, bf16), full steps of "
+                       f"route + layout + scatter + combine: {steps} steps on {threads} threads "
+                       f"(per step: route {ms(per[0])}, layout {ms(per[1])} on one thread, scatter {ms(per[2])}, "
+                       f"combine {ms(per[3])}), and one step on one thread (route {ms(one[0])}, layout "
+                       f"{ms(one[1])}, scatter {ms(one[2])}, combine {ms(one[3])}); combine backward once each "
+                       f"way ({ms(t2 - t1)} on {threads} threads, {ms(t1 - t0)} on one)")
+
+
+def config_entry(o):
+    """The bench line's entry for one of the other workloads' dispatch -> combine."""
+    byts = o["dispatch_bytes"] + o["combine_bytes"]
+    gbs = lambda ms: round(byts / (ms * 1e-3) / 1e9, 1)
+    d = {"dispatch_combine_us": round(o["warm_ms"] * 1e3, 2), "dispatch_combine_gbs": gbs(o["warm_ms"]),
+         "frac_hbm_peak": round(byts / (o["warm_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+         "cold_us": round(o["cold_ms"] * 1e3, 2), "cold_p10_p90_us": [round(o["cold_p10"] * 1e3, 2),
+                                                                      round(o["cold_p90"] * 1e3, 2)],
+         "cold_gbs": gbs(o["cold_ms"]), "cold_frac_hbm_peak": round(byts / (o["cold_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+         "bytes": byts, "kept_rows": o["kept"]}
+    if "step_ms" in o:
+        d["step_us"] = round(o["step_ms"] * 1e3, 2)
+        d["graph_step_us"] = round(o["graph_step_ms"] * 1e3, 2)
+    if "combine_bwd_ms" in o:
+        b = o["combine_bwd_bytes"]
+        d["combine_bwd_us"] = round(o["combine_bwd_ms"] * 1e3, 2)
+        d["combine_bwd_gbs"] = round(b / (o["combine_bwd_ms"] * 1e-3) / 1e9, 1)
+        d["combine_bwd_frac_hbm_peak"] = round(b / (o["combine_bwd_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)
+        d["combine_bwd_cold_us"] = round(o["combine_bwd_cold_ms"] * 1e3, 2)
+        d["combine_bwd_bytes"] = b
+    return d
 
 
 def main():
@@ -648,6 +863,14 @@ def main():
     dc = bench_dispatch_combine(moe, mi, torch, args.steps, args.warmup)
     log("dispatch+combine: Zipf-skewed workload with capacity 160, both drop policies")
     skew = bench_skewed_capacity(moe, mi, torch, 20, 3)
+    flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    other = {}
+    for wid in (1, 4, 5):
+        log(f"dispatch+combine: workload {mi.workload(wid).name}")
+        other[wid] = dispatch_combine_at(moe, mi, torch, wid, min(args.steps, 100), 5, flush)
+    del flush
+    log("layout alone at 4096 / 32768 / 65536 tokens")
+    layout_us = bench_layout_sizes(moe, torch, min(args.steps, 100), 5)
     gemm = []
     if not args.skip_gemm:
         for wid in (4, 5):
@@ -741,6 +964,8 @@ def main():
                          **({"replication": {k_: (round(v, 2) if isinstance(v, float) else v)
                                              for k_, v in g["replication"].items()}} if "replication" in g else {})}
                         for g in gemm],
+        "configs": {o["workload"]: config_entry(o) for o in other.values()},
+        "layout_us": {f"N{n_}_E256_k8": round(v, 2) for n_, v in layout_us.items()},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

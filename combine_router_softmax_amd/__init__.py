@@ -27,7 +27,7 @@ MOE_DROP_POSITION, MOE_DROP_PROBS = 0, 1
 
 # Every symbol include/moe.h declares.
 EXPORTS = ("moe_layout_rows", "moe_workspace_size", "moe_route", "moe_route_random", "moe_dispatch",
-           "moe_dispatch_noalloc",
+           "moe_dispatch_noalloc", "moe_build_layout",
            "moe_dispatch_mxfp8", "moe_expert_ffn",
            "moe_expert_ffn_bwd", "moe_combine", "moe_dispatch_bwd", "moe_combine_bwd", "moe_status_string",
            "moe_version", "moe_replica_plan", "moe_reroute", "moe_replica_sync", "moe_replica_grad_reduce",
@@ -64,6 +64,7 @@ def _load():
     lib.moe_route_random.argtypes = [sp, C.c_uint64, p, p, p, p, p, p, p]
     lib.moe_dispatch.argtypes = [sp, p, p, p, lp, p, p, p, C.c_size_t, p]
     lib.moe_dispatch_noalloc.argtypes = [sp, p, p, p, lp, p, p, p]
+    lib.moe_build_layout.argtypes = [sp, p, p, lp, p, p, C.c_size_t, p]
     lib.moe_dispatch_mxfp8.argtypes = [sp, p, p, p, lp, p, p, p, p, C.c_size_t, p]
     lib.moe_expert_ffn.argtypes = [sp, p, lp, p, p, p, p, p, C.c_size_t, p]
     lib.moe_expert_ffn_bwd.argtypes = [sp, p, p, p, lp, p, p, p, p, p, p, C.c_size_t, p]
@@ -78,7 +79,7 @@ def _load():
     lib.moe_replica_grad_reduce.argtypes = [sp, p, i32, p, p, p, p, p]
     lib.moe_expert_ffn_replicas.argtypes = [sp, i32, p, lp, p, p, p, p, p, p, p, C.c_size_t, p]
     lib.moe_expert_ffn_bwd_replicas.argtypes = [sp, i32, p, p, p, lp, p, p, p, p, p, p, p, p, p, p, C.c_size_t, p]
-    for f in ("moe_workspace_size", "moe_route", "moe_route_random", "moe_dispatch", "moe_dispatch_noalloc", "moe_dispatch_mxfp8", "moe_expert_ffn", "moe_expert_ffn_bwd", "moe_combine",
+    for f in ("moe_workspace_size", "moe_route", "moe_route_random", "moe_dispatch", "moe_dispatch_noalloc", "moe_build_layout", "moe_dispatch_mxfp8", "moe_expert_ffn", "moe_expert_ffn_bwd", "moe_combine",
               "moe_combine_bwd", "moe_dispatch_bwd", "moe_replica_plan", "moe_reroute", "moe_replica_sync",
               "moe_replica_grad_reduce", "moe_expert_ffn_replicas", "moe_expert_ffn_bwd_replicas", "moe_mx_quantize",
               "moe_expert_ffn_mxfp8"):
@@ -301,6 +302,34 @@ def moe_dispatch(x: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor |
     _check(lib.moe_dispatch(C.byref(shape), _ptr(x), _ptr(topk_idx), _ptr(topk_w), C.byref(lc), _ptr(x_perm),
                             _ptr(w_perm_out if w_perm else None), _ws_ptr(ws), nbytes, _stream(dev)), "moe_dispatch")
     return x_perm, (w_perm_out if w_perm else None), layout
+
+
+def moe_build_layout(topk_idx: torch.Tensor, topk_w: torch.Tensor | None, n_experts: int, *, hidden: int = 8,
+                     act_dtype: int = MOE_DT_BF16, capacity: int = 0, max_rows: int = 0, row_align: int = 0,
+                     drop_policy: int = MOE_DROP_POSITION, w_perm: bool = True, layout: Layout | None = None,
+                     w_perm_out: torch.Tensor | None = None, workspace=None):
+    """The dispatch layout without the row copy (include/moe.h moe_build_layout) -> (w_perm, layout).
+    hidden / act_dtype only enter the shape checks (no activations are read)."""
+    _contig(topk_idx, "topk_idx")
+    n, k = topk_idx.shape
+    dev = topk_idx.device
+    shape = make_shape(n, hidden, n_experts, k, capacity, 0, max_rows, act_dtype, row_align, drop_policy)
+    rows = int(lib.moe_layout_rows(C.byref(shape)))
+    if rows < 0:
+        _check(-1, "moe_build_layout")
+    if layout is None:
+        layout = Layout.empty(n, k, n_experts, capacity, rows, dev, row_align, drop_policy)
+    if w_perm and w_perm_out is None:
+        w_perm_out = torch.empty(rows, dtype=torch.float32, device=dev)
+    if workspace is None:
+        ws, nbytes = _workspace(MOE_OP_DISPATCH, shape, dev)
+    else:
+        ws, nbytes = workspace, workspace.numel() - 256
+    lc = layout.c()
+    _check(lib.moe_build_layout(C.byref(shape), _ptr(topk_idx), _ptr(topk_w), C.byref(lc),
+                                _ptr(w_perm_out if w_perm else None), _ws_ptr(ws), nbytes, _stream(dev)),
+           "moe_build_layout")
+    return (w_perm_out if w_perm else None), layout
 
 
 def moe_dispatch_noalloc(x: torch.Tensor, topk_idx: torch.Tensor, topk_w: torch.Tensor | None, n_experts: int, *,

@@ -168,12 +168,13 @@ namespace {
 moe_status dispatch_layout(const moe_shape *s, int64_t rows, const void *x, const int32_t *topk_idx,
                            const float *topk_w, const moe_layout *layout, std::initializer_list<const void *> outs,
                            float *w_perm, void *workspace, size_t workspace_bytes, hipStream_t hs,
-                           bool place_in_scatter) {
+                           bool place_in_scatter, bool needs_x = true) {
   if (!layout) return MOE_ERR_INVALID_ARG;
   const int64_t n = s->n_tokens, a = n * s->top_k;
   if (!layout->tokens_per_expert || !layout->expert_offsets || !layout->counters) return MOE_ERR_INVALID_ARG;
   if ((a > 0 && (!topk_idx || !layout->ordinal || !layout->assign_row || !layout->drop_mask)) ||
-      (rows > 0 && (!layout->row_src || !layout->pad_mask)) || (n > 0 && !x) || (w_perm && a > 0 && !topk_w))
+      (rows > 0 && (!layout->row_src || !layout->pad_mask)) || (needs_x && n > 0 && !x) ||
+      (w_perm && a > 0 && !topk_w))
     return MOE_ERR_INVALID_ARG;
   for (const void *o : outs)
     if (rows > 0 && !o) return MOE_ERR_INVALID_ARG;
@@ -266,6 +267,17 @@ moe_status moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_i
                         const moe_layout *layout, void *x_perm, float *w_perm, void *workspace,
                         size_t workspace_bytes, void *stream) {
   return dispatch_impl(s, x, topk_idx, topk_w, layout, x_perm, w_perm, workspace, workspace_bytes, stream);
+}
+
+moe_status moe_build_layout(const moe_shape *s, const int32_t *topk_idx, const float *topk_w,
+                            const moe_layout *layout, float *w_perm, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  moe_status st = check_shape(s);
+  if (st != MOE_OK) return st;
+  int64_t row_bytes, rows;
+  if ((st = check_rows(s, &row_bytes, &rows)) != MOE_OK) return st;
+  return dispatch_layout(s, rows, nullptr, topk_idx, topk_w, layout, {}, w_perm, workspace, workspace_bytes,
+                         as_stream(stream), false, false);
 }
 
 moe_status moe_dispatch_noalloc(const moe_shape *s, const void *x, const int32_t *topk_idx, const float *topk_w,

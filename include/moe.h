@@ -6,6 +6,7 @@
  *   moe_dispatch    per-expert histogram + prefix sum, stable per-expert ordinals,
  *                   capacity drop/pad masks, row scatter into expert-contiguous rows
  *   moe_dispatch_noalloc the same with library-owned scratch (no workspace)
+ *   moe_build_layout the dispatch layout alone (no row copy)
  *   moe_dispatch_mxfp8 the same, the permuted rows quantised to MXFP8 (E4M3 + E8M0)
  *   moe_expert_ffn  grouped SwiGLU expert GEMM (bf16 MFMA, fp32 accumulation)
  *   moe_expert_ffn_bwd backward of moe_expert_ffn (grads of rows and weights)
@@ -211,6 +212,18 @@ moe_status moe_route_random(const moe_shape *s, uint64_t seed, const float *expe
 moe_status moe_dispatch(const moe_shape *s, const void *x, const int32_t *topk_idx, const float *topk_w,
                         const moe_layout *layout, void *x_perm, float *w_perm, void *workspace,
                         size_t workspace_bytes, void *stream);
+
+/* The layout of moe_dispatch without the row copy: every array of *layout and
+ * w_perm (nullable) exactly as moe_dispatch writes them, from topk_idx and
+ * topk_w alone (the per-assignment payload of DeepSpeed's ep_tp_dispatch.py --
+ * capacity slots, drop and pad masks, stable ordinals -- computed on its own,
+ * for callers that move the rows themselves or only need the counts, offsets
+ * and permutation).  s->hidden and s->act_dtype are checked as for
+ * moe_dispatch but no activations are read.  Same options, workspace
+ * (moe_workspace_size(MOE_OP_DISPATCH)) and errors as moe_dispatch. */
+moe_status moe_build_layout(const moe_shape *s, const int32_t *topk_idx, const float *topk_w,
+                            const moe_layout *layout, float *w_perm, void *workspace, size_t workspace_bytes,
+                            void *stream);
 
 /* Bytes of the static scratch of moe_dispatch_noalloc (per GPU). */
 #define MOE_NOALLOC_SCRATCH_BYTES ((size_t)8 << 20)

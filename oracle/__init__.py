@@ -20,7 +20,12 @@ import numpy as np
 
 _HERE = Path(__file__).resolve().parent
 _SRC = _HERE / "moe_oracle.c"
-_LIB = _HERE / "libmoe_oracle.so"
+# MOE_ORACLE_SANITIZE=1: a separate build with AddressSanitizer and
+# UndefinedBehaviorSanitizer (host code only; the process must preload the
+# ASan runtime), for running the pins under the sanitizers
+_SANITIZE = os.environ.get("MOE_ORACLE_SANITIZE") == "1"
+_LIB = _HERE / ("libmoe_oracle_san.so" if _SANITIZE else "libmoe_oracle.so")
+_SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
 
 DT_F32 = 0
 DT_BF16 = 1
@@ -31,7 +36,7 @@ def build(force: bool = True) -> Path:
     if force or not _LIB.exists():
         tmp = _LIB.with_suffix(".so.tmp")
         subprocess.check_call(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC",
-                               "-shared", "-o", str(tmp), str(_SRC), "-lm"])
+                               *(_SAN_FLAGS if _SANITIZE else []), "-shared", "-o", str(tmp), str(_SRC), "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
