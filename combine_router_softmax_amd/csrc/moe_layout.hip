@@ -19,17 +19,18 @@
 //   its tile number from an atomic ticket, so every earlier tile belongs to a
 //   workgroup that is already running (or done) and waiting on it cannot
 //   deadlock.  It builds per-wave LDS histograms of its ids, publishes the
-//   tile's per-expert counts, then finds the counts of all earlier tiles by a
-//   decoupled look-back (Merrill and Garland, "Single-pass Parallel Prefix Scan
-//   with Decoupled Look-back", 2016): walking back over the earlier tiles'
-//   published words -- a tile's own count (AGG) or its inclusive prefix (INCL),
-//   which ends the walk -- sixteen words in flight per round.  It publishes its
-//   inclusive prefix, and ranks its assignments: lanes holding the same expert
-//   find each other with one ballot per bit of the expert id (a wave64 match),
-//   ordinal = earlier tiles + earlier waves + rank among the peers below.  The
-//   tile with the last ticket holds the totals and writes the counts, segment
-//   offsets and counters.  Ordinals never depend on atomic order: the tiles are
-//   scanned in assignment order whatever order they run in.
+//   tile's per-expert counts, and ranks its assignments inside the tile: lanes
+//   holding the same expert find each other with one ballot per bit of the
+//   expert id (a wave64 match), local rank = earlier waves + peers below.  Then
+//   it finds the counts of all earlier tiles by a decoupled look-back (Merrill
+//   and Garland, "Single-pass Parallel Prefix Scan with Decoupled Look-back",
+//   2016): walking back over the earlier tiles' published words -- a tile's own
+//   count (AGG) or its inclusive prefix (INCL), which ends the walk -- sixteen
+//   words in flight per round; publishes its inclusive prefix; and writes
+//   ordinal = earlier tiles + local rank.  The tile with the last ticket holds
+//   the totals and writes the counts, segment offsets and counters.  Ordinals
+//   never depend on atomic order: the tiles are scanned in assignment order
+//   whatever order they run in.
 //   Rows are then placed from (ordinal, kept, offset) alone (moe_place.hpp):
 //   by the scatter as it copies the rows, or by layout_finish where no scatter
 //   follows.
@@ -85,37 +86,56 @@ __device__ __forceinline__ void st_status(uint64_t *p, uint64_t v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Poll a status word until it carries this call's epoch; past the bound, record
-// the fault and return an empty inclusive word (ends the walk).
-__device__ uint64_t wait_status(const uint64_t *p, uint32_t epoch, ScanHeader *hdr) {
-  for (uint32_t it = 0; it < kSpinLimit; ++it) {
-    const uint64_t w = ld_status(p);
-    if (status_ready(w, epoch)) return w;
-    __builtin_amdgcn_s_sleep(2);
-  }
-  __hip_atomic_store(&hdr->fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return status_word(epoch, kFlagIncl, 0);
+// The first kLookback status words of bin x before `tile` (nearest first).
+__device__ __forceinline__ void look_back_first(const uint64_t *status, int64_t tile, int nbins, int x,
+                                                uint64_t (&w)[kLookback]) {
+#pragma unroll
+  for (int i = 0; i < kLookback; ++i) w[i] = tile - 1 - i >= 0 ? ld_status(status + (tile - 1 - i) * nbins + x) : 0ull;
 }
 
 // Sum of bin x over the tiles before `tile`: walk back over their status words,
-// kLookback at a time, adding counts until an inclusive prefix.
-__device__ uint32_t look_back(const uint64_t *status, int64_t tile, int nbins, int x, uint32_t epoch, ScanHeader *hdr) {
+// kLookback at a time (`w` holds the first batch, look_back_first),
+// adding each tile's count down to the nearest inclusive prefix, which is added
+// and ends the walk.  A batch is summed once every word it needs -- those up to
+// its nearest inclusive prefix -- carries this call's epoch; the words still
+// missing are requested again together, so each round costs one memory round
+// trip however many of them are missing.  Past the bound a wait records the
+// fault and the walk ends (see the file comment).
+__device__ __forceinline__ uint32_t look_back(const uint64_t *status, int64_t tile, int nbins, int x, uint32_t epoch,
+                                              ScanHeader *hdr, uint64_t (&w)[kLookback]) {
   uint32_t sum = 0;
   for (int64_t p = tile - 1; p >= 0; p -= kLookback) {
-    uint64_t w[kLookback];
+    if (p != tile - 1) {
 #pragma unroll
-    for (int i = 0; i < kLookback; ++i) w[i] = p - i >= 0 ? ld_status(status + (p - i) * nbins + x) : 0ull;
-    bool stop = false;
-#pragma unroll
-    for (int i = 0; i < kLookback; ++i) {
-      if (!stop && p - i >= 0) {
-        uint64_t v = w[i];
-        if (!status_ready(v, epoch)) v = wait_status(status + (p - i) * nbins + x, epoch, hdr);
-        sum += (uint32_t)v;
-        stop = ((v >> 32) & 3u) == kFlagIncl;
-      }
+      for (int i = 0; i < kLookback; ++i) w[i] = p - i >= 0 ? ld_status(status + (p - i) * nbins + x) : 0ull;
     }
-    if (stop) break;
+    const int n = p + 1 < kLookback ? (int)(p + 1) : kLookback;  // words of this batch (tile 0 is the last)
+    for (uint32_t spin = 0;; ++spin) {
+      uint32_t missing = 0, incl = 0;
+#pragma unroll
+      for (int i = 0; i < kLookback; ++i) {
+        const bool ready = i < n && status_ready(w[i], epoch);
+        missing |= (i < n && !ready ? 1u : 0u) << i;
+        incl |= (ready && ((w[i] >> 32) & 3u) == kFlagIncl ? 1u : 0u) << i;
+      }
+      const int last = incl ? __builtin_ctz(incl) : n - 1;  // the batch's words that count: 0..last
+      const uint32_t needed = last >= 31 ? ~0u : (2u << last) - 1u;
+      if (!(missing & needed)) {
+#pragma unroll
+        for (int i = 0; i < kLookback; ++i)
+          if (i <= last) sum += (uint32_t)w[i];
+        if (incl) return sum;
+        break;  // every word of the batch is a tile's own count: the next batch
+      }
+      if (spin == kSpinLimit) {
+        __hip_atomic_store(&hdr->fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        return sum;
+      }
+      __builtin_amdgcn_s_sleep(2);
+#pragma unroll
+      for (int i = 0; i < kLookback; ++i)
+        if ((missing & needed) >> i & 1u) w[i] = ld_status(status + (p - i) * nbins + x);
+    }
   }
   return sum;
 }
@@ -136,38 +156,85 @@ __device__ __forceinline__ int32_t wave_sum_i32(int32_t v) {
   return v;
 }
 
-// Exclusive scan of in[0..n) (n <= 1024) into out[]; every thread of the block calls it.
-__device__ void block_exclusive_scan(const int32_t *in, int32_t *out, int n) {
-  __shared__ int32_t wave_tot[kScanWaves];
+// The last tile: from the expert totals (total[0..e), total[e] = invalid ids)
+// the kept counts, segment starts and counters.  Each thread holds kPer
+// consecutive experts; the segment lengths (C, or the count rounded up to the
+// alignment) and the totals are scanned together across the block (one
+// barrier), each start and kept count clipped to the row budget R, and the
+// kept counts reduced (a second barrier).
+__device__ void finalize_layout(const int32_t *total, int e, int capacity, int row_align, int64_t rows,
+                                int32_t *__restrict__ tokens_per_expert, int32_t *__restrict__ expert_offsets,
+                                int32_t *__restrict__ counters, int32_t *__restrict__ full_off) {
   constexpr int kPer = kMaxExperts / kScanThreads;
-  const int t = threadIdx.x;
-  int32_t v[kPer];
-  int32_t s = 0;
+  __shared__ int32_t wsum[3][kScanWaves];
+  const int t = threadIdx.x, w = t / kWave, l = lane_id();
+  int32_t tot[kPer], len[kPer];
+  int32_t s_len = 0, s_tot = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int x = t * kPer + i;
-    v[i] = x < n ? in[x] : 0;
-    s += v[i];
+    tot[i] = x < e ? total[x] : 0;
+    len[i] = x >= e ? 0 : (capacity > 0 ? capacity : (tot[i] + row_align - 1) / row_align * row_align);
+    s_len += len[i];
+    s_tot += tot[i];
   }
-  const int32_t incl = wave_incl_scan(s);
-  if (lane_id() == kWave - 1) wave_tot[t / kWave] = incl;
+  const int32_t i_len = wave_incl_scan(s_len), i_tot = wave_incl_scan(s_tot);
+  if (l == kWave - 1) {
+    wsum[0][w] = i_len;
+    wsum[1][w] = i_tot;
+  }
   __syncthreads();
-  int32_t run = incl - s;
-  for (int w = 0; w < t / kWave; ++w) run += wave_tot[w];
+  int32_t off = i_len - s_len, foff = i_tot - s_tot, all_len = 0, all_tot = 0;
+#pragma unroll
+  for (int ww = 0; ww < kScanWaves; ++ww) {
+    off += ww < w ? wsum[0][ww] : 0;
+    foff += ww < w ? wsum[1][ww] : 0;
+    all_len += wsum[0][ww];
+    all_tot += wsum[1][ww];
+  }
+  const int32_t used_end = (int32_t)(all_len < rows ? all_len : rows);  // rows = E*C with a capacity
+  int32_t k_sum = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
     const int x = t * kPer + i;
-    if (x < n) out[x] = run;
-    run += v[i];
+    if (x < e) {
+      const int32_t s0 = off < rows ? off : (int32_t)rows;
+      const int64_t room = capacity > 0 ? capacity : rows - s0;
+      const int32_t kept = (int32_t)(tot[i] < room ? tot[i] : room);
+      tokens_per_expert[x] = kept;
+      expert_offsets[x] = s0;
+      if (full_off) full_off[x] = foff;  // drop by weight: where the expert's list starts
+      k_sum += kept;
+    }
+    off += len[i];
+    foff += tot[i];
   }
+  if (t == 0) {
+    expert_offsets[e] = used_end;
+    if (full_off) full_off[e] = all_tot;
+  }
+  k_sum = wave_sum_i32(k_sum);
+  if (l == 0) wsum[2][w] = k_sum;
   __syncthreads();
+  if (t == 0) {
+    int32_t ks = 0;
+#pragma unroll
+    for (int ww = 0; ww < kScanWaves; ++ww) ks += wsum[2][ww];
+    counters[0] = ks;
+    counters[1] = all_tot - ks;
+    counters[2] = used_end - ks;  // rows below the end of the last segment holding nothing: pads
+    counters[3] = total[e];
+  }
 }
 
 // One workgroup per tile of kLayoutTile assignments (see the file comment).
 // Wave w owns the tile's assignments w*256 .. w*256+255, in four 64-wide
 // chunks; bin e (E + 1 bins) counts the invalid ids (neither -1 nor an expert).
+// BITS: an upper bound of the expert id's bit count (a compile-time count keeps
+// the ballot loop unrolled; bits above the ids' own are zero in every lane).
+template <int BITS>
 __global__ __launch_bounds__(kScanThreads) void layout_scan(
-    const int32_t *__restrict__ topk_idx, int64_t a_total, int64_t tiles, int e, int id_bits, int capacity,
+    const int32_t *__restrict__ topk_idx, int64_t a_total, int64_t tiles, int e, int capacity,
     int row_align, int64_t rows, ScanHeader *hdr, uint64_t *status, int32_t *__restrict__ ordinal,
     int32_t *__restrict__ tokens_per_expert, int32_t *__restrict__ expert_offsets, int32_t *__restrict__ counters,
     int32_t *__restrict__ full_off) {
@@ -176,10 +243,7 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan(
   int32_t *run = sm;                  // [waves][nb] per-wave counts, then running bases
   int32_t *agg = run + kScanWaves * nb;  // [nb] this tile's counts
   int32_t *base = agg + nb;           // [nb] counts of the earlier tiles
-  int32_t *kept = base + nb;          // [e] (last tile)
-  int32_t *off = kept + e;            // [e + 1] (last tile)
   __shared__ uint32_t sh_ticket, sh_epoch;
-  __shared__ int32_t red[3][kScanWaves];
   const int tid = threadIdx.x;
   const int w = tid / kWave;
   const int l = lane_id();
@@ -218,125 +282,71 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan(
     }
     __syncthreads();
 
-    // this tile's counts, published at once (tile 0's are already inclusive)
+    // this tile's counts, published at once (tile 0's are already inclusive),
+    // and each wave's base inside the tile (its earlier waves' counts)
     uint64_t *mine = status + tile * nb;
     for (int x = tid; x < nb; x += kScanThreads) {
+      int32_t c[kScanWaves];
+#pragma unroll
+      for (int ww = 0; ww < kScanWaves; ++ww) c[ww] = run[ww * nb + x];
       int32_t s = 0;
 #pragma unroll
-      for (int ww = 0; ww < kScanWaves; ++ww) s += run[ww * nb + x];
+      for (int ww = 0; ww < kScanWaves; ++ww) {
+        run[ww * nb + x] = s;
+        s += c[ww];
+      }
       agg[x] = s;
       st_status(mine + x, status_word(epoch, tile == 0 ? kFlagIncl : kFlagAgg, (uint32_t)s));
     }
-    // the earlier tiles' counts by look-back, then this tile's inclusive prefix
-    for (int x = tid; x < nb; x += kScanThreads) {
-      const int32_t b = tile == 0 ? 0 : (int32_t)look_back(status, tile, nb, x, epoch, hdr);
-      base[x] = b;
-      if (tile > 0) st_status(mine + x, status_word(epoch, kFlagIncl, (uint32_t)(b + agg[x])));
-    }
     __syncthreads();
 
-    // running base of each wave: earlier tiles + earlier waves of this tile
-    for (int x = tid; x < e; x += kScanThreads) {
-      int32_t b = base[x];
-#pragma unroll
-      for (int ww = 0; ww < kScanWaves; ++ww) {
-        const int32_t c = run[ww * nb + x];
-        run[ww * nb + x] = b;
-        b += c;
-      }
-    }
-    __syncthreads();
-
-    // stable ranks: chunks in order, peers found by a ballot per id bit
+    // stable ranks inside the tile: chunks in order, peers found by a ballot per
+    // id bit; the earlier tiles' counts are added once the look-back has them
     const uint64_t below = lanes_below_mask();
+    int32_t local[kScanChunks];
 #pragma unroll
     for (int c = 0; c < kScanChunks; ++c) {
-      const int64_t a = a_wave + c * kWave + l;
       const int32_t x = ids[c];
       const bool valid = valid_id(x, e);
       uint64_t peers = ballot(valid);
-      for (int b = 0; b < id_bits; ++b) {
+#pragma unroll
+      for (int b = 0; b < BITS; ++b) {
         const bool bit = (x >> b) & 1;
         const uint64_t bal = ballot(valid && bit);
         peers &= bit ? bal : ~bal;
       }
+      local[c] = 0;
       if (valid) {
         const int rank = __popcll(peers & below);
         const int32_t b = run[w * nb + x];
         if (rank == 0) run[w * nb + x] = b + __popcll(peers);
-        ordinal[a] = b + rank;
-      } else if (a < a_total) {
-        ordinal[a] = -1;
+        local[c] = b + rank;
       }
       __builtin_amdgcn_wave_barrier();
     }
 
-    if (tile == tiles - 1) {  // the totals: counts, segment offsets, counters
-      int32_t *total = agg;   // reused: total = base + this tile's count
-      __syncthreads();
-      for (int x = tid; x < nb; x += kScanThreads) total[x] += base[x];
-      __syncthreads();
-      if (full_off) {  // drop by weight: where each expert's list of assignments starts
-        block_exclusive_scan(total, off, e);
-        for (int x = tid; x < e; x += kScanThreads) full_off[x] = off[x];
-        if (tid == 0) full_off[e] = off[e - 1] + total[e - 1];
-        __syncthreads();
-      }
-      if (capacity > 0) {
-        for (int x = tid; x < e; x += kScanThreads) {
-          off[x] = x * capacity;
-          kept[x] = total[x] < capacity ? total[x] : capacity;
-        }
-        if (tid == 0) off[e] = (int32_t)rows;
-        __syncthreads();
-      } else {
-        // segment lengths rounded up to the alignment (kept[] as scratch), their
-        // exclusive scan, then each start and kept count clipped to the budget
-        __shared__ int32_t used_end;
-        for (int x = tid; x < e; x += kScanThreads) kept[x] = (total[x] + row_align - 1) / row_align * row_align;
-        __syncthreads();
-        block_exclusive_scan(kept, off, e);
-        if (tid == 0) {
-          const int64_t end = (int64_t)off[e - 1] + kept[e - 1];
-          used_end = (int32_t)(end < rows ? end : rows);
-        }
-        __syncthreads();
-        for (int x = tid; x < e; x += kScanThreads) {
-          const int32_t s0 = off[x] < rows ? off[x] : (int32_t)rows;
-          const int64_t room = rows - s0;
-          kept[x] = (int32_t)(total[x] < room ? total[x] : room);
-          off[x] = s0;
-        }
-        if (tid == 0) off[e] = used_end;
-        __syncthreads();
-      }
-      int32_t k_sum = 0, t_sum = 0;
-      for (int x = tid; x < e; x += kScanThreads) {
-        tokens_per_expert[x] = kept[x];
-        expert_offsets[x] = off[x];
-        k_sum += kept[x];
-        t_sum += total[x];
-      }
-      if (tid == 0) expert_offsets[e] = off[e];
-      k_sum = wave_sum_i32(k_sum);
-      t_sum = wave_sum_i32(t_sum);
-      if (l == 0) {
-        red[0][w] = k_sum;
-        red[1][w] = t_sum;
-      }
-      __syncthreads();
-      if (tid == 0) {
-        int32_t ks = 0, ts = 0;
-        for (int ww = 0; ww < kScanWaves; ++ww) {
-          ks += red[0][ww];
-          ts += red[1][ww];
-        }
-        counters[0] = ks;
-        counters[1] = ts - ks;
-        counters[2] = off[e] - ks;
-        counters[3] = total[e];
-      }
+    // the earlier tiles' counts by look-back, then this tile's inclusive prefix
+    // (agg becomes the inclusive prefix: the totals, in the last tile)
+    // (requested after the ranking, which gives the earlier tiles time to publish:
+    // requesting them before it measured slower)
+    for (int x = tid; x < nb; x += kScanThreads) {
+      uint64_t first[kLookback];
+      if (tile > 0) look_back_first(status, tile, nb, x, first);
+      const int32_t b = tile == 0 ? 0 : (int32_t)look_back(status, tile, nb, x, epoch, hdr, first);
+      base[x] = b;
+      agg[x] += b;
+      if (tile > 0) st_status(mine + x, status_word(epoch, kFlagIncl, (uint32_t)agg[x]));
     }
+    __syncthreads();
+#pragma unroll
+    for (int c = 0; c < kScanChunks; ++c) {
+      const int64_t a = a_wave + c * kWave + l;
+      if (valid_id(ids[c], e)) ordinal[a] = base[ids[c]] + local[c];
+      else if (a < a_total) ordinal[a] = -1;
+    }
+
+    if (tile == tiles - 1)  // the totals: counts, segment offsets, counters
+      finalize_layout(agg, e, capacity, row_align, rows, tokens_per_expert, expert_offsets, counters, full_off);
   } else if (tid == 0) {
     __hip_atomic_store(&hdr->fault, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
@@ -561,11 +571,16 @@ hipError_t scan(const int32_t *topk_idx, int64_t a_total, int e, int capacity, i
                 int32_t *tokens_per_expert, int32_t *expert_offsets, int32_t *ordinal, int32_t *counters,
                 const LayoutWorkspace &w, hipStream_t stream) {
   const int64_t tiles = layout_tiles(a_total);
-  const int id_bits = e <= 1 ? 0 : 32 - __builtin_clz((unsigned)(e - 1));
-  const size_t lds = sizeof(int32_t) * ((size_t)(kScanWaves + 2) * (e + 1) + 2 * (size_t)e + 1);
-  hipLaunchKernelGGL(layout_scan, dim3((unsigned)tiles), dim3(kScanThreads), lds, stream, topk_idx, a_total, tiles, e,
-                     id_bits, capacity, row_align > 1 ? row_align : 1, rows, w.hdr, w.status, ordinal,
-                     tokens_per_expert, expert_offsets, counters, w.full_off);
+  const size_t lds = sizeof(int32_t) * (size_t)(kScanWaves + 2) * (e + 1);
+#define MOE_SCAN(B)                                                                                                  \
+  hipLaunchKernelGGL(layout_scan<B>, dim3((unsigned)tiles), dim3(kScanThreads), lds, stream, topk_idx, a_total,     \
+                     tiles, e, capacity, row_align > 1 ? row_align : 1, rows, w.hdr, w.status, ordinal,               \
+                     tokens_per_expert, expert_offsets, counters, w.full_off)
+  if (e <= 16) MOE_SCAN(4);
+  else if (e <= 64) MOE_SCAN(6);
+  else if (e <= 256) MOE_SCAN(8);
+  else MOE_SCAN(10);  // E <= 1024
+#undef MOE_SCAN
   return hipGetLastError();
 }
 
