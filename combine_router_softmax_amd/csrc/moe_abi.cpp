@@ -123,7 +123,7 @@ moe_status moe_workspace_size(moe_op op, const moe_shape *s, size_t *bytes) {
       return MOE_OK;
     case MOE_OP_EXPERT_FFN_BWD:
       if (s->inter < 1) return MOE_ERR_INVALID_ARG;
-      *bytes = moe::ffn_bwd_workspace_bytes(rows_of(s), s->inter);
+      *bytes = moe::ffn_bwd_workspace_bytes(rows_of(s), s->inter, s->n_experts);
       return MOE_OK;
   }
   return MOE_ERR_INVALID_ARG;
@@ -358,7 +358,7 @@ moe_status expert_ffn_bwd(const moe_shape *s, const void *x_perm, const void *gr
     if (in && (in == grad_x_perm || in == grad_w_gate_up || in == grad_w_down)) return MOE_ERR_INVALID_ARG;
   if (grad_w_gate_up == grad_w_down || (grad_x_perm && (grad_x_perm == grad_w_gate_up || grad_x_perm == grad_w_down)))
     return MOE_ERR_INVALID_ARG;
-  const size_t need_ws = moe::ffn_bwd_workspace_bytes(rows, s->inter);
+  const size_t need_ws = moe::ffn_bwd_workspace_bytes(rows, s->inter, s->n_experts);
   if (workspace_bytes < need_ws || (need_ws > 0 && (!workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))))
     return MOE_ERR_WORKSPACE;
   return hip_status(moe::launch_expert_ffn_bwd(

@@ -262,22 +262,6 @@ __device__ __forceinline__ void load_frags(const char *__restrict__ as, const ch
   }
 }
 
-// Zeroes the K values >= kvalid (counted from the start of the K step) of the B
-// fragments of slice ks: the ragged last K step of a weight-gradient tile.
-__device__ __forceinline__ void mask_k_tail(bf16x8 (&b)[4], int ks, int kvalid, int l) {
-  const int lim = kvalid - 16 * ks - 8 * (l >> 5);  // this lane's values j < lim are real
-  uint32_t m[4];
-#pragma unroll
-  for (int d = 0; d < 4; ++d) m[d] = (2 * d < lim ? 0xFFFFu : 0u) | (2 * d + 1 < lim ? 0xFFFF0000u : 0u);
-#pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    u32x4 v = __builtin_bit_cast(u32x4, b[ni]);
-#pragma unroll
-    for (int d = 0; d < 4; ++d) v[d] &= m[d];
-    b[ni] = __builtin_bit_cast(bf16x8, v);
-  }
-}
-
 // MFMAs FIRST .. FIRST+COUNT-1 of one 16-wide K slice, numbered row block
 // major (i = 4*mi + ni).  The weight fragment is the MFMA's first operand, so
 // block (mi, ni) of the result holds, in lane l, activation row l%32 of the
@@ -399,31 +383,27 @@ __device__ __forceinline__ void slice_fp8(const i32x8 (&a)[4], const i32x8 (&b)[
 // Modes of the grouped GEMM.  kModePlain: per expert segment, C = A B_e^T
 // (y = act W_down^T, and the backward's products with the weights).
 // kModeSwiGLU: B tile rows 0..127 are gate rows n0.., rows 128..255 the up rows
-// I+n0..; output the [rows, I] SwiGLU intermediate.  kModeWGrad: per expert e,
-// C_e [M, N] = A_e^T B_e with A_e [rows_e, M] and B_e [rows_e, N] the rows of
-// expert e's segment -- the weight gradients, reducing over the expert's rows.
-// kAT / kBT: the operand is K-major (stored [K, M] / [K, N]; row length M / N)
-// instead of K-contiguous ([M, K] / [N, K], row length K).  Plain mode takes
-// only kBT (B = a weight [K, N] of each expert); weight-gradient mode takes both.
+// I+n0..; output the [rows, I] SwiGLU intermediate.  kBT: B is K-major (a
+// weight [K, N] of each expert, row length N) instead of K-contiguous ([N, K]);
+// plain mode only.
 // gate_up (SwiGLU mode, nullable): also store the pre-activations [rows, 2I],
 // gate columns then up columns, for the backward.
 // kFp8: A and B are MXFP8 (E4M3 codes [.., K] with E8M0 scales A_scale [rows,
 // K/32], B_scale [E, N rows, K/32]; K a multiple of 512); plain mode writes
 // bf16 C, SwiGLU mode writes the intermediate as MXFP8 (codes into C as bytes
 // [rows, ldc], scales into C_scale [rows, ldc/32]).
-constexpr int kModePlain = 0, kModeSwiGLU = 1, kModeWGrad = 2;
+constexpr int kModePlain = 0, kModeSwiGLU = 1;
 
-template <int kMode, bool kAT, bool kBT, bool kFp8 = false>
+template <int kMode, bool kBT, bool kFp8 = false>
 __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
-    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int64_t b_expert_stride, int K, int M, int N,
-    int m_tiles, int n_tiles, const int32_t *__restrict__ tokens_per_expert,
-    const int32_t *__restrict__ expert_offsets, int e, uint16_t *__restrict__ C, int64_t ldc,
-    uint16_t *__restrict__ gate_up, const uint16_t *__restrict__ B_rep, uint16_t *__restrict__ C_rep, int e_master,
-    const uint8_t *__restrict__ A_scale, const uint8_t *__restrict__ B_scale, uint8_t *__restrict__ C_scale) {
-  constexpr bool kSwiGLU = kMode == kModeSwiGLU, kWGrad = kMode == kModeWGrad;
-  static_assert(kWGrad ? (kAT && kBT) : !kAT, "operand layouts of the modes");
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int64_t b_expert_stride, int K, int N,
+    int n_tiles, const int32_t *__restrict__ tokens_per_expert, const int32_t *__restrict__ expert_offsets, int e,
+    uint16_t *__restrict__ C, int64_t ldc, uint16_t *__restrict__ gate_up, const uint16_t *__restrict__ B_rep,
+    int e_master, const uint8_t *__restrict__ A_scale, const uint8_t *__restrict__ B_scale,
+    uint8_t *__restrict__ C_scale) {
+  constexpr bool kSwiGLU = kMode == kModeSwiGLU;
   static_assert(!(kSwiGLU && kBT), "the SwiGLU pairing reads K-contiguous weights");
-  static_assert(!kFp8 || (!kAT && !kBT && !kWGrad), "MXFP8 operands: K-contiguous forward GEMMs");
+  static_assert(!kFp8 || !kBT, "MXFP8 operands: K-contiguous forward GEMMs");
   constexpr int kEsz = kFp8 ? 1 : 2;            // bytes per operand element
   constexpr int kStepK = kRowBytes / kEsz;      // K values per step
   // ring of operand tiles (MXFP8: and the scale groups after it); also
@@ -435,34 +415,14 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wm = w >> 1, wn = w & 1;
   // tile coordinates (the same in every lane: kept in scalar registers): n0 the
-  // first output column, rows_valid the output rows of the tile, KT the K steps
-  // and k_len the K extent (ragged only in weight-gradient mode), the operand
-  // bases at K = 0 and the output base
-  int n0, rows_valid, KT, k_len;
+  // first output column, rows_valid the output rows of the tile, KT the K
+  // steps, the operand bases at K = 0 and the output base
+  int n0, rows_valid, KT;
   const char *a_base, *b_base;
   const uint8_t *as_base = nullptr, *bs_base = nullptr;  // MXFP8 scale rows of the tile at K = 0
   uint8_t *q_base = nullptr, *qs_base = nullptr;        // MXFP8 intermediate: codes and scales of row0
   uint16_t *c_base, *gu_base = nullptr;
-  if constexpr (kWGrad) {
-    // each XCD (workgroup b runs on XCD b % 8) takes one eighth of every
-    // expert's tiles, m fastest, expert after expert: the experts' different
-    // row counts (the K of these GEMMs) load the XCDs evenly
-    const int per_e = m_tiles * n_tiles, chunk = (per_e + kXcds - 1) / kXcds;
-    const int slot = (int)blockIdx.x / kXcds;
-    const int te = slot / chunk;
-    const int local = ((int)blockIdx.x % kXcds) * chunk + slot % chunk;
-    if (te >= e || local >= per_e) return;
-    const int m0 = (local % m_tiles) * kBM;
-    n0 = (local / m_tiles) * kBN;
-    rows_valid = M - m0 < kBM ? M - m0 : kBM;
-    k_len = __builtin_amdgcn_readfirstlane(tokens_per_expert[te]);
-    const int64_t r0 = __builtin_amdgcn_readfirstlane(expert_offsets[te]);
-    KT = (k_len + kBK - 1) / kBK;
-    a_base = reinterpret_cast<const char *>(A + r0 * M + m0);
-    b_base = reinterpret_cast<const char *>(B + r0 * N + n0);
-    // replica slots (experts from e_master on) write to the replica buffer
-    c_base = (te < e_master ? C + (int64_t)te * M * N : C_rep + (int64_t)(te - e_master) * M * N) + (int64_t)m0 * N;
-  } else {
+  {
     TileCoord tc;
     if (!find_tile(tokens_per_expert, expert_offsets, e, n_tiles, reinterpret_cast<int32_t *>(ring), tc)) return;
     const int te = __builtin_amdgcn_readfirstlane(tc.e);
@@ -471,7 +431,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
                          (uint32_t)__builtin_amdgcn_readfirstlane((int)tc.row0);
     rows_valid = __builtin_amdgcn_readfirstlane((int)(tc.row_end - tc.row0 < kBM ? tc.row_end - tc.row0 : kBM));
     KT = K / kStepK;
-    k_len = K;
     a_base = reinterpret_cast<const char *>(A) + row0 * K * kEsz;
     // replica slots (experts from e_master on) read the replica weights
     const char *b_e = te < e_master
@@ -490,7 +449,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     if (kSwiGLU && gate_up) gu_base = gate_up + row0 * 2 * N;
   }
   // bytes between the operand tiles of consecutive K steps
-  const int64_t a_step = kAT ? (int64_t)kBK * M * 2 : kRowBytes;
+  const int64_t a_step = kRowBytes;
   const int64_t b_step = kBT ? (int64_t)kBK * N * 2 : kRowBytes;
 
   // the tile's 32-row blocks 0..7 alternate between the two row groups of waves
@@ -509,20 +468,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   // chunk position ^ swz_t(row); columns past the operand's end re-read its last
   // chunk.  Addresses are a per-step scalar base plus a 32-bit per-lane offset.
   uint32_t a_off[kLoads], b_off[kLoads];
-  int a_row[kLoads], b_row[kLoads];  // K-major: the tile row each load instruction fills
 #pragma unroll
   for (int i = 0; i < kLoads; ++i) {
-    if constexpr (kAT) {
-      const int k = w * 16 + 2 * i + l / 32;
-      int col = ((l % 32) ^ swz_t(k)) * 8;
-      if (col > rows_valid - 8) col = rows_valid - 8;  // M is a multiple of 64
-      a_row[i] = k;
-      a_off[i] = (uint32_t)col * 2u;
-    } else {
+    {
       const int r = w * 64 + i * kLoadRows + l / kChunks;
       const int c = (l % kChunks) ^ swz(r);
       const int ar = r < rows_valid ? r : rows_valid - 1;  // ragged tail: re-read the last row
-      a_row[i] = 0;
       a_off[i] = (uint32_t)ar * (uint32_t)(K * kEsz) + (uint32_t)(c * 16);
     }
     if constexpr (kBT) {
@@ -530,8 +481,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
       const int n_lim = N - n0;  // columns of the operand from n0 on
       int col = ((l % 32) ^ swz_t(k)) * 8;
       if (col > n_lim - 8) col = n_lim - 8;
-      b_row[i] = k;
-      b_off[i] = (uint32_t)col * 2u;
+      b_off[i] = (uint32_t)col * 2u + (uint32_t)k * (uint32_t)N * 2u;
     } else {
       const int r = w * 64 + i * kLoadRows + l / kChunks;
       const int c = (l % kChunks) ^ swz(r);
@@ -543,42 +493,28 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
       } else {
         br = n0 + r < N ? n0 + r : N - 1;
       }
-      b_row[i] = 0;
       b_off[i] = (uint32_t)br * (uint32_t)(K * kEsz) + (uint32_t)(c * 16);  // < 4*I*H bytes
     }
   }
   const uint32_t ring_lds = lds_address(ring) + w * 64 * kRowBytes;  // = w * 16 * kTRowBytes
   // load instruction i (0..7) of this wave for the A (B) tile of step kt into
-  // ring slot `slot`.  K-major rows past the K extent (the ragged last step of
-  // a weight gradient) re-read the extent's last row; mask_k_tail zeroes their
-  // contribution.
+  // ring slot `slot`
   auto load_a = [&](int slot, int kt, int i) {
-    uint32_t off = a_off[i];
-    if constexpr (kAT) {
-      const int last = k_len - 1 - kt * kBK;
-      off += (uint32_t)(a_row[i] < last ? a_row[i] : last) * (uint32_t)M * 2u;
-    }
-    dma16(a_base + kt * a_step, off, ring_lds + slot * kOperandBytes + i * 1024);
+    dma16(a_base + kt * a_step, a_off[i], ring_lds + slot * kOperandBytes + i * 1024);
   };
   auto load_b = [&](int slot, int kt, int i) {
-    uint32_t off = b_off[i];
-    if constexpr (kBT) {
-      const int last = k_len - 1 - kt * kBK;
-      off += (uint32_t)(b_row[i] < last ? b_row[i] : last) * (uint32_t)N * 2u;
-    }
-    dma16(b_base + kt * b_step, off, ring_lds + slot * kOperandBytes + i * 1024);
+    dma16(b_base + kt * b_step, b_off[i], ring_lds + slot * kOperandBytes + i * 1024);
   };
-  // per-lane offsets of the transposed fragment reads
+  // per-lane offsets of the transposed fragment reads (A is never K-major here)
   uint32_t ta[4][2], tb[4][2];
 #pragma unroll
   for (int j = 0; j < 4; ++j)
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      ta[j][h] = kAT ? tr_off(l, 2 * j + wm, h) : 0u;
+      ta[j][h] = 0u;
       tb[j][h] = kBT ? tr_off(l, 4 * wn + j, h) : 0u;
     }
-  constexpr int kReads = (kAT ? 8 : 4) + (kBT ? 8 : 4);
-  const int k_tail = k_len - (KT - 1) * kBK;  // K values of the last step (64 unless ragged)
+  constexpr int kReads = 4 + (kBT ? 8 : 4);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -602,8 +538,6 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   // exposed; and the load instructions are spread over the MFMA stream.  The
   // barrier orders LDS accesses only (a full workgroup fence would also wait
   // for the loads in flight).
-  // (a weight-gradient tile of an expert without rows has no K step: its
-  // accumulators stay zero)
   if constexpr (kFp8) {
     // MXFP8 K loop: 128 codes per step in two 64-wide slices.  Four ring slots:
     // step kt's B and A tiles in slots (2kt) % 4 and (2kt) % 4 + 1.  Slice 0
@@ -724,50 +658,43 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   }
   lds_barrier();
   __builtin_amdgcn_sched_barrier(0);
-  load_frags<kSwiGLU, kAT, kBT>(ring + kOperandBytes, ring, 0, wm, wn, l, fa[0], fb[0], ta, tb);
+  load_frags<kSwiGLU, false, kBT>(ring + kOperandBytes, ring, 0, wm, wn, l, fa[0], fb[0], ta, tb);
   __builtin_amdgcn_sched_barrier(0);
 
   // one K step with MI row blocks per wave; sb, sa: slots of step kt's B and A
-  // tiles; nb, na: of step kt+1's; pb: slot for step kt+2's B tile.  In the
-  // ragged last step of a weight gradient, each slice's B fragments are masked
-  // before use (the first slice's here, the others as they are read).
-#define MOE_K_STEP(MI)                                                                                   \
-  {                                                                                                     \
-    const int nb = sb + 2 < kSlots ? sb + 2 : sb + 2 - kSlots;                                          \
-    const int na = sa + 2 < kSlots ? sa + 2 : sa + 2 - kSlots;                                          \
-    const int pb = na + 1 < kSlots ? na + 1 : na + 1 - kSlots;                                          \
-    const bool ahead = kt + 2 < KT;                                                                     \
-    const bool tail = kWGrad && kt == KT - 1 && k_tail < kBK;                                           \
-    const char *as = ring + sa * kOperandBytes;                                                         \
-    const char *bs = ring + sb * kOperandBytes;                                                         \
-    if (tail) mask_k_tail(fb[0], 0, k_tail, l);                                                         \
-    load_frags<kSwiGLU, kAT, kBT>(as, bs, 1, wm, wn, l, fa[1], fb[1], ta, tb);                          \
-    if (tail) mask_k_tail(fb[1], 1, k_tail, l);                                                         \
-    slice<MI, kReads>(fa[0], fb[0], acc, [&](int d) {                                                   \
-      if (ahead) load_b(pb, kt + 2, d);                                                                 \
-    });                                                                                                 \
-    load_frags<kSwiGLU, kAT, kBT>(as, bs, 2, wm, wn, l, fa[0], fb[0], ta, tb);                          \
-    if (tail) mask_k_tail(fb[0], 2, k_tail, l);                                                         \
-    slice<MI, kReads>(fa[1], fb[1], acc, [&](int d) {                                                   \
-      if (ahead) load_b(pb, kt + 2, 4 + d);                                                             \
-    });                                                                                                 \
-    load_frags<kSwiGLU, kAT, kBT>(as, bs, 3, wm, wn, l, fa[1], fb[1], ta, tb);                          \
-    if (tail) mask_k_tail(fb[1], 3, k_tail, l);                                                         \
-    slice<MI, kReads>(fa[0], fb[0], acc, [&](int) {});                                                  \
-    if (ahead) wait_vmcnt<kLoads>();                                                                    \
-    else wait_vmcnt<0>();                                                                               \
-    lds_barrier();                                                                                      \
-    __builtin_amdgcn_sched_barrier(0);                                                                  \
-    load_frags<kSwiGLU, kAT, kBT>(ring + na * kOperandBytes, ring + nb * kOperandBytes, 0, wm, wn, l,   \
-                                  fa[0], fb[0], ta, tb);                                                \
-    slice<MI, kReads>(fa[1], fb[1], acc, [&](int d) {                                                   \
-      if (ahead) {                                                                                      \
-        load_a(sb, kt + 2, 2 * d);                                                                      \
-        load_a(sb, kt + 2, 2 * d + 1);                                                                  \
-      }                                                                                                 \
-    });                                                                                                 \
-    sb = nb;                                                                                            \
-    sa = na;                                                                                            \
+  // tiles; nb, na: of step kt+1's; pb: slot for step kt+2's B tile.
+#define MOE_K_STEP(MI)                                                                                 \
+  {                                                                                                    \
+    const int nb = sb + 2 < kSlots ? sb + 2 : sb + 2 - kSlots;                                         \
+    const int na = sa + 2 < kSlots ? sa + 2 : sa + 2 - kSlots;                                         \
+    const int pb = na + 1 < kSlots ? na + 1 : na + 1 - kSlots;                                         \
+    const bool ahead = kt + 2 < KT;                                                                    \
+    const char *as = ring + sa * kOperandBytes;                                                        \
+    const char *bs = ring + sb * kOperandBytes;                                                        \
+    load_frags<kSwiGLU, false, kBT>(as, bs, 1, wm, wn, l, fa[1], fb[1], ta, tb);                       \
+    slice<MI, kReads>(fa[0], fb[0], acc, [&](int d) {                                                  \
+      if (ahead) load_b(pb, kt + 2, d);                                                                \
+    });                                                                                                \
+    load_frags<kSwiGLU, false, kBT>(as, bs, 2, wm, wn, l, fa[0], fb[0], ta, tb);                       \
+    slice<MI, kReads>(fa[1], fb[1], acc, [&](int d) {                                                  \
+      if (ahead) load_b(pb, kt + 2, 4 + d);                                                            \
+    });                                                                                                \
+    load_frags<kSwiGLU, false, kBT>(as, bs, 3, wm, wn, l, fa[1], fb[1], ta, tb);                       \
+    slice<MI, kReads>(fa[0], fb[0], acc, [&](int) {});                                                 \
+    if (ahead) wait_vmcnt<kLoads>();                                                                   \
+    else wait_vmcnt<0>();                                                                              \
+    lds_barrier();                                                                                     \
+    __builtin_amdgcn_sched_barrier(0);                                                                 \
+    load_frags<kSwiGLU, false, kBT>(ring + na * kOperandBytes, ring + nb * kOperandBytes, 0, wm, wn, l,\
+                                  fa[0], fb[0], ta, tb);                                               \
+    slice<MI, kReads>(fa[1], fb[1], acc, [&](int d) {                                                  \
+      if (ahead) {                                                                                     \
+        load_a(sb, kt + 2, 2 * d);                                                                     \
+        load_a(sb, kt + 2, 2 * d + 1);                                                                 \
+      }                                                                                                \
+    });                                                                                                \
+    sb = nb;                                                                                           \
+    sa = na;                                                                                           \
   }
   // the ragged last tile of an expert runs the loop with the MFMAs of the row
   // blocks that hold rows: a quarter or half of them when the waves hold at
@@ -874,7 +801,7 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     stage_acc();
     const int ch = l % 16;
     const int col = n0 + wn * 128 + ch * 8;
-    const int64_t c_ld = kWGrad ? (int64_t)N : ldc;
+    const int64_t c_ld = ldc;
 #pragma unroll 4
     for (int r = l / 16; r < 128; r += 4) {
       const int row = tile_row(r);
@@ -894,40 +821,548 @@ int64_t tile_bound(int64_t rows, int e, int capacity, int n_tiles) {
   return (t + kXcds - 1) / kXcds * kXcds;  // the launchers reject a grid past INT32_MAX (tile ids are int32)
 }
 
+// ------------------------------------------------------------------ weight gradients
+
+// The weight gradients C_e [M, N] = A_e^T B_e reduce over the rows of expert
+// e's segment: K is the expert's row count (about 512 in a 128-expert layer of
+// 65536 rows), so a 256 x 256 output tile has only a handful of K steps.
+//
+// Operand layouts.  One operand of each gradient is an input stored with its
+// features contiguous (grad_y for dW_down, x_perm for dW_gate_up): K-major,
+// read through the LDS transpose loads.  The other is made by the SwiGLU
+// backward, which also writes it expert-major with K contiguous ("K-major
+// copies" below): expert e's part is [features][kp_e] at element offset
+// features * poff_e, where kp_e is the expert's row count rounded up to a
+// multiple of 64 (zeros after the last row) and poff_e the sum of kp over the
+// experts before e.  Measured on gfx950, a K step whose fragments all come
+// through transpose loads takes about twice as long as one with half of them
+// read as plain 16-byte rows.  The zero padding also makes the ragged last K
+// step exact without masking: the K-major operand re-reads its last row there,
+// which meets zeros.
+//
+// Schedule.  A persistent kernel (one workgroup per CU) walks a sequence of
+// tiles per workgroup with one load ring across tile boundaries: the first K
+// steps of the next tile are requested while the current one finishes, and a
+// finished tile leaves through the one ring slot that is free between two K
+// steps, its stores draining while the next tile's first steps run.
+//
+// Work plan (a small kernel at the start of the backward): a unit is an expert
+// -- or, with fewer than 16 experts, one of `parts` equal ranges of its tiles.
+// The units with rows are ranked by K steps, most first, and dealt to the 8
+// XCDs in snake order (0..7, 7..0, 0..7, ...): each XCD holds whole experts,
+// so an expert's operand panels are fetched into that XCD's L2 only, and every
+// XCD gets about the same number of K steps.  Inside an XCD the workgroups take
+// its tiles round-robin, unit after unit.  Experts without rows are listed
+// apart: their gradient tiles are zero.  The plan also holds poff and, for the
+// SwiGLU backward, the expert of every 64-row block of the padded K extents.
+// plan: [0..8] start of each XCD's unit list in plan[kPlanHead..]; [9] the
+// number of experts without rows, listed from plan[kPlanZero] on; [10] the
+// number of 64-row blocks (poff_E / 64); poff_0 .. poff_E from plan[kPlanPoff].
+constexpr int kPlanHead = 16;
+constexpr int kPlanZero = kPlanHead + kMaxExperts;
+constexpr int kPlanPoff = kPlanZero + kMaxExperts;
+constexpr int kPlanInts = kPlanPoff + kMaxExperts + 16;
+constexpr int kPlanThreads = 1024;
+constexpr int kWgradMinUnits = 2 * kXcds;    // fewer experts: each is split into parts
+constexpr int kMaxXcdUnits = 2 * kWave;      // unit list entries per XCD, two per lane
+constexpr int kEpiStores = kBM * kBN / 4 * 2 / 16 / kWave;  // 16-byte stores per wave for one tile
+static_assert(kMaxExperts == kPlanThreads, "one plan thread per unit");
+static_assert(kMaxExperts <= kXcds * kMaxXcdUnits, "an XCD's unit list fits two entries per lane");
+static_assert(kEpiStores == 32 && kLoads + kEpiStores < 64, "vmcnt range of the waits below");
+
+int wgrad_parts(int e) { return e >= kWgradMinUnits ? 1 : (kWgradMinUnits + e - 1) / e; }
+
+// 64-row blocks of the K-major copies: at most one partial block per expert.
+int64_t kmajor_blocks(int64_t rows, int e) { return rows / kBK + e + 1; }
+
+__global__ __launch_bounds__(kPlanThreads) void wgrad_plan_kernel(const int32_t *__restrict__ tokens_per_expert,
+                                                                  int e, int parts, int32_t *__restrict__ plan,
+                                                                  int32_t *__restrict__ block_expert) {
+  __shared__ int32_t cost[kPlanThreads];
+  __shared__ int32_t poff[kMaxExperts + 1];
+  __shared__ int32_t count[kXcds];
+  __shared__ int32_t zero_in_wave[kPlanThreads / kWave];
+  __shared__ int32_t steps_in_wave[kPlanThreads / kWave];
+  const int u = threadIdx.x, l = lane_id(), wv = u / kWave;
+  const int units = e * parts;
+  // a unit's cost: two per K step and one for the tile's fixed work; -1: no rows
+  int c = -1;
+  if (u < units) {
+    const int rows = tokens_per_expert[u / parts];
+    if (rows > 0) c = 2 * ((rows + kBK - 1) / kBK) + 1;
+  }
+  cost[u] = c;
+  if (u < kXcds) count[u] = 0;
+  // per expert u: K steps (kp_u / 64), scanned over the block; no rows
+  const int rows_u = u < e ? tokens_per_expert[u] : 0;
+  const int steps = (rows_u + kBK - 1) / kBK;
+  int incl = steps;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(incl, off, kWave);
+    if (l >= off) incl += o;
+  }
+  const bool zero = u < e && rows_u == 0;
+  const uint64_t zb = __ballot(zero);
+  if (l == 0) zero_in_wave[wv] = __popcll(zb);
+  if (l == kWave - 1) steps_in_wave[wv] = incl;
+  __syncthreads();
+  int rank = 0, xcd = 0;
+  if (c >= 0) {
+    for (int v = 0; v < units; ++v) {
+      const int cv = cost[v];
+      rank += (cv > c || (cv == c && v < u)) ? 1 : 0;
+    }
+    xcd = ((rank / kXcds) & 1) ? kXcds - 1 - rank % kXcds : rank % kXcds;
+    atomicAdd(&count[xcd], 1);
+  }
+  int zpos = __popcll(zb & ((1ull << l) - 1ull)), sbase = 0, stotal = 0, ztotal = 0;
+  for (int i = 0; i < kPlanThreads / kWave; ++i) {
+    zpos += i < wv ? zero_in_wave[i] : 0;
+    sbase += i < wv ? steps_in_wave[i] : 0;
+    stotal += steps_in_wave[i];
+    ztotal += zero_in_wave[i];
+  }
+  if (u < e) poff[u] = (sbase + incl - steps) * kBK;
+  if (u == 0) poff[e] = stotal * kBK;
+  __syncthreads();
+  // the unit of rank r sits at position r / 8 of its XCD's list
+  int start = 0;
+  for (int x = 0; x < xcd; ++x) start += count[x];
+  if (c >= 0) plan[kPlanHead + start + rank / kXcds] = u;
+  if (zero) plan[kPlanZero + zpos] = u;
+  if (u <= kXcds) {
+    int s = 0;
+    for (int x = 0; x < u; ++x) s += count[x];
+    plan[u] = s;
+  }
+  if (u == kXcds + 1) plan[9] = ztotal;
+  if (u == kXcds + 2) plan[10] = stotal;
+  if (u <= e) plan[kPlanPoff + u] = poff[u];
+  // the expert of each 64-row block: the last one whose first block is <= t
+  for (int t = u; t < stotal; t += kPlanThreads) {
+    int lo = 0, hi = e - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (poff[mid] <= t * kBK) lo = mid;
+      else hi = mid - 1;
+    }
+    block_expert[t] = lo;
+  }
+}
+
+// One output tile of a weight gradient: expert x, output rows m0 .. m0 +
+// rows_valid - 1 and columns n0 .. n0 + 255 (those below N); K extent k_len
+// (the expert's rows) in KT steps, from row r0 of the segment buffer (the
+// K-major operand) and from K position 0 of the expert's part at poff of the
+// K-major copy.
+struct WgTile {
+  int x, m0, n0, rows_valid, k_len, KT, r0, poff;
+};
+
+// kAT: A is the K-major input and B the K-contiguous copy (dW_down = dy^T a);
+// else A is the copy and B the input (dW_gate_up = [dG | dU]^T x).  kNFast: a
+// unit's tiles run n-tile fastest (else m-tile fastest).  The workgroups of an
+// XCD work on consecutive tiles side by side, so the faster index should be
+// the operand with fewer tiles: each pass over it re-reads the smaller panel
+// set.
+template <bool kNFast, bool kAT>
+__global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int M, int N, int m_tiles, int n_tiles, int parts,
+    const int32_t *__restrict__ tokens_per_expert, const int32_t *__restrict__ expert_offsets,
+    const int32_t *__restrict__ plan, uint16_t *__restrict__ C, uint16_t *__restrict__ C_rep, int e_master) {
+  constexpr bool kBT = !kAT;
+  __shared__ __attribute__((aligned(1024))) char ring[kSlots * kOperandBytes];
+  const int l = lane_id();
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wm = w >> 1, wn = w & 1;
+  const int per_e = m_tiles * n_tiles;
+  const int chunk = (per_e + parts - 1) / parts;
+  auto out_base = [&](int x) {
+    return x < e_master ? C + (int64_t)x * M * N : C_rep + (int64_t)(x - e_master) * M * N;
+  };
+  auto tile_at = [&](int loc, int &m0, int &n0) {
+    m0 = (kNFast ? loc / n_tiles : loc % m_tiles) * kBM;
+    n0 = (kNFast ? loc % n_tiles : loc / m_tiles) * kBN;
+  };
+
+  // experts without rows: their tiles are zero, dealt over the whole grid
+  {
+    const int nz = plan[9];
+    const int64_t zt_end = (int64_t)nz * per_e;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int64_t zt = blockIdx.x; zt < zt_end; zt += gridDim.x) {
+      int m0, n0;
+      tile_at((int)(zt % per_e), m0, n0);
+      uint16_t *cb = out_base(plan[kPlanZero + (int)(zt / per_e)]);
+      for (int i = threadIdx.x; i < kBM * (kBN / 8); i += kThreads) {
+        const int row = m0 + i / (kBN / 8), col = n0 + (i % (kBN / 8)) * 8;
+        if (row < M && col < N) st16(cb + (int64_t)row * N + col, z);
+      }
+    }
+  }
+
+  // this XCD's unit list, two entries per lane: entry i in lane i % 64 of
+  // entry array [i / 64], with its expert's row count, segment start and poff
+  const int xcd = blockIdx.x % kXcds, J = gridDim.x / kXcds, j = blockIdx.x / kXcds;
+  if (j >= J) return;
+  const int n_units = plan[xcd + 1] - plan[xcd];
+  int ent_u[2], ent_k[2], ent_r[2], ent_p[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int i = h * kWave + l;
+    ent_u[h] = i < n_units ? plan[kPlanHead + plan[xcd] + i] : 0;
+    const int x = ent_u[h] / parts;
+    ent_k[h] = tokens_per_expert[x];
+    ent_r[h] = expert_offsets[x];
+    ent_p[h] = plan[kPlanPoff + x];
+  }
+  auto entry = [&](const int (&v)[2], int i) {
+    return i < kWave ? __builtin_amdgcn_readlane(v[0], i) : __builtin_amdgcn_readlane(v[1], i - kWave);
+  };
+  // walks: list entry ui, whose first tile is the XCD's tile `base`; moves to
+  // the XCD's tile t (not before the walk's position); false past the list's end
+  struct Walk {
+    int ui, base;
+  };
+  auto walk_to = [&](Walk &wk, int t, WgTile &T) -> bool {
+    while (wk.ui < n_units) {
+      const int u = entry(ent_u, wk.ui);
+      const int first = (u % parts) * chunk;
+      const int last = first + chunk < per_e ? first + chunk : per_e;
+      const int nt = last > first ? last - first : 0;
+      if (t < wk.base + nt) {
+        T.x = u / parts;
+        tile_at(first + t - wk.base, T.m0, T.n0);
+        T.rows_valid = M - T.m0 < kBM ? M - T.m0 : kBM;
+        T.k_len = entry(ent_k, wk.ui);
+        T.r0 = entry(ent_r, wk.ui);
+        T.poff = entry(ent_p, wk.ui);
+        T.KT = (T.k_len + kBK - 1) / kBK;
+        return true;
+      }
+      wk.base += nt;
+      ++wk.ui;
+    }
+    return false;
+  };
+
+  // the load cursor (tile lt, K step lkt) runs two steps ahead of the compute
+  // cursor (tile ct); each walks the same tile sequence
+  Walk lw = {0, 0}, cw = {0, 0};
+  WgTile lt, ct;
+  int lt_t = j, ct_t = j;
+  if (!walk_to(lw, lt_t, lt)) return;
+  cw = lw;
+  ct = lt;
+  int lkt = 0;
+  bool have_load = true;
+
+  // Direct loads.  The K-major input: row k of a step holds 256 columns in 512
+  // bytes; this wave fills rows w*16 .. w*16+15, two per instruction: lane l
+  // fills row k = w*16 + 2i + l/32, 16-byte position l % 32 with chunk
+  // position ^ swz_t(k); columns past the operand's end re-read its last
+  // chunk, rows past the K extent its last row.  The K-contiguous copy: tile
+  // row r (an output row or column) holds K step kt in 128 bytes; this wave
+  // fills rows w*64 .. w*64+63, 8 per instruction: lane l fills row
+  // w*64 + 8i + l/8, position l % 8 with chunk position ^ swz(r); rows past the
+  // operand's end re-read its last row.
+  uint32_t a_off[kLoads], b_off[kLoads];
+  auto set_offsets = [&]() {
+    const uint32_t kp2 = (uint32_t)lt.KT * (uint32_t)kRowBytes;  // bytes per row of the copy
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int k = w * 16 + 2 * i + l / 32;
+      const int ct8 = ((l % 32) ^ swz_t(k)) * 8;
+      const int r = w * 64 + i * kLoadRows + l / kChunks;
+      const uint32_t cc = (uint32_t)(((l % kChunks) ^ swz(r)) * 16);
+      if constexpr (kAT) {
+        a_off[i] = (uint32_t)(ct8 > lt.rows_valid - 8 ? lt.rows_valid - 8 : ct8) * 2u;
+        b_off[i] = (uint32_t)(r < N - lt.n0 ? r : N - lt.n0 - 1) * kp2 + cc;
+      } else {
+        a_off[i] = (uint32_t)(r < lt.rows_valid ? r : lt.rows_valid - 1) * kp2 + cc;
+        b_off[i] = (uint32_t)(ct8 > N - lt.n0 - 8 ? N - lt.n0 - 8 : ct8) * 2u;
+      }
+    }
+  };
+  set_offsets();
+  const uint32_t ring_lds = lds_address(ring) + w * 64 * kRowBytes;  // = w * 16 * kTRowBytes
+  auto load_a = [&](int slot, int i) {
+    const uint32_t dst = ring_lds + slot * kOperandBytes + i * 1024;
+    if constexpr (kAT) {
+      const int k = w * 16 + 2 * i + l / 32, last = lt.k_len - 1 - lkt * kBK;
+      const char *base = reinterpret_cast<const char *>(A + ((int64_t)lt.r0 + (int64_t)lkt * kBK) * M + lt.m0);
+      dma16(base, a_off[i] + (uint32_t)(k < last ? k : last) * (uint32_t)M * 2u, dst);
+    } else {
+      const char *base = reinterpret_cast<const char *>(A + (int64_t)M * lt.poff + (int64_t)lt.m0 * lt.KT * kBK +
+                                                        (int64_t)lkt * kBK);
+      dma16(base, a_off[i], dst);
+    }
+  };
+  auto load_b = [&](int slot, int i) {
+    const uint32_t dst = ring_lds + slot * kOperandBytes + i * 1024;
+    if constexpr (kBT) {
+      const int k = w * 16 + 2 * i + l / 32, last = lt.k_len - 1 - lkt * kBK;
+      const char *base = reinterpret_cast<const char *>(B + ((int64_t)lt.r0 + (int64_t)lkt * kBK) * N + lt.n0);
+      dma16(base, b_off[i] + (uint32_t)(k < last ? k : last) * (uint32_t)N * 2u, dst);
+    } else {
+      const char *base = reinterpret_cast<const char *>(B + (int64_t)N * lt.poff + (int64_t)lt.n0 * lt.KT * kBK +
+                                                        (int64_t)lkt * kBK);
+      dma16(base, b_off[i], dst);
+    }
+  };
+  auto advance_load = [&]() {
+    if (++lkt == lt.KT) {
+      lkt = 0;
+      lt_t += J;
+      have_load = walk_to(lw, lt_t, lt);
+      if (have_load) set_offsets();
+    }
+  };
+  uint32_t ta[4][2], tb[4][2];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      ta[q][h] = kAT ? tr_off(l, 2 * q + wm, h) : 0u;
+      tb[q][h] = kBT ? tr_off(l, 4 * wn + q, h) : 0u;
+    }
+  constexpr int kReads = 12;
+
+  f32x16 acc[4][4];
+
+  // a finished tile: each wave converts its 128 x 128 sub-tile to bf16 and
+  // writes it out in four rounds of one 32-row block through its 8 KiB of the
+  // free ring slot (16-byte chunks XOR-swizzled by row), as whole 256-byte rows
+  // of 16-byte stores -- 32 store instructions per wave
+  auto store_tile = [&](const WgTile &T, char *slot, bool whole) {
+    char *stage = slot + w * (kOperandBytes / 4);
+    uint16_t *cb = out_base(T.x);
+    const int ch = l % 16, col = T.n0 + wn * 128 + ch * 8;
+    const int rr = l & 31;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16 &c = acc[mi][ni];
+          const int f = ni * 32 + 8 * g + 4 * (l >> 5);
+          *reinterpret_cast<uint2 *>(stage + rr * 256 + ((f >> 3) ^ (rr & 15)) * 16 + (f & 7) * 2) =
+              make_uint2(pack_bf16x2(c[4 * g], c[4 * g + 1]), pack_bf16x2(c[4 * g + 2], c[4 * g + 3]));
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+      __builtin_amdgcn_wave_barrier();
+      // all eight reads first, then the stores (one LDS round trip per block);
+      // a whole tile stores unconditionally
+      u32x4 v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int r = l / 16 + 4 * q;
+        v[q] = *reinterpret_cast<const u32x4 *>(stage + r * 256 + (ch ^ (r & 15)) * 16);
+      }
+      uint16_t *c_blk = cb + (int64_t)(T.m0 + (2 * mi + wm) * 32 + l / 16) * N + col;
+      if (whole) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) st16(c_blk + (int64_t)(4 * q) * N, v[q]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int row = T.m0 + (2 * mi + wm) * 32 + l / 16 + 4 * q;
+          if (row < M && col < N) st16(c_blk + (int64_t)(4 * q) * N, v[q]);
+        }
+      }
+    }
+  };
+
+  // prologue: the first two K steps of the sequence (B tiles in slots 0 and 2,
+  // A tiles in 1 and 3)
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) load_b(0, i);
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) load_a(1, i);
+  advance_load();
+  if (have_load) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) load_b(2, i);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) load_a(3, i);
+    advance_load();
+    wait_vmcnt<2 * kLoads>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  lds_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8 fa[2][4], fb[2][4];
+  load_frags<false, kAT, kBT>(ring + kOperandBytes, ring, 0, wm, wn, l, fa[0], fb[0], ta, tb);
+  __builtin_amdgcn_sched_barrier(0);
+
+  // The K steps of the whole sequence, as in the grouped GEMM's K loop: step s
+  // reads slots sb (B) and sa (A); its slices 0 and 1 load step s+2's B tile
+  // into slot pb, slice 3 its A tile into slot sb; after slice 2 every wave
+  // waits for step s+1's tiles and passes a barrier.  A tile's last step is
+  // followed by its output, staged in slot sa (free until step s+1 loads step
+  // s+3's B tile there); those 32 stores per wave are issued after step s+2's
+  // loads, so the wait of step s+1 lets them stay in flight (memory operations
+  // of a wave complete in issue order) -- unless the tile was ragged and
+  // issued fewer.
+  int sb = 0, sa = 1;
+  bool stores_ahead = false;
+  for (;;) {
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.0f;
+    int free_slot = sa;
+    for (int ckt = 0; ckt < ct.KT; ++ckt) {
+      const int nb = sb + 2 < kSlots ? sb + 2 : sb + 2 - kSlots;
+      const int na = sa + 2 < kSlots ? sa + 2 : sa + 2 - kSlots;
+      const int pb = na + 1 < kSlots ? na + 1 : na + 1 - kSlots;
+      const char *as = ring + sa * kOperandBytes;
+      const char *bs = ring + sb * kOperandBytes;
+      load_frags<false, kAT, kBT>(as, bs, 1, wm, wn, l, fa[1], fb[1], ta, tb);
+      slice<4, kReads>(fa[0], fb[0], acc, [&](int d) {
+        if (have_load) load_b(pb, d);
+      });
+      load_frags<false, kAT, kBT>(as, bs, 2, wm, wn, l, fa[0], fb[0], ta, tb);
+      slice<4, kReads>(fa[1], fb[1], acc, [&](int d) {
+        if (have_load) load_b(pb, 4 + d);
+      });
+      load_frags<false, kAT, kBT>(as, bs, 3, wm, wn, l, fa[1], fb[1], ta, tb);
+      slice<4, kReads>(fa[0], fb[0], acc, [&](int) {});
+      if (have_load) {
+        if (stores_ahead) wait_vmcnt<kLoads + kEpiStores>();
+        else wait_vmcnt<kLoads>();
+      } else {
+        if (stores_ahead) wait_vmcnt<kEpiStores>();
+        else wait_vmcnt<0>();
+      }
+      stores_ahead = false;
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // step s+1's first fragments (after the sequence's last step: stale, unused)
+      load_frags<false, kAT, kBT>(ring + na * kOperandBytes, ring + nb * kOperandBytes, 0, wm, wn, l, fa[0], fb[0],
+                                  ta, tb);
+      slice<4, kReads>(fa[1], fb[1], acc, [&](int d) {
+        if (have_load) {
+          load_a(sb, 2 * d);
+          load_a(sb, 2 * d + 1);
+        }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+      if (have_load) advance_load();
+      free_slot = sa;
+      sb = nb;
+      sa = na;
+    }
+    const bool whole = ct.rows_valid == kBM && ct.n0 + kBN <= N;
+    store_tile(ct, ring + free_slot * kOperandBytes, whole);
+    stores_ahead = whole;  // all 32 stores issued
+    ct_t += J;
+    if (!walk_to(cw, ct_t, ct)) break;
+  }
+}
+
 // ------------------------------------------------------------------ backward
 
-// SwiGLU backward, 8 features per thread.  For row r and feature i, with
+// SwiGLU backward, one 64-row block of an expert's padded K extent and up to
+// kSwFeatures features per workgroup (blockIdx.y), 64 features at a time.  For row r and feature i, with
 // g = gu[r, i], u = gu[r, I+i], da = d_act[r, i], s = sigmoid(g):
 //   dgu[r, i]     = bf16(da * u * s * (1 + g * (1 - s)))   (silu'(g) = s (1 + g (1 - s)))
 //   dgu[r, I + i] = bf16(da * g * s)
-//   d_act[r, i]  <- bf16(g * s * u)                         (the activation itself)
-// fp32 arithmetic.  Every element is read and written by the same thread, so
-// dgu may be gu (in place).
-__global__ __launch_bounds__(kThreads) void swiglu_bwd_kernel(const uint16_t *gu, uint16_t *dgu, uint16_t *d_act,
-                                                              int64_t rows, int inter) {
-  const int per_row = inter / 8;
-  const int64_t n = rows * per_row;
-  for (int64_t idx = (int64_t)blockIdx.x * kThreads + threadIdx.x; idx < n; idx += (int64_t)gridDim.x * kThreads) {
-    const int64_t r = idx / per_row;
-    const int c = (int)(idx % per_row) * 8;
-    const uint16_t *pg = gu + r * 2 * inter + c;
-    uint16_t *qg = dgu + r * 2 * inter + c;
-    uint16_t *pa = d_act + r * inter + c;
-    float g[8], u[8], da[8], dg[8], du[8], a[8];
-    Vec16<true>::unpack(ld16(pg), g);
-    Vec16<true>::unpack(ld16(pg + inter), u);
-    Vec16<true>::unpack(ld16(pa), da);
+//   a[r, i]       = bf16(g * s * u)                         (the activation itself)
+// fp32 arithmetic.  dgu is written [rows, 2I] (for dx); every element is read
+// and written by the same thread, so dgu may be gu (in place).  a and
+// [dG | dU] also go to the K-major copies aT ([I][kp_e] per expert) and gT
+// ([2I][kp_e]) that the weight gradients read, with zeros at the padded K
+// positions.  The transposition goes through LDS: a thread holds two rows x 8
+// features and writes each feature's pair of values as one 32-bit word of the
+// feature's 128-byte LDS row, word k/2 at position k/2 ^ 4*(feature/8) (the 32
+// lanes of each half-wave then hit 32 distinct banks); each thread then reads
+// 16 K values of one feature as two 16-byte reads and stores them.
+constexpr int kSwThreads = 256;
+constexpr int kSwFeatures = 256;
+__global__ __launch_bounds__(kSwThreads) void swiglu_bwd_kernel(
+    const uint16_t *gu, uint16_t *dgu, const uint16_t *__restrict__ d_act, int inter,
+    const int32_t *__restrict__ tokens_per_expert, const int32_t *__restrict__ expert_offsets,
+    const int32_t *__restrict__ plan, const int32_t *__restrict__ block_expert, uint16_t *__restrict__ aT,
+    uint16_t *__restrict__ gT) {
+  __shared__ __attribute__((aligned(16))) uint32_t tile[3][64 * 32];  // a, dG, dU: [feature][k/2] words
+  const int b = blockIdx.x;
+  if (b >= plan[10]) return;
+  const int x = block_expert[b];
+  const int rows_x = tokens_per_expert[x];
+  const int64_t kp = (int64_t)((rows_x + kBK - 1) / kBK) * kBK;
+  const int64_t poff = plan[kPlanPoff + x];
+  const int kb = b * kBK - (int)poff;  // the block's first K position inside the expert
+  const int valid = rows_x - kb < kBK ? rows_x - kb : kBK;
+  const int64_t r0 = (int64_t)expert_offsets[x] + kb;
+  const int t = threadIdx.x;
+  const int kpair = t / 8, fg = t % 8;  // rows 2*kpair, 2*kpair+1 of the block; features fg*8 .. fg*8+7
+  const int tf = t / 4, tq = t % 4;     // transposed: feature tf, K positions 16*tq .. 16*tq+15
+  const int swz_w = 4 * fg, swz_r = 4 * (tf / 8);
+  uint16_t *a_row = aT + (int64_t)inter * poff + (int64_t)tf * kp + kb + 16 * tq;
+  uint16_t *g_row = gT + (int64_t)2 * inter * poff + (int64_t)tf * kp + kb + 16 * tq;
+  const int f_end = (int)blockIdx.y * kSwFeatures + kSwFeatures < inter ? (int)blockIdx.y * kSwFeatures + kSwFeatures
+                                                                          : inter;
+  for (int f0 = (int)blockIdx.y * kSwFeatures; f0 < f_end; f0 += 64) {
+    uint32_t wa[8], wg[8], wu[8];  // per feature: the two rows' bf16 values, row 2*kpair low
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = 2 * kpair + h;
+      float dg[8], du[8], a[8];
+      if (k < valid) {
+        const int64_t r = r0 + k;
+        const uint16_t *pg = gu + r * 2 * inter + f0 + fg * 8;
+        float g[8], u[8], da[8];
+        Vec16<true>::unpack(ld16(pg), g);
+        Vec16<true>::unpack(ld16(pg + inter), u);
+        Vec16<true>::unpack(ld16(d_act + r * inter + f0 + fg * 8), da);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float sg = 1.0f / (1.0f + __expf(-g[i]));
+          const float gs = g[i] * sg;
+          dg[i] = da[i] * u[i] * (sg * (1.0f + g[i] * (1.0f - sg)));
+          du[i] = da[i] * gs;
+          a[i] = gs * u[i];
+        }
+        uint16_t *qg = dgu + r * 2 * inter + f0 + fg * 8;
+        st16(qg, Vec16<true>::pack(dg));
+        st16(qg + inter, Vec16<true>::pack(du));
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dg[i] = du[i] = a[i] = 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t sh = 16 * h;
+        const uint32_t ba = bf16_bits(a[i]), bg = bf16_bits(dg[i]), bu = bf16_bits(du[i]);
+        wa[i] = h ? (wa[i] | (ba << sh)) : ba;
+        wg[i] = h ? (wg[i] | (bg << sh)) : bg;
+        wu[i] = h ? (wu[i] | (bu << sh)) : bu;
+      }
+    }
+    __syncthreads();  // the previous feature block's transposed reads are done
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const float sg = 1.0f / (1.0f + __expf(-g[i]));
-      const float gs = g[i] * sg;
-      dg[i] = da[i] * u[i] * (sg * (1.0f + g[i] * (1.0f - sg)));
-      du[i] = da[i] * gs;
-      a[i] = gs * u[i];
+      const int wi = (fg * 8 + i) * 32 + (kpair ^ swz_w);
+      tile[0][wi] = wa[i];
+      tile[1][wi] = wg[i];
+      tile[2][wi] = wu[i];
     }
-    st16(qg, Vec16<true>::pack(dg));
-    st16(qg + inter, Vec16<true>::pack(du));
-    st16(pa, Vec16<true>::pack(a));
+    __syncthreads();
+    const int w0 = tf * 32 + ((8 * tq) ^ swz_r), w1 = tf * 32 + ((8 * tq + 4) ^ swz_r);
+    const int64_t fo = (int64_t)f0 * kp;
+    st16(a_row + fo, *reinterpret_cast<const u32x4 *>(&tile[0][w0]));
+    st16(a_row + fo + 8, *reinterpret_cast<const u32x4 *>(&tile[0][w1]));
+    st16(g_row + fo, *reinterpret_cast<const u32x4 *>(&tile[1][w0]));
+    st16(g_row + fo + 8, *reinterpret_cast<const u32x4 *>(&tile[1][w1]));
+    st16(g_row + fo + (int64_t)inter * kp, *reinterpret_cast<const u32x4 *>(&tile[2][w0]));
+    st16(g_row + fo + (int64_t)inter * kp + 8, *reinterpret_cast<const u32x4 *>(&tile[2][w1]));
   }
 }
 
@@ -940,28 +1375,80 @@ hipError_t launch_plain(const uint16_t *A, const uint16_t *B, const uint16_t *B_
   const int nt = (N + kBN - 1) / kBN;
   const int64_t g = tile_bound(rows, e, capacity, nt);
   if (g > INT32_MAX) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((grouped_gemm_kernel<kModePlain, false, kBT>), dim3((unsigned)g), dim3(kThreads), 0, stream, A,
-                     B, b_stride, K, 0, N, 0, nt, tokens_per_expert, expert_offsets, e, C, (int64_t)N, nullptr, B_rep,
-                     nullptr, e_master, nullptr, nullptr, nullptr);
+  hipLaunchKernelGGL((grouped_gemm_kernel<kModePlain, kBT>), dim3((unsigned)g), dim3(kThreads), 0, stream, A, B,
+                     b_stride, K, N, nt, tokens_per_expert, expert_offsets, e, C, (int64_t)N, nullptr, B_rep, e_master,
+                     nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 
-// Weight-gradient GEMM: C_e [M, N] = A_e^T B_e for every expert, A_e [rows_e, M]
-// and B_e [rows_e, N] the rows of expert e's segment.
+// Workgroups of the persistent weight-gradient kernel: one per CU (its LDS
+// ring takes a CU's whole LDS), a multiple of the 8 XCDs.  The CU count is read
+// once per device.
+int persistent_grid() {
+  static int cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cus[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < kXcds) n = 256;
+    cus[dev] = n / kXcds * kXcds;
+  }
+  return cus[dev];
+}
+
+// Weight-gradient GEMM: C_e [M, N] = A_e^T B_e for every expert over the rows of
+// its segment, on the work plan `plan` (wgrad_plan_kernel over the same row
+// counts).  kAT: A is the K-major input [rows, M] and B the K-contiguous copy
+// ([N][kp_e] per expert); else A is the copy ([M][kp_e]) and B the input
+// [rows, N].
+template <bool kAT>
 hipError_t launch_wgrad(const uint16_t *A, const uint16_t *B, int M, int N, int e, const int32_t *tokens_per_expert,
-                        const int32_t *expert_offsets, uint16_t *C, uint16_t *C_rep, int e_master, hipStream_t stream) {
+                        const int32_t *expert_offsets, const int32_t *plan, uint16_t *C, uint16_t *C_rep, int e_master,
+                        hipStream_t stream) {
   const int mt = (M + kBM - 1) / kBM, nt = (N + kBN - 1) / kBN;
-  const int chunk = (mt * nt + kXcds - 1) / kXcds;
-  hipLaunchKernelGGL((grouped_gemm_kernel<kModeWGrad, true, true>), dim3((unsigned)(kXcds * e * chunk)),
-                     dim3(kThreads), 0, stream, A, B, (int64_t)0, 0, M, N, mt, nt, tokens_per_expert, expert_offsets,
-                     e, C, (int64_t)N, nullptr, nullptr, C_rep, e_master, nullptr, nullptr, nullptr);
+  const int parts = wgrad_parts(e);
+  if (nt <= mt)
+    hipLaunchKernelGGL((wgrad_kernel<true, kAT>), dim3((unsigned)persistent_grid()), dim3(kThreads), 0, stream, A, B,
+                       M, N, mt, nt, parts, tokens_per_expert, expert_offsets, plan, C, C_rep, e_master);
+  else
+    hipLaunchKernelGGL((wgrad_kernel<false, kAT>), dim3((unsigned)persistent_grid()), dim3(kThreads), 0, stream, A,
+                       B, M, N, mt, nt, parts, tokens_per_expert, expert_offsets, plan, C, C_rep, e_master);
   return hipGetLastError();
+}
+
+// Workspace of the backward, in order: [dG | dU] [rows, 2I] (holding the
+// recomputed [G | U] before, when the forward did not store them); dA [rows,
+// I]; the weight gradients' work plan; the expert of each 64-row block of the
+// K-major copies; the K-major copies of the activation (I features) and of
+// [dG | dU] (2I features), each over at most kmajor_blocks * 64 K positions.
+struct BwdWorkspace {
+  uint16_t *gu, *dact;
+  int32_t *plan, *block_expert;
+  uint16_t *aT, *gT;
+};
+
+BwdWorkspace carve_bwd(void *workspace, int64_t rows, int inter, int e, size_t *total) {
+  const size_t kb = (size_t)kmajor_blocks(rows, e);
+  const size_t sizes[6] = {align256(4 * (size_t)rows * inter), align256(2 * (size_t)rows * inter),
+                           align256(4 * (size_t)kPlanInts), align256(4 * kb),
+                           align256(2 * (size_t)inter * kb * kBK), align256(4 * (size_t)inter * kb * kBK)};
+  char *p[6];
+  size_t off = 0;
+  for (int i = 0; i < 6; ++i) {
+    p[i] = static_cast<char *>(workspace) + off;
+    off += sizes[i];
+  }
+  if (total) *total = off;
+  return {reinterpret_cast<uint16_t *>(p[0]), reinterpret_cast<uint16_t *>(p[1]), reinterpret_cast<int32_t *>(p[2]),
+          reinterpret_cast<int32_t *>(p[3]), reinterpret_cast<uint16_t *>(p[4]), reinterpret_cast<uint16_t *>(p[5])};
 }
 
 }  // namespace
 
-size_t ffn_bwd_workspace_bytes(int64_t rows, int inter) {
-  return align256(4 * (size_t)rows * inter) + align256(2 * (size_t)rows * inter);
+size_t ffn_bwd_workspace_bytes(int64_t rows, int inter, int e) {
+  size_t total = 0;
+  carve_bwd(nullptr, rows, inter, e, &total);
+  return total;
 }
 
 hipError_t launch_expert_ffn_bwd(const uint16_t *x_perm, const uint16_t *grad_y, int64_t rows, int64_t hidden,
@@ -973,36 +1460,39 @@ hipError_t launch_expert_ffn_bwd(const uint16_t *x_perm, const uint16_t *grad_y,
   const int em = rep ? rep->e_master : e;
   const uint16_t *wgu_r = rep ? rep->w_gate_up : nullptr, *wd_r = rep ? rep->w_down : nullptr;
   uint16_t *gwgu_r = rep ? rep->grad_w_gate_up : nullptr, *gwd_r = rep ? rep->grad_w_down : nullptr;
-  // workspace: [dG | dU] ([rows, 2I], holding the recomputed [G | U] before
-  // when gate_up is null); dA then the activation ([rows, I])
-  uint16_t *gu = static_cast<uint16_t *>(workspace);
-  uint16_t *dact = reinterpret_cast<uint16_t *>(static_cast<char *>(workspace) + align256(4 * (size_t)rows * inter));
+  if (e < 1 || e > kMaxExperts) return hipErrorInvalidValue;
+  const BwdWorkspace ws = carve_bwd(workspace, rows, inter, e, nullptr);
   const int H = (int)hidden, I = inter;
   hipError_t st;
 #define MOE_TRY(x)                    \
   if ((st = (x)) != hipSuccess) return st;
+  // the weight gradients' work plan, the padded K extents and their blocks' experts
+  hipLaunchKernelGGL(wgrad_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, tokens_per_expert, e, wgrad_parts(e),
+                     ws.plan, ws.block_expert);
+  MOE_TRY(hipGetLastError());
   if (rows > 0) {
     // [G | U] = x W_gate_up^T unless saved by the forward; dA = dy W_down (W_down [H, I]: K-major)
     if (!gate_up)
       MOE_TRY(launch_plain<false>(x_perm, w_gate_up, wgu_r, em, (int64_t)2 * I * H, H, 2 * I, rows, e, capacity,
-                                  tokens_per_expert, expert_offsets, gu, stream));
+                                  tokens_per_expert, expert_offsets, ws.gu, stream));
     MOE_TRY(launch_plain<true>(grad_y, w_down, wd_r, em, (int64_t)I * H, H, I, rows, e, capacity, tokens_per_expert,
-                               expert_offsets, dact, stream));
-    // [dG | dU] (in place of the recomputed [G | U]); the activation in place of dA
-    const int64_t chunks = rows * (I / 8);
-    int64_t blocks = (chunks + kThreads - 1) / kThreads;
-    if (blocks > 65536) blocks = 65536;
-    hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream,
-                       gate_up ? gate_up : gu, gu, dact, rows, I);
+                               expert_offsets, ws.dact, stream));
+    // [dG | dU] (in place of the recomputed [G | U]) and the K-major copies of a and [dG | dU]
+    hipLaunchKernelGGL(swiglu_bwd_kernel,
+                       dim3((unsigned)kmajor_blocks(rows, e), (unsigned)((I + kSwFeatures - 1) / kSwFeatures)),
+                       dim3(kSwThreads), 0, stream,
+                       gate_up ? gate_up : ws.gu, ws.gu, ws.dact, I, tokens_per_expert, expert_offsets, ws.plan,
+                       ws.block_expert, ws.aT, ws.gT);
     MOE_TRY(hipGetLastError());
     // dx = [dG | dU] W_gate_up (W_gate_up [2I, H]: K-major)
-    MOE_TRY(launch_plain<true>(gu, w_gate_up, wgu_r, em, (int64_t)H * 2 * I, 2 * I, H, rows, e, capacity,
+    MOE_TRY(launch_plain<true>(ws.gu, w_gate_up, wgu_r, em, (int64_t)H * 2 * I, 2 * I, H, rows, e, capacity,
                                tokens_per_expert, expert_offsets, grad_x_perm, stream));
   }
   // dW_down_e = dy_e^T a_e;  [dW_gate; dW_up]_e = [dG | dU]_e^T x_e  (experts without rows: zeros)
-  MOE_TRY(launch_wgrad(grad_y, dact, H, I, e, tokens_per_expert, expert_offsets, grad_w_down, gwd_r, em, stream));
-  MOE_TRY(launch_wgrad(gu, x_perm, 2 * I, H, e, tokens_per_expert, expert_offsets, grad_w_gate_up, gwgu_r, em,
-                       stream));
+  MOE_TRY(launch_wgrad<true>(grad_y, ws.aT, H, I, e, tokens_per_expert, expert_offsets, ws.plan, grad_w_down, gwd_r,
+                             em, stream));
+  MOE_TRY(launch_wgrad<false>(ws.gT, x_perm, 2 * I, H, e, tokens_per_expert, expert_offsets, ws.plan, grad_w_gate_up,
+                              gwgu_r, em, stream));
 #undef MOE_TRY
   return hipSuccess;
 }
@@ -1020,17 +1510,15 @@ hipError_t launch_expert_ffn(const uint16_t *x_perm, int64_t rows, int64_t hidde
   const int64_t g1 = tile_bound(rows, e, capacity, n1);
   const int64_t g2 = tile_bound(rows, e, capacity, (int)((hidden + kBN - 1) / kBN));
   if (g1 > INT32_MAX || g2 > INT32_MAX) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((grouped_gemm_kernel<kModeSwiGLU, false, false>), dim3((unsigned)g1), dim3(kThreads), 0, stream,
-                     x_perm, w_gate_up, (int64_t)2 * inter * hidden, (int)hidden, 0, inter, 0, n1, tokens_per_expert,
-                     expert_offsets, e, act, (int64_t)inter, gate_up, rep ? rep->w_gate_up : nullptr, nullptr, em,
-                     nullptr, nullptr, nullptr);
+  hipLaunchKernelGGL((grouped_gemm_kernel<kModeSwiGLU, false>), dim3((unsigned)g1), dim3(kThreads), 0, stream, x_perm,
+                     w_gate_up, (int64_t)2 * inter * hidden, (int)hidden, inter, n1, tokens_per_expert, expert_offsets,
+                     e, act, (int64_t)inter, gate_up, rep ? rep->w_gate_up : nullptr, em, nullptr, nullptr, nullptr);
   hipError_t st = hipGetLastError();
   if (st != hipSuccess) return st;
   const int n2 = (int)((hidden + kBN - 1) / kBN);
-  hipLaunchKernelGGL((grouped_gemm_kernel<kModePlain, false, false>), dim3((unsigned)g2), dim3(kThreads), 0, stream,
-                     act, w_down, (int64_t)hidden * inter, inter, 0, (int)hidden, 0, n2, tokens_per_expert,
-                     expert_offsets, e, y, hidden, nullptr, rep ? rep->w_down : nullptr, nullptr, em, nullptr, nullptr,
-                     nullptr);
+  hipLaunchKernelGGL((grouped_gemm_kernel<kModePlain, false>), dim3((unsigned)g2), dim3(kThreads), 0, stream, act,
+                     w_down, (int64_t)hidden * inter, inter, (int)hidden, n2, tokens_per_expert, expert_offsets, e, y,
+                     hidden, nullptr, rep ? rep->w_down : nullptr, em, nullptr, nullptr, nullptr);
   return hipGetLastError();
 }
 
@@ -1052,17 +1540,17 @@ hipError_t launch_expert_ffn_mxfp8(const uint8_t *x_q, const uint8_t *x_s, int64
   const int64_t g1 = tile_bound(rows, e, capacity, n1);
   const int64_t g2 = tile_bound(rows, e, capacity, n2);
   if (g1 > INT32_MAX || g2 > INT32_MAX) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((grouped_gemm_kernel<kModeSwiGLU, false, false, true>), dim3((unsigned)g1), dim3(kThreads), 0,
-                     stream, reinterpret_cast<const uint16_t *>(x_q), reinterpret_cast<const uint16_t *>(w_gate_up_q),
-                     (int64_t)2 * inter * hidden, (int)hidden, 0, inter, 0, n1, tokens_per_expert, expert_offsets, e,
-                     reinterpret_cast<uint16_t *>(act_q), (int64_t)inter, nullptr, nullptr, nullptr, e, x_s,
-                     w_gate_up_s, act_s);
+  hipLaunchKernelGGL((grouped_gemm_kernel<kModeSwiGLU, false, true>), dim3((unsigned)g1), dim3(kThreads), 0, stream,
+                     reinterpret_cast<const uint16_t *>(x_q), reinterpret_cast<const uint16_t *>(w_gate_up_q),
+                     (int64_t)2 * inter * hidden, (int)hidden, inter, n1, tokens_per_expert, expert_offsets, e,
+                     reinterpret_cast<uint16_t *>(act_q), (int64_t)inter, nullptr, nullptr, e, x_s, w_gate_up_s,
+                     act_s);
   hipError_t st = hipGetLastError();
   if (st != hipSuccess) return st;
-  hipLaunchKernelGGL((grouped_gemm_kernel<kModePlain, false, false, true>), dim3((unsigned)g2), dim3(kThreads), 0,
-                     stream, reinterpret_cast<const uint16_t *>(act_q), reinterpret_cast<const uint16_t *>(w_down_q),
-                     (int64_t)hidden * inter, inter, 0, (int)hidden, 0, n2, tokens_per_expert, expert_offsets, e, y,
-                     hidden, nullptr, nullptr, nullptr, e, act_s, w_down_s, nullptr);
+  hipLaunchKernelGGL((grouped_gemm_kernel<kModePlain, false, true>), dim3((unsigned)g2), dim3(kThreads), 0, stream,
+                     reinterpret_cast<const uint16_t *>(act_q), reinterpret_cast<const uint16_t *>(w_down_q),
+                     (int64_t)hidden * inter, inter, (int)hidden, n2, tokens_per_expert, expert_offsets, e, y, hidden,
+                     nullptr, nullptr, e, act_s, w_down_s, nullptr);
   return hipGetLastError();
 }
 

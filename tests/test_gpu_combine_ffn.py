@@ -210,6 +210,9 @@ def entries(t: torch.Tensor, idx) -> np.ndarray:
     (2000, 4, 2, 128, 320, 0),    # long expert segments: many K steps in the weight gradients
     (600, 8, 2, 256, 64, 1.0),    # capacity layout with drops and pads
     (5, 4, 1, 64, 64, 0),         # tiny, most experts empty
+    (300, 1, 1, 256, 192, 0),     # one expert: its weight-gradient tiles split over the XCDs
+    (400, 2, 1, 512, 256, 0),     # two experts
+    (2048, 64, 2, 1024, 512, 0),  # whole tiles of one or two K steps, several per workgroup in a row
 ])
 def test_expert_ffn_bwd_small_full_compare(moe, n, e, k, h, inter, cap):
     w, idx, wts, x, wgu, wd, xp, lay, y = ffn_case(moe, n, e, k, h, inter, cap, zero_expert=1 if e > 2 else None)

@@ -15,7 +15,8 @@ multiply-adds in slot order, so the bits agree), the dispatch backward.
 Tolerance (max|got - ref| / max|ref| per tensor): the FFN output on EVERY row
 (the oracle's segment-wise fp64 products with the two bf16 roundings), the
 combine backward, and the FFN backward of whole experts -- the hottest, the
-coldest non-empty one and the two with the most ragged last 256-row tile.
+two with the most ragged last 256-row tile, the most ragged last K step of the
+weight gradients and the eight least-loaded non-empty ones (one per XCD).
 Each oracle input is the oracle's own value where the GPU must match it bit for
 bit (routing indices, layout, scatter) and otherwise the GPU output that an
 earlier test proved within tolerance (router weights, y, grad_y)."""
@@ -139,12 +140,18 @@ def test_combine_bwd_full(layer):
 
 
 def bwd_experts(cnt: np.ndarray):
-    """The hottest expert, the coldest non-empty one and the two whose last 256-row
-    tile is the most ragged (fewest rows in it)."""
+    """The hottest expert, the two whose last 256-row tile is the most ragged
+    (fewest rows in it), the one with the fewest rows in its last 64-row K step of
+    the weight gradients, and the eight least-loaded non-empty ones -- the weight
+    gradients' work plan deals experts to the eight XCDs in order of load, so
+    these eight sit on eight different XCDs (the coldest among them)."""
     nz = np.nonzero(cnt > 0)[0]
-    pick = {int(np.argmax(cnt)), int(nz[np.argmin(cnt[nz])])}
+    pick = {int(np.argmax(cnt))}
     tail = (cnt[nz] - 1) % 256 + 1
     for i in np.argsort(tail, kind="stable")[:2]:
+        pick.add(int(nz[i]))
+    pick.add(int(nz[np.argmin((cnt[nz] - 1) % 64)]))
+    for i in np.argsort(cnt[nz], kind="stable")[:8]:
         pick.add(int(nz[i]))
     return sorted(pick)
 
