@@ -319,24 +319,43 @@ __global__ __launch_bounds__(kRowThreads) void combine_bwd_kernel(
       wts[j] = j0 + j < k ? topk_w[t * k + j0 + j] : 0.0f;
       dot[j] = 0.0f;
     }
-    for (int64_t v = threadIdx.x; v < vpr; v += kRowThreads) {
-      float gf[EL];
-      V::unpack(ld16_stream(g + v * 16), gf);
-      u32x4 yv[KC];
+    // two row segments per thread per round: 2*(KC+1) loads in flight
+    for (int64_t v0 = threadIdx.x; v0 < vpr; v0 += 2 * kRowThreads) {
+      const int64_t v1 = v0 + kRowThreads;
+      const bool has1 = v1 < vpr;
+      const u32x4 g0 = ld16_stream(g + v0 * 16);
+      u32x4 g1 = {0u, 0u, 0u, 0u};
+      if (has1) g1 = ld16_stream(g + v1 * 16);
+      u32x4 y0[KC], y1[KC];
 #pragma unroll
       for (int j = 0; j < KC; ++j)
-        if (rows[j] >= 0) yv[j] = ld16_stream(row_ptr(y, rows[j], row_bytes) + v * 16);
+        if (rows[j] >= 0) {
+          y0[j] = ld16_stream(row_ptr(y, rows[j], row_bytes) + v0 * 16);
+          if (has1) y1[j] = ld16_stream(row_ptr(y, rows[j], row_bytes) + v1 * 16);
+        }
+      float gf0[EL], gf1[EL];
+      V::unpack(g0, gf0);
+      V::unpack(g1, gf1);
 #pragma unroll
       for (int j = 0; j < KC; ++j) {
         if (rows[j] < 0) continue;
         float yf[EL], o[EL];
-        V::unpack(yv[j], yf);
+        V::unpack(y0[j], yf);
 #pragma unroll
         for (int i = 0; i < EL; ++i) {
-          dot[j] = __builtin_fmaf(gf[i], yf[i], dot[j]);
-          o[i] = wts[j] * gf[i];
+          dot[j] = __builtin_fmaf(gf0[i], yf[i], dot[j]);
+          o[i] = wts[j] * gf0[i];
         }
-        st16_stream(row_ptr(grad_y, rows[j], row_bytes) + v * 16, V::pack(o));
+        st16_stream(row_ptr(grad_y, rows[j], row_bytes) + v0 * 16, V::pack(o));
+        if (has1) {
+          V::unpack(y1[j], yf);
+#pragma unroll
+          for (int i = 0; i < EL; ++i) {
+            dot[j] = __builtin_fmaf(gf1[i], yf[i], dot[j]);
+            o[i] = wts[j] * gf1[i];
+          }
+          st16_stream(row_ptr(grad_y, rows[j], row_bytes) + v1 * 16, V::pack(o));
+        }
       }
     }
 #pragma unroll
