@@ -835,228 +835,243 @@ int64_t tile_bound(int64_t rows, int e, int capacity, int n_tiles) {
 // features * poff_e, where kp_e is the expert's row count rounded up to a
 // multiple of 64 (zeros after the last row) and poff_e the sum of kp over the
 // experts before e.  Measured on gfx950, a K step whose fragments all come
-// through transpose loads takes about twice as long as one with half of them
-// read as plain 16-byte rows.  The zero padding also makes the ragged last K
-// step exact without masking: the K-major operand re-reads its last row there,
-// which meets zeros.
+// through transpose loads takes about 1.5 times as long as one with half of
+// them read as plain 16-byte rows.  The zero padding also makes the ragged last
+// K step exact without masking: the K-major operand re-reads its last row
+// there, which meets zeros.
 //
-// Schedule.  A persistent kernel (one workgroup per CU) walks a sequence of
-// tiles per workgroup with one load ring across tile boundaries: the first K
-// steps of the next tile are requested while the current one finishes, and a
-// finished tile leaves through the one ring slot that is free between two K
-// steps, its stores draining while the next tile's first steps run.
-//
-// Work plan (a small kernel at the start of the backward): a unit is an expert
-// -- or, with fewer than 16 experts, one of `parts` equal ranges of its tiles.
-// The units with rows are ranked by K steps, most first, and dealt to the 8
-// XCDs in snake order (0..7, 7..0, 0..7, ...): each XCD holds whole experts,
-// so an expert's operand panels are fetched into that XCD's L2 only, and every
-// XCD gets about the same number of K steps.  Inside an XCD the workgroups take
-// its tiles round-robin, unit after unit.  Experts without rows are listed
-// apart: their gradient tiles are zero.  The plan also holds poff and, for the
-// SwiGLU backward, the expert of every 64-row block of the padded K extents.
-// plan: [0..8] start of each XCD's unit list in plan[kPlanHead..]; [9] the
-// number of experts without rows, listed from plan[kPlanZero] on; [10] the
-// number of 64-row blocks (poff_E / 64); poff_0 .. poff_E from plan[kPlanPoff].
-constexpr int kPlanHead = 16;
-constexpr int kPlanZero = kPlanHead + kMaxExperts;
-constexpr int kPlanPoff = kPlanZero + kMaxExperts;
+// Work plan (a small kernel at the start of the backward).  A unit is a range
+// of one expert's output tiles: the whole expert, or, when the expert holds
+// more than 1/16 of all K steps, one of ceil(16 * steps / all steps) equal
+// ranges.  Units are ranked by K steps per range, most first, and dealt to the
+// 8 XCDs in snake order (0..7, 7..0, 0..7, ...), so each XCD works through
+// whole experts or large parts of one: their operand panels are fetched into
+// that XCD's L2 only.  Experts without rows are units too (their tiles are
+// zero).  Each XCD's units form a list; a workgroup takes the next tile of its
+// XCD's list (workgroup b runs on XCD b % 8 and takes tile b / 8), so the
+// hardware's dispatch balances the tiles over the XCD's CUs as they free up
+// (simulated on the Zipf-loaded 32-expert layer: the XCD finishing last ends
+// 3 % after the mean; whole experts on fixed per-CU tile lists end 170 % after
+// it).
+// plan (int32): [0..8] first entry of each XCD's list; [9..16] and [17..24]
+// tiles of each XCD's list in dW_down and in dW_gate_up; [25] 64-row blocks of
+// the K-major copies (poff_E / 64); entries of kEntryInts from kPlanEntries
+// in XCD-list order: the unit (expert | part << 11 | parts << 21), the
+// expert's rows, its segment start, its poff, its first tile in dW_down's list
+// and in dW_gate_up's; poff_0 .. poff_E from kPlanPoff.
+constexpr int kWgradDiv = 16;
+constexpr int kMaxUnits = kMaxExperts + kWgradDiv;  // sum of ceil(16 steps_e / S) <= 16 + E
+constexpr int kEntryInts = 8;
+constexpr int kPlanEntries = 32;
+constexpr int kPlanPoff = kPlanEntries + kEntryInts * kMaxUnits;
 constexpr int kPlanInts = kPlanPoff + kMaxExperts + 16;
 constexpr int kPlanThreads = 1024;
-constexpr int kWgradMinUnits = 2 * kXcds;    // fewer experts: each is split into parts
-constexpr int kMaxXcdUnits = 2 * kWave;      // unit list entries per XCD, two per lane
+constexpr int kListLanes = 3;  // an XCD's list holds at most 3 * 64 entries
 constexpr int kEpiStores = kBM * kBN / 4 * 2 / 16 / kWave;  // 16-byte stores per wave for one tile
-static_assert(kMaxExperts == kPlanThreads, "one plan thread per unit");
-static_assert(kMaxExperts <= kXcds * kMaxXcdUnits, "an XCD's unit list fits two entries per lane");
-static_assert(kEpiStores == 32 && kLoads + kEpiStores < 64, "vmcnt range of the waits below");
+static_assert(kMaxExperts == kPlanThreads, "one plan thread per expert");
+static_assert((kMaxUnits + kXcds - 1) / kXcds <= kListLanes * kWave, "an XCD's list fits the lookup");
+static_assert(kMaxUnits <= 2 * kPlanThreads, "two units per plan thread");
 
-int wgrad_parts(int e) { return e >= kWgradMinUnits ? 1 : (kWgradMinUnits + e - 1) / e; }
+// Upper bound of the tiles of one XCD's list (the grid is 8 times that).
+int64_t wgrad_list_bound(int e, int per_e) { return (int64_t)((e + kWgradDiv + kXcds - 1) / kXcds) * per_e; }
 
 // 64-row blocks of the K-major copies: at most one partial block per expert.
 int64_t kmajor_blocks(int64_t rows, int e) { return rows / kBK + e + 1; }
 
-__global__ __launch_bounds__(kPlanThreads) void wgrad_plan_kernel(const int32_t *__restrict__ tokens_per_expert,
-                                                                  int e, int parts, int32_t *__restrict__ plan,
-                                                                  int32_t *__restrict__ block_expert) {
-  __shared__ int32_t cost[kPlanThreads];
-  __shared__ int32_t poff[kMaxExperts + 1];
-  __shared__ int32_t count[kXcds];
-  __shared__ int32_t zero_in_wave[kPlanThreads / kWave];
-  __shared__ int32_t steps_in_wave[kPlanThreads / kWave];
-  const int u = threadIdx.x, l = lane_id(), wv = u / kWave;
-  const int units = e * parts;
-  // a unit's cost: two per K step and one for the tile's fixed work; -1: no rows
-  int c = -1;
-  if (u < units) {
-    const int rows = tokens_per_expert[u / parts];
-    if (rows > 0) c = 2 * ((rows + kBK - 1) / kBK) + 1;
-  }
-  cost[u] = c;
-  if (u < kXcds) count[u] = 0;
-  // per expert u: K steps (kp_u / 64), scanned over the block; no rows
-  const int rows_u = u < e ? tokens_per_expert[u] : 0;
-  const int steps = (rows_u + kBK - 1) / kBK;
-  int incl = steps;
+// Tiles of part p of `parts` of an expert with per_e tiles.
+__device__ __forceinline__ int part_tiles(int p, int parts, int per_e, int &first) {
+  const int chunk = (per_e + parts - 1) / parts;
+  first = p * chunk;
+  const int last = first + chunk < per_e ? first + chunk : per_e;
+  return last > first ? last - first : 0;
+}
+
+// Inclusive scan of v over the 1024-thread block (tmp: 16 LDS words); total out.
+__device__ int block_scan(int v, int32_t *tmp, int &total) {
+  const int l = lane_id(), wv = threadIdx.x / kWave;
+  int incl = v;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
     const int o = __shfl_up(incl, off, kWave);
     if (l >= off) incl += o;
   }
-  const bool zero = u < e && rows_u == 0;
-  const uint64_t zb = __ballot(zero);
-  if (l == 0) zero_in_wave[wv] = __popcll(zb);
-  if (l == kWave - 1) steps_in_wave[wv] = incl;
+  if (l == kWave - 1) tmp[wv] = incl;
   __syncthreads();
-  int rank = 0, xcd = 0;
-  if (c >= 0) {
-    for (int v = 0; v < units; ++v) {
-      const int cv = cost[v];
-      rank += (cv > c || (cv == c && v < u)) ? 1 : 0;
-    }
-    xcd = ((rank / kXcds) & 1) ? kXcds - 1 - rank % kXcds : rank % kXcds;
-    atomicAdd(&count[xcd], 1);
-  }
-  int zpos = __popcll(zb & ((1ull << l) - 1ull)), sbase = 0, stotal = 0, ztotal = 0;
+  int base = 0;
+  total = 0;
   for (int i = 0; i < kPlanThreads / kWave; ++i) {
-    zpos += i < wv ? zero_in_wave[i] : 0;
-    sbase += i < wv ? steps_in_wave[i] : 0;
-    stotal += steps_in_wave[i];
-    ztotal += zero_in_wave[i];
+    base += i < wv ? tmp[i] : 0;
+    total += tmp[i];
   }
-  if (u < e) poff[u] = (sbase + incl - steps) * kBK;
-  if (u == 0) poff[e] = stotal * kBK;
   __syncthreads();
-  // the unit of rank r sits at position r / 8 of its XCD's list
-  int start = 0;
-  for (int x = 0; x < xcd; ++x) start += count[x];
-  if (c >= 0) plan[kPlanHead + start + rank / kXcds] = u;
-  if (zero) plan[kPlanZero + zpos] = u;
-  if (u <= kXcds) {
-    int s = 0;
-    for (int x = 0; x < u; ++x) s += count[x];
-    plan[u] = s;
+  return base + incl;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void wgrad_plan_kernel(const int32_t *__restrict__ tokens_per_expert,
+                                                                  const int32_t *__restrict__ expert_offsets, int e,
+                                                                  int per_e_down, int per_e_gu,
+                                                                  int32_t *__restrict__ plan,
+                                                                  int32_t *__restrict__ block_expert) {
+  __shared__ int32_t s_cost[kMaxUnits], s_unit[kMaxUnits], s_by_slot[kMaxUnits];
+  __shared__ int32_t s_poff[kMaxExperts + 1];
+  __shared__ int32_t tmp[kPlanThreads / kWave], count[kXcds], start[kXcds + 1];
+  const int x = threadIdx.x, l = lane_id(), wv = x / kWave;
+  const int rows = x < e ? tokens_per_expert[x] : 0;
+  const int steps = (rows + kBK - 1) / kBK;
+  int S = 0;
+  const int s_incl = block_scan(steps, tmp, S);
+  if (x < e) s_poff[x] = (s_incl - steps) * kBK;
+  if (x == 0) s_poff[e] = S * kBK;
+  if (x < kXcds) count[x] = 0;
+  // the expert's parts and units
+  const int parts = x >= e ? 0 : (rows > 0 ? ((steps * kWgradDiv + S - 1) / S > 1 ? (steps * kWgradDiv + S - 1) / S : 1)
+                                           : 1);
+  int U = 0;
+  const int u_incl = block_scan(parts, tmp, U);
+  for (int p = 0; p < parts; ++p) {
+    const int u = u_incl - parts + p;
+    s_unit[u] = x | (p << 11) | (parts << 21);
+    const int64_t c = (((int64_t)2 * steps + 1) << 6) / parts;
+    s_cost[u] = rows > 0 ? (int)(c < INT32_MAX ? c : INT32_MAX) : 0;
   }
-  if (u == kXcds + 1) plan[9] = ztotal;
-  if (u == kXcds + 2) plan[10] = stotal;
-  if (u <= e) plan[kPlanPoff + u] = poff[u];
+  __syncthreads();
+  // rank (most K steps per unit first, then unit order) and snake order
+  int rank_of[2] = {0, 0}, xcd_of[2] = {0, 0};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int u = x + h * kPlanThreads;
+    if (u < U) {
+      const int c = s_cost[u];
+      int r = 0;
+      for (int v = 0; v < U; ++v) {
+        const int cv = s_cost[v];
+        r += (cv > c || (cv == c && v < u)) ? 1 : 0;
+      }
+      rank_of[h] = r;
+      xcd_of[h] = ((r / kXcds) & 1) ? kXcds - 1 - r % kXcds : r % kXcds;
+      atomicAdd(&count[xcd_of[h]], 1);
+    }
+  }
+  __syncthreads();
+  if (x == 0) {
+    int s = 0;
+    for (int i = 0; i < kXcds; ++i) {
+      start[i] = s;
+      s += count[i];
+    }
+    start[kXcds] = s;
+  }
+  __syncthreads();
+  // each unit's entry (its rank r sits at position r / 8 of its XCD's list)
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int u = x + h * kPlanThreads;
+    if (u < U) {
+      const int slot = start[xcd_of[h]] + rank_of[h] / kXcds;
+      const int unit = s_unit[u], ex = unit & 2047;
+      s_by_slot[slot] = unit;
+      int32_t *en = plan + kPlanEntries + slot * kEntryInts;
+      en[0] = unit;
+      en[1] = tokens_per_expert[ex];
+      en[2] = expert_offsets[ex];
+      en[3] = s_poff[ex];
+    }
+  }
+  if (x <= kXcds) plan[x] = start[x];
+  if (x == kXcds + 1) plan[25] = S;
+  if (x <= e) plan[kPlanPoff + x] = s_poff[x];
+  __syncthreads();
+  // first tile of every entry in its XCD's list, for both gradients: wave g
+  // (0..7) scans list g for dW_down, wave 8 + g for dW_gate_up
+  {
+    const int g = wv % kXcds, gu = wv >= kXcds;
+    const int per_e = gu ? per_e_gu : per_e_down;
+    int carry = 0;
+    for (int i0 = start[g]; i0 < start[g + 1]; i0 += kWave) {
+      const int i = i0 + l;
+      int nt = 0;
+      if (i < start[g + 1]) {
+        const int unit = s_by_slot[i];
+        int first;
+        nt = part_tiles((unit >> 11) & 1023, unit >> 21, per_e, first);
+      }
+      int incl = nt;
+#pragma unroll
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(incl, off, kWave);
+        if (l >= off) incl += o;
+      }
+      if (i < start[g + 1]) plan[kPlanEntries + i * kEntryInts + 4 + gu] = carry + incl - nt;
+      carry += __shfl(incl, kWave - 1, kWave);
+    }
+    if (l == 0) plan[9 + 8 * gu + g] = carry;
+  }
   // the expert of each 64-row block: the last one whose first block is <= t
-  for (int t = u; t < stotal; t += kPlanThreads) {
+  for (int t = x; t < S; t += kPlanThreads) {
     int lo = 0, hi = e - 1;
     while (lo < hi) {
       const int mid = (lo + hi + 1) >> 1;
-      if (poff[mid] <= t * kBK) lo = mid;
+      if (s_poff[mid] <= t * kBK) lo = mid;
       else hi = mid - 1;
     }
     block_expert[t] = lo;
   }
 }
 
-// One output tile of a weight gradient: expert x, output rows m0 .. m0 +
-// rows_valid - 1 and columns n0 .. n0 + 255 (those below N); K extent k_len
-// (the expert's rows) in KT steps, from row r0 of the segment buffer (the
-// K-major operand) and from K position 0 of the expert's part at poff of the
-// K-major copy.
-struct WgTile {
-  int x, m0, n0, rows_valid, k_len, KT, r0, poff;
-};
-
 // kAT: A is the K-major input and B the K-contiguous copy (dW_down = dy^T a);
 // else A is the copy and B the input (dW_gate_up = [dG | dU]^T x).  kNFast: a
 // unit's tiles run n-tile fastest (else m-tile fastest).  The workgroups of an
 // XCD work on consecutive tiles side by side, so the faster index should be
 // the operand with fewer tiles: each pass over it re-reads the smaller panel
-// set.
+// set.  `field`: which of the plan's two tile lists (0 dW_down, 1 dW_gate_up).
 template <bool kNFast, bool kAT>
 __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(
-    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int M, int N, int m_tiles, int n_tiles, int parts,
-    const int32_t *__restrict__ tokens_per_expert, const int32_t *__restrict__ expert_offsets,
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int M, int N, int m_tiles, int n_tiles, int field,
     const int32_t *__restrict__ plan, uint16_t *__restrict__ C, uint16_t *__restrict__ C_rep, int e_master) {
   constexpr bool kBT = !kAT;
   __shared__ __attribute__((aligned(1024))) char ring[kSlots * kOperandBytes];
   const int l = lane_id();
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int wm = w >> 1, wn = w & 1;
-  const int per_e = m_tiles * n_tiles;
-  const int chunk = (per_e + parts - 1) / parts;
-  auto out_base = [&](int x) {
-    return x < e_master ? C + (int64_t)x * M * N : C_rep + (int64_t)(x - e_master) * M * N;
-  };
-  auto tile_at = [&](int loc, int &m0, int &n0) {
-    m0 = (kNFast ? loc / n_tiles : loc % m_tiles) * kBM;
-    n0 = (kNFast ? loc % n_tiles : loc / m_tiles) * kBN;
-  };
+  const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
+  if (slot >= plan[9 + 8 * field + xcd]) return;
 
-  // experts without rows: their tiles are zero, dealt over the whole grid
-  {
-    const int nz = plan[9];
-    const int64_t zt_end = (int64_t)nz * per_e;
-    const u32x4 z = {0u, 0u, 0u, 0u};
-    for (int64_t zt = blockIdx.x; zt < zt_end; zt += gridDim.x) {
-      int m0, n0;
-      tile_at((int)(zt % per_e), m0, n0);
-      uint16_t *cb = out_base(plan[kPlanZero + (int)(zt / per_e)]);
-      for (int i = threadIdx.x; i < kBM * (kBN / 8); i += kThreads) {
-        const int row = m0 + i / (kBN / 8), col = n0 + (i % (kBN / 8)) * 8;
-        if (row < M && col < N) st16(cb + (int64_t)row * N + col, z);
-      }
-    }
-  }
-
-  // this XCD's unit list, two entries per lane: entry i in lane i % 64 of
-  // entry array [i / 64], with its expert's row count, segment start and poff
-  const int xcd = blockIdx.x % kXcds, J = gridDim.x / kXcds, j = blockIdx.x / kXcds;
-  if (j >= J) return;
-  const int n_units = plan[xcd + 1] - plan[xcd];
-  int ent_u[2], ent_k[2], ent_r[2], ent_p[2];
+  // the entry of this tile: the last one of the XCD's list whose first tile is
+  // <= slot, found by one ballot per 64 entries over all of them at once
+  const int base = plan[xcd], n_ent = plan[xcd + 1] - base;
+  const int32_t *ent = plan + kPlanEntries;
+  int v_unit[kListLanes], v_rows[kListLanes], v_r0[kListLanes], v_poff[kListLanes], v_first[kListLanes];
+  uint64_t hit[kListLanes];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < kListLanes; ++h) {
     const int i = h * kWave + l;
-    ent_u[h] = i < n_units ? plan[kPlanHead + plan[xcd] + i] : 0;
-    const int x = ent_u[h] / parts;
-    ent_k[h] = tokens_per_expert[x];
-    ent_r[h] = expert_offsets[x];
-    ent_p[h] = plan[kPlanPoff + x];
+    const int32_t *en = ent + (int64_t)(base + (i < n_ent ? i : 0)) * kEntryInts;
+    v_unit[h] = en[0];
+    v_rows[h] = en[1];
+    v_r0[h] = en[2];
+    v_poff[h] = en[3];
+    v_first[h] = en[4 + field];
+    hit[h] = __ballot(i < n_ent && v_first[h] <= slot);
   }
-  auto entry = [&](const int (&v)[2], int i) {
-    return i < kWave ? __builtin_amdgcn_readlane(v[0], i) : __builtin_amdgcn_readlane(v[1], i - kWave);
+  const int hsel = hit[2] ? 2 : (hit[1] ? 1 : 0);
+  const uint64_t hm = hit[hsel];
+  const int src = 63 - __builtin_clzll(hm);  // hm is not empty: the first entry starts at tile 0
+  auto pick = [&](const int (&v)[kListLanes]) {
+    const int a = __builtin_amdgcn_readlane(v[0], src), b = __builtin_amdgcn_readlane(v[1], src),
+              c = __builtin_amdgcn_readlane(v[2], src);
+    return hsel == 2 ? c : (hsel == 1 ? b : a);
   };
-  // walks: list entry ui, whose first tile is the XCD's tile `base`; moves to
-  // the XCD's tile t (not before the walk's position); false past the list's end
-  struct Walk {
-    int ui, base;
-  };
-  auto walk_to = [&](Walk &wk, int t, WgTile &T) -> bool {
-    while (wk.ui < n_units) {
-      const int u = entry(ent_u, wk.ui);
-      const int first = (u % parts) * chunk;
-      const int last = first + chunk < per_e ? first + chunk : per_e;
-      const int nt = last > first ? last - first : 0;
-      if (t < wk.base + nt) {
-        T.x = u / parts;
-        tile_at(first + t - wk.base, T.m0, T.n0);
-        T.rows_valid = M - T.m0 < kBM ? M - T.m0 : kBM;
-        T.k_len = entry(ent_k, wk.ui);
-        T.r0 = entry(ent_r, wk.ui);
-        T.poff = entry(ent_p, wk.ui);
-        T.KT = (T.k_len + kBK - 1) / kBK;
-        return true;
-      }
-      wk.base += nt;
-      ++wk.ui;
-    }
-    return false;
-  };
-
-  // the load cursor (tile lt, K step lkt) runs two steps ahead of the compute
-  // cursor (tile ct); each walks the same tile sequence
-  Walk lw = {0, 0}, cw = {0, 0};
-  WgTile lt, ct;
-  int lt_t = j, ct_t = j;
-  if (!walk_to(lw, lt_t, lt)) return;
-  cw = lw;
-  ct = lt;
-  int lkt = 0;
-  bool have_load = true;
+  const int unit = pick(v_unit), k_len = pick(v_rows), r0 = pick(v_r0), poff = pick(v_poff),
+            first_slot = pick(v_first);
+  const int x = unit & 2047;
+  int first;
+  part_tiles((unit >> 11) & 1023, unit >> 21, m_tiles * n_tiles, first);
+  const int loc = first + slot - first_slot;
+  const int m0 = (kNFast ? loc / n_tiles : loc % m_tiles) * kBM;
+  const int n0 = (kNFast ? loc % n_tiles : loc / m_tiles) * kBN;
+  const int rows_valid = M - m0 < kBM ? M - m0 : kBM;
+  const int KT = (k_len + kBK - 1) / kBK;
+  uint16_t *cb = x < e_master ? C + (int64_t)x * M * N : C_rep + (int64_t)(x - e_master) * M * N;
 
   // Direct loads.  The K-major input: row k of a step holds 256 columns in 512
   // bytes; this wave fills rows w*16 .. w*16+15, two per instruction: lane l
@@ -1068,55 +1083,44 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(
   // w*64 + 8i + l/8, position l % 8 with chunk position ^ swz(r); rows past the
   // operand's end re-read its last row.
   uint32_t a_off[kLoads], b_off[kLoads];
-  auto set_offsets = [&]() {
-    const uint32_t kp2 = (uint32_t)lt.KT * (uint32_t)kRowBytes;  // bytes per row of the copy
+  const uint32_t kp2 = (uint32_t)KT * (uint32_t)kRowBytes;  // bytes per row of the copy
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) {
-      const int k = w * 16 + 2 * i + l / 32;
-      const int ct8 = ((l % 32) ^ swz_t(k)) * 8;
-      const int r = w * 64 + i * kLoadRows + l / kChunks;
-      const uint32_t cc = (uint32_t)(((l % kChunks) ^ swz(r)) * 16);
-      if constexpr (kAT) {
-        a_off[i] = (uint32_t)(ct8 > lt.rows_valid - 8 ? lt.rows_valid - 8 : ct8) * 2u;
-        b_off[i] = (uint32_t)(r < N - lt.n0 ? r : N - lt.n0 - 1) * kp2 + cc;
-      } else {
-        a_off[i] = (uint32_t)(r < lt.rows_valid ? r : lt.rows_valid - 1) * kp2 + cc;
-        b_off[i] = (uint32_t)(ct8 > N - lt.n0 - 8 ? N - lt.n0 - 8 : ct8) * 2u;
-      }
-    }
-  };
-  set_offsets();
-  const uint32_t ring_lds = lds_address(ring) + w * 64 * kRowBytes;  // = w * 16 * kTRowBytes
-  auto load_a = [&](int slot, int i) {
-    const uint32_t dst = ring_lds + slot * kOperandBytes + i * 1024;
+  for (int i = 0; i < kLoads; ++i) {
+    const int k = w * 16 + 2 * i + l / 32;
+    const int ct8 = ((l % 32) ^ swz_t(k)) * 8;
+    const int r = w * 64 + i * kLoadRows + l / kChunks;
+    const uint32_t cc = (uint32_t)(((l % kChunks) ^ swz(r)) * 16);
     if constexpr (kAT) {
-      const int k = w * 16 + 2 * i + l / 32, last = lt.k_len - 1 - lkt * kBK;
-      const char *base = reinterpret_cast<const char *>(A + ((int64_t)lt.r0 + (int64_t)lkt * kBK) * M + lt.m0);
-      dma16(base, a_off[i] + (uint32_t)(k < last ? k : last) * (uint32_t)M * 2u, dst);
+      a_off[i] = (uint32_t)(ct8 > rows_valid - 8 ? rows_valid - 8 : ct8) * 2u;
+      b_off[i] = (uint32_t)(r < N - n0 ? r : N - n0 - 1) * kp2 + cc;
     } else {
-      const char *base = reinterpret_cast<const char *>(A + (int64_t)M * lt.poff + (int64_t)lt.m0 * lt.KT * kBK +
-                                                        (int64_t)lkt * kBK);
-      dma16(base, a_off[i], dst);
+      a_off[i] = (uint32_t)(r < rows_valid ? r : rows_valid - 1) * kp2 + cc;
+      b_off[i] = (uint32_t)(ct8 > N - n0 - 8 ? N - n0 - 8 : ct8) * 2u;
+    }
+  }
+  const uint32_t ring_lds = lds_address(ring) + w * 64 * kRowBytes;  // = w * 16 * kTRowBytes
+  auto load_a = [&](int slot_, int kt, int i) {
+    const uint32_t dst = ring_lds + slot_ * kOperandBytes + i * 1024;
+    if constexpr (kAT) {
+      const int k = w * 16 + 2 * i + l / 32, last = k_len - 1 - kt * kBK;
+      const char *src_ = reinterpret_cast<const char *>(A + ((int64_t)r0 + (int64_t)kt * kBK) * M + m0);
+      dma16(src_, a_off[i] + (uint32_t)(k < last ? k : last) * (uint32_t)M * 2u, dst);
+    } else {
+      const char *src_ =
+          reinterpret_cast<const char *>(A + (int64_t)M * poff + (int64_t)m0 * KT * kBK + (int64_t)kt * kBK);
+      dma16(src_, a_off[i], dst);
     }
   };
-  auto load_b = [&](int slot, int i) {
-    const uint32_t dst = ring_lds + slot * kOperandBytes + i * 1024;
+  auto load_b = [&](int slot_, int kt, int i) {
+    const uint32_t dst = ring_lds + slot_ * kOperandBytes + i * 1024;
     if constexpr (kBT) {
-      const int k = w * 16 + 2 * i + l / 32, last = lt.k_len - 1 - lkt * kBK;
-      const char *base = reinterpret_cast<const char *>(B + ((int64_t)lt.r0 + (int64_t)lkt * kBK) * N + lt.n0);
-      dma16(base, b_off[i] + (uint32_t)(k < last ? k : last) * (uint32_t)N * 2u, dst);
+      const int k = w * 16 + 2 * i + l / 32, last = k_len - 1 - kt * kBK;
+      const char *src_ = reinterpret_cast<const char *>(B + ((int64_t)r0 + (int64_t)kt * kBK) * N + n0);
+      dma16(src_, b_off[i] + (uint32_t)(k < last ? k : last) * (uint32_t)N * 2u, dst);
     } else {
-      const char *base = reinterpret_cast<const char *>(B + (int64_t)N * lt.poff + (int64_t)lt.n0 * lt.KT * kBK +
-                                                        (int64_t)lkt * kBK);
-      dma16(base, b_off[i], dst);
-    }
-  };
-  auto advance_load = [&]() {
-    if (++lkt == lt.KT) {
-      lkt = 0;
-      lt_t += J;
-      have_load = walk_to(lw, lt_t, lt);
-      if (have_load) set_offsets();
+      const char *src_ =
+          reinterpret_cast<const char *>(B + (int64_t)N * poff + (int64_t)n0 * KT * kBK + (int64_t)kt * kBK);
+      dma16(src_, b_off[i], dst);
     }
   };
   uint32_t ta[4][2], tb[4][2];
@@ -1130,140 +1134,112 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(
   constexpr int kReads = 12;
 
   f32x16 acc[4][4];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.0f;
 
-  // a finished tile: each wave converts its 128 x 128 sub-tile to bf16 and
-  // writes it out in four rounds of one 32-row block through its 8 KiB of the
-  // free ring slot (16-byte chunks XOR-swizzled by row), as whole 256-byte rows
-  // of 16-byte stores -- 32 store instructions per wave
-  auto store_tile = [&](const WgTile &T, char *slot, bool whole) {
-    char *stage = slot + w * (kOperandBytes / 4);
-    uint16_t *cb = out_base(T.x);
-    const int ch = l % 16, col = T.n0 + wn * 128 + ch * 8;
-    const int rr = l & 31;
+  // K loop, as the grouped GEMM's: step kt's B and A tiles in slots sb, sa;
+  // slices 0 and 1 load step kt+2's B tile into slot pb, slice 3 its A tile
+  // into slot sb; after slice 2 every wave waits for step kt+1's tiles and
+  // passes a barrier.  (An expert without rows has no K step: a zero tile.)
+  if (KT > 0) {
+    bf16x8 fa[2][4], fb[2][4];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
+    for (int i = 0; i < kLoads; ++i) load_b(0, 0, i);
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
+    for (int i = 0; i < kLoads; ++i) load_a(1, 0, i);
+    if (KT > 1) {
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const f32x16 &c = acc[mi][ni];
-          const int f = ni * 32 + 8 * g + 4 * (l >> 5);
-          *reinterpret_cast<uint2 *>(stage + rr * 256 + ((f >> 3) ^ (rr & 15)) * 16 + (f & 7) * 2) =
-              make_uint2(pack_bf16x2(c[4 * g], c[4 * g + 1]), pack_bf16x2(c[4 * g + 2], c[4 * g + 3]));
-        }
-      }
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
-      __builtin_amdgcn_wave_barrier();
-      // all eight reads first, then the stores (one LDS round trip per block);
-      // a whole tile stores unconditionally
-      u32x4 v[8];
+      for (int i = 0; i < kLoads; ++i) load_b(2, 1, i);
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int r = l / 16 + 4 * q;
-        v[q] = *reinterpret_cast<const u32x4 *>(stage + r * 256 + (ch ^ (r & 15)) * 16);
-      }
-      uint16_t *c_blk = cb + (int64_t)(T.m0 + (2 * mi + wm) * 32 + l / 16) * N + col;
-      if (whole) {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) st16(c_blk + (int64_t)(4 * q) * N, v[q]);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          const int row = T.m0 + (2 * mi + wm) * 32 + l / 16 + 4 * q;
-          if (row < M && col < N) st16(c_blk + (int64_t)(4 * q) * N, v[q]);
-        }
-      }
+      for (int i = 0; i < kLoads; ++i) load_a(3, 1, i);
+      wait_vmcnt<2 * kLoads>();
+    } else {
+      wait_vmcnt<0>();
     }
-  };
-
-  // prologue: the first two K steps of the sequence (B tiles in slots 0 and 2,
-  // A tiles in 1 and 3)
-#pragma unroll
-  for (int i = 0; i < kLoads; ++i) load_b(0, i);
-#pragma unroll
-  for (int i = 0; i < kLoads; ++i) load_a(1, i);
-  advance_load();
-  if (have_load) {
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) load_b(2, i);
-#pragma unroll
-    for (int i = 0; i < kLoads; ++i) load_a(3, i);
-    advance_load();
-    wait_vmcnt<2 * kLoads>();
-  } else {
-    wait_vmcnt<0>();
-  }
-  lds_barrier();
-  __builtin_amdgcn_sched_barrier(0);
-  bf16x8 fa[2][4], fb[2][4];
-  load_frags<false, kAT, kBT>(ring + kOperandBytes, ring, 0, wm, wn, l, fa[0], fb[0], ta, tb);
-  __builtin_amdgcn_sched_barrier(0);
-
-  // The K steps of the whole sequence, as in the grouped GEMM's K loop: step s
-  // reads slots sb (B) and sa (A); its slices 0 and 1 load step s+2's B tile
-  // into slot pb, slice 3 its A tile into slot sb; after slice 2 every wave
-  // waits for step s+1's tiles and passes a barrier.  A tile's last step is
-  // followed by its output, staged in slot sa (free until step s+1 loads step
-  // s+3's B tile there); those 32 stores per wave are issued after step s+2's
-  // loads, so the wait of step s+1 lets them stay in flight (memory operations
-  // of a wave complete in issue order) -- unless the tile was ragged and
-  // issued fewer.
-  int sb = 0, sa = 1;
-  bool stores_ahead = false;
-  for (;;) {
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.0f;
-    int free_slot = sa;
-    for (int ckt = 0; ckt < ct.KT; ++ckt) {
+    lds_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags<false, kAT, kBT>(ring + kOperandBytes, ring, 0, wm, wn, l, fa[0], fb[0], ta, tb);
+    __builtin_amdgcn_sched_barrier(0);
+    int sb = 0, sa = 1;
+    for (int kt = 0; kt < KT; ++kt) {
       const int nb = sb + 2 < kSlots ? sb + 2 : sb + 2 - kSlots;
       const int na = sa + 2 < kSlots ? sa + 2 : sa + 2 - kSlots;
       const int pb = na + 1 < kSlots ? na + 1 : na + 1 - kSlots;
+      const bool ahead = kt + 2 < KT;
       const char *as = ring + sa * kOperandBytes;
       const char *bs = ring + sb * kOperandBytes;
       load_frags<false, kAT, kBT>(as, bs, 1, wm, wn, l, fa[1], fb[1], ta, tb);
       slice<4, kReads>(fa[0], fb[0], acc, [&](int d) {
-        if (have_load) load_b(pb, d);
+        if (ahead) load_b(pb, kt + 2, d);
       });
       load_frags<false, kAT, kBT>(as, bs, 2, wm, wn, l, fa[0], fb[0], ta, tb);
       slice<4, kReads>(fa[1], fb[1], acc, [&](int d) {
-        if (have_load) load_b(pb, 4 + d);
+        if (ahead) load_b(pb, kt + 2, 4 + d);
       });
       load_frags<false, kAT, kBT>(as, bs, 3, wm, wn, l, fa[1], fb[1], ta, tb);
       slice<4, kReads>(fa[0], fb[0], acc, [&](int) {});
-      if (have_load) {
-        if (stores_ahead) wait_vmcnt<kLoads + kEpiStores>();
-        else wait_vmcnt<kLoads>();
-      } else {
-        if (stores_ahead) wait_vmcnt<kEpiStores>();
-        else wait_vmcnt<0>();
-      }
-      stores_ahead = false;
+      if (ahead) wait_vmcnt<kLoads>();
+      else wait_vmcnt<0>();
       lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      // step s+1's first fragments (after the sequence's last step: stale, unused)
+      // step kt+1's first fragments (after the last step: stale, unused)
       load_frags<false, kAT, kBT>(ring + na * kOperandBytes, ring + nb * kOperandBytes, 0, wm, wn, l, fa[0], fb[0],
                                   ta, tb);
       slice<4, kReads>(fa[1], fb[1], acc, [&](int d) {
-        if (have_load) {
-          load_a(sb, 2 * d);
-          load_a(sb, 2 * d + 1);
+        if (ahead) {
+          load_a(sb, kt + 2, 2 * d);
+          load_a(sb, kt + 2, 2 * d + 1);
         }
       });
       __builtin_amdgcn_sched_barrier(0);
-      if (have_load) advance_load();
-      free_slot = sa;
       sb = nb;
       sa = na;
     }
-    const bool whole = ct.rows_valid == kBM && ct.n0 + kBN <= N;
-    store_tile(ct, ring + free_slot * kOperandBytes, whole);
-    stores_ahead = whole;  // all 32 stores issued
-    ct_t += J;
-    if (!walk_to(cw, ct_t, ct)) break;
+  }
+
+  // epilogue: each wave converts its 128 x 128 sub-tile to bf16 and writes it
+  // out in four rounds of one 32-row block through its own 8 KiB of LDS (every
+  // real LDS read is done: the last barrier has passed; 16-byte chunks
+  // XOR-swizzled by row), as whole 256-byte rows of 16-byte stores
+  char *stage = ring + w * (kOperandBytes / 4);
+  const bool whole = rows_valid == kBM && n0 + kBN <= N;
+  const int ch = l % 16, col = n0 + wn * 128 + ch * 8;
+  const int rr = l & 31;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+    for (int ni = 0; ni < 4; ++ni)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x16 &c = acc[mi][ni];
+        const int f = ni * 32 + 8 * g + 4 * (l >> 5);
+        *reinterpret_cast<uint2 *>(stage + rr * 256 + ((f >> 3) ^ (rr & 15)) * 16 + (f & 7) * 2) =
+            make_uint2(pack_bf16x2(c[4 * g], c[4 * g + 1]), pack_bf16x2(c[4 * g + 2], c[4 * g + 3]));
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+    __builtin_amdgcn_wave_barrier();
+    // all eight reads first, then the stores; a whole tile stores unconditionally
+    u32x4 v[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      const int r = l / 16 + 4 * q;
+      v[q] = *reinterpret_cast<const u32x4 *>(stage + r * 256 + (ch ^ (r & 15)) * 16);
+    }
+    uint16_t *c_blk = cb + (int64_t)(m0 + (2 * mi + wm) * 32 + l / 16) * N + col;
+    if (whole) {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) st16(c_blk + (int64_t)(4 * q) * N, v[q]);
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int row = m0 + (2 * mi + wm) * 32 + l / 16 + 4 * q;
+        if (row < M && col < N) st16(c_blk + (int64_t)(4 * q) * N, v[q]);
+      }
+    }
   }
 }
 
@@ -1293,7 +1269,7 @@ __global__ __launch_bounds__(kSwThreads) void swiglu_bwd_kernel(
     uint16_t *__restrict__ gT) {
   __shared__ __attribute__((aligned(16))) uint32_t tile[3][64 * 32];  // a, dG, dU: [feature][k/2] words
   const int b = blockIdx.x;
-  if (b >= plan[10]) return;
+  if (b >= plan[25]) return;
   const int x = block_expert[b];
   const int rows_x = tokens_per_expert[x];
   const int64_t kp = (int64_t)((rows_x + kBK - 1) / kBK) * kBK;
@@ -1381,38 +1357,23 @@ hipError_t launch_plain(const uint16_t *A, const uint16_t *B, const uint16_t *B_
   return hipGetLastError();
 }
 
-// Workgroups of the persistent weight-gradient kernel: one per CU (its LDS
-// ring takes a CU's whole LDS), a multiple of the 8 XCDs.  The CU count is read
-// once per device.
-int persistent_grid() {
-  static int cus[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < kXcds) n = 256;
-    cus[dev] = n / kXcds * kXcds;
-  }
-  return cus[dev];
-}
-
 // Weight-gradient GEMM: C_e [M, N] = A_e^T B_e for every expert over the rows of
 // its segment, on the work plan `plan` (wgrad_plan_kernel over the same row
-// counts).  kAT: A is the K-major input [rows, M] and B the K-contiguous copy
-// ([N][kp_e] per expert); else A is the copy ([M][kp_e]) and B the input
-// [rows, N].
+// counts; `field` 0 for dW_down, 1 for dW_gate_up).  kAT: A is the K-major
+// input [rows, M] and B the K-contiguous copy ([N][kp_e] per expert); else A
+// is the copy ([M][kp_e]) and B the input [rows, N].
 template <bool kAT>
-hipError_t launch_wgrad(const uint16_t *A, const uint16_t *B, int M, int N, int e, const int32_t *tokens_per_expert,
-                        const int32_t *expert_offsets, const int32_t *plan, uint16_t *C, uint16_t *C_rep, int e_master,
-                        hipStream_t stream) {
+hipError_t launch_wgrad(const uint16_t *A, const uint16_t *B, int M, int N, int e, int field, const int32_t *plan,
+                        uint16_t *C, uint16_t *C_rep, int e_master, hipStream_t stream) {
   const int mt = (M + kBM - 1) / kBM, nt = (N + kBN - 1) / kBN;
-  const int parts = wgrad_parts(e);
+  const int64_t g = kXcds * wgrad_list_bound(e, mt * nt);
+  if (g > INT32_MAX) return hipErrorInvalidConfiguration;
   if (nt <= mt)
-    hipLaunchKernelGGL((wgrad_kernel<true, kAT>), dim3((unsigned)persistent_grid()), dim3(kThreads), 0, stream, A, B,
-                       M, N, mt, nt, parts, tokens_per_expert, expert_offsets, plan, C, C_rep, e_master);
+    hipLaunchKernelGGL((wgrad_kernel<true, kAT>), dim3((unsigned)g), dim3(kThreads), 0, stream, A, B, M, N, mt, nt,
+                       field, plan, C, C_rep, e_master);
   else
-    hipLaunchKernelGGL((wgrad_kernel<false, kAT>), dim3((unsigned)persistent_grid()), dim3(kThreads), 0, stream, A,
-                       B, M, N, mt, nt, parts, tokens_per_expert, expert_offsets, plan, C, C_rep, e_master);
+    hipLaunchKernelGGL((wgrad_kernel<false, kAT>), dim3((unsigned)g), dim3(kThreads), 0, stream, A, B, M, N, mt, nt,
+                       field, plan, C, C_rep, e_master);
   return hipGetLastError();
 }
 
@@ -1467,8 +1428,10 @@ hipError_t launch_expert_ffn_bwd(const uint16_t *x_perm, const uint16_t *grad_y,
 #define MOE_TRY(x)                    \
   if ((st = (x)) != hipSuccess) return st;
   // the weight gradients' work plan, the padded K extents and their blocks' experts
-  hipLaunchKernelGGL(wgrad_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, tokens_per_expert, e, wgrad_parts(e),
-                     ws.plan, ws.block_expert);
+  const int t_down = ((H + kBM - 1) / kBM) * ((I + kBN - 1) / kBN);
+  const int t_gu = ((2 * I + kBM - 1) / kBM) * ((H + kBN - 1) / kBN);
+  hipLaunchKernelGGL(wgrad_plan_kernel, dim3(1), dim3(kPlanThreads), 0, stream, tokens_per_expert, expert_offsets, e,
+                     t_down, t_gu, ws.plan, ws.block_expert);
   MOE_TRY(hipGetLastError());
   if (rows > 0) {
     // [G | U] = x W_gate_up^T unless saved by the forward; dA = dy W_down (W_down [H, I]: K-major)
@@ -1489,10 +1452,8 @@ hipError_t launch_expert_ffn_bwd(const uint16_t *x_perm, const uint16_t *grad_y,
                                tokens_per_expert, expert_offsets, grad_x_perm, stream));
   }
   // dW_down_e = dy_e^T a_e;  [dW_gate; dW_up]_e = [dG | dU]_e^T x_e  (experts without rows: zeros)
-  MOE_TRY(launch_wgrad<true>(grad_y, ws.aT, H, I, e, tokens_per_expert, expert_offsets, ws.plan, grad_w_down, gwd_r,
-                             em, stream));
-  MOE_TRY(launch_wgrad<false>(ws.gT, x_perm, 2 * I, H, e, tokens_per_expert, expert_offsets, ws.plan, grad_w_gate_up,
-                              gwgu_r, em, stream));
+  MOE_TRY(launch_wgrad<true>(grad_y, ws.aT, H, I, e, 0, ws.plan, grad_w_down, gwd_r, em, stream));
+  MOE_TRY(launch_wgrad<false>(ws.gT, x_perm, 2 * I, H, e, 1, ws.plan, grad_w_gate_up, gwgu_r, em, stream));
 #undef MOE_TRY
   return hipSuccess;
 }
