@@ -67,7 +67,7 @@ hipError_t launch_scatter_mxfp8(const uint16_t *x, int64_t n, int k, int64_t h, 
                                 uint8_t *q, uint8_t *scale, int64_t pad_rows, const int32_t *pad_limit,
                                 const int32_t *row_src, hipStream_t stream);
 
-// ---- grouped SwiGLU FFN (moe_ffn.hip); bf16 operands as uint16_t bit patterns
+// ---- grouped SwiGLU FFN (moe_ffn.hip, MXFP8 in moe_ffn_mx.hip); bf16 operands as uint16_t bit patterns
 // Replica weight slots: experts from e_master on take their weights from (and
 // write their weight gradients to) the replica buffers, slot e - e_master.
 struct ReplicaBases {

@@ -4,7 +4,7 @@
 // expert ids), replica weights synchronised from the masters, and the replica
 // weight gradients reduced into the masters'.  The grouped FFN over master and
 // replica experts (weights from two storage bases) is the grouped GEMM of
-// moe_ffn.hip with replica bases.
+// moe_gemm.hpp with replica bases.
 //
 // Physical expert p < E is the master of logical expert p; p = E + i is
 // replica slot i, holding a copy of logical expert replica_of[i].
