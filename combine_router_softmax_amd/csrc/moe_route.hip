@@ -122,6 +122,8 @@ __global__ void fill_i32(int32_t *p, int64_t n, int32_t v) {
 // thread owns one 16-byte column slice and a strided set of rows of the block's
 // row range; a few dozen workgroups each add their partial counts with one
 // atomic per expert, which keeps same-address atomic traffic small.
+constexpr int kCountRows = 8;  // routing-map rows a thread requests at once
+
 __global__ __launch_bounds__(kRouteThreads) void count_map_kernel(const uint8_t *__restrict__ routing_map, int64_t n,
                                                                   int e, int64_t rows_per_block,
                                                                   int32_t *__restrict__ tokens_per_expert) {
@@ -138,10 +140,22 @@ __global__ __launch_bounds__(kRouteThreads) void count_map_kernel(const uint8_t 
     uint32_t c[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) c[i] = 0;
-    for (int64_t r = r0 + rl; r < r1; r += row_lanes) {
-      const u32x4 m = ld16(routing_map + r * e + v * 16);
+    // kCountRows rows per round, all requested before any is added (a row at a
+    // time costs a memory round trip per row); rows past the range re-read the
+    // first row and add nothing
+    for (int64_t r = r0 + rl; r < r1; r += (int64_t)kCountRows * row_lanes) {
+      u32x4 m[kCountRows];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) c[i] += (m[i / 4] >> (8 * (i % 4))) & 0xFFu;
+      for (int u = 0; u < kCountRows; ++u) {
+        const int64_t rr = r + (int64_t)u * row_lanes;
+        m[u] = ld16(routing_map + (rr < r1 ? rr : r0) * e + v * 16);
+      }
+#pragma unroll
+      for (int u = 0; u < kCountRows; ++u) {
+        const uint32_t keep = r + (int64_t)u * row_lanes < r1 ? 0xFFu : 0u;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) c[i] += (m[u][i / 4] >> (8 * (i % 4))) & keep;
+      }
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -190,14 +204,35 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float *__res
   } else if (t < n) {
     const float *row = logits ? logits + t * e : nullptr;
     auto logit = [&](int x) { return row ? row[x] : random_logit(t, x, seed); };
+    // the lane's logits (and biases) are all requested before any is used: one
+    // memory round trip per token (loading them one by one, each behind the
+    // branch on the logit source, took one round trip each)
+    float lx[VPL];
+    if (row) {
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int x = l + kWave * i;
+        lx[i] = row[x < e ? x : e - 1];
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) lx[i] = random_logit(t, l + kWave * i, seed);
+    }
+    if (expert_bias) {  // selection score: the logit plus the expert's bias
+      float bx[VPL];
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) {
+        const int x = l + kWave * i;
+        bx[i] = expert_bias[x < e ? x : e - 1];
+      }
+#pragma unroll
+      for (int i = 0; i < VPL; ++i) lx[i] += bx[i];
+    }
     uint64_t key[VPL];
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
       const int x = l + kWave * i;
-      // selection score: the logit, plus the expert's bias when one is given
-      const float lx = x < e ? logit(x) : 0.0f;
-      const float sc = expert_bias && x < e ? lx + expert_bias[x] : lx;
-      key[i] = x < e ? ((uint64_t)logit_key(sc) << 32) | (uint32_t)~(uint32_t)x : 0ull;
+      key[i] = x < e ? ((uint64_t)logit_key(lx[i]) << 32) | (uint32_t)~(uint32_t)x : 0ull;
     }
     uint32_t taken = 0;
     for (int j = 0; j < k; ++j) {
