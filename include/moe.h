@@ -135,14 +135,19 @@ int64_t moe_layout_rows(const moe_shape *s);
 
 /* Bytes of device workspace `op` needs for shape `s` (0 is a valid answer).
  * Workspace must be 256-byte aligned.  The dispatch and reroute workspaces
- * (MOE_OP_DISPATCH, MOE_OP_REROUTE) start with a 256-byte header, the state of
- * the single-pass layout scan, which must be zero before the workspace is
- * first used (zero-fill it once when it is allocated); every call leaves it
- * zero again, so the workspace then serves any number of calls in stream
- * order.  Two calls in flight at once must not share a workspace.  No other
- * workspace needs initialisation.  A dispatch whose header was not zero does
- * not hang or write outside its arrays: its scan gives up after a bounded wait
- * and reports counters[3] = -1. */
+ * (MOE_OP_DISPATCH, MOE_OP_REROUTE) hold the state of the single-pass layout
+ * scan: a 256-byte header, then status words tagged with the header's call
+ * counter.  Zero-fill the whole workspace once when it is allocated, before
+ * its first use: a status word that an earlier workspace left in the same
+ * memory carries a tag of that workspace's calls, and with only the header
+ * cleared it could pass for a word of this call.  Every call leaves the
+ * workspace ready for the next (the header zero again, its status words
+ * tagged with a count the next call does not use), so it then serves any
+ * number of calls in stream order, at any shape it is large enough for.  Two
+ * calls in flight at once must not share a workspace.  No other workspace
+ * needs initialisation.  A dispatch whose header was not zero does not hang or
+ * write outside its arrays: its scan gives up after a bounded wait and reports
+ * counters[3] = -1. */
 moe_status moe_workspace_size(moe_op op, const moe_shape *s, size_t *bytes);
 
 /* Router: the routing stage of MoELayer.forward ("Megatron MoE 实现",
@@ -233,7 +238,9 @@ moe_status moe_build_layout(const moe_shape *s, const int32_t *topk_idx, const f
  * takes no workspace: its scratch is a static device array of
  * MOE_NOALLOC_SCRATCH_BYTES owned by the library, one per GPU it runs on, held
  * until the process ends (found with hipGetSymbolAddress at the first call on
- * a device, which also enqueues the clearing of its header on `stream`).  The
+ * a device, which also enqueues the clearing of its header on `stream`; the
+ * array is zero when the library is loaded, so its status words need no
+ * clearing).  The
  * call allocates nothing: no hipMalloc, no hipFree, no allocating library
  * routine.  A shape whose dispatch workspace (moe_workspace_size with
  * MOE_OP_DISPATCH) exceeds MOE_NOALLOC_SCRATCH_BYTES returns MOE_ERR_WORKSPACE
