@@ -550,9 +550,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     // its loads of step kt+1 and passes a barrier (no wave reads step kt's
     // tiles any more); slice 1 runs under the reads of step kt+1's first
     // fragments and scales and loads step kt+2's tiles into step kt's slots,
-    // all sixteen load instructions at its start (measured 2-4 % faster than
-    // spreading them over the slice: with four slots a tile is requested only
-    // about one step before use, so every cycle of lead counts).
+    // over the first three of its four load slots: issuing all sixteen loads
+    // at once leaves the MFMA pipe without work while they issue, spreading
+    // them over all four slots requests the last ones too late (with four ring
+    // slots a tile is requested only about one step before use); measured,
+    // three slots: equal to one at the Qwen3-like layer, 2 % faster at the
+    // 32-expert share; four slots 2-3 % slower.
     // The E8M0 scales come in groups of four K steps (16 bytes per tile row per
     // operand) into two LDS buffers: group g+1 is loaded in step 4g, after its
     // buffer's previous group was last read (in step 4g-2), and is waited for
@@ -625,9 +628,12 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     load_frags_fp8<kSwiGLU>(nbs + kOperandBytes, nbs, 0, wm, wn, l, fa[0], fb[0]);                    \
     read_scales(kt + 1, sa_n, sb_n);                                                                  \
     slice_fp8<MI, 24, 2>(fa[1], fb[1], sa_c, sb_c, acc, [&](int d) {                                  \
-      if (ahead && d == 0) { /* all at the first slot: the four-slot ring prefetches only a step */     \
-        _Pragma("unroll") for (int q = 0; q < kLoads; ++q) load_b(sbt, kt + 2, q);                    \
-        _Pragma("unroll") for (int q = 0; q < kLoads; ++q) load_a(sbt + 1, kt + 2, q);                \
+      if (ahead && d < 3) { /* B then A, 6 / 5 / 5 loads at the first three slots */                   \
+        _Pragma("unroll") for (int q = 0; q < 2 * kLoads; ++q)                                         \
+          if (q * 3 / (2 * kLoads) == d) {                                                            \
+            if (q < kLoads) load_b(sbt, kt + 2, q);                                                   \
+            else load_a(sbt + 1, kt + 2, q - kLoads);                                                 \
+          }                                                                                           \
       }                                                                                               \
       if (d == 0 && scales_ahead) load_scales((kt >> 2) + 1);                                         \
     });                                                                                               \
