@@ -257,18 +257,22 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan(
   const int w = tid / kWave;
   const int l = lane_id();
 
-  if (tid == 0) {
-    sh_ticket = __hip_atomic_fetch_add(&hdr->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    sh_epoch = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  // the ids of tile blockIdx.x are requested while the ticket is on its way
-  // (tickets mostly follow dispatch order); another ticket reloads them
+  // the ids of tile blockIdx.x are requested first and the ticket and epoch
+  // together while they are on their way, so the three cost one memory round
+  // trip (tickets mostly follow dispatch order; another ticket reloads the
+  // ids).  The epoch does not change during the call.
   const int64_t guess = blockIdx.x;
   int32_t ids[kScanChunks];
 #pragma unroll
   for (int c = 0; c < kScanChunks; ++c) {
     const int64_t a = guess * kLayoutTile + (int64_t)w * kScanChunks * kWave + c * kWave + l;
     ids[c] = a < a_total ? topk_idx[a] : -1;
+  }
+  if (tid == 0) {
+    const uint32_t ep = __hip_atomic_load(&hdr->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t tk = __hip_atomic_fetch_add(&hdr->ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    sh_epoch = ep;
+    sh_ticket = tk;
   }
   for (int x = tid; x < kScanWaves * nb; x += kScanThreads) run[x] = 0;
   lds_barrier();
