@@ -313,6 +313,10 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan(
     }
     lds_barrier();
 
+    // the first look-back batch of this thread's bin is requested now and
+    // read after the ranking, which hides its memory round trip
+    uint64_t first0[kLookback];
+    if (tile > 0 && tid < nb) look_back_first(status, tile, nb, tid, first0);
     // stable ranks inside the tile: chunks in order, peers found by a ballot per
     // id bit; the earlier tiles' counts are added once the look-back has them
     const uint64_t below = lanes_below_mask();
@@ -339,12 +343,21 @@ __global__ __launch_bounds__(kScanThreads) void layout_scan(
     }
 
     // the earlier tiles' counts by look-back, then this tile's inclusive prefix
-    // (agg becomes the inclusive prefix: the totals, in the last tile)
-    // (requested after the ranking, which gives the earlier tiles time to publish:
-    // requesting them before it measured slower)
+    // (agg becomes the inclusive prefix: the totals, in the last tile).  Words
+    // of the first batch that were not ready when requested are requested
+    // again by the walk.  (Requesting the batch before the ranking measured
+    // slower while the tile's start took three round trips; with one, it is
+    // 0.6-1 us faster at 4096 x 8 over 256 experts.)
     for (int x = tid; x < nb; x += kScanThreads) {
       uint64_t first[kLookback];
-      if (tile > 0) look_back_first(status, tile, nb, x, first);
+      if (tile > 0) {
+        if (x == tid) {
+#pragma unroll
+          for (int i = 0; i < kLookback; ++i) first[i] = first0[i];
+        } else {
+          look_back_first(status, tile, nb, x, first);
+        }
+      }
       const int32_t b = tile == 0 ? 0 : (int32_t)look_back(status, tile, nb, x, epoch, hdr, first);
       base[x] = b;
       agg[x] += b;
