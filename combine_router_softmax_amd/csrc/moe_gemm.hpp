@@ -23,7 +23,14 @@
 // so the m-tiles that share a weight tile run side by side.  Ids are first
 // remapped so that each of the 8 XCDs (workgroups are dealt to XCDs round-robin)
 // receives one contiguous range of that order: weight and activation tiles are
-// then re-read from the XCD's own L2.  Surplus workgroups exit at once.
+// then re-read from the XCD's own L2.  Surplus workgroups exit at once.  An
+// expert's rows are split evenly over its ceil(rows / 256) m-tiles in whole
+// 32-row blocks (520 rows: 192 + 192 + 136, not 256 + 256 + 8), so the m-tiles
+// that share a weight tile run the same MFMA loop and stay in step: a short
+// last tile ran ahead of its partners through the weights, which they then
+// fetched from HBM again (measured at 520 rows per expert: GEMM1 read 8.8 GB
+// of HBM against 4.0 GB at 512).  The MFMA work is the same either way: each
+// wave runs the MFMAs of its row blocks that hold rows.
 //
 // Tile: 256 rows x 256 columns (GEMM1: 128 gate + 128 up columns), 4 waves in
 // a 2 x 2 arrangement of 128 x 128 sub-tiles (4 x 4 MFMA 32x32 blocks, 256 fp32
@@ -118,8 +125,8 @@ inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 struct TileCoord {
   int e;
   int n_tile;
-  int64_t row0;
-  int64_t row_end;
+  int64_t row0;     // the tile's first row
+  int64_t row_end;  // one past its last row (at most row0 + 256)
 };
 
 // Maps blockIdx.x to an output tile; returns false for surplus workgroups.
@@ -190,10 +197,16 @@ __device__ bool find_tile(const int32_t *__restrict__ tokens_per_expert, const i
     const int32_t mt = (nrows + kBM - 1) / kBM;
     const int32_t local_id = logical - pre[lo];
     const int32_t m_tile = local_id % mt;
+    // the expert's 32-row blocks split evenly over its m-tiles (q blocks each,
+    // the last one fewer; q <= 8 and every tile holds rows)
+    const int32_t blocks = (nrows + 31) / 32;
+    const int32_t q = (blocks + mt - 1) / mt;
+    const int32_t first = m_tile * q * 32;
+    const int32_t last = first + q * 32 < nrows ? first + q * 32 : nrows;
     tc.e = lo;
     tc.n_tile = local_id / mt;
-    tc.row0 = (int64_t)offs_s[lo] + (int64_t)m_tile * kBM;
-    tc.row_end = (int64_t)offs_s[lo] + nrows;
+    tc.row0 = (int64_t)offs_s[lo] + first;
+    tc.row_end = (int64_t)offs_s[lo] + last;
   }
   __syncthreads();
   return ok;
@@ -642,8 +655,10 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
       sb_c[j] = sb_n[j];                                                                              \
     }                                                                                                 \
   }
-      if (mi_count > 2) {
+      if (mi_count > 3) {
         for (int kt = 0; kt < KT; ++kt) MOE_K_STEP8(4)
+      } else if (mi_count == 3) {
+        for (int kt = 0; kt < KT; ++kt) MOE_K_STEP8(3)
       } else if (mi_count == 2) {
         for (int kt = 0; kt < KT; ++kt) MOE_K_STEP8(2)
       } else {
@@ -707,12 +722,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     sb = nb;                                                                                           \
     sa = na;                                                                                           \
   }
-  // the ragged last tile of an expert runs the loop with the MFMAs of the row
-  // blocks that hold rows: a quarter or half of them when the waves hold at
-  // most one or two such blocks
+  // a tile of fewer than 256 rows runs the loop with the MFMAs of the row
+  // blocks that hold rows: one to four of each wave's four
   int sb = 0, sa = 1;
-  if (mi_count > 2) {
+  if (mi_count > 3) {
     for (int kt = 0; kt < KT; ++kt) MOE_K_STEP(4)
+  } else if (mi_count == 3) {
+    for (int kt = 0; kt < KT; ++kt) MOE_K_STEP(3)
   } else if (mi_count == 2) {
     for (int kt = 0; kt < KT; ++kt) MOE_K_STEP(2)
   } else {
