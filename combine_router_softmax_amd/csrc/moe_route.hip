@@ -40,39 +40,26 @@ __device__ __forceinline__ uint32_t logit_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Wave-wide max of a 64-bit key with DPP row operations instead of LDS
+// Wave-wide max of a 32-bit value with DPP row operations instead of LDS
 // permutes: four row_shr steps leave each row's max in its lane 15, two row
 // broadcasts carry it to lane 63, which is read back into every lane.  The
 // top-k loop makes k of these reductions in a row, so their latency matters.
+// A lane without a source (or outside ROW_MASK) reads 0, which leaves an
+// unsigned max unchanged; so the move and the max fuse into one DPP max.
 template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
-  // lanes without a source (or outside ROW_MASK) keep their own value
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)v, (int)(uint32_t)v, CTRL, ROW_MASK, 0xF,
-                                                            false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(v >> 32), (int)(uint32_t)(v >> 32), CTRL,
-                                                            ROW_MASK, 0xF, false);
-  return ((uint64_t)hi << 32) | lo;
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v) {
+  const uint32_t t = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, true);
+  return t > v ? t : v;
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64_dpp(uint64_t v) {
-  constexpr int kRowShr1 = 0x111, kRowShr2 = 0x112, kRowShr4 = 0x114, kRowShr8 = 0x118;
-  constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
-  uint64_t t;
-  t = dpp_u64<kRowShr1, 0xF>(v);
-  v = t > v ? t : v;
-  t = dpp_u64<kRowShr2, 0xF>(v);
-  v = t > v ? t : v;
-  t = dpp_u64<kRowShr4, 0xF>(v);
-  v = t > v ? t : v;
-  t = dpp_u64<kRowShr8, 0xF>(v);
-  v = t > v ? t : v;
-  t = dpp_u64<kRowBcast15, 0xA>(v);
-  v = t > v ? t : v;
-  t = dpp_u64<kRowBcast31, 0xC>(v);
-  v = t > v ? t : v;
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, kWave - 1);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), kWave - 1);
-  return ((uint64_t)hi << 32) | lo;
+__device__ __forceinline__ uint32_t wave_max_u32_dpp(uint32_t v) {
+  v = dpp_max_u32<0x111, 0xF>(v);
+  v = dpp_max_u32<0x112, 0xF>(v);
+  v = dpp_max_u32<0x114, 0xF>(v);
+  v = dpp_max_u32<0x118, 0xF>(v);
+  v = dpp_max_u32<0x142, 0xA>(v);
+  v = dpp_max_u32<0x143, 0xC>(v);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
 }
 
 __device__ __forceinline__ float key_logit(uint32_t key) {
@@ -234,21 +221,35 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const float *__res
       const int x = l + kWave * i;
       key[i] = x < e ? ((uint64_t)logit_key(lx[i]) << 32) | (uint32_t)~(uint32_t)x : 0ull;
     }
+    // Each round takes the largest remaining 64-bit key.  Every lane keeps its
+    // own largest key; the wave's largest logit key (the high words) comes from
+    // one 32-bit reduction, and only when several lanes hold it does a second
+    // reduction over their low words (~expert) pick the lowest expert.  The
+    // lane holding the chosen expert (x mod 64, slot x / 64) clears it.  (One
+    // 64-bit reduction per round, a compare and two selects per step, took
+    // about 930 cycles a round.)
     uint32_t taken = 0;
-    for (int j = 0; j < k; ++j) {
-      uint64_t best = key[0];
+    uint64_t lbest = key[0];
 #pragma unroll
-      for (int i = 1; i < VPL; ++i) best = key[i] > best ? key[i] : best;
-      best = wave_max_u64_dpp(best);
-      const uint32_t x = ~(uint32_t)best;
+    for (int i = 1; i < VPL; ++i) lbest = key[i] > lbest ? key[i] : lbest;
+    for (int j = 0; j < k; ++j) {
+      const uint32_t hi = (uint32_t)(lbest >> 32), lo = (uint32_t)lbest;
+      const uint32_t m_hi = wave_max_u32_dpp(hi);
+      const uint64_t cand = ballot(hi == m_hi);
+      const uint32_t m_lo = __popcll(cand) == 1 ? (uint32_t)__builtin_amdgcn_readlane((int)lo, __builtin_ctzll(cand))
+                                                : wave_max_u32_dpp(hi == m_hi ? lo : 0u);
+      const uint32_t x = ~m_lo;
 #pragma unroll
       for (int i = 0; i < VPL; ++i)
         if ((uint32_t)(l + kWave * i) == x) {
           key[i] = 0ull;
           taken |= 1u << i;
         }
+      lbest = key[0];
+#pragma unroll
+      for (int i = 1; i < VPL; ++i) lbest = key[i] > lbest ? key[i] : lbest;
       if (l == 0) {
-        sel_key[j] = (uint32_t)(best >> 32);
+        sel_key[j] = m_hi;
         sel_idx[j] = (int32_t)x;
       }
     }
