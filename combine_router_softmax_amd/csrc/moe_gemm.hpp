@@ -516,9 +516,13 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   }
   const uint32_t ring_lds = lds_address(ring) + w * 64 * kRowBytes;  // = w * 16 * kTRowBytes
   // load instruction i (0..7) of this wave for the A (B) tile of step kt into
-  // ring slot `slot`
+  // ring slot `slot`.  A wave whose 64 A rows all lie past the segment's end
+  // (a tile of at most 192 rows) issues no A loads: no wave multiplies those
+  // row blocks, so their stale LDS rows are never used; such a wave's waits
+  // count its B loads only.
+  const bool a_live = w * 64 < rows_valid;
   auto load_a = [&](int slot, int kt, int i) {
-    dma16(a_base + kt * a_step, a_off[i], ring_lds + slot * kOperandBytes + i * 1024);
+    if (a_live) dma16(a_base + kt * a_step, a_off[i], ring_lds + slot * kOperandBytes + i * 1024);
   };
   auto load_b = [&](int slot, int kt, int i) {
     dma16(b_base + kt * b_step, b_off[i], ring_lds + slot * kOperandBytes + i * 1024);
@@ -616,7 +620,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
         for (int i = 0; i < kLoads; ++i) load_b(2, 1, i);
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) load_a(3, 1, i);
-        wait_vmcnt<2 * kLoads>();
+        if (a_live) wait_vmcnt<2 * kLoads>();  // step 0's tiles (and the scales) have landed
+        else wait_vmcnt<kLoads>();
       } else {
         wait_vmcnt<0>();
       }
@@ -678,7 +683,8 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     for (int i = 0; i < kLoads; ++i) load_b(2, 1, i);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) load_a(3, 1, i);
-    wait_vmcnt<2 * kLoads>();
+    if (a_live) wait_vmcnt<2 * kLoads>();  // step 0's tiles have landed
+    else wait_vmcnt<kLoads>();
   } else {
     wait_vmcnt<0>();
   }
