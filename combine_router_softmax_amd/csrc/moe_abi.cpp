@@ -183,14 +183,16 @@ moe_status dispatch_layout(const moe_shape *s, int64_t rows, const void *x, cons
   const size_t need_ws = moe::layout_workspace_bytes(a, s->n_experts, by_weight(s));
   if (workspace_bytes < need_ws || !workspace || (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return MOE_ERR_WORKSPACE;
+  // the scan launch also reads the rows that the scatter after it copies
+  const int64_t x_bytes = x ? n * s->hidden * elem_bytes(s->act_dtype) : 0;
   if (place_in_scatter)  // the scan alone; the scatter places the rows
     return hip_status(moe::launch_layout_scan(topk_idx, n, s->top_k, s->n_experts, s->capacity, s->row_align, rows,
                                               layout->tokens_per_expert, layout->expert_offsets, layout->ordinal,
-                                              layout->counters, workspace, hs));
+                                              layout->counters, workspace, x, x_bytes, hs));
   return hip_status(moe::launch_layout(topk_idx, topk_w, n, s->top_k, s->n_experts, s->capacity, s->row_align,
                                        by_weight(s), rows, layout->tokens_per_expert, layout->expert_offsets,
                                        layout->ordinal, layout->assign_row, layout->row_src, layout->drop_mask,
-                                       layout->pad_mask, layout->counters, w_perm, workspace, hs));
+                                       layout->pad_mask, layout->counters, w_perm, workspace, x, x_bytes, hs));
 }
 
 // Pad rows to zero: capacity pads (every row without an assignment), or the

@@ -30,16 +30,20 @@ hipError_t clear_layout_header(void *workspace, hipStream_t stream);
 // the scan alone: ordinal, tokens_per_expert, expert_offsets, counters; rows
 // are then placed by launch_scatter_placing (or not at all: the reroute).  The
 // next kernel of the call must run finish_scan on the workspace header.
+// warm, warm_bytes (both launches): the source rows that the call's scatter
+// reads, which the scan launch reads alongside into the memory-side cache
+// (nullptr, 0 where no rows follow).
 hipError_t launch_layout_scan(const int32_t *topk_idx, int64_t n, int k, int e, int capacity, int row_align,
                               int64_t rows, int32_t *tokens_per_expert, int32_t *expert_offsets, int32_t *ordinal,
-                              int32_t *counters, void *workspace, hipStream_t stream);
+                              int32_t *counters, void *workspace, const void *warm, int64_t warm_bytes,
+                              hipStream_t stream);
 // the whole layout with the rows placed in a launch of their own;
 // drop_by_weight (with a capacity): keep each expert's `capacity` largest weights
 hipError_t launch_layout(const int32_t *topk_idx, const float *topk_w, int64_t n, int k, int e, int capacity,
                          int row_align, bool drop_by_weight, int64_t rows, int32_t *tokens_per_expert,
                          int32_t *expert_offsets, int32_t *ordinal, int32_t *assign_row, int32_t *row_src,
                          uint8_t *drop_mask, uint8_t *pad_mask, int32_t *counters, float *w_perm, void *workspace,
-                         hipStream_t stream);
+                         const void *warm, int64_t warm_bytes, hipStream_t stream);
 
 // ---- row movement (moe_rows.hip); `row_bytes` is a multiple of 16.  Pad rows
 // (row_src < 0) below pad_rows, and below *pad_limit when pad_limit is given,

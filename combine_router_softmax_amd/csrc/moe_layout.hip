@@ -33,7 +33,9 @@
 //   whatever order they run in.
 //   Rows are then placed from (ordinal, kept, offset) alone (moe_place.hpp):
 //   by the scatter as it copies the rows, or by layout_finish where no scatter
-//   follows.
+//   follows.  In a dispatch, extra workgroups of the scan launch read the
+//   source rows meanwhile, so that the scatter finds them in the memory-side
+//   cache (layout_scan).
 // Status words are 64-bit: [63:34] the call's epoch, [33:32] the flag, [31:0]
 // the count, written and read with device-scope atomics, so one word carries
 // flag and value together.  The workspace header holds the ticket and the
@@ -62,6 +64,16 @@ constexpr int kLookback = 16;                // status words in flight per threa
 constexpr uint32_t kSpinLimit = 1u << 17;    // polls of one word before giving up (~0.1 s)
 constexpr uint64_t kFlagAgg = 1, kFlagIncl = 2;
 constexpr uint32_t kEpochMask = 0x3FFFFFFFu;
+constexpr int kWarmLoads = 8;                     // 16-byte loads in flight per thread
+// row-reading workgroups beside the scan: one per compute unit (the scan's
+// registers allow one 512-thread workgroup per unit); 64 and 128 measured
+// 3-9 us slower cold
+constexpr int64_t kWarmBlocks = 256;
+// at most 64 MiB of rows, about what HBM delivers while the scan runs: reading
+// more outlasts the scan and delays the scatter (measured: 128 MiB of a
+// 235 MB source took a warm dispatch from 117 to 125 us and gained nothing
+// cold; 64 MiB: 117 -> 119 us warm, 142 -> 140 us cold)
+constexpr int64_t kWarmMaxBytes = 64ll << 20;
 
 inline size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
@@ -241,12 +253,35 @@ __device__ void finalize_layout(const int32_t *total, int e, int capacity, int r
 // chunks; bin e (E + 1 bins) counts the invalid ids (neither -1 nor an expert).
 // BITS: an upper bound of the expert id's bit count (a compile-time count keeps
 // the ballot loop unrolled; bits above the ids' own are zero in every lane).
+// Workgroups from `tiles` on take no ticket: they read the dispatch's source
+// rows (the first `warm_vecs` 16-byte vectors) and exit.  The scan is bound by
+// memory round trips and leaves HBM idle meanwhile; the reads bring the rows
+// into the memory-side cache, where the scatter that follows finds them, and
+// HBM still delivers each byte once.  The values are consumed by an empty asm
+// statement, so the loads stay whole 16-byte loads.
 template <int BITS>
 __global__ __launch_bounds__(kScanThreads) void layout_scan(
     const int32_t *__restrict__ topk_idx, int64_t a_total, int64_t tiles, int e, int capacity,
     int row_align, int64_t rows, ScanHeader *hdr, uint64_t *status, int32_t *__restrict__ ordinal,
     int32_t *__restrict__ tokens_per_expert, int32_t *__restrict__ expert_offsets, int32_t *__restrict__ counters,
-    int32_t *__restrict__ full_off) {
+    int32_t *__restrict__ full_off, const u32x4 *__restrict__ warm, int64_t warm_vecs) {
+  if (blockIdx.x >= tiles) {  // block-uniform
+    const int64_t stride = (int64_t)(gridDim.x - tiles) * kScanThreads * kWarmLoads;
+    uint32_t acc = 0;
+    for (int64_t v0 = (blockIdx.x - tiles) * kScanThreads * kWarmLoads + threadIdx.x; v0 < warm_vecs;
+         v0 += stride) {
+      u32x4 r[kWarmLoads];
+#pragma unroll
+      for (int i = 0; i < kWarmLoads; ++i) {
+        const int64_t v = v0 + i * kScanThreads;
+        r[i] = warm[v < warm_vecs ? v : warm_vecs - 1];  // past the end: the last vector again
+      }
+#pragma unroll
+      for (int i = 0; i < kWarmLoads; ++i) acc ^= r[i].x ^ r[i].y ^ r[i].z ^ r[i].w;
+    }
+    asm volatile("" ::"v"(acc));
+    return;
+  }
   extern __shared__ int32_t sm[];
   const int nb = e + 1;
   int32_t *run = sm;                  // [waves][nb] per-wave counts, then running bases
@@ -593,15 +628,21 @@ LayoutWorkspace carve(void *workspace, int64_t a_total, int e, bool by_weight) {
   return w;
 }
 
+// warm, warm_bytes: the rows the next kernel reads (nullptr, 0: none); the
+// scan launch reads up to kWarmMaxBytes of them alongside (see layout_scan)
 hipError_t scan(const int32_t *topk_idx, int64_t a_total, int e, int capacity, int row_align, int64_t rows,
                 int32_t *tokens_per_expert, int32_t *expert_offsets, int32_t *ordinal, int32_t *counters,
-                const LayoutWorkspace &w, hipStream_t stream) {
+                const LayoutWorkspace &w, const void *warm, int64_t warm_bytes, hipStream_t stream) {
   const int64_t tiles = layout_tiles(a_total);
   const size_t lds = sizeof(int32_t) * (size_t)(kScanWaves + 2) * (e + 1);
+  const int64_t warm_vecs = warm ? (warm_bytes < kWarmMaxBytes ? warm_bytes : kWarmMaxBytes) / 16 : 0;
+  const int64_t per_block = (int64_t)kScanThreads * kWarmLoads;
+  const int64_t warm_blocks = warm_vecs > 0 ? std::min<int64_t>(kWarmBlocks, (warm_vecs + per_block - 1) / per_block) : 0;
 #define MOE_SCAN(B)                                                                                                  \
-  hipLaunchKernelGGL(layout_scan<B>, dim3((unsigned)tiles), dim3(kScanThreads), lds, stream, topk_idx, a_total,     \
-                     tiles, e, capacity, row_align > 1 ? row_align : 1, rows, w.hdr, w.status, ordinal,               \
-                     tokens_per_expert, expert_offsets, counters, w.full_off)
+  hipLaunchKernelGGL(layout_scan<B>, dim3((unsigned)(tiles + warm_blocks)), dim3(kScanThreads), lds, stream,        \
+                     topk_idx, a_total, tiles, e, capacity, row_align > 1 ? row_align : 1, rows, w.hdr, w.status,     \
+                     ordinal, tokens_per_expert, expert_offsets, counters, w.full_off,                                \
+                     static_cast<const u32x4 *>(warm), warm_vecs)
   if (e <= 16) MOE_SCAN(4);
   else if (e <= 64) MOE_SCAN(6);
   else if (e <= 256) MOE_SCAN(8);
@@ -620,22 +661,23 @@ hipError_t clear_layout_header(void *workspace, hipStream_t stream) {
 
 hipError_t launch_layout_scan(const int32_t *topk_idx, int64_t n, int k, int e, int capacity, int row_align,
                               int64_t rows, int32_t *tokens_per_expert, int32_t *expert_offsets, int32_t *ordinal,
-                              int32_t *counters, void *workspace, hipStream_t stream) {
+                              int32_t *counters, void *workspace, const void *warm, int64_t warm_bytes,
+                              hipStream_t stream) {
   const int64_t a_total = n * k;
   return scan(topk_idx, a_total, e, capacity, row_align, rows, tokens_per_expert, expert_offsets, ordinal, counters,
-              carve(workspace, a_total, e, false), stream);
+              carve(workspace, a_total, e, false), warm, warm_bytes, stream);
 }
 
 hipError_t launch_layout(const int32_t *topk_idx, const float *topk_w, int64_t n, int k, int e, int capacity,
                          int row_align, bool drop_by_weight, int64_t rows, int32_t *tokens_per_expert,
                          int32_t *expert_offsets, int32_t *ordinal, int32_t *assign_row, int32_t *row_src,
                          uint8_t *drop_mask, uint8_t *pad_mask, int32_t *counters, float *w_perm, void *workspace,
-                         hipStream_t stream) {
+                         const void *warm, int64_t warm_bytes, hipStream_t stream) {
   const int64_t a_total = n * k;
   const bool by_weight = drop_by_weight && capacity > 0;
   const LayoutWorkspace w = carve(workspace, a_total, e, by_weight);
   hipError_t st = scan(topk_idx, a_total, e, capacity, row_align, rows, tokens_per_expert, expert_offsets, ordinal,
-                       counters, w, stream);
+                       counters, w, warm, warm_bytes, stream);
   if (st != hipSuccess) return st;
   const PlaceArgs p = place_args(topk_idx, topk_w, ordinal, tokens_per_expert, expert_offsets, e, capacity,
                                  row_align, rows, assign_row, drop_mask, row_src, pad_mask, w_perm, workspace,

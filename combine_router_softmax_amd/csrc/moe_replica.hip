@@ -179,7 +179,7 @@ hipError_t launch_reroute(const int32_t *topk_idx, int64_t n, int k, int e, cons
   int32_t *ord = reinterpret_cast<int32_t *>(take(4 * (size_t)a));
   int32_t *ctr = reinterpret_cast<int32_t *>(take(16));
   // the layout scan alone gives the ordinals and counts of the logical ids
-  hipError_t st = launch_layout_scan(topk_idx, n, k, e, 0, 0, a, tpe, off, ord, ctr, workspace, stream);
+  hipError_t st = launch_layout_scan(topk_idx, n, k, e, 0, 0, a, tpe, off, ord, ctr, workspace, nullptr, 0, stream);
   if (st != hipSuccess) return st;
   hipLaunchKernelGGL(reroute_kernel, dim3(grid_for(a, 4096)), dim3(kThreads), 0, stream, topk_idx, a, e, ord, tpe,
                      replica_of, r, phys_idx, static_cast<ScanHeader *>(workspace), ctr);
