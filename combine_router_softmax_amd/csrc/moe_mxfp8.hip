@@ -48,8 +48,7 @@ __device__ __forceinline__ uint32_t mx_half(const u32x4 (&in)[2], u32x4 &out) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const uint32_t w0 = in[i][2 * h], w1 = in[i][2 * h + 1];
-      out[2 * i + h] = e4m3_code(bf16_lo(w0) * inv) | (e4m3_code(bf16_hi(w0) * inv) << 8) |
-                       (e4m3_code(bf16_lo(w1) * inv) << 16) | (e4m3_code(bf16_hi(w1) * inv) << 24);
+      out[2 * i + h] = e4m3x4(bf16_lo(w0) * inv, bf16_hi(w0) * inv, bf16_lo(w1) * inv, bf16_hi(w1) * inv);
     }
   return (uint32_t)code;
 }

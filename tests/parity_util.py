@@ -74,3 +74,29 @@ def workload_inputs(w: mi.Workload, seed: int = 0):
         return None, None, mi.router_logits(w, seed), x
     idx, wts = mi.received_routing(w, seed)
     return idx, wts, None, x
+
+
+def every_value_at_every_scale():
+    """bf16 rows in 32-element blocks: for each exponent field f_a = 0..254 the
+    blocks hold the largest value of that field (the block maximum, so the
+    scale code is max(f_a - 8, 0): every code a finite block can have) and,
+    both signs, every pattern of the 21 exponent fields f_a - 20 .. f_a (from
+    the largest codes down through E4M3's subnormals to values that round to
+    zero), the last block of each f_a filled up with zeros."""
+    blocks = []
+    for fa in range(255):
+        top = (fa << 7) | 0x7F
+        lo = max(fa - 20, 0) << 7
+        mag = np.arange(lo, top + 1, dtype=np.uint32)
+        vals = np.concatenate([mag, mag | 0x8000]).astype(np.uint16)
+        nb = -(-vals.size // 31)
+        body = np.zeros(nb * 31, np.uint16)
+        body[:vals.size] = vals
+        blk = np.empty((nb, 32), np.uint16)
+        blk[:, 0] = top
+        blk[:, 1:] = body.reshape(nb, 31)
+        blocks.append(blk)
+    b = np.concatenate(blocks)
+    pad = -b.shape[0] % 32
+    b = np.concatenate([b, np.zeros((pad, 32), np.uint16)])
+    return b.reshape(-1, 32 * 32)                                   # rows of 1024 elements

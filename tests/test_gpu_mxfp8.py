@@ -11,7 +11,8 @@ import torch
 
 import moe_inputs as mi
 import oracle
-from parity_util import TOL_BF16, assert_layout_equal, dev, host, layout_host, max_rel_err, values, workload_inputs
+from parity_util import (TOL_BF16, assert_layout_equal, dev, every_value_at_every_scale, host, layout_host,
+                         max_rel_err, values, workload_inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -158,6 +159,17 @@ def test_mx_quantize(moe, rows, cols):
     g = np.random.default_rng(rows + cols)
     x = mi.f32_to_bf16_bits((g.standard_normal((rows, cols)) * np.exp(g.uniform(-10, 10, (rows, 1)))).astype(np.float32))
     x[0, :32] = 0
+    q, s = moe.moe_mx_quantize(dev(x))
+    torch.cuda.synchronize()
+    ref_q, ref_s = oracle.mx_quantize(x)
+    np.testing.assert_array_equal(host(s), ref_s)
+    np.testing.assert_array_equal(host(q), ref_q)
+
+
+def test_mx_quantize_every_value_at_every_scale(moe):
+    """The device encoder against the oracle for every bf16 value within 20
+    binades below a block maximum, at every scale code (about 1.4 M elements)."""
+    x = every_value_at_every_scale()
     q, s = moe.moe_mx_quantize(dev(x))
     torch.cuda.synchronize()
     ref_q, ref_s = oracle.mx_quantize(x)

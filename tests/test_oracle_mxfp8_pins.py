@@ -23,6 +23,7 @@ import torch
 
 import moe_inputs as mi
 import oracle
+from parity_util import every_value_at_every_scale
 
 RNG = np.random.default_rng(2024)
 
@@ -248,3 +249,11 @@ def test_expert_ffn_mxfp8_zero_gate():
     lay = {"expert_offsets": np.array([0, 4, 8], np.int32), "tokens_per_expert": np.array([4, 4], np.int32)}
     got, _ = oracle.expert_ffn_mxfp8_rows(np.arange(rows), xq, xs, lay, gq, gs, dq, ds)
     assert not got.any()
+
+
+def test_every_value_at_every_scale_covers_the_codes():
+    x = every_value_at_every_scale()
+    _, sc = oracle.mx_quantize(x)
+    assert set(np.unique(sc).tolist()) == set(range(247))           # scale codes 0 .. 246
+    mag = x & 0x7FFF
+    assert ((mag >> 7) != 0xFF).all()                                # finite only
