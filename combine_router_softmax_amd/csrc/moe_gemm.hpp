@@ -130,17 +130,18 @@ struct TileCoord {
 };
 
 // Maps blockIdx.x to an output tile; returns false for surplus workgroups.
-// `scratch` (LDS) must hold 3 * kMaxExperts + kThreads / kWave int32 and is
-// free again on return.  The experts' row counts and offsets are read in one
-// round of loads and kept in LDS; the tile counts are scanned with wave scans
-// and one barrier.  Tile counts fit in int32: their total bounds the grid.
+// `scratch` (LDS) must hold kThreads / kWave + 4 int32 and is free again on
+// return.  The experts' row counts and offsets are read in one round of loads
+// (kPer experts per thread, in registers); the tile counts are scanned with
+// wave scans and one barrier, after which each thread knows the first tile of
+// each of its experts, and the thread whose expert holds the workgroup's tile
+// publishes the tile's coordinates for a second barrier.  Tile counts fit in
+// int32: their total bounds the grid.
 __device__ bool find_tile(const int32_t *__restrict__ tokens_per_expert, const int32_t *__restrict__ expert_offsets,
                           int e, int n_tiles, int32_t *scratch, TileCoord &tc) {
   constexpr int kPer = kMaxExperts / kThreads;  // experts per thread
-  int32_t *pre = scratch;                       // [kMaxExperts] first tile of each expert
-  int32_t *rows_s = pre + kMaxExperts;          // [kMaxExperts]
-  int32_t *offs_s = rows_s + kMaxExperts;       // [kMaxExperts]
-  int32_t *wave_tot = offs_s + kMaxExperts;     // [kThreads / kWave]
+  int32_t *wave_tot = scratch;                  // [kThreads / kWave]
+  int32_t *found = wave_tot + kThreads / kWave; // [4]: expert, n-tile, first row, one past the last
   const int tid = threadIdx.x;
   int32_t rows[kPer], offs[kPer];
 #pragma unroll
@@ -153,11 +154,8 @@ __device__ bool find_tile(const int32_t *__restrict__ tokens_per_expert, const i
   int32_t s = 0;
 #pragma unroll
   for (int i = 0; i < kPer; ++i) {
-    const int x = tid * kPer + i;
     local[i] = ((rows[i] + kBM - 1) / kBM) * n_tiles;
     s += local[i];
-    rows_s[x] = rows[i];
-    offs_s[x] = offs[i];
   }
   const int l = lane_id(), wv = tid / kWave;
   int32_t incl = s;  // inclusive scan over the wave
@@ -174,39 +172,40 @@ __device__ bool find_tile(const int32_t *__restrict__ tokens_per_expert, const i
     run += i < wv ? wave_tot[i] : 0;
     total += wave_tot[i];
   }
-#pragma unroll
-  for (int i = 0; i < kPer; ++i) {
-    pre[tid * kPer + i] = run;
-    run += local[i];
-  }
-  __syncthreads();
-
   const int32_t bid = blockIdx.x;
   const int32_t share = (total + kXcds - 1) / kXcds;
   const int32_t slot = bid / kXcds;
   const int32_t logical = (bid % kXcds) * share + slot;
-  bool ok = slot < share && logical < total;
+  const bool ok = slot < share && logical < total;  // block-uniform
   if (ok) {
-    int lo = 0, hi = e - 1;  // last expert whose first tile is <= logical
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (pre[mid] <= logical) lo = mid;
-      else hi = mid - 1;
+    // exactly one expert's tile range [run, run + local) holds `logical`
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+      if (logical >= run && logical < run + local[i]) {
+        const int32_t nrows = rows[i];
+        const int32_t mt = (nrows + kBM - 1) / kBM;
+        const int32_t local_id = logical - run;
+        const int32_t m_tile = local_id % mt;
+        // the expert's 32-row blocks split evenly over its m-tiles (q blocks
+        // each, the last one fewer; q <= 8 and every tile holds rows)
+        const int32_t blocks = (nrows + 31) / 32;
+        const int32_t q = (blocks + mt - 1) / mt;
+        const int32_t first = m_tile * q * 32;
+        const int32_t last = first + q * 32 < nrows ? first + q * 32 : nrows;
+        found[0] = tid * kPer + i;
+        found[1] = local_id / mt;
+        found[2] = offs[i] + first;  // row offsets are int32 (the layout's row maps are)
+        found[3] = offs[i] + last;
+      }
+      run += local[i];
     }
-    const int32_t nrows = rows_s[lo];
-    const int32_t mt = (nrows + kBM - 1) / kBM;
-    const int32_t local_id = logical - pre[lo];
-    const int32_t m_tile = local_id % mt;
-    // the expert's 32-row blocks split evenly over its m-tiles (q blocks each,
-    // the last one fewer; q <= 8 and every tile holds rows)
-    const int32_t blocks = (nrows + 31) / 32;
-    const int32_t q = (blocks + mt - 1) / mt;
-    const int32_t first = m_tile * q * 32;
-    const int32_t last = first + q * 32 < nrows ? first + q * 32 : nrows;
-    tc.e = lo;
-    tc.n_tile = local_id / mt;
-    tc.row0 = (int64_t)offs_s[lo] + first;
-    tc.row_end = (int64_t)offs_s[lo] + last;
+  }
+  __syncthreads();
+  if (ok) {
+    tc.e = found[0];
+    tc.n_tile = found[1];
+    tc.row0 = found[2];
+    tc.row_end = found[3];
   }
   __syncthreads();
   return ok;
