@@ -562,16 +562,17 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
   if constexpr (kFp8) {
     // MXFP8 K loop: 128 codes per step in two 64-wide slices.  Four ring slots:
     // step kt's B and A tiles in slots (2kt) % 4 and (2kt) % 4 + 1.  Slice 0
-    // runs under the reads of slice 1's fragments; then every wave waits for
-    // its loads of step kt+1 and passes a barrier (no wave reads step kt's
-    // tiles any more); slice 1 runs under the reads of step kt+1's first
-    // fragments and scales and loads step kt+2's tiles into step kt's slots,
-    // over the first three of its four load slots: issuing all sixteen loads
-    // at once leaves the MFMA pipe without work while they issue, spreading
-    // them over all four slots requests the last ones too late (with four ring
-    // slots a tile is requested only about one step before use); measured,
-    // three slots: equal to one at the Qwen3-like layer, 2 % faster at the
-    // 32-expert share; four slots 2-3 % slower.
+    // runs under the reads of slice 1's fragments; once they have arrived,
+    // every wave holds all of step kt's fragments, so an LDS barrier there
+    // frees step kt's slots and the rest of slice 0 loads step kt+2's B tile
+    // into its B slot (two loads per load slot).  Then every wave waits for its
+    // loads of step kt+1 (step kt+2's B tile may stay in flight) and passes a
+    // barrier; slice 1 runs under the reads of step kt+1's first fragments and
+    // scales and loads step kt+2's A tile (two per load slot).  Issuing all
+    // sixteen loads in slice 1 (after the second barrier, the first point at
+    // which the slots were known free) had the loads' address processing hold
+    // the waves' MFMA issue: slice 1 took about twice its MFMA time (in-kernel
+    // clock stamps), and the extra barrier made the MXFP8 FFN 12-13 % faster.
     // The E8M0 scales come in groups of four K steps (16 bytes per tile row per
     // operand) into two LDS buffers: group g+1 is loaded in step 4g, after its
     // buffer's previous group was last read (in step 4g-2), and is waited for
@@ -637,20 +638,25 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     const bool ahead = kt + 2 < KT;                                                                   \
     const bool scales_ahead = (kt & 3) == 0 && kt + 4 < KT;                                           \
     load_frags_fp8<kSwiGLU>(bs + kOperandBytes, bs, 1, wm, wn, l, fa[1], fb[1]);                      \
-    slice_fp8<MI, 16, 0>(fa[0], fb[0], sa_c, sb_c, acc, [&](int) {});                                 \
-    wait_vmcnt<0>();                                                                                  \
+    slice_fp8<MI, 16, 0>(fa[0], fb[0], sa_c, sb_c, acc, [&](int d) {                                  \
+      /* once every wave holds step kt's last fragments, its B slot takes step kt+2's B tile */        \
+      if (d == 0) lds_barrier();                                                                      \
+      if (ahead) {                                                                                    \
+        load_b(sbt, kt + 2, 2 * d);                                                                   \
+        load_b(sbt, kt + 2, 2 * d + 1);                                                               \
+      }                                                                                               \
+    });                                                                                               \
+    if (ahead) wait_vmcnt<kLoads>(); /* all but step kt+2's B tile */                                 \
+    else wait_vmcnt<0>();                                                                             \
     lds_barrier();                                                                                    \
     __builtin_amdgcn_sched_barrier(0);                                                                \
     /* the last step reads stale slots here; those values are not used */                           \
     load_frags_fp8<kSwiGLU>(nbs + kOperandBytes, nbs, 0, wm, wn, l, fa[0], fb[0]);                    \
     read_scales(kt + 1, sa_n, sb_n);                                                                  \
     slice_fp8<MI, 24, 2>(fa[1], fb[1], sa_c, sb_c, acc, [&](int d) {                                  \
-      if (ahead && d < 3) { /* B then A, 6 / 5 / 5 loads at the first three slots */                   \
-        _Pragma("unroll") for (int q = 0; q < 2 * kLoads; ++q)                                         \
-          if (q * 3 / (2 * kLoads) == d) {                                                            \
-            if (q < kLoads) load_b(sbt, kt + 2, q);                                                   \
-            else load_a(sbt + 1, kt + 2, q - kLoads);                                                 \
-          }                                                                                           \
+      if (ahead) {                                                                                    \
+        load_a(sbt + 1, kt + 2, 2 * d);                                                               \
+        load_a(sbt + 1, kt + 2, 2 * d + 1);                                                           \
       }                                                                                               \
       if (d == 0 && scales_ahead) load_scales((kt >> 2) + 1);                                         \
     });                                                                                               \
