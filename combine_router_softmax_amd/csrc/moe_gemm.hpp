@@ -800,24 +800,39 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
       // the bf16 intermediate quantised to MXFP8 on the way out: the four lanes
       // ch 0..3 (4..7) of a row hold one 32-feature block (N % 512 == 0, so
       // every column exists); all lanes quantise, the rows inside the tile store
-#pragma unroll 4
-      for (int i = 0; i < 16; ++i) {
-        const int r = l / 8 + 8 * i;
-        const int row = tile_row(r);
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * 128 + pos8(r, ch) * 16);
-        u32x2 q;
-        const uint32_t code = mx_quad(v, q);
-        if (row < rows_valid) {
-          *reinterpret_cast<u32x2 *>(q_base + (int64_t)row * ldc + col) = q;
-          if ((ch & 3) == 0) qs_base[(int64_t)row * (ldc / 32) + col / 32] = (uint8_t)code;
+#pragma unroll
+      for (int b = 0; b < 16; b += 8) {
+        u32x4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int r = l / 8 + 8 * (b + j);
+          v[j] = *reinterpret_cast<const u32x4 *>(stage + r * 128 + pos8(r, ch) * 16);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int row = tile_row(l / 8 + 8 * (b + j));
+          u32x2 q;
+          const uint32_t code = mx_quad(v[j], q);
+          if (row < rows_valid) {
+            *reinterpret_cast<u32x2 *>(q_base + (int64_t)row * ldc + col) = q;
+            if ((ch & 3) == 0) qs_base[(int64_t)row * (ldc / 32) + col / 32] = (uint8_t)code;
+          }
         }
       }
     } else {
-#pragma unroll 4
-      for (int r = l / 8; r < 128; r += 8) {
-        const int row = tile_row(r);
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * 128 + pos8(r, ch) * 16);
-        if (row < rows_valid && col < N) st16(c_base + (int64_t)row * ldc + col, v);
+#pragma unroll
+      for (int b = 0; b < 16; b += 8) {
+        u32x4 v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int r = l / 8 + 8 * (b + q);
+          v[q] = *reinterpret_cast<const u32x4 *>(stage + r * 128 + pos8(r, ch) * 16);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int row = tile_row(l / 8 + 8 * (b + q));
+          if (row < rows_valid && col < N) st16(c_base + (int64_t)row * ldc + col, v[q]);
+        }
       }
     }
     if (gu_base) {
@@ -829,11 +844,19 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
       const int ch16 = l % 16;
       const int feat = n0 + wn * 64 + (ch16 & 7) * 8;
       const int gcol = (ch16 >= 8 ? N : 0) + feat;
-#pragma unroll 4
-      for (int r = l / 16; r < 128; r += 4) {
-        const int row = tile_row(r);
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * 256 + pos16(r, ch16) * 16);
-        if (row < rows_valid && feat < N) st16(gu_base + (int64_t)row * 2 * N + gcol, v);
+#pragma unroll
+      for (int b = 0; b < 32; b += 8) {
+        u32x4 v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int r = l / 16 + 4 * (b + q);
+          v[q] = *reinterpret_cast<const u32x4 *>(stage + r * 256 + pos16(r, ch16) * 16);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int row = tile_row(l / 16 + 4 * (b + q));
+          if (row < rows_valid && feat < N) st16(gu_base + (int64_t)row * 2 * N + gcol, v[q]);
+        }
       }
     }
   } else {
@@ -841,11 +864,21 @@ __global__ __launch_bounds__(kThreads, 1) void grouped_gemm_kernel(
     const int ch = l % 16;
     const int col = n0 + wn * 128 + ch * 8;
     const int64_t c_ld = ldc;
-#pragma unroll 4
-    for (int r = l / 16; r < 128; r += 4) {
-      const int row = tile_row(r);
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(stage + r * 256 + pos16(r, ch) * 16);
-      if (row < rows_valid && col < N) st16(c_base + (int64_t)row * c_ld + col, v);
+    // eight staged vectors read (unconditionally: the stage is in bounds), then
+    // their stores, so that one LDS wait serves eight stores
+#pragma unroll
+    for (int b = 0; b < 32; b += 8) {
+      u32x4 v[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int r = l / 16 + 4 * (b + q);
+        v[q] = *reinterpret_cast<const u32x4 *>(stage + r * 256 + pos16(r, ch) * 16);
+      }
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const int row = tile_row(l / 16 + 4 * (b + q));
+        if (row < rows_valid && col < N) st16(c_base + (int64_t)row * c_ld + col, v[q]);
+      }
     }
   }
 }
