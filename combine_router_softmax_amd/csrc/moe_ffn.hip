@@ -33,18 +33,19 @@ namespace {
 // 8 XCDs in snake order (0..7, 7..0, 0..7, ...), so each XCD works through
 // whole experts or large parts of one: their operand panels are fetched into
 // that XCD's L2 only.  Experts without rows are units too (their tiles are
-// zero).  Each XCD's units form a list; a workgroup takes the next tile of its
-// XCD's list (workgroup b runs on XCD b % 8 and takes tile b / 8), so the
-// hardware's dispatch balances the tiles over the XCD's CUs as they free up
-// (simulated on the Zipf-loaded 32-expert layer: the XCD finishing last ends
-// 3 % after the mean; whole experts on fixed per-CU tile lists end 170 % after
+// zero).  Each XCD's units form a list; a workgroup takes the next chain of
+// tiles (kChain tiles of one unit, below) of its XCD's list (workgroup b runs
+// on XCD b % 8 and takes chain b / 8), so the hardware's dispatch balances the
+// chains over the XCD's CUs as they free up (simulated on the Zipf-loaded
+// 32-expert layer with one tile per workgroup: the XCD finishing last ends 3 %
+// after the mean; whole experts on fixed per-CU tile lists end 170 % after
 // it).
 // plan (int32): [0..8] first entry of each XCD's list; [9..16] and [17..24]
-// tiles of each XCD's list in dW_down and in dW_gate_up; [25] 64-row blocks of
-// the K-major copies (poff_E / 64); entries of kEntryInts from kPlanEntries
+// chains of each XCD's list in dW_down and in dW_gate_up; [25] 64-row blocks
+// of the K-major copies (poff_E / 64); entries of kEntryInts from kPlanEntries
 // in XCD-list order: the unit (expert | part << 11 | parts << 21), the
-// expert's rows, its segment start, its poff, its first tile in dW_down's list
-// and in dW_gate_up's; poff_0 .. poff_E from kPlanPoff.
+// expert's rows, its segment start, its poff, its first chain in dW_down's
+// list and in dW_gate_up's; poff_0 .. poff_E from kPlanPoff.
 constexpr int kWgradDiv = 16;
 constexpr int kMaxUnits = kMaxExperts + kWgradDiv;  // sum of ceil(16 steps_e / S) <= 16 + E
 constexpr int kEntryInts = 8;
@@ -57,8 +58,23 @@ static_assert(kMaxExperts == kPlanThreads, "one plan thread per expert");
 static_assert((kMaxUnits + kXcds - 1) / kXcds <= kListLanes * kWave, "an XCD's list fits the lookup");
 static_assert(kMaxUnits <= 2 * kPlanThreads, "two units per plan thread");
 
-// Upper bound of the tiles of one XCD's list (the grid is 8 times that).
-int64_t wgrad_list_bound(int e, int per_e) { return (int64_t)((e + kWgradDiv + kXcds - 1) / kXcds) * per_e; }
+// Tiles per workgroup: a workgroup runs a chain of kChain tiles of one unit
+// one after the other (below).  Measured against one tile per workgroup (same
+// output bits): the backward 2.7 % faster on the Qwen3-like layer (8-step
+// tiles) and 1.2 % on the Zipf-loaded 32-expert share (tiles of up to about
+// 160 steps).  Chains of 4 were 4.0 % faster on the former but 1.5 % slower on
+// the latter, chains of 8 26 % slower there: longer chains leave the XCD's
+// dispatcher coarser pieces to balance.  A chain length chosen per expert from
+// its K steps needs a grid sized for one tile per workgroup; the workgroups
+// left without a chain each hold a CU (all of its LDS) while they start and
+// exit, which cost that variant what the longer chains saved.
+constexpr int kChain = 2;
+
+// Upper bound of the workgroups of one XCD's list (the grid is 8 times that):
+// at most ceil(units / 8) units, each of at most ceil(per_e / kChain) chains.
+int64_t wgrad_list_bound(int e, int per_e) {
+  return (int64_t)((e + kWgradDiv + kXcds - 1) / kXcds) * ((per_e + kChain - 1) / kChain);
+}
 
 // 64-row blocks of the K-major copies: at most one partial block per expert.
 int64_t kmajor_blocks(int64_t rows, int e) { return rows / kBK + e + 1; }
@@ -166,7 +182,7 @@ __global__ __launch_bounds__(kPlanThreads) void wgrad_plan_kernel(const int32_t 
   if (x == kXcds + 1) plan[25] = S;
   if (x <= e) plan[kPlanPoff + x] = s_poff[x];
   __syncthreads();
-  // first tile of every entry in its XCD's list, for both gradients: wave g
+  // first chain of every entry in its XCD's list, for both gradients: wave g
   // (0..7) scans list g for dW_down, wave 8 + g for dW_gate_up
   {
     const int g = wv % kXcds, gu = wv >= kXcds;
@@ -178,7 +194,7 @@ __global__ __launch_bounds__(kPlanThreads) void wgrad_plan_kernel(const int32_t 
       if (i < start[g + 1]) {
         const int unit = s_by_slot[i];
         int first;
-        nt = part_tiles((unit >> 11) & 1023, unit >> 21, per_e, first);
+        nt = (part_tiles((unit >> 11) & 1023, unit >> 21, per_e, first) + kChain - 1) / kChain;
       }
       int incl = nt;
 #pragma unroll
@@ -208,7 +224,21 @@ __global__ __launch_bounds__(kPlanThreads) void wgrad_plan_kernel(const int32_t 
 // unit's tiles run n-tile fastest (else m-tile fastest).  The workgroups of an
 // XCD work on consecutive tiles side by side, so the faster index should be
 // the operand with fewer tiles: each pass over it re-reads the smaller panel
-// set.  `field`: which of the plan's two tile lists (0 dW_down, 1 dW_gate_up).
+// set.  `field`: which of the plan's two lists (0 dW_down, 1 dW_gate_up).
+//
+// Chains.  A unit of T tiles is covered by C = ceil(T / kChain) workgroups;
+// workgroup c of the unit runs tiles c, c + C, c + 2C, ... (those below T) one
+// after the other.  Every tile of the unit has the same K extent, so the load
+// ring runs on across the tile boundary: the next tile's first two K steps are
+// loaded during the current tile's last two, and the current tile's epilogue
+// stages its output through the one ring slot that no load in flight targets.
+// Measured on exact uniform layouts of 65536 rows (H 4096, I 1536) with 256
+// to 4096 rows per expert, a weight-gradient tile costs about 6.5-7.7 us
+// beyond its K steps.  A chain pays the tile lookup, the wait for the first
+// loads and the workgroup's launch once; the epilogue stays per tile, and its
+// stores share the CU's memory pipeline with the next tile's loads.  The
+// workgroups of an XCD still run consecutive tile numbers side by side, as
+// without chains: first tiles c .. c+31 of the unit, then c+C .. c+C+31.
 template <bool kNFast, bool kAT>
 __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int M, int N, int m_tiles, int n_tiles, int field,
@@ -221,8 +251,8 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(
   const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds;
   if (slot >= plan[9 + 8 * field + xcd]) return;
 
-  // the entry of this tile: the last one of the XCD's list whose first tile is
-  // <= slot, found by one ballot per 64 entries over all of them at once
+  // the entry of this chain: the last one of the XCD's list whose first chain
+  // is <= slot, found by one ballot per 64 entries over all of them at once
   const int base = plan[xcd], n_ent = plan[xcd + 1] - base;
   const int32_t *ent = plan + kPlanEntries;
   int v_unit[kListLanes], v_rows[kListLanes], v_r0[kListLanes], v_poff[kListLanes], v_first[kListLanes];
@@ -240,7 +270,7 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(
   }
   const int hsel = hit[2] ? 2 : (hit[1] ? 1 : 0);
   const uint64_t hm = hit[hsel];
-  const int src = 63 - __builtin_clzll(hm);  // hm is not empty: the first entry starts at tile 0
+  const int src = 63 - __builtin_clzll(hm);  // hm is not empty: the first entry starts at chain 0
   auto pick = [&](const int (&v)[kListLanes]) {
     const int a = __builtin_amdgcn_readlane(v[0], src), b = __builtin_amdgcn_readlane(v[1], src),
               c = __builtin_amdgcn_readlane(v[2], src);
@@ -250,12 +280,21 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(
             first_slot = pick(v_first);
   const int x = unit & 2047;
   int first;
-  part_tiles((unit >> 11) & 1023, unit >> 21, m_tiles * n_tiles, first);
-  const int loc = first + slot - first_slot;
-  const int m0 = (kNFast ? loc / n_tiles : loc % m_tiles) * kBM;
-  const int n0 = (kNFast ? loc % n_tiles : loc / m_tiles) * kBN;
-  const int rows_valid = M - m0 < kBM ? M - m0 : kBM;
+  const int unit_tiles = part_tiles((unit >> 11) & 1023, unit >> 21, m_tiles * n_tiles, first);
   const int KT = (k_len + kBK - 1) / kBK;
+  const int chains = (unit_tiles + kChain - 1) / kChain;
+  const int chain = slot - first_slot;
+  // tiles of this chain: chain + i * chains for i < n_in (at least one)
+  const int n_in = (unit_tiles - chain + chains - 1) / chains < kChain ? (unit_tiles - chain + chains - 1) / chains
+                                                                       : kChain;
+  auto tile_m0 = [&](int i) {
+    const int loc = first + chain + i * chains;
+    return (kNFast ? loc / n_tiles : loc % m_tiles) * kBM;
+  };
+  auto tile_n0 = [&](int i) {
+    const int loc = first + chain + i * chains;
+    return (kNFast ? loc % n_tiles : loc / m_tiles) * kBN;
+  };
   uint16_t *cb = x < e_master ? C + (int64_t)x * M * N : C_rep + (int64_t)(x - e_master) * M * N;
 
   // Direct loads.  The K-major input: row k of a step holds 256 columns in 512
@@ -266,33 +305,40 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(
   // row r (an output row or column) holds K step kt in 128 bytes; this wave
   // fills rows w*64 .. w*64+63, 8 per instruction: lane l fills row
   // w*64 + 8i + l/8, position l % 8 with chunk position ^ swz(r); rows past the
-  // operand's end re-read its last row.
+  // operand's end re-read its last row.  The offsets depend on the tile only
+  // through those clamps at the matrix edges; they are set for the tile whose
+  // K steps are being loaded (ld_m0, ld_n0).
   uint32_t a_off[kLoads], b_off[kLoads];
   const uint32_t kp2 = (uint32_t)KT * (uint32_t)kRowBytes;  // bytes per row of the copy
+  auto set_offsets = [&](int m0_, int n0_) {
+    const int rows_valid = M - m0_ < kBM ? M - m0_ : kBM;
 #pragma unroll
-  for (int i = 0; i < kLoads; ++i) {
-    const int k = w * 16 + 2 * i + l / 32;
-    const int ct8 = ((l % 32) ^ swz_t(k)) * 8;
-    const int r = w * 64 + i * kLoadRows + l / kChunks;
-    const uint32_t cc = (uint32_t)(((l % kChunks) ^ swz(r)) * 16);
-    if constexpr (kAT) {
-      a_off[i] = (uint32_t)(ct8 > rows_valid - 8 ? rows_valid - 8 : ct8) * 2u;
-      b_off[i] = (uint32_t)(r < N - n0 ? r : N - n0 - 1) * kp2 + cc;
-    } else {
-      a_off[i] = (uint32_t)(r < rows_valid ? r : rows_valid - 1) * kp2 + cc;
-      b_off[i] = (uint32_t)(ct8 > N - n0 - 8 ? N - n0 - 8 : ct8) * 2u;
+    for (int i = 0; i < kLoads; ++i) {
+      const int k = w * 16 + 2 * i + l / 32;
+      const int ct8 = ((l % 32) ^ swz_t(k)) * 8;
+      const int r = w * 64 + i * kLoadRows + l / kChunks;
+      const uint32_t cc = (uint32_t)(((l % kChunks) ^ swz(r)) * 16);
+      if constexpr (kAT) {
+        a_off[i] = (uint32_t)(ct8 > rows_valid - 8 ? rows_valid - 8 : ct8) * 2u;
+        b_off[i] = (uint32_t)(r < N - n0_ ? r : N - n0_ - 1) * kp2 + cc;
+      } else {
+        a_off[i] = (uint32_t)(r < rows_valid ? r : rows_valid - 1) * kp2 + cc;
+        b_off[i] = (uint32_t)(ct8 > N - n0_ - 8 ? N - n0_ - 8 : ct8) * 2u;
+      }
     }
-  }
+  };
+  int ld_m0 = tile_m0(0), ld_n0 = tile_n0(0);
+  set_offsets(ld_m0, ld_n0);
   const uint32_t ring_lds = lds_address(ring) + w * 64 * kRowBytes;  // = w * 16 * kTRowBytes
   auto load_a = [&](int slot_, int kt, int i) {
     const uint32_t dst = ring_lds + slot_ * kOperandBytes + i * 1024;
     if constexpr (kAT) {
       const int k = w * 16 + 2 * i + l / 32, last = k_len - 1 - kt * kBK;
-      const char *src_ = reinterpret_cast<const char *>(A + ((int64_t)r0 + (int64_t)kt * kBK) * M + m0);
+      const char *src_ = reinterpret_cast<const char *>(A + ((int64_t)r0 + (int64_t)kt * kBK) * M + ld_m0);
       dma16(src_, a_off[i] + (uint32_t)(k < last ? k : last) * (uint32_t)M * 2u, dst);
     } else {
       const char *src_ =
-          reinterpret_cast<const char *>(A + (int64_t)M * poff + (int64_t)m0 * KT * kBK + (int64_t)kt * kBK);
+          reinterpret_cast<const char *>(A + (int64_t)M * poff + (int64_t)ld_m0 * KT * kBK + (int64_t)kt * kBK);
       dma16(src_, a_off[i], dst);
     }
   };
@@ -300,11 +346,11 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(
     const uint32_t dst = ring_lds + slot_ * kOperandBytes + i * 1024;
     if constexpr (kBT) {
       const int k = w * 16 + 2 * i + l / 32, last = k_len - 1 - kt * kBK;
-      const char *src_ = reinterpret_cast<const char *>(B + ((int64_t)r0 + (int64_t)kt * kBK) * N + n0);
+      const char *src_ = reinterpret_cast<const char *>(B + ((int64_t)r0 + (int64_t)kt * kBK) * N + ld_n0);
       dma16(src_, b_off[i] + (uint32_t)(k < last ? k : last) * (uint32_t)N * 2u, dst);
     } else {
       const char *src_ =
-          reinterpret_cast<const char *>(B + (int64_t)N * poff + (int64_t)n0 * KT * kBK + (int64_t)kt * kBK);
+          reinterpret_cast<const char *>(B + (int64_t)N * poff + (int64_t)ld_n0 * KT * kBK + (int64_t)kt * kBK);
       dma16(src_, b_off[i], dst);
     }
   };
@@ -319,28 +365,93 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(
   constexpr int kReads = 12;
 
   f32x16 acc[4][4];
+  auto zero_acc = [&]() {
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
+      for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-      for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.0f;
+        for (int q = 0; q < 16; ++q) acc[mi][ni][q] = 0.0f;
+  };
 
-  // K loop, as the grouped GEMM's: step kt's B and A tiles in slots sb, sa;
-  // slices 0 and 1 load step kt+2's B tile into slot pb, slice 3 its A tile
-  // into slot sb; after slice 2 every wave waits for step kt+1's tiles and
-  // passes a barrier.  (An expert without rows has no K step: a zero tile.)
-  if (KT > 0) {
-    bf16x8 fa[2][4], fb[2][4];
+  // Epilogue of tile (m0, n0): each wave converts its 128 x 128 sub-tile to
+  // bf16 and writes it out in four rounds of one 32-row block through its own
+  // 8 KiB of `stage_slot` (16-byte chunks XOR-swizzled by row), as whole
+  // 256-byte rows of 16-byte stores.  No load in flight targets that slot and
+  // no wave still reads it.
+  auto epilogue = [&](int m0, int n0, char *stage_slot) __attribute__((always_inline)) {
+    char *stage = stage_slot + w * (kOperandBytes / 4);
+    const int rows_valid = M - m0 < kBM ? M - m0 : kBM;
+    const bool whole = rows_valid == kBM && n0 + kBN <= N;
+    const int ch = l % 16, col = n0 + wn * 128 + ch * 8;
+    const int rr = l & 31;
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) load_b(0, 0, i);
+    for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) load_a(1, 0, i);
-    if (KT > 1) {
+      for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-      for (int i = 0; i < kLoads; ++i) load_b(2, 1, i);
+        for (int g = 0; g < 4; ++g) {
+          const f32x16 &c = acc[mi][ni];
+          const int f = ni * 32 + 8 * g + 4 * (l >> 5);
+          *reinterpret_cast<uint2 *>(stage + rr * 256 + ((f >> 3) ^ (rr & 15)) * 16 + (f & 7) * 2) =
+              make_uint2(pack_bf16x2(c[4 * g], c[4 * g + 1]), pack_bf16x2(c[4 * g + 2], c[4 * g + 3]));
+        }
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
+      __builtin_amdgcn_wave_barrier();
+      // all eight reads first, then the stores; a whole tile stores unconditionally
+      u32x4 v[8];
 #pragma unroll
-      for (int i = 0; i < kLoads; ++i) load_a(3, 1, i);
+      for (int q = 0; q < 8; ++q) {
+        const int r = l / 16 + 4 * q;
+        v[q] = *reinterpret_cast<const u32x4 *>(stage + r * 256 + (ch ^ (r & 15)) * 16);
+      }
+      uint16_t *c_blk = cb + (int64_t)(m0 + (2 * mi + wm) * 32 + l / 16) * N + col;
+      if (whole) {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) st16(c_blk + (int64_t)(4 * q) * N, v[q]);
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int row = m0 + (2 * mi + wm) * 32 + l / 16 + 4 * q;
+          if (row < M && col < N) st16(c_blk + (int64_t)(4 * q) * N, v[q]);
+        }
+      }
+    }
+  };
+
+  // K loop, as the grouped GEMM's, over the chain's n_in * KT steps: step s's
+  // B and A tiles in slots sb, sa; slices 0 and 1 load step s+2's B tile into
+  // slot pb, slice 3 its A tile into slot sb; after slice 2 every wave waits
+  // for step s+1's tiles and passes a barrier.  (lt, lk) is the tile and K
+  // step whose loads are issued next; (ct, ck) those of the MFMAs.  After the
+  // last step of a tile its epilogue stages through slot sa, which holds only
+  // that step's A tile, already read; a barrier then keeps step s+1's loads
+  // into that slot (its pb) behind every wave's staging reads.
+  const int total = n_in * KT;
+  int lt = 0, lk = 0;
+  auto advance = [&]() {
+    if (++lk == KT) {
+      lk = 0;
+      if (++lt < n_in) {
+        ld_m0 = tile_m0(lt);
+        ld_n0 = tile_n0(lt);
+        set_offsets(ld_m0, ld_n0);
+      }
+    }
+  };
+  bf16x8 fa[2][4], fb[2][4];
+  if (total > 0) {
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) load_b(0, lk, i);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) load_a(1, lk, i);
+    advance();
+    if (total > 1) {
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) load_b(2, lk, i);
+#pragma unroll
+      for (int i = 0; i < kLoads; ++i) load_a(3, lk, i);
+      advance();
       wait_vmcnt<2 * kLoads>();
     } else {
       wait_vmcnt<0>();
@@ -349,21 +460,24 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(
     __builtin_amdgcn_sched_barrier(0);
     load_frags<false, kAT, kBT>(ring + kOperandBytes, ring, 0, wm, wn, l, fa[0], fb[0], ta, tb);
     __builtin_amdgcn_sched_barrier(0);
-    int sb = 0, sa = 1;
-    for (int kt = 0; kt < KT; ++kt) {
+  }
+  int sb = 0, sa = 1;
+  for (int ct = 0; ct < n_in; ++ct) {
+    zero_acc();
+    for (int ck = 0; ck < KT; ++ck) {
       const int nb = sb + 2 < kSlots ? sb + 2 : sb + 2 - kSlots;
       const int na = sa + 2 < kSlots ? sa + 2 : sa + 2 - kSlots;
       const int pb = na + 1 < kSlots ? na + 1 : na + 1 - kSlots;
-      const bool ahead = kt + 2 < KT;
+      const bool ahead = ct * KT + ck + 2 < total;
       const char *as = ring + sa * kOperandBytes;
       const char *bs = ring + sb * kOperandBytes;
       load_frags<false, kAT, kBT>(as, bs, 1, wm, wn, l, fa[1], fb[1], ta, tb);
       slice<4, kReads>(fa[0], fb[0], acc, [&](int d) {
-        if (ahead) load_b(pb, kt + 2, d);
+        if (ahead) load_b(pb, lk, d);
       });
       load_frags<false, kAT, kBT>(as, bs, 2, wm, wn, l, fa[0], fb[0], ta, tb);
       slice<4, kReads>(fa[1], fb[1], acc, [&](int d) {
-        if (ahead) load_b(pb, kt + 2, 4 + d);
+        if (ahead) load_b(pb, lk, 4 + d);
       });
       load_frags<false, kAT, kBT>(as, bs, 3, wm, wn, l, fa[1], fb[1], ta, tb);
       slice<4, kReads>(fa[0], fb[0], acc, [&](int) {});
@@ -371,59 +485,26 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(
       else wait_vmcnt<0>();
       lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      // step kt+1's first fragments (after the last step: stale, unused)
+      // step s+1's first fragments (after the last step: stale, unused)
       load_frags<false, kAT, kBT>(ring + na * kOperandBytes, ring + nb * kOperandBytes, 0, wm, wn, l, fa[0], fb[0],
                                   ta, tb);
       slice<4, kReads>(fa[1], fb[1], acc, [&](int d) {
         if (ahead) {
-          load_a(sb, kt + 2, 2 * d);
-          load_a(sb, kt + 2, 2 * d + 1);
+          load_a(sb, lk, 2 * d);
+          load_a(sb, lk, 2 * d + 1);
         }
       });
       __builtin_amdgcn_sched_barrier(0);
+      if (ahead) advance();
       sb = nb;
       sa = na;
     }
-  }
-
-  // epilogue: each wave converts its 128 x 128 sub-tile to bf16 and writes it
-  // out in four rounds of one 32-row block through its own 8 KiB of LDS (every
-  // real LDS read is done: the last barrier has passed; 16-byte chunks
-  // XOR-swizzled by row), as whole 256-byte rows of 16-byte stores
-  char *stage = ring + w * (kOperandBytes / 4);
-  const bool whole = rows_valid == kBM && n0 + kBN <= N;
-  const int ch = l % 16, col = n0 + wn * 128 + ch * 8;
-  const int rr = l & 31;
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) {
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x16 &c = acc[mi][ni];
-        const int f = ni * 32 + 8 * g + 4 * (l >> 5);
-        *reinterpret_cast<uint2 *>(stage + rr * 256 + ((f >> 3) ^ (rr & 15)) * 16 + (f & 7) * 2) =
-            make_uint2(pack_bf16x2(c[4 * g], c[4 * g + 1]), pack_bf16x2(c[4 * g + 2], c[4 * g + 3]));
-      }
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's staging writes are done
-    __builtin_amdgcn_wave_barrier();
-    // all eight reads first, then the stores; a whole tile stores unconditionally
-    u32x4 v[8];
-#pragma unroll
-    for (int q = 0; q < 8; ++q) {
-      const int r = l / 16 + 4 * q;
-      v[q] = *reinterpret_cast<const u32x4 *>(stage + r * 256 + (ch ^ (r & 15)) * 16);
-    }
-    uint16_t *c_blk = cb + (int64_t)(m0 + (2 * mi + wm) * 32 + l / 16) * N + col;
-    if (whole) {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) st16(c_blk + (int64_t)(4 * q) * N, v[q]);
-    } else {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const int row = m0 + (2 * mi + wm) * 32 + l / 16 + 4 * q;
-        if (row < M && col < N) st16(c_blk + (int64_t)(4 * q) * N, v[q]);
-      }
+    // the last step's A slot, two behind the current one (an expert without
+    // rows has no step: any slot)
+    epilogue(tile_m0(ct), tile_n0(ct), ring + (sa + kSlots - 2) % kSlots * kOperandBytes);
+    if (ct + 1 < n_in) {
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 }

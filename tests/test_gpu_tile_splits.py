@@ -106,6 +106,49 @@ def test_tile_splits_bf16_forward_and_backward(moe):
             assert not dwgu_h[ex].any() and not dwd_h[ex].any()
 
 
+# Weight gradients run their output tiles in chains: workgroup c of a unit of T
+# tiles (a whole expert, or a part of a heavy one) runs tiles c and c + C with
+# C = ceil(T / 2), the load ring running on across the two.  H = 576 and
+# I = 192 make ragged edge tiles in both output dimensions of both gradients
+# (dW_gate_up 384 x 576: 2 x 3 tiles; dW_down 576 x 192: 3 x 1 tiles, so one
+# chain of a single tile), so a chain joins tiles with different edge clamps;
+# the 2000-row expert holds more than 1/16 of all K steps and is split into
+# parts, some with no tile, and so are the 300- and 513-row experts; expert 0
+# has no rows.
+CHAIN_COUNTS = [0, 1, 65, 300, 2000, 70, 129, 513]
+
+
+@pytest.mark.gpu
+def test_weight_gradient_chains(moe):
+    w, idx, wts, x, wgu, wd = split_case(CHAIN_COUNTS, 576, 192, 7)
+    e = w.n_experts
+    xp, wp, lay = moe.moe_dispatch(dev(x), dev(idx), dev(wts), e)
+    y, gu = moe.moe_expert_ffn(xp, lay, dev(wgu), dev(wd), save_gate_up=True)
+    dy = mi.grad_expert_rows(w, lay.rows, 7)
+    gx, dwgu, dwd = moe.moe_expert_ffn_bwd(xp, dev(dy), lay, dev(wgu), dev(wd), gate_up=gu)
+    torch.cuda.synchronize()
+    lay_h = layout_host(lay)
+    lay_h["rows"] = lay.rows
+    np.testing.assert_array_equal(lay_h["tokens_per_expert"], np.asarray(CHAIN_COUNTS, np.int32))
+    ref_gx, ref_dwgu, ref_dwd = oracle.expert_ffn_bwd(host(xp), dy, lay_h, wgu, wd)
+    gx_h, dwgu_h, dwd_h = host(gx), host(dwgu), host(dwd)
+    offs = lay_h["expert_offsets"]
+    for ex, c in enumerate(CHAIN_COUNTS):
+        if c:
+            seg = slice(offs[ex], offs[ex] + c)
+            errs = (max_rel_err(gx_h[seg], ref_gx[seg]), max_rel_err(dwgu_h[ex], ref_dwgu[ex]),
+                    max_rel_err(dwd_h[ex], ref_dwd[ex]))
+            assert max(errs) <= TOL_BF16, (ex, c, errs)
+            # every 256 x 256 tile of both gradients on its own, edge tiles included
+            for g, r in ((dwgu_h[ex], ref_dwgu[ex]), (dwd_h[ex], ref_dwd[ex])):
+                for m0 in range(0, g.shape[0], 256):
+                    for n0 in range(0, g.shape[1], 256):
+                        t = (slice(m0, m0 + 256), slice(n0, n0 + 256))
+                        assert max_rel_err(g[t], r[t]) <= TOL_BF16, (ex, c, g.shape, m0, n0)
+        else:
+            assert not dwgu_h[ex].any() and not dwd_h[ex].any()
+
+
 @pytest.mark.gpu
 def test_tile_splits_mxfp8_forward(moe):
     counts = [33, 96, 160, 224, 257, 385, 513, 769]
