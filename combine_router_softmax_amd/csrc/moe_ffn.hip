@@ -59,15 +59,17 @@ static_assert((kMaxUnits + kXcds - 1) / kXcds <= kListLanes * kWave, "an XCD's l
 static_assert(kMaxUnits <= 2 * kPlanThreads, "two units per plan thread");
 
 // Tiles per workgroup: a workgroup runs a chain of kChain tiles of one unit
-// one after the other (below).  Measured against one tile per workgroup (same
-// output bits): the backward 2.7 % faster on the Qwen3-like layer (8-step
-// tiles) and 1.2 % on the Zipf-loaded 32-expert share (tiles of up to about
-// 160 steps).  Chains of 4 were 4.0 % faster on the former but 1.5 % slower on
-// the latter, chains of 8 26 % slower there: longer chains leave the XCD's
-// dispatcher coarser pieces to balance.  A chain length chosen per expert from
-// its K steps needs a grid sized for one tile per workgroup; the workgroups
-// left without a chain each hold a CU (all of its LDS) while they start and
-// exit, which cost that variant what the longer chains saved.
+// one after the other (below).  Measured in one process against the kernel
+// with one tile per workgroup (same output bits): both weight-gradient kernels
+// 3 % faster at 512-row experts, the FFN backward 1.5 % faster on the
+// Qwen3-like layer and 1.2 % on the Zipf-loaded 32-expert share.  Chains of 4
+// made the kernels 5-6 % faster at 512-row experts but the share's backward
+// 0.5 % slower than one tile per workgroup (its hot experts' tiles have about
+// 160 K steps, so long chains leave the XCD's dispatcher coarse pieces to
+// balance; chains of 8 were 26 % slower there).  A chain length chosen per
+// expert from its K steps needs a grid sized for one tile per workgroup: the
+// workgroups left without a chain each hold a CU (all of its LDS) while they
+// start and exit, which cost that variant what its longer chains saved.
 constexpr int kChain = 2;
 
 // Upper bound of the workgroups of one XCD's list (the grid is 8 times that):
@@ -232,13 +234,12 @@ __global__ __launch_bounds__(kPlanThreads) void wgrad_plan_kernel(const int32_t 
 // ring runs on across the tile boundary: the next tile's first two K steps are
 // loaded during the current tile's last two, and the current tile's epilogue
 // stages its output through the one ring slot that no load in flight targets.
-// Measured on exact uniform layouts of 65536 rows (H 4096, I 1536) with 256
-// to 4096 rows per expert, a weight-gradient tile costs about 6.5-7.7 us
-// beyond its K steps.  A chain pays the tile lookup, the wait for the first
-// loads and the workgroup's launch once; the epilogue stays per tile, and its
-// stores share the CU's memory pipeline with the next tile's loads.  The
-// workgroups of an XCD still run consecutive tile numbers side by side, as
-// without chains: first tiles c .. c+31 of the unit, then c+C .. c+C+31.
+// A chain pays the tile lookup, the wait for the first loads and the
+// workgroup's launch once; the epilogue stays per tile (timing copies at
+// 512-row experts: without its global stores each kernel ran 8 % faster,
+// without its LDS staging 4-7 %).  The workgroups of an XCD still run
+// consecutive tile numbers side by side, as without chains: first tiles
+// c .. c+31 of the unit, then c+C .. c+C+31.
 template <bool kNFast, bool kAT>
 __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, int M, int N, int m_tiles, int n_tiles, int field,
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(
   // w*64 + 8i + l/8, position l % 8 with chunk position ^ swz(r); rows past the
   // operand's end re-read its last row.  The offsets depend on the tile only
   // through those clamps at the matrix edges; they are set for the tile whose
-  // K steps are being loaded (ld_m0, ld_n0).
+  // K steps are being loaded (start_tile below).
   uint32_t a_off[kLoads], b_off[kLoads];
   const uint32_t kp2 = (uint32_t)KT * (uint32_t)kRowBytes;  // bytes per row of the copy
   auto set_offsets = [&](int m0_, int n0_) {
@@ -327,31 +328,46 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(
       }
     }
   };
-  int ld_m0 = tile_m0(0), ld_n0 = tile_n0(0);
-  set_offsets(ld_m0, ld_n0);
+  // The load stream: the sources of the A and B tiles of the K step whose
+  // loads are issued next, and that step's last valid K row (the K-major
+  // operand clamps its rows to it), kept as running values so that a step
+  // costs a few scalar adds (recomputing them from the tile and step numbers
+  // put about 200 scalar instructions into every step, among the MFMAs).
+  const char *ld_a, *ld_b;
+  int ld_last;
+  auto start_tile = [&](int i) {
+    const int m0_ = tile_m0(i), n0_ = tile_n0(i);
+    set_offsets(m0_, n0_);
+    if constexpr (kAT) {
+      ld_a = reinterpret_cast<const char *>(A + (int64_t)r0 * M + m0_);
+      ld_b = reinterpret_cast<const char *>(B + (int64_t)N * poff + (int64_t)n0_ * KT * kBK);
+    } else {
+      ld_a = reinterpret_cast<const char *>(A + (int64_t)M * poff + (int64_t)m0_ * KT * kBK);
+      ld_b = reinterpret_cast<const char *>(B + (int64_t)r0 * N + n0_);
+    }
+    ld_last = k_len - 1;
+  };
+  // bytes between consecutive K steps of the two operands
+  const int64_t a_step = kAT ? (int64_t)kBK * M * 2 : (int64_t)kRowBytes;
+  const int64_t b_step = kAT ? (int64_t)kRowBytes : (int64_t)kBK * N * 2;
+  start_tile(0);
   const uint32_t ring_lds = lds_address(ring) + w * 64 * kRowBytes;  // = w * 16 * kTRowBytes
-  auto load_a = [&](int slot_, int kt, int i) {
+  auto load_a = [&](int slot_, int i) {
     const uint32_t dst = ring_lds + slot_ * kOperandBytes + i * 1024;
     if constexpr (kAT) {
-      const int k = w * 16 + 2 * i + l / 32, last = k_len - 1 - kt * kBK;
-      const char *src_ = reinterpret_cast<const char *>(A + ((int64_t)r0 + (int64_t)kt * kBK) * M + ld_m0);
-      dma16(src_, a_off[i] + (uint32_t)(k < last ? k : last) * (uint32_t)M * 2u, dst);
+      const int k = w * 16 + 2 * i + l / 32;
+      dma16(ld_a, a_off[i] + (uint32_t)(k < ld_last ? k : ld_last) * (uint32_t)M * 2u, dst);
     } else {
-      const char *src_ =
-          reinterpret_cast<const char *>(A + (int64_t)M * poff + (int64_t)ld_m0 * KT * kBK + (int64_t)kt * kBK);
-      dma16(src_, a_off[i], dst);
+      dma16(ld_a, a_off[i], dst);
     }
   };
-  auto load_b = [&](int slot_, int kt, int i) {
+  auto load_b = [&](int slot_, int i) {
     const uint32_t dst = ring_lds + slot_ * kOperandBytes + i * 1024;
     if constexpr (kBT) {
-      const int k = w * 16 + 2 * i + l / 32, last = k_len - 1 - kt * kBK;
-      const char *src_ = reinterpret_cast<const char *>(B + ((int64_t)r0 + (int64_t)kt * kBK) * N + ld_n0);
-      dma16(src_, b_off[i] + (uint32_t)(k < last ? k : last) * (uint32_t)N * 2u, dst);
+      const int k = w * 16 + 2 * i + l / 32;
+      dma16(ld_b, b_off[i] + (uint32_t)(k < ld_last ? k : ld_last) * (uint32_t)N * 2u, dst);
     } else {
-      const char *src_ =
-          reinterpret_cast<const char *>(B + (int64_t)N * poff + (int64_t)ld_n0 * KT * kBK + (int64_t)kt * kBK);
-      dma16(src_, b_off[i], dst);
+      dma16(ld_b, b_off[i], dst);
     }
   };
   uint32_t ta[4][2], tb[4][2];
@@ -432,25 +448,25 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(
   auto advance = [&]() {
     if (++lk == KT) {
       lk = 0;
-      if (++lt < n_in) {
-        ld_m0 = tile_m0(lt);
-        ld_n0 = tile_n0(lt);
-        set_offsets(ld_m0, ld_n0);
-      }
+      if (++lt < n_in) start_tile(lt);
+    } else {
+      ld_a += a_step;
+      ld_b += b_step;
+      ld_last -= kBK;
     }
   };
   bf16x8 fa[2][4], fb[2][4];
   if (total > 0) {
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) load_b(0, lk, i);
+    for (int i = 0; i < kLoads; ++i) load_b(0, i);
 #pragma unroll
-    for (int i = 0; i < kLoads; ++i) load_a(1, lk, i);
+    for (int i = 0; i < kLoads; ++i) load_a(1, i);
     advance();
     if (total > 1) {
 #pragma unroll
-      for (int i = 0; i < kLoads; ++i) load_b(2, lk, i);
+      for (int i = 0; i < kLoads; ++i) load_b(2, i);
 #pragma unroll
-      for (int i = 0; i < kLoads; ++i) load_a(3, lk, i);
+      for (int i = 0; i < kLoads; ++i) load_a(3, i);
       advance();
       wait_vmcnt<2 * kLoads>();
     } else {
@@ -473,11 +489,11 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(
       const char *bs = ring + sb * kOperandBytes;
       load_frags<false, kAT, kBT>(as, bs, 1, wm, wn, l, fa[1], fb[1], ta, tb);
       slice<4, kReads>(fa[0], fb[0], acc, [&](int d) {
-        if (ahead) load_b(pb, lk, d);
+        if (ahead) load_b(pb, d);
       });
       load_frags<false, kAT, kBT>(as, bs, 2, wm, wn, l, fa[0], fb[0], ta, tb);
       slice<4, kReads>(fa[1], fb[1], acc, [&](int d) {
-        if (ahead) load_b(pb, lk, 4 + d);
+        if (ahead) load_b(pb, 4 + d);
       });
       load_frags<false, kAT, kBT>(as, bs, 3, wm, wn, l, fa[1], fb[1], ta, tb);
       slice<4, kReads>(fa[0], fb[0], acc, [&](int) {});
@@ -490,8 +506,8 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(
                                   ta, tb);
       slice<4, kReads>(fa[1], fb[1], acc, [&](int d) {
         if (ahead) {
-          load_a(sb, lk, 2 * d);
-          load_a(sb, lk, 2 * d + 1);
+          load_a(sb, 2 * d);
+          load_a(sb, 2 * d + 1);
         }
       });
       __builtin_amdgcn_sched_barrier(0);
