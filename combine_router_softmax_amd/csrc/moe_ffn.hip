@@ -394,7 +394,10 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(
   // bf16 and writes it out in four rounds of one 32-row block through its own
   // 8 KiB of `stage_slot` (16-byte chunks XOR-swizzled by row), as whole
   // 256-byte rows of 16-byte stores.  No load in flight targets that slot and
-  // no wave still reads it.
+  // no wave still reads it.  The stores are non-temporal: the gradients (as
+  // many bytes as the kernel reads) are not read again here, and streaming
+  // them past the L2 leaves the operand panels there (dW_gate_up 2 % faster,
+  // the backward 0.3-0.6 %, in one process against plain stores).
   auto epilogue = [&](int m0, int n0, char *stage_slot) __attribute__((always_inline)) {
     char *stage = stage_slot + w * (kOperandBytes / 4);
     const int rows_valid = M - m0 < kBM ? M - m0 : kBM;
@@ -424,12 +427,12 @@ __global__ __launch_bounds__(kThreads, 1) void wgrad_kernel(
       uint16_t *c_blk = cb + (int64_t)(m0 + (2 * mi + wm) * 32 + l / 16) * N + col;
       if (whole) {
 #pragma unroll
-        for (int q = 0; q < 8; ++q) st16(c_blk + (int64_t)(4 * q) * N, v[q]);
+        for (int q = 0; q < 8; ++q) st16_stream(c_blk + (int64_t)(4 * q) * N, v[q]);
       } else {
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           const int row = m0 + (2 * mi + wm) * 32 + l / 16 + 4 * q;
-          if (row < M && col < N) st16(c_blk + (int64_t)(4 * q) * N, v[q]);
+          if (row < M && col < N) st16_stream(c_blk + (int64_t)(4 * q) * N, v[q]);
         }
       }
     }
