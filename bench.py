@@ -305,6 +305,11 @@ def dispatch_combine_at(moe, mi, torch, wid, steps, warmup, flush):
         for _ in range(warmup):
             for f in fns: f()
         torch.cuda.synchronize()
+        # a compute-only spin (about 40 us of GPU clock per call to queue) runs
+        # ahead of the start event, so every call is queued before the timed
+        # region begins: at the tiny workload a call's kernels take less time
+        # than the host needs to issue it, and the events would time the host
+        torch.cuda._sleep(int(reps * len(fns) * 80_000))
         t0.record()
         for _ in range(reps):
             for f in fns: f()
