@@ -49,6 +49,14 @@ def pct(v, q):
     return v[min(len(v) - 1, max(0, int(round(q / 100.0 * (len(v) - 1)))))] if v else float("nan")
 
 
+def queue_ahead(torch, calls):
+    """A compute-only spin kernel (about 40 us of GPU clock per call to be queued)
+    ahead of a timed batch: every call is queued before the start event, so the
+    events time the GPU, not the host issuing calls whose kernels take less time
+    than their issue (the tiny workload, the router, the layout alone)."""
+    torch.cuda._sleep(int(calls * 80_000))
+
+
 def bench_dispatch_combine(moe, mi, torch, steps, warmup, options=True):
     import numpy as np
     w = mi.workload(2)
@@ -96,6 +104,7 @@ def bench_dispatch_combine(moe, mi, torch, steps, warmup, options=True):
         for _ in range(warmup):
             for f in fns: f()
         torch.cuda.synchronize()
+        queue_ahead(torch, n * len(fns))
         t0.record()
         for _ in range(n):
             for f in fns: f()
@@ -305,11 +314,7 @@ def dispatch_combine_at(moe, mi, torch, wid, steps, warmup, flush):
         for _ in range(warmup):
             for f in fns: f()
         torch.cuda.synchronize()
-        # a compute-only spin (about 40 us of GPU clock per call to queue) runs
-        # ahead of the start event, so every call is queued before the timed
-        # region begins: at the tiny workload a call's kernels take less time
-        # than the host needs to issue it, and the events would time the host
-        torch.cuda._sleep(int(reps * len(fns) * 80_000))
+        queue_ahead(torch, reps * len(fns))
         t0.record()
         for _ in range(reps):
             for f in fns: f()
@@ -382,6 +387,7 @@ def bench_layout_sizes(moe, torch, steps, warmup, sizes=(4096, 32768, 65536)):
         for _ in range(warmup):
             run()
         torch.cuda.synchronize()
+        queue_ahead(torch, steps)
         t0.record()
         for _ in range(steps):
             run()
