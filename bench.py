@@ -53,8 +53,10 @@ def queue_ahead(torch, calls):
     """A compute-only spin kernel (about 40 us of GPU clock per call to be queued)
     ahead of a timed batch: every call is queued before the start event, so the
     events time the GPU, not the host issuing calls whose kernels take less time
-    than their issue (the tiny workload, the router, the layout alone)."""
-    torch.cuda._sleep(int(calls * 80_000))
+    than their issue (the tiny workload, the router, the layout alone).  Without
+    torch's spin kernel the batch is timed as issued."""
+    if hasattr(torch.cuda, "_sleep"):
+        torch.cuda._sleep(int(calls * 80_000))
 
 
 def bench_dispatch_combine(moe, mi, torch, steps, warmup, options=True):
