@@ -1,4 +1,4 @@
-"""Seeded random draws of the expert FFN backward through the C ABI, against the oracle.
+"""Seeded random draws of the expert FFN forward and backward through the C ABI, against the oracle.
 
 Each draw picks the expert count (1-23), hidden size (64-640) and intermediate size
 (64-512, multiples of 64, so most weight gradients have ragged edge tiles in both
@@ -6,9 +6,10 @@ dimensions) and a row-count pattern: uniform 0-699 rows per expert, one heavy
 expert of 1000-4000 rows over light ones (a unit the weight gradients' work plan
 splits into parts, whose tiles run in chains of two), or Zipf-distributed counts.
 Rows go to experts with one slot per token.  The forward stores the
-pre-activations, the backward takes them; dX on every segment row, dW_gate_up and
-dW_down of every expert (and of every 256 x 256 tile of them on its own) must meet
-the bf16 tolerance, and experts without rows must get zero gradients."""
+pre-activations, the backward takes them; the output on every kept row and on
+every expert's segment, dX on every segment row, dW_gate_up and dW_down of every
+expert (and of every 256 x 256 tile of them on its own) must meet the bf16
+tolerance, and experts without rows must get zero gradients."""
 from __future__ import annotations
 
 import numpy as np
@@ -49,7 +50,7 @@ def draw(rng):
 
 @pytest.mark.gpu
 @pytest.mark.parametrize("seed", range(12))
-def test_ffn_bwd_random_draw(moe, seed):
+def test_ffn_random_draw(moe, seed):
     e, h, inter, counts = draw(np.random.default_rng(1000 + seed))
     n = int(counts.sum())
     print(f"seed {seed}: e={e} h={h} inter={inter} counts={counts.tolist()}", flush=True)
@@ -66,6 +67,9 @@ def test_ffn_bwd_random_draw(moe, seed):
     lay_h = layout_host(lay)
     lay_h["rows"] = lay.rows
     np.testing.assert_array_equal(lay_h["tokens_per_expert"], counts.astype(np.int32))
+    ref_y = oracle.expert_ffn(host(xp), lay_h, wgu, wd)
+    kept = lay_h["pad_mask"] == 0
+    assert max_rel_err(host(y)[kept], ref_y[kept]) <= TOL_BF16
     ref_gx, ref_dwgu, ref_dwd = oracle.expert_ffn_bwd(host(xp), dy, lay_h, wgu, wd)
     gx_h, dwgu_h, dwd_h = host(gx), host(dwgu), host(dwd)
     offs = lay_h["expert_offsets"]
@@ -74,6 +78,7 @@ def test_ffn_bwd_random_draw(moe, seed):
             assert not dwgu_h[ex].any() and not dwd_h[ex].any(), ex
             continue
         seg = slice(offs[ex], offs[ex] + c)
+        assert max_rel_err(host(y)[seg], ref_y[seg]) <= TOL_BF16, (ex, int(c))
         errs = (max_rel_err(gx_h[seg], ref_gx[seg]), max_rel_err(dwgu_h[ex], ref_dwgu[ex]),
                 max_rel_err(dwd_h[ex], ref_dwd[ex]))
         assert max(errs) <= TOL_BF16, (ex, int(c), errs)
